@@ -1,0 +1,132 @@
+"""CPU fp64 oracle for Simple GLA -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It wraps ``sgla_oracle.c`` (plain C,
+fp64, one thread per (sequence, head) unit) through ctypes and shares nothing
+with the GPU library: no code, header, constant or helper.
+
+Semantics (page "flash-linear-attention 中的 Simple GLA", section 一 for the
+recurrence, section 二 for shapes and conventions):
+
+    S_t = exp(g_t) S_{t-1} + k_t v_t^T,   o_t = scale * S_t^T q_t.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sgla_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(out_path: str = _LIB_PATH, mutant: int = 0) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math).  ``mutant`` != 0 builds
+    a deliberately wrong copy for the plant-a-mistake tests."""
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-Wall", "-o", out_path, _SRC,
+           "-lpthread", "-lm"]
+    if mutant:
+        cmd.insert(1, f"-DSGLA_ORACLE_MUTANT={int(mutant)}")
+    subprocess.run(cmd, check=True)
+    return out_path
+
+
+def _bind(lib):
+    dp = ctypes.POINTER(ctypes.c_double)
+    lp = ctypes.POINTER(ctypes.c_int64)
+    lib.sgla_oracle_fwd.restype = ctypes.c_int
+    lib.sgla_oracle_fwd.argtypes = [ctypes.c_int] * 5 + [dp] * 5 + [ctypes.c_double, dp, lp,
+                                                                     ctypes.c_int, dp, dp,
+                                                                     ctypes.c_int]
+    lib.sgla_oracle_step.restype = ctypes.c_int
+    lib.sgla_oracle_step.argtypes = [ctypes.c_int] * 4 + [dp] * 4 + [ctypes.c_double, dp, dp,
+                                                                     ctypes.c_int]
+    return lib
+
+
+def load(path: str | None = None):
+    """Load (building first if absent) the oracle library."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _f64(x):
+    if x is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    return a
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None, cu_seqlens=None,
+        output_final_state=True, nthreads=None, lib=None):
+    """Token-by-token forward.
+
+    q, k: [B, T, H, K]; v: [B, T, H, V]; g: [B, T, H] or None; g_gamma: [H] or None;
+    initial_state: [N, H, K, V] or None; cu_seqlens: int [N+1] or None (then N = B).
+    Returns (o [B, T, H, V], final_state [N, H, K, V] or None), both float64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if scale is None:
+        scale = K ** -0.5
+    g = _f64(g)
+    g_gamma = _f64(g_gamma)
+    h0 = _f64(initial_state)
+    cu = None
+    N = B
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N = cu.shape[0] - 1
+    o = np.zeros((B, T, H, V), dtype=np.float64)
+    ht = np.zeros((N, H, K, V), dtype=np.float64) if output_final_state else None
+    lib = lib or load()
+    rc = lib.sgla_oracle_fwd(B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(g_gamma),
+                             float(scale), _ptr(h0),
+                             None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                             N, _ptr(o), _ptr(ht), int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"sgla_oracle_fwd rejected its arguments (code {rc})")
+    return o, ht
+
+
+def step(q, k, v, g, state, scale=None, nthreads=None, lib=None):
+    """One decode step.  q, k: [N, H, K]; v: [N, H, V]; g: [N, H];
+    state: [N, H, K, V] (not modified; the updated copy is returned).
+    Returns (o [N, H, V], new_state [N, H, K, V]), float64."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    S = np.array(state, dtype=np.float64, order="C", copy=True)
+    N, H, K = q.shape
+    V = v.shape[-1]
+    if scale is None:
+        scale = K ** -0.5
+    o = np.zeros((N, H, V), dtype=np.float64)
+    lib = lib or load()
+    rc = lib.sgla_oracle_step(N, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), float(scale),
+                              _ptr(S), _ptr(o), int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"sgla_oracle_step rejected its arguments (code {rc})")
+    return o, S

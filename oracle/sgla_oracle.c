@@ -1,0 +1,273 @@
+/*
+ * Simple GLA CPU oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, fp64, token-by-token evaluation of the head-wise gated linear
+ * attention recurrence.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library; the GPU product path
+ * never links, loads or calls it, and it shares no code, header or constant
+ * with the GPU library.
+ *
+ * What is computed (page "flash-linear-attention 中的 Simple GLA" (xxqk.cn),
+ * section 一, the recurrence and the naive_recurrent_simple_gla description;
+ * section 二 for the argument conventions):
+ *
+ *     S_t = exp(g_t) * S_{t-1} + k_t v_t^T           (K x V state per head)
+ *     o_t = scale * S_t^T q_t                       (uses the updated state)
+ *
+ * The printed recurrence lost its '=' and '+' in extraction; it is read as
+ * S_{t+1} = g_{t+1} (.) S_t + K_{t+1} V_{t+1}^T with g the per-head scalar
+ * gate.  The API passes the gate in log space (section 二: g are log forget
+ * gates, g_gamma is a head-wise log decay), so the multiplier is exp(g).
+ *
+ * Sequences: dense input is B rows of T tokens; packed (varlen) input has
+ * B == 1 and cu_seqlens[N+1] marking sequence n as tokens
+ * [cu_seqlens[n], cu_seqlens[n+1]) (section 二, FlashAttention convention).
+ * Every sequence starts from initial_state[n] (or zeros) and its state after
+ * its last token is final_state[n].
+ *
+ * Decode step (section 四, the fused_recurrent path for short inputs): one
+ * token per sequence, S <- exp(g) S + k v^T in place, o = scale S^T q.
+ *
+ * Parity pins for this file live in tests/test_oracle_pins.py.  The
+ * SGLA_ORACLE_MUTANT macro (default 0) exists only so that the test suite can
+ * build deliberately wrong copies of this file and show that the pins catch
+ * each planted mistake; the shipped build never defines it.
+ */
+#ifndef SGLA_ORACLE_MUTANT
+#define SGLA_ORACLE_MUTANT 0
+#endif
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    int64_t bos, len;   /* token range of the sequence, in packed token index */
+    int64_t seq;        /* sequence index: row of initial_state / final_state */
+    int head;
+} unit_t;
+
+typedef struct {
+    int T_row;          /* unused for packed input */
+    int H, K, V;
+    const double *q, *k, *v, *g, *g_gamma, *h0;
+    double scale;
+    double *o, *ht;
+    const unit_t *units;
+    int64_t n_units;
+    int64_t next;       /* next unit to take (guarded by mu) */
+    pthread_mutex_t mu;
+} fwd_job_t;
+
+/* One (sequence, head) recurrence, token by token. */
+static void run_unit(const fwd_job_t *J, const unit_t *u, double *S)
+{
+    const int H = J->H, K = J->K, V = J->V, h = u->head;
+    const size_t KV = (size_t)K * V;
+#if SGLA_ORACLE_MUTANT == 3
+    if (J->h0)
+        memcpy(S, J->h0 + ((size_t)u->seq * H + (H - 1 - h)) * KV, KV * sizeof(double));
+#else
+    if (J->h0)
+        memcpy(S, J->h0 + ((size_t)u->seq * H + h) * KV, KV * sizeof(double));
+#endif
+    else
+        memset(S, 0, KV * sizeof(double));
+
+    for (int64_t i = 0; i < u->len; ++i) {
+        const int64_t t = u->bos + i;
+        const double *qt = J->q + ((size_t)t * H + h) * K;
+        const double *kt = J->k + ((size_t)t * H + h) * K;
+        const double *vt = J->v + ((size_t)t * H + h) * V;
+        double logg = 0.0;
+#if SGLA_ORACLE_MUTANT == 4
+        if (J->g) logg = J->g[(size_t)h * J->T_row + (t % (J->T_row > 0 ? J->T_row : 1))];
+#else
+        if (J->g) logg = J->g[(size_t)t * H + h];
+#endif
+        else if (J->g_gamma) logg = J->g_gamma[h];
+        const double gamma = exp(logg);
+        double *ot = J->o + ((size_t)t * H + h) * V;
+#if SGLA_ORACLE_MUTANT == 2
+        for (int b = 0; b < V; ++b) ot[b] = 0.0;
+        for (int a = 0; a < K; ++a)
+            for (int b = 0; b < V; ++b) ot[b] += S[(size_t)a * V + b] * qt[a];
+#endif
+
+        /* state update: decay the previous state, then add k_t v_t^T */
+        for (int a = 0; a < K; ++a) {
+            double *row = S + (size_t)a * V;
+            const double ka = kt[a];
+            for (int b = 0; b < V; ++b)
+#if SGLA_ORACLE_MUTANT == 1
+                row[b] = gamma * (row[b] + ka * vt[b]);
+#else
+                row[b] = gamma * row[b] + ka * vt[b];
+#endif
+        }
+#if SGLA_ORACLE_MUTANT != 2
+        /* output from the updated state: o_t[b] = scale * sum_a S[a][b] q_t[a] */
+        for (int b = 0; b < V; ++b) ot[b] = 0.0;
+        for (int a = 0; a < K; ++a) {
+            const double *row = S + (size_t)a * V;
+#if SGLA_ORACLE_MUTANT == 6
+            const double qa = kt[a];
+#else
+            const double qa = qt[a];
+#endif
+            for (int b = 0; b < V; ++b) ot[b] += row[b] * qa;
+        }
+#endif
+#if SGLA_ORACLE_MUTANT != 5
+        for (int b = 0; b < V; ++b) ot[b] *= J->scale;
+#endif
+    }
+    if (J->ht)
+        memcpy(J->ht + ((size_t)u->seq * H + h) * KV, S, KV * sizeof(double));
+}
+
+static void *fwd_worker(void *arg)
+{
+    fwd_job_t *J = (fwd_job_t *)arg;
+    double *S = (double *)malloc((size_t)J->K * J->V * sizeof(double));
+    if (!S) return (void *)1;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int64_t i = J->next++;
+        pthread_mutex_unlock(&J->mu);
+        if (i >= J->n_units) break;
+        run_unit(J, &J->units[i], S);
+    }
+    free(S);
+    return NULL;
+}
+
+/*
+ * Forward over all sequences and heads.
+ *   q, k : [B, T, H, K]   v, o : [B, T, H, V]   (packed: B = 1, T = total tokens)
+ *   g    : [B, T, H] log gates, or NULL
+ *   g_gamma : [H] per-head log decay, or NULL (at most one of g / g_gamma;
+ *             neither means no decay)
+ *   h0, ht : [N, H, K, V] or NULL; N = B (dense) or num_seqs (packed)
+ *   cu_seqlens : [num_seqs + 1] token offsets (packed) or NULL (dense)
+ * Returns 0 on success, negative on a malformed argument.
+ */
+int sgla_oracle_fwd(int B, int T, int H, int K, int V,
+                    const double *q, const double *k, const double *v,
+                    const double *g, const double *g_gamma, double scale,
+                    const double *h0, const int64_t *cu_seqlens, int num_seqs,
+                    double *o, double *ht, int nthreads)
+{
+    if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return -1;
+    if (g && g_gamma) return -2;
+    if (cu_seqlens && B != 1) return -3;
+    int N = cu_seqlens ? num_seqs : B;
+    if (N < 0) return -1;
+    int64_t n_units = (int64_t)N * H;
+    unit_t *units = (unit_t *)malloc((size_t)(n_units > 0 ? n_units : 1) * sizeof(unit_t));
+    if (!units) return -4;
+    for (int n = 0; n < N; ++n) {
+        int64_t bos, len;
+        if (cu_seqlens) {
+            bos = cu_seqlens[n];
+            len = cu_seqlens[n + 1] - cu_seqlens[n];
+            if (len < 0 || bos < 0 || cu_seqlens[n + 1] > (int64_t)T) { free(units); return -5; }
+        } else {
+            bos = (int64_t)n * T;
+            len = T;
+        }
+        for (int h = 0; h < H; ++h) {
+            unit_t *u = &units[(int64_t)n * H + h];
+            u->bos = bos; u->len = len; u->seq = n; u->head = h;
+        }
+    }
+    fwd_job_t J;
+    J.T_row = T; J.H = H; J.K = K; J.V = V;
+    J.q = q; J.k = k; J.v = v; J.g = g; J.g_gamma = g_gamma; J.h0 = h0;
+    J.scale = scale; J.o = o; J.ht = ht; J.units = units; J.n_units = n_units; J.next = 0;
+    pthread_mutex_init(&J.mu, NULL);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    int started = 0, rc = 0;
+    for (int i = 1; i < nthreads; ++i)
+        if (pthread_create(&th[started], NULL, fwd_worker, &J) == 0) ++started;
+    if (fwd_worker(&J) != NULL) rc = -4;
+    for (int i = 0; i < started; ++i) {
+        void *r = NULL;
+        pthread_join(th[i], &r);
+        if (r != NULL) rc = -4;
+    }
+    pthread_mutex_destroy(&J.mu);
+    free(units);
+    return rc;
+}
+
+typedef struct {
+    int H, K, V;
+    const double *q, *k, *v, *g;
+    double scale;
+    double *S, *o;
+    int64_t n_units, next;
+    pthread_mutex_t mu;
+} step_job_t;
+
+static void *step_worker(void *arg)
+{
+    step_job_t *J = (step_job_t *)arg;
+    const int K = J->K, V = J->V;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int64_t u = J->next++;
+        pthread_mutex_unlock(&J->mu);
+        if (u >= J->n_units) break;
+        /* unit u = (sequence n, head h) flattened as n * H + h */
+        const double *qt = J->q + (size_t)u * K;
+        const double *kt = J->k + (size_t)u * K;
+        const double *vt = J->v + (size_t)u * V;
+        const double gamma = exp(J->g[u]);
+        double *S = J->S + (size_t)u * K * V;
+        double *ot = J->o + (size_t)u * V;
+        for (int a = 0; a < K; ++a)
+            for (int b = 0; b < V; ++b)
+#if SGLA_ORACLE_MUTANT == 7
+                S[(size_t)a * V + b] = gamma * S[(size_t)a * V + b] + kt[b % K] * vt[a % V];
+#else
+                S[(size_t)a * V + b] = gamma * S[(size_t)a * V + b] + kt[a] * vt[b];
+#endif
+        for (int b = 0; b < V; ++b) ot[b] = 0.0;
+        for (int a = 0; a < K; ++a)
+            for (int b = 0; b < V; ++b) ot[b] += S[(size_t)a * V + b] * qt[a];
+        for (int b = 0; b < V; ++b) ot[b] *= J->scale;
+    }
+    return NULL;
+}
+
+/*
+ * One decode step for N sequences x H heads.
+ *   q, k : [N, H, K]  v, o : [N, H, V]  g : [N, H] log gate
+ *   S    : [N, H, K, V], updated in place.
+ */
+int sgla_oracle_step(int N, int H, int K, int V,
+                     const double *q, const double *k, const double *v,
+                     const double *g, double scale, double *S, double *o,
+                     int nthreads)
+{
+    if (N < 0 || H <= 0 || K <= 0 || V <= 0 || !g || !S) return -1;
+    step_job_t J;
+    J.H = H; J.K = K; J.V = V; J.q = q; J.k = k; J.v = v; J.g = g;
+    J.scale = scale; J.S = S; J.o = o;
+    J.n_units = (int64_t)N * H; J.next = 0;
+    pthread_mutex_init(&J.mu, NULL);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    int started = 0;
+    for (int i = 1; i < nthreads; ++i)
+        if (pthread_create(&th[started], NULL, step_worker, &J) == 0) ++started;
+    step_worker(&J);
+    for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+    pthread_mutex_destroy(&J.mu);
+    return 0;
+}
