@@ -1,0 +1,244 @@
+"""Python binding of libsgla -- Simple GLA (head-wise gated linear attention)
+on MI355X (gfx950).
+
+This module only marshals arguments: it allocates outputs and workspace with
+torch on the inputs' device, passes raw device pointers and torch's current
+HIP stream through the C ABI declared in ``include/sgla.h``, and turns error
+statuses into exceptions.  Every step of the computation runs in the HIP
+kernels of ``libsgla.so``; there is no CPU or PyTorch fallback.  If the
+library has not been built, importing this package raises ImportError.
+
+Operator (page "flash-linear-attention 中的 Simple GLA", section 一):
+    S_t = exp(g_t) S_{t-1} + k_t v_t^T,    o_t = scale * S_t^T q_t
+API conventions follow section 二 of that page: q, k [B, T, H, K], v [B, T,
+H, V], g [B, T, H] log gates or g_gamma [H] per-head log decay (not both),
+scale defaulting to 1/sqrt(K), states [N, H, K, V], cu_seqlens [N + 1] with
+B == 1 for packed input, chunk_size a power of two (64).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["chunk_fwd", "recurrent_step", "chunk_local_cumsum", "library_path", "lib",
+           "SglaError", "ABI_VERSION"]
+
+ABI_VERSION = 1
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsgla.so")
+
+_OK, _INVALID, _SHAPE, _DTYPE, _UNSUPPORTED, _WORKSPACE, _HIP = range(7)
+_BF16, _F32 = 1, 2
+
+
+class SglaError(RuntimeError):
+    """A HIP runtime failure reported by libsgla."""
+
+
+class _ChunkArgs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("chunk_size", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32),
+                ("o_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("output_final_state", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"libsgla.so is not built ({_LIB_PATH} missing); run "
+            "`python -m gated_linear_attention_amd.build` (hipcc, gfx950). There is no fallback.")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    pargs = ctypes.POINTER(_ChunkArgs)
+    lib.sgla_abi_version.restype = ctypes.c_int
+    lib.sgla_abi_version.argtypes = []
+    lib.sgla_last_error.restype = ctypes.c_char_p
+    lib.sgla_last_error.argtypes = []
+    lib.sgla_chunk_fwd_workspace_size.restype = sz
+    lib.sgla_chunk_fwd_workspace_size.argtypes = [pargs, vp]
+    lib.sgla_chunk_fwd.restype = ctypes.c_int
+    lib.sgla_chunk_fwd.argtypes = [pargs, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sgla_chunk_local_cumsum.restype = ctypes.c_int
+    lib.sgla_chunk_local_cumsum.argtypes = [pargs, vp, vp, vp, vp, sz, vp]
+    lib.sgla_recurrent_step.restype = ctypes.c_int
+    lib.sgla_recurrent_step.argtypes = [i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp,
+                                        vp, vp]
+    if lib.sgla_abi_version() != ABI_VERSION:
+        raise ImportError(f"libsgla ABI {lib.sgla_abi_version()} != binding ABI {ABI_VERSION}")
+    return lib
+
+
+lib = _load()
+
+
+def _raise(status: int, what: str):
+    msg = lib.sgla_last_error().decode(errors="replace")
+    if status in (_INVALID, _SHAPE, _DTYPE, _UNSUPPORTED, _WORKSPACE):
+        raise ValueError(f"{what}: {msg}")
+    raise SglaError(f"{what} failed (status {status}): {msg}")
+
+
+def _dtype_code(t: torch.dtype, what: str) -> int:
+    if t == torch.bfloat16:
+        return _BF16
+    if t == torch.float32:
+        return _F32
+    raise ValueError(f"{what} must be bfloat16 or float32, got {t}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(name, t, dev, dtype=None, shape=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _host_cu(cu_seqlens):
+    if cu_seqlens is None:
+        return None
+    if isinstance(cu_seqlens, torch.Tensor):
+        cu = cu_seqlens.detach().to("cpu", torch.int64).contiguous()
+    else:
+        cu = torch.as_tensor(list(cu_seqlens), dtype=torch.int64)
+    if cu.dim() != 1 or cu.numel() < 2:
+        raise ValueError("cu_seqlens must be a 1-D sequence of N + 1 offsets")
+    return cu
+
+
+def _chunk_args(B, T, H, K, V, N, chunk_size, qkv, o_dtype, scale, out_final):
+    return _ChunkArgs(B, T, H, K, V, N, chunk_size, qkv, o_dtype, float(scale), int(out_final))
+
+
+def _workspace_size(args, cu_ptr) -> int:
+    n = lib.sgla_chunk_fwd_workspace_size(ctypes.byref(args), cu_ptr)
+    if n == 0:
+        msg = lib.sgla_last_error()
+        if msg:
+            raise ValueError(f"sgla_chunk_fwd_workspace_size: {msg.decode(errors='replace')}")
+    return n
+
+
+def chunk_fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None,
+              output_final_state=False, cu_seqlens=None, chunk_size=64,
+              o_dtype=torch.float32, out=None):
+    """Chunked Simple GLA forward on the GPU.
+
+    Returns ``(o, final_state)``; ``final_state`` is None unless
+    ``output_final_state``.  ``out`` optionally supplies a preallocated o."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor [B, T, H, K]")
+    dev = q.device
+    B, T, H, K = q.shape
+    if v.dim() != 4:
+        raise ValueError("v must be a 4-D tensor [B, T, H, V]")
+    V = v.shape[-1]
+    qkv = _dtype_code(q.dtype, "q")
+    _check_dev("q", q, dev)
+    _check_dev("k", k, dev, q.dtype, (B, T, H, K))
+    _check_dev("v", v, dev, q.dtype, (B, T, H, V))
+    if g is not None and g_gamma is not None:
+        raise ValueError("g and g_gamma are mutually exclusive; pass at most one")
+    _check_dev("g", g, dev, torch.float32, (B, T, H))
+    _check_dev("g_gamma", g_gamma, dev, torch.float32, (H,))
+    cu = _host_cu(cu_seqlens)
+    N = B if cu is None else cu.numel() - 1
+    if cu is not None and B != 1:
+        raise ValueError(f"packed input (cu_seqlens) requires B == 1, got B={B}")
+    if initial_state is not None and initial_state.shape[0] != N:
+        raise ValueError(f"initial_state must have {N} rows (one per sequence), got "
+                         f"{initial_state.shape[0]}")
+    _check_dev("initial_state", initial_state, dev, torch.float32, (N, H, K, V))
+    if scale is None:
+        scale = K ** -0.5
+    od = _dtype_code(o_dtype, "o_dtype")
+    args = _chunk_args(B, T, H, K, V, N, chunk_size, qkv, od, scale, output_final_state)
+    cu_ptr = None if cu is None else ctypes.c_void_p(cu.data_ptr())
+    ws_bytes = _workspace_size(args, cu_ptr)
+    if out is None:
+        o = torch.empty((B, T, H, V), device=dev, dtype=o_dtype)
+    else:
+        _check_dev("out", out, dev, o_dtype, (B, T, H, V))
+        o = out
+    ht = torch.empty((N, H, K, V), device=dev, dtype=torch.float32) if output_final_state else None
+    ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    st = lib.sgla_chunk_fwd(ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                            _ptr(g_gamma), _ptr(initial_state), cu_ptr, _ptr(o), _ptr(ht),
+                            _ptr(ws), ws_bytes, _stream(dev))
+    if st != _OK:
+        _raise(st, "sgla_chunk_fwd")
+    return o, ht
+
+
+def chunk_local_cumsum(g, chunk_size=64, cu_seqlens=None):
+    """Step (1) alone: chunk-local inclusive cumulative sum of g times 1/ln 2
+    (float32 [B, T, H] in, float32 [B, T, H] out)."""
+    if not isinstance(g, torch.Tensor) or g.dim() != 3:
+        raise ValueError("g must be a 3-D tensor [B, T, H]")
+    dev = g.device
+    _check_dev("g", g, dev, torch.float32)
+    B, T, H = g.shape
+    cu = _host_cu(cu_seqlens)
+    N = B if cu is None else cu.numel() - 1
+    args = _chunk_args(B, T, H, 64, 64, N, chunk_size, _BF16, _F32, 1.0, 0)
+    cu_ptr = None if cu is None else ctypes.c_void_p(cu.data_ptr())
+    ws_bytes = _workspace_size(args, cu_ptr)
+    ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    gc = torch.empty_like(g)
+    st = lib.sgla_chunk_local_cumsum(ctypes.byref(args), _ptr(g), cu_ptr, _ptr(gc), _ptr(ws),
+                                     ws_bytes, _stream(dev))
+    if st != _OK:
+        _raise(st, "sgla_chunk_local_cumsum")
+    return gc
+
+
+def recurrent_step(q, k, v, g, state, scale=None, o_dtype=torch.float32, out=None):
+    """One decode step; ``state`` [N, H, K, V] float32 is updated in place.
+    q, k [N, H, K], v [N, H, V] (bf16 or float32), g [N, H] float32.
+    Returns o [N, H, V]."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a 3-D tensor [N, H, K]")
+    dev = q.device
+    N, H, K = q.shape
+    V = v.shape[-1]
+    qkv = _dtype_code(q.dtype, "q")
+    _check_dev("q", q, dev)
+    _check_dev("k", k, dev, q.dtype, (N, H, K))
+    _check_dev("v", v, dev, q.dtype, (N, H, V))
+    _check_dev("g", g, dev, torch.float32, (N, H))
+    _check_dev("state", state, dev, torch.float32, (N, H, K, V))
+    if scale is None:
+        scale = K ** -0.5
+    od = _dtype_code(o_dtype, "o_dtype")
+    if out is None:
+        o = torch.empty((N, H, V), device=dev, dtype=o_dtype)
+    else:
+        _check_dev("out", out, dev, o_dtype, (N, H, V))
+        o = out
+    st = lib.sgla_recurrent_step(N, H, K, V, float(scale), qkv, od, _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(g), _ptr(state), _ptr(o), _stream(dev))
+    if st != _OK:
+        _raise(st, "sgla_recurrent_step")
+    return o

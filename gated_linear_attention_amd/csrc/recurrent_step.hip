@@ -1,0 +1,129 @@
+// Step (4): one decode token per sequence, updating the float32 state in place
+// (page "flash-linear-attention 中的 Simple GLA", section 四: for single-token
+// inference the layer switches from the chunk kernel to a fused recurrent
+// kernel because a chunk launch for one token is slower; section 二: states
+// are [N, H, K, V] with S[k][v]):
+//
+//     S <- exp(g) * S + k v^T ;    o = scale * S^T q   (post-update state).
+//
+// The step is a pure read-modify-write stream over the state: 2 * K * V * 4
+// bytes per (sequence, head) against 5 * K * V flops, so it is bound by HBM.
+// One 256-thread workgroup owns one (sequence, head) state.  Each thread owns
+// four adjacent v columns (16-byte accesses) and every RG-th k row, so a wave
+// touches whole contiguous state rows.  All of a thread's rows of a batch are
+// loaded before any is used so that many 16-byte loads are in flight per
+// wave; the q-weighted column sums are then reduced across row groups through
+// LDS.
+#include <hip/hip_runtime.h>
+
+#include "sgla_internal.h"
+
+namespace sgla {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x);
+template <>
+__device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ float to_f32<__bf16>(__bf16 x) { return (float)x; }
+
+template <int V, typename TIn, typename TOut>
+__global__ void __launch_bounds__(256)
+recurrent_step_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                      const TIn* __restrict__ v, const float* __restrict__ g,
+                      float* __restrict__ state, TOut* __restrict__ o, float scale, int32_t K) {
+  constexpr int TPR = V / 4;          // threads per state row
+  constexpr int RG = 256 / TPR;       // row groups
+  constexpr int BATCH = 16;           // rows in flight per thread
+  __shared__ float part[RG][V];
+
+  const int64_t unit = blockIdx.x;    // n * H + h
+  const int tid = threadIdx.x;
+  const int cq = tid % TPR;
+  const int rg = tid / TPR;
+  const float gamma = expf(g[unit]);
+  const TIn* qu = q + unit * K;
+  const TIn* ku = k + unit * K;
+  f32x4 vv;
+  {
+    const TIn* vu = v + unit * V + 4 * cq;
+    vv = f32x4{to_f32(vu[0]), to_f32(vu[1]), to_f32(vu[2]), to_f32(vu[3])};
+  }
+  f32x4* S = reinterpret_cast<f32x4*>(state + unit * (int64_t)K * V);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+
+  for (int r0 = rg; r0 < K; r0 += RG * BATCH) {
+    f32x4 s[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int r = r0 + b * RG;
+      if (r < K) s[b] = __builtin_nontemporal_load(&S[(int64_t)r * TPR + cq]);
+    }
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int r = r0 + b * RG;
+      if (r < K) {
+        const float kr = to_f32(ku[r]);
+        const float qr = to_f32(qu[r]);
+        f32x4 x = s[b];
+        x.x = fmaf(gamma, x.x, kr * vv.x);
+        x.y = fmaf(gamma, x.y, kr * vv.y);
+        x.z = fmaf(gamma, x.z, kr * vv.z);
+        x.w = fmaf(gamma, x.w, kr * vv.w);
+        __builtin_nontemporal_store(x, &S[(int64_t)r * TPR + cq]);
+        acc.x = fmaf(x.x, qr, acc.x);
+        acc.y = fmaf(x.y, qr, acc.y);
+        acc.z = fmaf(x.z, qr, acc.z);
+        acc.w = fmaf(x.w, qr, acc.w);
+      }
+    }
+  }
+  static_assert(RG >= 2 && RG * TPR == 256, "V must be a power of two in [32, 512]");
+  *reinterpret_cast<f32x4*>(&part[rg][4 * cq]) = acc;
+  __syncthreads();
+  for (int c = tid; c < V; c += 256) {
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < RG; ++i) sum += part[i][c];
+    o[unit * V + c] = (TOut)(sum * scale);
+  }
+}
+
+template <int V, typename TIn, typename TOut>
+hipError_t launch_v(const StepParams& p, hipStream_t stream) {
+  const int64_t units = (int64_t)p.N * p.H;
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL((recurrent_step_kernel<V, TIn, TOut>), dim3((unsigned)units), dim3(256), 0,
+                     stream, static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k),
+                     static_cast<const TIn*>(p.v), p.g, p.state, static_cast<TOut*>(p.o),
+                     p.scale, p.K);
+  return hipGetLastError();
+}
+
+template <typename TIn, typename TOut>
+hipError_t launch_dtypes(const StepParams& p, hipStream_t stream) {
+  switch (p.V) {
+    case 32: return launch_v<32, TIn, TOut>(p, stream);
+    case 64: return launch_v<64, TIn, TOut>(p, stream);
+    case 128: return launch_v<128, TIn, TOut>(p, stream);
+    case 256: return launch_v<256, TIn, TOut>(p, stream);
+    case 512: return launch_v<512, TIn, TOut>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_recurrent_step(const StepParams& p, hipStream_t stream) {
+  if (p.qkv_bf16) {
+    return p.o_bf16 ? launch_dtypes<__bf16, __bf16>(p, stream)
+                    : launch_dtypes<__bf16, float>(p, stream);
+  }
+  return p.o_bf16 ? launch_dtypes<float, __bf16>(p, stream)
+                  : launch_dtypes<float, float>(p, stream);
+}
+
+}  // namespace sgla

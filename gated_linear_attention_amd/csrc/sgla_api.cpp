@@ -1,0 +1,295 @@
+// C ABI of libsgla: argument validation, workspace sizing, packed-sequence
+// tables and kernel launches.  Every check happens on the host before any
+// work is enqueued, so a rejected call leaves outputs, state and workspace
+// untouched (page "flash-linear-attention 中的 Simple GLA", section 二: g and
+// g_gamma are exclusive, packed input needs B == 1 and one initial state per
+// sequence, chunk_size is a power of two; errors are raised, never absorbed
+// by a silent fallback).
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "sgla.h"
+#include "sgla_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sgla_status fail(sgla_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+sgla_status ok() {
+  g_last_error.clear();
+  return SGLA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Validated description of one chunk_fwd request.
+struct Plan {
+  int32_t N = 0;             // sequences
+  int64_t total_tokens = 0;  // B * T
+  int32_t num_chunks = 0;
+  bool packed = false;
+  std::vector<sgla::SeqEntry> seqs;      // packed only, longest first
+  std::vector<sgla::ChunkEntry> chunks;  // packed only
+  size_t gc_bytes = 0;
+  size_t seq_off = 0, chunk_off = 0, total_bytes = 0;
+};
+
+sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv_support,
+                       Plan* P) {
+  if (a == nullptr) return fail(SGLA_ERR_INVALID_ARG, "args is NULL");
+  if (a->B < 0 || a->T < 0) return fail(SGLA_ERR_SHAPE, "B and T must be >= 0 (got B=%d T=%d)", a->B, a->T);
+  if (a->H <= 0) return fail(SGLA_ERR_SHAPE, "H must be > 0 (got %d)", a->H);
+  const int32_t cs = a->chunk_size == 0 ? sgla::kChunk : a->chunk_size;
+  if (!is_pow2(cs)) return fail(SGLA_ERR_SHAPE, "chunk_size must be a power of two (got %d)", cs);
+  if (cs != sgla::kChunk)
+    return fail(SGLA_ERR_UNSUPPORTED, "chunk_size %d is not implemented (only 64)", cs);
+  if (need_kv_support) {
+    if (a->K <= 0 || a->V <= 0) return fail(SGLA_ERR_SHAPE, "K and V must be > 0");
+    if (a->qkv_dtype == SGLA_BF16) {
+      if (!(a->K == 64 || a->K == 128 || a->K == 256 || a->K == 512))
+        return fail(SGLA_ERR_UNSUPPORTED, "bf16 inputs support K in {64,128,256,512} (got %d)", a->K);
+      if (a->V % 64 != 0)
+        return fail(SGLA_ERR_UNSUPPORTED, "bf16 inputs support V a multiple of 64 (got %d)", a->V);
+    } else if (a->qkv_dtype == SGLA_F32) {
+      if (!(a->K == 16 || a->K == 32 || a->K == 64 || a->K == 128))
+        return fail(SGLA_ERR_UNSUPPORTED, "float32 inputs support K in {16,32,64,128} (got %d)", a->K);
+      if (a->V % 32 != 0)
+        return fail(SGLA_ERR_UNSUPPORTED, "float32 inputs support V a multiple of 32 (got %d)", a->V);
+    } else {
+      return fail(SGLA_ERR_DTYPE, "qkv_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", a->qkv_dtype);
+    }
+    if (a->o_dtype != SGLA_BF16 && a->o_dtype != SGLA_F32)
+      return fail(SGLA_ERR_DTYPE, "o_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", a->o_dtype);
+    if (!std::isfinite(a->scale)) return fail(SGLA_ERR_INVALID_ARG, "scale must be finite");
+  }
+  P->total_tokens = (int64_t)a->B * a->T;
+  if (P->total_tokens > INT32_MAX)
+    return fail(SGLA_ERR_UNSUPPORTED, "B*T = %lld tokens exceeds 2^31-1", (long long)P->total_tokens);
+  if (cu != nullptr) {
+    P->packed = true;
+    if (a->B != 1) return fail(SGLA_ERR_SHAPE, "packed input (cu_seqlens given) requires B == 1 (got B=%d)", a->B);
+    if (a->num_seqs < 1) return fail(SGLA_ERR_SHAPE, "num_seqs must be >= 1 with cu_seqlens (got %d)", a->num_seqs);
+    P->N = a->num_seqs;
+    if (cu[0] != 0) return fail(SGLA_ERR_SHAPE, "cu_seqlens[0] must be 0 (got %lld)", (long long)cu[0]);
+    for (int32_t n = 0; n < P->N; ++n)
+      if (cu[n + 1] < cu[n])
+        return fail(SGLA_ERR_SHAPE, "cu_seqlens must be non-decreasing (cu[%d]=%lld > cu[%d]=%lld)", n,
+                    (long long)cu[n], n + 1, (long long)cu[n + 1]);
+    if (cu[P->N] != a->T)
+      return fail(SGLA_ERR_SHAPE, "cu_seqlens[N] must equal T (got %lld, T=%d)", (long long)cu[P->N], a->T);
+    P->seqs.resize(P->N);
+    for (int32_t n = 0; n < P->N; ++n) {
+      sgla::SeqEntry& e = P->seqs[n];
+      e.bos = (int32_t)cu[n];
+      e.len = (int32_t)(cu[n + 1] - cu[n]);
+      e.seq = n;
+      e.pad = 0;
+    }
+    // longest sequences first: they bound the critical path
+    std::stable_sort(P->seqs.begin(), P->seqs.end(),
+                     [](const sgla::SeqEntry& x, const sgla::SeqEntry& y) { return x.len > y.len; });
+    for (int32_t n = 0; n < P->N; ++n)
+      for (int64_t t = cu[n]; t < cu[n + 1]; t += sgla::kChunk)
+        P->chunks.push_back({(int32_t)t, (int32_t)std::min<int64_t>(sgla::kChunk, cu[n + 1] - t)});
+    P->num_chunks = (int32_t)P->chunks.size();
+  } else {
+    P->N = a->B;
+    P->num_chunks = a->T > 0 ? a->B * ((a->T + sgla::kChunk - 1) / sgla::kChunk) : 0;
+  }
+  P->gc_bytes = align_up((size_t)P->total_tokens * a->H * sizeof(float), 256);
+  P->seq_off = P->gc_bytes;
+  P->chunk_off = P->seq_off + align_up(P->seqs.size() * sizeof(sgla::SeqEntry), 256);
+  P->total_bytes = P->chunk_off + align_up(P->chunks.size() * sizeof(sgla::ChunkEntry), 256);
+  return SGLA_OK;
+}
+
+sgla_status hip_fail(hipError_t e, const char* what) {
+  return fail(SGLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Copy the packed-sequence tables into the workspace (stream-ordered; the
+// host source is staged by the runtime before the call returns).
+sgla_status upload_tables(const Plan& P, char* ws, hipStream_t stream) {
+  if (!P.packed) return SGLA_OK;
+  hipError_t e = hipMemcpyAsync(ws + P.seq_off, P.seqs.data(), P.seqs.size() * sizeof(sgla::SeqEntry),
+                                hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "copying the sequence table");
+  if (!P.chunks.empty()) {
+    e = hipMemcpyAsync(ws + P.chunk_off, P.chunks.data(), P.chunks.size() * sizeof(sgla::ChunkEntry),
+                       hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "copying the chunk table");
+  }
+  return SGLA_OK;
+}
+
+sgla::SeqLayout layout_of(const sgla_chunk_args* a, const Plan& P, char* ws) {
+  sgla::SeqLayout L;
+  L.num_seqs = P.N;
+  L.T = a->T;
+  L.seq_table = P.packed ? reinterpret_cast<const sgla::SeqEntry*>(ws + P.seq_off) : nullptr;
+  L.chunk_table = P.packed ? reinterpret_cast<const sgla::ChunkEntry*>(ws + P.chunk_off) : nullptr;
+  L.num_chunks = P.num_chunks;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sgla_abi_version(void) { return SGLA_ABI_VERSION; }
+
+const char* sgla_last_error(void) { return g_last_error.c_str(); }
+
+size_t sgla_chunk_fwd_workspace_size(const sgla_chunk_args* args, const int64_t* cu_seqlens_host) {
+  Plan P;
+  if (plan_shape(args, cu_seqlens_host, true, &P) != SGLA_OK) return 0;
+  g_last_error.clear();
+  return P.total_bytes;
+}
+
+sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const void* k, const void* v,
+                           const float* g, const float* g_gamma, const float* initial_state,
+                           const int64_t* cu_seqlens_host, void* o, float* final_state,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Plan P;
+  sgla_status st = plan_shape(args, cu_seqlens_host, true, &P);
+  if (st != SGLA_OK) return st;
+  const sgla_chunk_args& a = *args;
+  if (g != nullptr && g_gamma != nullptr)
+    return fail(SGLA_ERR_INVALID_ARG, "g and g_gamma are mutually exclusive; pass at most one");
+  const bool any_tokens = P.total_tokens > 0;
+  if (any_tokens && (q == nullptr || k == nullptr || v == nullptr || o == nullptr))
+    return fail(SGLA_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
+  if (a.output_final_state && final_state == nullptr)
+    return fail(SGLA_ERR_INVALID_ARG, "output_final_state is set but final_state is NULL");
+  if (any_tokens && !(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(o, 16)))
+    return fail(SGLA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if ((g && !aligned(g, 4)) || (initial_state && !aligned(initial_state, 16)) ||
+      (final_state && !aligned(final_state, 16)))
+    return fail(SGLA_ERR_INVALID_ARG, "g and state pointers must be aligned");
+  const size_t need = P.total_bytes;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(SGLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
+                workspace == nullptr ? " (NULL)" : "");
+  if (need > 0 && !aligned(workspace, 256)) return fail(SGLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (final_state != nullptr && initial_state != nullptr && final_state != initial_state) {
+    const size_t sb = (size_t)P.N * a.H * a.K * a.V * sizeof(float);
+    const char* f0 = reinterpret_cast<const char*>(final_state);
+    const char* i0 = reinterpret_cast<const char*>(initial_state);
+    if (f0 < i0 + sb && i0 < f0 + sb)
+      return fail(SGLA_ERR_INVALID_ARG, "final_state partially overlaps initial_state (only exact aliasing is allowed)");
+  }
+
+  char* ws = static_cast<char*>(workspace);
+  st = upload_tables(P, ws, stream);
+  if (st != SGLA_OK) return st;
+  const sgla::SeqLayout L = layout_of(args, P, ws);
+
+  float* gc = nullptr;
+  if (g != nullptr && any_tokens) {
+    gc = reinterpret_cast<float*>(ws);
+    hipError_t e = sgla::launch_gate_cumsum(g, gc, a.H, L, stream);
+    if (e != hipSuccess) return hip_fail(e, "launching the gate cumsum kernel");
+  }
+  sgla::ChunkFwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.gc = gc;
+  p.g_gamma = g_gamma;
+  p.h0 = initial_state;
+  p.o = o;
+  p.ht = a.output_final_state ? final_state : nullptr;
+  p.scale = a.scale;
+  p.H = a.H;
+  p.K = a.K;
+  p.V = a.V;
+  p.o_bf16 = a.o_dtype == SGLA_BF16;
+  p.seqs = L;
+  if (p.ht == nullptr && !any_tokens) return ok();
+  hipError_t e = a.qkv_dtype == SGLA_BF16 ? sgla::launch_chunk_fwd_bf16(p, stream)
+                                          : sgla::launch_chunk_fwd_f32(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "launching the chunk kernel");
+  return ok();
+}
+
+sgla_status sgla_chunk_local_cumsum(const sgla_chunk_args* args, const float* g, const int64_t* cu_seqlens_host,
+                                    float* gc, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Plan P;
+  sgla_status st = plan_shape(args, cu_seqlens_host, false, &P);
+  if (st != SGLA_OK) return st;
+  if (P.total_tokens > 0 && (g == nullptr || gc == nullptr))
+    return fail(SGLA_ERR_INVALID_ARG, "g and gc must be non-NULL");
+  if (P.packed && (workspace == nullptr || workspace_bytes < P.total_bytes))
+    return fail(SGLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", P.total_bytes, workspace_bytes);
+  char* ws = static_cast<char*>(workspace);
+  st = upload_tables(P, ws, stream);
+  if (st != SGLA_OK) return st;
+  const sgla::SeqLayout L = layout_of(args, P, ws);
+  hipError_t e = sgla::launch_gate_cumsum(g, gc, args->H, L, stream);
+  if (e != hipSuccess) return hip_fail(e, "launching the gate cumsum kernel");
+  return ok();
+}
+
+sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t K, int32_t V, float scale, int32_t qkv_dtype,
+                                int32_t o_dtype, const void* q, const void* k, const void* v, const float* g,
+                                float* state, void* o, hipStream_t stream) {
+  if (N < 0 || H <= 0) return fail(SGLA_ERR_SHAPE, "N must be >= 0 and H > 0 (got N=%d H=%d)", N, H);
+  if (K < 1 || K > 1024) return fail(SGLA_ERR_UNSUPPORTED, "decode supports 1 <= K <= 1024 (got %d)", K);
+  if (!(V == 32 || V == 64 || V == 128 || V == 256 || V == 512))
+    return fail(SGLA_ERR_UNSUPPORTED, "decode supports V in {32,64,128,256,512} (got %d)", V);
+  if (qkv_dtype != SGLA_BF16 && qkv_dtype != SGLA_F32)
+    return fail(SGLA_ERR_DTYPE, "qkv_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", qkv_dtype);
+  if (o_dtype != SGLA_BF16 && o_dtype != SGLA_F32)
+    return fail(SGLA_ERR_DTYPE, "o_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", o_dtype);
+  if (!std::isfinite(scale)) return fail(SGLA_ERR_INVALID_ARG, "scale must be finite");
+  if (N == 0) return ok();
+  if (q == nullptr || k == nullptr || v == nullptr || g == nullptr || state == nullptr || o == nullptr)
+    return fail(SGLA_ERR_INVALID_ARG, "q, k, v, g, state and o must be non-NULL");
+  if (!aligned(state, 16)) return fail(SGLA_ERR_INVALID_ARG, "state must be 16-byte aligned");
+  const size_t osz = (size_t)N * H * V * (o_dtype == SGLA_BF16 ? 2 : 4);
+  const size_t ssz = (size_t)N * H * K * V * sizeof(float);
+  const char* oc = static_cast<const char*>(o);
+  const char* sc = reinterpret_cast<const char*>(state);
+  if (oc < sc + ssz && sc < oc + osz) return fail(SGLA_ERR_INVALID_ARG, "o must not alias the state");
+  sgla::StepParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = g;
+  p.state = state;
+  p.o = o;
+  p.scale = scale;
+  p.N = N;
+  p.H = H;
+  p.K = K;
+  p.V = V;
+  p.qkv_bf16 = qkv_dtype == SGLA_BF16;
+  p.o_bf16 = o_dtype == SGLA_BF16;
+  hipError_t e = sgla::launch_recurrent_step(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "launching the decode kernel");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Internal launch interface between the C-ABI layer (sgla_api.cpp) and the
+// HIP kernels.  Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <hip/hip_runtime_api.h>
+
+namespace sgla {
+
+constexpr int kChunk = 64;        // tokens per chunk
+constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
+
+// Per-sequence entry of the packed-input table, sorted longest first.
+struct SeqEntry {
+  int32_t bos;   // first packed token of the sequence
+  int32_t len;   // tokens
+  int32_t seq;   // index into initial_state / final_state
+  int32_t pad;
+};
+
+// Per-chunk entry used by the gate kernel for packed input.
+struct ChunkEntry {
+  int32_t t0;    // first packed token of the chunk
+  int32_t len;   // tokens in the chunk (1..kChunk)
+};
+
+// Description of the token ranges a launch covers.  Dense input: seq_table ==
+// nullptr and every sequence b has bos = b * T, len = T.  Packed input: the
+// table lives in device memory (workspace).
+struct SeqLayout {
+  int32_t num_seqs;          // N
+  int32_t T;                 // dense: tokens per row
+  const SeqEntry* seq_table; // packed only (device)
+  const ChunkEntry* chunk_table; // packed only (device)
+  int32_t num_chunks;        // total chunks over all sequences
+};
+
+struct ChunkFwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* gc;           // chunk-local cumulative log2 gates [T_total, H], or nullptr
+  const float* g_gamma;      // [H] natural-log decay, or nullptr
+  const float* h0;           // [N, H, K, V] or nullptr
+  void* o;
+  float* ht;                 // [N, H, K, V] or nullptr
+  float scale;
+  int32_t H, K, V;
+  int32_t o_bf16;            // 1: o is bf16, 0: float32
+  SeqLayout seqs;
+};
+
+hipError_t launch_gate_cumsum(const float* g, float* gc, int32_t H, const SeqLayout& seqs,
+                              hipStream_t stream);
+
+// bf16 q/k/v, MFMA path.  K in {64,128,256,512}, V % 64 == 0.
+hipError_t launch_chunk_fwd_bf16(const ChunkFwdParams& p, hipStream_t stream);
+
+// float32 q/k/v, VALU path.  K in {16,32,64,128}, V % 32 == 0.
+hipError_t launch_chunk_fwd_f32(const ChunkFwdParams& p, hipStream_t stream);
+
+struct StepParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  float* state;
+  void* o;
+  float scale;
+  int32_t N, H, K, V;
+  int32_t qkv_bf16;
+  int32_t o_bf16;
+};
+
+// V in {32,64,128,256,512}, 1 <= K <= 1024.
+hipError_t launch_recurrent_step(const StepParams& p, hipStream_t stream);
+
+}  // namespace sgla

@@ -1,0 +1,164 @@
+/*
+ * sgla.h -- C ABI of libsgla, the gfx950 (MI355X) implementation of Simple GLA
+ * (head-wise gated linear attention).
+ *
+ * Operator (page "flash-linear-attention 中的 Simple GLA", section 一): per
+ * sequence and head, with a K x V state S,
+ *
+ *     S_t = exp(g_t) * S_{t-1} + k_t v_t^T,        o_t = scale * S_t^T q_t,
+ *
+ * where g_t is a scalar log gate per (token, head), or a per-head constant
+ * log decay g_gamma[h] (section 二).  The output uses the state after token t.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor arguments are DEVICE pointers to contiguous row-major memory
+ *     allocated and owned by the caller.  The library never allocates, frees,
+ *     retains a pointer past the call, or synchronizes the stream; all work
+ *     is enqueued on the caller's `stream`.
+ *   - Layouts follow section 二: q, k [B, T, H, K]; v, o [B, T, H, V];
+ *     g [B, T, H]; g_gamma [H]; states [N, H, K, V] with S[k][v] (key index
+ *     major).  Packed (varlen) input has B == 1 and N sequences given by
+ *     cu_seqlens[N + 1] (FlashAttention convention, section 二); dense input
+ *     has N == B.
+ *   - Gates, states and the state accumulation are float32.  q, k, v are all
+ *     bf16 or all float32 (SGLA_BF16 / SGLA_F32); o is float32 or bf16.
+ *   - Every argument check runs on the host before anything is enqueued.  On
+ *     a non-OK status nothing has been written to any output, to the state or
+ *     to the workspace, and sgla_last_error() describes the problem.  There is
+ *     no fallback: an unsupported shape or dtype is an error, never a slower
+ *     path.
+ *   - A kernel launch failure reported by the runtime is returned as
+ *     SGLA_ERR_HIP; asynchronous faults surface at the caller's next
+ *     synchronization, as for any HIP work.
+ */
+#ifndef SGLA_H
+#define SGLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGLA_ABI_VERSION 1
+
+typedef enum {
+  SGLA_OK = 0,
+  SGLA_ERR_INVALID_ARG = 1, /* NULL required pointer, both gates, bad scale, ... */
+  SGLA_ERR_SHAPE = 2,       /* inconsistent sizes, malformed cu_seqlens, B != 1 with cu_seqlens */
+  SGLA_ERR_DTYPE = 3,       /* dtype code not supported for this argument */
+  SGLA_ERR_UNSUPPORTED = 4, /* valid request outside what the kernels implement */
+  SGLA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than sgla_chunk_fwd_workspace_size */
+  SGLA_ERR_HIP = 6          /* the HIP runtime rejected a launch or copy */
+} sgla_status;
+
+typedef enum { SGLA_BF16 = 1, SGLA_F32 = 2 } sgla_dtype;
+
+typedef struct {
+  int32_t B, T, H, K, V;      /* packed input: B == 1 and T = total tokens */
+  int32_t num_seqs;           /* packed: number of sequences N; dense: ignored (N = B) */
+  int32_t chunk_size;         /* tokens per chunk; 0 selects 64; must be 64 (see below) */
+  int32_t qkv_dtype;          /* sgla_dtype of q, k and v */
+  int32_t o_dtype;            /* sgla_dtype of o */
+  float scale;                /* finite; callers wanting the default pass 1/sqrt(K) */
+  int32_t output_final_state; /* nonzero: write final_state */
+} sgla_chunk_args;
+
+/* ABI revision of the loaded library (SGLA_ABI_VERSION it was built with). */
+int sgla_abi_version(void);
+
+/* Message for the last non-OK status returned on the calling thread
+ * (thread-local; empty string if none).  Valid until the next call on the
+ * same thread. */
+const char *sgla_last_error(void);
+
+/*
+ * Bytes of device workspace sgla_chunk_fwd needs for these arguments (the
+ * chunk-local cumulative gates plus, for packed input, a per-sequence table).
+ * `cu_seqlens_host` is the same host array later passed to sgla_chunk_fwd, or
+ * NULL for dense input.  Returns 0 if the arguments are invalid (the reason is
+ * in sgla_last_error()); a valid call may also legitimately need 0 bytes only
+ * when there is no token to process.
+ */
+size_t sgla_chunk_fwd_workspace_size(const sgla_chunk_args *args, const int64_t *cu_seqlens_host);
+
+/*
+ * Chunked Simple GLA forward (prefill), section 三's three steps on gfx950:
+ *   (1) chunk-local cumulative sum of the log gates, pre-multiplied by 1/ln 2
+ *       so decays are evaluated with exp2;
+ *   (2) the inter-chunk state pass, h_{n+1} = 2^{b_last} h_n +
+ *       (K_n * 2^{b_last - b})^T V_n, kept in an fp32 K x V state on chip;
+ *   (3) the output pass, O_n = scale * [ (Q_n K_n^T (.) M_n) V_n +
+ *       diag(2^b) Q_n h_n ], M_ij = 2^{b_i - b_j} for j <= i, else 0.
+ * Steps (2) and (3) run fused in one kernel per (sequence, head, V tile).
+ *
+ * Arguments (device pointers unless stated):
+ *   q, k            [B, T, H, K] in qkv_dtype
+ *   v               [B, T, H, V] in qkv_dtype
+ *   g               [B, T, H] float32 log gates, or NULL
+ *   g_gamma         [H] float32 per-head log decay, or NULL.  At most one of
+ *                   g / g_gamma may be given (section 二); neither means no
+ *                   decay (plain causal linear attention).
+ *   initial_state   [N, H, K, V] float32, or NULL for zeros.
+ *   cu_seqlens_host HOST array [N + 1] of int64 token offsets for packed
+ *                   input (cu[0] == 0, non-decreasing, cu[N] == T), or NULL
+ *                   for dense input.  Sequences may have any length >= 0; a
+ *                   zero-length sequence passes its initial state through.
+ *   o               [B, T, H, V] output in o_dtype.
+ *   final_state     [N, H, K, V] float32, written when output_final_state is
+ *                   nonzero (may be NULL otherwise).  May alias initial_state
+ *                   exactly (in-place state update); no other aliasing.
+ *   workspace       device buffer of at least workspace_bytes >=
+ *                   sgla_chunk_fwd_workspace_size(args, cu_seqlens_host).
+ * Supported: K in {64, 128, 256, 512} and V a multiple of 64 (bf16 inputs);
+ * K in {16, 32, 64, 128} and V a multiple of 32 (float32 inputs);
+ * chunk_size 64.  Other powers of two are valid requests that return
+ * SGLA_ERR_UNSUPPORTED; a chunk_size that is not a power of two is
+ * SGLA_ERR_SHAPE (section 二 requires a power of two).
+ */
+sgla_status sgla_chunk_fwd(const sgla_chunk_args *args,
+                           const void *q, const void *k, const void *v,
+                           const float *g, const float *g_gamma,
+                           const float *initial_state,
+                           const int64_t *cu_seqlens_host,
+                           void *o, float *final_state,
+                           void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
+ * Step (1) alone: chunk-local inclusive cumulative sum of g times 1/ln 2,
+ * restarting at every chunk_size-token chunk of every sequence (section 三,
+ * the chunk_local_cumsum call with the RCP_LN2 scale).  g and gc are device
+ * [B, T, H] float32; cu_seqlens_host as for sgla_chunk_fwd.  `workspace`
+ * (device) must hold sgla_chunk_fwd_workspace_size(args, cu_seqlens_host)
+ * bytes when cu_seqlens_host is not NULL (it carries the sequence table) and
+ * may be NULL otherwise.  Only B, T, H, num_seqs and chunk_size of `args` are
+ * read.  Exposed for testing the step in isolation.
+ */
+sgla_status sgla_chunk_local_cumsum(const sgla_chunk_args *args, const float *g,
+                                    const int64_t *cu_seqlens_host, float *gc,
+                                    void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/*
+ * One decode step for N independent sequences x H heads (section 四: single
+ * tokens take the fused recurrent path instead of a chunk launch), in place:
+ *     S <- exp(g) * S + k v^T ;   o = scale * S^T q   (updated state)
+ *   q, k   [N, H, K] in qkv_dtype;  v [N, H, V] in qkv_dtype
+ *   g      [N, H] float32 log gate
+ *   state  [N, H, K, V] float32, read and written in place
+ *   o      [N, H, V] in o_dtype; must not alias any input
+ * Supported: K a multiple of 8 in [8, 512], V a multiple of 32 in [32, 512].
+ */
+sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t K, int32_t V, float scale,
+                                int32_t qkv_dtype, int32_t o_dtype,
+                                const void *q, const void *k, const void *v,
+                                const float *g, float *state, void *o,
+                                hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SGLA_H */

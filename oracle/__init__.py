@@ -42,6 +42,9 @@ def _bind(lib):
     lib.sgla_oracle_fwd.argtypes = [ctypes.c_int] * 5 + [dp] * 5 + [ctypes.c_double, dp, lp,
                                                                      ctypes.c_int, dp, dp,
                                                                      ctypes.c_int]
+    lib.sgla_oracle_chunk_local_cumsum.restype = ctypes.c_int
+    lib.sgla_oracle_chunk_local_cumsum.argtypes = [ctypes.c_int] * 3 + [dp, lp, ctypes.c_int,
+                                                                        ctypes.c_int, dp]
     lib.sgla_oracle_step.restype = ctypes.c_int
     lib.sgla_oracle_step.argtypes = [ctypes.c_int] * 4 + [dp] * 4 + [ctypes.c_double, dp, dp,
                                                                      ctypes.c_int]
@@ -130,3 +133,23 @@ def step(q, k, v, g, state, scale=None, nthreads=None, lib=None):
     if rc != 0:
         raise ValueError(f"sgla_oracle_step rejected its arguments (code {rc})")
     return o, S
+
+
+def chunk_local_cumsum(g, chunk_size=64, cu_seqlens=None, lib=None):
+    """Chunk-local inclusive cumulative sum of g [B, T, H], divided by ln 2,
+    restarting at every chunk of every sequence.  Returns float64 [B, T, H]."""
+    g = _f64(g)
+    B, T, H = g.shape
+    cu = None
+    N = B
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N = cu.shape[0] - 1
+    gc = np.zeros_like(g)
+    lib = lib or load()
+    rc = lib.sgla_oracle_chunk_local_cumsum(
+        B, T, H, _ptr(g), None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        N, int(chunk_size), _ptr(gc))
+    if rc != 0:
+        raise ValueError(f"sgla_oracle_chunk_local_cumsum rejected its arguments (code {rc})")
+    return gc

@@ -271,3 +271,35 @@ int sgla_oracle_step(int N, int H, int K, int V,
     pthread_mutex_destroy(&J.mu);
     return 0;
 }
+
+/*
+ * Chunk-local cumulative log gate, pre-scaled by 1/ln 2 (page "flash-linear-
+ * attention 中的 Simple GLA", section 三: the chunk_local_cumsum call with
+ * the RCP_LN2 scale, one scalar sequence per head).  For token t of a
+ * sequence that starts at bos, the chunk starts at
+ * c0 = bos + floor((t - bos) / chunk) * chunk and
+ *     gc[t][h] = (sum_{j = c0..t} g[j][h]) / ln 2.
+ *   g, gc : [B, T, H];  cu_seqlens as for sgla_oracle_fwd.
+ */
+int sgla_oracle_chunk_local_cumsum(int B, int T, int H, const double *g,
+                                   const int64_t *cu_seqlens, int num_seqs,
+                                   int chunk, double *gc)
+{
+    if (B < 0 || T < 0 || H <= 0 || chunk <= 0) return -1;
+    if (cu_seqlens && B != 1) return -3;
+    const int N = cu_seqlens ? num_seqs : B;
+    const double ln2 = log(2.0);
+    for (int n = 0; n < N; ++n) {
+        const int64_t bos = cu_seqlens ? cu_seqlens[n] : (int64_t)n * T;
+        const int64_t eos = cu_seqlens ? cu_seqlens[n + 1] : (int64_t)(n + 1) * T;
+        for (int h = 0; h < H; ++h) {
+            double run = 0.0;
+            for (int64_t t = bos; t < eos; ++t) {
+                if ((t - bos) % chunk == 0) run = 0.0;
+                run += g[(size_t)t * H + h];
+                gc[(size_t)t * H + h] = run / ln2;
+            }
+        }
+    }
+    return 0;
+}

@@ -1,0 +1,228 @@
+"""CPU tests of the C ABI boundary (no GPU needed).
+
+libsgla.so is loaded and checked to export every function include/sgla.h
+declares.  Argument validation runs on the host before anything is enqueued,
+so every error path can be exercised here: the calls below pass HOST buffers
+in place of device pointers and confirm both the status code and that not a
+byte of any buffer changed (section 二 of page "flash-linear-attention 中的
+Simple GLA": g xor g_gamma, B == 1 with cu_seqlens, one initial state per
+sequence, chunk_size a power of two; no silent fallback)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgla.h")
+
+OK, INVALID, SHAPE, DTYPE, UNSUPPORTED, WORKSPACE, HIP = range(7)
+BF16, F32 = 1, 2
+
+
+@pytest.fixture(scope="module")
+def G():
+    import gated_linear_attention_amd as G
+    return G
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sgla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("sgla_chunk_fwd", "sgla_recurrent_step", "sgla_chunk_fwd_workspace_size",
+              "sgla_chunk_local_cumsum", "sgla_last_error", "sgla_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(G):
+    out = subprocess.run(["nm", "-D", "--defined-only", G.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    for n in declared_functions():
+        assert hasattr(G.lib, n)
+
+
+def test_single_hip_runtime_in_process(G):
+    maps = open("/proc/self/maps").read()
+    libs = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(libs) == 1, libs
+
+
+def test_abi_version(G):
+    assert G.lib.sgla_abi_version() == G.ABI_VERSION == 1
+
+
+class Buffers:
+    """Host buffers standing in for device pointers; snapshot() / unchanged()
+    detect any write."""
+
+    def __init__(self, B=1, T=128, H=2, K=64, V=64, N=None):
+        N = B if N is None else N
+        rng = np.random.default_rng(0)
+        self.arrs = {}
+        for name, shape, dt in [("q", (B, T, H, K), np.uint16), ("k", (B, T, H, K), np.uint16),
+                                ("v", (B, T, H, V), np.uint16), ("g", (B, T, H), np.float32),
+                                ("gg", (H,), np.float32), ("h0", (N, H, K, V), np.float32),
+                                ("o", (B, T, H, V), np.float32), ("ht", (N, H, K, V), np.float32),
+                                ("ws", (1 << 20,), np.uint8)]:
+            n = int(np.prod(shape)) * np.dtype(dt).itemsize
+            raw = rng.integers(0, 255, size=n + 256, dtype=np.uint8)
+            off = (-raw.ctypes.data) % 256          # 256-byte aligned view, like device memory
+            self.arrs[name] = raw[off:off + n]
+        self.snap = {k: a.copy() for k, a in self.arrs.items()}
+
+    def p(self, name, offset=0):
+        return ctypes.c_void_p(self.arrs[name].ctypes.data + offset)
+
+    def unchanged(self):
+        return all(np.array_equal(self.arrs[k], self.snap[k]) for k in self.arrs)
+
+
+def chunk_call(G, args, b, cu=None, g=True, gg=False, h0=True, ht=True, ws_bytes=1 << 20,
+               ht_ptr=None, **ptr_override):
+    cu_arr = None if cu is None else np.asarray(cu, dtype=np.int64)
+    ptrs = dict(q=b.p("q"), k=b.p("k"), v=b.p("v"), g=b.p("g") if g else None,
+                gg=b.p("gg") if gg else None, h0=b.p("h0") if h0 else None,
+                o=b.p("o"), ht=b.p("ht") if ht else None, ws=b.p("ws"))
+    ptrs.update(ptr_override)
+    if ht_ptr is not None:
+        ptrs["ht"] = ht_ptr
+    st = G.lib.sgla_chunk_fwd(
+        None if args is None else ctypes.byref(args), ptrs["q"], ptrs["k"], ptrs["v"], ptrs["g"],
+        ptrs["gg"], ptrs["h0"],
+        None if cu_arr is None else ctypes.c_void_p(cu_arr.ctypes.data),
+        ptrs["o"], ptrs["ht"], ptrs["ws"], ws_bytes, None)
+    return st, G.lib.sgla_last_error().decode()
+
+
+def mkargs(G, B=1, T=128, H=2, K=64, V=64, N=1, chunk=64, qkv=BF16, od=F32, scale=0.125, fs=1):
+    return G._ChunkArgs(B, T, H, K, V, N, chunk, qkv, od, scale, fs)
+
+
+CASES = [
+    # (description, args overrides, call overrides, expected status, message fragment)
+    ("null args", None, {}, INVALID, "args"),
+    ("both gates", {}, dict(gg=True), INVALID, "mutually exclusive"),
+    ("B != 1 with cu_seqlens", dict(B=2, N=2), dict(cu=[0, 64, 128]), SHAPE, "B == 1"),
+    ("cu not from 0", dict(N=2), dict(cu=[1, 64, 128]), SHAPE, "cu_seqlens[0]"),
+    ("cu decreasing", dict(N=2), dict(cu=[0, 100, 90]), SHAPE, "non-decreasing"),
+    ("cu not ending at T", dict(N=2), dict(cu=[0, 64, 127]), SHAPE, "equal T"),
+    ("chunk not power of 2", dict(chunk=48), {}, SHAPE, "power of two"),
+    ("chunk 32 unsupported", dict(chunk=32), {}, UNSUPPORTED, "chunk_size"),
+    ("bf16 K=96", dict(K=96), {}, UNSUPPORTED, "K in"),
+    ("bf16 V=96", dict(V=96), {}, UNSUPPORTED, "V a multiple"),
+    ("f32 K=256", dict(qkv=F32, K=256), {}, UNSUPPORTED, "K in"),
+    ("f32 V=48", dict(qkv=F32, V=48), {}, UNSUPPORTED, "V a multiple"),
+    ("fp16 inputs", dict(qkv=3), {}, DTYPE, "qkv_dtype"),
+    ("bad o dtype", dict(od=0), {}, DTYPE, "o_dtype"),
+    ("nan scale", dict(scale=float("nan")), {}, INVALID, "scale"),
+    ("inf scale", dict(scale=float("inf")), {}, INVALID, "scale"),
+    ("H = 0", dict(H=0), {}, SHAPE, "H must"),
+    ("negative T", dict(T=-1), {}, SHAPE, ">= 0"),
+    ("NULL q", {}, dict(q=None), INVALID, "non-NULL"),
+    ("final requested, NULL", {}, dict(ht=False), INVALID, "final_state is NULL"),
+    ("workspace small", {}, dict(ws_bytes=16), WORKSPACE, "workspace"),
+    ("workspace NULL", {}, dict(ws=None), WORKSPACE, "workspace"),
+    ("misaligned q", {}, dict(q="misaligned"), INVALID, "aligned"),
+    ("partial state overlap", {}, dict(ht="overlap"), INVALID, "overlap"),
+    ("num_seqs 0 with cu", dict(N=0), dict(cu=[0]), SHAPE, "num_seqs"),
+]
+
+
+@pytest.mark.parametrize("desc,aover,cover,status,frag", CASES, ids=[c[0] for c in CASES])
+def test_chunk_fwd_rejects_without_writing(G, desc, aover, cover, status, frag):
+    b = Buffers()
+    args = None if aover is None else mkargs(G, **aover)
+    cover = dict(cover)
+    kw = {}
+    if cover.pop("gg", False):
+        kw["gg"] = True
+    if "ht" in cover and cover["ht"] is False:
+        kw["ht"] = False
+        cover.pop("ht")
+    if cover.get("q") == "misaligned":
+        cover["q"] = b.p("q", 2)
+    if cover.get("ht") == "overlap":
+        cover.pop("ht")
+        kw["ht_ptr"] = b.p("h0", 256)
+    for key in ("cu", "ws_bytes"):
+        if key in cover:
+            kw[key] = cover.pop(key)
+    st, msg = chunk_call(G, args, b, **kw, **cover)
+    assert st == status, (st, msg)
+    assert frag in msg, msg
+    assert b.unchanged()
+
+
+def test_workspace_size(G):
+    a = mkargs(G, B=2, T=100, H=3)
+    n = G.lib.sgla_chunk_fwd_workspace_size(ctypes.byref(a), None)
+    assert n >= 2 * 100 * 3 * 4 and n % 256 == 0
+    cu = np.array([0, 15, 100, 300], dtype=np.int64)
+    a = mkargs(G, B=1, T=300, H=3, N=3)
+    n2 = G.lib.sgla_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.c_void_p(cu.ctypes.data))
+    assert n2 >= 300 * 3 * 4 + 3 * 16 + 6 * 8
+    bad = mkargs(G, K=96)
+    assert G.lib.sgla_chunk_fwd_workspace_size(ctypes.byref(bad), None) == 0
+    assert "K in" in G.lib.sgla_last_error().decode()
+
+
+STEP_CASES = [
+    ("V=48", dict(V=48), UNSUPPORTED, "V in"),
+    ("K=0", dict(K=0), UNSUPPORTED, "K <="),
+    ("K=2048", dict(K=2048), UNSUPPORTED, "K <="),
+    ("H=0", dict(H=0), SHAPE, "H > 0"),
+    ("fp16", dict(qkv=3), DTYPE, "qkv_dtype"),
+    ("o dtype", dict(od=9), DTYPE, "o_dtype"),
+    ("nan scale", dict(scale=float("nan")), INVALID, "scale"),
+    ("null g", dict(g=None), INVALID, "non-NULL"),
+    ("o aliases state", dict(o="state"), INVALID, "alias"),
+    ("misaligned state", dict(state="misaligned"), INVALID, "aligned"),
+]
+
+
+@pytest.mark.parametrize("desc,over,status,frag", STEP_CASES, ids=[c[0] for c in STEP_CASES])
+def test_recurrent_step_rejects_without_writing(G, desc, over, status, frag):
+    b = Buffers(B=1, T=4, H=2, K=64, V=64, N=4)
+    kw = dict(N=4, H=2, K=64, V=64, scale=0.125, qkv=BF16, od=F32, q=b.p("q"), k=b.p("k"),
+              v=b.p("v"), g=b.p("g"), state=b.p("h0"), o=b.p("o"))
+    for key, val in over.items():
+        if val == "state":
+            val = b.p("h0", 64)
+        elif val == "misaligned":
+            val = b.p("h0", 4)
+        kw[key] = val
+    st = G.lib.sgla_recurrent_step(kw["N"], kw["H"], kw["K"], kw["V"], kw["scale"], kw["qkv"],
+                                   kw["od"], kw["q"], kw["k"], kw["v"], kw["g"], kw["state"],
+                                   kw["o"], None)
+    msg = G.lib.sgla_last_error().decode()
+    assert st == status, (st, msg)
+    assert frag in msg, msg
+    assert b.unchanged()
+
+
+def test_binding_checks_initial_state_rows(G):
+    """initial_state must have one row per sequence (len(cu_seqlens) - 1)."""
+    import torch
+    q = torch.zeros(1, 10, 2, 64, dtype=torch.bfloat16)
+    v = torch.zeros(1, 10, 2, 64, dtype=torch.bfloat16)
+    h0 = torch.zeros(3, 2, 64, 64)
+    with pytest.raises(ValueError, match="initial_state"):
+        G.chunk_fwd(q, q, v, initial_state=h0, cu_seqlens=[0, 4, 10])
+    with pytest.raises(ValueError, match="B == 1"):
+        G.chunk_fwd(torch.zeros(2, 5, 2, 64, dtype=torch.bfloat16),
+                    torch.zeros(2, 5, 2, 64, dtype=torch.bfloat16),
+                    torch.zeros(2, 5, 2, 64, dtype=torch.bfloat16), cu_seqlens=[0, 4, 10])
+    with pytest.raises(ValueError, match="mutually exclusive"):
+        G.chunk_fwd(q, q, v, g=torch.zeros(1, 10, 2), g_gamma=torch.zeros(2))
+    with pytest.raises(ValueError, match="float16|bfloat16"):
+        G.chunk_fwd(q.half(), q.half(), v.half())

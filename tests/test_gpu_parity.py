@@ -1,0 +1,358 @@
+"""GPU parity: libsgla's HIP kernels against the fp64 CPU oracle.
+
+Every test calls the C ABI through the thin ctypes binding and compares with
+the oracle on the same seeded inputs.  The bar (one number per output
+tensor): max |gpu - oracle| / RMS(oracle) <= 2e-2 for bf16 inputs and 1e-4
+for float32 inputs.  Small cases compare every element; the full-size named
+workloads run the whole launch (as the benchmark does) and compare every
+output of a sample of (sequence, head) units, which the oracle computes one
+by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gla_workloads import (CHUNK_CONFIGS, DECODE_CONFIGS, ChunkWorkload, DecodeWorkload,
+                           make_chunk_inputs, make_decode_inputs)
+from gpu_common import (DEV, TOL_BF16, TOL_F32, device_inputs, err_ratio, gpu_unit_slices,
+                        oracle_units, to_dev)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+if torch.cuda.is_available():
+    import gated_linear_attention_amd as sgla
+else:  # pragma: no cover - collected on CPU-only hosts, never run
+    sgla = None
+
+
+def _tol(dtype):
+    return TOL_BF16 if dtype == "bf16" else TOL_F32
+
+
+def run_chunk(inp, o_dtype=torch.float32, output_final_state=None):
+    d = device_inputs(inp)
+    ofs = inp["output_final_state"] if output_final_state is None else output_final_state
+    o, ht = sgla.chunk_fwd(d["q"], d["k"], d["v"], g=d["g"], g_gamma=d["g_gamma"],
+                           scale=inp["scale"], initial_state=d["initial_state"],
+                           output_final_state=ofs, cu_seqlens=inp["cu_seqlens"],
+                           chunk_size=inp["chunk_size"], o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), (None if ht is None else ht.cpu().numpy())
+
+
+def check_full(inp, o_gpu, ht_gpu):
+    o_ref, ht_ref = oracle.fwd(inp["q"], inp["k"], inp["v"], g=inp["g"], g_gamma=inp["g_gamma"],
+                               scale=inp["scale"], initial_state=inp["initial_state"],
+                               cu_seqlens=inp["cu_seqlens"])
+    tol = _tol(inp["dtype"])
+    eo = err_ratio(o_gpu, o_ref)
+    assert np.all(np.isfinite(o_gpu))
+    assert eo <= tol, f"o: max err / RMS = {eo:.3e} > {tol}"
+    if ht_gpu is not None:
+        eh = err_ratio(ht_gpu, ht_ref)
+        assert eh <= tol, f"final_state: max err / RMS = {eh:.3e} > {tol}"
+    return o_ref, ht_ref
+
+
+def small(name, **kw):
+    base = dict(B=2, T=200, H=3, K=64, V=64, dtype="bf16", gate="g", seed=7)
+    base.update(kw)
+    return ChunkWorkload(name, **base)
+
+
+# ---------------------------------------------------------------------------
+# step (1): chunk-local cumulative gate
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cu", [None, [0, 15, 100, 300, 1200, 2000], [0, 0, 1, 65, 65, 200]])
+def test_gate_cumsum(cu):
+    rng = np.random.default_rng(3)
+    if cu is None:
+        g = (-np.abs(rng.standard_normal((3, 333, 5)))).astype(np.float32)
+    else:
+        g = (-np.abs(rng.standard_normal((1, cu[-1], 5)))).astype(np.float32)
+    gc = sgla.chunk_local_cumsum(to_dev(g, torch.float32), chunk_size=64, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    ref = oracle.chunk_local_cumsum(g, chunk_size=64, cu_seqlens=cu)
+    got = gc.cpu().numpy().astype(np.float64)
+    # one float32 rounding of a float64 sum
+    assert np.all(np.abs(got - ref) <= 1e-6 * np.maximum(1.0, np.abs(ref)))
+
+
+# ---------------------------------------------------------------------------
+# steps (2)+(3): chunked forward, small cases compared element by element
+# ---------------------------------------------------------------------------
+
+SMALL_CASES = [
+    small("ragged_k64", T=200),
+    small("ragged_k128_v128", K=128, V=128, T=131),
+    small("k256_v64", K=256, V=64, T=150, H=2),
+    small("k512_v128", K=512, V=128, T=140, B=1, H=2),
+    small("v192_multi_tile", K=64, V=192, T=97),
+    small("gamma", gate="gamma", K=128, V=128, T=300, normalize_k=True),
+    small("no_gate", gate="none", K=64, V=64, T=129),
+    small("h0", initial_state=True, K=128, V=64, T=77),
+    small("norm0.1_scale0.1", gate_normalizer=0.1, scale=0.1, T=190),
+    small("norm10_scale1", gate_normalizer=10.0, scale=1.0, T=190),
+    small("t1", T=1, initial_state=True),
+    small("t63", T=63),
+    small("t64", T=64),
+    small("t65", T=65, initial_state=True),
+    small("empty_T0", T=0, initial_state=True),
+    small("varlen_fla", B=1, T=0, H=2, K=128, V=128, fixed_lengths=(15, 85, 200, 900, 800),
+          initial_state=True),
+    small("varlen_zero_len", B=1, T=0, H=2, K=64, V=64, fixed_lengths=(0, 1, 64, 0, 65, 130),
+          initial_state=True),
+    small("f32_k16_v32", dtype="f32", K=16, V=32, T=150),
+    small("f32_k32_v96", dtype="f32", K=32, V=96, T=70, initial_state=True),
+    small("f32_k128_v64", dtype="f32", K=128, V=64, T=130, gate="gamma"),
+    small("f32_varlen", dtype="f32", B=1, T=0, K=64, V=64, fixed_lengths=(15, 85, 200),
+          initial_state=True),
+]
+
+
+@pytest.mark.parametrize("w", SMALL_CASES, ids=lambda w: w.name)
+def test_chunk_small(w):
+    inp = make_chunk_inputs(w)
+    o, ht = run_chunk(inp)
+    check_full(inp, o, ht)
+
+
+def test_chunk_bf16_output():
+    """A bf16 o is the fp32 result rounded once: its error is bounded by the
+    fp32 tolerance plus half a bf16 ulp of each element."""
+    inp = make_chunk_inputs(small("bf16o", K=128, V=128, T=257))
+    o, _ = run_chunk(inp, o_dtype=torch.bfloat16)
+    o_ref, _ = oracle.fwd(inp["q"], inp["k"], inp["v"], g=inp["g"], scale=inp["scale"])
+    rms = np.sqrt(np.mean(o_ref ** 2))
+    bound = TOL_BF16 * rms + 2.0 ** -8 * np.abs(o_ref)
+    assert np.all(np.abs(o - o_ref) <= bound)
+
+
+# ---------------------------------------------------------------------------
+# the named workloads at full size (sampled units)
+# ---------------------------------------------------------------------------
+
+def _sample_units(N, H, n_units, seed, must=()):
+    rng = np.random.default_rng(seed)
+    units = set(must)
+    while len(units) < min(n_units, N * H):
+        units.add((int(rng.integers(N)), int(rng.integers(H))))
+    return sorted(units)
+
+
+def test_tiny_f32_full():
+    inp = make_chunk_inputs(CHUNK_CONFIGS["tiny_f32"])
+    o, ht = run_chunk(inp)
+    check_full(inp, o, ht)
+
+
+@pytest.mark.parametrize("cfg", ["dense_bf16_k512", "varlen_bf16_k128", "long_gamma_k128"])
+def test_named_workload_sampled(cfg):
+    w = CHUNK_CONFIGS[cfg]
+    inp = make_chunk_inputs(w)
+    print(f"[{cfg}] B={inp['B']} T={inp['T']} H={inp['H']} K={inp['K']} V={inp['V']} "
+          f"N={inp['N']}", flush=True)
+    o, ht = run_chunk(inp)
+    assert np.all(np.isfinite(o))
+    N, H = inp["N"], inp["H"]
+    must = [(0, 0), (N - 1, H - 1)]
+    if inp["cu_seqlens"] is not None:
+        lens = np.diff(inp["cu_seqlens"])
+        must += [(int(np.argmax(lens)), 1), (int(np.argmin(lens)), H // 2)]
+    units = _sample_units(N, H, 6, seed=5, must=must)
+    ref = oracle_units(inp, units)
+    xo, ro, xh, rh = gpu_unit_slices(o, ht, ref)
+    eo, eh = err_ratio(xo, ro), err_ratio(xh, rh)
+    print(f"[{cfg}] o err/RMS={eo:.3e} final err/RMS={eh:.3e}", flush=True)
+    assert eo <= TOL_BF16 and eh <= TOL_BF16
+
+
+# ---------------------------------------------------------------------------
+# cross-path properties
+# ---------------------------------------------------------------------------
+
+def test_varlen_equals_per_sequence_bitwise():
+    """Packed sequences give exactly the per-sequence results (each sequence
+    is processed by the same code from its own start)."""
+    w = small("pack", B=1, T=0, H=2, K=128, V=128, fixed_lengths=(100, 64, 257, 1),
+              initial_state=True)
+    inp = make_chunk_inputs(w)
+    o, ht = run_chunk(inp)
+    cu = inp["cu_seqlens"]
+    for n in range(len(cu) - 1):
+        s, e = int(cu[n]), int(cu[n + 1])
+        sub = dict(inp)
+        for key in ("q", "k", "v", "g"):
+            sub[key] = inp[key][:, s:e].copy()
+        sub["initial_state"] = inp["initial_state"][n:n + 1].copy()
+        sub["cu_seqlens"] = None
+        on, hn = run_chunk(sub)
+        assert np.array_equal(on[0], o[0, s:e])
+        assert np.array_equal(hn[0], ht[n])
+
+
+def test_split_at_chunk_boundary_bitwise():
+    """Running tokens [0, 128) then [128, T) from the carried state equals one
+    pass exactly (the split falls on a chunk boundary)."""
+    inp = make_chunk_inputs(small("split", B=1, T=300, H=2, K=128, V=64, initial_state=True))
+    o, ht = run_chunk(inp)
+    a, b = dict(inp), dict(inp)
+    for key in ("q", "k", "v", "g"):
+        a[key] = inp[key][:, :128].copy()
+        b[key] = inp[key][:, 128:].copy()
+    oa, ha = run_chunk(a)
+    b["initial_state"] = ha
+    ob, hb = run_chunk(b)
+    assert np.array_equal(np.concatenate([oa, ob], axis=1), o)
+    assert np.array_equal(hb, ht)
+
+
+def test_deterministic():
+    inp = make_chunk_inputs(small("det", K=128, V=128, T=333, initial_state=True))
+    o1, h1 = run_chunk(inp)
+    o2, h2 = run_chunk(inp)
+    assert np.array_equal(o1, o2) and np.array_equal(h1, h2)
+
+
+def test_in_place_state():
+    """final_state may alias initial_state exactly."""
+    inp = make_chunk_inputs(small("inplace", K=64, V=64, T=100, initial_state=True))
+    d = device_inputs(inp)
+    o_ref, h_ref = run_chunk(inp)
+    state = d["initial_state"]
+    args = sgla._chunk_args(inp["B"], inp["T"], inp["H"], inp["K"], inp["V"], inp["N"], 64,
+                            1, 2, inp["scale"], 1)
+    ws_n = sgla._workspace_size(args, None)
+    ws = torch.empty(max(ws_n, 1), device=DEV, dtype=torch.uint8)
+    o = torch.empty((inp["B"], inp["T"], inp["H"], inp["V"]), device=DEV, dtype=torch.float32)
+    st = sgla.lib.sgla_chunk_fwd(
+        __import__("ctypes").byref(args), sgla._ptr(d["q"]), sgla._ptr(d["k"]), sgla._ptr(d["v"]),
+        sgla._ptr(d["g"]), None, sgla._ptr(state), None, sgla._ptr(o), sgla._ptr(state),
+        sgla._ptr(ws), ws_n, sgla._stream(DEV))
+    assert st == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(o.cpu().numpy(), o_ref)
+    assert np.array_equal(state.cpu().numpy(), h_ref)
+
+
+def test_prefill_then_decode():
+    """A chunked prefill of T tokens and T decode steps from the same initial
+    state agree (both within tolerance of the oracle and of each other)."""
+    w = small("pd", B=3, T=70, H=2, K=128, V=128, initial_state=True)
+    inp = make_chunk_inputs(w)
+    o_chunk, ht_chunk = run_chunk(inp)
+    d = device_inputs(inp)
+    state = d["initial_state"].clone()
+    outs = []
+    for t in range(inp["T"]):
+        ot = sgla.recurrent_step(d["q"][:, t].contiguous(), d["k"][:, t].contiguous(),
+                                 d["v"][:, t].contiguous(), d["g"][:, t].contiguous(), state,
+                                 scale=inp["scale"])
+        outs.append(ot)
+    torch.cuda.synchronize()
+    o_dec = torch.stack(outs, dim=1).cpu().numpy()
+    o_ref, ht_ref = check_full(inp, o_chunk, ht_chunk)
+    assert err_ratio(o_dec, o_ref) <= TOL_BF16
+    assert err_ratio(state.cpu().numpy(), ht_ref) <= TOL_BF16
+    assert err_ratio(o_dec, o_chunk) <= TOL_BF16
+
+
+def test_chunk_then_decode_handoff():
+    """The state a prefill leaves behind drives decode exactly like the
+    oracle's state (the [N, H, K, V] layout is shared by both entry points)."""
+    inp = make_chunk_inputs(small("handoff", B=2, T=130, H=2, K=64, V=64))
+    _, ht = run_chunk(inp, output_final_state=True)
+    rng = np.random.default_rng(9)
+    q, k = [rng.standard_normal((2, 2, 64)).astype(np.float32) for _ in range(2)]
+    v = rng.standard_normal((2, 2, 64)).astype(np.float32)
+    g = -np.abs(rng.standard_normal((2, 2))).astype(np.float32)
+    state = torch.from_numpy(ht).to(DEV)
+    o = sgla.recurrent_step(to_dev(q, torch.float32), to_dev(k, torch.float32),
+                            to_dev(v, torch.float32), to_dev(g, torch.float32), state)
+    torch.cuda.synchronize()
+    _, ht_ref = oracle.fwd(inp["q"], inp["k"], inp["v"], g=inp["g"], scale=inp["scale"])
+    o_ref, s_ref = oracle.step(q, k, v, g, ht_ref)
+    assert err_ratio(o.cpu().numpy(), o_ref) <= TOL_BF16
+    assert err_ratio(state.cpu().numpy(), s_ref) <= TOL_BF16
+
+
+# ---------------------------------------------------------------------------
+# step (4): decode
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("K,V", [(8, 32), (64, 64), (100, 128), (128, 128), (128, 256),
+                                 (64, 512)])
+def test_decode_small(dtype, K, V):
+    w = DecodeWorkload("small", N=3, H=5, K=K, V=V, steps=3, dtype=dtype, seed=K + V)
+    inp = make_decode_inputs(w)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    state = to_dev(inp["state"], torch.float32)
+    S_ref = inp["state"].astype(np.float64)
+    for s in range(inp["steps"]):
+        o = sgla.recurrent_step(to_dev(inp["q"][s], dt), to_dev(inp["k"][s], dt),
+                                to_dev(inp["v"][s], dt), to_dev(inp["g"][s], torch.float32),
+                                state, scale=inp["scale"])
+        o_ref, S_ref = oracle.step(inp["q"][s], inp["k"][s], inp["v"][s], inp["g"][s], S_ref,
+                                   scale=inp["scale"])
+        torch.cuda.synchronize()
+        assert err_ratio(o.cpu().numpy(), o_ref) <= TOL_F32
+    assert err_ratio(state.cpu().numpy(), S_ref) <= TOL_F32
+
+
+def test_decode_named_workload_sampled():
+    """256 sequences x 32 heads, 64 in-place steps; every step's o and the final
+    state are compared on a sample of (sequence, head) units."""
+    w = DECODE_CONFIGS["decode_n256_h32_k128"]
+    inp = make_decode_inputs(w)
+    N, H = inp["N"], inp["H"]
+    units = _sample_units(N, H, 48, seed=11, must=[(0, 0), (N - 1, H - 1)])
+    ns = np.array([u[0] for u in units])
+    hs = np.array([u[1] for u in units])
+    state = to_dev(inp["state"], torch.float32)
+    S_ref = inp["state"][ns, hs][:, None].astype(np.float64)   # [U, 1, K, V]
+    worst = 0.0
+    for s in range(inp["steps"]):
+        o = sgla.recurrent_step(to_dev(inp["q"][s], torch.bfloat16),
+                                to_dev(inp["k"][s], torch.bfloat16),
+                                to_dev(inp["v"][s], torch.bfloat16),
+                                to_dev(inp["g"][s], torch.float32), state, scale=inp["scale"])
+        o_ref, S_ref = oracle.step(inp["q"][s][ns, hs][:, None], inp["k"][s][ns, hs][:, None],
+                                   inp["v"][s][ns, hs][:, None], inp["g"][s][ns, hs][:, None],
+                                   S_ref, scale=inp["scale"])
+        got = o[torch.from_numpy(ns).to(DEV), torch.from_numpy(hs).to(DEV)].cpu().numpy()
+        worst = max(worst, err_ratio(got, o_ref[:, 0]))
+    torch.cuda.synchronize()
+    st = state[torch.from_numpy(ns).to(DEV), torch.from_numpy(hs).to(DEV)].cpu().numpy()
+    es = err_ratio(st, S_ref[:, 0])
+    print(f"[decode] worst step o err/RMS={worst:.3e} state err/RMS={es:.3e}", flush=True)
+    assert worst <= TOL_BF16 and es <= TOL_BF16
+
+
+# ---------------------------------------------------------------------------
+# errors surface as exceptions and leave outputs untouched
+# ---------------------------------------------------------------------------
+
+def test_errors_leave_outputs_untouched():
+    inp = make_chunk_inputs(small("err", K=64, V=64, T=64))
+    d = device_inputs(inp)
+    out = torch.full((inp["B"], inp["T"], inp["H"], inp["V"]), 7.0, device=DEV)
+    with pytest.raises(ValueError, match="chunk_size"):
+        sgla.chunk_fwd(d["q"], d["k"], d["v"], g=d["g"], chunk_size=32, out=out)
+    with pytest.raises(ValueError):
+        sgla.chunk_fwd(d["q"], d["k"], d["v"], g=d["g"], g_gamma=torch.zeros(3, device=DEV),
+                       out=out)
+    with pytest.raises(ValueError, match="chunk_size"):
+        sgla.chunk_fwd(d["q"], d["k"], d["v"], g=d["g"], chunk_size=48, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+    state = torch.full((2, 2, 64, 64), 3.0, device=DEV)
+    with pytest.raises(ValueError):
+        sgla.recurrent_step(torch.zeros(2, 2, 64, device=DEV), torch.zeros(2, 2, 64, device=DEV),
+                            torch.zeros(2, 2, 48, device=DEV), torch.zeros(2, 2, device=DEV),
+                            torch.zeros(2, 2, 64, 48, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.all(state == 3.0)

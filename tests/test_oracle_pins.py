@@ -294,7 +294,32 @@ def pin_step_brute_force(lib, seed=9, N=2, H=3, K=3, V=2):
     return True
 
 
-ALL_PINS = [pin_hand_example, pin_brute_force, pin_zero_gate, pin_full_forget,
+def pin_chunk_local_cumsum(lib, seed=10, H=3):
+    """Gate prep: with g = ln 2 everywhere the scaled chunk-local sum counts
+    tokens since the chunk start (1, 2, ..., restarting at every chunk and every
+    sequence); for random gates 2^gc equals the product of exp(g_j) over the
+    chunk prefix."""
+    cu = np.array([0, 15, 100, 300, 301, 301, 420], dtype=np.int64)
+    T = int(cu[-1])
+    gc = oracle.chunk_local_cumsum(np.full((1, T, H), np.log(2.0)), chunk_size=32,
+                                   cu_seqlens=cu, lib=lib)
+    for n in range(len(cu) - 1):
+        for t in range(cu[n], cu[n + 1]):
+            if abs(gc[0, t, 0] - ((t - cu[n]) % 32 + 1)) > 1e-12:
+                return False
+    rng = np.random.default_rng(seed)
+    g = logsigmoid(_rand(rng, 2, 130, H))
+    gc = oracle.chunk_local_cumsum(g, chunk_size=64, lib=lib)
+    for b in range(2):
+        for t in range(130):
+            c0 = (t // 64) * 64
+            prod = np.prod(np.exp(g[b, c0:t + 1]), axis=0)
+            if np.max(np.abs(np.exp2(gc[b, t]) - prod) / prod) > 1e-12:
+                return False
+    return True
+
+
+ALL_PINS = [pin_chunk_local_cumsum, pin_hand_example, pin_brute_force, pin_zero_gate, pin_full_forget,
             pin_split_sequence, pin_varlen_equals_per_sequence, pin_chunk_form,
             pin_gamma_is_broadcast_g, pin_retnet_closed_form, pin_invariants,
             pin_prefill_then_decode, pin_step_brute_force]
