@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""Benchmark of the Simple GLA hot path on one MI355X.
+
+A step is one pass of the whole chunked forward (chunk-local gate cumsum,
+inter-chunk state pass and output pass -- one fused kernel launch) over one
+batch of the dense bf16 prefill workload: B=4, T=2048, H=4, K=V=512, q/k/v
+~ N(0,1) in bf16, g = logsigmoid(N(0,1)), scale 1/sqrt(K), chunk 64, fp32 o,
+final state written.  ``value`` is tokens/s over the K timed steps with all
+inputs already resident in HBM (three input/output copies are rotated so the
+256 MB last-level cache cannot hold a step's working set).
+
+The JSON line also carries:
+  roofline      -- the fused chunk kernel against its bound (HBM for this
+                   workload), from algorithmic bytes per launch and the
+                   kernel's average duration measured with HIP events on the
+                   stream it runs on; ``traffic`` comes from a committed
+                   rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it matches the
+                   current kernel sources, else null;
+  mfma          -- the same launch's algorithmic FLOPs against the bf16 dense
+                   MFMA peak;
+  decode        -- the in-place decode step on 256 sequences x 32 heads x
+                   128 x 128 fp32 state, 64 consecutive steps, HBM GB/s;
+  cpu_baseline  -- the fp64 CPU oracle timed on the host cores on one full
+                   batch of the same workload (a reported baseline only).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+MALL_BYTES = 256 << 20
+METRIC = "chunked Simple-GLA fwd tokens/s + % bf16 MFMA peak; decode HBM GB/s"
+
+
+def kernel_source_hash() -> str:
+    d = os.path.join(ROOT, "gated_linear_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def chunk_algorithmic(inp) -> tuple[float, float]:
+    """(bytes, flops) one launch must move / perform at minimum.
+
+    bytes: q, k, v read once, g read once (if given), initial state read once
+    (if given), o written once, final state written once.  flops per chunk of
+    L tokens and head: L(L+1)(K+V) for the causal q k^T and A v products plus
+    4 L K V for q h and the state update."""
+    B, T, H, K, V = inp["B"], inp["T"], inp["H"], inp["K"], inp["V"]
+    esz = 2 if inp["dtype"] == "bf16" else 4
+    N = inp["N"]
+    tokens = B * T
+    nbytes = tokens * H * (2 * K + V) * esz + tokens * H * 4 * V
+    if inp["g"] is not None:
+        nbytes += tokens * H * 4
+    if inp["initial_state"] is not None:
+        nbytes += N * H * K * V * 4
+    if inp["output_final_state"]:
+        nbytes += N * H * K * V * 4
+    if inp["cu_seqlens"] is not None:
+        lens = [int(x) for x in (inp["cu_seqlens"][1:] - inp["cu_seqlens"][:-1])]
+    else:
+        lens = [T] * B
+    flops = 0
+    for L in lens:
+        for s in range(0, L, 64):
+            c = min(64, L - s)
+            flops += c * (c + 1) * (K + V) + 4 * c * K * V
+    flops *= H
+    return float(nbytes), float(flops)
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def bench_chunk(workload: str, steps: int, warmup: int):
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import gated_linear_attention_amd as sgla
+    from gla_workloads import CHUNK_CONFIGS, make_chunk_inputs
+
+    w = CHUNK_CONFIGS[workload]
+    inp = make_chunk_inputs(w)
+    dev = torch.device("cuda:0")
+    qdt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+    B, T, H, K, V, N = inp["B"], inp["T"], inp["H"], inp["K"], inp["V"], inp["N"]
+    alg_bytes, alg_flops = chunk_algorithmic(inp)
+    ncopies = max(1, min(4, math.ceil(2 * MALL_BYTES / alg_bytes) + 1))
+    qkv_code = 1 if inp["dtype"] == "bf16" else 2
+    args = sgla._chunk_args(B, T, H, K, V, N, inp["chunk_size"], qkv_code, 2, inp["scale"],
+                            inp["output_final_state"])
+    cu = None
+    cu_ptr = None
+    if inp["cu_seqlens"] is not None:
+        cu = torch.as_tensor(inp["cu_seqlens"], dtype=torch.int64).contiguous()
+        cu_ptr = ctypes.c_void_p(cu.data_ptr())
+    ws_bytes = sgla._workspace_size(args, cu_ptr)
+    t = lambda a, dt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+    copies = []
+    for _ in range(ncopies):
+        c = dict(q=t(inp["q"], qdt), k=t(inp["k"], qdt), v=t(inp["v"], qdt),
+                 g=t(inp["g"], torch.float32), gg=t(inp["g_gamma"], torch.float32),
+                 h0=t(inp["initial_state"], torch.float32),
+                 o=torch.empty((B, T, H, V), device=dev, dtype=torch.float32),
+                 ht=torch.empty((N, H, K, V), device=dev, dtype=torch.float32)
+                 if inp["output_final_state"] else None,
+                 ws=torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8))
+        p = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
+        c["call"] = (ctypes.byref(args), p(c["q"]), p(c["k"]), p(c["v"]), p(c["g"]), p(c["gg"]),
+                     p(c["h0"]), cu_ptr, p(c["o"]), p(c["ht"]), p(c["ws"]), ws_bytes)
+        copies.append(c)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    fn = sgla.lib.sgla_chunk_fwd
+
+    def step(i):
+        st = fn(*copies[i % ncopies]["call"], sp)
+        if st != 0:
+            raise RuntimeError(f"sgla_chunk_fwd failed: {sgla.lib.sgla_last_error().decode()}")
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # per-launch HIP events on the launch stream (kernel duration) ...
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    # ... and the whole timed region
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    kern_ms = sum(per) / len(per)
+    return dict(inp=inp, total_ms=total_ms, wall_s=wall, kernel_ms_mean=kern_ms,
+                kernel_ms_median=per[len(per) // 2], alg_bytes=alg_bytes, alg_flops=alg_flops,
+                ncopies=ncopies)
+
+
+def bench_decode(steps_timed: int, warmup: int):
+    import numpy as np
+    import torch
+
+    import gated_linear_attention_amd as sgla
+    from gla_workloads import DECODE_CONFIGS, make_decode_inputs
+
+    w = DECODE_CONFIGS["decode_n256_h32_k128"]
+    inp = make_decode_inputs(w)
+    dev = torch.device("cuda:0")
+    N, H, K, V, S = inp["N"], inp["H"], inp["K"], inp["V"], inp["steps"]
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+    state = t(inp["state"], torch.float32)
+    q, k, v, g = (t(inp["q"], torch.bfloat16), t(inp["k"], torch.bfloat16),
+                  t(inp["v"], torch.bfloat16), t(inp["g"], torch.float32))
+    o = torch.empty((N, H, V), device=dev, dtype=torch.float32)
+    for i in range(warmup):
+        sgla.recurrent_step(q[i % S], k[i % S], v[i % S], g[i % S], state, scale=inp["scale"], out=o)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(S)]
+    torch.cuda.synchronize()
+    for i in range(S):
+        ev[i][0].record(stream)
+        sgla.recurrent_step(q[i], k[i], v[i], g[i], state, scale=inp["scale"], out=o)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_ms = sum(per) / len(per)
+    nbytes = 2 * N * H * K * V * 4 + N * H * (2 * K + V) * 2 + N * H * 4 + N * H * V * 4
+    gbs = nbytes / (mean_ms * 1e-3) / 1e9
+    return {"workload": w.name, "N": N, "H": H, "K": K, "V": V, "steps": S,
+            "ms_per_step_mean": round(mean_ms, 5), "ms_per_step_median": round(per[S // 2], 5),
+            "bytes_per_step": nbytes, "achieved_GBs": round(gbs, 1),
+            "peak_GBs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "tokens_per_s": round(N / (mean_ms * 1e-3), 1),
+            "traffic": load_traffic(w.name, "recurrent_step")}
+
+
+def cpu_baseline(inp):
+    import oracle
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.fwd(inp["q"], inp["k"], inp["v"], g=inp["g"], g_gamma=inp["g_gamma"],
+               scale=inp["scale"], initial_state=inp["initial_state"],
+               cu_seqlens=inp["cu_seqlens"], output_final_state=inp["output_final_state"],
+               nthreads=threads)
+    dt = time.perf_counter() - t0
+    tokens = inp["B"] * inp["T"]
+    return {"value": round(tokens / dt, 2), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"one full batch of the timed workload (B={inp['B']}, T={inp['T']}, "
+                      f"H={inp['H']}, K={inp['K']}, V={inp['V']}: all "
+                      f"{inp['N'] * inp['H']} sequence-head units), fp64 token-by-token"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dense_bf16_k512",
+                    help="chunked workload to time (default: the dense bf16 K=V=512 prefill)")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {a.gpus} is not supported (every "
+              "(sequence, head) unit is independent, so more GPUs would each run their own "
+              "share with no communication; run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        sys.exit(2)
+
+    r = bench_chunk(a.workload, a.steps, a.warmup)
+    inp = r["inp"]
+    tokens = inp["B"] * inp["T"]
+    ms_step = r["total_ms"] / a.steps
+    kern_s = r["kernel_ms_mean"] * 1e-3
+    t_mem = r["alg_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = r["alg_flops"] / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+    bound = "hbm" if t_mem >= t_mfma else "mfma"
+    gbs = r["alg_bytes"] / kern_s / 1e9
+    tflops = r["alg_flops"] / kern_s / 1e12
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
+    roof["traffic"] = load_traffic(a.workload, "chunk_fwd")
+    roof.update({"kernel": "chunk_fwd_bf16_kernel" if inp["dtype"] == "bf16"
+                 else "chunk_fwd_f32_kernel",
+                 "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
+                 "kernel_ms_median": round(r["kernel_ms_median"], 5),
+                 "algorithmic_bytes_per_launch": int(r["alg_bytes"]),
+                 "algorithmic_flops_per_launch": int(r["alg_flops"]),
+                 "attainable_frac": round(max(t_mem, t_mfma) / kern_s, 4)})
+    out = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp["dtype"],
+        "data": "synthetic",
+        "config": {"workload": a.workload, "B": inp["B"], "T": inp["T"], "H": inp["H"],
+                   "K": inp["K"], "V": inp["V"], "num_seqs": inp["N"],
+                   "chunk_size": inp["chunk_size"], "o_dtype": "f32",
+                   "gate": "g" if inp["g"] is not None else
+                           ("g_gamma" if inp["g_gamma"] is not None else "none"),
+                   "output_final_state": bool(inp["output_final_state"]),
+                   "rotated_input_copies": r["ncopies"], "seed": _seed_of(a.workload)},
+        "roofline": roof,
+        "mfma": {"achieved_tflops": round(tflops, 2), "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+                 "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)},
+    }
+    if not a.no_decode:
+        out["decode"] = bench_decode(64, a.warmup)
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+
+
+def _seed_of(workload):
+    from gla_workloads import CHUNK_CONFIGS
+    return CHUNK_CONFIGS[workload].seed
+
+
+if __name__ == "__main__":
+    main()

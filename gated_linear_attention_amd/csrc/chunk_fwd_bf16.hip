@@ -5,7 +5,8 @@
 // pass, which with a head-wise gate are plain matrix products).
 //
 // For chunk n of one (sequence, head), with b the chunk-local cumulative log2
-// gate from step (1), b_last = b at the chunk's last token, and h_n the K x V
+// gate of step (1) -- formed in each chunk's prologue by a wave scan, so the
+// whole forward is a single launch -- b_last = b at the chunk's last token, and h_n the K x V
 // state entering the chunk:
 //
 //   A      = (Q K^T) (.) M,  M[c][j] = 2^(b_c - b_j) for j <= c, else 0
@@ -37,6 +38,7 @@
 // issued twice (hi and lo), keeping ~16 significant bits for those operands.
 #include <hip/hip_runtime.h>
 
+#include "gate_scan.h"
 #include "sgla_internal.h"
 
 #ifndef SGLA_TR_READ
@@ -54,7 +56,6 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int C = kChunk;  // 64 tokens per chunk
 constexpr int VT = 64;     // state / output columns per workgroup
-constexpr int NTHREADS = 256;
 constexpr int LDV = VT + 16;  // V tile row stride (elements)
 constexpr int LDA = C + 8;    // A tile row stride (elements)
 constexpr float kRcpLn2f = 1.44269504088896341f;
@@ -62,6 +63,10 @@ constexpr float kRcpLn2f = 1.44269504088896341f;
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+
+// 2^x with the hardware v_exp_f32 (results below 2^-126 may flush to zero,
+// far below any contribution that matters at fp32 accumulation).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -93,47 +98,73 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& 
   }
 }
 
+// Work split inside a workgroup (8 waves, two per SIMD): wave w owns state
+// columns [16*(w%4), +16) of the workgroup's V tile and state rows
+// [kh*K/2, +K/2) with kh = w/4.  Each wave forms the q.h contribution of its
+// own K/2 rows for all 64 tokens; the two halves are summed through LDS.  The
+// output rows are split between the two waves of a column group (c tiles
+// {0,3} for kh = 0, {1,2} for kh = 1, which also balances the causal A V work).
 template <int K>
-struct Smem {
-  static constexpr int LDQ = K + 8;
-  static constexpr int LDK = K + 16;
-  static constexpr int OFF_Q = 0;
-  static constexpr int OFF_K = OFF_Q + C * LDQ * 2;
-  static constexpr int OFF_V = OFF_K + C * LDK * 2;
-  static constexpr int OFF_AH = OFF_V + C * LDV * 2;
-  static constexpr int OFF_AL = OFF_AH + C * LDA * 2;
-  static constexpr int OFF_G = OFF_AL + C * LDA * 2;
-  static constexpr int BYTES = OFF_G + C * 4;
+struct Layout {
+  static constexpr int NW = 8;
+  static constexpr int NT = 64 * NW;
+  static constexpr int KH = K / 2;            // state rows per wave
+  static constexpr int KT = KH / 16;          // 16-row state tiles per wave
+  static constexpr int KS = KH / 32;          // 32-deep steps over a wave's rows
+  static constexpr int KSF = K / 32;          // 32-deep steps over all K
+  static constexpr bool DB = K <= 128;        // double-buffered chunk staging
+  static constexpr bool PF2 = DB;             // loads run two chunks ahead
+  static constexpr int NBUF = DB ? 2 : 1;
+  static constexpr int LDQ = K + 8;           // row strides in elements; padding
+  static constexpr int LDK = K + 16;          // keeps the 16-byte and transposing
+  static constexpr int SZ_Q = C * LDQ * 2;    // reads free of bank conflicts
+  static constexpr int SZ_K = C * LDK * 2;
+  static constexpr int SZ_V = C * LDV * 2;
+  static constexpr int SZ_G = 3 * C * 4;      // b, 2^b, 2^(b_last - b)
+  static constexpr int SZ_A = 2 * C * LDA * 2;   // hi and lo
+  static constexpr int SZ_STAGE = SZ_Q + SZ_K + SZ_V + SZ_G + SZ_A;
+  static constexpr int SZ_X = NW * 2 * 64 * 16;  // two 16x16 fp32 tiles per wave
+  // single-buffered: the exchange tiles reuse the Q staging area, which is no
+  // longer read once a chunk's A, q.h and state-update products are formed
+  static constexpr int OFF_X = DB ? NBUF * SZ_STAGE : 0;
+  static constexpr int BYTES = NBUF * SZ_STAGE + (DB ? SZ_X : 0);
+  static_assert(DB || SZ_X <= SZ_Q, "exchange tiles must fit in the Q area");
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
 // Causal 16x16 tiles (c tile, j tile) of the 64 x 64 A matrix.
 __constant__ int8_t kTileC[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
 __constant__ int8_t kTileJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
-template <int K, bool PREFETCH, typename TOut>
-__global__ void __launch_bounds__(NTHREADS)
+template <typename TOut>
+__device__ __forceinline__ void store4(TOut* p, f32x4 x);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, f32x4 x) {
+  *reinterpret_cast<f32x4*>(p) = x;
+}
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, f32x4 x) {
+  bf16x4 y;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = (bf16)x[i];
+  *reinterpret_cast<bf16x4*>(p) = y;
+}
+
+template <int K, typename TOut>
+__global__ void __launch_bounds__(Layout<K>::NT)
 chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                      const bf16* __restrict__ v, const float* __restrict__ gc,
+                      const bf16* __restrict__ v, const float* __restrict__ g,
                       const float* __restrict__ g_gamma, const float* __restrict__ h0,
                       TOut* __restrict__ o, float* __restrict__ ht, float scale, int32_t H,
                       int32_t V, SeqLayout seqs) {
-  using S = Smem<K>;
-  constexpr int LDQ = S::LDQ;
-  constexpr int LDK = S::LDK;
+  using L = Layout<K>;
+  constexpr int NT = L::NT;
   constexpr int SEG = K / 8;                 // 16-byte segments per q/k row
-  constexpr int NQ = C * SEG / NTHREADS;     // q (and k) segments per thread
-  constexpr int NV = C * (VT / 8) / NTHREADS;  // v segments per thread (2)
-  constexpr int KT = K / 16;                 // 16-row state tiles per wave
-  constexpr int KS = K / 32;                 // 32-deep k steps
-  static_assert(NQ * NTHREADS == C * SEG, "K must be a multiple of 32");
+  constexpr int NQ = C * SEG / NT;           // q (and k) segments per thread
+  constexpr int NV = C * (VT / 8) / NT;      // v segments per thread
+  static_assert(NQ * NT == C * SEG && NV * NT == C * (VT / 8), "load split");
 
-  __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
-  bf16* sQ = reinterpret_cast<bf16*>(smem + S::OFF_Q);
-  bf16* sK = reinterpret_cast<bf16*>(smem + S::OFF_K);
-  bf16* sV = reinterpret_cast<bf16*>(smem + S::OFF_V);
-  bf16* sAh = reinterpret_cast<bf16*>(smem + S::OFF_AH);
-  bf16* sAl = reinterpret_cast<bf16*>(smem + S::OFF_AL);
-  float* sG = reinterpret_cast<float*>(smem + S::OFF_G);
+  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
 
   // ---- which (sequence, head, V tile) this workgroup owns ----------------
   const int nvt = V / VT;
@@ -164,219 +195,337 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int lane = tid & 63;
   const int g4 = lane >> 4;   // 16-lane group 0..3
   const int r = lane & 15;
-  const int vcol = vt * VT + 16 * w + r;   // this lane's state / output column
-  const int64_t row_stride_qk = (int64_t)H * K;
-  const int64_t row_stride_v = (int64_t)H * V;
+  const int kh = w >> 2;      // state row half
+  const int vc = w & 3;       // 16-column group
+  const int krow0 = kh * L::KH;
+  const int vcol = vt * VT + 16 * vc + r;   // this lane's state column
+  const int own0 = kh == 0 ? 0 : 1;         // output c tiles owned by this wave
+  const int own1 = kh == 0 ? 3 : 2;
+  const int RSK = H * K;                    // token stride of q and k (elements)
+  const int RSV = H * V;                    // token stride of v and o
+  const bf16* qb = q + (bos * H + hd) * (int64_t)K;
+  const bf16* kb = k + (bos * H + hd) * (int64_t)K;
+  const bf16* vb = v + (bos * H + hd) * (int64_t)V + vt * VT;
+  const float* gb = g != nullptr ? g + bos * H + hd : nullptr;
+  TOut* ob = o + (bos * H + hd) * (int64_t)V + vt * VT + 16 * vc + 4 * g4;
   const float gam2 = g_gamma != nullptr ? g_gamma[hd] * kRcpLn2f : 0.f;
 
-  // Upper-triangle A tiles are never written: zero both A buffers once.
-  for (int i = tid; i < 2 * C * LDA / 8; i += NTHREADS)
-    reinterpret_cast<uint4*>(sAh)[i] = make_uint4(0, 0, 0, 0);
+  auto sQ = [&](int p) { return reinterpret_cast<bf16*>(smem + p * L::SZ_STAGE); };
+  auto sK = [&](int p) { return reinterpret_cast<bf16*>(smem + p * L::SZ_STAGE + L::SZ_Q); };
+  auto sV = [&](int p) {
+    return reinterpret_cast<bf16*>(smem + p * L::SZ_STAGE + L::SZ_Q + L::SZ_K);
+  };
+  auto sG = [&](int p) {
+    return reinterpret_cast<float*>(smem + p * L::SZ_STAGE + L::SZ_Q + L::SZ_K + L::SZ_V);
+  };
+  auto sA = [&](int p) {
+    return reinterpret_cast<bf16*>(smem + p * L::SZ_STAGE + L::SZ_Q + L::SZ_K + L::SZ_V + L::SZ_G);
+  };
+  f32x4* sX = reinterpret_cast<f32x4*>(smem + L::OFF_X);
 
-  // ---- state in registers: h[kt][i] = state[16kt + 4g + i][vcol] ---------
-  f32x4 h[KT];
+  // Upper-triangle A tiles are never written: zero the A buffers once.
+  for (int p = 0; p < L::NBUF; ++p)
+    for (int i = tid; i < L::SZ_A / 16; i += NT)
+      reinterpret_cast<uint4*>(sA(p))[i] = make_uint4(0, 0, 0, 0);
+
+  // ---- state in registers: h[kt][i] = S[krow0 + 16kt + 4g + i][vcol] ------
+  f32x4 h[L::KT];
   {
     const float* h0u = h0 != nullptr ? h0 + ((int64_t)seq * H + hd) * K * V : nullptr;
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+    for (int kt = 0; kt < L::KT; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        h[kt][i] = h0u != nullptr ? h0u[(int64_t)(16 * kt + 4 * g4 + i) * V + vcol] : 0.f;
+        h[kt][i] = h0u != nullptr ? h0u[(int64_t)(krow0 + 16 * kt + 4 * g4 + i) * V + vcol] : 0.f;
   }
 
   // ---- chunk staging registers -------------------------------------------
-  uint4 pq[NQ], pk[NQ], pv[NV];
-  float pg = 0.f;
-  auto load_chunk = [&](int m) {
-    const int64_t t0 = bos + (int64_t)m * C;
+  struct Stage {
+    uint4 q[NQ], k[NQ], v[NV];
+    float g;
+    int len;
+  };
+  auto load_chunk = [&](int m, Stage& st) {
+    uint4* pq = st.q;
+    uint4* pk = st.k;
+    uint4* pv = st.v;
     const int cl = min(C, len - m * C);
+    st.len = cl;
+    const int64_t tok = (int64_t)m * C;
+    const bf16* qc = qb + tok * RSK;
+    const bf16* kc = kb + tok * RSK;
+    const bf16* vcp = vb + tok * RSV;
+    if (cl == C) {
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const int s = tid + i * NT;
+        const int off = (s / SEG) * RSK + (s % SEG) * 8;
+        pq[i] = *reinterpret_cast<const uint4*>(qc + off);
+        pk[i] = *reinterpret_cast<const uint4*>(kc + off);
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int s = tid + i * NT;
+        pv[i] = *reinterpret_cast<const uint4*>(vcp + (s / (VT / 8)) * RSV + (s % (VT / 8)) * 8);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const int s = tid + i * NT;
+        const int row = s / SEG;
+        const int off = row * RSK + (s % SEG) * 8;
+        pq[i] = row < cl ? *reinterpret_cast<const uint4*>(qc + off) : make_uint4(0, 0, 0, 0);
+        pk[i] = row < cl ? *reinterpret_cast<const uint4*>(kc + off) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int s = tid + i * NT;
+        const int row = s / (VT / 8);
+        pv[i] = row < cl ? *reinterpret_cast<const uint4*>(vcp + row * RSV + (s % (VT / 8)) * 8)
+                         : make_uint4(0, 0, 0, 0);
+      }
+    }
+    // per-token log gate; rows past the chunk's end contribute 0, so their
+    // cumulative value equals the last real token's (a finite decay for their
+    // zero k and v rows)
+    st.g = 0.f;
+    if (tid < C && gb != nullptr) st.g = tid < cl ? gb[(tok + tid) * H] : 0.f;
+  };
+  auto store_chunk = [&](int p, const Stage& st) {
+    const uint4* pq = st.q;
+    const uint4* pk = st.k;
+    const uint4* pv = st.v;
+    bf16* q_s = sQ(p);
+    bf16* k_s = sK(p);
+    bf16* v_s = sV(p);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
-      const int s = tid + i * NTHREADS;
-      const int row = s / SEG, c8 = s % SEG;
-      if (row < cl) {
-        const int64_t off = (t0 + row) * row_stride_qk + (int64_t)hd * K + c8 * 8;
-        pq[i] = *reinterpret_cast<const uint4*>(q + off);
-        pk[i] = *reinterpret_cast<const uint4*>(k + off);
-      } else {
-        pq[i] = make_uint4(0, 0, 0, 0);
-        pk[i] = make_uint4(0, 0, 0, 0);
-      }
+      const int s = tid + i * NT;
+      *reinterpret_cast<uint4*>(q_s + (s / SEG) * L::LDQ + (s % SEG) * 8) = pq[i];
+      *reinterpret_cast<uint4*>(k_s + (s / SEG) * L::LDK + (s % SEG) * 8) = pk[i];
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int s = tid + i * NTHREADS;
-      const int row = s / (VT / 8), c8 = s % (VT / 8);
-      if (row < cl) {
-        const int64_t off = (t0 + row) * row_stride_v + (int64_t)hd * V + vt * VT + c8 * 8;
-        pv[i] = *reinterpret_cast<const uint4*>(v + off);
-      } else {
-        pv[i] = make_uint4(0, 0, 0, 0);
-      }
+      const int s = tid + i * NT;
+      *reinterpret_cast<uint4*>(v_s + (s / (VT / 8)) * LDV + (s % (VT / 8)) * 8) = pv[i];
     }
     if (tid < C) {
-      // rows past the chunk's end repeat the last gate value so that their
-      // (zero) k and v rows get a finite decay factor
-      const int c = min(tid, cl - 1);
-      if (gc != nullptr) pg = gc[(t0 + c) * H + hd];
-      else pg = (float)(c + 1) * gam2;
+      // step (1): chunk-local cumulative log2 gate b, plus the per-token
+      // factors 2^b (inter-chunk term) and 2^(b_last - b) (state update)
+      float* g_s = sG(p);
+      const float b = gb != nullptr ? wave_cumsum_log2(st.g)
+                                    : (float)min(tid + 1, st.len) * gam2;
+      const float blast = __shfl(b, C - 1, 64);
+      g_s[tid] = b;
+      g_s[C + tid] = exp2_hw(b);
+      g_s[2 * C + tid] = exp2_hw(blast - b);
     }
   };
-  auto store_chunk = [&]() {
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int s = tid + i * NTHREADS;
-      const int row = s / SEG, c8 = s % SEG;
-      *reinterpret_cast<uint4*>(sQ + row * LDQ + c8 * 8) = pq[i];
-      *reinterpret_cast<uint4*>(sK + row * LDK + c8 * 8) = pk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int s = tid + i * NTHREADS;
-      const int row = s / (VT / 8), c8 = s % (VT / 8);
-      *reinterpret_cast<uint4*>(sV + row * LDV + c8 * 8) = pv[i];
-    }
-    if (tid < C) sG[tid] = pg;
+
+  // output tiles of the previous chunk still to be combined and stored
+  f32x4 oown0 = {0.f, 0.f, 0.f, 0.f}, oown1 = {0.f, 0.f, 0.f, 0.f};
+  int prev_m = -1, prev_cl = 0;
+  auto finalize = [&]() {
+    // partner's q.h partial for this wave's two c tiles, then scale and store
+    const f32x4 x0 = sX[((w ^ 4) * 2 + 0) * 64 + lane];
+    const f32x4 x1 = sX[((w ^ 4) * 2 + 1) * 64 + lane];
+    TOut* oc = ob + (int64_t)prev_m * C * RSV;
+    const int c0 = 16 * own0 + r, c1 = 16 * own1 + r;
+    if (c0 < prev_cl) store4(oc + (int64_t)c0 * RSV, (oown0 + x0) * scale);
+    if (c1 < prev_cl) store4(oc + (int64_t)c1 * RSV, (oown1 + x1) * scale);
   };
 
-  if (nchunks > 0 && PREFETCH) load_chunk(0);
+  Stage st0, st1;
+  if (nchunks > 0) load_chunk(0, st0);
+  if (L::PF2 && nchunks > 1) load_chunk(1, st1);
 
-  for (int m = 0; m < nchunks; ++m) {
-    if (!PREFETCH) load_chunk(m);
-    store_chunk();
-    __syncthreads();
-    if (PREFETCH && m + 1 < nchunks) load_chunk(m + 1);
-    const int64_t t0 = bos + (int64_t)m * C;
-    const int cl = min(C, len - m * C);
+  // one chunk: stage it, then A, q.h, state update, A v and the exchange
+  auto body = [&](const int m, const int p, Stage& st) {
+    const int cl = st.len;
+    store_chunk(p, st);
+    __syncthreads();   // chunk m staged; previous chunk's exchange tiles visible
+    if (L::DB && prev_m >= 0) finalize();
+    const int next = m + (L::PF2 ? 2 : 1);
+    if (next < nchunks) load_chunk(next, st);
+    const bf16* q_s = sQ(p);
+    const bf16* k_s = sK(p);
+    const bf16* v_s = sV(p);
+    const float* g_s = sG(p);
+    bf16* a_hi = sA(p);
+    bf16* a_lo = a_hi + C * LDA;
 
     // ---- A = (Q K^T) (.) M, split into bf16 hi + lo, into LDS ------------
-    for (int ti = w; ti < 10; ti += 4) {
+    for (int ti = w; ti < 10; ti += L::NW) {
       const int ct = kTileC[ti], jt = kTileJ[ti];
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + (16 * jt + r) * LDK + 32 * s + 8 * g4);
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(sQ + (16 * ct + r) * LDQ + 32 * s + 8 * g4);
-        acc = mfma(a, b, acc);  // acc[i] = (q_c . k_j), c = 16ct + r, j = 16jt + 4g + i
+      for (int s = 0; s < L::KSF; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(k_s + (16 * jt + r) * L::LDK + 32 * s + 8 * g4);
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(q_s + (16 * ct + r) * L::LDQ + 32 * s + 8 * g4);
+        acc = mfma(a, b, acc);  // acc[i] = q_c . k_j, c = 16ct + r, j = 16jt + 4g + i
       }
       const int c = 16 * ct + r;
-      const float bc = sG[c];
+      const float bc = g_s[c];
       bf16x4 hi, lo;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 16 * jt + 4 * g4 + i;
-        const float x = (j <= c) ? acc[i] * exp2f(bc - sG[j]) : 0.f;
+        const float x = (j <= c) ? acc[i] * exp2_hw(bc - g_s[j]) : 0.f;
         const bf16 hv = (bf16)x;
         hi[i] = hv;
         lo[i] = (bf16)(x - (float)hv);
       }
-      *reinterpret_cast<bf16x4*>(sAh + c * LDA + 16 * jt + 4 * g4) = hi;
-      *reinterpret_cast<bf16x4*>(sAl + c * LDA + 16 * jt + 4 * g4) = lo;
+      *reinterpret_cast<bf16x4*>(a_hi + c * LDA + 16 * jt + 4 * g4) = hi;
+      *reinterpret_cast<bf16x4*>(a_lo + c * LDA + 16 * jt + 4 * g4) = lo;
     }
-    __syncthreads();
 
-    // ---- O = scale * (diag(2^b) Q h + A V) for this wave's 16 columns -----
+    // ---- O^T partial = h^T Q^T over this wave's K/2 state rows -----------
     f32x4 oacc[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      // B operand from the state: k rows 32s + 4g + {0..3} and 32s + 16 + 4g + {0..3}
+    for (int s = 0; s < L::KS; ++s) {
+      // A operand from the state: rows krow0 + 32s + 4g + {0..3} and
+      // krow0 + 32s + 16 + 4g + {0..3}; q is read with the same k order
       float x[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         x[i] = h[2 * s][i];
         x[4 + i] = h[2 * s + 1][i];
       }
-      bf16x8 bh, bl;
-      split8(x, bh, bl);
+      bf16x8 hh, hl;
+      split8(x, hh, hl);
+      bf16x8 b[4];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        const bf16* qrow = sQ + (16 * ct + r) * LDQ + 32 * s + 4 * g4;
-        const bf16x8 a = cat(*reinterpret_cast<const bf16x4*>(qrow),
-                             *reinterpret_cast<const bf16x4*>(qrow + 16));
-        oacc[ct] = mfma(a, bh, oacc[ct]);
-        oacc[ct] = mfma(a, bl, oacc[ct]);
+        const bf16* qrow = q_s + (16 * ct + r) * L::LDQ + krow0 + 32 * s + 4 * g4;
+        b[ct] = cat(*reinterpret_cast<const bf16x4*>(qrow), *reinterpret_cast<const bf16x4*>(qrow + 16));
       }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) oacc[ct] = mfma(hh, b[ct], oacc[ct]);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) oacc[ct] = mfma(hl, b[ct], oacc[ct]);
     }
+    // diag(2^b): O^T column c = 16ct + r
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[ct][i] *= exp2f(sG[16 * ct + 4 * g4 + i]);
+    for (int ct = 0; ct < 4; ++ct) oacc[ct] *= g_s[C + 16 * ct + r];
 
-    // V tile fragments: vf[s][e] = V[32s + 8g + e][16w + r]
+    // ---- h <- 2^b_last h + K^T (diag(2^(b_last - b)) V), own rows ---------
+    // V fragments vf[s][e] = V[32s + 8g + e][16vc + r]
     bf16x8 vf[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-      vf[s] = cat(tr_read(sV, LDV, 32 * s + 8 * g4, 16 * w),
-                  tr_read(sV, LDV, 32 * s + 8 * g4 + 4, 16 * w));
+      vf[s] = cat(tr_read(v_s, LDV, 32 * s + 8 * g4, 16 * vc),
+                  tr_read(v_s, LDV, 32 * s + 8 * g4 + 4, 16 * vc));
+    {
+      const float dall = g_s[C + C - 1];   // 2^b_last
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const int nsteps = ct < 2 ? 1 : 2;   // j < 32 suffices for c < 32
-#pragma unroll
-      for (int s = 0; s < nsteps; ++s) {
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sAh + (16 * ct + r) * LDA + 32 * s + 8 * g4);
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(sAl + (16 * ct + r) * LDA + 32 * s + 8 * g4);
-        oacc[ct] = mfma(ah, vf[s], oacc[ct]);
-        oacc[ct] = mfma(al, vf[s], oacc[ct]);
-      }
-    }
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = 16 * ct + 4 * g4 + i;
-        if (c < cl) o[((t0 + c) * H + hd) * (int64_t)V + vcol] = (TOut)(oacc[ct][i] * scale);
-      }
-
-    // ---- h <- 2^b_last h + K^T (diag(2^(b_last - b)) V) --------------------
-    const float blast = sG[C - 1];
-    const float dall = exp2f(blast);
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) h[kt][i] *= dall;
-    bf16x8 vth[2], vtl[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (float)vf[s][e] * exp2f(blast - sG[32 * s + 8 * g4 + e]);
-      split8(x, vth[s], vtl[s]);
-    }
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
+      for (int kt = 0; kt < L::KT; ++kt) h[kt] *= dall;
+      bf16x8 vth[2], vtl[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        // A operand: K^T[16kt + r][32s + 8g + e]
-        const bf16x8 a = cat(tr_read(sK, LDK, 32 * s + 8 * g4, 16 * kt),
-                             tr_read(sK, LDK, 32 * s + 8 * g4 + 4, 16 * kt));
-        h[kt] = mfma(a, vth[s], h[kt]);
-        h[kt] = mfma(a, vtl[s], h[kt]);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(g_s + 2 * C + 32 * s + 8 * g4);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(g_s + 2 * C + 32 * s + 8 * g4 + 4);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = (float)vf[s][e] * d0[e];
+          x[4 + e] = (float)vf[s][4 + e] * d1[e];
+        }
+        split8(x, vth[s], vtl[s]);
+      }
+      constexpr int KG = L::KT < 4 ? L::KT : 4;   // state tiles per MFMA group
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int k0 = 0; k0 < L::KT; k0 += KG) {
+          // A operands: K^T[krow0 + 16kt + r][32s + 8g + e]
+          bf16x8 a[KG];
+#pragma unroll
+          for (int u = 0; u < KG; ++u)
+            a[u] = cat(tr_read(k_s, L::LDK, 32 * s + 8 * g4, krow0 + 16 * (k0 + u)),
+                       tr_read(k_s, L::LDK, 32 * s + 8 * g4 + 4, krow0 + 16 * (k0 + u)));
+#pragma unroll
+          for (int u = 0; u < KG; ++u) h[k0 + u] = mfma(a[u], vth[s], h[k0 + u]);
+#pragma unroll
+          for (int u = 0; u < KG; ++u) h[k0 + u] = mfma(a[u], vtl[s], h[k0 + u]);
+        }
       }
     }
+    __syncthreads();   // A complete
+
+    // ---- O^T += V^T A^T for this wave's two c tiles ------------------------
+    // own tiles: kh = 0 -> c tiles 0 (j < 32) and 3 (j < 64);
+    //            kh = 1 -> c tiles 1 (j < 32) and 2 (j < 64)
+    const bool hi_half = kh != 0;
+    f32x4 mine0 = hi_half ? oacc[1] : oacc[0];
+    f32x4 mine1 = hi_half ? oacc[2] : oacc[3];
+    const f32x4 give0 = hi_half ? oacc[0] : oacc[1];
+    const f32x4 give1 = hi_half ? oacc[3] : oacc[2];
+    {
+      const bf16* ah0 = a_hi + (16 * own0 + r) * LDA + 8 * g4;
+      const bf16* ah1 = a_hi + (16 * own1 + r) * LDA + 8 * g4;
+      const bf16x8 p0h = *reinterpret_cast<const bf16x8*>(ah0);
+      const bf16x8 p0l = *reinterpret_cast<const bf16x8*>(ah0 + C * LDA);
+      const bf16x8 p1h = *reinterpret_cast<const bf16x8*>(ah1);
+      const bf16x8 p1l = *reinterpret_cast<const bf16x8*>(ah1 + C * LDA);
+      const bf16x8 p2h = *reinterpret_cast<const bf16x8*>(ah1 + 32);
+      const bf16x8 p2l = *reinterpret_cast<const bf16x8*>(ah1 + 32 + C * LDA);
+      mine0 = mfma(vf[0], p0h, mine0);
+      mine1 = mfma(vf[0], p1h, mine1);
+      mine0 = mfma(vf[0], p0l, mine0);
+      mine1 = mfma(vf[0], p1l, mine1);
+      mine1 = mfma(vf[1], p2h, mine1);
+      mine1 = mfma(vf[1], p2l, mine1);
+    }
+    if (!L::DB) __syncthreads();   // Q area is about to hold exchange tiles
+    // partner's c tiles go through LDS
+    sX[(w * 2 + 0) * 64 + lane] = give0;
+    sX[(w * 2 + 1) * 64 + lane] = give1;
+    oown0 = mine0;
+    oown1 = mine1;
+    prev_m = m;
+    prev_cl = cl;
+    if (!L::DB) {
+      __syncthreads();
+      finalize();
+      __syncthreads();   // exchange tiles read before the next chunk is staged
+    }
+  };
+
+  if (L::PF2) {
+    for (int m = 0; m < nchunks; m += 2) {
+      body(m, 0, st0);
+      if (m + 1 < nchunks) body(m + 1, 1, st1);
+    }
+  } else {
+    for (int m = 0; m < nchunks; ++m) body(m, L::DB ? (m & 1) : 0, st0);
+  }
+  if (L::DB && prev_m >= 0) {
     __syncthreads();
+    finalize();
   }
 
   if (ht != nullptr) {
     float* htu = ht + ((int64_t)seq * H + hd) * K * V;
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+    for (int kt = 0; kt < L::KT; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) htu[(int64_t)(16 * kt + 4 * g4 + i) * V + vcol] = h[kt][i];
+      for (int i = 0; i < 4; ++i)
+        htu[(int64_t)(krow0 + 16 * kt + 4 * g4 + i) * V + vcol] = h[kt][i];
   }
 }
 
-template <int K, bool PREFETCH, typename TOut>
+template <int K, typename TOut>
 hipError_t launch_k(const ChunkFwdParams& p, hipStream_t stream) {
   const int num_units = p.seqs.num_seqs * p.H;
   if (num_units == 0) return hipSuccess;
   const int nvt = p.V / VT;
   const int groups = (num_units + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(groups * kXcds * nvt));
-  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<K, PREFETCH, TOut>), grid, dim3(NTHREADS), 0, stream,
+  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<K, TOut>), grid, dim3(Layout<K>::NT), 0, stream,
                      static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
-                     static_cast<const bf16*>(p.v), p.gc, p.g_gamma, p.h0,
+                     static_cast<const bf16*>(p.v), p.g, p.g_gamma, p.h0,
                      static_cast<TOut*>(p.o), p.ht, p.scale, p.H, p.V, p.seqs);
   return hipGetLastError();
 }
@@ -384,10 +533,10 @@ hipError_t launch_k(const ChunkFwdParams& p, hipStream_t stream) {
 template <typename TOut>
 hipError_t launch_out(const ChunkFwdParams& p, hipStream_t stream) {
   switch (p.K) {
-    case 64: return launch_k<64, true, TOut>(p, stream);
-    case 128: return launch_k<128, true, TOut>(p, stream);
-    case 256: return launch_k<256, true, TOut>(p, stream);
-    case 512: return launch_k<512, false, TOut>(p, stream);
+    case 64: return launch_k<64, TOut>(p, stream);
+    case 128: return launch_k<128, TOut>(p, stream);
+    case 256: return launch_k<256, TOut>(p, stream);
+    case 512: return launch_k<512, TOut>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

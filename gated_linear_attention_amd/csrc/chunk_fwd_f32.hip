@@ -6,7 +6,7 @@
 // peaks are the same, so MFMA would not buy throughput here.
 //
 // Same per-chunk algebra as the bf16 kernel, with b the chunk-local
-// cumulative log2 gate:
+// cumulative log2 gate (formed in the chunk prologue by a wave scan):
 //   A = (Q K^T) (.) M,   M[c][j] = 2^(b_c - b_j) (j <= c), 0 otherwise
 //   O = scale * (A V + diag(2^b) Q h)
 //   h <- 2^b_last h + K^T (diag(2^(b_last - b)) V)
@@ -14,6 +14,7 @@
 // tile lives in LDS for the whole sequence.
 #include <hip/hip_runtime.h>
 
+#include "gate_scan.h"
 #include "sgla_internal.h"
 
 namespace sgla {
@@ -27,7 +28,7 @@ constexpr float kRcpLn2f = 1.44269504088896341f;
 template <int K, typename TOut>
 __global__ void __launch_bounds__(NTHREADS)
 chunk_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
-                     const float* __restrict__ v, const float* __restrict__ gc,
+                     const float* __restrict__ v, const float* __restrict__ g,
                      const float* __restrict__ g_gamma, const float* __restrict__ h0,
                      TOut* __restrict__ o, float* __restrict__ ht, float scale, int32_t H,
                      int32_t V, SeqLayout seqs) {
@@ -85,8 +86,9 @@ chunk_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
       sV[c][vv] = c < cl ? v[((t0 + c) * H + hd) * (int64_t)V + vt * VT + vv] : 0.f;
     }
     if (tid < C) {
-      const int c = min(tid, cl - 1);
-      sG[tid] = gc != nullptr ? gc[(t0 + c) * H + hd] : (float)(c + 1) * gam2;
+      // step (1): chunk-local cumulative log2 gate (padding rows add 0)
+      if (g != nullptr) sG[tid] = wave_cumsum_log2(tid < cl ? g[(t0 + tid) * H + hd] : 0.f);
+      else sG[tid] = (float)min(tid + 1, cl) * gam2;
     }
     __syncthreads();
     const float blast = sG[C - 1];
@@ -152,7 +154,7 @@ hipError_t launch_k(const ChunkFwdParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(groups * kXcds * nvt));
   hipLaunchKernelGGL((chunk_fwd_f32_kernel<K, TOut>), grid, dim3(NTHREADS), 0, stream,
                      static_cast<const float*>(p.q), static_cast<const float*>(p.k),
-                     static_cast<const float*>(p.v), p.gc, p.g_gamma, p.h0,
+                     static_cast<const float*>(p.v), p.g, p.g_gamma, p.h0,
                      static_cast<TOut*>(p.o), p.ht, p.scale, p.H, p.V, p.seqs);
   return hipGetLastError();
 }

@@ -6,17 +6,16 @@
 //
 // One 64-lane wavefront per (chunk, head): lane c holds token c of the chunk,
 // and a wave-level inclusive scan (log2(64) = 6 shuffle rounds) forms the
-// prefix sums.  The scan accumulates in float64 and rounds once to float32;
-// the kernel moves 8 bytes per (token, head) and is negligible next to the
-// chunk kernel.
+// prefix sums.  The scan accumulates in float64 and rounds once to float32.
+// The chunk kernels run the same scan in their chunk prologue; this kernel
+// serves the standalone sgla_chunk_local_cumsum entry point.
 #include <hip/hip_runtime.h>
 
+#include "gate_scan.h"
 #include "sgla_internal.h"
 
 namespace sgla {
 namespace {
-
-constexpr double kRcpLn2 = 1.4426950408889634074;  // 1 / ln 2
 
 __global__ void __launch_bounds__(256)
 gate_cumsum_kernel(const float* __restrict__ g, float* __restrict__ gc, int32_t H,
@@ -38,13 +37,8 @@ gate_cumsum_kernel(const float* __restrict__ g, float* __restrict__ gc, int32_t 
     len = min(kChunk, seqs.T - m * kChunk);
   }
   const bool active = lane < len;
-  double x = active ? (double)g[(t0 + lane) * H + head] : 0.0;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const double y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  if (active) gc[(t0 + lane) * H + head] = (float)(x * kRcpLn2);
+  const float b = wave_cumsum_log2(active ? g[(t0 + lane) * H + head] : 0.f);
+  if (active) gc[(t0 + lane) * H + head] = b;
 }
 
 }  // namespace

@@ -51,7 +51,6 @@ struct Plan {
   bool packed = false;
   std::vector<sgla::SeqEntry> seqs;      // packed only, longest first
   std::vector<sgla::ChunkEntry> chunks;  // packed only
-  size_t gc_bytes = 0;
   size_t seq_off = 0, chunk_off = 0, total_bytes = 0;
 };
 
@@ -117,8 +116,7 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
     P->N = a->B;
     P->num_chunks = a->T > 0 ? a->B * ((a->T + sgla::kChunk - 1) / sgla::kChunk) : 0;
   }
-  P->gc_bytes = align_up((size_t)P->total_tokens * a->H * sizeof(float), 256);
-  P->seq_off = P->gc_bytes;
+  P->seq_off = 0;
   P->chunk_off = P->seq_off + align_up(P->seqs.size() * sizeof(sgla::SeqEntry), 256);
   P->total_bytes = P->chunk_off + align_up(P->chunks.size() * sizeof(sgla::ChunkEntry), 256);
   return SGLA_OK;
@@ -206,17 +204,11 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
   if (st != SGLA_OK) return st;
   const sgla::SeqLayout L = layout_of(args, P, ws);
 
-  float* gc = nullptr;
-  if (g != nullptr && any_tokens) {
-    gc = reinterpret_cast<float*>(ws);
-    hipError_t e = sgla::launch_gate_cumsum(g, gc, a.H, L, stream);
-    if (e != hipSuccess) return hip_fail(e, "launching the gate cumsum kernel");
-  }
   sgla::ChunkFwdParams p;
   p.q = q;
   p.k = k;
   p.v = v;
-  p.gc = gc;
+  p.g = g;
   p.g_gamma = g_gamma;
   p.h0 = initial_state;
   p.o = o;

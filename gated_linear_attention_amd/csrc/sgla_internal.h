@@ -40,7 +40,7 @@ struct ChunkFwdParams {
   const void* q;
   const void* k;
   const void* v;
-  const float* gc;           // chunk-local cumulative log2 gates [T_total, H], or nullptr
+  const float* g;            // per-token natural-log gates [T_total, H], or nullptr
   const float* g_gamma;      // [H] natural-log decay, or nullptr
   const float* h0;           // [N, H, K, V] or nullptr
   void* o;
