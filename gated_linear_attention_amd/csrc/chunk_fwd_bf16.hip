@@ -53,6 +53,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int C = kChunk;  // 64 tokens per chunk
 constexpr int VT = 64;     // state / output columns per workgroup
@@ -88,14 +90,47 @@ __device__ __forceinline__ bf16x4 tr_read(const bf16* base, int ld, int row0, in
 #endif
 }
 
-// x = hi + lo with hi, lo bf16 (round to nearest even on both roundings).
+// Raw buffer descriptor over [base, base + bytes).  Loads past the end return
+// zeros and stores past the end are dropped, which is how a chunk's tail rows
+// (and a chunk past the sequence's end, with bytes = 0) are handled without
+// branches: every wave issues the same memory instructions on every chunk.
+// Callers pass workgroup-uniform values; they are moved to scalar registers
+// explicitly so the descriptor never has to be rebuilt per lane.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// bf16 pair <-> two floats (element 0 is the low half of the 32-bit word)
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+
+// (a, b) = hi + lo with hi = bf16(x) and lo = bf16(x - hi), both rounded to
+// nearest even; 6 VALU per pair (one paired convert for each half).
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const f32x2 v = {a, b};
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  const f32x2 hf = {bf_lo(hi), bf_hi(hi)};
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(v - hf, bf16x2));
+}
+
 __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const bf16 h = (bf16)x[e];
-    hi[e] = h;
-    lo[e] = (bf16)(x[e] - (float)h);
+  for (int i = 0; i < 4; ++i) {
+    uint32_t a, b;
+    split2(x[2 * i], x[2 * i + 1], a, b);
+    h[i] = a;
+    l[i] = b;
   }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
 }
 
 // Work split inside a workgroup (8 waves, two per SIMD): wave w owns state
@@ -124,30 +159,34 @@ struct Layout {
   static constexpr int SZ_A = 2 * C * LDA * 2;   // hi and lo
   static constexpr int SZ_STAGE = SZ_Q + SZ_K + SZ_V + SZ_G + SZ_A;
   static constexpr int SZ_X = NW * 2 * 64 * 16;  // two 16x16 fp32 tiles per wave
-  // single-buffered: the exchange tiles reuse the Q staging area, which is no
-  // longer read once a chunk's A, q.h and state-update products are formed
+  // double-buffered (pipelined) mode: one exchange area per chunk parity;
+  // single-buffered mode: the exchange tiles reuse the Q staging area, which
+  // is no longer read once a chunk's A, q.h and state-update products exist
   static constexpr int OFF_X = DB ? NBUF * SZ_STAGE : 0;
-  static constexpr int BYTES = NBUF * SZ_STAGE + (DB ? SZ_X : 0);
+  static constexpr int BYTES = NBUF * SZ_STAGE + (DB ? 2 * SZ_X : 0);
   static_assert(DB || SZ_X <= SZ_Q, "exchange tiles must fit in the Q area");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-// Causal 16x16 tiles (c tile, j tile) of the 64 x 64 A matrix.
-__constant__ int8_t kTileC[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ int8_t kTileJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+// Causal 16x16 tiles (c tile, j tile) of the 64 x 64 A matrix, packed 4 bits
+// per tile (c | j << 2) so a wave picks its tiles with scalar shifts instead
+// of a memory load: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3).
+constexpr uint64_t kCausalTiles = 0xFB73A62510ull;
+__device__ __forceinline__ int tile_c(int ti) { return (int)(kCausalTiles >> (4 * ti)) & 3; }
+__device__ __forceinline__ int tile_j(int ti) { return (int)(kCausalTiles >> (4 * ti + 2)) & 3; }
 
 template <typename TOut>
-__device__ __forceinline__ void store4(TOut* p, f32x4 x);
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t rs, uint32_t off, f32x4 x);
 template <>
-__device__ __forceinline__ void store4<float>(float* p, f32x4 x) {
-  *reinterpret_cast<f32x4*>(p) = x;
+__device__ __forceinline__ void store4<float>(__amdgpu_buffer_rsrc_t rs, uint32_t off, f32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, off, 0, 0);
 }
 template <>
-__device__ __forceinline__ void store4<bf16>(bf16* p, f32x4 x) {
+__device__ __forceinline__ void store4<bf16>(__amdgpu_buffer_rsrc_t rs, uint32_t off, f32x4 x) {
   bf16x4 y;
 #pragma unroll
   for (int i = 0; i < 4; ++i) y[i] = (bf16)x[i];
-  *reinterpret_cast<bf16x4*>(p) = y;
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, y), rs, off, 0, 0);
 }
 
 template <int K, typename TOut>
@@ -179,10 +218,12 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   int64_t bos;
   int32_t len, seq;
   if (seqs.seq_table != nullptr) {
+    // workgroup-uniform: keep in scalar registers so buffer descriptors built
+    // from them stay scalar
     const SeqEntry e = seqs.seq_table[rank];
-    bos = e.bos;
-    len = e.len;
-    seq = e.seq;
+    bos = __builtin_amdgcn_readfirstlane(e.bos);
+    len = __builtin_amdgcn_readfirstlane(e.len);
+    seq = __builtin_amdgcn_readfirstlane(e.seq);
   } else {
     bos = (int64_t)rank * seqs.T;
     len = seqs.T;
@@ -191,7 +232,7 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int nchunks = (len + C - 1) / C;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g4 = lane >> 4;   // 16-lane group 0..3
   const int r = lane & 15;
@@ -201,14 +242,20 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int vcol = vt * VT + 16 * vc + r;   // this lane's state column
   const int own0 = kh == 0 ? 0 : 1;         // output c tiles owned by this wave
   const int own1 = kh == 0 ? 3 : 2;
+  // c tiles in q.h order: this wave's two, then its partner's (w ^ 4) two
+  const int ctile[4] = {own0, own1, kh == 0 ? 1 : 0, kh == 0 ? 2 : 3};
   const int RSK = H * K;                    // token stride of q and k (elements)
   const int RSV = H * V;                    // token stride of v and o
   const bf16* qb = q + (bos * H + hd) * (int64_t)K;
   const bf16* kb = k + (bos * H + hd) * (int64_t)K;
   const bf16* vb = v + (bos * H + hd) * (int64_t)V + vt * VT;
   const float* gb = g != nullptr ? g + bos * H + hd : nullptr;
-  TOut* ob = o + (bos * H + hd) * (int64_t)V + vt * VT + 16 * vc + 4 * g4;
-  const float gam2 = g_gamma != nullptr ? g_gamma[hd] * kRcpLn2f : 0.f;
+  TOut* ob = o + (bos * H + hd) * (int64_t)V + vt * VT;     // workgroup-uniform base
+  const uint32_t ocol = (16 * vc + 4 * g4) * (uint32_t)sizeof(TOut);   // lane's 4 columns
+  const float gam2 = g_gamma != nullptr
+                         ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                         __builtin_bit_cast(int, g_gamma[hd]))) * kRcpLn2f
+                         : 0.f;
 
   auto sQ = [&](int p) { return reinterpret_cast<bf16*>(smem + p * L::SZ_STAGE); };
   auto sK = [&](int p) { return reinterpret_cast<bf16*>(smem + p * L::SZ_STAGE + L::SZ_Q); };
@@ -221,7 +268,7 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   auto sA = [&](int p) {
     return reinterpret_cast<bf16*>(smem + p * L::SZ_STAGE + L::SZ_Q + L::SZ_K + L::SZ_V + L::SZ_G);
   };
-  f32x4* sX = reinterpret_cast<f32x4*>(smem + L::OFF_X);
+  auto sX = [&](int p) { return reinterpret_cast<f32x4*>(smem + L::OFF_X + p * L::SZ_X); };
 
   // Upper-triangle A tiles are never written: zero the A buffers once.
   for (int p = 0; p < L::NBUF; ++p)
@@ -241,122 +288,80 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   // ---- chunk staging registers -------------------------------------------
   struct Stage {
-    uint4 q[NQ], k[NQ], v[NV];
+    u32x4 q[NQ], k[NQ], v[NV];
     float g;
     int len;
   };
+  // Loads chunk m (zeros past the sequence's end) into st; every thread issues
+  // the same instructions whatever m is.
   auto load_chunk = [&](int m, Stage& st) {
-    uint4* pq = st.q;
-    uint4* pk = st.k;
-    uint4* pv = st.v;
-    const int cl = min(C, len - m * C);
+    const int cl = max(0, min(C, len - m * C));
     st.len = cl;
     const int64_t tok = (int64_t)m * C;
-    const bf16* qc = qb + tok * RSK;
-    const bf16* kc = kb + tok * RSK;
-    const bf16* vcp = vb + tok * RSV;
-    if (cl == C) {
+    const auto rq = make_rsrc(qb + tok * RSK, (uint32_t)cl * RSK * 2);
+    const auto rk = make_rsrc(kb + tok * RSK, (uint32_t)cl * RSK * 2);
+    const auto rv = make_rsrc(vb + tok * RSV, (uint32_t)cl * RSV * 2);
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        const int s = tid + i * NT;
-        const int off = (s / SEG) * RSK + (s % SEG) * 8;
-        pq[i] = *reinterpret_cast<const uint4*>(qc + off);
-        pk[i] = *reinterpret_cast<const uint4*>(kc + off);
-      }
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int s = tid + i * NT;
-        pv[i] = *reinterpret_cast<const uint4*>(vcp + (s / (VT / 8)) * RSV + (s % (VT / 8)) * 8);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        const int s = tid + i * NT;
-        const int row = s / SEG;
-        const int off = row * RSK + (s % SEG) * 8;
-        pq[i] = row < cl ? *reinterpret_cast<const uint4*>(qc + off) : make_uint4(0, 0, 0, 0);
-        pk[i] = row < cl ? *reinterpret_cast<const uint4*>(kc + off) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int s = tid + i * NT;
-        const int row = s / (VT / 8);
-        pv[i] = row < cl ? *reinterpret_cast<const uint4*>(vcp + row * RSV + (s % (VT / 8)) * 8)
-                         : make_uint4(0, 0, 0, 0);
-      }
+    for (int i = 0; i < NQ; ++i) {
+      const int s = tid + i * NT;
+      const uint32_t off = ((s / SEG) * RSK + (s % SEG) * 8) * 2;
+      st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+      st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
     }
-    // per-token log gate; rows past the chunk's end contribute 0, so their
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int s = tid + i * NT;
+      const uint32_t off = ((s / (VT / 8)) * RSV + (s % (VT / 8)) * 8) * 2;
+      st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+    }
+    // per-token log gate; rows past the chunk's end read 0, so their
     // cumulative value equals the last real token's (a finite decay for their
     // zero k and v rows)
     st.g = 0.f;
-    if (tid < C && gb != nullptr) st.g = tid < cl ? gb[(tok + tid) * H] : 0.f;
+    if (gb != nullptr) {
+      const auto rg = make_rsrc(gb + tok * H, (uint32_t)cl * H * 4);
+      st.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)(lane * H * 4), 0, 0));
+    }
   };
   auto store_chunk = [&](int p, const Stage& st) {
-    const uint4* pq = st.q;
-    const uint4* pk = st.k;
-    const uint4* pv = st.v;
     bf16* q_s = sQ(p);
     bf16* k_s = sK(p);
     bf16* v_s = sV(p);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       const int s = tid + i * NT;
-      *reinterpret_cast<uint4*>(q_s + (s / SEG) * L::LDQ + (s % SEG) * 8) = pq[i];
-      *reinterpret_cast<uint4*>(k_s + (s / SEG) * L::LDK + (s % SEG) * 8) = pk[i];
+      *reinterpret_cast<u32x4*>(q_s + (s / SEG) * L::LDQ + (s % SEG) * 8) = st.q[i];
+      *reinterpret_cast<u32x4*>(k_s + (s / SEG) * L::LDK + (s % SEG) * 8) = st.k[i];
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int s = tid + i * NT;
-      *reinterpret_cast<uint4*>(v_s + (s / (VT / 8)) * LDV + (s % (VT / 8)) * 8) = pv[i];
+      *reinterpret_cast<u32x4*>(v_s + (s / (VT / 8)) * LDV + (s % (VT / 8)) * 8) = st.v[i];
     }
-    if (tid < C) {
-      // step (1): chunk-local cumulative log2 gate b, plus the per-token
-      // factors 2^b (inter-chunk term) and 2^(b_last - b) (state update)
+    if (w == L::NW - 1) {
+      // step (1) on the last wave (it owns one A tile, the first waves two):
+      // chunk-local cumulative log2 gate b, plus the per-token factors
+      // scale * 2^b (inter-chunk term) and 2^(b_last - b) (state update)
       float* g_s = sG(p);
       const float b = gb != nullptr ? wave_cumsum_log2(st.g)
-                                    : (float)min(tid + 1, st.len) * gam2;
+                                    : (float)min(lane + 1, st.len) * gam2;
       const float blast = __shfl(b, C - 1, 64);
-      g_s[tid] = b;
-      g_s[C + tid] = exp2_hw(b);
-      g_s[2 * C + tid] = exp2_hw(blast - b);
+      g_s[lane] = b;
+      g_s[C + lane] = exp2_hw(b) * scale;
+      g_s[2 * C + lane] = exp2_hw(blast - b);
     }
   };
 
-  // output tiles of the previous chunk still to be combined and stored
-  f32x4 oown0 = {0.f, 0.f, 0.f, 0.f}, oown1 = {0.f, 0.f, 0.f, 0.f};
-  int prev_m = -1, prev_cl = 0;
-  auto finalize = [&]() {
-    // partner's q.h partial for this wave's two c tiles, then scale and store
-    const f32x4 x0 = sX[((w ^ 4) * 2 + 0) * 64 + lane];
-    const f32x4 x1 = sX[((w ^ 4) * 2 + 1) * 64 + lane];
-    TOut* oc = ob + (int64_t)prev_m * C * RSV;
-    const int c0 = 16 * own0 + r, c1 = 16 * own1 + r;
-    if (c0 < prev_cl) store4(oc + (int64_t)c0 * RSV, (oown0 + x0) * scale);
-    if (c1 < prev_cl) store4(oc + (int64_t)c1 * RSV, (oown1 + x1) * scale);
-  };
-
-  Stage st0, st1;
-  if (nchunks > 0) load_chunk(0, st0);
-  if (L::PF2 && nchunks > 1) load_chunk(1, st1);
-
-  // one chunk: stage it, then A, q.h, state update, A v and the exchange
-  auto body = [&](const int m, const int p, Stage& st) {
-    const int cl = st.len;
-    store_chunk(p, st);
-    __syncthreads();   // chunk m staged; previous chunk's exchange tiles visible
-    if (L::DB && prev_m >= 0) finalize();
-    const int next = m + (L::PF2 ? 2 : 1);
-    if (next < nchunks) load_chunk(next, st);
+  // ---- per-chunk phases ----------------------------------------------------
+  // A = (Q K^T) (.) M, split into bf16 hi + lo, into sA(p)
+  auto phase_A = [&](int p) {
     const bf16* q_s = sQ(p);
     const bf16* k_s = sK(p);
-    const bf16* v_s = sV(p);
     const float* g_s = sG(p);
     bf16* a_hi = sA(p);
     bf16* a_lo = a_hi + C * LDA;
-
-    // ---- A = (Q K^T) (.) M, split into bf16 hi + lo, into LDS ------------
     for (int ti = w; ti < 10; ti += L::NW) {
-      const int ct = kTileC[ti], jt = kTileJ[ti];
+      const int ct = tile_c(ti), jt = tile_j(ti);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < L::KSF; ++s) {
@@ -366,21 +371,26 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       }
       const int c = 16 * ct + r;
       const float bc = g_s[c];
-      bf16x4 hi, lo;
+      const f32x4 bj = *reinterpret_cast<const f32x4*>(g_s + 16 * jt + 4 * g4);
+      float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 16 * jt + 4 * g4 + i;
-        const float x = (j <= c) ? acc[i] * exp2_hw(bc - g_s[j]) : 0.f;
-        const bf16 hv = (bf16)x;
-        hi[i] = hv;
-        lo[i] = (bf16)(x - (float)hv);
+        x[i] = (j <= c) ? acc[i] * exp2_hw(bc - bj[i]) * scale : 0.f;
       }
-      *reinterpret_cast<bf16x4*>(a_hi + c * LDA + 16 * jt + 4 * g4) = hi;
-      *reinterpret_cast<bf16x4*>(a_lo + c * LDA + 16 * jt + 4 * g4) = lo;
+      uint32_t h0, l0, h1, l1;
+      split2(x[0], x[1], h0, l0);
+      split2(x[2], x[3], h1, l1);
+      const u32x2 hi = {h0, h1}, lo = {l0, l1};
+      *reinterpret_cast<u32x2*>(a_hi + c * LDA + 16 * jt + 4 * g4) = hi;
+      *reinterpret_cast<u32x2*>(a_lo + c * LDA + 16 * jt + 4 * g4) = lo;
     }
-
-    // ---- O^T partial = h^T Q^T over this wave's K/2 state rows -----------
-    f32x4 oacc[4];
+  };
+  // O^T partial = scale diag(2^b) (h^T Q^T) over this wave's K/2 state rows,
+  // for c tiles in the order (own0, own1, partner's two)
+  auto phase_inter = [&](int p, f32x4 (&oacc)[4]) {
+    const bf16* q_s = sQ(p);
+    const float* g_s = sG(p);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -397,113 +407,168 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       split8(x, hh, hl);
       bf16x8 b[4];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const bf16* qrow = q_s + (16 * ct + r) * L::LDQ + krow0 + 32 * s + 4 * g4;
-        b[ct] = cat(*reinterpret_cast<const bf16x4*>(qrow), *reinterpret_cast<const bf16x4*>(qrow + 16));
+      for (int t = 0; t < 4; ++t) {
+        const bf16* qrow = q_s + (16 * ctile[t] + r) * L::LDQ + krow0 + 32 * s + 4 * g4;
+        b[t] = cat(*reinterpret_cast<const bf16x4*>(qrow), *reinterpret_cast<const bf16x4*>(qrow + 16));
       }
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) oacc[ct] = mfma(hh, b[ct], oacc[ct]);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) oacc[ct] = mfma(hl, b[ct], oacc[ct]);
     }
-    // diag(2^b): O^T column c = 16ct + r
+    // scale * diag(2^b): O^T column c = 16 ctile + r
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) oacc[ct] *= g_s[C + 16 * ct + r];
-
-    // ---- h <- 2^b_last h + K^T (diag(2^(b_last - b)) V), own rows ---------
-    // V fragments vf[s][e] = V[32s + 8g + e][16vc + r]
-    bf16x8 vf[2];
+    for (int t = 0; t < 4; ++t) oacc[t] *= g_s[C + 16 * ctile[t] + r];
+  };
+  // V fragments vf[s][e] = V[32s + 8g + e][16vc + r]
+  auto load_vf = [&](int p, bf16x8 (&vf)[2]) {
+    const bf16* v_s = sV(p);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       vf[s] = cat(tr_read(v_s, LDV, 32 * s + 8 * g4, 16 * vc),
                   tr_read(v_s, LDV, 32 * s + 8 * g4 + 4, 16 * vc));
-    {
-      const float dall = g_s[C + C - 1];   // 2^b_last
+  };
+  // h <- 2^b_last h + K^T (diag(2^(b_last - b)) V) for this wave's rows
+  auto phase_update = [&](int p, const bf16x8 (&vf)[2]) {
+    const bf16* k_s = sK(p);
+    const float* g_s = sG(p);
+    const float dall = exp2_hw(g_s[C - 1]);   // 2^b_last
 #pragma unroll
-      for (int kt = 0; kt < L::KT; ++kt) h[kt] *= dall;
-      bf16x8 vth[2], vtl[2];
+    for (int kt = 0; kt < L::KT; ++kt) h[kt] *= dall;
+    bf16x8 vth[2], vtl[2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(g_s + 2 * C + 32 * s + 8 * g4);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(g_s + 2 * C + 32 * s + 8 * g4 + 4);
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] = (float)vf[s][e] * d0[e];
-          x[4 + e] = (float)vf[s][4 + e] * d1[e];
-        }
-        split8(x, vth[s], vtl[s]);
-      }
-      constexpr int KG = L::KT < 4 ? L::KT : 4;   // state tiles per MFMA group
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int k0 = 0; k0 < L::KT; k0 += KG) {
-          // A operands: K^T[krow0 + 16kt + r][32s + 8g + e]
-          bf16x8 a[KG];
-#pragma unroll
-          for (int u = 0; u < KG; ++u)
-            a[u] = cat(tr_read(k_s, L::LDK, 32 * s + 8 * g4, krow0 + 16 * (k0 + u)),
-                       tr_read(k_s, L::LDK, 32 * s + 8 * g4 + 4, krow0 + 16 * (k0 + u)));
-#pragma unroll
-          for (int u = 0; u < KG; ++u) h[k0 + u] = mfma(a[u], vth[s], h[k0 + u]);
-#pragma unroll
-          for (int u = 0; u < KG; ++u) h[k0 + u] = mfma(a[u], vtl[s], h[k0 + u]);
-        }
-      }
+    for (int s = 0; s < 2; ++s) {
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(g_s + 2 * C + 32 * s + 8 * g4);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(g_s + 2 * C + 32 * s + 8 * g4 + 4);
+      const u32x4 raw = __builtin_bit_cast(u32x4, vf[s]);
+      float x[8];
+      x[0] = bf_lo(raw[0]) * d0[0];
+      x[1] = bf_hi(raw[0]) * d0[1];
+      x[2] = bf_lo(raw[1]) * d0[2];
+      x[3] = bf_hi(raw[1]) * d0[3];
+      x[4] = bf_lo(raw[2]) * d1[0];
+      x[5] = bf_hi(raw[2]) * d1[1];
+      x[6] = bf_lo(raw[3]) * d1[2];
+      x[7] = bf_hi(raw[3]) * d1[3];
+      split8(x, vth[s], vtl[s]);
     }
-    __syncthreads();   // A complete
-
-    // ---- O^T += V^T A^T for this wave's two c tiles ------------------------
-    // own tiles: kh = 0 -> c tiles 0 (j < 32) and 3 (j < 64);
-    //            kh = 1 -> c tiles 1 (j < 32) and 2 (j < 64)
-    const bool hi_half = kh != 0;
-    f32x4 mine0 = hi_half ? oacc[1] : oacc[0];
-    f32x4 mine1 = hi_half ? oacc[2] : oacc[3];
-    const f32x4 give0 = hi_half ? oacc[0] : oacc[1];
-    const f32x4 give1 = hi_half ? oacc[3] : oacc[2];
-    {
-      const bf16* ah0 = a_hi + (16 * own0 + r) * LDA + 8 * g4;
-      const bf16* ah1 = a_hi + (16 * own1 + r) * LDA + 8 * g4;
-      const bf16x8 p0h = *reinterpret_cast<const bf16x8*>(ah0);
-      const bf16x8 p0l = *reinterpret_cast<const bf16x8*>(ah0 + C * LDA);
-      const bf16x8 p1h = *reinterpret_cast<const bf16x8*>(ah1);
-      const bf16x8 p1l = *reinterpret_cast<const bf16x8*>(ah1 + C * LDA);
-      const bf16x8 p2h = *reinterpret_cast<const bf16x8*>(ah1 + 32);
-      const bf16x8 p2l = *reinterpret_cast<const bf16x8*>(ah1 + 32 + C * LDA);
-      mine0 = mfma(vf[0], p0h, mine0);
-      mine1 = mfma(vf[0], p1h, mine1);
-      mine0 = mfma(vf[0], p0l, mine0);
-      mine1 = mfma(vf[0], p1l, mine1);
-      mine1 = mfma(vf[1], p2h, mine1);
-      mine1 = mfma(vf[1], p2l, mine1);
-    }
-    if (!L::DB) __syncthreads();   // Q area is about to hold exchange tiles
-    // partner's c tiles go through LDS
-    sX[(w * 2 + 0) * 64 + lane] = give0;
-    sX[(w * 2 + 1) * 64 + lane] = give1;
-    oown0 = mine0;
-    oown1 = mine1;
-    prev_m = m;
-    prev_cl = cl;
-    if (!L::DB) {
-      __syncthreads();
-      finalize();
-      __syncthreads();   // exchange tiles read before the next chunk is staged
+    constexpr int KG = L::KT < 4 ? L::KT : 4;   // state tiles per MFMA group
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int k0 = 0; k0 < L::KT; k0 += KG) {
+        // A operands: K^T[krow0 + 16kt + r][32s + 8g + e]
+        bf16x8 a[KG];
+#pragma unroll
+        for (int u = 0; u < KG; ++u)
+          a[u] = cat(tr_read(k_s, L::LDK, 32 * s + 8 * g4, krow0 + 16 * (k0 + u)),
+                     tr_read(k_s, L::LDK, 32 * s + 8 * g4 + 4, krow0 + 16 * (k0 + u)));
+#pragma unroll
+        for (int u = 0; u < KG; ++u) h[k0 + u] = mfma(a[u], vth[s], h[k0 + u]);
+#pragma unroll
+        for (int u = 0; u < KG; ++u) h[k0 + u] = mfma(a[u], vtl[s], h[k0 + u]);
+      }
     }
   };
+  // own c tiles: kh = 0 -> c tiles 0 (j < 32) and 3 (j < 64);
+  //              kh = 1 -> c tiles 1 (j < 32) and 2 (j < 64)
+  // O^T (own tiles) += V^T A^T with A from sA(p)
+  auto phase_intra = [&](int p, const bf16x8 (&vf)[2], f32x4& mine0, f32x4& mine1) {
+    const bf16* ah0 = sA(p) + (16 * own0 + r) * LDA + 8 * g4;
+    const bf16* ah1 = sA(p) + (16 * own1 + r) * LDA + 8 * g4;
+    const bf16x8 p0h = *reinterpret_cast<const bf16x8*>(ah0);
+    const bf16x8 p0l = *reinterpret_cast<const bf16x8*>(ah0 + C * LDA);
+    const bf16x8 p1h = *reinterpret_cast<const bf16x8*>(ah1);
+    const bf16x8 p1l = *reinterpret_cast<const bf16x8*>(ah1 + C * LDA);
+    const bf16x8 p2h = *reinterpret_cast<const bf16x8*>(ah1 + 32);
+    const bf16x8 p2l = *reinterpret_cast<const bf16x8*>(ah1 + 32 + C * LDA);
+    mine0 = mfma(vf[0], p0h, mine0);
+    mine1 = mfma(vf[0], p1h, mine1);
+    mine0 = mfma(vf[0], p0l, mine0);
+    mine1 = mfma(vf[0], p1l, mine1);
+    mine1 = mfma(vf[1], p2h, mine1);
+    mine1 = mfma(vf[1], p2l, mine1);
+  };
+  // the partner's two c tiles of this wave's q.h partial go through LDS
+  auto exchange_write = [&](int px, const f32x4 (&oacc)[4]) {
+    f32x4* x = sX(px);
+    x[(w * 2 + 0) * 64 + lane] = oacc[2];
+    x[(w * 2 + 1) * 64 + lane] = oacc[3];
+  };
+  // own tiles + partner's partial, scaled, stored (rows past the chunk's end
+  // fall outside the descriptor and are dropped; cl = 0 stores nothing)
+  auto finalize = [&](int px, int m, int cl, f32x4 mine0, f32x4 mine1) {
+    const f32x4* x = sX(px);
+    const f32x4 x0 = x[((w ^ 4) * 2 + 0) * 64 + lane];
+    const f32x4 x1 = x[((w ^ 4) * 2 + 1) * 64 + lane];
+    const auto ro = make_rsrc(ob + (int64_t)m * C * RSV, (uint32_t)cl * RSV * sizeof(TOut));
+    const uint32_t c0 = 16 * own0 + r, c1 = 16 * own1 + r;
+    store4<TOut>(ro, c0 * RSV * (uint32_t)sizeof(TOut) + ocol, mine0 + x0);
+    store4<TOut>(ro, c1 * RSV * (uint32_t)sizeof(TOut) + ocol, mine1 + x1);
+  };
 
-  if (L::PF2) {
-    for (int m = 0; m < nchunks; m += 2) {
-      body(m, 0, st0);
-      if (m + 1 < nchunks) body(m + 1, 1, st1);
+  Stage st0, st1;
+  load_chunk(0, st0);
+  if (L::PF2) load_chunk(1, st1);
+
+  if constexpr (L::DB) {
+    // Pipelined: one barrier per chunk.  Iteration m stages chunk m, then
+    // finishes chunk m-1 (A V and the output store, from buffers of parity
+    // p^1 and registers carried over) and forms chunk m's A, q.h partials
+    // and state update.
+    bf16x8 vf_prev[2] = {};
+    f32x4 mine0 = {0.f, 0.f, 0.f, 0.f}, mine1 = {0.f, 0.f, 0.f, 0.f};
+    int prev_m = 0, prev_cl = 0;   // prev_cl = 0: nothing to store yet
+    auto step = [&](const int m, const int p, Stage& st) {
+      const int cl = st.len;
+      store_chunk(p, st);
+      __syncthreads();   // chunk m staged; chunk m-1's A and exchange tiles visible
+      phase_intra(p ^ 1, vf_prev, mine0, mine1);
+      finalize(p ^ 1, prev_m, prev_cl, mine0, mine1);
+      load_chunk(m + 2, st);
+      phase_A(p);
+      f32x4 oacc[4];
+      phase_inter(p, oacc);
+      exchange_write(p, oacc);
+      mine0 = oacc[0];
+      mine1 = oacc[1];
+      load_vf(p, vf_prev);
+      phase_update(p, vf_prev);
+      prev_m = m;
+      prev_cl = cl;
+    };
+    int m = 0;
+    for (; m + 1 < nchunks; m += 2) {
+      step(m, 0, st0);
+      step(m + 1, 1, st1);
     }
-  } else {
-    for (int m = 0; m < nchunks; ++m) body(m, L::DB ? (m & 1) : 0, st0);
-  }
-  if (L::DB && prev_m >= 0) {
+    if (m < nchunks) step(m, 0, st0);
     __syncthreads();
-    finalize();
+    const int pl = (nchunks - 1) & 1;
+    phase_intra(pl, vf_prev, mine0, mine1);
+    finalize(pl, prev_m, prev_cl, mine0, mine1);
+  } else {
+    for (int m = 0; m < nchunks; ++m) {
+      const int cl = st0.len;
+      store_chunk(0, st0);
+      __syncthreads();   // chunk m staged
+      load_chunk(m + 1, st0);
+      phase_A(0);
+      f32x4 oacc[4];
+      phase_inter(0, oacc);
+      bf16x8 vf[2];
+      load_vf(0, vf);
+      phase_update(0, vf);
+      __syncthreads();   // A complete
+      f32x4 mine0 = oacc[0];
+      f32x4 mine1 = oacc[1];
+      phase_intra(0, vf, mine0, mine1);
+      __syncthreads();   // Q area is about to hold exchange tiles
+      exchange_write(0, oacc);
+      __syncthreads();
+      finalize(0, m, cl, mine0, mine1);
+      __syncthreads();   // exchange tiles read before the next chunk is staged
+    }
   }
 
   if (ht != nullptr) {
