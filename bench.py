@@ -6,8 +6,10 @@ inter-chunk state pass and output pass -- one fused kernel launch) over one
 batch of the dense bf16 prefill workload: B=4, T=2048, H=4, K=V=512, q/k/v
 ~ N(0,1) in bf16, g = logsigmoid(N(0,1)), scale 1/sqrt(K), chunk 64, fp32 o,
 final state written.  ``value`` is tokens/s over the K timed steps with all
-inputs already resident in HBM (three input/output copies are rotated so the
-256 MB last-level cache cannot hold a step's working set).
+inputs already resident in HBM (input/output copies are rotated so the 256 MB
+last-level cache cannot hold a step's working set).  Before the counted
+warmup steps the device runs untimed steps for --warm-seconds (default 1 s) so
+the timed steps see steady-state clocks.
 
 The JSON line also carries:
   roofline      -- the fused chunk kernel against its bound (HBM for this
@@ -99,7 +101,23 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def bench_chunk(workload: str, steps: int, warmup: int):
+def warm_device(fn, seconds: float):
+    """Run untimed work for ``seconds`` so clocks reach their steady state
+    before the counted warmup and timed steps."""
+    import torch
+    if seconds <= 0:
+        return
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def bench_chunk(workload: str, steps: int, warmup: int, warm_seconds: float):
     import ctypes
 
     import numpy as np
@@ -147,6 +165,7 @@ def bench_chunk(workload: str, steps: int, warmup: int):
         if st != 0:
             raise RuntimeError(f"sgla_chunk_fwd failed: {sgla.lib.sgla_last_error().decode()}")
 
+    warm_device(step, warm_seconds)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -173,7 +192,7 @@ def bench_chunk(workload: str, steps: int, warmup: int):
                 ncopies=ncopies)
 
 
-def bench_decode(steps_timed: int, warmup: int):
+def bench_decode(steps_timed: int, warmup: int, warm_seconds: float):
     import numpy as np
     import torch
 
@@ -189,6 +208,8 @@ def bench_decode(steps_timed: int, warmup: int):
     q, k, v, g = (t(inp["q"], torch.bfloat16), t(inp["k"], torch.bfloat16),
                   t(inp["v"], torch.bfloat16), t(inp["g"], torch.float32))
     o = torch.empty((N, H, V), device=dev, dtype=torch.float32)
+    warm_device(lambda i: sgla.recurrent_step(q[i % S], k[i % S], v[i % S], g[i % S], state,
+                                              scale=inp["scale"], out=o), warm_seconds)
     for i in range(warmup):
         sgla.recurrent_step(q[i % S], k[i % S], v[i % S], g[i % S], state, scale=inp["scale"], out=o)
     stream = torch.cuda.current_stream(dev)
@@ -236,6 +257,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_bf16_k512",
                     help="chunked workload to time (default: the dense bf16 K=V=512 prefill)")
+    ap.add_argument("--warm-seconds", type=float, default=1.0,
+                    help="untimed device warm-up before the counted warmup steps")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     a = ap.parse_args()
@@ -249,7 +272,7 @@ def main():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(2)
 
-    r = bench_chunk(a.workload, a.steps, a.warmup)
+    r = bench_chunk(a.workload, a.steps, a.warmup, a.warm_seconds)
     inp = r["inp"]
     tokens = inp["B"] * inp["T"]
     ms_step = r["total_ms"] / a.steps
@@ -298,7 +321,7 @@ def main():
                  "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)},
     }
     if not a.no_decode:
-        out["decode"] = bench_decode(64, a.warmup)
+        out["decode"] = bench_decode(64, a.warmup, a.warm_seconds)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)

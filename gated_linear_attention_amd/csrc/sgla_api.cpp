@@ -68,8 +68,10 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
     if (a->qkv_dtype == SGLA_BF16) {
       if (!(a->K == 64 || a->K == 128 || a->K == 256 || a->K == 512))
         return fail(SGLA_ERR_UNSUPPORTED, "bf16 inputs support K in {64,128,256,512} (got %d)", a->K);
-      if (a->V % 64 != 0)
-        return fail(SGLA_ERR_UNSUPPORTED, "bf16 inputs support V a multiple of 64 (got %d)", a->V);
+      const int vmul = a->K >= 256 ? 32 : 64;
+      if (a->V % vmul != 0)
+        return fail(SGLA_ERR_UNSUPPORTED, "bf16 inputs with K=%d support V a multiple of %d (got %d)",
+                    a->K, vmul, a->V);
     } else if (a->qkv_dtype == SGLA_F32) {
       if (!(a->K == 16 || a->K == 32 || a->K == 64 || a->K == 128))
         return fail(SGLA_ERR_UNSUPPORTED, "float32 inputs support K in {16,32,64,128} (got %d)", a->K);
@@ -220,8 +222,9 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
   p.o_bf16 = a.o_dtype == SGLA_BF16;
   p.seqs = L;
   if (p.ht == nullptr && !any_tokens) return ok();
-  hipError_t e = a.qkv_dtype == SGLA_BF16 ? sgla::launch_chunk_fwd_bf16(p, stream)
-                                          : sgla::launch_chunk_fwd_f32(p, stream);
+  hipError_t e = a.qkv_dtype != SGLA_BF16 ? sgla::launch_chunk_fwd_f32(p, stream)
+                 : a.K >= 256            ? sgla::launch_chunk_fwd_bf16_ks(p, stream)
+                                         : sgla::launch_chunk_fwd_bf16(p, stream);
   if (e != hipSuccess) return hip_fail(e, "launching the chunk kernel");
   return ok();
 }

@@ -54,8 +54,13 @@ struct ChunkFwdParams {
 hipError_t launch_gate_cumsum(const float* g, float* gc, int32_t H, const SeqLayout& seqs,
                               hipStream_t stream);
 
-// bf16 q/k/v, MFMA path.  K in {64,128,256,512}, V % 64 == 0.
+// bf16 q/k/v, MFMA path, whole key dimension per chunk step.  K in {64,128},
+// V % 64 == 0.
 hipError_t launch_chunk_fwd_bf16(const ChunkFwdParams& p, hipStream_t stream);
+
+// bf16 q/k/v, MFMA path, key dimension streamed in 128-wide slices.  K in
+// {256,512}, V % 32 == 0.
+hipError_t launch_chunk_fwd_bf16_ks(const ChunkFwdParams& p, hipStream_t stream);
 
 // float32 q/k/v, VALU path.  K in {16,32,64,128}, V % 32 == 0.
 hipError_t launch_chunk_fwd_f32(const ChunkFwdParams& p, hipStream_t stream);

@@ -112,7 +112,8 @@ size_t sgla_chunk_fwd_workspace_size(const sgla_chunk_args *args, const int64_t 
  *                   exactly (in-place state update); no other aliasing.
  *   workspace       device buffer of at least workspace_bytes >=
  *                   sgla_chunk_fwd_workspace_size(args, cu_seqlens_host).
- * Supported: K in {64, 128, 256, 512} and V a multiple of 64 (bf16 inputs);
+ * Supported: K in {64, 128} with V a multiple of 64, or K in {256, 512}
+ * with V a multiple of 32 (bf16 inputs);
  * K in {16, 32, 64, 128} and V a multiple of 32 (float32 inputs);
  * chunk_size 64.  Other powers of two are valid requests that return
  * SGLA_ERR_UNSUPPORTED; a chunk_size that is not a power of two is

@@ -120,6 +120,7 @@ CASES = [
     ("chunk 32 unsupported", dict(chunk=32), {}, UNSUPPORTED, "chunk_size"),
     ("bf16 K=96", dict(K=96), {}, UNSUPPORTED, "K in"),
     ("bf16 V=96", dict(V=96), {}, UNSUPPORTED, "V a multiple"),
+    ("bf16 K=512 V=48", dict(K=512, V=48), {}, UNSUPPORTED, "V a multiple"),
     ("f32 K=256", dict(qkv=F32, K=256), {}, UNSUPPORTED, "K in"),
     ("f32 V=48", dict(qkv=F32, V=48), {}, UNSUPPORTED, "V a multiple"),
     ("fp16 inputs", dict(qkv=3), {}, DTYPE, "qkv_dtype"),

@@ -90,6 +90,10 @@ SMALL_CASES = [
     small("ragged_k128_v128", K=128, V=128, T=131),
     small("k256_v64", K=256, V=64, T=150, H=2),
     small("k512_v128", K=512, V=128, T=140, B=1, H=2),
+    small("k512_v96_varlen", B=1, T=0, H=2, K=512, V=96, fixed_lengths=(70, 1, 0, 130),
+          initial_state=True),
+    small("k256_v32_gamma", K=256, V=32, gate="gamma", T=200, normalize_k=True),
+    small("k256_v64_t64", K=256, V=64, T=64, initial_state=True),
     small("v192_multi_tile", K=64, V=192, T=97),
     small("gamma", gate="gamma", K=128, V=128, T=300, normalize_k=True),
     small("no_gate", gate="none", K=64, V=64, T=129),
