@@ -88,6 +88,13 @@ def chunk_algorithmic(inp) -> tuple[float, float]:
     return float(nbytes), float(flops)
 
 
+def chunk_kernel_name(inp) -> str:
+    """The kernel sgla_chunk_fwd dispatches for these inputs."""
+    if inp["dtype"] != "bf16":
+        return "chunk_fwd_f32_kernel"
+    return "chunk_fwd_bf16_ks_kernel" if inp["K"] >= 256 else "chunk_fwd_bf16_kernel"
+
+
 def load_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources."""
@@ -230,24 +237,52 @@ def bench_decode(steps_timed: int, warmup: int, warm_seconds: float):
             "bytes_per_step": nbytes, "achieved_GBs": round(gbs, 1),
             "peak_GBs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
             "tokens_per_s": round(N / (mean_ms * 1e-3), 1),
-            "traffic": load_traffic(w.name, "recurrent_step")}
+            "traffic": load_traffic(w.name, "recurrent_step_kernel")}
 
 
-def cpu_baseline(inp):
+def cpu_baseline(inp, min_seconds: float = 10.0):
+    """The fp64 CPU oracle on whole batches of the timed workload, repeated
+    until at least ``min_seconds`` of wall time (a bounded sample)."""
     import oracle
     threads = oracle.default_threads()
+    units = inp["N"] * inp["H"]
+    reps = 0
     t0 = time.perf_counter()
-    oracle.fwd(inp["q"], inp["k"], inp["v"], g=inp["g"], g_gamma=inp["g_gamma"],
-               scale=inp["scale"], initial_state=inp["initial_state"],
-               cu_seqlens=inp["cu_seqlens"], output_final_state=inp["output_final_state"],
-               nthreads=threads)
-    dt = time.perf_counter() - t0
-    tokens = inp["B"] * inp["T"]
-    return {"value": round(tokens / dt, 2), "unit": "tokens/s", "cores": threads,
+    while True:
+        oracle.fwd(inp["q"], inp["k"], inp["v"], g=inp["g"], g_gamma=inp["g_gamma"],
+                   scale=inp["scale"], initial_state=inp["initial_state"],
+                   cu_seqlens=inp["cu_seqlens"], output_final_state=inp["output_final_state"],
+                   nthreads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    tokens = inp["B"] * inp["T"] * reps
+    return {"value": round(tokens / dt, 2), "unit": "tokens/s", "cores": min(threads, units),
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"one full batch of the timed workload (B={inp['B']}, T={inp['T']}, "
-                      f"H={inp['H']}, K={inp['K']}, V={inp['V']}: all "
-                      f"{inp['N'] * inp['H']} sequence-head units), fp64 token-by-token"}
+            "sample": f"{reps} repetitions of one full batch of the timed workload "
+                      f"(B={inp['B']}, T={inp['T']}, H={inp['H']}, K={inp['K']}, V={inp['V']}: "
+                      f"{units} sequence-head units, one per thread), fp64 token-by-token"}
+
+
+COPY_BYTES = 512 << 20
+
+
+def calibrate_copy(reps: int = 3):
+    """A plain copy of COPY_BYTES: reads and writes exactly that many bytes of
+    HBM per launch (twice the 256 MB last-level cache, so neither side can be
+    absorbed by it)."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, device=dev, dtype=torch.float32)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        # an elementwise kernel (not a DMA memcpy) so the counters see it
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_launch": COPY_BYTES,
+                      "bytes_written_per_launch": COPY_BYTES, "launches": reps}), flush=True)
 
 
 def main():
@@ -261,6 +296,9 @@ def main():
                     help="untimed device warm-up before the counted warmup steps")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device-to-device copy of known size (the reference "
+                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {a.gpus} is not supported (every "
@@ -272,6 +310,9 @@ def main():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(2)
 
+    if a.calibrate_copy:
+        calibrate_copy()
+        return
     r = bench_chunk(a.workload, a.steps, a.warmup, a.warm_seconds)
     inp = r["inp"]
     tokens = inp["B"] * inp["T"]
@@ -288,9 +329,8 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
-    roof["traffic"] = load_traffic(a.workload, "chunk_fwd")
-    roof.update({"kernel": "chunk_fwd_bf16_kernel" if inp["dtype"] == "bf16"
-                 else "chunk_fwd_f32_kernel",
+    roof["traffic"] = load_traffic(a.workload, chunk_kernel_name(inp))
+    roof.update({"kernel": chunk_kernel_name(inp),
                  "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
                  "kernel_ms_median": round(r["kernel_ms_median"], 5),
                  "algorithmic_bytes_per_launch": int(r["alg_bytes"]),

@@ -64,6 +64,11 @@ def load(path: str | None = None):
 
 
 def default_threads() -> int:
+    """Worker threads: OMP_NUM_THREADS when set (the host's share of cores),
+    else the CPUs this process may run on."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
     try:
         return max(1, len(os.sched_getaffinity(0)))
     except AttributeError:  # pragma: no cover

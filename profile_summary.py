@@ -1,0 +1,141 @@
+#!/usr/bin/env python3
+"""Turn rocprofv3 CSV output of bench.py runs into the short text summaries
+kept under profiles/ and the per-launch HBM traffic record bench.py reads.
+
+  python profile_summary.py trace   --dir D --kernel REGEX --steps N --out F --command CMD
+      kernel-trace statistics of every kernel in D, plus the mean duration of
+      the last N dispatches of the kernel matching REGEX (bench.py's timed
+      launches) -- the figure to compare with bench.py's HIP-event timing.
+
+  python profile_summary.py traffic --fetch D1 --write D2 --calib-fetch D3 --calib-write D4
+                                    --kernel REGEX --name KERNEL --workload W --out-json J
+                                    --out-txt F --command CMD [--command CMD ...]
+      FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernel, each scaled
+      by the ratio of known bytes to the same counter's reading for a plain
+      elementwise copy of 512 MiB (bench.py --calibrate-copy).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import re
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def _rows(d: str, suffix: str):
+    files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        sys.exit(f"no *{suffix} under {d}")
+    out = []
+    for fn in files:
+        with open(fn, newline="") as f:
+            out.extend(csv.DictReader(f))
+    return out
+
+
+def trace(a):
+    rows = _rows(a.dir, "kernel_trace.csv")
+    by = {}
+    for r in rows:
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        by.setdefault(r["Kernel_Name"], []).append((int(r["Start_Timestamp"]), dur))
+    lines = [f"# rocprofv3 kernel trace: {a.title}", "", "Command (from the repository root):", "",
+             f"    {a.command}", "",
+             "| kernel | dispatches | mean us | median us | min us | max us |", "|---|---|---|---|---|---|"]
+    pat = re.compile(a.kernel)
+    timed = None
+    for name, v in sorted(by.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        durs = [d / 1e3 for _, d in v]
+        short = name if len(name) < 110 else name[:107] + "..."
+        lines.append(f"| `{short}` | {len(durs)} | {statistics.mean(durs):.2f} | "
+                     f"{statistics.median(durs):.2f} | {min(durs):.2f} | {max(durs):.2f} |")
+        if pat.search(name):
+            last = [d / 1e3 for _, d in sorted(v)[-a.steps:]]
+            timed = (name, len(last), statistics.mean(last), statistics.median(last))
+    if timed is None:
+        sys.exit(f"no kernel matches {a.kernel}")
+    lines += ["", f"Timed launches (the last {timed[1]} dispatches of the kernel matching "
+              f"`{a.kernel}`, i.e. the ones bench.py times after its warm-up): "
+              f"mean {timed[2]:.2f} us, median {timed[3]:.2f} us.", ""]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def _counter(d: str, kernel: str, counter: str):
+    pat = re.compile(kernel)
+    vals = {}
+    for r in _rows(d, "counter_collection.csv"):
+        if r["Counter_Name"] == counter and pat.search(r["Kernel_Name"]):
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    if not vals:
+        sys.exit(f"no {counter} rows for {kernel} under {d}")
+    return list(vals.values())
+
+
+def traffic(a):
+    copy_bytes = 512 << 20
+    fetch = _counter(a.fetch, a.kernel, "FETCH_SIZE")
+    write = _counter(a.write, a.kernel, "WRITE_SIZE")
+    cf = _counter(a.calib_fetch, a.calib_kernel, "FETCH_SIZE")
+    cw = _counter(a.calib_write, a.calib_kernel, "WRITE_SIZE")
+    f_fetch = copy_bytes / (statistics.median(cf) * 1024.0)
+    f_write = copy_bytes / (statistics.median(cw) * 1024.0)
+    rd = statistics.median(fetch) * 1024.0 * f_fetch
+    wr = statistics.median(write) * 1024.0 * f_write
+    sys.path.insert(0, ROOT)
+    from bench import kernel_source_hash
+    rec = {"kernel": a.name, "workload": a.workload, "hbm_bytes_per_launch": round(rd + wr),
+           "read_bytes_per_launch": round(rd), "write_bytes_per_launch": round(wr),
+           "fetch_size_kib_median": statistics.median(fetch),
+           "write_size_kib_median": statistics.median(write), "dispatches": len(fetch),
+           "copy_calibration": {"bytes": copy_bytes, "fetch_size_kib": statistics.median(cf),
+                                "write_size_kib": statistics.median(cw),
+                                "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)},
+           "kernel_source_hash": kernel_source_hash()}
+    with open(a.out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = [f"# HBM traffic of {a.name} on {a.workload} (rocprofv3 counters)", "",
+             "Commands (from the repository root; one counter per run):", ""]
+    lines += [f"    {c}" for c in a.command]
+    lines += ["", f"- dispatches of the kernel: {len(fetch)}; FETCH_SIZE median "
+              f"{statistics.median(fetch):.0f} KiB, WRITE_SIZE median {statistics.median(write):.0f} KiB",
+              f"- copy calibration (elementwise copy of {copy_bytes} B): FETCH_SIZE "
+              f"{statistics.median(cf):.0f} KiB, WRITE_SIZE {statistics.median(cw):.0f} KiB -> "
+              f"factors {f_fetch:.4f} (fetch), {f_write:.4f} (write)",
+              f"- scaled HBM bytes per launch: read {rd / 1e6:.2f} MB + write {wr / 1e6:.2f} MB = "
+              f"{(rd + wr) / 1e6:.2f} MB", f"- kernel source hash: {rec['kernel_source_hash']}", ""]
+    with open(a.out_txt, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = ap.add_subparsers(dest="mode", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("--dir", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--steps", type=int, required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--title", required=True)
+    t.add_argument("--command", required=True)
+    c = sub.add_parser("traffic")
+    for k in ("fetch", "write", "calib_fetch", "calib_write", "kernel", "name", "workload",
+              "out_json", "out_txt"):
+        c.add_argument("--" + k.replace("_", "-"), required=True)
+    c.add_argument("--calib-kernel", default="Mul")
+    c.add_argument("--command", action="append", required=True)
+    a = ap.parse_args()
+    trace(a) if a.mode == "trace" else traffic(a)
+
+
+if __name__ == "__main__":
+    main()
