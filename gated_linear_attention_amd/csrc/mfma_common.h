@@ -31,6 +31,14 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_32x32x16_bf16, per lane l with h = l / 32 and n = l % 32:
+//   A operand: A[m = n][k = 8h + 0..7]     B operand: B[k = 8h + 0..7][n]
+//   result   : acc[4j + i] = D[m = 8j + 4h + i][n], j, i = 0..3
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // 2^x with the hardware v_exp_f32 (results below 2^-126 may flush to zero,
 // far below any contribution that matters at fp32 accumulation).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }

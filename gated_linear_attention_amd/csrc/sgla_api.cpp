@@ -51,7 +51,8 @@ struct Plan {
   bool packed = false;
   std::vector<sgla::SeqEntry> seqs;      // packed only, longest first
   std::vector<sgla::ChunkEntry> chunks;  // packed only
-  size_t seq_off = 0, chunk_off = 0, total_bytes = 0;
+  bool prep = false;                     // wide-key bf16 path: per-chunk preparation buffers
+  size_t seq_off = 0, chunk_off = 0, gate_off = 0, amat_off = 0, total_bytes = 0;
 };
 
 sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv_support,
@@ -105,8 +106,10 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
       e.bos = (int32_t)cu[n];
       e.len = (int32_t)(cu[n + 1] - cu[n]);
       e.seq = n;
-      e.pad = 0;
+      e.chunk0 = 0;
     }
+    for (int32_t n = 1; n < P->N; ++n)
+      P->seqs[n].chunk0 = P->seqs[n - 1].chunk0 + (P->seqs[n - 1].len + sgla::kChunk - 1) / sgla::kChunk;
     // longest sequences first: they bound the critical path
     std::stable_sort(P->seqs.begin(), P->seqs.end(),
                      [](const sgla::SeqEntry& x, const sgla::SeqEntry& y) { return x.len > y.len; });
@@ -118,9 +121,18 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
     P->N = a->B;
     P->num_chunks = a->T > 0 ? a->B * ((a->T + sgla::kChunk - 1) / sgla::kChunk) : 0;
   }
+  P->prep = need_kv_support && a->qkv_dtype == SGLA_BF16 && a->K >= 256;
   P->seq_off = 0;
   P->chunk_off = P->seq_off + align_up(P->seqs.size() * sizeof(sgla::SeqEntry), 256);
-  P->total_bytes = P->chunk_off + align_up(P->chunks.size() * sizeof(sgla::ChunkEntry), 256);
+  P->gate_off = P->chunk_off + align_up(P->chunks.size() * sizeof(sgla::ChunkEntry), 256);
+  P->amat_off = P->gate_off;
+  if (P->prep) {
+    const size_t tasks = (size_t)P->num_chunks * a->H;
+    P->amat_off = P->gate_off + align_up(tasks * sgla::kGateStride * sizeof(float), 256);
+    P->total_bytes = P->amat_off + tasks * 2 * sgla::kChunk * sgla::kChunk * 2;
+  } else {
+    P->total_bytes = P->gate_off;
+  }
   return SGLA_OK;
 }
 
@@ -221,10 +233,29 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
   p.V = a.V;
   p.o_bf16 = a.o_dtype == SGLA_BF16;
   p.seqs = L;
+  p.gates = P.prep ? reinterpret_cast<const float*>(ws + P.gate_off) : nullptr;
+  p.amat = P.prep ? ws + P.amat_off : nullptr;
   if (p.ht == nullptr && !any_tokens) return ok();
-  hipError_t e = a.qkv_dtype != SGLA_BF16 ? sgla::launch_chunk_fwd_f32(p, stream)
-                 : a.K >= 256            ? sgla::launch_chunk_fwd_bf16_ks(p, stream)
-                                         : sgla::launch_chunk_fwd_bf16(p, stream);
+  hipError_t e;
+  if (P.prep) {
+    sgla::ChunkPrepParams pp;
+    pp.q = q;
+    pp.k = k;
+    pp.g = g;
+    pp.g_gamma = g_gamma;
+    pp.scale = a.scale;
+    pp.H = a.H;
+    pp.K = a.K;
+    pp.seqs = L;
+    pp.gates = reinterpret_cast<float*>(ws + P.gate_off);
+    pp.amat = ws + P.amat_off;
+    e = sgla::launch_chunk_prep_bf16(pp, stream);
+    if (e != hipSuccess) return hip_fail(e, "launching the chunk preparation kernel");
+    e = sgla::launch_chunk_fwd_bf16_wide(p, stream);
+  } else {
+    e = a.qkv_dtype != SGLA_BF16 ? sgla::launch_chunk_fwd_f32(p, stream)
+                                 : sgla::launch_chunk_fwd_bf16(p, stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "launching the chunk kernel");
   return ok();
 }

@@ -13,10 +13,10 @@ constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robi
 
 // Per-sequence entry of the packed-input table, sorted longest first.
 struct SeqEntry {
-  int32_t bos;   // first packed token of the sequence
-  int32_t len;   // tokens
-  int32_t seq;   // index into initial_state / final_state
-  int32_t pad;
+  int32_t bos;     // first packed token of the sequence
+  int32_t len;     // tokens
+  int32_t seq;     // index into initial_state / final_state
+  int32_t chunk0;  // index of the sequence's first chunk in the chunk table
 };
 
 // Per-chunk entry used by the gate kernel for packed input.
@@ -36,6 +36,23 @@ struct SeqLayout {
   int32_t num_chunks;        // total chunks over all sequences
 };
 
+// Per-(chunk, head) outputs of the preparation kernel (wide-key bf16 path):
+// kGateStride floats of gates [sc[64], dv[64], dall, pad] and a [2][64][64]
+// bf16 hi/lo plane pair of the decay-masked, scaled q k^T.
+constexpr int kGateStride = 3 * kChunk;
+
+struct ChunkPrepParams {
+  const void* q;
+  const void* k;
+  const float* g;
+  const float* g_gamma;
+  float scale;
+  int32_t H, K;
+  SeqLayout seqs;
+  float* gates;              // [num_chunks, H, kGateStride]
+  void* amat;                // [num_chunks, H, 2, 64, 64] bf16
+};
+
 struct ChunkFwdParams {
   const void* q;
   const void* k;
@@ -49,6 +66,8 @@ struct ChunkFwdParams {
   int32_t H, K, V;
   int32_t o_bf16;            // 1: o is bf16, 0: float32
   SeqLayout seqs;
+  const float* gates;        // wide-key path: preparation outputs (workspace)
+  const void* amat;
 };
 
 hipError_t launch_gate_cumsum(const float* g, float* gc, int32_t H, const SeqLayout& seqs,
@@ -61,6 +80,11 @@ hipError_t launch_chunk_fwd_bf16(const ChunkFwdParams& p, hipStream_t stream);
 // bf16 q/k/v, MFMA path, key dimension streamed in 128-wide slices.  K in
 // {256,512}, V % 32 == 0.
 hipError_t launch_chunk_fwd_bf16_ks(const ChunkFwdParams& p, hipStream_t stream);
+
+// Wide-key bf16 path (K in {256,512}, V % 32 == 0): per-(chunk, head)
+// preparation, then the state and output passes reading its results.
+hipError_t launch_chunk_prep_bf16(const ChunkPrepParams& p, hipStream_t stream);
+hipError_t launch_chunk_fwd_bf16_wide(const ChunkFwdParams& p, hipStream_t stream);
 
 // float32 q/k/v, VALU path.  K in {16,32,64,128}, V % 32 == 0.
 hipError_t launch_chunk_fwd_f32(const ChunkFwdParams& p, hipStream_t stream);
