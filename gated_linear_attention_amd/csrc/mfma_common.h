@@ -63,6 +63,17 @@ __device__ __forceinline__ bf16x4 tr_read(const bf16* base, int ld, int row0, in
 #endif
 }
 
+// Transposed LDS read with the key order used by the wide-key state layout:
+// lane r of each 16-lane group receives base[(row0 + e) * ld + col0 + perm(r)]
+// for e = 0..3, where perm swaps the middle two 4-key blocks of the 16
+// (0-3, 8-11, 4-7, 12-15).
+__device__ __forceinline__ bf16x4 tr_read_perm(const bf16* base, int ld, int row0, int col0) {
+  const int lane = threadIdx.x & 15;
+  const int blk = ((lane & 1) << 3) | ((lane & 2) << 1);
+  const bf16* p = base + (row0 + (lane >> 2)) * ld + col0 + blk;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
 // Raw buffer descriptor over [base, base + bytes).  Loads past the end return
 // zeros and stores past the end are dropped, which is how a chunk's tail rows
 // (and a chunk past the sequence's end, with bytes = 0) are handled without

@@ -52,7 +52,7 @@ struct Plan {
   std::vector<sgla::SeqEntry> seqs;      // packed only, longest first
   std::vector<sgla::ChunkEntry> chunks;  // packed only
   bool prep = false;                     // wide-key bf16 path: per-chunk preparation buffers
-  size_t seq_off = 0, chunk_off = 0, gate_off = 0, amat_off = 0, total_bytes = 0;
+  size_t seq_off = 0, chunk_off = 0, gate_off = 0, amat_off = 0, kt_off = 0, total_bytes = 0;
 };
 
 sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv_support,
@@ -129,7 +129,8 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
   if (P->prep) {
     const size_t tasks = (size_t)P->num_chunks * a->H;
     P->amat_off = P->gate_off + align_up(tasks * sgla::kGateStride * sizeof(float), 256);
-    P->total_bytes = P->amat_off + tasks * 2 * sgla::kChunk * sgla::kChunk * 2;
+    P->kt_off = P->amat_off + tasks * 2 * sgla::kChunk * sgla::kChunk * 2;
+    P->total_bytes = P->kt_off + tasks * (size_t)a->K * sgla::kChunk * 2;
   } else {
     P->total_bytes = P->gate_off;
   }
@@ -235,6 +236,7 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
   p.seqs = L;
   p.gates = P.prep ? reinterpret_cast<const float*>(ws + P.gate_off) : nullptr;
   p.amat = P.prep ? ws + P.amat_off : nullptr;
+  p.ktf = P.prep ? ws + P.kt_off : nullptr;
   if (p.ht == nullptr && !any_tokens) return ok();
   hipError_t e;
   if (P.prep) {
@@ -249,6 +251,7 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
     pp.seqs = L;
     pp.gates = reinterpret_cast<float*>(ws + P.gate_off);
     pp.amat = ws + P.amat_off;
+    pp.ktf = ws + P.kt_off;
     e = sgla::launch_chunk_prep_bf16(pp, stream);
     if (e != hipSuccess) return hip_fail(e, "launching the chunk preparation kernel");
     e = sgla::launch_chunk_fwd_bf16_wide(p, stream);

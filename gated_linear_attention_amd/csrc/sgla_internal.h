@@ -51,6 +51,7 @@ struct ChunkPrepParams {
   SeqLayout seqs;
   float* gates;              // [num_chunks, H, kGateStride]
   void* amat;                // [num_chunks, H, 2, 64, 64] bf16
+  void* ktf;                 // [num_chunks, H, K * 64] bf16, state-update operand order
 };
 
 struct ChunkFwdParams {
@@ -68,6 +69,7 @@ struct ChunkFwdParams {
   SeqLayout seqs;
   const float* gates;        // wide-key path: preparation outputs (workspace)
   const void* amat;
+  const void* ktf;
 };
 
 hipError_t launch_gate_cumsum(const float* g, float* gc, int32_t H, const SeqLayout& seqs,
