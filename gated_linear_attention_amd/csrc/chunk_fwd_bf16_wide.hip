@@ -3,8 +3,9 @@
 // (page "flash-linear-attention 中的 Simple GLA", section 一: chunk view with a
 // scalar-decayed state between chunks; section 三: the state pass and the
 // output pass).  The per-chunk gates, the decay-masked A = scale (Q K^T (.) M)
-// and the transposed keys come from the preparation kernel
-// (chunk_prep_bf16.hip).
+// and the Q, K^T and A operands in MFMA operand order come from the
+// preparation kernel (chunk_prep_bf16.hip), so every operand load here is one
+// contiguous 1 KB block.
 //
 // For chunk n with state h_n (K x V, fp32):
 //   O_n     = diag(sc) Q_n h_n + A_n V_n,        sc = scale 2^b
@@ -14,10 +15,9 @@
 // w owns the K/8 state rows [K/8 w, +K/8) of the tile's 32 columns, as 32 x 32
 // fp32 MFMA accumulators (v_mfma_f32_32x32x16_bf16) that stay in registers
 // for the whole sequence.  Per chunk each wave
-//   1. multiplies its rows of Q (loaded from HBM straight into MFMA operand
-//      layout) with its state rows: a 64 x 32 partial of Q h_n;
-//   2. updates its state rows with K^T (one contiguous 1 KB load per operand
-//      from the preparation output) times the decayed V (hi + lo);
+//   1. multiplies the chunk's Q, restricted to its keys, with its state rows:
+//      a 64 x 32 partial of Q h_n;
+//   2. updates its state rows with K^T times the decayed V (hi + lo);
 //   3. writes its partial to LDS; one barrier per chunk.  During the next
 //      chunk's q.h MFMAs, wave (ct, vh) sums the eight partials of output
 //      rows [16 ct, +16) x columns [16 vh, +16), scales them by sc, adds the
@@ -77,7 +77,7 @@ __device__ __forceinline__ void store1<bf16>(__amdgpu_buffer_rsrc_t rs, uint32_t
 
 template <int K, typename TOut>
 __global__ void __launch_bounds__(NT)
-chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ v,
+chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict__ v,
                            const float* __restrict__ h0, TOut* __restrict__ o,
                            float* __restrict__ ht, int32_t H, int32_t V, SeqLayout seqs,
                            int32_t chunks_per_row, const float* __restrict__ gates,
@@ -127,13 +127,13 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
   const int vh = w & 1;            //                           columns [16 vh, +16)
   const int RSK = H * K;
   const int RSV = H * V;
-  const bf16* qb = q + (bos * H + hd) * (int64_t)K;
   const bf16* vb = v + (bos * H + hd) * (int64_t)V + vt * VT;
   TOut* ob = o + (bos * H + hd) * (int64_t)V + vt * VT;
   const int64_t task0 = (int64_t)chunk0 * H + hd;          // preparation record of chunk 0
   const float* gbase = gates + task0 * kGateStride;
   const bf16* abase = amat + task0 * (2 * C * C);
   const bf16* ktbase = ktf + task0 * (int64_t)K * C;
+  const bf16* qbase = qfr + task0 * (int64_t)K * C;
   const int64_t gstep = (int64_t)H * kGateStride;          // record strides between chunks
   const int64_t astep = (int64_t)H * 2 * C * C;
   const int64_t kstep = (int64_t)H * K * C;
@@ -176,11 +176,10 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
     }
   };
 
-  // ---- Q operand of q.h: rows 32 c2 + l32, keys k0w + 32 rt + 16 s + 8 hf ---
+  // ---- Q operand of q.h: blocks (key block, c2, s) -------------------------
   bf16x8 qf[2][NRT][2];
   auto load_q = [&](int m) {
-    const int cl = max(0, min(C, len - m * C));
-    const auto rq = make_rsrc(qb + (int64_t)m * C * RSK, (uint32_t)cl * RSK * 2);
+    const auto rq = make_rsrc(qbase + m * kstep, m < nchunks ? (uint32_t)K * C * 2 : 0u);
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
@@ -189,7 +188,7 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
         for (int s = 0; s < 2; ++s)
           qf[c2][rt][s] = __builtin_bit_cast(
               bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                          rq, (uint32_t)((32 * c2 + l32) * RSK + k0w + 32 * rt + 16 * s + 8 * hf) * 2, 0, 0));
+                          rq, (uint32_t)(((((k0w >> 5) + rt) * 2 + c2) * 2 + s) * 64 + lane) * 16, 0, 0));
   };
 
   // ---- K^T operand of the update: fragments (key block, token step) --------
@@ -205,7 +204,7 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
                         rk, (uint32_t)((((k0w >> 5) + rt) * 4 + ts) * 64 + lane) * 16, 0, 0));
   };
 
-  // ---- A operand of the intra product: rows 16 ct + r, tokens 32 u + 8 g4 --
+  // ---- A operand of the intra product: blocks (ct, u, plane) --------------
   bf16x8 af[2][2];   // [u][hi, lo]
   auto load_a = [&](int m) {
     const uint32_t bytes = m < nchunks ? (uint32_t)(2 * C * C * 2) : 0u;
@@ -213,9 +212,10 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
     const auto ra1 = make_rsrc(abase + m * astep, ct >= 2 ? bytes : 0u);   // tokens 32..63
 #pragma unroll
     for (int pl = 0; pl < 2; ++pl) {
-      const uint32_t off = (uint32_t)(pl * C * C + (16 * ct + r) * C + 8 * g4) * 2;
-      af[0][pl] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra0, off, 0, 0));
-      af[1][pl] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra1, off + 64, 0, 0));
+      af[0][pl] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 ra0, (uint32_t)((((ct * 2 + 0) * 2 + pl) * 64 + lane) * 16), 0, 0));
+      af[1][pl] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 ra1, (uint32_t)((((ct * 2 + 1) * 2 + pl) * 64 + lane) * 16), 0, 0));
     }
   };
 
@@ -353,7 +353,7 @@ hipError_t launch_k(const ChunkFwdParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(groups * kXcds * nvt));
   const int per_row = p.seqs.T > 0 ? (p.seqs.T + C - 1) / C : 0;
   hipLaunchKernelGGL((chunk_fwd_bf16_wide_kernel<K, TOut>), grid, dim3(NT), 0, stream,
-                     static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.v), p.h0,
+                     static_cast<const bf16*>(p.qfr), static_cast<const bf16*>(p.v), p.h0,
                      static_cast<TOut*>(p.o), p.ht, p.H, p.V, p.seqs, per_row, p.gates,
                      static_cast<const bf16*>(p.amat), static_cast<const bf16*>(p.ktf));
   return hipGetLastError();

@@ -11,17 +11,26 @@
 //          dv[j]  = 2^(b_last - b_j)        (decay of k_j v_j^T to the chunk end)
 //          dall   = 2^b_last                (decay of h_n across the chunk)
 //   A[c][j] = scale * (q_c . k_j) * 2^(b_c - b_j) for j <= c, 0 otherwise,
-//             stored as bf16 hi + lo planes (A = hi + lo to ~2^-16 relative).
-//   K^T     : the chunk's keys transposed into the operand order of the state
-//             update of chunk_fwd_bf16_wide.hip (layout at the K^T step below), so
-//             that kernel loads them with one contiguous 1 KB read per MFMA
-//             operand instead of transposing through LDS in every V tile.
-// Tokens at or past L read as zeros (q, k, g), so their A rows and columns
-// and K^T entries are zero and b stays at b_last.
+//             as bf16 hi + lo (A = hi + lo to ~2^-16 relative).
+// Besides the gates, three operand streams of chunk_fwd_bf16_wide.hip are
+// written in that kernel's MFMA operand order, one 1 KB block (64 lanes x
+// 16 bytes, lane-major) per operand, so every load there is one contiguous
+// kilobyte:
+//   Q   blocks (kb, c2, s): lane (n = l % 32, h = l / 32) holds
+//       Q[32 c2 + n][32 kb + 16 s + 8 h + e], e = 0..7       (q.h A operand)
+//   K^T blocks (kb, ts):    lane (n, h) holds
+//       K[16 ts + 8 h + e][32 kb + perm(n)]                  (update A operand)
+//       with perm swapping the middle two 4-key blocks of each 16, the state
+//       row order of that kernel
+//   A   blocks (ct, u, plane): lane (r = l % 16, g = l / 16) holds
+//       A[16 ct + r][32 u + 8 g + e]                         (intra A operand)
+// Tokens at or past L read as zeros (q, k, g), so their A rows and columns,
+// Q rows and K^T entries are zero and b stays at b_last.
 //
-// One workgroup of four waves per (chunk, head).  The K chunk is staged in
-// LDS once; Q K^T runs on v_mfma_f32_16x16x32_bf16 with the Q operand loaded
-// from HBM in MFMA layout and the K operand read from LDS.
+// One workgroup of four waves per (chunk, head).  All HBM reads (the K chunk
+// into registers then LDS, the wave's Q blocks into registers) are issued
+// up front.  Q K^T runs on v_mfma_f32_32x32x16_bf16: wave w covers query
+// rows [32 (w / 2), +32) over key half w % 2; the two halves are added in LDS.
 #include <hip/hip_runtime.h>
 
 #include "gate_scan.h"
@@ -35,25 +44,20 @@ using namespace mf;
 
 constexpr int C = kChunk;
 constexpr int NTP = 256;          // threads
-constexpr int LDA = C + 8;        // A staging row stride (elements)
-
-// Causal 16 x 16 tiles (c tile, j tile) of each wave, packed 4 bits per tile
-// (c | j << 2), up to three per wave:
-//   wave 0: (3,0) (3,1) (3,2)   wave 1: (3,3) (0,0)
-//   wave 2: (2,0) (2,1) (2,2)   wave 3: (1,0) (1,1)
-constexpr uint32_t kPrepTiles[4] = {0xB73u, 0x0Fu, 0xA62u, 0x51u};
-constexpr int kPrepCount[4] = {3, 2, 3, 2};
+constexpr int LDS_ACC = C + 4;    // row stride of the fp32 A accumulator (floats)
 
 template <int K>
 __global__ void __launch_bounds__(NTP)
 chunk_prep_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                        const float* __restrict__ g, const float* __restrict__ g_gamma, float scale,
                        int32_t H, SeqLayout seqs, int32_t chunks_per_row, float* __restrict__ gates,
-                       bf16* __restrict__ amat, bf16* __restrict__ ktf) {
-  constexpr int LDK = K + 8;      // row stride: conflict-free 16-byte row reads
+                       bf16* __restrict__ amat, bf16* __restrict__ ktf, bf16* __restrict__ qfr) {
+  constexpr int LDK = K + 8;      // key row stride: conflict-free 16-byte row reads
   constexpr int KP = K / 8;       // 16-byte pieces per key row
   constexpr int NKS = C * KP / NTP;
-  __shared__ __attribute__((aligned(16))) bf16 sK[C * LDK];   // later: A staging
+  constexpr int NKB = K / 64;     // 32-key blocks per wave (half the keys)
+  static_assert(C * LDS_ACC * 4 <= C * LDK * 2, "A accumulator aliases the K chunk");
+  __shared__ __attribute__((aligned(16))) bf16 sK[C * LDK];
   __shared__ float sb[C];
 
   const int gc = blockIdx.x;      // global chunk index
@@ -73,34 +77,44 @@ chunk_prep_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+  const int grp = lane >> 4;
   const int g4 = lane >> 4;
   const int r = lane & 15;
+  const int c2 = w >> 1;           // query rows [32 c2, +32)
+  const int kb0 = (w & 1) * NKB;   // key blocks [kb0, kb0 + NKB)
   const int64_t task = (int64_t)gc * H + hd;
-  const int RS = H * K;             // elements between consecutive tokens
+  const int RS = H * K;            // elements between consecutive tokens
 
-  // ---- stage the K chunk (rows past L read as zeros) -----------------------
-  {
-    const auto rk = make_rsrc(k + (t0 * H + hd) * (int64_t)K, (uint32_t)cl * RS * 2);
-    u32x4 x[NKS];
+  // ---- all HBM reads up front ----------------------------------------------
+  const auto rk = make_rsrc(k + (t0 * H + hd) * (int64_t)K, (uint32_t)cl * RS * 2);
+  const auto rq = make_rsrc(q + (t0 * H + hd) * (int64_t)K, (uint32_t)cl * RS * 2);
+  u32x4 kx[NKS];
 #pragma unroll
-    for (int u = 0; u < NKS; ++u) {
-      const int p = tid + NTP * u;
-      x[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)((p / KP) * RS + (p % KP) * 8) * 2, 0, 0);
-    }
+  for (int u = 0; u < NKS; ++u) {
+    const int p = tid + NTP * u;
+    kx[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)((p / KP) * RS + (p % KP) * 8) * 2, 0, 0);
+  }
+  bf16x8 qx[NKB][2];
 #pragma unroll
-    for (int u = 0; u < NKS; ++u) {
-      const int p = tid + NTP * u;
-      *reinterpret_cast<u32x4*>(sK + (p / KP) * LDK + (p % KP) * 8) = x[u];
-    }
+  for (int i = 0; i < NKB; ++i)
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      qx[i][s] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                      rq, (uint32_t)((32 * c2 + l32) * RS + 32 * (kb0 + i) + 16 * s + 8 * hf) * 2, 0, 0));
+  float gx = 0.f;
+  if (w == 0 && g != nullptr) {
+    const auto rg = make_rsrc(g + t0 * H + hd, (uint32_t)cl * H * 4);
+    gx = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)(lane * H * 4), 0, 0));
   }
 
   // ---- gates ----------------------------------------------------------------
   if (w == 0) {
     float b;
     if (g != nullptr) {
-      const auto rg = make_rsrc(g + t0 * H + hd, (uint32_t)cl * H * 4);
-      b = wave_cumsum_log2(__builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)(lane * H * 4), 0, 0)));
+      b = wave_cumsum_log2(gx);
     } else if (g_gamma != nullptr) {
       b = (float)min(lane + 1, cl) * (g_gamma[hd] * kRcpLn2f);
     } else {
@@ -113,16 +127,26 @@ chunk_prep_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     gt[C + lane] = exp2_hw(blast - b);
     if (lane == 0) gt[2 * C] = exp2_hw(blast);
   }
+
+  // ---- K chunk to LDS; Q blocks out ----------------------------------------
+#pragma unroll
+  for (int u = 0; u < NKS; ++u) {
+    const int p = tid + NTP * u;
+    *reinterpret_cast<u32x4*>(sK + (p / KP) * LDK + (p % KP) * 8) = kx[u];
+  }
+  {
+    bf16* qo = qfr + task * (int64_t)K * C;
+#pragma unroll
+    for (int i = 0; i < NKB; ++i)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        *reinterpret_cast<bf16x8*>(qo + ((((kb0 + i) * 2 + c2) * 2 + s) * 64 + lane) * 8) = qx[i][s];
+  }
   __syncthreads();
 
-  // ---- K^T fragments ----------------------------------------------------------
-  // Fragment (kb, ts), kb = 32-key block, ts = 16-token step: lane l holds
-  // K[t = 16 ts + 8 (l / 32) + e][key = 32 kb + perm(l % 32)], e = 0..7, with
-  // perm swapping the middle two 4-key blocks of each 16.  1 KB per fragment,
-  // lane-major, fragments ordered (kb, ts).
+  // ---- K^T blocks -------------------------------------------------------------
   {
     bf16* kt = ktf + task * (int64_t)K * C;
-    const int grp = lane >> 4;
 #pragma unroll
     for (int f = w; f < (K / 32) * 4; f += 4) {
       const int kb = f >> 2, ts = f & 3;
@@ -133,62 +157,71 @@ chunk_prep_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
   }
 
-  // ---- Q K^T: Q operand from HBM, K operand from LDS --------------------------
-  const uint32_t tiles = kPrepTiles[w];
-  const int ntile = kPrepCount[w];
-  const auto rq = make_rsrc(q + (t0 * H + hd) * (int64_t)K, (uint32_t)cl * RS * 2);
-  f32x4 acc[3];
+  // ---- partial Q K^T over this wave's key half: tiles (c2, j2), j2 <= c2 ---
+  f32x16 acc[2];
 #pragma unroll
-  for (int i = 0; i < 3; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int u = 0; u < K / 32; ++u) {
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int t = 0; t < 3; ++t) {
-      if (t >= ntile) continue;
-      const int ct = (tiles >> (4 * t)) & 3, jt = (tiles >> (4 * t + 2)) & 3;
-      const bf16x8 qa = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                      rq, (uint32_t)((16 * ct + r) * RS + 32 * u + 8 * g4) * 2, 0, 0));
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + (16 * jt + r) * LDK + 32 * u + 8 * g4);
-      acc[t] = mfma(qa, kf, acc[t]);
+    for (int a = 0; a < 16; ++a) acc[t][a] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NKB; ++i)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int col = 32 * (kb0 + i) + 16 * s + 8 * hf;
+      const bf16x8 k0f = *reinterpret_cast<const bf16x8*>(sK + l32 * LDK + col);
+      acc[0] = mfma32(qx[i][s], k0f, acc[0]);
+      if (c2 == 1) {
+        const bf16x8 k1f = *reinterpret_cast<const bf16x8*>(sK + (32 + l32) * LDK + col);
+        acc[1] = mfma32(qx[i][s], k1f, acc[1]);
+      }
     }
-  }
-  __syncthreads();   // every read of the K chunk is done: reuse it for A
+  __syncthreads();   // every read of the K chunk is done: reuse it as the accumulator
 
-  // ---- mask, decay, scale, split; stage both planes in LDS -----------------
-  bf16* sA = sK;     // [2][C][LDA]
-  for (int i = tid; i < 2 * C * LDA / 8; i += NTP)
-    reinterpret_cast<u32x4*>(sA)[i] = u32x4{0u, 0u, 0u, 0u};
-  __syncthreads();
+  // ---- add the two key halves in LDS (fixed order: deterministic) ---------
+  // acc[t][4 jj + i] = D[c = 32 c2 + 8 jj + 4 hf + i][j = 32 t + l32]
+  float* sacc = reinterpret_cast<float*>(sK);
+  auto tile_io = [&](bool add) {
 #pragma unroll
-  for (int t = 0; t < 3; ++t) {
-    if (t >= ntile) continue;
-    const int ct = (tiles >> (4 * t)) & 3, jt = (tiles >> (4 * t + 2)) & 3;
-    // acc element i: A[16 ct + 4 g + i][16 jt + r]
-    const int j = 16 * jt + r;
-    const float bj = sb[j];
+    for (int t = 0; t < 2; ++t) {
+      if (t > c2) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = 16 * ct + 4 * g4 + i;
-      const float x = j <= c ? acc[t][i] * exp2_hw(sb[c] - bj) * scale : 0.f;
-      const bf16 hi = (bf16)x;
-      const bf16 lo = (bf16)(x - (float)hi);
-      sA[c * LDA + j] = hi;
-      sA[C * LDA + c * LDA + j] = lo;
+      for (int a = 0; a < 16; ++a) {
+        float* p = sacc + (32 * c2 + 8 * (a >> 2) + 4 * hf + (a & 3)) * LDS_ACC + 32 * t + l32;
+        *p = add ? *p + acc[t][a] : acc[t][a];
+      }
     }
-  }
+  };
+  if ((w & 1) == 0) tile_io(false);
+  __syncthreads();
+  if ((w & 1) == 1) tile_io(true);
   __syncthreads();
 
-  // ---- store both planes row-major [2][64][64] ------------------------------
-  bf16* at = amat + task * (2 * C * C);
+  // ---- mask, decay, scale, split; A blocks out ------------------------------
+  // wave w: c tile ct = w, u = 0 and (ct >= 2) u = 1
+  {
+    const int ct = w;
+    const int c = 16 * ct + r;
+    const float bc = sb[c];
+    bf16* ao = amat + task * (2 * C * C);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int p = tid + NTP * u;          // 1024 pieces of 8 elements
-    const int plane = p >> 9;
-    const int row = (p >> 3) & 63;
-    const int c8 = p & 7;
-    *reinterpret_cast<u32x4*>(at + plane * C * C + row * C + 8 * c8) =
-        *reinterpret_cast<const u32x4*>(sA + plane * C * LDA + row * LDA + 8 * c8);
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && ct < 2) continue;
+      const int j0 = 32 * u + 8 * g4;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(sacc + c * LDS_ACC + j0);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(sacc + c * LDS_ACC + j0 + 4);
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(sb + j0);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(sb + j0 + 4);
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = j0 + e <= c ? a0[e] * exp2_hw(bc - b0[e]) * scale : 0.f;
+        x[4 + e] = j0 + 4 + e <= c ? a1[e] * exp2_hw(bc - b1[e]) * scale : 0.f;
+      }
+      bf16x8 hi, lo;
+      split8(x, hi, lo);
+      *reinterpret_cast<bf16x8*>(ao + (((ct * 2 + u) * 2 + 0) * 64 + lane) * 8) = hi;
+      *reinterpret_cast<bf16x8*>(ao + (((ct * 2 + u) * 2 + 1) * 64 + lane) * 8) = lo;
+    }
   }
 }
 
@@ -199,7 +232,7 @@ hipError_t launch_k(const ChunkPrepParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((chunk_prep_bf16_kernel<K>), grid, dim3(NTP), 0, stream,
                      static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k), p.g, p.g_gamma,
                      p.scale, p.H, p.seqs, per_row, p.gates, static_cast<bf16*>(p.amat),
-                     static_cast<bf16*>(p.ktf));
+                     static_cast<bf16*>(p.ktf), static_cast<bf16*>(p.qfr));
   return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ struct Plan {
   std::vector<sgla::SeqEntry> seqs;      // packed only, longest first
   std::vector<sgla::ChunkEntry> chunks;  // packed only
   bool prep = false;                     // wide-key bf16 path: per-chunk preparation buffers
-  size_t seq_off = 0, chunk_off = 0, gate_off = 0, amat_off = 0, kt_off = 0, total_bytes = 0;
+  size_t seq_off = 0, chunk_off = 0, gate_off = 0, amat_off = 0, kt_off = 0, q_off = 0, total_bytes = 0;
 };
 
 sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv_support,
@@ -130,7 +130,8 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
     const size_t tasks = (size_t)P->num_chunks * a->H;
     P->amat_off = P->gate_off + align_up(tasks * sgla::kGateStride * sizeof(float), 256);
     P->kt_off = P->amat_off + tasks * 2 * sgla::kChunk * sgla::kChunk * 2;
-    P->total_bytes = P->kt_off + tasks * (size_t)a->K * sgla::kChunk * 2;
+    P->q_off = P->kt_off + tasks * (size_t)a->K * sgla::kChunk * 2;
+    P->total_bytes = P->q_off + tasks * (size_t)a->K * sgla::kChunk * 2;
   } else {
     P->total_bytes = P->gate_off;
   }
@@ -237,6 +238,7 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
   p.gates = P.prep ? reinterpret_cast<const float*>(ws + P.gate_off) : nullptr;
   p.amat = P.prep ? ws + P.amat_off : nullptr;
   p.ktf = P.prep ? ws + P.kt_off : nullptr;
+  p.qfr = P.prep ? ws + P.q_off : nullptr;
   if (p.ht == nullptr && !any_tokens) return ok();
   hipError_t e;
   if (P.prep) {
@@ -252,6 +254,7 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
     pp.gates = reinterpret_cast<float*>(ws + P.gate_off);
     pp.amat = ws + P.amat_off;
     pp.ktf = ws + P.kt_off;
+    pp.qfr = ws + P.q_off;
     e = sgla::launch_chunk_prep_bf16(pp, stream);
     if (e != hipSuccess) return hip_fail(e, "launching the chunk preparation kernel");
     e = sgla::launch_chunk_fwd_bf16_wide(p, stream);

@@ -38,7 +38,8 @@ struct SeqLayout {
 
 // Per-(chunk, head) outputs of the preparation kernel (wide-key bf16 path):
 // kGateStride floats of gates [sc[64], dv[64], dall, pad] and a [2][64][64]
-// bf16 hi/lo plane pair of the decay-masked, scaled q k^T.
+// bf16 hi/lo pair of the decay-masked, scaled q k^T, plus the chunk's Q and
+// K^T, all in the MFMA operand order of the state/output kernel.
 constexpr int kGateStride = 3 * kChunk;
 
 struct ChunkPrepParams {
@@ -52,6 +53,7 @@ struct ChunkPrepParams {
   float* gates;              // [num_chunks, H, kGateStride]
   void* amat;                // [num_chunks, H, 2, 64, 64] bf16
   void* ktf;                 // [num_chunks, H, K * 64] bf16, state-update operand order
+  void* qfr;                 // [num_chunks, H, K * 64] bf16, q.h operand order
 };
 
 struct ChunkFwdParams {
@@ -70,6 +72,7 @@ struct ChunkFwdParams {
   const float* gates;        // wide-key path: preparation outputs (workspace)
   const void* amat;
   const void* ktf;
+  const void* qfr;
 };
 
 hipError_t launch_gate_cumsum(const float* g, float* gc, int32_t H, const SeqLayout& seqs,
