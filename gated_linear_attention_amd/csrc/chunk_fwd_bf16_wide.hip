@@ -17,16 +17,17 @@
 // for the whole sequence.  Per chunk each wave
 //   1. multiplies the chunk's Q, restricted to its keys, with its state rows:
 //      a 64 x 32 partial of Q h_n;
-//   2. updates its state rows with K^T times the decayed V (hi + lo);
-//   3. writes its partial to LDS; one barrier per chunk.  During the next
-//      chunk's q.h MFMAs, wave (ct, vh) sums the eight partials of output
-//      rows [16 ct, +16) x columns [16 vh, +16), scales them by sc, adds the
-//      intra-chunk A V (16x16x32 MFMAs, A from the preparation output) and
-//      stores the tile, so the reduction overlaps matrix work.
+//   2. updates its state rows with K^T times the decayed V (hi + lo), read
+//      from LDS where the eight waves computed it together (each wave an
+//      eighth of the tile) during the previous chunk;
+//   3. writes its partial to LDS; after a barrier, wave (ct, vh) sums the
+//      eight partials of output rows [16 ct, +16) x columns [16 vh, +16),
+//      scales them by sc, adds the intra-chunk A V (16x16x32 MFMAs, A from
+//      the preparation output) and stores the tile; then the waves stage the
+//      next decayed V tile and the V tile and gates two chunks ahead, and a
+//      second barrier closes the chunk.
 // Q, K^T and A fragments are loaded one chunk ahead into the registers that
-// use them; the V tile and gates go through LDS, written two chunks ahead
-// (four buffers), and the partials are double buffered, so the single
-// barrier orders everything.
+// use them.
 //
 // State row order: accumulator element a of lane (n = l % 32, h = l / 32) in
 // row tile rt holds S[K/8 w + 32 rt + 16 (a / 8) + 8 h + a % 8][column n], so
@@ -55,12 +56,14 @@ constexpr int LDV = VT + 8;      // V tile row stride (elements)
 constexpr int LDP = C + 4;       // partial row stride (floats)
 
 struct WideLayout {
-  static constexpr int SZ_P = NW * VT * LDP * 4;     // per-wave partials [w][v][c], two buffers
-  static constexpr int OFF_V = 2 * SZ_P;
-  static constexpr int SZ_V = C * LDV * 2;           // V tile, four buffers
-  static constexpr int OFF_G = OFF_V + 4 * SZ_V;
-  static constexpr int SZ_G = kGateStride * 4;       // gates, four buffers
-  static constexpr int BYTES = OFF_G + 4 * SZ_G;
+  static constexpr int SZ_P = NW * VT * LDP * 4;     // per-wave partials [w][v][c]
+  static constexpr int OFF_V = SZ_P;
+  static constexpr int SZ_V = C * LDV * 2;           // V tile, three buffers
+  static constexpr int OFF_G = OFF_V + 3 * SZ_V;
+  static constexpr int SZ_G = kGateStride * 4;       // gates, three buffers
+  static constexpr int OFF_T = OFF_G + 3 * SZ_G;
+  static constexpr int SZ_T = 2 * C * LDV * 2;       // decayed V hi + lo, two buffers
+  static constexpr int BYTES = OFF_T + 2 * SZ_T;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -141,6 +144,7 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
   float* sPb = reinterpret_cast<float*>(smem);
   auto sV = [&](int p) { return reinterpret_cast<bf16*>(smem + L::OFF_V + p * L::SZ_V); };
   auto sG = [&](int p) { return reinterpret_cast<float*>(smem + L::OFF_G + p * L::SZ_G); };
+  auto sT = [&](int p) { return reinterpret_cast<bf16*>(smem + L::OFF_T + p * L::SZ_T); };
 
   // ---- state ---------------------------------------------------------------
   f32x16 h[NRT];
@@ -219,17 +223,16 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
     }
   };
 
-  // ---- output tile (ct, vh) of chunk mp: rows 16 ct + 4 g4 + i, column
-  //      16 vh + r; partials of chunk mp are in sP[mp & 1] --------------------
-  auto finish = [&](int mp) {
-    const float* sP = sPb + (mp & 1) * (NW * VT * LDP);
-    const float* sg = sG(mp & 3);
-    const bf16* sv = sV(mp & 3);
-    const int cl = min(C, len - mp * C);
-    f32x4 acc = *reinterpret_cast<const f32x4*>(sP + (16 * vh + r) * LDP + 16 * ct + 4 * g4);
+  // ---- output tile (ct, vh) of chunk m: rows 16 ct + 4 g4 + i, column
+  //      16 vh + r ---------------------------------------------------------------
+  auto finish = [&](int m) {
+    const float* sg = sG(m % 3);
+    const bf16* sv = sV(m % 3);
+    const int cl = min(C, len - m * C);
+    f32x4 acc = *reinterpret_cast<const f32x4*>(sPb + (16 * vh + r) * LDP + 16 * ct + 4 * g4);
 #pragma unroll
     for (int w2 = 1; w2 < NW; ++w2)
-      acc += *reinterpret_cast<const f32x4*>(sP + (w2 * VT + 16 * vh + r) * LDP + 16 * ct + 4 * g4);
+      acc += *reinterpret_cast<const f32x4*>(sPb + (w2 * VT + 16 * vh + r) * LDP + 16 * ct + 4 * g4);
     acc *= *reinterpret_cast<const f32x4*>(sg + 16 * ct + 4 * g4);
     {
       const bf16x8 vf = cat(tr_read(sv, LDV, 8 * g4, 16 * vh), tr_read(sv, LDV, 8 * g4 + 4, 16 * vh));
@@ -241,10 +244,27 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
       acc = mfma(af[1][0], vf, acc);
       acc = mfma(af[1][1], vf, acc);
     }
-    const auto ro = make_rsrc(ob + (int64_t)mp * C * RSV, (uint32_t)cl * RSV * (uint32_t)sizeof(TOut));
+    const auto ro = make_rsrc(ob + (int64_t)m * C * RSV, (uint32_t)cl * RSV * (uint32_t)sizeof(TOut));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       store1<TOut>(ro, (uint32_t)((16 * ct + 4 * g4 + i) * RSV + 16 * vh + r) * (uint32_t)sizeof(TOut), acc[i]);
+  };
+
+  // ---- decayed V of chunk m, hi + lo: wave w computes tokens [8 w, +8) ------
+  auto decay_v = [&](int m) {
+    const bf16* sv = sV(m % 3);
+    const float* sg = sG(m % 3);
+    bf16* st = sT(m & 1);
+    const int row = 8 * w + (lane >> 3);
+    const int col = 4 * (lane & 7);
+    const u32x2 raw = *reinterpret_cast<const u32x2*>(sv + row * LDV + col);
+    const float d = sg[C + row];
+    float x[4] = {bf_lo(raw[0]) * d, bf_hi(raw[0]) * d, bf_lo(raw[1]) * d, bf_hi(raw[1]) * d};
+    uint32_t h0w, l0w, h1w, l1w;
+    split2(x[0], x[1], h0w, l0w);
+    split2(x[2], x[3], h1w, l1w);
+    *reinterpret_cast<u32x2*>(st + row * LDV + col) = u32x2{h0w, h1w};
+    *reinterpret_cast<u32x2*>(st + C * LDV + row * LDV + col) = u32x2{l0w, l1w};
   };
 
   store_vg(load_vg(0), 0);
@@ -254,10 +274,12 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
   load_kt(0);
   load_a(0);
   __syncthreads();
+  decay_v(0);
+  __syncthreads();
 
   for (int m = 0; m < nchunks; ++m) {
-    const float* sg = sG(m & 3);
-    const bf16* sv = sV(m & 3);
+    const float* sg = sG(m % 3);
+    const bf16* stv = sT(m & 1);
 
     // ---- 1. partial q.h over this wave's state rows ----------------------
     f32x16 pacc[2];
@@ -280,38 +302,18 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
           pacc[c2] = mfma32(qf[c2][rt][s], hl, pacc[c2]);
         }
       }
-
-    // ---- 2. previous chunk's output, overlapping the q.h MFMAs -----------
-    if (m > 0) finish(m - 1);
-    load_a(m);
-
-    // ---- 3. V tile and gates of chunk m + 2 (buffer of chunk m - 2) ------
-    store_vg(vg, (m + 2) & 3);
-    vg = load_vg(m + 3);
     load_q(m + 1);
 
-    // ---- 4. state update: h <- dall h + K^T diag(dv) V -------------------
+    // ---- 2. state update: h <- dall h + K^T (decayed V hi + lo) ------------
     const float dall = sg[2 * C];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) h[rt] *= dall;
 #pragma unroll
     for (int ts = 0; ts < 4; ++ts) {
       const int row0 = 16 * ts + 8 * (grp >> 1);
-      const bf16x8 vraw = cat(tr_read(sv, LDV, row0, 16 * (grp & 1)), tr_read(sv, LDV, row0 + 4, 16 * (grp & 1)));
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(sg + C + 16 * ts + 8 * hf);
-      const f32x4 d1 = *reinterpret_cast<const f32x4*>(sg + C + 16 * ts + 8 * hf + 4);
-      const u32x4 raw = __builtin_bit_cast(u32x4, vraw);
-      float x[8];
-      x[0] = bf_lo(raw[0]) * d0[0];
-      x[1] = bf_hi(raw[0]) * d0[1];
-      x[2] = bf_lo(raw[1]) * d0[2];
-      x[3] = bf_hi(raw[1]) * d0[3];
-      x[4] = bf_lo(raw[2]) * d1[0];
-      x[5] = bf_hi(raw[2]) * d1[1];
-      x[6] = bf_lo(raw[3]) * d1[2];
-      x[7] = bf_hi(raw[3]) * d1[3];
-      bf16x8 vth, vtl;
-      split8(x, vth, vtl);
+      const int col0 = 16 * (grp & 1);
+      const bf16x8 vth = cat(tr_read(stv, LDV, row0, col0), tr_read(stv, LDV, row0 + 4, col0));
+      const bf16x8 vtl = cat(tr_read(stv + C * LDV, LDV, row0, col0), tr_read(stv + C * LDV, LDV, row0 + 4, col0));
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
         h[rt] = mfma32(kt[ts][rt], vth, h[rt]);
@@ -320,9 +322,9 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
     }
     load_kt(m + 1);
 
-    // ---- 5. partials to LDS: pacc[c2][4 j + i] = P[32 c2 + 8 j + 4 hf + i][l32]
+    // ---- 3. partials to LDS: pacc[c2][4 j + i] = P[32 c2 + 8 j + 4 hf + i][l32]
     {
-      float* pw = sPb + (m & 1) * (NW * VT * LDP) + (w * VT + l32) * LDP + 4 * hf;
+      float* pw = sPb + (w * VT + l32) * LDP + 4 * hf;
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
@@ -331,8 +333,15 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
               f32x4{pacc[c2][4 * j], pacc[c2][4 * j + 1], pacc[c2][4 * j + 2], pacc[c2][4 * j + 3]};
     }
     __syncthreads();
+
+    // ---- 4. output of chunk m; next decayed V; V and gates two ahead -------
+    finish(m);
+    load_a(m + 1);
+    if (m + 1 < nchunks) decay_v(m + 1);
+    store_vg(vg, (m + 2) % 3);
+    vg = load_vg(m + 3);
+    __syncthreads();
   }
-  if (nchunks > 0) finish(nchunks - 1);
 
   if (ht != nullptr) {
     float* htu = ht + ((int64_t)seq * H + hd) * K * V + vt * VT + l32;
