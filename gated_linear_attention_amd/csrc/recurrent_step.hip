@@ -9,12 +9,16 @@
 // The step is a pure read-modify-write stream over the state: 2 * K * V * 4
 // bytes per (sequence, head) against 5 * K * V flops, so it is bound by HBM.
 // One 256-thread workgroup owns one (sequence, head) state.  Each thread owns
-// four adjacent v columns (16-byte accesses) and every RG-th k row, so a wave
-// touches whole contiguous state rows.  All of a thread's rows of a batch are
-// loaded before any is used so that many 16-byte loads are in flight per
-// wave; the q-weighted column sums are then reduced across row groups through
-// LDS.
+// four adjacent v columns (16-byte accesses) and, when the rows split evenly
+// into 4, 8 or 16 per row group, a contiguous block of k rows (row group rg
+// owns rows [rg * rpt, +rpt)); otherwise every RG-th row.  Either way each
+// load instruction of a wave covers whole contiguous state rows.  All rows of
+// a batch are loaded before any is used so that many 16-byte loads are in
+// flight per wave; the q-weighted column sums are then reduced across row
+// groups through LDS.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "sgla_internal.h"
 
@@ -55,29 +59,68 @@ recurrent_step_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   f32x4* S = reinterpret_cast<f32x4*>(state + unit * (int64_t)K * V);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
-  for (int r0 = rg; r0 < K; r0 += RG * BATCH) {
-    f32x4 s[BATCH];
+  const int rpt = K / RG;             // rows per row group when K % RG == 0
+  // the usual case: row group rg owns the contiguous rows [rg * rpt, +rpt),
+  // with rpt a compile-time count so nothing is predicated
+  auto block_rows = [&](auto rows_c) {
+    constexpr int R = decltype(rows_c)::value;
+    const int r0 = rg * R;
+    f32x4 s[R];
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      const int r = r0 + b * RG;
-      if (r < K) s[b] = __builtin_nontemporal_load(&S[(int64_t)r * TPR + cq]);
+    for (int b = 0; b < R; ++b) s[b] = __builtin_nontemporal_load(&S[(int64_t)(r0 + b) * TPR + cq]);
+    float kr[R], qr[R];
+#pragma unroll
+    for (int b = 0; b < R; ++b) {
+      kr[b] = to_f32(ku[r0 + b]);
+      qr[b] = to_f32(qu[r0 + b]);
     }
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      const int r = r0 + b * RG;
-      if (r < K) {
-        const float kr = to_f32(ku[r]);
-        const float qr = to_f32(qu[r]);
-        f32x4 x = s[b];
-        x.x = fmaf(gamma, x.x, kr * vv.x);
-        x.y = fmaf(gamma, x.y, kr * vv.y);
-        x.z = fmaf(gamma, x.z, kr * vv.z);
-        x.w = fmaf(gamma, x.w, kr * vv.w);
-        __builtin_nontemporal_store(x, &S[(int64_t)r * TPR + cq]);
-        acc.x = fmaf(x.x, qr, acc.x);
-        acc.y = fmaf(x.y, qr, acc.y);
-        acc.z = fmaf(x.z, qr, acc.z);
-        acc.w = fmaf(x.w, qr, acc.w);
+    for (int b = 0; b < R; ++b) {
+      f32x4 x = s[b];
+      x.x = fmaf(gamma, x.x, kr[b] * vv.x);
+      x.y = fmaf(gamma, x.y, kr[b] * vv.y);
+      x.z = fmaf(gamma, x.z, kr[b] * vv.z);
+      x.w = fmaf(gamma, x.w, kr[b] * vv.w);
+      __builtin_nontemporal_store(x, &S[(int64_t)(r0 + b) * TPR + cq]);
+      acc.x = fmaf(x.x, qr[b], acc.x);
+      acc.y = fmaf(x.y, qr[b], acc.y);
+      acc.z = fmaf(x.z, qr[b], acc.z);
+      acc.w = fmaf(x.w, qr[b], acc.w);
+    }
+  };
+  const bool even = K % RG == 0;
+  if (even && rpt == 16) {
+    block_rows(std::integral_constant<int, 16>{});
+  } else if (even && rpt == 8) {
+    block_rows(std::integral_constant<int, 8>{});
+  } else if (even && rpt == 4) {
+    block_rows(std::integral_constant<int, 4>{});
+  } else {
+    // general K: row group rg owns rows rg, rg + RG, ...
+    for (int r0 = rg; r0 < K; r0 += RG * BATCH) {
+      f32x4 s[BATCH];
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        const int r = r0 + b * RG;
+        if (r < K) s[b] = __builtin_nontemporal_load(&S[(int64_t)r * TPR + cq]);
+      }
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        const int r = r0 + b * RG;
+        if (r < K) {
+          const float kr = to_f32(ku[r]);
+          const float qr = to_f32(qu[r]);
+          f32x4 x = s[b];
+          x.x = fmaf(gamma, x.x, kr * vv.x);
+          x.y = fmaf(gamma, x.y, kr * vv.y);
+          x.z = fmaf(gamma, x.z, kr * vv.z);
+          x.w = fmaf(gamma, x.w, kr * vv.w);
+          __builtin_nontemporal_store(x, &S[(int64_t)r * TPR + cq]);
+          acc.x = fmaf(x.x, qr, acc.x);
+          acc.y = fmaf(x.y, qr, acc.y);
+          acc.z = fmaf(x.z, qr, acc.z);
+          acc.w = fmaf(x.w, qr, acc.w);
+        }
       }
     }
   }
