@@ -2,28 +2,30 @@
 """Benchmark of the Simple GLA hot path on one MI355X.
 
 A step is one pass of the whole chunked forward (chunk-local gate cumsum,
-inter-chunk state pass and output pass -- one fused kernel launch) over one
-batch of the dense bf16 prefill workload: B=4, T=2048, H=4, K=V=512, q/k/v
-~ N(0,1) in bf16, g = logsigmoid(N(0,1)), scale 1/sqrt(K), chunk 64, fp32 o,
-final state written.  ``value`` is tokens/s over the K timed steps with all
-inputs already resident in HBM (input/output copies are rotated so the 256 MB
-last-level cache cannot hold a step's working set).  Before the counted
-warmup steps the device runs untimed steps for --warm-seconds (default 1 s) so
-the timed steps see steady-state clocks.
+inter-chunk state pass and output pass: one sgla_chunk_fwd call, which for
+K >= 256 is a per-chunk preparation kernel followed by the state/output
+kernel) over one batch of the dense bf16 prefill workload: B=4, T=2048, H=4,
+K=V=512, q/k/v ~ N(0,1) in bf16, g = logsigmoid(N(0,1)), scale 1/sqrt(K),
+chunk 64, fp32 o, final state written.  ``value`` is tokens/s over the K timed
+steps with all inputs already resident in HBM (input/output copies are
+rotated so the 256 MB last-level cache cannot hold a step's working set).
+Before the counted warmup steps the device runs untimed steps for
+--warm-seconds (default 1 s) so the timed steps see steady-state clocks.
 
 The JSON line also carries:
-  roofline      -- the fused chunk kernel against its bound (HBM for this
-                   workload), from algorithmic bytes per launch and the
-                   kernel's average duration measured with HIP events on the
-                   stream it runs on; ``traffic`` comes from a committed
-                   rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it matches the
-                   current kernel sources, else null;
-  mfma          -- the same launch's algorithmic FLOPs against the bf16 dense
+  roofline      -- the chunked forward against its bound (HBM for this
+                   workload): algorithmic bytes per call divided by the call's
+                   average duration, measured with HIP events on the stream
+                   the kernels run on (the events bracket every launch of the
+                   call; ``kernel`` names them); ``traffic`` comes from a
+                   committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it
+                   matches the current kernel sources, else null;
+  mfma          -- the same call's algorithmic FLOPs against the bf16 dense
                    MFMA peak;
   decode        -- the in-place decode step on 256 sequences x 32 heads x
                    128 x 128 fp32 state, 64 consecutive steps, HBM GB/s;
-  cpu_baseline  -- the fp64 CPU oracle timed on the host cores on one full
-                   batch of the same workload (a reported baseline only).
+  cpu_baseline  -- the fp64 CPU oracle timed on the host cores on whole
+                   batches of the same workload (a reported baseline only).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -88,11 +90,15 @@ def chunk_algorithmic(inp) -> tuple[float, float]:
     return float(nbytes), float(flops)
 
 
-def chunk_kernel_name(inp) -> str:
-    """The kernel sgla_chunk_fwd dispatches for these inputs."""
+def chunk_kernels(inp) -> list:
+    """The kernels one sgla_chunk_fwd call dispatches for these inputs, in
+    launch order (K >= 256 bf16: a per-chunk preparation kernel, then the
+    state/output kernel)."""
     if inp["dtype"] != "bf16":
-        return "chunk_fwd_f32_kernel"
-    return "chunk_fwd_bf16_ks_kernel" if inp["K"] >= 256 else "chunk_fwd_bf16_kernel"
+        return ["chunk_fwd_f32_kernel"]
+    if inp["K"] >= 256:
+        return ["chunk_prep_bf16_kernel", "chunk_fwd_bf16_wide_kernel"]
+    return ["chunk_fwd_bf16_kernel"]
 
 
 def load_traffic(workload: str, kernel: str):
@@ -329,8 +335,9 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
-    roof["traffic"] = load_traffic(a.workload, chunk_kernel_name(inp))
-    roof.update({"kernel": chunk_kernel_name(inp),
+    roof["traffic"] = load_traffic(a.workload, "chunk_fwd")
+    roof.update({"kernel": "+".join(chunk_kernels(inp)),
+                 "launches_per_call": len(chunk_kernels(inp)),
                  "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
                  "kernel_ms_median": round(r["kernel_ms_median"], 5),
                  "algorithmic_bytes_per_launch": int(r["alg_bytes"]),

@@ -82,10 +82,6 @@ hipError_t launch_gate_cumsum(const float* g, float* gc, int32_t H, const SeqLay
 // V % 64 == 0.
 hipError_t launch_chunk_fwd_bf16(const ChunkFwdParams& p, hipStream_t stream);
 
-// bf16 q/k/v, MFMA path, key dimension streamed in 128-wide slices.  K in
-// {256,512}, V % 32 == 0.
-hipError_t launch_chunk_fwd_bf16_ks(const ChunkFwdParams& p, hipStream_t stream);
-
 // Wide-key bf16 path (K in {256,512}, V % 32 == 0): per-(chunk, head)
 // preparation, then the state and output passes reading its results.
 hipError_t launch_chunk_prep_bf16(const ChunkPrepParams& p, hipStream_t stream);

@@ -29,13 +29,18 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
 def _rows(d: str, suffix: str):
+    """Rows of every rocprofv3 CSV with this suffix under d (one file per
+    profiled process), each tagged with its file so dispatch ids of different
+    processes stay apart."""
     files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
     if not files:
         sys.exit(f"no *{suffix} under {d}")
     out = []
     for fn in files:
         with open(fn, newline="") as f:
-            out.extend(csv.DictReader(f))
+            for r in csv.DictReader(f):
+                r["_file"] = fn
+                out.append(r)
     return out
 
 
@@ -49,7 +54,7 @@ def trace(a):
              f"    {a.command}", "",
              "| kernel | dispatches | mean us | median us | min us | max us |", "|---|---|---|---|---|---|"]
     pat = re.compile(a.kernel)
-    timed = None
+    timed = []
     for name, v in sorted(by.items(), key=lambda kv: -sum(d for _, d in kv[1])):
         durs = [d / 1e3 for _, d in v]
         short = name if len(name) < 110 else name[:107] + "..."
@@ -57,35 +62,44 @@ def trace(a):
                      f"{statistics.median(durs):.2f} | {min(durs):.2f} | {max(durs):.2f} |")
         if pat.search(name):
             last = [d / 1e3 for _, d in sorted(v)[-a.steps:]]
-            timed = (name, len(last), statistics.mean(last), statistics.median(last))
-    if timed is None:
+            timed.append((short, len(last), statistics.mean(last), statistics.median(last)))
+    if not timed:
         sys.exit(f"no kernel matches {a.kernel}")
-    lines += ["", f"Timed launches (the last {timed[1]} dispatches of the kernel matching "
-              f"`{a.kernel}`, i.e. the ones bench.py times after its warm-up): "
-              f"mean {timed[2]:.2f} us, median {timed[3]:.2f} us.", ""]
+    lines += ["", f"Timed launches: the last {timed[0][1]} dispatches of each kernel matching "
+              f"`{a.kernel}` (the ones bench.py times after its warm-up):", ""]
+    lines += [f"- `{n}`: mean {mn:.2f} us, median {md:.2f} us" for n, _, mn, md in timed]
+    if len(timed) > 1:
+        lines += [f"- sum over the call's kernels: mean {sum(t[2] for t in timed):.2f} us, "
+                  f"median {sum(t[3] for t in timed):.2f} us"]
+    lines += [""]
     with open(a.out, "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
 
 
 def _counter(d: str, kernel: str, counter: str):
+    """Per-call value of a counter: for each kernel name matching the pattern,
+    the median over its dispatches, summed over the matching kernels (a call
+    that launches several kernels launches each once)."""
     pat = re.compile(kernel)
-    vals = {}
+    by = {}
     for r in _rows(d, "counter_collection.csv"):
         if r["Counter_Name"] == counter and pat.search(r["Kernel_Name"]):
-            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
-            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
-    if not vals:
+            key = (r["_file"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
+            per = by.setdefault(r["Kernel_Name"], {})
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not by:
         sys.exit(f"no {counter} rows for {kernel} under {d}")
-    return list(vals.values())
+    return [sum(statistics.median(v.values()) for v in by.values())], \
+        {name: statistics.median(v.values()) for name, v in by.items()}
 
 
 def traffic(a):
     copy_bytes = 512 << 20
-    fetch = _counter(a.fetch, a.kernel, "FETCH_SIZE")
-    write = _counter(a.write, a.kernel, "WRITE_SIZE")
-    cf = _counter(a.calib_fetch, a.calib_kernel, "FETCH_SIZE")
-    cw = _counter(a.calib_write, a.calib_kernel, "WRITE_SIZE")
+    fetch, fetch_by = _counter(a.fetch, a.kernel, "FETCH_SIZE")
+    write, write_by = _counter(a.write, a.kernel, "WRITE_SIZE")
+    cf, _ = _counter(a.calib_fetch, a.calib_kernel, "FETCH_SIZE")
+    cw, _ = _counter(a.calib_write, a.calib_kernel, "WRITE_SIZE")
     f_fetch = copy_bytes / (statistics.median(cf) * 1024.0)
     f_write = copy_bytes / (statistics.median(cw) * 1024.0)
     rd = statistics.median(fetch) * 1024.0 * f_fetch
@@ -95,7 +109,8 @@ def traffic(a):
     rec = {"kernel": a.name, "workload": a.workload, "hbm_bytes_per_launch": round(rd + wr),
            "read_bytes_per_launch": round(rd), "write_bytes_per_launch": round(wr),
            "fetch_size_kib_median": statistics.median(fetch),
-           "write_size_kib_median": statistics.median(write), "dispatches": len(fetch),
+           "write_size_kib_median": statistics.median(write),
+           "per_kernel_fetch_kib": fetch_by, "per_kernel_write_kib": write_by,
            "copy_calibration": {"bytes": copy_bytes, "fetch_size_kib": statistics.median(cf),
                                 "write_size_kib": statistics.median(cw),
                                 "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)},
@@ -105,8 +120,11 @@ def traffic(a):
     lines = [f"# HBM traffic of {a.name} on {a.workload} (rocprofv3 counters)", "",
              "Commands (from the repository root; one counter per run):", ""]
     lines += [f"    {c}" for c in a.command]
-    lines += ["", f"- dispatches of the kernel: {len(fetch)}; FETCH_SIZE median "
-              f"{statistics.median(fetch):.0f} KiB, WRITE_SIZE median {statistics.median(write):.0f} KiB",
+    lines += ["", f"- per call (median per kernel, summed over the call's kernels): FETCH_SIZE "
+              f"{statistics.median(fetch):.0f} KiB, WRITE_SIZE {statistics.median(write):.0f} KiB"]
+    lines += [f"  - `{n[:90]}`: FETCH_SIZE {fetch_by[n]:.0f} KiB, WRITE_SIZE {write_by.get(n, 0):.0f} KiB"
+              for n in fetch_by]
+    lines += [
               f"- copy calibration (elementwise copy of {copy_bytes} B): FETCH_SIZE "
               f"{statistics.median(cf):.0f} KiB, WRITE_SIZE {statistics.median(cw):.0f} KiB -> "
               f"factors {f_fetch:.4f} (fetch), {f_write:.4f} (write)",
