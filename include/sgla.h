@@ -75,8 +75,11 @@ int sgla_abi_version(void);
 const char *sgla_last_error(void);
 
 /*
- * Bytes of device workspace sgla_chunk_fwd needs for these arguments (the
- * chunk-local cumulative gates plus, for packed input, a per-sequence table).
+ * Bytes of device workspace sgla_chunk_fwd needs for these arguments: for
+ * packed input the sequence and chunk tables; for bf16 inputs with K = 256 or
+ * 512 also the per-(chunk, head) preparation records (gates, the masked
+ * intra-chunk q k^T as bf16 hi/lo, and the chunk's q and k^T rearranged for
+ * the state kernel: about (4 K + 8 KiB + 768 B) per 64-token chunk and head).
  * `cu_seqlens_host` is the same host array later passed to sgla_chunk_fwd, or
  * NULL for dense input.  Returns 0 if the arguments are invalid (the reason is
  * in sgla_last_error()); a valid call may also legitimately need 0 bytes only
@@ -93,6 +96,10 @@ size_t sgla_chunk_fwd_workspace_size(const sgla_chunk_args *args, const int64_t 
  *   (3) the output pass, O_n = scale * [ (Q_n K_n^T (.) M_n) V_n +
  *       diag(2^b) Q_n h_n ], M_ij = 2^{b_i - b_j} for j <= i, else 0.
  * Steps (2) and (3) run fused in one kernel per (sequence, head, V tile).
+ * For bf16 inputs with K = 256 or 512 a preparation kernel first computes,
+ * once per (chunk, head), step (1), the masked scale * Q K^T of step (3) and
+ * the operand rearrangements the fused kernel reads; the workspace carries
+ * them between the two launches, so a call enqueues two kernels.
  *
  * Arguments (device pointers unless stated):
  *   q, k            [B, T, H, K] in qkv_dtype
