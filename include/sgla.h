@@ -79,7 +79,7 @@ const char *sgla_last_error(void);
  * packed input the sequence and chunk tables; for bf16 inputs with K = 256 or
  * 512 also the per-(chunk, head) preparation records (gates, the masked
  * intra-chunk q k^T as bf16 hi/lo, and the chunk's q and k^T rearranged for
- * the state kernel: about (4 K + 8 KiB + 768 B) per 64-token chunk and head).
+ * the state kernel: 256 K + 16 KiB + 768 bytes per 64-token chunk and head).
  * `cu_seqlens_host` is the same host array later passed to sgla_chunk_fwd, or
  * NULL for dense input.  Returns 0 if the arguments are invalid (the reason is
  * in sgla_last_error()); a valid call may also legitimately need 0 bytes only
