@@ -94,6 +94,9 @@ SMALL_CASES = [
           initial_state=True),
     small("k256_v32_gamma", K=256, V=32, gate="gamma", T=200, normalize_k=True),
     small("k256_v64_t64", K=256, V=64, T=64, initial_state=True),
+    small("k256_no_gate", K=256, V=64, T=150, gate="none", H=2),
+    small("k512_strong_gate", K=512, V=64, T=150, B=1, H=2, gate_normalizer=0.1, scale=0.1),
+    small("k512_v512_16_tiles", K=512, V=512, T=100, B=1, H=1, initial_state=True),
     small("v192_multi_tile", K=64, V=192, T=97),
     small("gamma", gate="gamma", K=128, V=128, T=300, normalize_k=True),
     small("no_gate", gate="none", K=64, V=64, T=129),
@@ -124,10 +127,11 @@ def test_chunk_small(w):
     check_full(inp, o, ht)
 
 
-def test_chunk_bf16_output():
+@pytest.mark.parametrize("K", [128, 512])
+def test_chunk_bf16_output(K):
     """A bf16 o is the fp32 result rounded once: its error is bounded by the
     fp32 tolerance plus half a bf16 ulp of each element."""
-    inp = make_chunk_inputs(small("bf16o", K=128, V=128, T=257))
+    inp = make_chunk_inputs(small("bf16o", K=K, V=128, T=257, H=2))
     o, _ = run_chunk(inp, o_dtype=torch.bfloat16)
     o_ref, _ = oracle.fwd(inp["q"], inp["k"], inp["v"], g=inp["g"], scale=inp["scale"])
     rms = np.sqrt(np.mean(o_ref ** 2))
@@ -178,10 +182,11 @@ def test_named_workload_sampled(cfg):
 # cross-path properties
 # ---------------------------------------------------------------------------
 
-def test_varlen_equals_per_sequence_bitwise():
+@pytest.mark.parametrize("K", [128, 512])
+def test_varlen_equals_per_sequence_bitwise(K):
     """Packed sequences give exactly the per-sequence results (each sequence
     is processed by the same code from its own start)."""
-    w = small("pack", B=1, T=0, H=2, K=128, V=128, fixed_lengths=(100, 64, 257, 1),
+    w = small("pack", B=1, T=0, H=2, K=K, V=128, fixed_lengths=(100, 64, 257, 1),
               initial_state=True)
     inp = make_chunk_inputs(w)
     o, ht = run_chunk(inp)
@@ -198,10 +203,11 @@ def test_varlen_equals_per_sequence_bitwise():
         assert np.array_equal(hn[0], ht[n])
 
 
-def test_split_at_chunk_boundary_bitwise():
+@pytest.mark.parametrize("K", [128, 512])
+def test_split_at_chunk_boundary_bitwise(K):
     """Running tokens [0, 128) then [128, T) from the carried state equals one
     pass exactly (the split falls on a chunk boundary)."""
-    inp = make_chunk_inputs(small("split", B=1, T=300, H=2, K=128, V=64, initial_state=True))
+    inp = make_chunk_inputs(small("split", B=1, T=300, H=2, K=K, V=64, initial_state=True))
     o, ht = run_chunk(inp)
     a, b = dict(inp), dict(inp)
     for key in ("q", "k", "v", "g"):
@@ -214,16 +220,18 @@ def test_split_at_chunk_boundary_bitwise():
     assert np.array_equal(hb, ht)
 
 
-def test_deterministic():
-    inp = make_chunk_inputs(small("det", K=128, V=128, T=333, initial_state=True))
+@pytest.mark.parametrize("K", [128, 512])
+def test_deterministic(K):
+    inp = make_chunk_inputs(small("det", K=K, V=128, T=333, initial_state=True))
     o1, h1 = run_chunk(inp)
     o2, h2 = run_chunk(inp)
     assert np.array_equal(o1, o2) and np.array_equal(h1, h2)
 
 
-def test_in_place_state():
+@pytest.mark.parametrize("K", [64, 512])
+def test_in_place_state(K):
     """final_state may alias initial_state exactly."""
-    inp = make_chunk_inputs(small("inplace", K=64, V=64, T=100, initial_state=True))
+    inp = make_chunk_inputs(small("inplace", K=K, V=64, T=100, initial_state=True))
     d = device_inputs(inp)
     o_ref, h_ref = run_chunk(inp)
     state = d["initial_state"]
