@@ -39,14 +39,14 @@ def _bind(lib):
     dp = ctypes.POINTER(ctypes.c_double)
     lp = ctypes.POINTER(ctypes.c_int64)
     lib.sgla_oracle_fwd.restype = ctypes.c_int
-    lib.sgla_oracle_fwd.argtypes = [ctypes.c_int] * 5 + [dp] * 5 + [ctypes.c_double, dp, lp,
+    lib.sgla_oracle_fwd.argtypes = [ctypes.c_int] * 6 + [dp] * 5 + [ctypes.c_double, dp, lp,
                                                                      ctypes.c_int, dp, dp,
                                                                      ctypes.c_int]
     lib.sgla_oracle_chunk_local_cumsum.restype = ctypes.c_int
     lib.sgla_oracle_chunk_local_cumsum.argtypes = [ctypes.c_int] * 3 + [dp, lp, ctypes.c_int,
                                                                         ctypes.c_int, dp]
     lib.sgla_oracle_step.restype = ctypes.c_int
-    lib.sgla_oracle_step.argtypes = [ctypes.c_int] * 4 + [dp] * 4 + [ctypes.c_double, dp, dp,
+    lib.sgla_oracle_step.argtypes = [ctypes.c_int] * 5 + [dp] * 5 + [ctypes.c_double, dp, dp,
                                                                      ctypes.c_int]
     return lib
 
@@ -92,12 +92,15 @@ def fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None, cu_seqlen
         output_final_state=True, nthreads=None, lib=None):
     """Token-by-token forward.
 
-    q, k: [B, T, H, K]; v: [B, T, H, V]; g: [B, T, H] or None; g_gamma: [H] or None;
-    initial_state: [N, H, K, V] or None; cu_seqlens: int [N+1] or None (then N = B).
+    q: [B, T, H, K]; k: [B, T, Hkv, K]; v: [B, T, Hkv, V] (Hkv divides H: query
+    head h reads kv head h // (H // Hkv)); g: [B, T, H] or None; g_gamma: [H]
+    or None; initial_state: [N, H, K, V] or None; cu_seqlens: int [N+1] or
+    None (then N = B).
     Returns (o [B, T, H, V], final_state [N, H, K, V] or None), both float64.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, H, K = q.shape
+    Hkv = k.shape[2]
     V = v.shape[-1]
     if scale is None:
         scale = K ** -0.5
@@ -112,7 +115,7 @@ def fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None, cu_seqlen
     o = np.zeros((B, T, H, V), dtype=np.float64)
     ht = np.zeros((N, H, K, V), dtype=np.float64) if output_final_state else None
     lib = lib or load()
-    rc = lib.sgla_oracle_fwd(B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(g_gamma),
+    rc = lib.sgla_oracle_fwd(B, T, H, Hkv, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(g_gamma),
                              float(scale), _ptr(h0),
                              None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                              N, _ptr(o), _ptr(ht), int(nthreads or default_threads()))
@@ -121,20 +124,22 @@ def fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None, cu_seqlen
     return o, ht
 
 
-def step(q, k, v, g, state, scale=None, nthreads=None, lib=None):
-    """One decode step.  q, k: [N, H, K]; v: [N, H, V]; g: [N, H];
+def step(q, k, v, g, state, scale=None, g_gamma=None, nthreads=None, lib=None):
+    """One decode step.  q: [N, H, K]; k: [N, Hkv, K]; v: [N, Hkv, V];
+    g: [N, H] or None; g_gamma: [H] or None (at most one);
     state: [N, H, K, V] (not modified; the updated copy is returned).
     Returns (o [N, H, V], new_state [N, H, K, V]), float64."""
-    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    q, k, v, g, g_gamma = _f64(q), _f64(k), _f64(v), _f64(g), _f64(g_gamma)
     S = np.array(state, dtype=np.float64, order="C", copy=True)
     N, H, K = q.shape
+    Hkv = k.shape[1]
     V = v.shape[-1]
     if scale is None:
         scale = K ** -0.5
     o = np.zeros((N, H, V), dtype=np.float64)
     lib = lib or load()
-    rc = lib.sgla_oracle_step(N, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), float(scale),
-                              _ptr(S), _ptr(o), int(nthreads or default_threads()))
+    rc = lib.sgla_oracle_step(N, H, Hkv, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(g_gamma),
+                              float(scale), _ptr(S), _ptr(o), int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError(f"sgla_oracle_step rejected its arguments (code {rc})")
     return o, S

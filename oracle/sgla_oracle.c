@@ -26,7 +26,13 @@
  * its last token is final_state[n].
  *
  * Decode step (section 四, the fused_recurrent path for short inputs): one
- * token per sequence, S <- exp(g) S + k v^T in place, o = scale S^T q.
+ * token per sequence, S <- exp(g) S + k v^T in place, o = scale S^T q, with g
+ * per (sequence, head) or a per-head constant g_gamma.
+ *
+ * Grouped kv heads (the relinear pages, GQA: k and v have Hkv heads and query
+ * head h reads kv head h / (H / Hkv), the contiguous grouping of repeat_kv):
+ * every query head keeps its own state and gate; only the k and v rows are
+ * shared by the H / Hkv query heads of a group.
  *
  * Parity pins for this file live in tests/test_oracle_pins.py.  The
  * SGLA_ORACLE_MUTANT macro (default 0) exists only so that the test suite can
@@ -50,7 +56,7 @@ typedef struct {
 
 typedef struct {
     int T_row;          /* unused for packed input */
-    int H, K, V;
+    int H, Hkv, K, V;
     const double *q, *k, *v, *g, *g_gamma, *h0;
     double scale;
     double *o, *ht;
@@ -63,7 +69,12 @@ typedef struct {
 /* One (sequence, head) recurrence, token by token. */
 static void run_unit(const fwd_job_t *J, const unit_t *u, double *S)
 {
-    const int H = J->H, K = J->K, V = J->V, h = u->head;
+    const int H = J->H, Hkv = J->Hkv, K = J->K, V = J->V, h = u->head;
+#if SGLA_ORACLE_MUTANT == 8
+    const int hk = h % Hkv;                 /* planted: interleaved grouping */
+#else
+    const int hk = h / (H / Hkv);           /* kv head of query head h */
+#endif
     const size_t KV = (size_t)K * V;
 #if SGLA_ORACLE_MUTANT == 3
     if (J->h0)
@@ -78,8 +89,8 @@ static void run_unit(const fwd_job_t *J, const unit_t *u, double *S)
     for (int64_t i = 0; i < u->len; ++i) {
         const int64_t t = u->bos + i;
         const double *qt = J->q + ((size_t)t * H + h) * K;
-        const double *kt = J->k + ((size_t)t * H + h) * K;
-        const double *vt = J->v + ((size_t)t * H + h) * V;
+        const double *kt = J->k + ((size_t)t * Hkv + hk) * K;
+        const double *vt = J->v + ((size_t)t * Hkv + hk) * V;
         double logg = 0.0;
 #if SGLA_ORACLE_MUTANT == 4
         if (J->g) logg = J->g[(size_t)h * J->T_row + (t % (J->T_row > 0 ? J->T_row : 1))];
@@ -145,7 +156,8 @@ static void *fwd_worker(void *arg)
 
 /*
  * Forward over all sequences and heads.
- *   q, k : [B, T, H, K]   v, o : [B, T, H, V]   (packed: B = 1, T = total tokens)
+ *   q : [B, T, H, K]   k : [B, T, Hkv, K]   v : [B, T, Hkv, V]   o : [B, T, H, V]
+ *   (packed: B = 1, T = total tokens; Hkv divides H; Hkv = H is plain MHA)
  *   g    : [B, T, H] log gates, or NULL
  *   g_gamma : [H] per-head log decay, or NULL (at most one of g / g_gamma;
  *             neither means no decay)
@@ -153,13 +165,14 @@ static void *fwd_worker(void *arg)
  *   cu_seqlens : [num_seqs + 1] token offsets (packed) or NULL (dense)
  * Returns 0 on success, negative on a malformed argument.
  */
-int sgla_oracle_fwd(int B, int T, int H, int K, int V,
+int sgla_oracle_fwd(int B, int T, int H, int Hkv, int K, int V,
                     const double *q, const double *k, const double *v,
                     const double *g, const double *g_gamma, double scale,
                     const double *h0, const int64_t *cu_seqlens, int num_seqs,
                     double *o, double *ht, int nthreads)
 {
     if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return -1;
+    if (Hkv <= 0 || H % Hkv != 0) return -6;
     if (g && g_gamma) return -2;
     if (cu_seqlens && B != 1) return -3;
     int N = cu_seqlens ? num_seqs : B;
@@ -183,7 +196,7 @@ int sgla_oracle_fwd(int B, int T, int H, int K, int V,
         }
     }
     fwd_job_t J;
-    J.T_row = T; J.H = H; J.K = K; J.V = V;
+    J.T_row = T; J.H = H; J.Hkv = Hkv; J.K = K; J.V = V;
     J.q = q; J.k = k; J.v = v; J.g = g; J.g_gamma = g_gamma; J.h0 = h0;
     J.scale = scale; J.o = o; J.ht = ht; J.units = units; J.n_units = n_units; J.next = 0;
     pthread_mutex_init(&J.mu, NULL);
@@ -205,8 +218,8 @@ int sgla_oracle_fwd(int B, int T, int H, int K, int V,
 }
 
 typedef struct {
-    int H, K, V;
-    const double *q, *k, *v, *g;
+    int H, Hkv, K, V;
+    const double *q, *k, *v, *g, *g_gamma;
     double scale;
     double *S, *o;
     int64_t n_units, next;
@@ -222,11 +235,20 @@ static void *step_worker(void *arg)
         int64_t u = J->next++;
         pthread_mutex_unlock(&J->mu);
         if (u >= J->n_units) break;
-        /* unit u = (sequence n, head h) flattened as n * H + h */
+        /* unit u = (sequence n, head h) flattened as n * H + h; its k and v
+         * rows are those of kv head h / (H / Hkv) of sequence n */
+        const int64_t n = u / J->H;
+        const int h = (int)(u % J->H);
+        const int64_t ukv = n * J->Hkv + h / (J->H / J->Hkv);
         const double *qt = J->q + (size_t)u * K;
-        const double *kt = J->k + (size_t)u * K;
-        const double *vt = J->v + (size_t)u * V;
-        const double gamma = exp(J->g[u]);
+        const double *kt = J->k + (size_t)ukv * K;
+        const double *vt = J->v + (size_t)ukv * V;
+#if SGLA_ORACLE_MUTANT == 9
+        const double logg = J->g ? J->g[u] : (J->g_gamma ? J->g_gamma[n % J->H] : 0.0);
+#else
+        const double logg = J->g ? J->g[u] : (J->g_gamma ? J->g_gamma[h] : 0.0);
+#endif
+        const double gamma = exp(logg);
         double *S = J->S + (size_t)u * K * V;
         double *ot = J->o + (size_t)u * V;
         for (int a = 0; a < K; ++a)
@@ -246,17 +268,22 @@ static void *step_worker(void *arg)
 
 /*
  * One decode step for N sequences x H heads.
- *   q, k : [N, H, K]  v, o : [N, H, V]  g : [N, H] log gate
- *   S    : [N, H, K, V], updated in place.
+ *   q : [N, H, K]  k : [N, Hkv, K]  v : [N, Hkv, V]  o : [N, H, V]
+ *   g : [N, H] log gate, or g_gamma : [H] per-head log decay (at most one;
+ *       neither means no decay)
+ *   S : [N, H, K, V], updated in place.
  */
-int sgla_oracle_step(int N, int H, int K, int V,
+int sgla_oracle_step(int N, int H, int Hkv, int K, int V,
                      const double *q, const double *k, const double *v,
-                     const double *g, double scale, double *S, double *o,
-                     int nthreads)
+                     const double *g, const double *g_gamma, double scale,
+                     double *S, double *o, int nthreads)
 {
-    if (N < 0 || H <= 0 || K <= 0 || V <= 0 || !g || !S) return -1;
+    if (N < 0 || H <= 0 || K <= 0 || V <= 0 || !S) return -1;
+    if (g && g_gamma) return -2;
+    if (Hkv <= 0 || H % Hkv != 0) return -6;
     step_job_t J;
-    J.H = H; J.K = K; J.V = V; J.q = q; J.k = k; J.v = v; J.g = g;
+    J.H = H; J.Hkv = Hkv; J.K = K; J.V = V; J.q = q; J.k = k; J.v = v; J.g = g;
+    J.g_gamma = g_gamma;
     J.scale = scale; J.S = S; J.o = o;
     J.n_units = (int64_t)N * H; J.next = 0;
     pthread_mutex_init(&J.mu, NULL);

@@ -319,10 +319,69 @@ def pin_chunk_local_cumsum(lib, seed=10, H=3):
     return True
 
 
+def pin_gqa_is_repeated_mha(lib, seed=11, H=6, Hkv=2, K=4, V=3):
+    """Grouped kv heads (page "relinear", its GQA target; page "flash-linear-
+    attention 中的 Simple GLA", section 四, num_kv_heads dividing num_heads):
+    query head h reads kv head h // (H // Hkv), the contiguous grouping of
+    repeat_kv.  So the forward with Hkv kv heads equals, bit for bit, the
+    (brute-force pinned) multi-head forward on k and v whose every head is
+    repeated H // Hkv times in a row -- for packed sequences, per-token gates,
+    g_gamma and one shared kv head (MQA) alike."""
+    rng = np.random.default_rng(seed)
+    cu = np.array([0, 13, 50, 71], dtype=np.int64)
+    T = int(cu[-1])
+    q = _rand(rng, 1, T, H, K)
+    g = logsigmoid(_rand(rng, 1, T, H))
+    S0 = _rand(rng, 3, H, K, V)
+    for hkv in (Hkv, 1):
+        rep = H // hkv
+        k, v = _rand(rng, 1, T, hkv, K), _rand(rng, 1, T, hkv, V)
+        kr, vr = np.repeat(k, rep, axis=2), np.repeat(v, rep, axis=2)
+        o, ht = oracle.fwd(q, k, v, g=g, initial_state=S0, cu_seqlens=cu, lib=lib)
+        om, hm = oracle.fwd(q, kr, vr, g=g, initial_state=S0, cu_seqlens=cu, lib=lib)
+        if not (np.array_equal(o, om) and np.array_equal(ht, hm)):
+            return False
+        gam = retnet_gamma(H).astype(np.float64)
+        o, ht = oracle.fwd(q, k, v, g_gamma=gam, scale=0.3, lib=lib)
+        om, hm = oracle.fwd(q, kr, vr, g_gamma=gam, scale=0.3, lib=lib)
+        if not (np.array_equal(o, om) and np.array_equal(ht, hm)):
+            return False
+    return True
+
+
+def pin_step_variants(lib, seed=12, N=3, H=4, Hkv=2, K=3, V=5):
+    """Decode step with a per-head decay g_gamma (section 二: g and g_gamma are
+    alternatives) and with grouped kv heads: it equals the one-token forward
+    from the same state (forward pinned above), g_gamma equals the broadcast
+    per-token gate bit for bit, no gate at all equals g = 0, and Hkv kv heads
+    equal the repeated multi-head step bit for bit."""
+    rng = np.random.default_rng(seed)
+    q, k, v = _rand(rng, N, H, K), _rand(rng, N, Hkv, K), _rand(rng, N, Hkv, V)
+    S = _rand(rng, N, H, K, V)
+    gam = retnet_gamma(H).astype(np.float64)
+    o1, S1 = oracle.step(q, k, v, None, S, scale=0.6, g_gamma=gam, lib=lib)
+    of, hf = oracle.fwd(q[:, None], k[:, None], v[:, None], g_gamma=gam, scale=0.6,
+                        initial_state=S, lib=lib)
+    if _rel(o1, of[:, 0]) > 1e-14 or _rel(S1, hf) > 1e-14:
+        return False
+    o2, S2 = oracle.step(q, k, v, np.broadcast_to(gam, (N, H)).copy(), S, scale=0.6, lib=lib)
+    if not (np.array_equal(o1, o2) and np.array_equal(S1, S2)):
+        return False
+    o3, S3 = oracle.step(q, k, v, None, S, lib=lib)
+    o4, S4 = oracle.step(q, k, v, np.zeros((N, H)), S, lib=lib)
+    if not (np.array_equal(o3, o4) and np.array_equal(S3, S4)):
+        return False
+    rep = H // Hkv
+    o5, S5 = oracle.step(q, np.repeat(k, rep, axis=1), np.repeat(v, rep, axis=1), None, S,
+                         scale=0.6, g_gamma=gam, lib=lib)
+    return np.array_equal(o1, o5) and np.array_equal(S1, S5)
+
+
 ALL_PINS = [pin_chunk_local_cumsum, pin_hand_example, pin_brute_force, pin_zero_gate, pin_full_forget,
             pin_split_sequence, pin_varlen_equals_per_sequence, pin_chunk_form,
             pin_gamma_is_broadcast_g, pin_retnet_closed_form, pin_invariants,
-            pin_prefill_then_decode, pin_step_brute_force]
+            pin_prefill_then_decode, pin_step_brute_force, pin_gqa_is_repeated_mha,
+            pin_step_variants]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -365,6 +424,8 @@ MUTANTS = {
     5: "scale dropped from the output",
     6: "output contracts the state with k instead of q",
     7: "decode step forms v k^T instead of k v^T",
+    8: "query head h reads kv head h % Hkv (interleaved) instead of h // (H / Hkv)",
+    9: "decode step reads g_gamma by sequence instead of by head",
 }
 
 
