@@ -10,10 +10,13 @@ library has not been built, importing this package raises ImportError.
 
 Operator (page "flash-linear-attention 中的 Simple GLA", section 一):
     S_t = exp(g_t) S_{t-1} + k_t v_t^T,    o_t = scale * S_t^T q_t
-API conventions follow section 二 of that page: q, k [B, T, H, K], v [B, T,
-H, V], g [B, T, H] log gates or g_gamma [H] per-head log decay (not both),
-scale defaulting to 1/sqrt(K), states [N, H, K, V], cu_seqlens [N + 1] with
-B == 1 for packed input, chunk_size a power of two (64).
+API conventions follow section 二 of that page: q [B, T, H, K], k [B, T, Hkv,
+K], v [B, T, Hkv, V], g [B, T, H] log gates or g_gamma [H] per-head log decay
+(not both), scale defaulting to 1/sqrt(K), states [N, H, K, V], cu_seqlens
+[N + 1] with B == 1 for packed input, chunk_size a power of two (64).  The kv
+head count Hkv is read from k's shape and must divide H: query head h reads kv
+head h // (H // Hkv) (grouped-query attention, page "relinear", its GQA
+target); Hkv == H is plain multi-head attention.
 """
 from __future__ import annotations
 
@@ -25,7 +28,7 @@ import torch
 __all__ = ["chunk_fwd", "recurrent_step", "chunk_local_cumsum", "library_path", "lib",
            "SglaError", "ABI_VERSION"]
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsgla.so")
 
@@ -42,7 +45,7 @@ class _ChunkArgs(ctypes.Structure):
                 ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("chunk_size", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32),
                 ("o_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("output_final_state", ctypes.c_int32)]
+                ("output_final_state", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -53,7 +56,7 @@ def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
             f"libsgla.so is not built ({_LIB_PATH} missing); run "
-            "`python -m gated_linear_attention_amd.build` (hipcc, gfx950). There is no fallback.")
+            "`python gated_linear_attention_amd/build.py` (hipcc, gfx950). There is no fallback.")
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     pargs = ctypes.POINTER(_ChunkArgs)
@@ -68,8 +71,8 @@ def _load():
     lib.sgla_chunk_local_cumsum.restype = ctypes.c_int
     lib.sgla_chunk_local_cumsum.argtypes = [pargs, vp, vp, vp, vp, sz, vp]
     lib.sgla_recurrent_step.restype = ctypes.c_int
-    lib.sgla_recurrent_step.argtypes = [i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp,
-                                        vp, vp]
+    lib.sgla_recurrent_step.argtypes = [i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp,
+                                        vp, vp, vp, vp]
     if lib.sgla_abi_version() != ABI_VERSION:
         raise ImportError(f"libsgla ABI {lib.sgla_abi_version()} != binding ABI {ABI_VERSION}")
     return lib
@@ -128,8 +131,18 @@ def _host_cu(cu_seqlens):
     return cu
 
 
-def _chunk_args(B, T, H, K, V, N, chunk_size, qkv, o_dtype, scale, out_final):
-    return _ChunkArgs(B, T, H, K, V, N, chunk_size, qkv, o_dtype, float(scale), int(out_final))
+def _chunk_args(B, T, H, K, V, N, chunk_size, qkv, o_dtype, scale, out_final, Hkv=0):
+    return _ChunkArgs(B, T, H, K, V, N, chunk_size, qkv, o_dtype, float(scale), int(out_final),
+                      int(Hkv))
+
+
+def _kv_heads(k, H, axis):
+    if not isinstance(k, torch.Tensor) or k.dim() <= axis:
+        raise ValueError("k must be a tensor with a kv-head axis")
+    Hkv = k.shape[axis]
+    if Hkv < 1 or H % Hkv != 0:
+        raise ValueError(f"the kv head count of k ({Hkv}) must divide the query head count ({H})")
+    return Hkv
 
 
 def _workspace_size(args, cu_ptr) -> int:
@@ -155,10 +168,11 @@ def chunk_fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None,
     if v.dim() != 4:
         raise ValueError("v must be a 4-D tensor [B, T, H, V]")
     V = v.shape[-1]
+    Hkv = _kv_heads(k, H, 2)
     qkv = _dtype_code(q.dtype, "q")
     _check_dev("q", q, dev)
-    _check_dev("k", k, dev, q.dtype, (B, T, H, K))
-    _check_dev("v", v, dev, q.dtype, (B, T, H, V))
+    _check_dev("k", k, dev, q.dtype, (B, T, Hkv, K))
+    _check_dev("v", v, dev, q.dtype, (B, T, Hkv, V))
     if g is not None and g_gamma is not None:
         raise ValueError("g and g_gamma are mutually exclusive; pass at most one")
     _check_dev("g", g, dev, torch.float32, (B, T, H))
@@ -174,7 +188,7 @@ def chunk_fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None,
     if scale is None:
         scale = K ** -0.5
     od = _dtype_code(o_dtype, "o_dtype")
-    args = _chunk_args(B, T, H, K, V, N, chunk_size, qkv, od, scale, output_final_state)
+    args = _chunk_args(B, T, H, K, V, N, chunk_size, qkv, od, scale, output_final_state, Hkv)
     cu_ptr = None if cu is None else ctypes.c_void_p(cu.data_ptr())
     ws_bytes = _workspace_size(args, cu_ptr)
     if out is None:
@@ -214,20 +228,26 @@ def chunk_local_cumsum(g, chunk_size=64, cu_seqlens=None):
     return gc
 
 
-def recurrent_step(q, k, v, g, state, scale=None, o_dtype=torch.float32, out=None):
+def recurrent_step(q, k, v, g, state, scale=None, o_dtype=torch.float32, out=None,
+                   g_gamma=None):
     """One decode step; ``state`` [N, H, K, V] float32 is updated in place.
-    q, k [N, H, K], v [N, H, V] (bf16 or float32), g [N, H] float32.
-    Returns o [N, H, V]."""
+    q [N, H, K], k [N, Hkv, K], v [N, Hkv, V] (bf16 or float32); g [N, H]
+    float32 log gate or None; g_gamma [H] float32 per-head log decay or None
+    (at most one; neither means no decay).  Returns o [N, H, V]."""
     if not isinstance(q, torch.Tensor) or q.dim() != 3:
         raise ValueError("q must be a 3-D tensor [N, H, K]")
     dev = q.device
     N, H, K = q.shape
     V = v.shape[-1]
+    Hkv = _kv_heads(k, H, 1)
     qkv = _dtype_code(q.dtype, "q")
     _check_dev("q", q, dev)
-    _check_dev("k", k, dev, q.dtype, (N, H, K))
-    _check_dev("v", v, dev, q.dtype, (N, H, V))
+    _check_dev("k", k, dev, q.dtype, (N, Hkv, K))
+    _check_dev("v", v, dev, q.dtype, (N, Hkv, V))
+    if g is not None and g_gamma is not None:
+        raise ValueError("g and g_gamma are mutually exclusive; pass at most one")
     _check_dev("g", g, dev, torch.float32, (N, H))
+    _check_dev("g_gamma", g_gamma, dev, torch.float32, (H,))
     _check_dev("state", state, dev, torch.float32, (N, H, K, V))
     if scale is None:
         scale = K ** -0.5
@@ -237,8 +257,8 @@ def recurrent_step(q, k, v, g, state, scale=None, o_dtype=torch.float32, out=Non
     else:
         _check_dev("out", out, dev, o_dtype, (N, H, V))
         o = out
-    st = lib.sgla_recurrent_step(N, H, K, V, float(scale), qkv, od, _ptr(q), _ptr(k), _ptr(v),
-                                 _ptr(g), _ptr(state), _ptr(o), _stream(dev))
+    st = lib.sgla_recurrent_step(N, H, Hkv, K, V, float(scale), qkv, od, _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(g), _ptr(g_gamma), _ptr(state), _ptr(o), _stream(dev))
     if st != _OK:
         _raise(st, "sgla_recurrent_step")
     return o

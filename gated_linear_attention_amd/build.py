@@ -7,7 +7,8 @@ so that a process using torch for device memory and streams has exactly one
 HIP runtime and torch's stream handles are valid in libsgla.  Without torch
 the ROCm installation's runtime is used.
 
-Usage: python -m gated_linear_attention_amd.build   (or build() from Python)
+Usage: python gated_linear_attention_amd/build.py   (or build() from Python).  Run it
+as a script: importing the package loads the library that is already built.
 """
 from __future__ import annotations
 

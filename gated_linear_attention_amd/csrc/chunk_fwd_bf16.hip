@@ -19,8 +19,9 @@
 //
 // Layout of the work (gfx950, wave64, v_mfma_f32_16x16x32_bf16):
 //   * one workgroup of 4 waves per (sequence, head, 64-wide V tile); the
-//     workgroups of one (sequence, head) share an XCD so the second read of its
-//     q and k rows is served by that XCD's L2;
+//     workgroups of one (sequence, kv head) share an XCD so repeated reads of
+//     its q, k and v rows (other V tiles, other query heads of a kv group)
+//     are served by that XCD's L2;
 //   * wave w owns state columns [16w, 16w + 16) of the tile for all K rows, in
 //     MFMA accumulator registers (fp32), carried across chunks without ever
 //     leaving the chip -- only the final state is written;
@@ -41,6 +42,7 @@
 #include "gate_scan.h"
 #include "mfma_common.h"
 #include "sgla_internal.h"
+#include "unit_map.h"
 
 namespace sgla {
 namespace {
@@ -93,7 +95,7 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                       const bf16* __restrict__ v, const float* __restrict__ g,
                       const float* __restrict__ g_gamma, const float* __restrict__ h0,
                       TOut* __restrict__ o, float* __restrict__ ht, float scale, int32_t H,
-                      int32_t V, SeqLayout seqs) {
+                      int32_t Hkv, int32_t V, SeqLayout seqs) {
   using L = Layout<K>;
   constexpr int NT = L::NT;
   constexpr int SEG = K / 8;                 // 16-byte segments per q/k row
@@ -104,15 +106,9 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
 
   // ---- which (sequence, head, V tile) this workgroup owns ----------------
-  const int nvt = V / VT;
-  const int num_units = seqs.num_seqs * H;
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int unit = (slot / nvt) * kXcds + xcd;
-  const int vt = slot % nvt;
-  if (unit >= num_units) return;
-  const int rank = unit / H;
-  const int hd = unit - rank * H;
+  const UnitMap um = map_unit(blockIdx.x, V / VT, Hkv, H / Hkv, seqs.num_seqs);
+  if (!um.valid) return;
+  const int rank = um.rank, hd = um.hd, hk = um.hk, vt = um.vt;
   int64_t bos;
   int32_t len, seq;
   if (seqs.seq_table != nullptr) {
@@ -142,11 +138,13 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int own1 = kh == 0 ? 3 : 2;
   // c tiles in q.h order: this wave's two, then its partner's (w ^ 4) two
   const int ctile[4] = {own0, own1, kh == 0 ? 1 : 0, kh == 0 ? 2 : 3};
-  const int RSK = H * K;                    // token stride of q and k (elements)
-  const int RSV = H * V;                    // token stride of v and o
+  const int RSQ = H * K;                    // token stride of q (elements)
+  const int RSK = Hkv * K;                  // token stride of k
+  const int RSV = Hkv * V;                  // token stride of v
+  const int RSO = H * V;                    // token stride of o
   const bf16* qb = q + (bos * H + hd) * (int64_t)K;
-  const bf16* kb = k + (bos * H + hd) * (int64_t)K;
-  const bf16* vb = v + (bos * H + hd) * (int64_t)V + vt * VT;
+  const bf16* kb = k + (bos * Hkv + hk) * (int64_t)K;
+  const bf16* vb = v + (bos * Hkv + hk) * (int64_t)V + vt * VT;
   const float* gb = g != nullptr ? g + bos * H + hd : nullptr;
   TOut* ob = o + (bos * H + hd) * (int64_t)V + vt * VT;     // workgroup-uniform base
   const uint32_t ocol = (16 * vc + 4 * g4) * (uint32_t)sizeof(TOut);   // lane's 4 columns
@@ -196,15 +194,14 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int cl = max(0, min(C, len - m * C));
     st.len = cl;
     const int64_t tok = (int64_t)m * C;
-    const auto rq = make_rsrc(qb + tok * RSK, (uint32_t)cl * RSK * 2);
+    const auto rq = make_rsrc(qb + tok * RSQ, (uint32_t)cl * RSQ * 2);
     const auto rk = make_rsrc(kb + tok * RSK, (uint32_t)cl * RSK * 2);
     const auto rv = make_rsrc(vb + tok * RSV, (uint32_t)cl * RSV * 2);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       const int s = tid + i * NT;
-      const uint32_t off = ((s / SEG) * RSK + (s % SEG) * 8) * 2;
-      st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
-      st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+      st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((s / SEG) * RSQ + (s % SEG) * 8) * 2, 0, 0);
+      st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((s / SEG) * RSK + (s % SEG) * 8) * 2, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -399,10 +396,10 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const f32x4* x = sX(px);
     const f32x4 x0 = x[((w ^ 4) * 2 + 0) * 64 + lane];
     const f32x4 x1 = x[((w ^ 4) * 2 + 1) * 64 + lane];
-    const auto ro = make_rsrc(ob + (int64_t)m * C * RSV, (uint32_t)cl * RSV * sizeof(TOut));
+    const auto ro = make_rsrc(ob + (int64_t)m * C * RSO, (uint32_t)cl * RSO * sizeof(TOut));
     const uint32_t c0 = 16 * own0 + r, c1 = 16 * own1 + r;
-    store4<TOut>(ro, c0 * RSV * (uint32_t)sizeof(TOut) + ocol, mine0 + x0);
-    store4<TOut>(ro, c1 * RSV * (uint32_t)sizeof(TOut) + ocol, mine1 + x1);
+    store4<TOut>(ro, c0 * RSO * (uint32_t)sizeof(TOut) + ocol, mine0 + x0);
+    store4<TOut>(ro, c1 * RSO * (uint32_t)sizeof(TOut) + ocol, mine1 + x1);
   };
 
   Stage st0, st1;
@@ -481,15 +478,12 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
 template <int K, typename TOut>
 hipError_t launch_k(const ChunkFwdParams& p, hipStream_t stream) {
-  const int num_units = p.seqs.num_seqs * p.H;
-  if (num_units == 0) return hipSuccess;
-  const int nvt = p.V / VT;
-  const int groups = (num_units + kXcds - 1) / kXcds;
-  const dim3 grid((unsigned)(groups * kXcds * nvt));
+  if (p.seqs.num_seqs == 0) return hipSuccess;
+  const dim3 grid((unsigned)unit_grid(p.seqs.num_seqs, p.Hkv, p.H / p.Hkv, p.V / VT));
   hipLaunchKernelGGL((chunk_fwd_bf16_kernel<K, TOut>), grid, dim3(Layout<K>::NT), 0, stream,
                      static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
                      static_cast<const bf16*>(p.v), p.g, p.g_gamma, p.h0,
-                     static_cast<TOut*>(p.o), p.ht, p.scale, p.H, p.V, p.seqs);
+                     static_cast<TOut*>(p.o), p.ht, p.scale, p.H, p.Hkv, p.V, p.seqs);
   return hipGetLastError();
 }
 

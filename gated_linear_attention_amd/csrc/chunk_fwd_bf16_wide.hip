@@ -42,6 +42,7 @@
 
 #include "mfma_common.h"
 #include "sgla_internal.h"
+#include "unit_map.h"
 
 namespace sgla {
 namespace {
@@ -82,7 +83,7 @@ template <int K, typename TOut>
 __global__ void __launch_bounds__(NT)
 chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict__ v,
                            const float* __restrict__ h0, TOut* __restrict__ o,
-                           float* __restrict__ ht, int32_t H, int32_t V, SeqLayout seqs,
+                           float* __restrict__ ht, int32_t H, int32_t Hkv, int32_t V, SeqLayout seqs,
                            int32_t chunks_per_row, const float* __restrict__ gates,
                            const bf16* __restrict__ amat, const bf16* __restrict__ ktf) {
   using L = WideLayout;
@@ -92,15 +93,9 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
 
   // ---- which (sequence, head, V tile) this workgroup owns ----------------
-  const int nvt = V / VT;
-  const int num_units = seqs.num_seqs * H;
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int unit = (slot / nvt) * kXcds + xcd;
-  const int vt = slot % nvt;
-  if (unit >= num_units) return;
-  const int rank = unit / H;
-  const int hd = unit - rank * H;
+  const UnitMap um = map_unit(blockIdx.x, V / VT, Hkv, H / Hkv, seqs.num_seqs);
+  if (!um.valid) return;
+  const int rank = um.rank, hd = um.hd, hk = um.hk, vt = um.vt;
   int64_t bos;
   int32_t len, seq, chunk0;
   if (seqs.seq_table != nullptr) {
@@ -128,18 +123,19 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
   const int k0w = RW * w;
   const int ct = w >> 1;           // output tile of this wave: rows [16 ct, +16)
   const int vh = w & 1;            //                           columns [16 vh, +16)
-  const int RSK = H * K;
-  const int RSV = H * V;
-  const bf16* vb = v + (bos * H + hd) * (int64_t)V + vt * VT;
+  const int RSV = Hkv * V;                                 // token stride of v
+  const int RSO = H * V;                                   // token stride of o
+  const bf16* vb = v + (bos * Hkv + hk) * (int64_t)V + vt * VT;
   TOut* ob = o + (bos * H + hd) * (int64_t)V + vt * VT;
   const int64_t task0 = (int64_t)chunk0 * H + hd;          // preparation record of chunk 0
   const float* gbase = gates + task0 * kGateStride;
   const bf16* abase = amat + task0 * (2 * C * C);
-  const bf16* ktbase = ktf + task0 * (int64_t)K * C;
   const bf16* qbase = qfr + task0 * (int64_t)K * C;
+  const bf16* ktbase = ktf + ((int64_t)chunk0 * Hkv + hk) * K * C;   // K^T is per kv head
   const int64_t gstep = (int64_t)H * kGateStride;          // record strides between chunks
   const int64_t astep = (int64_t)H * 2 * C * C;
-  const int64_t kstep = (int64_t)H * K * C;
+  const int64_t qstep = (int64_t)H * K * C;
+  const int64_t kstep = (int64_t)Hkv * K * C;
 
   float* sPb = reinterpret_cast<float*>(smem);
   auto sV = [&](int p) { return reinterpret_cast<bf16*>(smem + L::OFF_V + p * L::SZ_V); };
@@ -183,7 +179,7 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
   // ---- Q operand of q.h: blocks (key block, c2, s) -------------------------
   bf16x8 qf[2][NRT][2];
   auto load_q = [&](int m) {
-    const auto rq = make_rsrc(qbase + m * kstep, m < nchunks ? (uint32_t)K * C * 2 : 0u);
+    const auto rq = make_rsrc(qbase + m * qstep, m < nchunks ? (uint32_t)K * C * 2 : 0u);
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
@@ -244,10 +240,10 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
       acc = mfma(af[1][0], vf, acc);
       acc = mfma(af[1][1], vf, acc);
     }
-    const auto ro = make_rsrc(ob + (int64_t)m * C * RSV, (uint32_t)cl * RSV * (uint32_t)sizeof(TOut));
+    const auto ro = make_rsrc(ob + (int64_t)m * C * RSO, (uint32_t)cl * RSO * (uint32_t)sizeof(TOut));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      store1<TOut>(ro, (uint32_t)((16 * ct + 4 * g4 + i) * RSV + 16 * vh + r) * (uint32_t)sizeof(TOut), acc[i]);
+      store1<TOut>(ro, (uint32_t)((16 * ct + 4 * g4 + i) * RSO + 16 * vh + r) * (uint32_t)sizeof(TOut), acc[i]);
   };
 
   // ---- decayed V of chunk m, hi + lo: wave w computes tokens [8 w, +8) ------
@@ -355,15 +351,12 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
 
 template <int K, typename TOut>
 hipError_t launch_k(const ChunkFwdParams& p, hipStream_t stream) {
-  const int num_units = p.seqs.num_seqs * p.H;
-  if (num_units == 0) return hipSuccess;
-  const int nvt = p.V / VT;
-  const int groups = (num_units + kXcds - 1) / kXcds;
-  const dim3 grid((unsigned)(groups * kXcds * nvt));
+  if (p.seqs.num_seqs == 0) return hipSuccess;
+  const dim3 grid((unsigned)unit_grid(p.seqs.num_seqs, p.Hkv, p.H / p.Hkv, p.V / VT));
   const int per_row = p.seqs.T > 0 ? (p.seqs.T + C - 1) / C : 0;
   hipLaunchKernelGGL((chunk_fwd_bf16_wide_kernel<K, TOut>), grid, dim3(NT), 0, stream,
                      static_cast<const bf16*>(p.qfr), static_cast<const bf16*>(p.v), p.h0,
-                     static_cast<TOut*>(p.o), p.ht, p.H, p.V, p.seqs, per_row, p.gates,
+                     static_cast<TOut*>(p.o), p.ht, p.H, p.Hkv, p.V, p.seqs, per_row, p.gates,
                      static_cast<const bf16*>(p.amat), static_cast<const bf16*>(p.ktf));
   return hipGetLastError();
 }

@@ -24,6 +24,7 @@
 
 #include "gate_scan.h"
 #include "sgla_internal.h"
+#include "unit_map.h"
 
 namespace sgla {
 namespace {
@@ -52,7 +53,7 @@ chunk_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                      const float* __restrict__ v, const float* __restrict__ g,
                      const float* __restrict__ g_gamma, const float* __restrict__ h0,
                      TOut* __restrict__ o, float* __restrict__ ht, float scale, int32_t H,
-                     int32_t V, SeqLayout seqs) {
+                     int32_t Hkv, int32_t V, SeqLayout seqs) {
   constexpr int LDQ = K + 4;          // Q / K row stride (floats)
   constexpr int NKT = K / 16;         // 16-row state tiles
   constexpr int NST = NKT * 2;        // state tiles (x 2 column tiles)
@@ -64,15 +65,9 @@ chunk_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
   __shared__ float sH[K * LDH];
   __shared__ float sG[C], sEb[C], sDk[C];
 
-  const int nvt = V / VT;
-  const int num_units = seqs.num_seqs * H;
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int unit = (slot / nvt) * kXcds + xcd;
-  const int vt = slot % nvt;
-  if (unit >= num_units) return;
-  const int rank = unit / H;
-  const int hd = unit - rank * H;
+  const UnitMap um = map_unit(blockIdx.x, V / VT, Hkv, H / Hkv, seqs.num_seqs);
+  if (!um.valid) return;
+  const int rank = um.rank, hd = um.hd, hk = um.hk, vt = um.vt;
   int64_t bos;
   int32_t len, seq;
   if (seqs.seq_table != nullptr) {
@@ -128,9 +123,8 @@ chunk_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
       const int c = i / (K / 4), k4 = i % (K / 4);
       f32x4 xq = {0.f, 0.f, 0.f, 0.f}, xk = {0.f, 0.f, 0.f, 0.f};
       if (c < cl) {
-        const int64_t off = ((t0 + c) * H + hd) * (int64_t)K + 4 * k4;
-        xq = *reinterpret_cast<const f32x4*>(q + off);
-        xk = *reinterpret_cast<const f32x4*>(k + off);
+        xq = *reinterpret_cast<const f32x4*>(q + ((t0 + c) * H + hd) * (int64_t)K + 4 * k4);
+        xk = *reinterpret_cast<const f32x4*>(k + ((t0 + c) * Hkv + hk) * (int64_t)K + 4 * k4);
       }
       *reinterpret_cast<f32x4*>(sQ + c * LDQ + 4 * k4) = xq;
       *reinterpret_cast<f32x4*>(sK + c * LDQ + 4 * k4) = xk;
@@ -138,7 +132,7 @@ chunk_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
     for (int i = tid; i < C * (VT / 4); i += NTHREADS) {
       const int c = i / (VT / 4), v4 = i % (VT / 4);
       f32x4 xv = {0.f, 0.f, 0.f, 0.f};
-      if (c < cl) xv = *reinterpret_cast<const f32x4*>(v + ((t0 + c) * H + hd) * (int64_t)V + vt * VT + 4 * v4);
+      if (c < cl) xv = *reinterpret_cast<const f32x4*>(v + ((t0 + c) * Hkv + hk) * (int64_t)V + vt * VT + 4 * v4);
       *reinterpret_cast<f32x4*>(sV + c * LDV + 4 * v4) = xv;
     }
     if (tid < C) {
@@ -233,15 +227,12 @@ chunk_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
 
 template <int K, typename TOut>
 hipError_t launch_k(const ChunkFwdParams& p, hipStream_t stream) {
-  const int num_units = p.seqs.num_seqs * p.H;
-  if (num_units == 0) return hipSuccess;
-  const int nvt = p.V / VT;
-  const int groups = (num_units + kXcds - 1) / kXcds;
-  const dim3 grid((unsigned)(groups * kXcds * nvt));
+  if (p.seqs.num_seqs == 0) return hipSuccess;
+  const dim3 grid((unsigned)unit_grid(p.seqs.num_seqs, p.Hkv, p.H / p.Hkv, p.V / VT));
   hipLaunchKernelGGL((chunk_fwd_f32_kernel<K, TOut>), grid, dim3(NTHREADS), 0, stream,
                      static_cast<const float*>(p.q), static_cast<const float*>(p.k),
                      static_cast<const float*>(p.v), p.g, p.g_gamma, p.h0,
-                     static_cast<TOut*>(p.o), p.ht, p.scale, p.H, p.V, p.seqs);
+                     static_cast<TOut*>(p.o), p.ht, p.scale, p.H, p.Hkv, p.V, p.seqs);
   return hipGetLastError();
 }
 

@@ -27,7 +27,10 @@
 // Tokens at or past L read as zeros (q, k, g), so their A rows and columns,
 // Q rows and K^T entries are zero and b stays at b_last.
 //
-// One workgroup of four waves per (chunk, head).  All HBM reads (the K chunk
+// With grouped kv heads the K^T blocks depend on the kv head alone: they are
+// stored once per (chunk, kv head), by the group's first query head.
+//
+// One workgroup of four waves per (chunk, query head).  All HBM reads (the K chunk
 // into registers then LDS, the wave's Q blocks into registers) are issued
 // up front.  Q K^T runs on v_mfma_f32_32x32x16_bf16: wave w covers query
 // rows [32 (w / 2), +32) over key half w % 2; the two halves are added in LDS.
@@ -50,7 +53,8 @@ template <int K>
 __global__ void __launch_bounds__(NTP)
 chunk_prep_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                        const float* __restrict__ g, const float* __restrict__ g_gamma, float scale,
-                       int32_t H, SeqLayout seqs, int32_t chunks_per_row, float* __restrict__ gates,
+                       int32_t H, int32_t Hkv, SeqLayout seqs, int32_t chunks_per_row,
+                       float* __restrict__ gates,
                        bf16* __restrict__ amat, bf16* __restrict__ ktf, bf16* __restrict__ qfr) {
   constexpr int LDK = K + 8;      // key row stride: conflict-free 16-byte row reads
   constexpr int KP = K / 8;       // 16-byte pieces per key row
@@ -60,8 +64,20 @@ chunk_prep_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   __shared__ __attribute__((aligned(16))) bf16 sK[C * LDK];
   __shared__ float sb[C];
 
-  const int gc = blockIdx.x;      // global chunk index
-  const int hd = blockIdx.y;
+  // ---- which (chunk, query head) this workgroup prepares ------------------
+  // Work units wu = hk * num_chunks + chunk (chunk fastest) are dealt to the
+  // XCDs round-robin; the n_rep query heads of a unit follow each other on its
+  // XCD, so the K chunk they share is re-read from that XCD's L2.
+  const int n_rep = H / Hkv;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int gs = slot / n_rep;
+  const int wu = gs * kXcds + xcd;
+  if (wu >= seqs.num_chunks * Hkv) return;
+  const int hk = wu / seqs.num_chunks;
+  const int gc = wu - hk * seqs.num_chunks;   // global chunk index
+  const int hd = hk * n_rep + (slot - gs * n_rep);
+  const bool write_kt = hd == hk * n_rep;
   int64_t t0;
   int cl;
   if (seqs.chunk_table != nullptr) {
@@ -85,16 +101,17 @@ chunk_prep_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int c2 = w >> 1;           // query rows [32 c2, +32)
   const int kb0 = (w & 1) * NKB;   // key blocks [kb0, kb0 + NKB)
   const int64_t task = (int64_t)gc * H + hd;
-  const int RS = H * K;            // elements between consecutive tokens
+  const int RS = H * K;            // elements between consecutive tokens of q
+  const int RSK = Hkv * K;         //                                     of k
 
   // ---- all HBM reads up front ----------------------------------------------
-  const auto rk = make_rsrc(k + (t0 * H + hd) * (int64_t)K, (uint32_t)cl * RS * 2);
+  const auto rk = make_rsrc(k + (t0 * Hkv + hk) * (int64_t)K, (uint32_t)cl * RSK * 2);
   const auto rq = make_rsrc(q + (t0 * H + hd) * (int64_t)K, (uint32_t)cl * RS * 2);
   u32x4 kx[NKS];
 #pragma unroll
-  for (int u = 0; u < NKS; ++u) {
-    const int p = tid + NTP * u;
-    kx[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)((p / KP) * RS + (p % KP) * 8) * 2, 0, 0);
+  for (int i = 0; i < NKS; ++i) {
+    const int p = tid + NTP * i;
+    kx[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)((p / KP) * RSK + (p % KP) * 8) * 2, 0, 0);
   }
   bf16x8 qx[NKB][2];
 #pragma unroll
@@ -130,9 +147,9 @@ chunk_prep_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   // ---- K chunk to LDS; Q blocks out ----------------------------------------
 #pragma unroll
-  for (int u = 0; u < NKS; ++u) {
-    const int p = tid + NTP * u;
-    *reinterpret_cast<u32x4*>(sK + (p / KP) * LDK + (p % KP) * 8) = kx[u];
+  for (int i = 0; i < NKS; ++i) {
+    const int p = tid + NTP * i;
+    *reinterpret_cast<u32x4*>(sK + (p / KP) * LDK + (p % KP) * 8) = kx[i];
   }
   {
     bf16* qo = qfr + task * (int64_t)K * C;
@@ -144,9 +161,9 @@ chunk_prep_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
   __syncthreads();
 
-  // ---- K^T blocks -------------------------------------------------------------
-  {
-    bf16* kt = ktf + task * (int64_t)K * C;
+  // ---- K^T blocks (once per kv head) --------------------------------------------
+  if (write_kt) {
+    bf16* kt = ktf + ((int64_t)gc * Hkv + hk) * K * C;
 #pragma unroll
     for (int f = w; f < (K / 32) * 4; f += 4) {
       const int kb = f >> 2, ts = f & 3;
@@ -227,11 +244,12 @@ chunk_prep_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
 template <int K>
 hipError_t launch_k(const ChunkPrepParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)p.seqs.num_chunks, (unsigned)p.H);
+  const int64_t units = (int64_t)p.seqs.num_chunks * p.Hkv;
+  const dim3 grid((unsigned)((units + kXcds - 1) / kXcds * kXcds * (p.H / p.Hkv)));
   const int per_row = p.seqs.T > 0 ? (p.seqs.T + C - 1) / C : 1;
   hipLaunchKernelGGL((chunk_prep_bf16_kernel<K>), grid, dim3(NTP), 0, stream,
                      static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k), p.g, p.g_gamma,
-                     p.scale, p.H, p.seqs, per_row, p.gates, static_cast<bf16*>(p.amat),
+                     p.scale, p.H, p.Hkv, p.seqs, per_row, p.gates, static_cast<bf16*>(p.amat),
                      static_cast<bf16*>(p.ktf), static_cast<bf16*>(p.qfr));
   return hipGetLastError();
 }

@@ -4,7 +4,12 @@
 // kernel because a chunk launch for one token is slower; section 二: states
 // are [N, H, K, V] with S[k][v]):
 //
-//     S <- exp(g) * S + k v^T ;    o = scale * S^T q   (post-update state).
+//     S <- exp(g) * S + k v^T ;    o = scale * S^T q   (post-update state),
+//
+// with g per (sequence, head), or a per-head constant g_gamma[h] (section 二),
+// or no decay.  With grouped kv heads, query head h reads the k and v rows of
+// kv head h / (H / Hkv) (page "relinear", its GQA target); state and gate stay
+// per query head.
 //
 // The step is a pure read-modify-write stream over the state: 2 * K * V * 4
 // bytes per (sequence, head) against 5 * K * V flops, so it is bound by HBM.
@@ -38,22 +43,26 @@ template <int V, typename TIn, typename TOut>
 __global__ void __launch_bounds__(256)
 recurrent_step_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                       const TIn* __restrict__ v, const float* __restrict__ g,
-                      float* __restrict__ state, TOut* __restrict__ o, float scale, int32_t K) {
+                      const float* __restrict__ g_gamma, float* __restrict__ state,
+                      TOut* __restrict__ o, float scale, int32_t H, int32_t Hkv, int32_t K) {
   constexpr int TPR = V / 4;          // threads per state row
   constexpr int RG = 256 / TPR;       // row groups
   constexpr int BATCH = 16;           // rows in flight per thread
   __shared__ float part[RG][V];
 
   const int64_t unit = blockIdx.x;    // n * H + h
+  const uint32_t n = blockIdx.x / (uint32_t)H;
+  const int h = (int)(blockIdx.x - n * (uint32_t)H);
+  const int64_t ukv = (int64_t)n * Hkv + h / (H / Hkv);   // (sequence, kv head) row of k and v
   const int tid = threadIdx.x;
   const int cq = tid % TPR;
   const int rg = tid / TPR;
-  const float gamma = expf(g[unit]);
+  const float gamma = expf(g != nullptr ? g[unit] : (g_gamma != nullptr ? g_gamma[h] : 0.f));
   const TIn* qu = q + unit * K;
-  const TIn* ku = k + unit * K;
+  const TIn* ku = k + ukv * K;
   f32x4 vv;
   {
-    const TIn* vu = v + unit * V + 4 * cq;
+    const TIn* vu = v + ukv * V + 4 * cq;
     vv = f32x4{to_f32(vu[0]), to_f32(vu[1]), to_f32(vu[2]), to_f32(vu[3])};
   }
   f32x4* S = reinterpret_cast<f32x4*>(state + unit * (int64_t)K * V);
@@ -141,8 +150,8 @@ hipError_t launch_v(const StepParams& p, hipStream_t stream) {
   if (units == 0) return hipSuccess;
   hipLaunchKernelGGL((recurrent_step_kernel<V, TIn, TOut>), dim3((unsigned)units), dim3(256), 0,
                      stream, static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k),
-                     static_cast<const TIn*>(p.v), p.g, p.state, static_cast<TOut*>(p.o),
-                     p.scale, p.K);
+                     static_cast<const TIn*>(p.v), p.g, p.g_gamma, p.state, static_cast<TOut*>(p.o),
+                     p.scale, p.H, p.Hkv, p.K);
   return hipGetLastError();
 }
 

@@ -46,6 +46,7 @@ bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 // Validated description of one chunk_fwd request.
 struct Plan {
   int32_t N = 0;             // sequences
+  int32_t Hkv = 0;           // kv heads (divides H)
   int64_t total_tokens = 0;  // B * T
   int32_t num_chunks = 0;
   bool packed = false;
@@ -60,6 +61,9 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
   if (a == nullptr) return fail(SGLA_ERR_INVALID_ARG, "args is NULL");
   if (a->B < 0 || a->T < 0) return fail(SGLA_ERR_SHAPE, "B and T must be >= 0 (got B=%d T=%d)", a->B, a->T);
   if (a->H <= 0) return fail(SGLA_ERR_SHAPE, "H must be > 0 (got %d)", a->H);
+  P->Hkv = a->num_kv_heads == 0 ? a->H : a->num_kv_heads;
+  if (P->Hkv < 0 || a->H % P->Hkv != 0)
+    return fail(SGLA_ERR_SHAPE, "num_kv_heads must divide H (got num_kv_heads=%d, H=%d)", a->num_kv_heads, a->H);
   const int32_t cs = a->chunk_size == 0 ? sgla::kChunk : a->chunk_size;
   if (!is_pow2(cs)) return fail(SGLA_ERR_SHAPE, "chunk_size must be a power of two (got %d)", cs);
   if (cs != sgla::kChunk)
@@ -121,16 +125,20 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
     P->N = a->B;
     P->num_chunks = a->T > 0 ? a->B * ((a->T + sgla::kChunk - 1) / sgla::kChunk) : 0;
   }
+  // workgroup counts of the launches must fit a 32-bit grid
+  if ((int64_t)P->num_chunks * a->H > INT32_MAX)
+    return fail(SGLA_ERR_UNSUPPORTED, "%d chunks x %d heads exceeds 2^31-1 work units", P->num_chunks, a->H);
   P->prep = need_kv_support && a->qkv_dtype == SGLA_BF16 && a->K >= 256;
   P->seq_off = 0;
   P->chunk_off = P->seq_off + align_up(P->seqs.size() * sizeof(sgla::SeqEntry), 256);
   P->gate_off = P->chunk_off + align_up(P->chunks.size() * sizeof(sgla::ChunkEntry), 256);
   P->amat_off = P->gate_off;
   if (P->prep) {
-    const size_t tasks = (size_t)P->num_chunks * a->H;
+    const size_t tasks = (size_t)P->num_chunks * a->H;        // (chunk, query head)
+    const size_t kv_tasks = (size_t)P->num_chunks * P->Hkv;   // (chunk, kv head)
     P->amat_off = P->gate_off + align_up(tasks * sgla::kGateStride * sizeof(float), 256);
     P->kt_off = P->amat_off + tasks * 2 * sgla::kChunk * sgla::kChunk * 2;
-    P->q_off = P->kt_off + tasks * (size_t)a->K * sgla::kChunk * 2;
+    P->q_off = P->kt_off + kv_tasks * (size_t)a->K * sgla::kChunk * 2;
     P->total_bytes = P->q_off + tasks * (size_t)a->K * sgla::kChunk * 2;
   } else {
     P->total_bytes = P->gate_off;
@@ -231,6 +239,7 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
   p.ht = a.output_final_state ? final_state : nullptr;
   p.scale = a.scale;
   p.H = a.H;
+  p.Hkv = P.Hkv;
   p.K = a.K;
   p.V = a.V;
   p.o_bf16 = a.o_dtype == SGLA_BF16;
@@ -249,6 +258,7 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
     pp.g_gamma = g_gamma;
     pp.scale = a.scale;
     pp.H = a.H;
+    pp.Hkv = P.Hkv;
     pp.K = a.K;
     pp.seqs = L;
     pp.gates = reinterpret_cast<float*>(ws + P.gate_off);
@@ -284,10 +294,16 @@ sgla_status sgla_chunk_local_cumsum(const sgla_chunk_args* args, const float* g,
   return ok();
 }
 
-sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t K, int32_t V, float scale, int32_t qkv_dtype,
-                                int32_t o_dtype, const void* q, const void* k, const void* v, const float* g,
-                                float* state, void* o, hipStream_t stream) {
+sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t num_kv_heads, int32_t K, int32_t V, float scale,
+                                int32_t qkv_dtype, int32_t o_dtype, const void* q, const void* k, const void* v,
+                                const float* g, const float* g_gamma, float* state, void* o,
+                                hipStream_t stream) {
   if (N < 0 || H <= 0) return fail(SGLA_ERR_SHAPE, "N must be >= 0 and H > 0 (got N=%d H=%d)", N, H);
+  const int32_t Hkv = num_kv_heads == 0 ? H : num_kv_heads;
+  if (Hkv < 0 || H % Hkv != 0)
+    return fail(SGLA_ERR_SHAPE, "num_kv_heads must divide H (got num_kv_heads=%d, H=%d)", num_kv_heads, H);
+  if ((int64_t)N * H > INT32_MAX)
+    return fail(SGLA_ERR_UNSUPPORTED, "N*H = %lld exceeds 2^31-1", (long long)N * H);
   if (K < 1 || K > 1024) return fail(SGLA_ERR_UNSUPPORTED, "decode supports 1 <= K <= 1024 (got %d)", K);
   if (!(V == 32 || V == 64 || V == 128 || V == 256 || V == 512))
     return fail(SGLA_ERR_UNSUPPORTED, "decode supports V in {32,64,128,256,512} (got %d)", V);
@@ -296,9 +312,11 @@ sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t K, int32_t V, floa
   if (o_dtype != SGLA_BF16 && o_dtype != SGLA_F32)
     return fail(SGLA_ERR_DTYPE, "o_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", o_dtype);
   if (!std::isfinite(scale)) return fail(SGLA_ERR_INVALID_ARG, "scale must be finite");
+  if (g != nullptr && g_gamma != nullptr)
+    return fail(SGLA_ERR_INVALID_ARG, "g and g_gamma are mutually exclusive; pass at most one");
   if (N == 0) return ok();
-  if (q == nullptr || k == nullptr || v == nullptr || g == nullptr || state == nullptr || o == nullptr)
-    return fail(SGLA_ERR_INVALID_ARG, "q, k, v, g, state and o must be non-NULL");
+  if (q == nullptr || k == nullptr || v == nullptr || state == nullptr || o == nullptr)
+    return fail(SGLA_ERR_INVALID_ARG, "q, k, v, state and o must be non-NULL");
   if (!aligned(state, 16)) return fail(SGLA_ERR_INVALID_ARG, "state must be 16-byte aligned");
   const size_t osz = (size_t)N * H * V * (o_dtype == SGLA_BF16 ? 2 : 4);
   const size_t ssz = (size_t)N * H * K * V * sizeof(float);
@@ -310,11 +328,13 @@ sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t K, int32_t V, floa
   p.k = k;
   p.v = v;
   p.g = g;
+  p.g_gamma = g_gamma;
   p.state = state;
   p.o = o;
   p.scale = scale;
   p.N = N;
   p.H = H;
+  p.Hkv = Hkv;
   p.K = K;
   p.V = V;
   p.qkv_bf16 = qkv_dtype == SGLA_BF16;

@@ -11,6 +11,14 @@ namespace sgla {
 constexpr int kChunk = 64;        // tokens per chunk
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
 
+// Workgroups of the chunk kernels per (sequence, kv head) group and V tile
+// count: kv groups are dealt to the XCDs round-robin, each group's n_rep
+// query heads and nvt V tiles adjacent in dispatch order on its XCD.
+inline int64_t unit_grid(int32_t num_seqs, int32_t Hkv, int32_t n_rep, int32_t nvt) {
+  const int64_t groups = (int64_t)num_seqs * Hkv;
+  return (groups + kXcds - 1) / kXcds * kXcds * n_rep * nvt;
+}
+
 // Per-sequence entry of the packed-input table, sorted longest first.
 struct SeqEntry {
   int32_t bos;     // first packed token of the sequence
@@ -48,11 +56,11 @@ struct ChunkPrepParams {
   const float* g;
   const float* g_gamma;
   float scale;
-  int32_t H, K;
+  int32_t H, Hkv, K;
   SeqLayout seqs;
   float* gates;              // [num_chunks, H, kGateStride]
   void* amat;                // [num_chunks, H, 2, 64, 64] bf16
-  void* ktf;                 // [num_chunks, H, K * 64] bf16, state-update operand order
+  void* ktf;                 // [num_chunks, Hkv, K * 64] bf16, state-update operand order
   void* qfr;                 // [num_chunks, H, K * 64] bf16, q.h operand order
 };
 
@@ -66,7 +74,7 @@ struct ChunkFwdParams {
   void* o;
   float* ht;                 // [N, H, K, V] or nullptr
   float scale;
-  int32_t H, K, V;
+  int32_t H, Hkv, K, V;      // Hkv divides H: query head h reads kv head h / (H / Hkv)
   int32_t o_bf16;            // 1: o is bf16, 0: float32
   SeqLayout seqs;
   const float* gates;        // wide-key path: preparation outputs (workspace)
@@ -94,11 +102,12 @@ struct StepParams {
   const void* q;
   const void* k;
   const void* v;
-  const float* g;
+  const float* g;            // [N, H] or nullptr
+  const float* g_gamma;      // [H] or nullptr
   float* state;
   void* o;
   float scale;
-  int32_t N, H, K, V;
+  int32_t N, H, Hkv, K, V;
   int32_t qkv_bf16;
   int32_t o_bf16;
 };

@@ -75,6 +75,7 @@ class ChunkWorkload:
     scale: Optional[float] = None   # None -> 1/sqrt(K)
     output_final_state: bool = True
     seed: int = 0
+    Hkv: int = 0                 # kv heads of k and v (0: H); divides H
 
     @property
     def packed(self) -> bool:
@@ -96,6 +97,8 @@ class DecodeWorkload:
     state_std: float = 0.1
     scale: Optional[float] = None
     seed: int = 0
+    Hkv: int = 0                 # kv heads of k and v (0: H); divides H
+    gate: str = "g"              # "g" (per token and head), "gamma" (per head) or "none"
 
     def with_(self, **kw) -> "DecodeWorkload":
         return dataclasses.replace(self, **kw)
@@ -131,9 +134,9 @@ def _as_input_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def make_chunk_inputs(w: ChunkWorkload) -> dict:
     """Draw one batch for a chunked forward.  Returns a dict with numpy arrays
-    q, k [B,T,H,K], v [B,T,H,V], g [B,T,H] or None, g_gamma [H] or None,
-    initial_state [N,H,K,V] or None, cu_seqlens int64 [N+1] or None, plus
-    scale, chunk_size, dtype and output_final_state."""
+    q [B,T,H,K], k [B,T,Hkv,K], v [B,T,Hkv,V], g [B,T,H] or None, g_gamma [H]
+    or None, initial_state [N,H,K,V] or None, cu_seqlens int64 [N+1] or None,
+    plus scale, chunk_size, dtype and output_final_state."""
     rng = np.random.default_rng(w.seed)
     cu = None
     if w.packed:
@@ -149,9 +152,12 @@ def make_chunk_inputs(w: ChunkWorkload) -> dict:
         B, T = w.B, w.T
         N = B
     H, K, V = w.H, w.K, w.V
+    Hkv = w.Hkv or H
+    if H % Hkv:
+        raise ValueError(f"Hkv={Hkv} must divide H={H}")
     q = rng.standard_normal((B, T, H, K), dtype=np.float32)
-    k = rng.standard_normal((B, T, H, K), dtype=np.float32)
-    v = rng.standard_normal((B, T, H, V), dtype=np.float32)
+    k = rng.standard_normal((B, T, Hkv, K), dtype=np.float32)
+    v = rng.standard_normal((B, T, Hkv, V), dtype=np.float32)
     if w.normalize_k:
         nrm = np.sqrt(np.sum(k.astype(np.float64) ** 2, axis=-1, keepdims=True))
         k = (k / np.maximum(nrm, 1e-30)).astype(np.float32)
@@ -171,22 +177,31 @@ def make_chunk_inputs(w: ChunkWorkload) -> dict:
     scale = w.scale if w.scale is not None else K ** -0.5
     return dict(q=q, k=k, v=v, g=g, g_gamma=g_gamma, initial_state=h0, cu_seqlens=cu,
                 scale=float(scale), chunk_size=w.chunk_size, dtype=w.dtype,
-                output_final_state=w.output_final_state, B=B, T=T, H=H, K=K, V=V, N=N)
+                output_final_state=w.output_final_state, B=B, T=T, H=H, K=K, V=V, N=N, Hkv=Hkv)
 
 
 def make_decode_inputs(w: DecodeWorkload, steps: Optional[int] = None) -> dict:
     """Draw the initial state [N,H,K,V] float32 and ``steps`` single-token
-    inputs: q, k [steps,N,H,K], v [steps,N,H,V], g [steps,N,H]."""
+    inputs: q [steps,N,H,K], k [steps,N,Hkv,K], v [steps,N,Hkv,V], and
+    g [steps,N,H] (gate "g") or g_gamma [H] (gate "gamma"); the other is None."""
     steps = w.steps if steps is None else steps
     rng = np.random.default_rng(w.seed)
     N, H, K, V = w.N, w.H, w.K, w.V
+    Hkv = w.Hkv or H
+    if H % Hkv:
+        raise ValueError(f"Hkv={Hkv} must divide H={H}")
+    if w.gate not in ("g", "gamma", "none"):
+        raise ValueError(f"unknown gate kind {w.gate!r}")
     state = rng.standard_normal((N, H, K, V), dtype=np.float32) * np.float32(w.state_std)
     qs, ks, vs, gs = [], [], [], []
     for _ in range(steps):
         qs.append(_as_input_dtype(rng.standard_normal((N, H, K), dtype=np.float32), w.dtype))
-        ks.append(_as_input_dtype(rng.standard_normal((N, H, K), dtype=np.float32), w.dtype))
-        vs.append(_as_input_dtype(rng.standard_normal((N, H, V), dtype=np.float32), w.dtype))
-        gs.append(logsigmoid(rng.standard_normal((N, H))).astype(np.float32))
+        ks.append(_as_input_dtype(rng.standard_normal((N, Hkv, K), dtype=np.float32), w.dtype))
+        vs.append(_as_input_dtype(rng.standard_normal((N, Hkv, V), dtype=np.float32), w.dtype))
+        if w.gate == "g":
+            gs.append(logsigmoid(rng.standard_normal((N, H))).astype(np.float32))
     scale = w.scale if w.scale is not None else K ** -0.5
-    return dict(state=state, q=np.stack(qs), k=np.stack(ks), v=np.stack(vs), g=np.stack(gs),
-                scale=float(scale), dtype=w.dtype, N=N, H=H, K=K, V=V, steps=steps)
+    return dict(state=state, q=np.stack(qs), k=np.stack(ks), v=np.stack(vs),
+                g=np.stack(gs) if w.gate == "g" else None,
+                g_gamma=retnet_gamma(H) if w.gate == "gamma" else None,
+                scale=float(scale), dtype=w.dtype, N=N, H=H, K=K, V=V, steps=steps, Hkv=Hkv)

@@ -15,9 +15,13 @@
  *     allocated and owned by the caller.  The library never allocates, frees,
  *     retains a pointer past the call, or synchronizes the stream; all work
  *     is enqueued on the caller's `stream`.
- *   - Layouts follow section 二: q, k [B, T, H, K]; v, o [B, T, H, V];
- *     g [B, T, H]; g_gamma [H]; states [N, H, K, V] with S[k][v] (key index
- *     major).  Packed (varlen) input has B == 1 and N sequences given by
+ *   - Layouts follow section 二: q [B, T, H, K]; k [B, T, Hkv, K];
+ *     v [B, T, Hkv, V]; o [B, T, H, V]; g [B, T, H]; g_gamma [H]; states
+ *     [N, H, K, V] with S[k][v] (key index major).  Hkv, the number of kv
+ *     heads, divides H; query head h reads kv head h / (H / Hkv), the
+ *     contiguous grouping of grouped-query attention (page "relinear", its
+ *     GQA target, and the Simple GLA layer's num_kv_heads, section 四).  Every
+ *     query head keeps its own gate and state.  Hkv == H is plain multi-head.  Packed (varlen) input has B == 1 and N sequences given by
  *     cu_seqlens[N + 1] (FlashAttention convention, section 二); dense input
  *     has N == B.
  *   - Gates, states and the state accumulation are float32.  q, k, v are all
@@ -42,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SGLA_ABI_VERSION 1
+#define SGLA_ABI_VERSION 2
 
 typedef enum {
   SGLA_OK = 0,
@@ -64,6 +68,7 @@ typedef struct {
   int32_t o_dtype;            /* sgla_dtype of o */
   float scale;                /* finite; callers wanting the default pass 1/sqrt(K) */
   int32_t output_final_state; /* nonzero: write final_state */
+  int32_t num_kv_heads;       /* Hkv: heads of k and v; 0 means H.  Must divide H */
 } sgla_chunk_args;
 
 /* ABI revision of the loaded library (SGLA_ABI_VERSION it was built with). */
@@ -79,7 +84,8 @@ const char *sgla_last_error(void);
  * packed input the sequence and chunk tables; for bf16 inputs with K = 256 or
  * 512 also the per-(chunk, head) preparation records (gates, the masked
  * intra-chunk q k^T as bf16 hi/lo, and the chunk's q and k^T rearranged for
- * the state kernel: 256 K + 16 KiB + 768 bytes per 64-token chunk and head).
+ * the state kernel: 128 K + 16 KiB + 768 bytes per 64-token chunk and query
+ * head, plus 128 K bytes per 64-token chunk and kv head).
  * `cu_seqlens_host` is the same host array later passed to sgla_chunk_fwd, or
  * NULL for dense input.  Returns 0 if the arguments are invalid (the reason is
  * in sgla_last_error()); a valid call may also legitimately need 0 bytes only
@@ -102,8 +108,9 @@ size_t sgla_chunk_fwd_workspace_size(const sgla_chunk_args *args, const int64_t 
  * them between the two launches, so a call enqueues two kernels.
  *
  * Arguments (device pointers unless stated):
- *   q, k            [B, T, H, K] in qkv_dtype
- *   v               [B, T, H, V] in qkv_dtype
+ *   q               [B, T, H, K] in qkv_dtype
+ *   k               [B, T, Hkv, K] in qkv_dtype
+ *   v               [B, T, Hkv, V] in qkv_dtype
  *   g               [B, T, H] float32 log gates, or NULL
  *   g_gamma         [H] float32 per-head log decay, or NULL.  At most one of
  *                   g / g_gamma may be given (section 二); neither means no
@@ -119,7 +126,7 @@ size_t sgla_chunk_fwd_workspace_size(const sgla_chunk_args *args, const int64_t 
  *                   exactly (in-place state update); no other aliasing.
  *   workspace       device buffer of at least workspace_bytes >=
  *                   sgla_chunk_fwd_workspace_size(args, cu_seqlens_host).
- * Supported: K in {64, 128} with V a multiple of 64, or K in {256, 512}
+ * Supported (any Hkv dividing H): K in {64, 128} with V a multiple of 64, or K in {256, 512}
  * with V a multiple of 32 (bf16 inputs);
  * K in {16, 32, 64, 128} and V a multiple of 32 (float32 inputs);
  * chunk_size 64.  Other powers of two are valid requests that return
@@ -154,16 +161,22 @@ sgla_status sgla_chunk_local_cumsum(const sgla_chunk_args *args, const float *g,
  * One decode step for N independent sequences x H heads (section 四: single
  * tokens take the fused recurrent path instead of a chunk launch), in place:
  *     S <- exp(g) * S + k v^T ;   o = scale * S^T q   (updated state)
- *   q, k   [N, H, K] in qkv_dtype;  v [N, H, V] in qkv_dtype
- *   g      [N, H] float32 log gate
- *   state  [N, H, K, V] float32, read and written in place
- *   o      [N, H, V] in o_dtype; must not alias any input
- * Supported: K a multiple of 8 in [8, 512], V a multiple of 32 in [32, 512].
+ *   q       [N, H, K] in qkv_dtype
+ *   k       [N, Hkv, K] in qkv_dtype;  v [N, Hkv, V] in qkv_dtype
+ *           (num_kv_heads = Hkv divides H, 0 means H; query head h reads kv
+ *           head h / (H / Hkv))
+ *   g       [N, H] float32 log gate, or NULL
+ *   g_gamma [H] float32 per-head log decay, or NULL.  At most one of g /
+ *           g_gamma (section 二); neither means no decay.
+ *   state   [N, H, K, V] float32, read and written in place
+ *   o       [N, H, V] in o_dtype; must not alias the state
+ * All pointers are device pointers.  Supported: 1 <= K <= 1024 and V in
+ * {32, 64, 128, 256, 512}.
  */
-sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t K, int32_t V, float scale,
-                                int32_t qkv_dtype, int32_t o_dtype,
+sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t num_kv_heads, int32_t K, int32_t V,
+                                float scale, int32_t qkv_dtype, int32_t o_dtype,
                                 const void *q, const void *k, const void *v,
-                                const float *g, float *state, void *o,
+                                const float *g, const float *g_gamma, float *state, void *o,
                                 hipStream_t stream);
 
 #ifdef __cplusplus

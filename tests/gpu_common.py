@@ -57,9 +57,10 @@ def oracle_units(inp: dict, units, nthreads=None):
         else:
             s, e = 0, inp["T"]
             b = n
+        hk = h // (inp["H"] // inp["k"].shape[2])    # kv head of query head h
         q = inp["q"][b:b + 1, s:e, h:h + 1]
-        k = inp["k"][b:b + 1, s:e, h:h + 1]
-        v = inp["v"][b:b + 1, s:e, h:h + 1]
+        k = inp["k"][b:b + 1, s:e, hk:hk + 1]
+        v = inp["v"][b:b + 1, s:e, hk:hk + 1]
         g = None if inp["g"] is None else inp["g"][b:b + 1, s:e, h:h + 1]
         gg = None if inp["g_gamma"] is None else inp["g_gamma"][h:h + 1]
         h0 = None if inp["initial_state"] is None else inp["initial_state"][n:n + 1, h:h + 1]

@@ -58,7 +58,7 @@ def test_single_hip_runtime_in_process(G):
 
 
 def test_abi_version(G):
-    assert G.lib.sgla_abi_version() == G.ABI_VERSION == 1
+    assert G.lib.sgla_abi_version() == G.ABI_VERSION == 2
 
 
 class Buffers:
@@ -104,8 +104,9 @@ def chunk_call(G, args, b, cu=None, g=True, gg=False, h0=True, ht=True, ws_bytes
     return st, G.lib.sgla_last_error().decode()
 
 
-def mkargs(G, B=1, T=128, H=2, K=64, V=64, N=1, chunk=64, qkv=BF16, od=F32, scale=0.125, fs=1):
-    return G._ChunkArgs(B, T, H, K, V, N, chunk, qkv, od, scale, fs)
+def mkargs(G, B=1, T=128, H=2, K=64, V=64, N=1, chunk=64, qkv=BF16, od=F32, scale=0.125, fs=1,
+           Hkv=0):
+    return G._ChunkArgs(B, T, H, K, V, N, chunk, qkv, od, scale, fs, Hkv)
 
 
 CASES = [
@@ -136,6 +137,8 @@ CASES = [
     ("misaligned q", {}, dict(q="misaligned"), INVALID, "aligned"),
     ("partial state overlap", {}, dict(ht="overlap"), INVALID, "overlap"),
     ("num_seqs 0 with cu", dict(N=0), dict(cu=[0]), SHAPE, "num_seqs"),
+    ("num_kv_heads not dividing H", dict(H=2, Hkv=3), {}, SHAPE, "num_kv_heads"),
+    ("negative num_kv_heads", dict(Hkv=-1), {}, SHAPE, "num_kv_heads"),
 ]
 
 
@@ -179,15 +182,27 @@ def test_workspace_size(G):
     assert "K in" in G.lib.sgla_last_error().decode()
 
 
+def test_workspace_size_wide_keys(G):
+    """bf16 K = 512: per (chunk, query head) 768 bytes of gates, 16 KiB of
+    A and K * 128 bytes of Q; per (chunk, kv head) K * 128 bytes of K^T."""
+    for H, Hkv in ((4, 4), (4, 2), (4, 1)):
+        a = mkargs(G, B=2, T=130, H=H, K=512, V=64, Hkv=Hkv)
+        n = G.lib.sgla_chunk_fwd_workspace_size(ctypes.byref(a), None)
+        chunks = 2 * 3
+        assert n == chunks * H * (768 + 16384 + 512 * 128) + chunks * Hkv * 512 * 128
+
+
 STEP_CASES = [
     ("V=48", dict(V=48), UNSUPPORTED, "V in"),
+    ("both gates", dict(gg="gg"), INVALID, "mutually exclusive"),
+    ("num_kv_heads not dividing H", dict(Hkv=3), SHAPE, "num_kv_heads"),
+    ("null k", dict(k=None), INVALID, "non-NULL"),
     ("K=0", dict(K=0), UNSUPPORTED, "K <="),
     ("K=2048", dict(K=2048), UNSUPPORTED, "K <="),
     ("H=0", dict(H=0), SHAPE, "H > 0"),
     ("fp16", dict(qkv=3), DTYPE, "qkv_dtype"),
     ("o dtype", dict(od=9), DTYPE, "o_dtype"),
     ("nan scale", dict(scale=float("nan")), INVALID, "scale"),
-    ("null g", dict(g=None), INVALID, "non-NULL"),
     ("o aliases state", dict(o="state"), INVALID, "alias"),
     ("misaligned state", dict(state="misaligned"), INVALID, "aligned"),
 ]
@@ -196,17 +211,19 @@ STEP_CASES = [
 @pytest.mark.parametrize("desc,over,status,frag", STEP_CASES, ids=[c[0] for c in STEP_CASES])
 def test_recurrent_step_rejects_without_writing(G, desc, over, status, frag):
     b = Buffers(B=1, T=4, H=2, K=64, V=64, N=4)
-    kw = dict(N=4, H=2, K=64, V=64, scale=0.125, qkv=BF16, od=F32, q=b.p("q"), k=b.p("k"),
-              v=b.p("v"), g=b.p("g"), state=b.p("h0"), o=b.p("o"))
+    kw = dict(N=4, H=2, Hkv=0, K=64, V=64, scale=0.125, qkv=BF16, od=F32, q=b.p("q"),
+              k=b.p("k"), v=b.p("v"), g=b.p("g"), gg=None, state=b.p("h0"), o=b.p("o"))
     for key, val in over.items():
         if val == "state":
             val = b.p("h0", 64)
         elif val == "misaligned":
             val = b.p("h0", 4)
+        elif val == "gg":
+            val = b.p("gg")
         kw[key] = val
-    st = G.lib.sgla_recurrent_step(kw["N"], kw["H"], kw["K"], kw["V"], kw["scale"], kw["qkv"],
-                                   kw["od"], kw["q"], kw["k"], kw["v"], kw["g"], kw["state"],
-                                   kw["o"], None)
+    st = G.lib.sgla_recurrent_step(kw["N"], kw["H"], kw["Hkv"], kw["K"], kw["V"], kw["scale"],
+                                   kw["qkv"], kw["od"], kw["q"], kw["k"], kw["v"], kw["g"],
+                                   kw["gg"], kw["state"], kw["o"], None)
     msg = G.lib.sgla_last_error().decode()
     assert st == status, (st, msg)
     assert frag in msg, msg
@@ -229,3 +246,16 @@ def test_binding_checks_initial_state_rows(G):
         G.chunk_fwd(q, q, v, g=torch.zeros(1, 10, 2), g_gamma=torch.zeros(2))
     with pytest.raises(ValueError, match="float16|bfloat16"):
         G.chunk_fwd(q.half(), q.half(), v.half())
+    q4 = torch.zeros(1, 10, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="must divide"):
+        G.chunk_fwd(q4, torch.zeros(1, 10, 3, 64, dtype=torch.bfloat16),
+                    torch.zeros(1, 10, 3, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="shape"):
+        G.chunk_fwd(q4, torch.zeros(1, 10, 2, 64, dtype=torch.bfloat16),
+                    torch.zeros(1, 10, 1, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="must divide"):
+        G.recurrent_step(torch.zeros(2, 4, 64), torch.zeros(2, 3, 64), torch.zeros(2, 3, 64),
+                         None, torch.zeros(2, 4, 64, 64))
+    with pytest.raises(ValueError, match="mutually exclusive"):
+        G.recurrent_step(torch.zeros(2, 4, 64), torch.zeros(2, 2, 64), torch.zeros(2, 2, 64),
+                         torch.zeros(2, 4), torch.zeros(2, 4, 64, 64), g_gamma=torch.zeros(4))

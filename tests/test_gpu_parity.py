@@ -117,6 +117,16 @@ SMALL_CASES = [
     small("f32_k128_v64", dtype="f32", K=128, V=64, T=130, gate="gamma"),
     small("f32_varlen", dtype="f32", B=1, T=0, K=64, V=64, fixed_lengths=(15, 85, 200),
           initial_state=True),
+    # grouped kv heads: query head h reads kv head h // (H // Hkv)
+    small("gqa_k64_h4_kv2", H=4, Hkv=2, K=64, V=128, T=150, initial_state=True),
+    small("mqa_k128_gamma", H=4, Hkv=1, K=128, V=64, T=200, gate="gamma", normalize_k=True),
+    small("gqa_k128_h6_kv2_varlen", B=1, T=0, H=6, Hkv=2, K=128, V=64,
+          fixed_lengths=(15, 85, 0, 200), initial_state=True),
+    small("gqa_k512_h4_kv2", B=1, T=140, H=4, Hkv=2, K=512, V=96),
+    small("mqa_k256_h3", T=130, H=3, Hkv=1, K=256, V=64, initial_state=True),
+    small("gqa_k256_h6_kv3_varlen", B=1, T=0, H=6, Hkv=3, K=256, V=32,
+          fixed_lengths=(70, 1, 0, 130), initial_state=True),
+    small("gqa_f32_k32", dtype="f32", H=4, Hkv=2, K=32, V=64, T=100, initial_state=True),
 ]
 
 
@@ -294,6 +304,47 @@ def test_chunk_then_decode_handoff():
 # ---------------------------------------------------------------------------
 # step (4): decode
 # ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("K,V,H,Hkv,dtype", [(64, 64, 4, 4, "bf16"), (128, 128, 6, 2, "bf16"),
+                                             (128, 256, 4, 1, "f32")])
+def test_gqa_equals_repeated_heads_bitwise(K, V, H, Hkv, dtype):
+    """Grouped kv heads give bit for bit the result of plain multi-head input
+    whose k and v repeat each kv head H // Hkv times in a row (the grouping
+    query head h -> kv head h // (H // Hkv)), through every chunk kernel."""
+    for KK in ((K, 512) if dtype == "bf16" else (K,)):
+        inp = make_chunk_inputs(small("gqa_rep", B=1, T=0, H=H, Hkv=Hkv, K=KK, V=V, dtype=dtype,
+                                      fixed_lengths=(100, 7, 64), initial_state=True, seed=21))
+        o1, h1 = run_chunk(inp)
+        rep_ = dict(inp)
+        rep_["k"] = np.repeat(inp["k"], H // Hkv, axis=2)
+        rep_["v"] = np.repeat(inp["v"], H // Hkv, axis=2)
+        o2, h2 = run_chunk(rep_)
+        assert np.array_equal(o1, o2) and np.array_equal(h1, h2), KK
+        check_full(inp, o1, h1)
+
+
+@pytest.mark.parametrize("gate", ["g", "gamma", "none"])
+@pytest.mark.parametrize("Hkv", [6, 2, 1])
+def test_decode_gate_kinds_and_kv_groups(gate, Hkv):
+    """Decode with a per-token gate, a per-head g_gamma or no decay, and with
+    grouped kv heads, against the oracle step."""
+    w = DecodeWorkload("var", N=5, H=6, K=128, V=128, steps=3, dtype="bf16", Hkv=Hkv, gate=gate,
+                       seed=40 + Hkv)
+    inp = make_decode_inputs(w)
+    bf = torch.bfloat16
+    state = to_dev(inp["state"], torch.float32)
+    S_ref = inp["state"].astype(np.float64)
+    gg = to_dev(inp["g_gamma"], torch.float32)
+    for s in range(inp["steps"]):
+        g = None if inp["g"] is None else inp["g"][s]
+        o = sgla.recurrent_step(to_dev(inp["q"][s], bf), to_dev(inp["k"][s], bf),
+                                to_dev(inp["v"][s], bf), to_dev(g, torch.float32), state,
+                                scale=inp["scale"], g_gamma=gg)
+        o_ref, S_ref = oracle.step(inp["q"][s], inp["k"][s], inp["v"][s], g, S_ref,
+                                   scale=inp["scale"], g_gamma=inp["g_gamma"])
+        torch.cuda.synchronize()
+        assert err_ratio(o.cpu().numpy(), o_ref) <= TOL_F32
+    assert err_ratio(state.cpu().numpy(), S_ref) <= TOL_F32
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("K,V", [(8, 32), (64, 64), (100, 128), (128, 128), (128, 256),
