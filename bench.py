@@ -62,15 +62,17 @@ def kernel_source_hash() -> str:
 def chunk_algorithmic(inp) -> tuple[float, float]:
     """(bytes, flops) one launch must move / perform at minimum.
 
-    bytes: q, k, v read once, g read once (if given), initial state read once
-    (if given), o written once, final state written once.  flops per chunk of
-    L tokens and head: L(L+1)(K+V) for the causal q k^T and A v products plus
-    4 L K V for q h and the state update."""
+    bytes: q read once, k and v read once per kv head, g read once (if
+    given), initial state read once (if given), o written once, final state
+    written once.  flops per chunk of L tokens and query head: L(L+1)(K+V)
+    for the causal q k^T and A v products plus 4 L K V for q h and the state
+    update."""
     B, T, H, K, V = inp["B"], inp["T"], inp["H"], inp["K"], inp["V"]
+    Hkv = inp.get("Hkv", H)
     esz = 2 if inp["dtype"] == "bf16" else 4
     N = inp["N"]
     tokens = B * T
-    nbytes = tokens * H * (2 * K + V) * esz + tokens * H * 4 * V
+    nbytes = tokens * (H * K + Hkv * (K + V)) * esz + tokens * H * 4 * V
     if inp["g"] is not None:
         nbytes += tokens * H * 4
     if inp["initial_state"] is not None:
@@ -130,7 +132,8 @@ def warm_device(fn, seconds: float):
     torch.cuda.synchronize()
 
 
-def bench_chunk(workload: str, steps: int, warmup: int, warm_seconds: float):
+def bench_chunk(workload: str, steps: int, warmup: int, warm_seconds: float,
+                expand_kv: bool = False):
     import ctypes
 
     import numpy as np
@@ -141,6 +144,12 @@ def bench_chunk(workload: str, steps: int, warmup: int, warm_seconds: float):
 
     w = CHUNK_CONFIGS[workload]
     inp = make_chunk_inputs(w)
+    if expand_kv and inp["Hkv"] != inp["H"]:
+        # the multi-head equivalent of grouped kv heads: every kv head repeated
+        # for the query heads that read it
+        rep_ = inp["H"] // inp["Hkv"]
+        inp = dict(inp, k=np.repeat(inp["k"], rep_, axis=2), v=np.repeat(inp["v"], rep_, axis=2),
+                   Hkv=inp["H"])
     dev = torch.device("cuda:0")
     qdt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
     B, T, H, K, V, N = inp["B"], inp["T"], inp["H"], inp["K"], inp["V"], inp["N"]
@@ -148,7 +157,7 @@ def bench_chunk(workload: str, steps: int, warmup: int, warm_seconds: float):
     ncopies = max(1, min(4, math.ceil(2 * MALL_BYTES / alg_bytes) + 1))
     qkv_code = 1 if inp["dtype"] == "bf16" else 2
     args = sgla._chunk_args(B, T, H, K, V, N, inp["chunk_size"], qkv_code, 2, inp["scale"],
-                            inp["output_final_state"])
+                            inp["output_final_state"], inp["Hkv"])
     cu = None
     cu_ptr = None
     if inp["cu_seqlens"] is not None:
@@ -215,7 +224,7 @@ def bench_decode(steps_timed: int, warmup: int, warm_seconds: float):
     w = DECODE_CONFIGS["decode_n256_h32_k128"]
     inp = make_decode_inputs(w)
     dev = torch.device("cuda:0")
-    N, H, K, V, S = inp["N"], inp["H"], inp["K"], inp["V"], inp["steps"]
+    N, H, K, V, S, Hkv = inp["N"], inp["H"], inp["K"], inp["V"], inp["steps"], inp["Hkv"]
     t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
     state = t(inp["state"], torch.float32)
     q, k, v, g = (t(inp["q"], torch.bfloat16), t(inp["k"], torch.bfloat16),
@@ -236,7 +245,7 @@ def bench_decode(steps_timed: int, warmup: int, warm_seconds: float):
     torch.cuda.synchronize()
     per = sorted(a.elapsed_time(b) for a, b in ev)
     mean_ms = sum(per) / len(per)
-    nbytes = 2 * N * H * K * V * 4 + N * H * (2 * K + V) * 2 + N * H * 4 + N * H * V * 4
+    nbytes = 2 * N * H * K * V * 4 + N * (H * K + Hkv * (K + V)) * 2 + N * H * 4 + N * H * V * 4
     gbs = nbytes / (mean_ms * 1e-3) / 1e9
     return {"workload": w.name, "N": N, "H": H, "K": K, "V": V, "steps": S,
             "ms_per_step_mean": round(mean_ms, 5), "ms_per_step_median": round(per[S // 2], 5),
@@ -300,6 +309,9 @@ def main():
                     help="chunked workload to time (default: the dense bf16 K=V=512 prefill)")
     ap.add_argument("--warm-seconds", type=float, default=1.0,
                     help="untimed device warm-up before the counted warmup steps")
+    ap.add_argument("--expand-kv", action="store_true",
+                    help="time grouped-kv-head workloads as plain multi-head input (k and v "
+                         "repeated per query head), for comparison")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -319,7 +331,7 @@ def main():
     if a.calibrate_copy:
         calibrate_copy()
         return
-    r = bench_chunk(a.workload, a.steps, a.warmup, a.warm_seconds)
+    r = bench_chunk(a.workload, a.steps, a.warmup, a.warm_seconds, a.expand_kv)
     inp = r["inp"]
     tokens = inp["B"] * inp["T"]
     ms_step = r["total_ms"] / a.steps
@@ -357,7 +369,7 @@ def main():
         "dtype": inp["dtype"],
         "data": "synthetic",
         "config": {"workload": a.workload, "B": inp["B"], "T": inp["T"], "H": inp["H"],
-                   "K": inp["K"], "V": inp["V"], "num_seqs": inp["N"],
+                   "num_kv_heads": inp["Hkv"], "K": inp["K"], "V": inp["V"], "num_seqs": inp["N"],
                    "chunk_size": inp["chunk_size"], "o_dtype": "f32",
                    "gate": "g" if inp["g"] is not None else
                            ("g_gamma" if inp["g_gamma"] is not None else "none"),

@@ -117,6 +117,11 @@ CHUNK_CONFIGS = {
                                      dtype="bf16", gate="gamma", normalize_k=True,
                                      output_final_state=True, seed=1003),
 }
+# Grouped kv heads (page "relinear", its GQA target: 9 query heads over 3 kv
+# heads, head dimension 64); measured beside the named workloads above.
+CHUNK_CONFIGS["gqa_bf16_k64_h9kv3"] = ChunkWorkload(
+    "gqa_bf16_k64_h9kv3", B=32, T=2048, H=9, K=64, V=64, dtype="bf16", gate="g", Hkv=3,
+    output_final_state=True, seed=1005)
 DECODE_CONFIGS = {
     "decode_n256_h32_k128": DecodeWorkload("decode_n256_h32_k128", N=256, H=32, K=128, V=128,
                                            steps=64, dtype="bf16", seed=1004),

@@ -167,7 +167,8 @@ def test_tiny_f32_full():
     check_full(inp, o, ht)
 
 
-@pytest.mark.parametrize("cfg", ["dense_bf16_k512", "varlen_bf16_k128", "long_gamma_k128"])
+@pytest.mark.parametrize("cfg", ["dense_bf16_k512", "varlen_bf16_k128", "long_gamma_k128",
+                                 "gqa_bf16_k64_h9kv3"])
 def test_named_workload_sampled(cfg):
     w = CHUNK_CONFIGS[cfg]
     inp = make_chunk_inputs(w)
