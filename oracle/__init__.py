@@ -45,6 +45,9 @@ def _bind(lib):
     lib.sgla_oracle_chunk_local_cumsum.restype = ctypes.c_int
     lib.sgla_oracle_chunk_local_cumsum.argtypes = [ctypes.c_int] * 3 + [dp, lp, ctypes.c_int,
                                                                         ctypes.c_int, dp]
+    lib.sgla_oracle_bwd.restype = ctypes.c_int
+    lib.sgla_oracle_bwd.argtypes = ([ctypes.c_int] * 5 + [dp] * 5 + [ctypes.c_double, dp, lp, ctypes.c_int]
+                                    + [dp] * 8 + [ctypes.c_int])
     lib.sgla_oracle_step.restype = ctypes.c_int
     lib.sgla_oracle_step.argtypes = [ctypes.c_int] * 5 + [dp] * 5 + [ctypes.c_double, dp, dp,
                                                                      ctypes.c_int]
@@ -122,6 +125,45 @@ def fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None, cu_seqlen
     if rc != 0:
         raise ValueError(f"sgla_oracle_fwd rejected its arguments (code {rc})")
     return o, ht
+
+
+def bwd(q, k, v, do, g=None, g_gamma=None, scale=None, initial_state=None, dht=None,
+        cu_seqlens=None, nthreads=None, lib=None):
+    """Token-by-token backward: gradients of sum <do, o> + sum <dht, final_state>.
+
+    q, k: [B, T, H, K]; v, do: [B, T, H, V]; g: [B, T, H] or None; g_gamma:
+    [H] or None; initial_state, dht: [N, H, K, V] or None; cu_seqlens as for
+    fwd.  Returns a dict of float64 arrays dq, dk [B, T, H, K], dv [B, T, H,
+    V], dg [B, T, H] (None without g), dg_gamma [H] (None without g_gamma),
+    dh0 [N, H, K, V]."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if k.shape[2] != H:
+        raise ValueError("the oracle backward takes multi-head k and v (H heads)")
+    if scale is None:
+        scale = K ** -0.5
+    g, g_gamma, h0, dht = _f64(g), _f64(g_gamma), _f64(initial_state), _f64(dht)
+    cu = None
+    N = B
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N = cu.shape[0] - 1
+    dq = np.zeros((B, T, H, K))
+    dk = np.zeros((B, T, H, K))
+    dv = np.zeros((B, T, H, V))
+    dg = np.zeros((B, T, H)) if g is not None else None
+    dgg = np.zeros(H) if g_gamma is not None else None
+    dh0 = np.zeros((N, H, K, V))
+    lib = lib or load()
+    rc = lib.sgla_oracle_bwd(B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(g_gamma),
+                             float(scale), _ptr(h0),
+                             None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                             N, _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dgg),
+                             _ptr(dh0), int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"sgla_oracle_bwd rejected its arguments (code {rc})")
+    return dict(dq=dq, dk=dk, dv=dv, dg=dg, dg_gamma=dgg, dh0=dh0)
 
 
 def step(q, k, v, g, state, scale=None, g_gamma=None, nthreads=None, lib=None):

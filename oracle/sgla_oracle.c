@@ -330,3 +330,212 @@ int sgla_oracle_chunk_local_cumsum(int B, int T, int H, const double *g,
     }
     return 0;
 }
+
+/*
+ * Backward of sgla_oracle_fwd (page "flash-linear-attention 中的 Simple GLA",
+ * section 三: the backward produces the q, k, v and gate gradients and the
+ * initial-state gradient from an fp32 state trajectory; section 五: its tests
+ * compare dq, dk, dv, dg and dh0 with the naive recurrent reference).
+ *
+ * Gradients of   L = sum_t <do_t, o_t> + sum_n <dht_n, final_state_n>
+ * by reverse-mode differentiation of the token recurrence itself.  Forward,
+ * keeping every state S_0 (initial) .. S_L:  S_t = gamma_t S_{t-1} + k_t v_t^T
+ * with gamma_t = exp(g_t).  Then in reverse, with D the gradient with respect
+ * to S_t:
+ *     D    = dht (or 0)                       before the last token
+ *     D   += scale q_t do_t^T                 (o_t = scale S_t^T q_t)
+ *     dq_t = scale S_t do_t
+ *     dk_t = D v_t ,   dv_t = D^T k_t         (S_t receives k_t v_t^T)
+ *     dg_t = gamma_t <D, S_{t-1}>             (d gamma_t / d g_t = gamma_t)
+ *     D    = gamma_t D                        (now the gradient of S_{t-1})
+ * and dh0 = D after the first token.  With g_gamma the gradient of g_gamma[h]
+ * is the sum of dg_t over every token of every sequence of head h.  Plain
+ * multi-head input (k and v with H heads).
+ */
+typedef struct {
+    int H, K, V;
+    const double *q, *k, *v, *g, *g_gamma, *h0, *dout, *dht;
+    double scale;
+    double *dq, *dk, *dv, *dg, *dh0;
+    double *gamma_part;   /* [n_units] sum of dg_t of the unit (g_gamma) */
+    const unit_t *units;
+    int64_t n_units, next;
+    int64_t max_len;
+    pthread_mutex_t mu;
+} bwd_job_t;
+
+static void bwd_unit(const bwd_job_t *J, int64_t ui, double *Sall, double *D)
+{
+    const unit_t *u = &J->units[ui];
+    const int H = J->H, K = J->K, V = J->V, h = u->head;
+    const int64_t KV = (int64_t)K * V;
+    /* forward, keeping S_0 .. S_len */
+    double *S0 = Sall;
+    const double *h0 = J->h0 ? J->h0 + (u->seq * H + h) * KV : NULL;
+    for (int64_t i = 0; i < KV; ++i) S0[i] = h0 ? h0[i] : 0.0;
+    for (int64_t s = 0; s < u->len; ++s) {
+        const int64_t t = u->bos + s;
+        const double *kt = J->k + ((size_t)t * H + h) * K;
+        const double *vt = J->v + ((size_t)t * H + h) * V;
+        const double logg = J->g ? J->g[(size_t)t * H + h] : (J->g_gamma ? J->g_gamma[h] : 0.0);
+        const double gamma = exp(logg);
+        const double *Sp = Sall + s * KV;
+        double *Sn = Sall + (s + 1) * KV;
+        for (int a = 0; a < K; ++a)
+            for (int b = 0; b < V; ++b)
+                Sn[(int64_t)a * V + b] = gamma * Sp[(int64_t)a * V + b] + kt[a] * vt[b];
+    }
+    /* reverse */
+    const double *dht = J->dht ? J->dht + (u->seq * H + h) * KV : NULL;
+    for (int64_t i = 0; i < KV; ++i) D[i] = dht ? dht[i] : 0.0;
+    double gsum = 0.0;
+    for (int64_t s = u->len - 1; s >= 0; --s) {
+        const int64_t t = u->bos + s;
+        const double *qt = J->q + ((size_t)t * H + h) * K;
+        const double *kt = J->k + ((size_t)t * H + h) * K;
+        const double *vt = J->v + ((size_t)t * H + h) * V;
+        const double *dot = J->dout + ((size_t)t * H + h) * V;
+        const double logg = J->g ? J->g[(size_t)t * H + h] : (J->g_gamma ? J->g_gamma[h] : 0.0);
+        const double gamma = exp(logg);
+        const double *St = Sall + (s + 1) * KV;
+        const double *Sp = Sall + s * KV;
+        double *dqt = J->dq + ((size_t)t * H + h) * K;
+        double *dkt = J->dk + ((size_t)t * H + h) * K;
+        double *dvt = J->dv + ((size_t)t * H + h) * V;
+#if SGLA_ORACLE_MUTANT != 12
+        for (int a = 0; a < K; ++a)
+            for (int b = 0; b < V; ++b) D[(int64_t)a * V + b] += J->scale * qt[a] * dot[b];
+#endif
+        for (int a = 0; a < K; ++a) {
+            double x = 0.0;
+            for (int b = 0; b < V; ++b) x += St[(int64_t)a * V + b] * dot[b];
+            dqt[a] = J->scale * x;
+        }
+        for (int a = 0; a < K; ++a) {
+            double x = 0.0;
+            for (int b = 0; b < V; ++b) x += D[(int64_t)a * V + b] * vt[b];
+            dkt[a] = x;
+        }
+        for (int b = 0; b < V; ++b) {
+            double x = 0.0;
+            for (int a = 0; a < K; ++a) x += D[(int64_t)a * V + b] * kt[a];
+            dvt[b] = x;
+        }
+#if SGLA_ORACLE_MUTANT == 12
+        for (int a = 0; a < K; ++a)
+            for (int b = 0; b < V; ++b) D[(int64_t)a * V + b] += J->scale * qt[a] * dot[b];
+#endif
+        double inner = 0.0;
+#if SGLA_ORACLE_MUTANT == 11
+        for (int64_t i = 0; i < KV; ++i) inner += D[i] * St[i];
+#else
+        for (int64_t i = 0; i < KV; ++i) inner += D[i] * Sp[i];
+#endif
+        const double dgt = gamma * inner;
+        if (J->dg) J->dg[(size_t)t * H + h] = dgt;
+        gsum += dgt;
+#if SGLA_ORACLE_MUTANT != 10
+        for (int64_t i = 0; i < KV; ++i) D[i] *= gamma;
+#endif
+    }
+    if (J->dh0) {
+        double *d0 = J->dh0 + (u->seq * H + h) * KV;
+        for (int64_t i = 0; i < KV; ++i) d0[i] = D[i];
+    }
+    J->gamma_part[ui] = gsum;
+}
+
+static void *bwd_worker(void *arg)
+{
+    bwd_job_t *J = (bwd_job_t *)arg;
+    const int64_t KV = (int64_t)J->K * J->V;
+    double *Sall = (double *)malloc((size_t)(J->max_len + 1) * KV * sizeof(double));
+    double *D = (double *)malloc((size_t)KV * sizeof(double));
+    if (!Sall || !D) { free(Sall); free(D); return (void *)1; }
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int64_t i = J->next++;
+        pthread_mutex_unlock(&J->mu);
+        if (i >= J->n_units) break;
+        bwd_unit(J, i, Sall, D);
+    }
+    free(Sall);
+    free(D);
+    return NULL;
+}
+
+/*
+ * Backward over all sequences and heads (multi-head: k, v have H heads).
+ *   q, k, dq, dk : [B, T, H, K]   v, dout, dv : [B, T, H, V]
+ *   g, dg : [B, T, H] or NULL;  g_gamma, dg_gamma : [H] or NULL
+ *   h0, dht, dh0 : [N, H, K, V] or NULL (dht NULL = no loss on the final state)
+ *   cu_seqlens : [num_seqs + 1] or NULL, as for sgla_oracle_fwd.
+ * dq, dk, dv are required; dg is written when given (g given), dg_gamma when
+ * given (g_gamma given), dh0 when given.  Returns 0, or negative on a
+ * malformed argument.
+ */
+int sgla_oracle_bwd(int B, int T, int H, int K, int V,
+                    const double *q, const double *k, const double *v,
+                    const double *g, const double *g_gamma, double scale,
+                    const double *h0, const int64_t *cu_seqlens, int num_seqs,
+                    const double *dout, const double *dht,
+                    double *dq, double *dk, double *dv, double *dg, double *dg_gamma,
+                    double *dh0, int nthreads)
+{
+    if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return -1;
+    if (g && g_gamma) return -2;
+    if (cu_seqlens && B != 1) return -3;
+    if (!dq || !dk || !dv) return -1;
+    int N = cu_seqlens ? num_seqs : B;
+    if (N < 0) return -1;
+    int64_t n_units = (int64_t)N * H;
+    unit_t *units = (unit_t *)malloc((size_t)(n_units > 0 ? n_units : 1) * sizeof(unit_t));
+    double *part = (double *)calloc((size_t)(n_units > 0 ? n_units : 1), sizeof(double));
+    if (!units || !part) { free(units); free(part); return -4; }
+    int64_t max_len = 0;
+    for (int n = 0; n < N; ++n) {
+        int64_t bos, len;
+        if (cu_seqlens) {
+            bos = cu_seqlens[n];
+            len = cu_seqlens[n + 1] - cu_seqlens[n];
+            if (len < 0 || bos < 0 || cu_seqlens[n + 1] > (int64_t)T) { free(units); free(part); return -5; }
+        } else {
+            bos = (int64_t)n * T;
+            len = T;
+        }
+        if (len > max_len) max_len = len;
+        for (int h = 0; h < H; ++h) {
+            unit_t *u = &units[(int64_t)n * H + h];
+            u->bos = bos; u->len = len; u->seq = n; u->head = h;
+        }
+    }
+    bwd_job_t J;
+    J.H = H; J.K = K; J.V = V;
+    J.q = q; J.k = k; J.v = v; J.g = g; J.g_gamma = g_gamma; J.h0 = h0; J.dout = dout; J.dht = dht;
+    J.scale = scale; J.dq = dq; J.dk = dk; J.dv = dv; J.dg = g ? dg : NULL; J.dh0 = dh0;
+    J.gamma_part = part; J.units = units; J.n_units = n_units; J.next = 0; J.max_len = max_len;
+    pthread_mutex_init(&J.mu, NULL);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    int started = 0, rc = 0;
+    for (int i = 1; i < nthreads; ++i)
+        if (pthread_create(&th[started], NULL, bwd_worker, &J) == 0) ++started;
+    if (bwd_worker(&J) != NULL) rc = -4;
+    for (int i = 0; i < started; ++i) {
+        void *r = NULL;
+        pthread_join(th[i], &r);
+        if (r != NULL) rc = -4;
+    }
+    pthread_mutex_destroy(&J.mu);
+    if (rc == 0 && g_gamma && dg_gamma) {
+        for (int h = 0; h < H; ++h) {
+            double s = 0.0;
+            for (int n = 0; n < N; ++n) s += part[(int64_t)n * H + h];
+            dg_gamma[h] = s;
+        }
+    }
+    free(units);
+    free(part);
+    return rc;
+}

@@ -377,11 +377,87 @@ def pin_step_variants(lib, seed=12, N=3, H=4, Hkv=2, K=3, V=5):
     return np.array_equal(o1, o5) and np.array_equal(S1, S5)
 
 
+def _loss(lib, q, k, v, g, gg, scale, S0, cu, do, dht):
+    o, ht = oracle.fwd(q, k, v, g=g, g_gamma=gg, scale=scale, initial_state=S0, cu_seqlens=cu,
+                       nthreads=1, lib=lib)
+    return float(np.sum(o * do) + np.sum(ht * dht))
+
+
+def pin_bwd_finite_differences(lib, seed=13, H=2, K=3, V=2):
+    """Backward (page "flash-linear-attention 中的 Simple GLA", section 三 and
+    the gradient tests of section 五): every gradient -- dq, dk, dv, dg or
+    dg_gamma, dh0 -- equals the central finite difference of L = <do, o> +
+    <dht, final_state> computed with the (pinned) forward, on packed sequences
+    with an empty one, for a per-token gate, a per-head g_gamma and no gate."""
+    rng = np.random.default_rng(seed)
+    cu = np.array([0, 5, 5, 13], dtype=np.int64)
+    T, N = 13, 3
+    q, k, v = _rand(rng, 1, T, H, K), _rand(rng, 1, T, H, K), _rand(rng, 1, T, H, V)
+    do = _rand(rng, 1, T, H, V)
+    dht = _rand(rng, N, H, K, V)
+    S0 = _rand(rng, N, H, K, V)
+    scale, eps = 0.7, 1e-6
+    for kind in ("g", "gamma", "none"):
+        g = logsigmoid(_rand(rng, 1, T, H)) if kind == "g" else None
+        gg = np.log([0.9, 0.6]) if kind == "gamma" else None
+        gr = oracle.bwd(q, k, v, do, g=g, g_gamma=gg, scale=scale, initial_state=S0, dht=dht,
+                        cu_seqlens=cu, nthreads=1, lib=lib)
+        args = dict(q=q, k=k, v=v, g=g, gg=gg, S0=S0)
+        want = dict(q="dq", k="dk", v="dv", g="dg", gg="dg_gamma", S0="dh0")
+        for name, gname in want.items():
+            x = args[name]
+            if x is None:
+                if gr.get(gname) is not None:
+                    return False
+                continue
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                a = dict(args)
+                xp = x.copy(); xp[idx] += eps
+                xm = x.copy(); xm[idx] -= eps
+                a[name] = xp
+                lp = _loss(lib, a["q"], a["k"], a["v"], a["g"], a["gg"], scale, a["S0"], cu, do, dht)
+                a[name] = xm
+                lm = _loss(lib, a["q"], a["k"], a["v"], a["g"], a["gg"], scale, a["S0"], cu, do, dht)
+                fd[idx] = (lp - lm) / (2 * eps)
+            if _rel(gr[gname], fd) > 1e-6:
+                return False
+    return True
+
+
+def pin_bwd_gate_identity(lib, seed=14, B=2, T=150, H=2, K=5, V=4):
+    """The gate gradient from the mathematics of the scalar gate: every term of
+    o_t and of the final state depends on the log gates only through
+    differences of their running sums G, so dL/dG_t = q_t . dq_t - k_t . dk_t
+    (+ <dht, S_T> at the last token), and dg_j is the reverse cumulative sum of
+    that over t >= j -- the relation behind section 三's reverse cumsum for dg.
+    Checked against the oracle's dg (computed as gamma_t <D, S_{t-1}>) and, for
+    g_gamma, the sum of dg over tokens."""
+    rng = np.random.default_rng(seed)
+    q, k, v = _rand(rng, B, T, H, K), _rand(rng, B, T, H, K), _rand(rng, B, T, H, V)
+    do, dht = _rand(rng, B, T, H, V), _rand(rng, B, H, K, V)
+    g = logsigmoid(_rand(rng, B, T, H))
+    S0 = _rand(rng, B, H, K, V)
+    _, ht = oracle.fwd(q, k, v, g=g, scale=0.5, initial_state=S0, lib=lib)
+    gr = oracle.bwd(q, k, v, do, g=g, scale=0.5, initial_state=S0, dht=dht, lib=lib)
+    r = np.sum(q * gr["dq"], axis=-1) - np.sum(k * gr["dk"], axis=-1)      # [B, T, H]
+    r[:, -1, :] += np.einsum("bhkv,bhkv->bh", dht, ht)
+    ref = np.flip(np.cumsum(np.flip(r, axis=1), axis=1), axis=1)
+    if _rel(gr["dg"], ref) > 1e-10:
+        return False
+    gam = retnet_gamma(H).astype(np.float64)
+    g2 = oracle.bwd(q, k, v, do, g=np.broadcast_to(gam, (B, T, H)).copy(), scale=0.5,
+                    initial_state=S0, dht=dht, lib=lib)
+    g3 = oracle.bwd(q, k, v, do, g_gamma=gam, scale=0.5, initial_state=S0, dht=dht, lib=lib)
+    return (_rel(g3["dg_gamma"], g2["dg"].sum(axis=(0, 1))) < 1e-12
+            and all(np.array_equal(g2[x], g3[x]) for x in ("dq", "dk", "dv", "dh0")))
+
+
 ALL_PINS = [pin_chunk_local_cumsum, pin_hand_example, pin_brute_force, pin_zero_gate, pin_full_forget,
             pin_split_sequence, pin_varlen_equals_per_sequence, pin_chunk_form,
             pin_gamma_is_broadcast_g, pin_retnet_closed_form, pin_invariants,
             pin_prefill_then_decode, pin_step_brute_force, pin_gqa_is_repeated_mha,
-            pin_step_variants]
+            pin_step_variants, pin_bwd_finite_differences, pin_bwd_gate_identity]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -426,6 +502,9 @@ MUTANTS = {
     7: "decode step forms v k^T instead of k v^T",
     8: "query head h reads kv head h % Hkv (interleaved) instead of h // (H / Hkv)",
     9: "decode step reads g_gamma by sequence instead of by head",
+    10: "backward: state gradient not decayed between tokens",
+    11: "backward: gate gradient pairs with the state after the token",
+    12: "backward: k and v gradients miss the token's own output term",
 }
 
 
