@@ -25,7 +25,7 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "recurrent_step", "chunk_local_cumsum", "library_path", "lib",
+__all__ = ["chunk_fwd", "chunk_bwd", "recurrent_step", "chunk_local_cumsum", "library_path", "lib",
            "SglaError", "ABI_VERSION"]
 
 ABI_VERSION = 2
@@ -68,6 +68,10 @@ def _load():
     lib.sgla_chunk_fwd_workspace_size.argtypes = [pargs, vp]
     lib.sgla_chunk_fwd.restype = ctypes.c_int
     lib.sgla_chunk_fwd.argtypes = [pargs, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sgla_chunk_bwd_workspace_size.restype = sz
+    lib.sgla_chunk_bwd_workspace_size.argtypes = [pargs, vp]
+    lib.sgla_chunk_bwd.restype = ctypes.c_int
+    lib.sgla_chunk_bwd.argtypes = [pargs] + [vp] * 15 + [vp, sz, vp]
     lib.sgla_chunk_local_cumsum.restype = ctypes.c_int
     lib.sgla_chunk_local_cumsum.argtypes = [pargs, vp, vp, vp, vp, sz, vp]
     lib.sgla_recurrent_step.restype = ctypes.c_int
@@ -204,6 +208,60 @@ def chunk_fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None,
     if st != _OK:
         _raise(st, "sgla_chunk_fwd")
     return o, ht
+
+
+def chunk_bwd(q, k, v, do, g=None, g_gamma=None, scale=None, initial_state=None, dht=None,
+              cu_seqlens=None, chunk_size=64):
+    """Backward of chunk_fwd on the GPU: gradients of sum <do, o> + sum <dht,
+    final_state> (dht None: no loss on the final state).
+
+    q, k [B, T, H, K], v, do [B, T, H, V] (all bf16 or all float32), g, g_gamma,
+    initial_state and cu_seqlens as for chunk_fwd.  Returns a dict of float32
+    tensors: dq, dk [B, T, H, K], dv [B, T, H, V], dg [B, T, H] (None without g),
+    dg_gamma [H] (None without g_gamma), dh0 [N, H, K, V]."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor [B, T, H, K]")
+    dev = q.device
+    B, T, H, K = q.shape
+    if not isinstance(v, torch.Tensor) or v.dim() != 4:
+        raise ValueError("v must be a 4-D tensor [B, T, H, V]")
+    V = v.shape[-1]
+    qkv = _dtype_code(q.dtype, "q")
+    _check_dev("q", q, dev)
+    _check_dev("k", k, dev, q.dtype, (B, T, H, K))
+    _check_dev("v", v, dev, q.dtype, (B, T, H, V))
+    _check_dev("do", do, dev, q.dtype, (B, T, H, V))
+    if g is not None and g_gamma is not None:
+        raise ValueError("g and g_gamma are mutually exclusive; pass at most one")
+    _check_dev("g", g, dev, torch.float32, (B, T, H))
+    _check_dev("g_gamma", g_gamma, dev, torch.float32, (H,))
+    cu = _host_cu(cu_seqlens)
+    N = B if cu is None else cu.numel() - 1
+    if cu is not None and B != 1:
+        raise ValueError(f"packed input (cu_seqlens) requires B == 1, got B={B}")
+    _check_dev("initial_state", initial_state, dev, torch.float32, (N, H, K, V))
+    _check_dev("dht", dht, dev, torch.float32, (N, H, K, V))
+    if scale is None:
+        scale = K ** -0.5
+    args = _chunk_args(B, T, H, K, V, N, chunk_size, qkv, _F32, scale, 0, H)
+    cu_ptr = None if cu is None else ctypes.c_void_p(cu.data_ptr())
+    n = lib.sgla_chunk_bwd_workspace_size(ctypes.byref(args), cu_ptr)
+    if n == 0 and lib.sgla_last_error():
+        raise ValueError(f"sgla_chunk_bwd_workspace_size: {lib.sgla_last_error().decode(errors='replace')}")
+    f32 = dict(device=dev, dtype=torch.float32)
+    dq = torch.empty((B, T, H, K), **f32)
+    dk = torch.empty((B, T, H, K), **f32)
+    dv = torch.empty((B, T, H, V), **f32)
+    dg = torch.empty((B, T, H), **f32) if g is not None else None
+    dgg = torch.empty((H,), **f32) if g_gamma is not None else None
+    dh0 = torch.empty((N, H, K, V), **f32)
+    ws = torch.empty(max(n, 1), device=dev, dtype=torch.uint8)
+    st = lib.sgla_chunk_bwd(ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(g_gamma),
+                            _ptr(initial_state), cu_ptr, _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk),
+                            _ptr(dv), _ptr(dg), _ptr(dgg), _ptr(dh0), _ptr(ws), n, _stream(dev))
+    if st != _OK:
+        _raise(st, "sgla_chunk_bwd")
+    return dict(dq=dq, dk=dk, dv=dv, dg=dg, dg_gamma=dgg, dh0=dh0)
 
 
 def chunk_local_cumsum(g, chunk_size=64, cu_seqlens=None):

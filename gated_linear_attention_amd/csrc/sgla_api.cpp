@@ -146,6 +146,36 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
   return SGLA_OK;
 }
 
+// Backward request: the forward's shape rules, then the backward's own
+// support set; workspace = tables, per-chunk states and state gradients,
+// per-chunk gate sums.
+struct BwdPlan {
+  Plan P;
+  size_t h_off = 0, dh_off = 0, gpart_off = 0, total_bytes = 0;
+};
+
+sgla_status plan_bwd(const sgla_chunk_args* a, const int64_t* cu, BwdPlan* B) {
+  sgla_status st = plan_shape(a, cu, false, &B->P);
+  if (st != SGLA_OK) return st;
+  if (a->qkv_dtype != SGLA_BF16 && a->qkv_dtype != SGLA_F32)
+    return fail(SGLA_ERR_DTYPE, "qkv_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", a->qkv_dtype);
+  if (!(a->K == 16 || a->K == 32 || a->K == 64 || a->K == 128))
+    return fail(SGLA_ERR_UNSUPPORTED, "the backward supports K in {16,32,64,128} (got %d)", a->K);
+  if (a->V <= 0 || a->V % 32 != 0)
+    return fail(SGLA_ERR_UNSUPPORTED, "the backward supports V a multiple of 32 (got %d)", a->V);
+  if (B->P.Hkv != a->H)
+    return fail(SGLA_ERR_UNSUPPORTED, "the backward supports multi-head k and v only (num_kv_heads=%d, H=%d)",
+                a->num_kv_heads, a->H);
+  if (!std::isfinite(a->scale)) return fail(SGLA_ERR_INVALID_ARG, "scale must be finite");
+  const size_t tasks = (size_t)B->P.num_chunks * a->H;
+  const size_t rec = tasks * (size_t)a->K * a->V * sizeof(float);
+  B->h_off = align_up(B->P.total_bytes, 256);
+  B->dh_off = B->h_off + align_up(rec, 256);
+  B->gpart_off = B->dh_off + align_up(rec, 256);
+  B->total_bytes = B->gpart_off + align_up(tasks * sizeof(float), 256);
+  return SGLA_OK;
+}
+
 sgla_status hip_fail(hipError_t e, const char* what) {
   return fail(SGLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -273,6 +303,76 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
                                  : sgla::launch_chunk_fwd_bf16(p, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "launching the chunk kernel");
+  return ok();
+}
+
+size_t sgla_chunk_bwd_workspace_size(const sgla_chunk_args* args, const int64_t* cu_seqlens_host) {
+  BwdPlan B;
+  if (plan_bwd(args, cu_seqlens_host, &B) != SGLA_OK) return 0;
+  g_last_error.clear();
+  return B.total_bytes;
+}
+
+sgla_status sgla_chunk_bwd(const sgla_chunk_args* args, const void* q, const void* k, const void* v,
+                           const float* g, const float* g_gamma, const float* initial_state,
+                           const int64_t* cu_seqlens_host, const void* dout, const float* dht,
+                           float* dq, float* dk, float* dv, float* dg, float* dg_gamma, float* dh0,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  BwdPlan B;
+  sgla_status st = plan_bwd(args, cu_seqlens_host, &B);
+  if (st != SGLA_OK) return st;
+  const Plan& P = B.P;
+  const sgla_chunk_args& a = *args;
+  if (g != nullptr && g_gamma != nullptr)
+    return fail(SGLA_ERR_INVALID_ARG, "g and g_gamma are mutually exclusive; pass at most one");
+  if (g != nullptr && dg == nullptr) return fail(SGLA_ERR_INVALID_ARG, "g is given but dg is NULL");
+  if (g_gamma != nullptr && dg_gamma == nullptr)
+    return fail(SGLA_ERR_INVALID_ARG, "g_gamma is given but dg_gamma is NULL");
+  const bool any_tokens = P.total_tokens > 0;
+  if (any_tokens && (q == nullptr || k == nullptr || v == nullptr || dout == nullptr || dq == nullptr ||
+                     dk == nullptr || dv == nullptr))
+    return fail(SGLA_ERR_INVALID_ARG, "q, k, v, dout, dq, dk and dv must be non-NULL");
+  if (any_tokens && !(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(dout, 16) &&
+                      aligned(dq, 16) && aligned(dk, 16) && aligned(dv, 16)))
+    return fail(SGLA_ERR_INVALID_ARG, "q, k, v, dout, dq, dk and dv must be 16-byte aligned");
+  if ((g && !aligned(g, 4)) || (dg && !aligned(dg, 4)) || (initial_state && !aligned(initial_state, 16)) ||
+      (dht && !aligned(dht, 16)) || (dh0 && !aligned(dh0, 16)))
+    return fail(SGLA_ERR_INVALID_ARG, "g, dg and state pointers must be aligned");
+  const size_t need = B.total_bytes;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(SGLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
+                workspace == nullptr ? " (NULL)" : "");
+  if (need > 0 && !aligned(workspace, 256)) return fail(SGLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+  char* ws = static_cast<char*>(workspace);
+  st = upload_tables(P, ws, stream);
+  if (st != SGLA_OK) return st;
+  sgla::ChunkBwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.dout = dout;
+  p.g = g;
+  p.g_gamma = g_gamma;
+  p.h0 = initial_state;
+  p.dht = dht;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dg = g != nullptr ? dg : nullptr;
+  p.dg_gamma = g_gamma != nullptr ? dg_gamma : nullptr;
+  p.dh0 = dh0;
+  p.scale = a.scale;
+  p.H = a.H;
+  p.K = a.K;
+  p.V = a.V;
+  p.qkv_bf16 = a.qkv_dtype == SGLA_BF16;
+  p.seqs = layout_of(args, P, ws);
+  p.hbuf = reinterpret_cast<float*>(ws + B.h_off);
+  p.dhbuf = reinterpret_cast<float*>(ws + B.dh_off);
+  p.gpart = reinterpret_cast<float*>(ws + B.gpart_off);
+  hipError_t e = sgla::launch_chunk_bwd(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "launching the backward kernels");
   return ok();
 }
 

@@ -98,6 +98,34 @@ hipError_t launch_chunk_fwd_bf16_wide(const ChunkFwdParams& p, hipStream_t strea
 // float32 q/k/v, VALU path.  K in {16,32,64,128}, V % 32 == 0.
 hipError_t launch_chunk_fwd_f32(const ChunkFwdParams& p, hipStream_t stream);
 
+// Backward (fp32 matrix-core path): q, k, v, dout all bf16 or all float32;
+// every gradient float32.  K in {16, 32, 64, 128}, V % 32 == 0, multi-head.
+struct ChunkBwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* g;            // [T_total, H] or nullptr
+  const float* g_gamma;      // [H] or nullptr
+  const float* h0;           // [N, H, K, V] or nullptr
+  const float* dht;          // [N, H, K, V] or nullptr
+  float* dq;                 // [T_total, H, K]
+  float* dk;
+  float* dv;                 // [T_total, H, V]
+  float* dg;                 // [T_total, H] or nullptr
+  float* dg_gamma;           // [H] or nullptr
+  float* dh0;                // [N, H, K, V] or nullptr
+  float scale;
+  int32_t H, K, V;
+  int32_t qkv_bf16;
+  SeqLayout seqs;
+  float* hbuf;               // workspace [num_chunks, H, K, V]: state entering each chunk
+  float* dhbuf;              // workspace [num_chunks, H, K, V]: gradient of the state leaving it
+  float* gpart;              // workspace [num_chunks, H]: per-chunk sums of dg (g_gamma)
+};
+
+hipError_t launch_chunk_bwd(const ChunkBwdParams& p, hipStream_t stream);
+
 struct StepParams {
   const void* q;
   const void* k;

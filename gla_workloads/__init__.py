@@ -28,6 +28,7 @@ import numpy as np
 
 __all__ = ["ChunkWorkload", "DecodeWorkload", "CHUNK_CONFIGS", "DECODE_CONFIGS",
            "round_to_bf16", "logsigmoid", "make_chunk_inputs", "make_decode_inputs",
+           "make_backward_inputs",
            "retnet_gamma"]
 
 
@@ -183,6 +184,19 @@ def make_chunk_inputs(w: ChunkWorkload) -> dict:
     return dict(q=q, k=k, v=v, g=g, g_gamma=g_gamma, initial_state=h0, cu_seqlens=cu,
                 scale=float(scale), chunk_size=w.chunk_size, dtype=w.dtype,
                 output_final_state=w.output_final_state, B=B, T=T, H=H, K=K, V=V, N=N, Hkv=Hkv)
+
+
+def make_backward_inputs(inp: dict, seed: int, final_state_grad: bool = True) -> dict:
+    """Draw the output gradient do [B,T,H,V] (N(0,1), rounded to the input
+    dtype) and, if ``final_state_grad``, the final-state gradient dht
+    [N,H,K,V] (0.1 N(0,1) float32) for a batch from make_chunk_inputs."""
+    rng = np.random.default_rng(seed)
+    B, T, H, K, V, N = inp["B"], inp["T"], inp["H"], inp["K"], inp["V"], inp["N"]
+    do = _as_input_dtype(rng.standard_normal((B, T, H, V), dtype=np.float32), inp["dtype"])
+    dht = None
+    if final_state_grad:
+        dht = rng.standard_normal((N, H, K, V), dtype=np.float32) * np.float32(0.1)
+    return dict(do=do, dht=dht)
 
 
 def make_decode_inputs(w: DecodeWorkload, steps: Optional[int] = None) -> dict:

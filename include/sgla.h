@@ -143,6 +143,55 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args *args,
                            hipStream_t stream);
 
 /*
+ * Bytes of device workspace sgla_chunk_bwd needs: the packed-sequence tables,
+ * the fp32 state entering every 64-token chunk and the fp32 gradient of the
+ * state leaving it (2 * 4 K V bytes per chunk and head), and 4 bytes per
+ * chunk and head for the g_gamma reduction.  Returns 0 on invalid arguments
+ * (reason in sgla_last_error()).
+ */
+size_t sgla_chunk_bwd_workspace_size(const sgla_chunk_args *args, const int64_t *cu_seqlens_host);
+
+/*
+ * Backward of sgla_chunk_fwd (section 三: the backward passes over the chunk
+ * states in fp32 and recovers the gate gradient by a reverse chunk-local
+ * cumulative sum; section 五 tests dq, dk, dv, dg and dh0).  Computes the
+ * gradients of
+ *     L = sum_t <dout_t, o_t> + sum_n <dht_n, final_state_n>
+ * with respect to q, k, v, the gates and initial_state, for the forward with
+ * the same arguments.  Three launches: a state pass (forward states and
+ * reverse state gradients, one workgroup per (sequence, head, 32-column V
+ * tile) each), a per-(chunk, head) gradient kernel, and with g_gamma a
+ * per-head reduction.  Every product runs on the fp32 matrix cores.
+ *
+ * Arguments (device pointers unless stated):
+ *   args            as for sgla_chunk_fwd; o_dtype and output_final_state
+ *                   are not read; num_kv_heads must be 0 or H.
+ *   q, k, v, g, g_gamma, initial_state, cu_seqlens_host
+ *                   the forward's inputs (same layouts and rules).
+ *   dout            [B, T, H, V] in qkv_dtype: gradient of o.
+ *   dht             [N, H, K, V] float32 gradient of final_state, or NULL
+ *                   (no loss on the final state).
+ *   dq, dk          [B, T, H, K] float32;  dv [B, T, H, V] float32.
+ *   dg              [B, T, H] float32; required when g is given, else unused.
+ *   dg_gamma        [H] float32; required when g_gamma is given, else unused.
+ *   dh0             [N, H, K, V] float32 gradient of initial_state, or NULL.
+ *   workspace       >= sgla_chunk_bwd_workspace_size(args, cu_seqlens_host).
+ * Outputs must not overlap inputs or each other.
+ * Supported: K in {16, 32, 64, 128}, V a multiple of 32, bf16 or float32
+ * inputs, chunk_size 64, multi-head k and v.
+ */
+sgla_status sgla_chunk_bwd(const sgla_chunk_args *args,
+                           const void *q, const void *k, const void *v,
+                           const float *g, const float *g_gamma,
+                           const float *initial_state,
+                           const int64_t *cu_seqlens_host,
+                           const void *dout, const float *dht,
+                           float *dq, float *dk, float *dv, float *dg, float *dg_gamma,
+                           float *dh0,
+                           void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
  * Step (1) alone: chunk-local inclusive cumulative sum of g times 1/ln 2,
  * restarting at every chunk_size-token chunk of every sequence (section 三,
  * the chunk_local_cumsum call with the RCP_LN2 scale).  g and gc are device

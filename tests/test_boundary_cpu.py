@@ -37,6 +37,7 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("sgla_chunk_fwd", "sgla_recurrent_step", "sgla_chunk_fwd_workspace_size",
+              "sgla_chunk_bwd", "sgla_chunk_bwd_workspace_size",
               "sgla_chunk_local_cumsum", "sgla_last_error", "sgla_abi_version"):
         assert n in names
 
@@ -73,7 +74,11 @@ class Buffers:
                                 ("v", (B, T, H, V), np.uint16), ("g", (B, T, H), np.float32),
                                 ("gg", (H,), np.float32), ("h0", (N, H, K, V), np.float32),
                                 ("o", (B, T, H, V), np.float32), ("ht", (N, H, K, V), np.float32),
-                                ("ws", (1 << 20,), np.uint8)]:
+                                ("do", (B, T, H, V), np.uint16), ("dq", (B, T, H, K), np.float32),
+                                ("dk", (B, T, H, K), np.float32), ("dv", (B, T, H, V), np.float32),
+                                ("dg", (B, T, H), np.float32), ("dgg", (H,), np.float32),
+                                ("dh0", (N, H, K, V), np.float32),
+                                ("ws", (1 << 22,), np.uint8)]:
             n = int(np.prod(shape)) * np.dtype(dt).itemsize
             raw = rng.integers(0, 255, size=n + 256, dtype=np.uint8)
             off = (-raw.ctypes.data) % 256          # 256-byte aligned view, like device memory
@@ -259,3 +264,53 @@ def test_binding_checks_initial_state_rows(G):
     with pytest.raises(ValueError, match="mutually exclusive"):
         G.recurrent_step(torch.zeros(2, 4, 64), torch.zeros(2, 2, 64), torch.zeros(2, 2, 64),
                          torch.zeros(2, 4), torch.zeros(2, 4, 64, 64), g_gamma=torch.zeros(4))
+
+
+def bwd_call(G, args, b, cu=None, g=True, gg=False, dg=True, dgg=False, ws_bytes=1 << 22, **over):
+    cu_arr = None if cu is None else np.asarray(cu, dtype=np.int64)
+    ptrs = dict(q=b.p("q"), k=b.p("k"), v=b.p("v"), g=b.p("g") if g else None,
+                gg=b.p("gg") if gg else None, h0=b.p("h0"), do=b.p("do"), dht=b.p("ht"),
+                dq=b.p("dq"), dk=b.p("dk"), dv=b.p("dv"), dg=b.p("dg") if dg else None,
+                dgg=b.p("dgg") if dgg else None, dh0=b.p("dh0"), ws=b.p("ws"))
+    ptrs.update(over)
+    st = G.lib.sgla_chunk_bwd(
+        ctypes.byref(args), ptrs["q"], ptrs["k"], ptrs["v"], ptrs["g"], ptrs["gg"], ptrs["h0"],
+        None if cu_arr is None else ctypes.c_void_p(cu_arr.ctypes.data), ptrs["do"], ptrs["dht"],
+        ptrs["dq"], ptrs["dk"], ptrs["dv"], ptrs["dg"], ptrs["dgg"], ptrs["dh0"], ptrs["ws"],
+        ws_bytes, None)
+    return st, G.lib.sgla_last_error().decode()
+
+
+BWD_CASES = [
+    ("K=256", dict(K=256), {}, UNSUPPORTED, "K in"),
+    ("V=48", dict(V=48), {}, UNSUPPORTED, "V a multiple"),
+    ("grouped kv heads", dict(H=2, Hkv=1), {}, UNSUPPORTED, "multi-head"),
+    ("fp16", dict(qkv=3), {}, DTYPE, "qkv_dtype"),
+    ("both gates", {}, dict(gg=True), INVALID, "mutually exclusive"),
+    ("g without dg", {}, dict(dg=False), INVALID, "dg is NULL"),
+    ("g_gamma without dg_gamma", {}, dict(g=False, gg=True), INVALID, "dg_gamma is NULL"),
+    ("NULL dout", {}, dict(do=None), INVALID, "non-NULL"),
+    ("chunk 32", dict(chunk=32), {}, UNSUPPORTED, "chunk_size"),
+    ("cu not ending at T", dict(N=2), dict(cu=[0, 64, 100]), SHAPE, "equal T"),
+    ("workspace small", dict(N=2), dict(cu=[0, 64, 128], ws_bytes=64), WORKSPACE, "workspace"),
+    ("nan scale", dict(scale=float("nan")), {}, INVALID, "scale"),
+]
+
+
+@pytest.mark.parametrize("desc,aover,cover,status,frag", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_chunk_bwd_rejects_without_writing(G, desc, aover, cover, status, frag):
+    b = Buffers()
+    args = mkargs(G, **aover)
+    st, msg = bwd_call(G, args, b, **cover)
+    assert st == status, (st, msg)
+    assert frag in msg, msg
+    assert b.unchanged()
+
+
+def test_chunk_bwd_workspace_size(G):
+    """Two fp32 K x V records per (chunk, head) plus 4 bytes per (chunk, head)."""
+    a = mkargs(G, B=2, T=130, H=3, K=64, V=96)
+    n = G.lib.sgla_chunk_bwd_workspace_size(ctypes.byref(a), None)
+    tasks = 2 * 3 * 3
+    rec = tasks * 64 * 96 * 4
+    assert n == 2 * rec + ((tasks * 4 + 255) // 256) * 256

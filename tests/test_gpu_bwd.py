@@ -1,0 +1,144 @@
+"""GPU parity of the backward (sgla_chunk_bwd) against the fp64 oracle backward.
+
+Gradients of L = <do, o> + <dht, final_state> with respect to q, k, v, the
+gates (dg per token, or dg_gamma per head) and the initial state (page
+"flash-linear-attention 中的 Simple GLA", section 五: dq, dk, dv, dg and dh0
+are the gradients its tests compare).  The bar, per gradient tensor, is the
+forward's: max |gpu - oracle| / RMS(oracle) <= 2e-2 for bf16 inputs and 1e-4
+for float32 inputs.  Small cases compare every element; the full-size packed
+workload is compared on a sample of (sequence, head) units that the oracle
+differentiates one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gla_workloads import CHUNK_CONFIGS, ChunkWorkload, make_backward_inputs, make_chunk_inputs
+from gpu_common import DEV, TOL_BF16, TOL_F32, device_inputs, err_ratio, to_dev
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+if torch.cuda.is_available():
+    import gated_linear_attention_amd as sgla
+else:  # pragma: no cover - collected on CPU-only hosts, never run
+    sgla = None
+
+GRADS = ("dq", "dk", "dv", "dg", "dg_gamma", "dh0")
+
+
+def small(name, **kw):
+    base = dict(B=2, T=150, H=2, K=64, V=64, dtype="bf16", gate="g", seed=31)
+    base.update(kw)
+    return ChunkWorkload(name, **base)
+
+
+def run_bwd(inp, bi):
+    d = device_inputs(inp)
+    dt = d["q"].dtype
+    out = sgla.chunk_bwd(d["q"], d["k"], d["v"], to_dev(bi["do"], dt), g=d["g"],
+                         g_gamma=d["g_gamma"], scale=inp["scale"], initial_state=d["initial_state"],
+                         dht=to_dev(bi["dht"], torch.float32), cu_seqlens=inp["cu_seqlens"],
+                         chunk_size=inp["chunk_size"])
+    torch.cuda.synchronize()
+    return {k: (None if v is None else v.cpu().numpy()) for k, v in out.items()}
+
+
+def oracle_bwd(inp, bi, **kw):
+    return oracle.bwd(inp["q"], inp["k"], inp["v"], bi["do"], g=inp["g"], g_gamma=inp["g_gamma"],
+                      scale=inp["scale"], initial_state=inp["initial_state"], dht=bi["dht"],
+                      cu_seqlens=inp["cu_seqlens"], **kw)
+
+
+def compare(got, ref, tol, label=""):
+    errs = {}
+    for name in GRADS:
+        if ref[name] is None:
+            assert got[name] is None, name
+            continue
+        assert np.all(np.isfinite(got[name])), name
+        errs[name] = err_ratio(got[name], ref[name])
+    print(f"[bwd {label}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if v > tol}
+    assert not bad, f"max err / RMS above {tol}: {bad}"
+
+
+SMALL = [
+    small("k64_v64_g"),
+    small("k128_v128_h0", K=128, V=128, T=131, initial_state=True),
+    small("k16_v32", K=16, V=32, T=97),
+    small("k32_v96_gamma", K=32, V=96, T=200, gate="gamma", normalize_k=True),
+    small("k128_v64_gamma_h0", K=128, V=64, T=70, gate="gamma", initial_state=True, H=3),
+    small("k64_no_gate", K=64, V=64, T=129, gate="none"),
+    small("strong_gate", K=64, V=32, T=150, gate_normalizer=0.1, scale=0.1),
+    small("t1", T=1, initial_state=True),
+    small("t64", T=64),
+    small("t65", T=65, initial_state=True),
+    small("empty_T0", T=0, initial_state=True),
+    small("varlen", B=1, T=0, H=2, K=64, V=64, fixed_lengths=(15, 85, 0, 1, 200, 64),
+          initial_state=True),
+    small("varlen_k128_gamma", B=1, T=0, H=2, K=128, V=128, fixed_lengths=(70, 130, 5),
+          gate="gamma", initial_state=True),
+    small("f32_k32_v64", dtype="f32", K=32, V=64, T=150, initial_state=True),
+    small("f32_k128_varlen", dtype="f32", B=1, T=0, K=128, V=32, fixed_lengths=(15, 85, 200),
+          initial_state=True),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+@pytest.mark.parametrize("with_dht", [True, False], ids=["dht", "no_dht"])
+def test_bwd_small(w, with_dht):
+    inp = make_chunk_inputs(w)
+    bi = make_backward_inputs(inp, seed=w.seed + 1, final_state_grad=with_dht)
+    got = run_bwd(inp, bi)
+    ref = oracle_bwd(inp, bi)
+    compare(got, ref, TOL_BF16 if inp["dtype"] == "bf16" else TOL_F32, w.name)
+
+
+def test_bwd_deterministic():
+    inp = make_chunk_inputs(small("det", B=1, T=0, K=128, V=128, fixed_lengths=(300, 77),
+                                  gate="gamma", initial_state=True))
+    bi = make_backward_inputs(inp, seed=5)
+    a, b = run_bwd(inp, bi), run_bwd(inp, bi)
+    for name in GRADS:
+        if a[name] is not None:
+            assert np.array_equal(a[name], b[name]), name
+
+
+def test_bwd_named_workload_sampled():
+    """The packed workload (8 sequences of 64..4096 tokens, 16 heads, K = V =
+    128, bf16, g, h0) in the full launch; the oracle differentiates 6 sampled
+    (sequence, head) units, each as its own one-sequence, one-head problem."""
+    w = CHUNK_CONFIGS["varlen_bf16_k128"]
+    inp = make_chunk_inputs(w)
+    bi = make_backward_inputs(inp, seed=w.seed + 100)
+    got = run_bwd(inp, bi)
+    cu = inp["cu_seqlens"]
+    N, H = inp["N"], inp["H"]
+    lens = np.diff(cu)
+    rng = np.random.default_rng(9)
+    units = {(int(np.argmax(lens)), 0), (int(np.argmin(lens)), H - 1), (N - 1, H // 2)}
+    while len(units) < 6:
+        units.add((int(rng.integers(N)), int(rng.integers(H))))
+    worst = {}
+    for n, h in sorted(units):
+        s, e = int(cu[n]), int(cu[n + 1])
+        sl = lambda x: x[:, s:e, h:h + 1]
+        ref = oracle.bwd(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(bi["do"]), g=sl(inp["g"]),
+                         scale=inp["scale"], initial_state=inp["initial_state"][n:n + 1, h:h + 1],
+                         dht=bi["dht"][n:n + 1, h:h + 1], nthreads=1)
+        pairs = dict(dq=(got["dq"][:, s:e, h:h + 1], ref["dq"]), dk=(got["dk"][:, s:e, h:h + 1], ref["dk"]),
+                     dv=(got["dv"][:, s:e, h:h + 1], ref["dv"]), dg=(got["dg"][:, s:e, h:h + 1], ref["dg"]),
+                     dh0=(got["dh0"][n:n + 1, h:h + 1], ref["dh0"]))
+        for name, (x, r) in pairs.items():
+            worst[name] = max(worst.get(name, 0.0), err_ratio(x, r))
+    print("[bwd varlen_bf16_k128] " + " ".join(f"{k}={v:.2e}" for k, v in worst.items()), flush=True)
+    assert all(v <= TOL_BF16 for v in worst.values()), worst
+
+
+def test_bwd_rejects_grouped_heads():
+    q = torch.zeros(1, 64, 4, 64, dtype=torch.bfloat16, device=DEV)
+    kv = torch.zeros(1, 64, 2, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        sgla.chunk_bwd(q, kv, kv, torch.zeros(1, 64, 4, 64, dtype=torch.bfloat16, device=DEV))
