@@ -24,6 +24,9 @@ The JSON line also carries:
                    MFMA peak;
   decode        -- the in-place decode step on 256 sequences x 32 heads x
                    128 x 128 fp32 state, 64 consecutive steps, HBM GB/s;
+  backward      -- sgla_chunk_bwd on the packed K = V = 128 workload (dq, dk,
+                   dv, dg, dh0), against the fp32 matrix-core peak its kernels
+                   run on;
   cpu_baseline  -- the fp64 CPU oracle timed on the host cores on whole
                    batches of the same workload (a reported baseline only).
 
@@ -45,6 +48,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+F32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA, TFLOP/s
 MALL_BYTES = 256 << 20
 METRIC = "chunked Simple-GLA fwd tokens/s + % bf16 MFMA peak; decode HBM GB/s"
 
@@ -255,6 +259,106 @@ def bench_decode(steps_timed: int, warmup: int, warm_seconds: float):
             "traffic": load_traffic(w.name, "recurrent_step_kernel")}
 
 
+def bwd_algorithmic(inp) -> tuple[float, float]:
+    """(bytes, flops) of one backward call at minimum.
+
+    bytes: q, k, v, do read once, g, h0 and dht read once if given; dq, dk,
+    dv (fp32), dg and dh0 written once.  flops per chunk of L tokens and head:
+    L(L+1)(3K + 2V) for the causal products (A, dA, the intra parts of dq, dk
+    and dv) plus 10 L K V for the dense ones (q.h and state parts of dq, dk,
+    dv, the state-gradient update and the state recomputation)."""
+    B, T, H, K, V, N = inp["B"], inp["T"], inp["H"], inp["K"], inp["V"], inp["N"]
+    esz = 2 if inp["dtype"] == "bf16" else 4
+    tokens = B * T
+    nbytes = tokens * H * (2 * K + 2 * V) * esz + tokens * H * (2 * K + V) * 4
+    if inp["g"] is not None:
+        nbytes += 2 * tokens * H * 4
+    if inp["initial_state"] is not None:
+        nbytes += N * H * K * V * 4
+    nbytes += 2 * N * H * K * V * 4          # dht in, dh0 out
+    if inp["cu_seqlens"] is not None:
+        lens = [int(x) for x in (inp["cu_seqlens"][1:] - inp["cu_seqlens"][:-1])]
+    else:
+        lens = [T] * B
+    flops = 0
+    for L in lens:
+        for s in range(0, L, 64):
+            c = min(64, L - s)
+            flops += c * (c + 1) * (3 * K + 2 * V) + 10 * c * K * V
+    return float(nbytes), float(flops * H)
+
+
+def bench_backward(workload: str, steps: int, warmup: int, warm_seconds: float):
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import gated_linear_attention_amd as sgla
+    from gla_workloads import CHUNK_CONFIGS, make_backward_inputs, make_chunk_inputs
+
+    w = CHUNK_CONFIGS[workload]
+    inp = make_chunk_inputs(w)
+    bi = make_backward_inputs(inp, seed=w.seed + 100)
+    dev = torch.device("cuda:0")
+    qdt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+    B, T, H, K, V, N = inp["B"], inp["T"], inp["H"], inp["K"], inp["V"], inp["N"]
+    t = lambda a, dt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+    q, k, v, do = t(inp["q"], qdt), t(inp["k"], qdt), t(inp["v"], qdt), t(bi["do"], qdt)
+    g, gg = t(inp["g"], torch.float32), t(inp["g_gamma"], torch.float32)
+    h0, dht = t(inp["initial_state"], torch.float32), t(bi["dht"], torch.float32)
+    args = sgla._chunk_args(B, T, H, K, V, N, 64, 1 if inp["dtype"] == "bf16" else 2, 2,
+                            inp["scale"], 0, H)
+    cu = None if inp["cu_seqlens"] is None else torch.as_tensor(inp["cu_seqlens"], dtype=torch.int64)
+    cu_ptr = None if cu is None else ctypes.c_void_p(cu.data_ptr())
+    ws_bytes = sgla.lib.sgla_chunk_bwd_workspace_size(ctypes.byref(args), cu_ptr)
+    f32 = dict(device=dev, dtype=torch.float32)
+    outs = dict(dq=torch.empty((B, T, H, K), **f32), dk=torch.empty((B, T, H, K), **f32),
+                dv=torch.empty((B, T, H, V), **f32),
+                dg=torch.empty((B, T, H), **f32) if g is not None else None,
+                dgg=torch.empty((H,), **f32) if gg is not None else None,
+                dh0=torch.empty((N, H, K, V), **f32))
+    ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    p = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
+    call = (ctypes.byref(args), p(q), p(k), p(v), p(g), p(gg), p(h0), cu_ptr, p(do), p(dht),
+            p(outs["dq"]), p(outs["dk"]), p(outs["dv"]), p(outs["dg"]), p(outs["dgg"]),
+            p(outs["dh0"]), p(ws), ws_bytes)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(_i):
+        st = sgla.lib.sgla_chunk_bwd(*call, sp)
+        if st != 0:
+            raise RuntimeError(f"sgla_chunk_bwd failed: {sgla.lib.sgla_last_error().decode()}")
+
+    warm_device(step, warm_seconds)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    ms = sum(per) / len(per)
+    nbytes, flops = bwd_algorithmic(inp)
+    tf = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": workload, "B": B, "T": T, "H": H, "K": K, "V": V, "num_seqs": N,
+            "kernel": "chunk_bwd_state_kernel+chunk_bwd_grad_kernel",
+            "launches_per_call": 2 + (1 if gg is not None else 0),
+            "ms_per_call_mean": round(ms, 5), "ms_per_call_median": round(per[len(per) // 2], 5),
+            "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "algorithmic_flops_per_call": int(flops), "algorithmic_bytes_per_call": int(nbytes),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": F32_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / F32_MFMA_PEAK_TFLOPS, 4),
+                         "dtype": "f32"},
+            "hbm": {"achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
 def cpu_baseline(inp, min_seconds: float = 10.0):
     """The fp64 CPU oracle on whole batches of the timed workload, repeated
     until at least ``min_seconds`` of wall time (a bounded sample)."""
@@ -313,6 +417,9 @@ def main():
                     help="time grouped-kv-head workloads as plain multi-head input (k and v "
                          "repeated per query head), for comparison")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-workload", default="varlen_bf16_k128",
+                    help="workload of the backward timing (K <= 128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device-to-device copy of known size (the reference "
@@ -381,6 +488,8 @@ def main():
     }
     if not a.no_decode:
         out["decode"] = bench_decode(64, a.warmup, a.warm_seconds)
+    if not a.no_backward:
+        out["backward"] = bench_backward(a.backward_workload, 20, a.warmup, a.warm_seconds)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)

@@ -49,32 +49,81 @@ constexpr int LDT = VT + 4;       // row stride of 32-column tiles (floats)
 constexpr int LDA = C + 4;        // row stride of the 64 x 64 A / dA tile
 constexpr float kRcpLn2f = 1.44269504088896341f;
 
-// Causal 16 x 16 tiles (c, j), j <= c, packed 4 bits each (c | j << 2); wave
-// w takes entries w, w + 4, w + 8.
-constexpr uint64_t kTiles = 0xFB73A62510ull;
-
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-__device__ __forceinline__ f32x4 load4(const __bf16* p) {
-  const uint2 u = *reinterpret_cast<const uint2*>(p);
+
+// Four consecutive input elements as loaded (bf16 kept packed until they are
+// widened on their way into LDS, which halves the registers a prefetch holds).
+template <typename T> struct Raw4;
+template <> struct Raw4<float> { typedef f32x4 type; };
+template <> struct Raw4<__bf16> { typedef uint2 type; };
+__device__ __forceinline__ f32x4 raw_load(const float* p) { return load4(p); }
+__device__ __forceinline__ uint2 raw_load(const __bf16* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ void raw_zero(f32x4& x) { x = f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ void raw_zero(uint2& x) { x = make_uint2(0u, 0u); }
+__device__ __forceinline__ f32x4 widen(f32x4 x) { return x; }
+__device__ __forceinline__ f32x4 widen(uint2 u) {
   return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
 }
 
-// rows [0, 64) x cols [0, W) of a token-major input (row stride RS elements)
-// into LDS (row stride LD floats); rows at or past `rows` read as zero.
-template <int W, typename T>
-__device__ __forceinline__ void stage_rows(float* dst, int LD, const T* src, int64_t RS, int rows) {
-  for (int i = threadIdx.x; i < C * (W / 4); i += NT) {
-    const int c = i / (W / 4), c4 = i % (W / 4);
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (c < rows) x = load4(src + c * RS + 4 * c4);
-    *reinterpret_cast<f32x4*>(dst + c * LD + 4 * c4) = x;
+// Staging of rows [0, 64) x cols [0, W) of a token-major input (row stride
+// RS elements) into LDS as fp32 (row stride LD floats) by NTH threads; rows
+// at or past `rows` read as zero.  Split into a register load and an LDS
+// store so that every load of a stage is in flight before the first store
+// (the stores go through a generic pointer the compiler cannot separate from
+// the loads), and so that a stage can be loaded ahead of its use.
+template <int W, int NTH, typename T>
+struct RowTile {
+  static constexpr int P = C * (W / 4);           // 4-element pieces
+  static constexpr int N = (P + NTH - 1) / NTH;   // per thread
+  typename Raw4<T>::type x[N];
+  __device__ __forceinline__ void load(const T* src, int64_t RS, int rows) {
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int i = threadIdx.x + u * NTH;
+      const int c = i / (W / 4), c4 = i % (W / 4);
+      raw_zero(x[u]);
+      if ((P % NTH == 0 || i < P) && c < rows) x[u] = raw_load(src + c * RS + 4 * c4);
+    }
   }
-}
+  __device__ __forceinline__ void store(float* dst, int LD) const {
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int i = threadIdx.x + u * NTH;
+      if (P % NTH == 0 || i < P)
+        *reinterpret_cast<f32x4*>(dst + (i / (W / 4)) * LD + 4 * (i % (W / 4))) = widen(x[u]);
+    }
+  }
+};
+
+// K rows x 32 columns of a [K][V] fp32 record, columns [c0, c0 + 32), by NTH
+// threads.
+template <int K, int NTH>
+struct RecTile {
+  static constexpr int P = K * (VT / 4);          // 16-byte pieces
+  static constexpr int N = (P + NTH - 1) / NTH;   // per thread
+  f32x4 x[N];
+  __device__ __forceinline__ void load(const float* src, int64_t V, int64_t c0) {
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int i = threadIdx.x + u * NTH;
+      x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (P % NTH == 0 || i < P) x[u] = load4(src + (i / (VT / 4)) * V + c0 + 4 * (i % (VT / 4)));
+    }
+  }
+  __device__ __forceinline__ void store(float* dst) const {
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int i = threadIdx.x + u * NTH;
+      if (P % NTH == 0 || i < P)
+        *reinterpret_cast<f32x4*>(dst + (i / (VT / 4)) * LDT + 4 * (i % (VT / 4))) = x[u];
+    }
+  }
+};
 
 // Where a (sequence, head) unit's tokens and chunk records are.
 struct SeqInfo {
@@ -109,10 +158,10 @@ __device__ __forceinline__ float chunk_gate(const float* g, const float* g_gamma
 }
 
 // ---------------------------------------------------------------------------
-// State pass.  Workgroups [0, half) run the forward recurrence of one
-// (sequence, head, 32-column V tile) and store the state entering every
-// chunk; workgroups [half, 2 half) run the reverse recurrence of the state
-// gradient and store the gradient of the state leaving every chunk, then dh0.
+// State pass.  For each (sequence, head, 32-column V tile) one workgroup runs
+// the forward recurrence and stores the state entering every chunk, and
+// another runs the reverse recurrence of the state gradient and stores the
+// gradient of the state leaving every chunk, then dh0.
 // The K x 32 (gradient) state stays in MFMA accumulators: wave w owns 16 x 16
 // tiles st = w + 4 s (rows 16 (st / 2), columns 16 (st % 2)).
 // ---------------------------------------------------------------------------
@@ -123,8 +172,7 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                        const float* __restrict__ g, const float* __restrict__ g_gamma,
                        const float* __restrict__ h0, const float* __restrict__ dht,
                        float* __restrict__ dh0, float scale, int32_t H, int32_t V, SeqLayout seqs,
-                       int32_t chunks_per_row, float* __restrict__ hbuf, float* __restrict__ dhbuf,
-                       int32_t half) {
+                       int32_t chunks_per_row, float* __restrict__ hbuf, float* __restrict__ dhbuf) {
   constexpr int LDX = K + 4;
   constexpr int NST = (K / 16) * 2;
   constexpr int SPW = (NST + 3) / 4;
@@ -133,14 +181,17 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   __shared__ float sW[C];           // 2^(b_last - b) (forward) or scale 2^b (reverse)
   __shared__ float sDall;
 
-  const bool rev = (int)blockIdx.x >= half;
-  const int bid = rev ? (int)blockIdx.x - half : (int)blockIdx.x;
+  // workgroups 2 u and 2 u + 1 run unit u's forward and reverse passes, so
+  // the longest units start both at once
+  const bool rev = (blockIdx.x & 1) != 0;
+  const int bid = (int)(blockIdx.x >> 1);
   const UnitMap um = map_unit(bid, V / VT, H, 1, seqs.num_seqs);
   if (!um.valid) return;
   const int hd = um.hd, vt = um.vt;
   const SeqInfo si = seq_info(seqs, um.rank, chunks_per_row);
   const int nchunks = (si.len + C - 1) / C;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int64_t KV = (int64_t)K * V;
   const int64_t ucol = vt * VT;
 
@@ -152,7 +203,7 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     for (int s = 0; s < SPW; ++s) {
       const int st = w + 4 * s;
       hs[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (st < NST && iu != nullptr) {
+      if ((NST % 4 == 0 || st < NST) && iu != nullptr) {
         const int kt = st >> 1, ctl = st & 1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) hs[s][i] = iu[(int64_t)(16 * kt + 4 * g4 + i) * V + 16 * ctl + r];
@@ -160,9 +211,21 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     }
   }
 
-  for (int it = 0; it < nchunks; ++it) {
+  // chunk m's rows and gate are loaded into registers one iteration ahead
+  RowTile<K, NT, TIn> xt;
+  RowTile<VT, NT, TIn> yt;
+  float gx = 0.f;
+  auto load_chunk = [&](int it) {
     const int m = rev ? nchunks - 1 - it : it;
     const int64_t t0 = si.bos + (int64_t)m * C;
+    const int cl = min(C, si.len - m * C);
+    xt.load((rev ? q : k) + (t0 * H + hd) * K, (int64_t)H * K, cl);
+    yt.load((rev ? dout : v) + (t0 * H + hd) * V + ucol, (int64_t)H * V, cl);
+    if (w == 0 && g != nullptr) gx = lane < cl ? g[(t0 + lane) * H + hd] : 0.f;
+  };
+  if (nchunks > 0) load_chunk(0);
+  for (int it = 0; it < nchunks; ++it) {
+    const int m = rev ? nchunks - 1 - it : it;
     const int cl = min(C, si.len - m * C);
     // record: forward -> the state entering chunk m; reverse -> the gradient
     // of the state leaving chunk m
@@ -170,39 +233,40 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
       const int st = w + 4 * s;
-      if (st < NST) {
+      if (NST % 4 == 0 || st < NST) {
         const int kt = st >> 1, ctl = st & 1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) rec[(int64_t)(16 * kt + 4 * g4 + i) * V + 16 * ctl + r] = hs[s][i];
       }
     }
-    if (rev) {
-      stage_rows<K>(sX, LDX, q + (t0 * H + hd) * K, (int64_t)H * K, cl);
-      stage_rows<VT>(sY, LDT, dout + (t0 * H + hd) * V + ucol, (int64_t)H * V, cl);
-    } else {
-      stage_rows<K>(sX, LDX, k + (t0 * H + hd) * K, (int64_t)H * K, cl);
-      stage_rows<VT>(sY, LDT, v + (t0 * H + hd) * V + ucol, (int64_t)H * V, cl);
-    }
+    xt.store(sX, LDX);
+    yt.store(sY, LDT);
     if (w == 0) {
-      const float b = chunk_gate(g, g_gamma, H, hd, t0, cl);
+      float b;
+      if (g != nullptr) b = wave_cumsum_log2(gx);
+      else if (g_gamma != nullptr) b = (float)min(lane + 1, cl) * (g_gamma[hd] * kRcpLn2f);
+      else b = 0.f;
       const float blast = __shfl(b, C - 1, 64);
       sW[lane] = rev ? exp2f(b) * scale : exp2f(blast - b);
       if (lane == 0) sDall = exp2f(blast);
     }
     __syncthreads();
+    if (it + 1 < nchunks) load_chunk(it + 1);
     const float dall = sDall;
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-      const int st = w + 4 * s;
-      if (st >= NST) continue;
-      const int kt = st >> 1, ctl = st & 1;
-      f32x4 acc = hs[s] * dall;
-#pragma unroll 8
-      for (int cs = 0; cs < C / 4; ++cs) {
-        const int c = 4 * cs + g4;
-        acc = mfma4(sX[c * LDX + 16 * kt + r] * sW[c], sY[c * LDT + 16 * ctl + r], acc);
+    for (int s = 0; s < SPW; ++s) hs[s] *= dall;
+    // the wave's tiles are independent accumulation chains: interleave them
+#pragma unroll 4
+    for (int cs = 0; cs < C / 4; ++cs) {
+      const int c = 4 * cs + g4;
+      const float wc = sW[c];
+#pragma unroll
+      for (int s = 0; s < SPW; ++s) {
+        const int st = w + 4 * s;
+        if (NST % 4 != 0 && st >= NST) continue;
+        const int kt = st >> 1, ctl = st & 1;
+        hs[s] = mfma4(sX[c * LDX + 16 * kt + r] * wc, sY[c * LDT + 16 * ctl + r], hs[s]);
       }
-      hs[s] = acc;
     }
     __syncthreads();
   }
@@ -211,7 +275,7 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
       const int st = w + 4 * s;
-      if (st < NST) {
+      if (NST % 4 == 0 || st < NST) {
         const int kt = st >> 1, ctl = st & 1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) du[(int64_t)(16 * kt + 4 * g4 + i) * V + 16 * ctl + r] = hs[s][i];
@@ -221,11 +285,17 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
 }
 
 // ---------------------------------------------------------------------------
-// Per-(chunk, head) gradients.  Wave w owns rows [16 w, +16) of dQ and dK (all
-// K columns) and walks V in 32-column slices; dA and A live in LDS.
+// Per-(chunk, head) gradients, 8 waves (two per SIMD).  Wave w works on row
+// tile rw = w % 4 (rows [16 rw, +16) of A, dA, dQ, dK, dV) and column half
+// kh = w / 4: A and dA column tiles {2 kh, 2 kh + 1}, dQ / dK column tiles
+// [kh NKT / 2, +NKT / 2), dV columns [16 kh, +16) of each 32-column V slice.
+// V is walked in 32-column slices, each loaded one slice ahead; A, then dA,
+// live in LDS.
 // ---------------------------------------------------------------------------
+constexpr int NTG = 512;          // grad-kernel threads (8 waves)
+
 template <int K, typename TIn>
-__global__ void __launch_bounds__(NT)
+__global__ void __launch_bounds__(NTG)
 chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                       const TIn* __restrict__ v, const TIn* __restrict__ dout,
                       const float* __restrict__ g, const float* __restrict__ g_gamma, float scale,
@@ -234,7 +304,8 @@ chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                       float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
                       float* __restrict__ dg, float* __restrict__ gpart) {
   constexpr int LDQ = K + 4;
-  constexpr int NKT = K / 16;       // 16-column tiles of dQ / dK per wave
+  constexpr int NKT = K / 16;                   // 16-column tiles of dQ / dK
+  constexpr int NKH = NKT >= 2 ? NKT / 2 : 1;   // per wave
   __shared__ float sQ[C * LDQ];
   __shared__ float sK[C * LDQ];
   __shared__ float sA[C * LDA];     // A during the slices, then dA
@@ -243,8 +314,8 @@ chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   __shared__ float sH[K * LDT];
   __shared__ float sdH[K * LDT];
   __shared__ float sb[C], ssc[C], sdv[C];
-  __shared__ float sR[C], sKs[C];
-  __shared__ float sFrob[4];
+  __shared__ float sR[2][C], sKs[2][C];
+  __shared__ float sFrob[8];
 
   const int gc = blockIdx.x;
   const int hd = blockIdx.y;
@@ -260,14 +331,23 @@ chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     t0 = (int64_t)row * seqs.T + (int64_t)m * C;
     cl = min(C, seqs.T - m * C);
   }
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+  const int rw = w & 3, kh = w >> 2;
+  const bool has_k = NKT >= 2 || kh == 0;       // K = 16: one column tile, taken by kh = 0
+  const int kt0 = kh * NKH;
   const int64_t RSK = (int64_t)H * K, RSV = (int64_t)H * V;
   const int64_t KV = (int64_t)K * V;
   const float* hu = hbuf + ((int64_t)gc * H + hd) * KV;
   const float* dhu = dhbuf + ((int64_t)gc * H + hd) * KV;
 
-  stage_rows<K>(sQ, LDQ, q + (t0 * H + hd) * K, RSK, cl);
-  stage_rows<K>(sK, LDQ, k + (t0 * H + hd) * K, RSK, cl);
+  {
+    RowTile<K, NTG, TIn> qt, kt;
+    qt.load(q + (t0 * H + hd) * K, RSK, cl);
+    kt.load(k + (t0 * H + hd) * K, RSK, cl);
+    qt.store(sQ, LDQ);
+    kt.store(sK, LDQ);
+  }
   if (w == 0) {
     const float b = chunk_gate(g, g_gamma, H, hd, t0, cl);
     const float blast = __shfl(b, C - 1, 64);
@@ -275,89 +355,88 @@ chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     ssc[lane] = exp2f(b) * scale;
     sdv[lane] = exp2f(blast - b);
   }
-  // upper-triangle tiles of A / dA are never written: zero them once
-  for (int i = tid; i < 6 * 256; i += NT) {
-    const int tt = i >> 8, e = i & 255;
-    const int ctile = tt < 3 ? 0 : (tt < 5 ? 1 : 2);
-    const int jtile = tt < 3 ? tt + 1 : (tt < 5 ? tt - 1 : 3);
-    sA[(16 * ctile + (e >> 4)) * LDA + 16 * jtile + (e & 15)] = 0.f;
-  }
+  // slice tiles, loaded one slice ahead of their use
+  RowTile<VT, NTG, TIn> vtile, otile;
+  RecTile<K, NTG> htile, dhtile;
+  auto load_slice = [&](int vs) {
+    vtile.load(v + (t0 * H + hd) * V + vs * VT, RSV, cl);
+    otile.load(dout + (t0 * H + hd) * V + vs * VT, RSV, cl);
+    htile.load(hu, V, (int64_t)vs * VT);
+    dhtile.load(dhu, V, (int64_t)vs * VT);
+  };
+  load_slice(0);
   __syncthreads();
 
-  // ---- A = scale (Q K^T) (.) M, causal tiles --------------------------------
+  // ---- A = scale (Q K^T) (.) M: row tile rw against column tiles 2 kh, 2 kh + 1
+  //      (upper tiles come out masked to zero) ------------------------------
+  {
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 4
+    for (int ks = 0; ks < K / 4; ++ks) {
+      const float a = sQ[(16 * rw + r) * LDQ + 4 * ks + g4];
 #pragma unroll
-  for (int t = 0; t < 3; ++t) {
-    const int ti = w + 4 * t;
-    if (ti >= 10) continue;
-    const int ctile = (int)(kTiles >> (4 * ti)) & 3, jtile = (int)(kTiles >> (4 * ti + 2)) & 3;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int ks = 0; ks < K / 4; ++ks)
-      acc = mfma4(sQ[(16 * ctile + r) * LDQ + 4 * ks + g4], sK[(16 * jtile + r) * LDQ + 4 * ks + g4], acc);
-    const int j = 16 * jtile + r;
+      for (int t = 0; t < 2; ++t) acc[t] = mfma4(a, sK[(16 * (2 * kh + t) + r) * LDQ + 4 * ks + g4], acc[t]);
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = 16 * ctile + 4 * g4 + i;
-      sA[c * LDA + j] = j <= c ? acc[i] * exp2f(sb[c] - sb[j]) * scale : 0.f;
+    for (int t = 0; t < 2; ++t) {
+      const int j = 16 * (2 * kh + t) + r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * rw + 4 * g4 + i;
+        sA[c * LDA + j] = j <= c ? acc[t][i] * exp2f(sb[c] - sb[j]) * scale : 0.f;
+      }
     }
   }
 
   // ---- walk V in 32-column slices ---------------------------------------------
-  f32x4 dAacc[3];
-  f32x4 dQi[NKT], dKs[NKT];
+  f32x4 dAacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  f32x4 dQi[NKH], dKs[NKH];
 #pragma unroll
-  for (int t = 0; t < 3; ++t) dAacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int t = 0; t < NKT; ++t) {
+  for (int t = 0; t < NKH; ++t) {
     dQi[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     dKs[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float frob = 0.f;
   for (int vs = 0; vs < V / VT; ++vs) {
-    __syncthreads();   // previous slice's reads done (first pass: A and gates published)
-    stage_rows<VT>(sV, LDT, v + (t0 * H + hd) * V + vs * VT, RSV, cl);
-    stage_rows<VT>(sdO, LDT, dout + (t0 * H + hd) * V + vs * VT, RSV, cl);
-    for (int i = tid; i < K * (VT / 4); i += NT) {
-      const int row = i / (VT / 4), c4 = i % (VT / 4);
-      const f32x4 x = load4(hu + (int64_t)row * V + vs * VT + 4 * c4);
-      const f32x4 y = load4(dhu + (int64_t)row * V + vs * VT + 4 * c4);
-      *reinterpret_cast<f32x4*>(sH + row * LDT + 4 * c4) = x;
-      *reinterpret_cast<f32x4*>(sdH + row * LDT + 4 * c4) = y;
+    __syncthreads();   // previous slice's reads done (first pass: A published)
+    vtile.store(sV, LDT);
+    otile.store(sdO, LDT);
+    htile.store(sH);
+    dhtile.store(sdH);
+#pragma unroll
+    for (int u = 0; u < RecTile<K, NTG>::N; ++u) {
+      const f32x4 x = htile.x[u], y = dhtile.x[u];
       frob += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
     }
+    if (vs + 1 < V / VT) load_slice(vs + 1);
     __syncthreads();
-    // dA += dO V^T over this slice (causal tiles)
+    // dA += dO V^T, dQ_inter += dO h^T, dK_state += V dH^T over this slice
 #pragma unroll
-    for (int t = 0; t < 3; ++t) {
-      const int ti = w + 4 * t;
-      if (ti >= 10) continue;
-      const int ctile = (int)(kTiles >> (4 * ti)) & 3, jtile = (int)(kTiles >> (4 * ti + 2)) & 3;
+    for (int s = 0; s < VT / 4; ++s) {
+      const float ao = sdO[(16 * rw + r) * LDT + 4 * s + g4];
+      const float av = sV[(16 * rw + r) * LDT + 4 * s + g4];
 #pragma unroll
-      for (int s = 0; s < VT / 4; ++s)
-        dAacc[t] = mfma4(sdO[(16 * ctile + r) * LDT + 4 * s + g4], sV[(16 * jtile + r) * LDT + 4 * s + g4], dAacc[t]);
-    }
-    // dQ_inter += dO h^T and dK_state += V dH^T: rows of wave w
+      for (int t = 0; t < 2; ++t) dAacc[t] = mfma4(ao, sV[(16 * (2 * kh + t) + r) * LDT + 4 * s + g4], dAacc[t]);
+      if (has_k) {
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-#pragma unroll
-      for (int s = 0; s < VT / 4; ++s) {
-        dQi[kt] = mfma4(sdO[(16 * w + r) * LDT + 4 * s + g4], sH[(16 * kt + r) * LDT + 4 * s + g4], dQi[kt]);
-        dKs[kt] = mfma4(sV[(16 * w + r) * LDT + 4 * s + g4], sdH[(16 * kt + r) * LDT + 4 * s + g4], dKs[kt]);
+        for (int t = 0; t < NKH; ++t) {
+          dQi[t] = mfma4(ao, sH[(16 * (kt0 + t) + r) * LDT + 4 * s + g4], dQi[t]);
+          dKs[t] = mfma4(av, sdH[(16 * (kt0 + t) + r) * LDT + 4 * s + g4], dKs[t]);
+        }
       }
     }
-    // dV slice: rows [16 w, +16), columns 16 cv + r of the slice
-#pragma unroll
-    for (int cv = 0; cv < 2; ++cv) {
-      f32x4 intra = {0.f, 0.f, 0.f, 0.f}, st = {0.f, 0.f, 0.f, 0.f};
-      for (int cs = 4 * w; cs < C / 4; ++cs)   // A[c][j] = 0 for c < j
-        intra = mfma4(sA[(4 * cs + g4) * LDA + 16 * w + r], sdO[(4 * cs + g4) * LDT + 16 * cv + r], intra);
+    // dV: rows [16 rw, +16), columns [16 kh, +16) of the slice
+    {
+      f32x4 in = {0.f, 0.f, 0.f, 0.f}, st = in;
+      for (int cs = 4 * rw; cs < C / 4; ++cs)   // A[c][j] = 0 for c < j
+        in = mfma4(sA[(4 * cs + g4) * LDA + 16 * rw + r], sdO[(4 * cs + g4) * LDT + 16 * kh + r], in);
 #pragma unroll 8
       for (int ks = 0; ks < K / 4; ++ks)
-        st = mfma4(sK[(16 * w + r) * LDQ + 4 * ks + g4], sdH[(4 * ks + g4) * LDT + 16 * cv + r], st);
+        st = mfma4(sK[(16 * rw + r) * LDQ + 4 * ks + g4], sdH[(4 * ks + g4) * LDT + 16 * kh + r], st);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = 16 * w + 4 * g4 + i;
-        if (j < cl) dv[((t0 + j) * H + hd) * (int64_t)V + vs * VT + 16 * cv + r] = intra[i] + sdv[j] * st[i];
+        const int j = 16 * rw + 4 * g4 + i;
+        if (j < cl) dv[((t0 + j) * H + hd) * (int64_t)V + vs * VT + 16 * kh + r] = in[i] + sdv[j] * st[i];
       }
     }
   }
@@ -365,14 +444,11 @@ chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
 
   // ---- dA masked and scaled, into the A buffer ------------------------------
 #pragma unroll
-  for (int t = 0; t < 3; ++t) {
-    const int ti = w + 4 * t;
-    if (ti >= 10) continue;
-    const int ctile = (int)(kTiles >> (4 * ti)) & 3, jtile = (int)(kTiles >> (4 * ti + 2)) & 3;
-    const int j = 16 * jtile + r;
+  for (int t = 0; t < 2; ++t) {
+    const int j = 16 * (2 * kh + t) + r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = 16 * ctile + 4 * g4 + i;
+      const int c = 16 * rw + 4 * g4 + i;
       sA[c * LDA + j] = j <= c ? dAacc[t][i] * exp2f(sb[c] - sb[j]) * scale : 0.f;
     }
   }
@@ -384,29 +460,44 @@ chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
 
   // ---- dQ = diag(sc) dQ_inter + dA K;  dK = dA^T Q + diag(dv) dK_state --------
   float rq[4] = {0.f, 0.f, 0.f, 0.f}, rk[4] = {0.f, 0.f, 0.f, 0.f}, ks4[4] = {0.f, 0.f, 0.f, 0.f};
+  if (has_k) {
+    constexpr int KP = NKH >= 2 ? 2 : 1;   // column tiles per pass (independent chains)
 #pragma unroll
-  for (int kt = 0; kt < NKT; ++kt) {
-    f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
-    for (int js = 0; js < 4 * (w + 1); ++js)   // dA[c][j] = 0 for j > c
-      aq = mfma4(sA[(16 * w + r) * LDA + 4 * js + g4], sK[(4 * js + g4) * LDQ + 16 * kt + r], aq);
-    for (int cs = 4 * w; cs < C / 4; ++cs)
-      ak = mfma4(sA[(4 * cs + g4) * LDA + 16 * w + r], sQ[(4 * cs + g4) * LDQ + 16 * kt + r], ak);
+    for (int k0 = 0; k0 < NKH; k0 += KP) {
+      f32x4 aq[KP], ak[KP];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = 16 * w + 4 * g4 + i;
-      const int col = 16 * kt + r;
-      const float xq = ssc[c] * dQi[kt][i] + aq[i];
-      const float xk = ak[i] + sdv[c] * dKs[kt][i];
-      rq[i] += sQ[c * LDQ + col] * xq;
-      rk[i] += sK[c * LDQ + col] * xk;
-      ks4[i] += sK[c * LDQ + col] * dKs[kt][i];
-      if (c < cl) {
-        dq[((t0 + c) * H + hd) * (int64_t)K + col] = xq;
-        dk[((t0 + c) * H + hd) * (int64_t)K + col] = xk;
+      for (int u = 0; u < KP; ++u) aq[u] = ak[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int js = 0; js < 4 * (rw + 1); ++js) {   // dA[c][j] = 0 for j > c
+        const float a = sA[(16 * rw + r) * LDA + 4 * js + g4];
+#pragma unroll
+        for (int u = 0; u < KP; ++u) aq[u] = mfma4(a, sK[(4 * js + g4) * LDQ + 16 * (kt0 + k0 + u) + r], aq[u]);
+      }
+      for (int cs = 4 * rw; cs < C / 4; ++cs) {
+        const float a = sA[(4 * cs + g4) * LDA + 16 * rw + r];
+#pragma unroll
+        for (int u = 0; u < KP; ++u) ak[u] = mfma4(a, sQ[(4 * cs + g4) * LDQ + 16 * (kt0 + k0 + u) + r], ak[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < KP; ++u) {
+        const int t = k0 + u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = 16 * rw + 4 * g4 + i;
+          const int col = 16 * (kt0 + t) + r;
+          const float xq = ssc[c] * dQi[t][i] + aq[u][i];
+          const float xk = ak[u][i] + sdv[c] * dKs[t][i];
+          rq[i] += sQ[c * LDQ + col] * xq;
+          rk[i] += sK[c * LDQ + col] * xk;
+          ks4[i] += sK[c * LDQ + col] * dKs[t][i];
+          if (c < cl) {
+            dq[((t0 + c) * H + hd) * (int64_t)K + col] = xq;
+            dk[((t0 + c) * H + hd) * (int64_t)K + col] = xk;
+          }
+        }
       }
     }
   }
-  // row sums over the 16 lanes of a column group
+  // row sums over the 16 lanes of a column group, one partial per column half
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -416,21 +507,23 @@ chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
       ks4[i] += __shfl_xor(ks4[i], d, 64);
     }
     if (r == 0) {
-      const int c = 16 * w + 4 * g4 + i;
-      sR[c] = rq[i] - rk[i];
-      sKs[c] = sdv[c] * ks4[i];
+      const int c = 16 * rw + 4 * g4 + i;
+      sR[kh][c] = rq[i] - rk[i];
+      sKs[kh][c] = sdv[c] * ks4[i];
     }
   }
   __syncthreads();
 
   // ---- gate gradient: reverse cumulative sum over the chunk ---------------
   if (w == 0) {
-    const float frob_all = sFrob[0] + sFrob[1] + sFrob[2] + sFrob[3];
+    float frob_all = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) frob_all += sFrob[i];
     // the chunk's share of the state it hands on, at its last real token
-    double extra = (double)sKs[lane];
+    double extra = (double)sKs[0][lane] + (double)sKs[1][lane];
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) extra += __shfl_xor(extra, d, 64);
-    double x = lane < cl ? (double)sR[lane] : 0.0;
+    double x = lane < cl ? (double)sR[0][lane] + (double)sR[1][lane] : 0.0;
     if (lane == cl - 1) x += (double)exp2f(sb[C - 1]) * (double)frob_all + extra;
     // reverse inclusive scan: lane c gets x_c + ... + x_63
 #pragma unroll
@@ -473,16 +566,16 @@ hipError_t launch_k(const ChunkBwdParams& p, hipStream_t stream) {
   const TIn* v = static_cast<const TIn*>(p.v);
   const TIn* dout = static_cast<const TIn*>(p.dout);
   if (p.seqs.num_seqs > 0) {
-    const int half = (int)unit_grid(p.seqs.num_seqs, p.H, 1, p.V / VT);
-    hipLaunchKernelGGL((chunk_bwd_state_kernel<K, TIn>), dim3((unsigned)(2 * half)), dim3(NT), 0, stream,
+    const int units = (int)unit_grid(p.seqs.num_seqs, p.H, 1, p.V / VT);
+    hipLaunchKernelGGL((chunk_bwd_state_kernel<K, TIn>), dim3((unsigned)(2 * units)), dim3(NT), 0, stream,
                        q, k, v, dout, p.g, p.g_gamma, p.h0, p.dht, p.dh0, p.scale, p.H, p.V, p.seqs,
-                       per_row, p.hbuf, p.dhbuf, half);
+                       per_row, p.hbuf, p.dhbuf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.seqs.num_chunks > 0) {
     hipLaunchKernelGGL((chunk_bwd_grad_kernel<K, TIn>), dim3((unsigned)p.seqs.num_chunks, (unsigned)p.H),
-                       dim3(NT), 0, stream, q, k, v, dout, p.g, p.g_gamma, p.scale, p.H, p.V, p.seqs,
+                       dim3(NTG), 0, stream, q, k, v, dout, p.g, p.g_gamma, p.scale, p.H, p.V, p.seqs,
                        per_row, p.hbuf, p.dhbuf, p.dq, p.dk, p.dv, p.dg,
                        p.dg_gamma != nullptr ? p.gpart : nullptr);
     hipError_t e = hipGetLastError();
