@@ -91,16 +91,26 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
+def _vk(x, state_v_first):
+    """States given or returned in the [V, K] layout (section 二, state_v_first)
+    are the transposes of the [K, V] states the C oracle works on."""
+    if x is None or not state_v_first:
+        return x
+    return np.ascontiguousarray(np.swapaxes(np.asarray(x, dtype=np.float64), -1, -2))
+
+
 def fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None, cu_seqlens=None,
-        output_final_state=True, nthreads=None, lib=None):
+        output_final_state=True, nthreads=None, lib=None, state_v_first=False):
     """Token-by-token forward.
 
     q: [B, T, H, K]; k: [B, T, Hkv, K]; v: [B, T, Hkv, V] (Hkv divides H: query
     head h reads kv head h // (H // Hkv)); g: [B, T, H] or None; g_gamma: [H]
     or None; initial_state: [N, H, K, V] or None; cu_seqlens: int [N+1] or
-    None (then N = B).
+    None (then N = B).  state_v_first: initial_state and final_state are
+    [N, H, V, K] (the transposed state) instead of [N, H, K, V].
     Returns (o [B, T, H, V], final_state [N, H, K, V] or None), both float64.
     """
+    initial_state = _vk(initial_state, state_v_first)
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, H, K = q.shape
     Hkv = k.shape[2]
@@ -124,18 +134,19 @@ def fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None, cu_seqlen
                              N, _ptr(o), _ptr(ht), int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError(f"sgla_oracle_fwd rejected its arguments (code {rc})")
-    return o, ht
+    return o, _vk(ht, state_v_first)
 
 
 def bwd(q, k, v, do, g=None, g_gamma=None, scale=None, initial_state=None, dht=None,
-        cu_seqlens=None, nthreads=None, lib=None):
+        cu_seqlens=None, nthreads=None, lib=None, state_v_first=False):
     """Token-by-token backward: gradients of sum <do, o> + sum <dht, final_state>.
 
     q, k: [B, T, H, K]; v, do: [B, T, H, V]; g: [B, T, H] or None; g_gamma:
     [H] or None; initial_state, dht: [N, H, K, V] or None; cu_seqlens as for
     fwd.  Returns a dict of float64 arrays dq, dk [B, T, H, K], dv [B, T, H,
     V], dg [B, T, H] (None without g), dg_gamma [H] (None without g_gamma),
-    dh0 [N, H, K, V]."""
+    dh0 [N, H, K, V].  state_v_first: initial_state, dht and dh0 are [N, H, V, K]."""
+    initial_state, dht = _vk(initial_state, state_v_first), _vk(dht, state_v_first)
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, T, H, K = q.shape
     V = v.shape[-1]
@@ -163,14 +174,17 @@ def bwd(q, k, v, do, g=None, g_gamma=None, scale=None, initial_state=None, dht=N
                              _ptr(dh0), int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError(f"sgla_oracle_bwd rejected its arguments (code {rc})")
-    return dict(dq=dq, dk=dk, dv=dv, dg=dg, dg_gamma=dgg, dh0=dh0)
+    return dict(dq=dq, dk=dk, dv=dv, dg=dg, dg_gamma=dgg, dh0=_vk(dh0, state_v_first))
 
 
-def step(q, k, v, g, state, scale=None, g_gamma=None, nthreads=None, lib=None):
+def step(q, k, v, g, state, scale=None, g_gamma=None, nthreads=None, lib=None,
+         state_v_first=False):
     """One decode step.  q: [N, H, K]; k: [N, Hkv, K]; v: [N, Hkv, V];
     g: [N, H] or None; g_gamma: [H] or None (at most one);
-    state: [N, H, K, V] (not modified; the updated copy is returned).
-    Returns (o [N, H, V], new_state [N, H, K, V]), float64."""
+    state: [N, H, K, V], or [N, H, V, K] with state_v_first (not modified; the
+    updated copy is returned in the same layout).
+    Returns (o [N, H, V], new_state), float64."""
+    state = _vk(state, state_v_first)
     q, k, v, g, g_gamma = _f64(q), _f64(k), _f64(v), _f64(g), _f64(g_gamma)
     S = np.array(state, dtype=np.float64, order="C", copy=True)
     N, H, K = q.shape
@@ -184,7 +198,7 @@ def step(q, k, v, g, state, scale=None, g_gamma=None, nthreads=None, lib=None):
                               float(scale), _ptr(S), _ptr(o), int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError(f"sgla_oracle_step rejected its arguments (code {rc})")
-    return o, S
+    return o, _vk(S, state_v_first)
 
 
 def chunk_local_cumsum(g, chunk_size=64, cu_seqlens=None, lib=None):

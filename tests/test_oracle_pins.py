@@ -453,11 +453,43 @@ def pin_bwd_gate_identity(lib, seed=14, B=2, T=150, H=2, K=5, V=4):
             and all(np.array_equal(g2[x], g3[x]) for x in ("dq", "dk", "dv", "dh0")))
 
 
+def pin_state_v_first(lib, seed=15, N=2, H=2, K=3, V=4):
+    """The [V, K] state layout (section 二, state_v_first): one token from a
+    zero state with g = 0 leaves the state v k^T (rows indexed by v); a
+    forward, a backward and a decode step in that layout equal the [K, V] ones
+    with every state transposed."""
+    rng = np.random.default_rng(seed)
+    q, k, v = _rand(rng, N, 1, H, K), _rand(rng, N, 1, H, K), _rand(rng, N, 1, H, V)
+    _, ht = oracle.fwd(q, k, v, g=np.zeros((N, 1, H)), lib=lib, state_v_first=True)
+    want = np.einsum("nhv,nhk->nhvk", v[:, 0], k[:, 0])
+    if _rel(ht, want) > TIGHT:
+        return False
+    T = 30
+    q, k, v = _rand(rng, N, T, H, K), _rand(rng, N, T, H, K), _rand(rng, N, T, H, V)
+    g = logsigmoid(_rand(rng, N, T, H))
+    S0 = _rand(rng, N, H, K, V)
+    S0t = np.ascontiguousarray(np.swapaxes(S0, -1, -2))
+    o1, h1 = oracle.fwd(q, k, v, g=g, initial_state=S0, lib=lib)
+    o2, h2 = oracle.fwd(q, k, v, g=g, initial_state=S0t, lib=lib, state_v_first=True)
+    if not (np.array_equal(o1, o2) and np.array_equal(np.swapaxes(h1, -1, -2), h2)):
+        return False
+    do, dht = _rand(rng, N, T, H, V), _rand(rng, N, H, K, V)
+    b1 = oracle.bwd(q, k, v, do, g=g, initial_state=S0, dht=dht, lib=lib)
+    b2 = oracle.bwd(q, k, v, do, g=g, initial_state=S0t, dht=np.swapaxes(dht, -1, -2), lib=lib,
+                    state_v_first=True)
+    if not (np.array_equal(b1["dq"], b2["dq"]) and np.array_equal(np.swapaxes(b1["dh0"], -1, -2), b2["dh0"])):
+        return False
+    s1, S1 = oracle.step(q[:, 0], k[:, 0], v[:, 0], g[:, 0], S0, lib=lib)
+    s2, S2 = oracle.step(q[:, 0], k[:, 0], v[:, 0], g[:, 0], S0t, lib=lib, state_v_first=True)
+    return np.array_equal(s1, s2) and np.array_equal(np.swapaxes(S1, -1, -2), S2)
+
+
 ALL_PINS = [pin_chunk_local_cumsum, pin_hand_example, pin_brute_force, pin_zero_gate, pin_full_forget,
             pin_split_sequence, pin_varlen_equals_per_sequence, pin_chunk_form,
             pin_gamma_is_broadcast_g, pin_retnet_closed_form, pin_invariants,
             pin_prefill_then_decode, pin_step_brute_force, pin_gqa_is_repeated_mha,
-            pin_step_variants, pin_bwd_finite_differences, pin_bwd_gate_identity]
+            pin_step_variants, pin_bwd_finite_differences, pin_bwd_gate_identity,
+            pin_state_v_first]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
