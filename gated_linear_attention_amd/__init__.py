@@ -16,7 +16,8 @@ K], v [B, T, Hkv, V], g [B, T, H] log gates or g_gamma [H] per-head log decay
 [N + 1] with B == 1 for packed input, chunk_size a power of two (64).  The kv
 head count Hkv is read from k's shape and must divide H: query head h reads kv
 head h // (H // Hkv) (grouped-query attention, page "relinear", its GQA
-target); Hkv == H is plain multi-head attention.
+target); Hkv == H is plain multi-head attention.  ``state_v_first=True``
+keeps every state in the [N, H, V, K] layout instead (section 二).
 """
 from __future__ import annotations
 
@@ -28,7 +29,7 @@ import torch
 __all__ = ["chunk_fwd", "chunk_bwd", "recurrent_step", "chunk_local_cumsum", "library_path", "lib",
            "SglaError", "ABI_VERSION"]
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsgla.so")
 
@@ -45,7 +46,8 @@ class _ChunkArgs(ctypes.Structure):
                 ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("chunk_size", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32),
                 ("o_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("output_final_state", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32)]
+                ("output_final_state", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("state_v_first", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -75,8 +77,8 @@ def _load():
     lib.sgla_chunk_local_cumsum.restype = ctypes.c_int
     lib.sgla_chunk_local_cumsum.argtypes = [pargs, vp, vp, vp, vp, sz, vp]
     lib.sgla_recurrent_step.restype = ctypes.c_int
-    lib.sgla_recurrent_step.argtypes = [i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp,
-                                        vp, vp, vp, vp]
+    lib.sgla_recurrent_step.argtypes = [i32, i32, i32, i32, i32, f32, i32, i32, i32, vp, vp, vp,
+                                        vp, vp, vp, vp, vp]
     if lib.sgla_abi_version() != ABI_VERSION:
         raise ImportError(f"libsgla ABI {lib.sgla_abi_version()} != binding ABI {ABI_VERSION}")
     return lib
@@ -135,9 +137,14 @@ def _host_cu(cu_seqlens):
     return cu
 
 
-def _chunk_args(B, T, H, K, V, N, chunk_size, qkv, o_dtype, scale, out_final, Hkv=0):
+def _chunk_args(B, T, H, K, V, N, chunk_size, qkv, o_dtype, scale, out_final, Hkv=0,
+                state_v_first=False):
     return _ChunkArgs(B, T, H, K, V, N, chunk_size, qkv, o_dtype, float(scale), int(out_final),
-                      int(Hkv))
+                      int(Hkv), int(bool(state_v_first)))
+
+
+def _state_shape(N, H, K, V, state_v_first):
+    return (N, H, V, K) if state_v_first else (N, H, K, V)
 
 
 def _kv_heads(k, H, axis):
@@ -160,7 +167,7 @@ def _workspace_size(args, cu_ptr) -> int:
 
 def chunk_fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None,
               output_final_state=False, cu_seqlens=None, chunk_size=64,
-              o_dtype=torch.float32, out=None):
+              o_dtype=torch.float32, out=None, state_v_first=False):
     """Chunked Simple GLA forward on the GPU.
 
     Returns ``(o, final_state)``; ``final_state`` is None unless
@@ -188,11 +195,13 @@ def chunk_fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None,
     if initial_state is not None and initial_state.shape[0] != N:
         raise ValueError(f"initial_state must have {N} rows (one per sequence), got "
                          f"{initial_state.shape[0]}")
-    _check_dev("initial_state", initial_state, dev, torch.float32, (N, H, K, V))
+    sshape = _state_shape(N, H, K, V, state_v_first)
+    _check_dev("initial_state", initial_state, dev, torch.float32, sshape)
     if scale is None:
         scale = K ** -0.5
     od = _dtype_code(o_dtype, "o_dtype")
-    args = _chunk_args(B, T, H, K, V, N, chunk_size, qkv, od, scale, output_final_state, Hkv)
+    args = _chunk_args(B, T, H, K, V, N, chunk_size, qkv, od, scale, output_final_state, Hkv,
+                       state_v_first)
     cu_ptr = None if cu is None else ctypes.c_void_p(cu.data_ptr())
     ws_bytes = _workspace_size(args, cu_ptr)
     if out is None:
@@ -200,7 +209,7 @@ def chunk_fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None,
     else:
         _check_dev("out", out, dev, o_dtype, (B, T, H, V))
         o = out
-    ht = torch.empty((N, H, K, V), device=dev, dtype=torch.float32) if output_final_state else None
+    ht = torch.empty(sshape, device=dev, dtype=torch.float32) if output_final_state else None
     ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
     st = lib.sgla_chunk_fwd(ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                             _ptr(g_gamma), _ptr(initial_state), cu_ptr, _ptr(o), _ptr(ht),
@@ -211,7 +220,7 @@ def chunk_fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None,
 
 
 def chunk_bwd(q, k, v, do, g=None, g_gamma=None, scale=None, initial_state=None, dht=None,
-              cu_seqlens=None, chunk_size=64):
+              cu_seqlens=None, chunk_size=64, state_v_first=False):
     """Backward of chunk_fwd on the GPU: gradients of sum <do, o> + sum <dht,
     final_state> (dht None: no loss on the final state).
 
@@ -239,11 +248,12 @@ def chunk_bwd(q, k, v, do, g=None, g_gamma=None, scale=None, initial_state=None,
     N = B if cu is None else cu.numel() - 1
     if cu is not None and B != 1:
         raise ValueError(f"packed input (cu_seqlens) requires B == 1, got B={B}")
-    _check_dev("initial_state", initial_state, dev, torch.float32, (N, H, K, V))
-    _check_dev("dht", dht, dev, torch.float32, (N, H, K, V))
+    sshape = _state_shape(N, H, K, V, state_v_first)
+    _check_dev("initial_state", initial_state, dev, torch.float32, sshape)
+    _check_dev("dht", dht, dev, torch.float32, sshape)
     if scale is None:
         scale = K ** -0.5
-    args = _chunk_args(B, T, H, K, V, N, chunk_size, qkv, _F32, scale, 0, H)
+    args = _chunk_args(B, T, H, K, V, N, chunk_size, qkv, _F32, scale, 0, H, state_v_first)
     cu_ptr = None if cu is None else ctypes.c_void_p(cu.data_ptr())
     n = lib.sgla_chunk_bwd_workspace_size(ctypes.byref(args), cu_ptr)
     if n == 0 and lib.sgla_last_error():
@@ -254,7 +264,7 @@ def chunk_bwd(q, k, v, do, g=None, g_gamma=None, scale=None, initial_state=None,
     dv = torch.empty((B, T, H, V), **f32)
     dg = torch.empty((B, T, H), **f32) if g is not None else None
     dgg = torch.empty((H,), **f32) if g_gamma is not None else None
-    dh0 = torch.empty((N, H, K, V), **f32)
+    dh0 = torch.empty(sshape, **f32)
     ws = torch.empty(max(n, 1), device=dev, dtype=torch.uint8)
     st = lib.sgla_chunk_bwd(ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(g_gamma),
                             _ptr(initial_state), cu_ptr, _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk),
@@ -287,7 +297,7 @@ def chunk_local_cumsum(g, chunk_size=64, cu_seqlens=None):
 
 
 def recurrent_step(q, k, v, g, state, scale=None, o_dtype=torch.float32, out=None,
-                   g_gamma=None):
+                   g_gamma=None, state_v_first=False):
     """One decode step; ``state`` [N, H, K, V] float32 is updated in place.
     q [N, H, K], k [N, Hkv, K], v [N, Hkv, V] (bf16 or float32); g [N, H]
     float32 log gate or None; g_gamma [H] float32 per-head log decay or None
@@ -306,7 +316,7 @@ def recurrent_step(q, k, v, g, state, scale=None, o_dtype=torch.float32, out=Non
         raise ValueError("g and g_gamma are mutually exclusive; pass at most one")
     _check_dev("g", g, dev, torch.float32, (N, H))
     _check_dev("g_gamma", g_gamma, dev, torch.float32, (H,))
-    _check_dev("state", state, dev, torch.float32, (N, H, K, V))
+    _check_dev("state", state, dev, torch.float32, _state_shape(N, H, K, V, state_v_first))
     if scale is None:
         scale = K ** -0.5
     od = _dtype_code(o_dtype, "o_dtype")
@@ -315,7 +325,8 @@ def recurrent_step(q, k, v, g, state, scale=None, o_dtype=torch.float32, out=Non
     else:
         _check_dev("out", out, dev, o_dtype, (N, H, V))
         o = out
-    st = lib.sgla_recurrent_step(N, H, Hkv, K, V, float(scale), qkv, od, _ptr(q), _ptr(k), _ptr(v),
+    st = lib.sgla_recurrent_step(N, H, Hkv, K, V, float(scale), qkv, od, int(bool(state_v_first)),
+                                 _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(g), _ptr(g_gamma), _ptr(state), _ptr(o), _stream(dev))
     if st != _OK:
         _raise(st, "sgla_recurrent_step")

@@ -171,7 +171,8 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                        const TIn* __restrict__ v, const TIn* __restrict__ dout,
                        const float* __restrict__ g, const float* __restrict__ g_gamma,
                        const float* __restrict__ h0, const float* __restrict__ dht,
-                       float* __restrict__ dh0, float scale, int32_t H, int32_t V, SeqLayout seqs,
+                       float* __restrict__ dh0, float scale, int32_t H, int32_t V, StateLayout sl,
+                       SeqLayout seqs,
                        int32_t chunks_per_row, float* __restrict__ hbuf, float* __restrict__ dhbuf) {
   constexpr int LDX = K + 4;
   constexpr int NST = (K / 16) * 2;
@@ -198,7 +199,7 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   f32x4 hs[SPW];
   {
     const float* init = rev ? dht : h0;
-    const float* iu = init != nullptr ? init + ((int64_t)si.seq * H + hd) * KV + ucol : nullptr;
+    const float* iu = init != nullptr ? init + ((int64_t)si.seq * H + hd) * KV : nullptr;
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
       const int st = w + 4 * s;
@@ -206,7 +207,8 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
       if ((NST % 4 == 0 || st < NST) && iu != nullptr) {
         const int kt = st >> 1, ctl = st & 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hs[s][i] = iu[(int64_t)(16 * kt + 4 * g4 + i) * V + 16 * ctl + r];
+        for (int i = 0; i < 4; ++i)
+          hs[s][i] = iu[(int64_t)(16 * kt + 4 * g4 + i) * sl.rs + (ucol + 16 * ctl + r) * sl.cs];
       }
     }
   }
@@ -271,14 +273,15 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     __syncthreads();
   }
   if (rev && dh0 != nullptr) {
-    float* du = dh0 + ((int64_t)si.seq * H + hd) * KV + ucol;
+    float* du = dh0 + ((int64_t)si.seq * H + hd) * KV;
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
       const int st = w + 4 * s;
       if (NST % 4 == 0 || st < NST) {
         const int kt = st >> 1, ctl = st & 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) du[(int64_t)(16 * kt + 4 * g4 + i) * V + 16 * ctl + r] = hs[s][i];
+        for (int i = 0; i < 4; ++i)
+          du[(int64_t)(16 * kt + 4 * g4 + i) * sl.rs + (ucol + 16 * ctl + r) * sl.cs] = hs[s][i];
       }
     }
   }
@@ -568,7 +571,7 @@ hipError_t launch_k(const ChunkBwdParams& p, hipStream_t stream) {
   if (p.seqs.num_seqs > 0) {
     const int units = (int)unit_grid(p.seqs.num_seqs, p.H, 1, p.V / VT);
     hipLaunchKernelGGL((chunk_bwd_state_kernel<K, TIn>), dim3((unsigned)(2 * units)), dim3(NT), 0, stream,
-                       q, k, v, dout, p.g, p.g_gamma, p.h0, p.dht, p.dh0, p.scale, p.H, p.V, p.seqs,
+                       q, k, v, dout, p.g, p.g_gamma, p.h0, p.dht, p.dh0, p.scale, p.H, p.V, p.sl, p.seqs,
                        per_row, p.hbuf, p.dhbuf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -95,7 +95,7 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                       const bf16* __restrict__ v, const float* __restrict__ g,
                       const float* __restrict__ g_gamma, const float* __restrict__ h0,
                       TOut* __restrict__ o, float* __restrict__ ht, float scale, int32_t H,
-                      int32_t Hkv, int32_t V, SeqLayout seqs) {
+                      int32_t Hkv, int32_t V, StateLayout sl, SeqLayout seqs) {
   using L = Layout<K>;
   constexpr int NT = L::NT;
   constexpr int SEG = K / 8;                 // 16-byte segments per q/k row
@@ -179,7 +179,7 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int kt = 0; kt < L::KT; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        h[kt][i] = h0u != nullptr ? h0u[(int64_t)(krow0 + 16 * kt + 4 * g4 + i) * V + vcol] : 0.f;
+        h[kt][i] = h0u != nullptr ? h0u[(int64_t)(krow0 + 16 * kt + 4 * g4 + i) * sl.rs + (int64_t)vcol * sl.cs] : 0.f;
   }
 
   // ---- chunk staging registers -------------------------------------------
@@ -472,7 +472,7 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int kt = 0; kt < L::KT; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        htu[(int64_t)(krow0 + 16 * kt + 4 * g4 + i) * V + vcol] = h[kt][i];
+        htu[(int64_t)(krow0 + 16 * kt + 4 * g4 + i) * sl.rs + (int64_t)vcol * sl.cs] = h[kt][i];
   }
 }
 
@@ -483,7 +483,7 @@ hipError_t launch_k(const ChunkFwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((chunk_fwd_bf16_kernel<K, TOut>), grid, dim3(Layout<K>::NT), 0, stream,
                      static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
                      static_cast<const bf16*>(p.v), p.g, p.g_gamma, p.h0,
-                     static_cast<TOut*>(p.o), p.ht, p.scale, p.H, p.Hkv, p.V, p.seqs);
+                     static_cast<TOut*>(p.o), p.ht, p.scale, p.H, p.Hkv, p.V, p.sl, p.seqs);
   return hipGetLastError();
 }
 

@@ -83,7 +83,8 @@ template <int K, typename TOut>
 __global__ void __launch_bounds__(NT)
 chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict__ v,
                            const float* __restrict__ h0, TOut* __restrict__ o,
-                           float* __restrict__ ht, int32_t H, int32_t Hkv, int32_t V, SeqLayout seqs,
+                           float* __restrict__ ht, int32_t H, int32_t Hkv, int32_t V, StateLayout sl,
+                           SeqLayout seqs,
                            int32_t chunks_per_row, const float* __restrict__ gates,
                            const bf16* __restrict__ amat, const bf16* __restrict__ ktf) {
   using L = WideLayout;
@@ -149,12 +150,12 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
 #pragma unroll
     for (int a = 0; a < 16; ++a) h[rt][a] = 0.f;
   if (h0 != nullptr) {
-    const float* h0u = h0 + ((int64_t)seq * H + hd) * K * V + vt * VT + l32;
+    const float* h0u = h0 + ((int64_t)seq * H + hd) * K * V + (int64_t)(vt * VT + l32) * sl.cs;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
       for (int a = 0; a < 16; ++a)
-        h[rt][a] = h0u[(int64_t)(k0w + 32 * rt + 16 * (a >> 3) + 8 * hf + (a & 7)) * V];
+        h[rt][a] = h0u[(int64_t)(k0w + 32 * rt + 16 * (a >> 3) + 8 * hf + (a & 7)) * sl.rs];
   }
 
   // ---- V tile and gates of one chunk: waves 0-3 load a V piece each, waves
@@ -340,12 +341,12 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
   }
 
   if (ht != nullptr) {
-    float* htu = ht + ((int64_t)seq * H + hd) * K * V + vt * VT + l32;
+    float* htu = ht + ((int64_t)seq * H + hd) * K * V + (int64_t)(vt * VT + l32) * sl.cs;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
       for (int a = 0; a < 16; ++a)
-        htu[(int64_t)(k0w + 32 * rt + 16 * (a >> 3) + 8 * hf + (a & 7)) * V] = h[rt][a];
+        htu[(int64_t)(k0w + 32 * rt + 16 * (a >> 3) + 8 * hf + (a & 7)) * sl.rs] = h[rt][a];
   }
 }
 
@@ -356,7 +357,7 @@ hipError_t launch_k(const ChunkFwdParams& p, hipStream_t stream) {
   const int per_row = p.seqs.T > 0 ? (p.seqs.T + C - 1) / C : 0;
   hipLaunchKernelGGL((chunk_fwd_bf16_wide_kernel<K, TOut>), grid, dim3(NT), 0, stream,
                      static_cast<const bf16*>(p.qfr), static_cast<const bf16*>(p.v), p.h0,
-                     static_cast<TOut*>(p.o), p.ht, p.H, p.Hkv, p.V, p.seqs, per_row, p.gates,
+                     static_cast<TOut*>(p.o), p.ht, p.H, p.Hkv, p.V, p.sl, p.seqs, per_row, p.gates,
                      static_cast<const bf16*>(p.amat), static_cast<const bf16*>(p.ktf));
   return hipGetLastError();
 }

@@ -53,7 +53,7 @@ chunk_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                      const float* __restrict__ v, const float* __restrict__ g,
                      const float* __restrict__ g_gamma, const float* __restrict__ h0,
                      TOut* __restrict__ o, float* __restrict__ ht, float scale, int32_t H,
-                     int32_t Hkv, int32_t V, SeqLayout seqs) {
+                     int32_t Hkv, int32_t V, StateLayout sl, SeqLayout seqs) {
   constexpr int LDQ = K + 4;          // Q / K row stride (floats)
   constexpr int NKT = K / 16;         // 16-row state tiles
   constexpr int NST = NKT * 2;        // state tiles (x 2 column tiles)
@@ -86,7 +86,9 @@ chunk_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
   const int g4 = lane >> 4;
   const int r = lane & 15;
   const float gam2 = g_gamma != nullptr ? g_gamma[hd] * kRcpLn2f : 0.f;
-  const int64_t su = ((int64_t)seq * H + hd) * K * V + vt * VT;
+  const int64_t su = ((int64_t)seq * H + hd) * K * V;
+  // state element (row, column c of this tile)
+  auto sidx = [&](int row, int c) { return su + (int64_t)row * sl.rs + (int64_t)(vt * VT + c) * sl.cs; };
 
   // state tiles of this wave: st = w + 4 s, rows [16 (st >> 1), +16),
   // columns [16 (st & 1), +16); acc element i = h[16 kt + 4 g + i][16 ct + r]
@@ -98,7 +100,7 @@ chunk_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
     if (st < NST && h0 != nullptr) {
       const int kt = st >> 1, ctl = st & 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hs[s][i] = h0[su + (int64_t)(16 * kt + 4 * g4 + i) * V + 16 * ctl + r];
+      for (int i = 0; i < 4; ++i) hs[s][i] = h0[sidx(16 * kt + 4 * g4 + i, 16 * ctl + r)];
     }
   }
   auto publish_state = [&]() {
@@ -219,7 +221,7 @@ chunk_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
       if (st < NST) {
         const int kt = st >> 1, ctl = st & 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ht[su + (int64_t)(16 * kt + 4 * g4 + i) * V + 16 * ctl + r] = hs[s][i];
+        for (int i = 0; i < 4; ++i) ht[sidx(16 * kt + 4 * g4 + i, 16 * ctl + r)] = hs[s][i];
       }
     }
   }
@@ -232,7 +234,7 @@ hipError_t launch_k(const ChunkFwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((chunk_fwd_f32_kernel<K, TOut>), grid, dim3(NTHREADS), 0, stream,
                      static_cast<const float*>(p.q), static_cast<const float*>(p.k),
                      static_cast<const float*>(p.v), p.g, p.g_gamma, p.h0,
-                     static_cast<TOut*>(p.o), p.ht, p.scale, p.H, p.Hkv, p.V, p.seqs);
+                     static_cast<TOut*>(p.o), p.ht, p.scale, p.H, p.Hkv, p.V, p.sl, p.seqs);
   return hipGetLastError();
 }
 

@@ -144,6 +144,93 @@ recurrent_step_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   }
 }
 
+// The same step on the [V, K] state layout ([SG] 二, state_v_first): row v
+// of a unit's state is S[.][v], K contiguous floats.  Each thread owns four
+// adjacent keys (16-byte accesses) of every RG-th row, so each load of a wave
+// covers whole contiguous rows; o[v] = scale * sum_k S[k][v] q[k] becomes a
+// reduction along the row: over the row's lanes by shuffles, and through LDS
+// when a row spans two waves (K = 512).
+template <int K, typename TIn, typename TOut>
+__global__ void __launch_bounds__(256)
+recurrent_step_vk_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                         const TIn* __restrict__ v, const float* __restrict__ g,
+                         const float* __restrict__ g_gamma, float* __restrict__ state,
+                         TOut* __restrict__ o, float scale, int32_t H, int32_t Hkv, int32_t V) {
+  constexpr int TPR = K / 4;                  // threads per state row
+  constexpr int RG = 256 / TPR;               // row groups
+  constexpr int LW = TPR < 64 ? TPR : 64;     // lanes of a row within one wave
+  constexpr int NSUB = TPR / LW;              // waves a row spans
+  constexpr int BATCH = 16;                   // rows in flight per thread
+  static_assert(RG >= 2 && RG * TPR == 256, "K must be a power of two in [32, 512]");
+  __shared__ float part[1024 * NSUB];
+
+  const int64_t unit = blockIdx.x;    // n * H + h
+  const uint32_t n = blockIdx.x / (uint32_t)H;
+  const int h = (int)(blockIdx.x - n * (uint32_t)H);
+  const int64_t ukv = (int64_t)n * Hkv + h / (H / Hkv);   // (sequence, kv head) row of k and v
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int cq = tid % TPR;
+  const int rg = tid / TPR;
+  const float gamma = expf(g != nullptr ? g[unit] : (g_gamma != nullptr ? g_gamma[h] : 0.f));
+  f32x4 kk, qq;
+  {
+    const TIn* ku = k + ukv * K + 4 * cq;
+    const TIn* qu = q + unit * K + 4 * cq;
+    kk = f32x4{to_f32(ku[0]), to_f32(ku[1]), to_f32(ku[2]), to_f32(ku[3])};
+    qq = f32x4{to_f32(qu[0]), to_f32(qu[1]), to_f32(qu[2]), to_f32(qu[3])};
+  }
+  const TIn* vu = v + ukv * V;
+  f32x4* S = reinterpret_cast<f32x4*>(state + unit * (int64_t)K * V);
+  const int rpt = V / RG;             // rows per row group (V % 32 == 0)
+  for (int b0 = 0; b0 < rpt; b0 += BATCH) {
+    f32x4 sv[BATCH];
+    float vr[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      if (b0 + b < rpt) {
+        const int row = rg + RG * (b0 + b);
+        sv[b] = __builtin_nontemporal_load(&S[(int64_t)row * TPR + cq]);
+        vr[b] = to_f32(vu[row]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      if (b0 + b < rpt) {                  // uniform over the workgroup
+        const int row = rg + RG * (b0 + b);
+        f32x4 x = sv[b];
+        x.x = fmaf(gamma, x.x, vr[b] * kk.x);
+        x.y = fmaf(gamma, x.y, vr[b] * kk.y);
+        x.z = fmaf(gamma, x.z, vr[b] * kk.z);
+        x.w = fmaf(gamma, x.w, vr[b] * kk.w);
+        __builtin_nontemporal_store(x, &S[(int64_t)row * TPR + cq]);
+        float pq = fmaf(x.x, qq.x, fmaf(x.y, qq.y, fmaf(x.z, qq.z, x.w * qq.w)));
+#pragma unroll
+        for (int d = LW / 2; d >= 1; d >>= 1) pq += __shfl_xor(pq, d, 64);
+        if (lane % LW == 0) part[row * NSUB + cq / LW] = pq;
+      }
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < V; c += 256) {
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NSUB; ++i) sum += part[c * NSUB + i];
+    o[unit * V + c] = (TOut)(sum * scale);
+  }
+}
+
+template <int K, typename TIn, typename TOut>
+hipError_t launch_vk(const StepParams& p, hipStream_t stream) {
+  const int64_t units = (int64_t)p.N * p.H;
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL((recurrent_step_vk_kernel<K, TIn, TOut>), dim3((unsigned)units), dim3(256), 0,
+                     stream, static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k),
+                     static_cast<const TIn*>(p.v), p.g, p.g_gamma, p.state, static_cast<TOut*>(p.o),
+                     p.scale, p.H, p.Hkv, p.V);
+  return hipGetLastError();
+}
+
 template <int V, typename TIn, typename TOut>
 hipError_t launch_v(const StepParams& p, hipStream_t stream) {
   const int64_t units = (int64_t)p.N * p.H;
@@ -157,6 +244,16 @@ hipError_t launch_v(const StepParams& p, hipStream_t stream) {
 
 template <typename TIn, typename TOut>
 hipError_t launch_dtypes(const StepParams& p, hipStream_t stream) {
+  if (p.state_v_first) {
+    switch (p.K) {
+      case 32: return launch_vk<32, TIn, TOut>(p, stream);
+      case 64: return launch_vk<64, TIn, TOut>(p, stream);
+      case 128: return launch_vk<128, TIn, TOut>(p, stream);
+      case 256: return launch_vk<256, TIn, TOut>(p, stream);
+      case 512: return launch_vk<512, TIn, TOut>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (p.V) {
     case 32: return launch_v<32, TIn, TOut>(p, stream);
     case 64: return launch_v<64, TIn, TOut>(p, stream);

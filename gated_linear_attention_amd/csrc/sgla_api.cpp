@@ -195,6 +195,13 @@ sgla_status upload_tables(const Plan& P, char* ws, hipStream_t stream) {
   return SGLA_OK;
 }
 
+sgla::StateLayout state_layout(const sgla_chunk_args& a) {
+  sgla::StateLayout s;
+  s.rs = a.state_v_first ? 1 : a.V;
+  s.cs = a.state_v_first ? a.K : 1;
+  return s;
+}
+
 sgla::SeqLayout layout_of(const sgla_chunk_args* a, const Plan& P, char* ws) {
   sgla::SeqLayout L;
   L.num_seqs = P.N;
@@ -273,6 +280,7 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
   p.K = a.K;
   p.V = a.V;
   p.o_bf16 = a.o_dtype == SGLA_BF16;
+  p.sl = state_layout(a);
   p.seqs = L;
   p.gates = P.prep ? reinterpret_cast<const float*>(ws + P.gate_off) : nullptr;
   p.amat = P.prep ? ws + P.amat_off : nullptr;
@@ -367,6 +375,7 @@ sgla_status sgla_chunk_bwd(const sgla_chunk_args* args, const void* q, const voi
   p.K = a.K;
   p.V = a.V;
   p.qkv_bf16 = a.qkv_dtype == SGLA_BF16;
+  p.sl = state_layout(a);
   p.seqs = layout_of(args, P, ws);
   p.hbuf = reinterpret_cast<float*>(ws + B.h_off);
   p.dhbuf = reinterpret_cast<float*>(ws + B.dh_off);
@@ -395,7 +404,8 @@ sgla_status sgla_chunk_local_cumsum(const sgla_chunk_args* args, const float* g,
 }
 
 sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t num_kv_heads, int32_t K, int32_t V, float scale,
-                                int32_t qkv_dtype, int32_t o_dtype, const void* q, const void* k, const void* v,
+                                int32_t qkv_dtype, int32_t o_dtype, int32_t state_v_first,
+                                const void* q, const void* k, const void* v,
                                 const float* g, const float* g_gamma, float* state, void* o,
                                 hipStream_t stream) {
   if (N < 0 || H <= 0) return fail(SGLA_ERR_SHAPE, "N must be >= 0 and H > 0 (got N=%d H=%d)", N, H);
@@ -404,9 +414,16 @@ sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t num_kv_heads, int3
     return fail(SGLA_ERR_SHAPE, "num_kv_heads must divide H (got num_kv_heads=%d, H=%d)", num_kv_heads, H);
   if ((int64_t)N * H > INT32_MAX)
     return fail(SGLA_ERR_UNSUPPORTED, "N*H = %lld exceeds 2^31-1", (long long)N * H);
-  if (K < 1 || K > 1024) return fail(SGLA_ERR_UNSUPPORTED, "decode supports 1 <= K <= 1024 (got %d)", K);
-  if (!(V == 32 || V == 64 || V == 128 || V == 256 || V == 512))
-    return fail(SGLA_ERR_UNSUPPORTED, "decode supports V in {32,64,128,256,512} (got %d)", V);
+  if (state_v_first) {
+    if (!(K == 32 || K == 64 || K == 128 || K == 256 || K == 512))
+      return fail(SGLA_ERR_UNSUPPORTED, "decode with the [V, K] state supports K in {32,64,128,256,512} (got %d)", K);
+    if (V < 32 || V > 1024 || V % 32 != 0)
+      return fail(SGLA_ERR_UNSUPPORTED, "decode with the [V, K] state supports V a multiple of 32 in [32, 1024] (got %d)", V);
+  } else {
+    if (K < 1 || K > 1024) return fail(SGLA_ERR_UNSUPPORTED, "decode supports 1 <= K <= 1024 (got %d)", K);
+    if (!(V == 32 || V == 64 || V == 128 || V == 256 || V == 512))
+      return fail(SGLA_ERR_UNSUPPORTED, "decode supports V in {32,64,128,256,512} (got %d)", V);
+  }
   if (qkv_dtype != SGLA_BF16 && qkv_dtype != SGLA_F32)
     return fail(SGLA_ERR_DTYPE, "qkv_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", qkv_dtype);
   if (o_dtype != SGLA_BF16 && o_dtype != SGLA_F32)
@@ -435,6 +452,7 @@ sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t num_kv_heads, int3
   p.N = N;
   p.H = H;
   p.Hkv = Hkv;
+  p.state_v_first = state_v_first != 0;
   p.K = K;
   p.V = V;
   p.qkv_bf16 = qkv_dtype == SGLA_BF16;

@@ -33,6 +33,14 @@ struct ChunkEntry {
   int32_t len;   // tokens in the chunk (1..kChunk)
 };
 
+// Layout of a caller's [N, H, K, V] or [N, H, V, K] state ([SG] 二,
+// state_v_first): element (k, v) of one (sequence, head) state sits at
+// k * rs + v * cs.
+struct StateLayout {
+  int32_t rs;   // stride between key rows: V, or 1 for the [V, K] layout
+  int32_t cs;   // stride between value columns: 1, or K for the [V, K] layout
+};
+
 // Description of the token ranges a launch covers.  Dense input: seq_table ==
 // nullptr and every sequence b has bos = b * T, len = T.  Packed input: the
 // table lives in device memory (workspace).
@@ -76,6 +84,7 @@ struct ChunkFwdParams {
   float scale;
   int32_t H, Hkv, K, V;      // Hkv divides H: query head h reads kv head h / (H / Hkv)
   int32_t o_bf16;            // 1: o is bf16, 0: float32
+  StateLayout sl;            // layout of h0 and ht
   SeqLayout seqs;
   const float* gates;        // wide-key path: preparation outputs (workspace)
   const void* amat;
@@ -118,6 +127,7 @@ struct ChunkBwdParams {
   float scale;
   int32_t H, K, V;
   int32_t qkv_bf16;
+  StateLayout sl;            // layout of h0, dht and dh0
   SeqLayout seqs;
   float* hbuf;               // workspace [num_chunks, H, K, V]: state entering each chunk
   float* dhbuf;              // workspace [num_chunks, H, K, V]: gradient of the state leaving it
@@ -132,10 +142,11 @@ struct StepParams {
   const void* v;
   const float* g;            // [N, H] or nullptr
   const float* g_gamma;      // [H] or nullptr
-  float* state;
+  float* state;              // [N, H, K, V], or [N, H, V, K] when state_v_first
   void* o;
   float scale;
   int32_t N, H, Hkv, K, V;
+  int32_t state_v_first;
   int32_t qkv_bf16;
   int32_t o_bf16;
 };

@@ -17,7 +17,10 @@
  *     is enqueued on the caller's `stream`.
  *   - Layouts follow section 二: q [B, T, H, K]; k [B, T, Hkv, K];
  *     v [B, T, Hkv, V]; o [B, T, H, V]; g [B, T, H]; g_gamma [H]; states
- *     [N, H, K, V] with S[k][v] (key index major).  Hkv, the number of kv
+ *     [N, H, K, V] with S[k][v] (key index major), or [N, H, V, K] (value
+ *     index major) when state_v_first is set (section 二: the [V, K] layout
+ *     some backends keep; it applies to initial_state, final_state, dht, dh0
+ *     and the decode state alike).  Hkv, the number of kv
  *     heads, divides H; query head h reads kv head h / (H / Hkv), the
  *     contiguous grouping of grouped-query attention (page "relinear", its
  *     GQA target, and the Simple GLA layer's num_kv_heads, section 四).  Every
@@ -46,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SGLA_ABI_VERSION 2
+#define SGLA_ABI_VERSION 3
 
 typedef enum {
   SGLA_OK = 0,
@@ -69,6 +72,7 @@ typedef struct {
   float scale;                /* finite; callers wanting the default pass 1/sqrt(K) */
   int32_t output_final_state; /* nonzero: write final_state */
   int32_t num_kv_heads;       /* Hkv: heads of k and v; 0 means H.  Must divide H */
+  int32_t state_v_first;      /* nonzero: every state argument is [N, H, V, K] */
 } sgla_chunk_args;
 
 /* ABI revision of the loaded library (SGLA_ABI_VERSION it was built with). */
@@ -217,13 +221,16 @@ sgla_status sgla_chunk_local_cumsum(const sgla_chunk_args *args, const float *g,
  *   g       [N, H] float32 log gate, or NULL
  *   g_gamma [H] float32 per-head log decay, or NULL.  At most one of g /
  *           g_gamma (section 二); neither means no decay.
- *   state   [N, H, K, V] float32, read and written in place
+ *   state   [N, H, K, V] float32, or [N, H, V, K] when state_v_first is
+ *           nonzero, read and written in place
  *   o       [N, H, V] in o_dtype; must not alias the state
- * All pointers are device pointers.  Supported: 1 <= K <= 1024 and V in
- * {32, 64, 128, 256, 512}.
+ * All pointers are device pointers.  Supported: [K, V] layout: 1 <= K <= 1024
+ * and V in {32, 64, 128, 256, 512}; [V, K] layout: K in {32, 64, 128, 256,
+ * 512} and V a multiple of 32 in [32, 1024].
  */
 sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t num_kv_heads, int32_t K, int32_t V,
                                 float scale, int32_t qkv_dtype, int32_t o_dtype,
+                                int32_t state_v_first,
                                 const void *q, const void *k, const void *v,
                                 const float *g, const float *g_gamma, float *state, void *o,
                                 hipStream_t stream);

@@ -59,7 +59,7 @@ def test_single_hip_runtime_in_process(G):
 
 
 def test_abi_version(G):
-    assert G.lib.sgla_abi_version() == G.ABI_VERSION == 2
+    assert G.lib.sgla_abi_version() == G.ABI_VERSION == 3
 
 
 class Buffers:
@@ -111,7 +111,7 @@ def chunk_call(G, args, b, cu=None, g=True, gg=False, h0=True, ht=True, ws_bytes
 
 def mkargs(G, B=1, T=128, H=2, K=64, V=64, N=1, chunk=64, qkv=BF16, od=F32, scale=0.125, fs=1,
            Hkv=0):
-    return G._ChunkArgs(B, T, H, K, V, N, chunk, qkv, od, scale, fs, Hkv)
+    return G._ChunkArgs(B, T, H, K, V, N, chunk, qkv, od, scale, fs, Hkv, 0)
 
 
 CASES = [
@@ -202,6 +202,8 @@ STEP_CASES = [
     ("both gates", dict(gg="gg"), INVALID, "mutually exclusive"),
     ("num_kv_heads not dividing H", dict(Hkv=3), SHAPE, "num_kv_heads"),
     ("null k", dict(k=None), INVALID, "non-NULL"),
+    ("[V, K] state with K=100", dict(vf=1, K=100), UNSUPPORTED, "[V, K]"),
+    ("[V, K] state with V=48", dict(vf=1, V=48), UNSUPPORTED, "[V, K]"),
     ("K=0", dict(K=0), UNSUPPORTED, "K <="),
     ("K=2048", dict(K=2048), UNSUPPORTED, "K <="),
     ("H=0", dict(H=0), SHAPE, "H > 0"),
@@ -216,7 +218,7 @@ STEP_CASES = [
 @pytest.mark.parametrize("desc,over,status,frag", STEP_CASES, ids=[c[0] for c in STEP_CASES])
 def test_recurrent_step_rejects_without_writing(G, desc, over, status, frag):
     b = Buffers(B=1, T=4, H=2, K=64, V=64, N=4)
-    kw = dict(N=4, H=2, Hkv=0, K=64, V=64, scale=0.125, qkv=BF16, od=F32, q=b.p("q"),
+    kw = dict(N=4, H=2, Hkv=0, K=64, V=64, scale=0.125, qkv=BF16, od=F32, vf=0, q=b.p("q"),
               k=b.p("k"), v=b.p("v"), g=b.p("g"), gg=None, state=b.p("h0"), o=b.p("o"))
     for key, val in over.items():
         if val == "state":
@@ -227,7 +229,7 @@ def test_recurrent_step_rejects_without_writing(G, desc, over, status, frag):
             val = b.p("gg")
         kw[key] = val
     st = G.lib.sgla_recurrent_step(kw["N"], kw["H"], kw["Hkv"], kw["K"], kw["V"], kw["scale"],
-                                   kw["qkv"], kw["od"], kw["q"], kw["k"], kw["v"], kw["g"],
+                                   kw["qkv"], kw["od"], kw["vf"], kw["q"], kw["k"], kw["v"], kw["g"],
                                    kw["gg"], kw["state"], kw["o"], None)
     msg = G.lib.sgla_last_error().decode()
     assert st == status, (st, msg)

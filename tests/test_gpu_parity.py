@@ -420,3 +420,73 @@ def test_errors_leave_outputs_untouched():
                             torch.zeros(2, 2, 64, 48, device=DEV))
     torch.cuda.synchronize()
     assert torch.all(state == 3.0)
+
+
+# ---------------------------------------------------------------------------
+# [V, K] state layout (section 二, state_v_first)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("K,V,dtype", [(64, 128, "bf16"), (128, 64, "bf16"), (256, 64, "bf16"),
+                                       (512, 96, "bf16"), (32, 64, "f32")])
+def test_state_v_first_forward(K, V, dtype):
+    """The forward with [V, K] states gives the same o bit for bit and the
+    transposed final state of the [K, V] call, and matches the oracle."""
+    inp = make_chunk_inputs(small("vf", B=1, T=0, H=2, K=K, V=V, dtype=dtype,
+                                  fixed_lengths=(130, 1, 70), initial_state=True, seed=K + V))
+    d = device_inputs(inp)
+    h0t = d["initial_state"].transpose(-1, -2).contiguous()
+    kw = dict(g=d["g"], scale=inp["scale"], output_final_state=True, cu_seqlens=inp["cu_seqlens"])
+    o1, h1 = sgla.chunk_fwd(d["q"], d["k"], d["v"], initial_state=d["initial_state"], **kw)
+    o2, h2 = sgla.chunk_fwd(d["q"], d["k"], d["v"], initial_state=h0t, state_v_first=True, **kw)
+    torch.cuda.synchronize()
+    assert tuple(h2.shape) == (3, 2, V, K)
+    assert torch.equal(o1, o2) and torch.equal(h1.transpose(-1, -2), h2)
+    o_ref, h_ref = oracle.fwd(inp["q"], inp["k"], inp["v"], g=inp["g"], scale=inp["scale"],
+                              initial_state=np.swapaxes(inp["initial_state"], -1, -2),
+                              cu_seqlens=inp["cu_seqlens"], state_v_first=True)
+    tol = _tol(dtype)
+    assert err_ratio(o2.cpu().numpy(), o_ref) <= tol
+    assert err_ratio(h2.cpu().numpy(), h_ref) <= tol
+
+
+def test_state_v_first_backward():
+    inp = make_chunk_inputs(small("vfb", B=1, T=0, H=2, K=64, V=96, fixed_lengths=(100, 30),
+                                  initial_state=True, seed=3))
+    d = device_inputs(inp)
+    rng = np.random.default_rng(4)
+    do = to_dev(rng.standard_normal((1, inp["T"], 2, 96)).astype(np.float32), torch.bfloat16)
+    dht = to_dev(rng.standard_normal((2, 2, 64, 96)).astype(np.float32), torch.float32)
+    kw = dict(g=d["g"], scale=inp["scale"], cu_seqlens=inp["cu_seqlens"])
+    a = sgla.chunk_bwd(d["q"], d["k"], d["v"], do, initial_state=d["initial_state"], dht=dht, **kw)
+    b = sgla.chunk_bwd(d["q"], d["k"], d["v"], do,
+                       initial_state=d["initial_state"].transpose(-1, -2).contiguous(),
+                       dht=dht.transpose(-1, -2).contiguous(), state_v_first=True, **kw)
+    torch.cuda.synchronize()
+    for name in ("dq", "dk", "dv", "dg"):
+        assert torch.equal(a[name], b[name]), name
+    assert torch.equal(a["dh0"].transpose(-1, -2), b["dh0"])
+
+
+@pytest.mark.parametrize("K,V", [(32, 32), (64, 96), (128, 128), (256, 64), (512, 128), (128, 1024)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_state_v_first(K, V, dtype):
+    """Decode on the [V, K] state (its own kernel: rows are value indices and
+    q.S reduces along a row) against the oracle step, with grouped kv heads
+    and a per-head g_gamma on some cases."""
+    Hkv, gate = (2, "gamma") if K in (64, 512) else (4, "g")
+    w = DecodeWorkload("vf", N=3, H=4, K=K, V=V, steps=3, dtype=dtype, Hkv=Hkv, gate=gate, seed=K + V)
+    inp = make_decode_inputs(w)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    S_ref = np.swapaxes(inp["state"], -1, -2).astype(np.float64)
+    state = to_dev(np.ascontiguousarray(np.swapaxes(inp["state"], -1, -2)), torch.float32)
+    gg = to_dev(inp["g_gamma"], torch.float32)
+    for s in range(inp["steps"]):
+        g = None if inp["g"] is None else inp["g"][s]
+        o = sgla.recurrent_step(to_dev(inp["q"][s], dt), to_dev(inp["k"][s], dt), to_dev(inp["v"][s], dt),
+                                to_dev(g, torch.float32), state, scale=inp["scale"], g_gamma=gg,
+                                state_v_first=True)
+        o_ref, S_ref = oracle.step(inp["q"][s], inp["k"][s], inp["v"][s], g, S_ref, scale=inp["scale"],
+                                   g_gamma=inp["g_gamma"], state_v_first=True)
+        torch.cuda.synchronize()
+        assert err_ratio(o.cpu().numpy(), o_ref) <= TOL_F32
+    assert err_ratio(state.cpu().numpy(), S_ref) <= TOL_F32
