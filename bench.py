@@ -218,7 +218,7 @@ def bench_chunk(workload: str, steps: int, warmup: int, warm_seconds: float,
                 ncopies=ncopies)
 
 
-def bench_decode(steps_timed: int, warmup: int, warm_seconds: float):
+def bench_decode(steps_timed: int, warmup: int, warm_seconds: float, state_v_first: bool = False):
     import numpy as np
     import torch
 
@@ -230,33 +230,35 @@ def bench_decode(steps_timed: int, warmup: int, warm_seconds: float):
     dev = torch.device("cuda:0")
     N, H, K, V, S, Hkv = inp["N"], inp["H"], inp["K"], inp["V"], inp["steps"], inp["Hkv"]
     t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
-    state = t(inp["state"], torch.float32)
+    state = t(np.swapaxes(inp["state"], -1, -2) if state_v_first else inp["state"], torch.float32)
     q, k, v, g = (t(inp["q"], torch.bfloat16), t(inp["k"], torch.bfloat16),
                   t(inp["v"], torch.bfloat16), t(inp["g"], torch.float32))
     o = torch.empty((N, H, V), device=dev, dtype=torch.float32)
-    warm_device(lambda i: sgla.recurrent_step(q[i % S], k[i % S], v[i % S], g[i % S], state,
-                                              scale=inp["scale"], out=o), warm_seconds)
+    step = lambda i: sgla.recurrent_step(q[i % S], k[i % S], v[i % S], g[i % S], state,
+                                         scale=inp["scale"], out=o, state_v_first=state_v_first)
+    warm_device(step, warm_seconds)
     for i in range(warmup):
-        sgla.recurrent_step(q[i % S], k[i % S], v[i % S], g[i % S], state, scale=inp["scale"], out=o)
+        step(i)
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(S)]
     torch.cuda.synchronize()
     for i in range(S):
         ev[i][0].record(stream)
-        sgla.recurrent_step(q[i], k[i], v[i], g[i], state, scale=inp["scale"], out=o)
+        step(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     per = sorted(a.elapsed_time(b) for a, b in ev)
     mean_ms = sum(per) / len(per)
     nbytes = 2 * N * H * K * V * 4 + N * (H * K + Hkv * (K + V)) * 2 + N * H * 4 + N * H * V * 4
     gbs = nbytes / (mean_ms * 1e-3) / 1e9
-    return {"workload": w.name, "N": N, "H": H, "K": K, "V": V, "steps": S,
+    return {"workload": w.name, "state_layout": "[V, K]" if state_v_first else "[K, V]",
+            "N": N, "H": H, "K": K, "V": V, "steps": S,
             "ms_per_step_mean": round(mean_ms, 5), "ms_per_step_median": round(per[S // 2], 5),
             "bytes_per_step": nbytes, "achieved_GBs": round(gbs, 1),
             "peak_GBs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
             "tokens_per_s": round(N / (mean_ms * 1e-3), 1),
-            "traffic": load_traffic(w.name, "recurrent_step_kernel")}
+            "traffic": None if state_v_first else load_traffic(w.name, "recurrent_step_kernel")}
 
 
 def bwd_algorithmic(inp) -> tuple[float, float]:
@@ -488,6 +490,7 @@ def main():
     }
     if not a.no_decode:
         out["decode"] = bench_decode(64, a.warmup, a.warm_seconds)
+        out["decode_state_v_first"] = bench_decode(64, a.warmup, a.warm_seconds, state_v_first=True)
     if not a.no_backward:
         out["backward"] = bench_backward(a.backward_workload, 20, a.warmup, a.warm_seconds)
     if not a.no_cpu_baseline:
