@@ -177,6 +177,24 @@ def bwd(q, k, v, do, g=None, g_gamma=None, scale=None, initial_state=None, dht=N
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, dg_gamma=dgg, dh0=_vk(dh0, state_v_first))
 
 
+def normalizer(q, k, g=None, g_gamma=None, scale=None, initial_z=None, cu_seqlens=None,
+               nthreads=None, lib=None):
+    """The running normalizer of the relinear pages (their "augmented value":
+    a column of ones appended to v): its state column is z_t = exp(g_t)
+    z_{t-1} + k_t and its output is scale * q_t . z_t.  Computed as exactly
+    that -- the forward with a single all-ones value column.
+
+    q: [B, T, H, K]; k: [B, T, Hkv, K]; initial_z: [N, H, K] or None.
+    Returns (den [B, T, H], final_z [N, H, K]), float64."""
+    k = _f64(k)
+    B, T, Hkv = k.shape[:3]
+    ones = np.ones((B, T, Hkv, 1))
+    h0 = None if initial_z is None else _f64(initial_z)[..., None]
+    o, ht = fwd(q, k, ones, g=g, g_gamma=g_gamma, scale=scale, initial_state=h0,
+                cu_seqlens=cu_seqlens, nthreads=nthreads, lib=lib)
+    return o[..., 0], ht[..., 0]
+
+
 def step(q, k, v, g, state, scale=None, g_gamma=None, nthreads=None, lib=None,
          state_v_first=False):
     """One decode step.  q: [N, H, K]; k: [N, Hkv, K]; v: [N, Hkv, V];

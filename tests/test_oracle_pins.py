@@ -484,12 +484,36 @@ def pin_state_v_first(lib, seed=15, N=2, H=2, K=3, V=4):
     return np.array_equal(s1, s2) and np.array_equal(np.swapaxes(S1, -1, -2), S2)
 
 
+def pin_normalizer(lib, seed=16, H=3, K=4, V=5):
+    """The running normalizer (relinear pages: the output of a ones column
+    appended to v is q . z).  With no gate it is scale * q_t . (k_0 + ... +
+    k_t) (closed form); with gates it equals the last output column and last
+    state column of a forward on [v, 1] bit for bit, on packed sequences with
+    an initial z."""
+    rng = np.random.default_rng(seed)
+    T = 40
+    q, k = _rand(rng, 1, T, H, K), _rand(rng, 1, T, H, K)
+    den, z = oracle.normalizer(q, k, scale=0.3, lib=lib)
+    cs = np.cumsum(k, axis=1)
+    if _rel(den, 0.3 * np.sum(q * cs, axis=-1)) > TIGHT or _rel(z[0], cs[0, -1]) > TIGHT:
+        return False
+    cu = np.array([0, 11, 11, 40], dtype=np.int64)
+    v = _rand(rng, 1, T, H, V)
+    g = logsigmoid(_rand(rng, 1, T, H))
+    z0 = _rand(rng, 3, H, K)
+    S0 = np.concatenate([_rand(rng, 3, H, K, V), z0[..., None]], axis=-1)
+    o, ht = oracle.fwd(q, k, np.concatenate([v, np.ones((1, T, H, 1))], axis=-1), g=g, scale=0.3,
+                       initial_state=S0, cu_seqlens=cu, lib=lib)
+    den, z = oracle.normalizer(q, k, g=g, scale=0.3, initial_z=z0, cu_seqlens=cu, lib=lib)
+    return np.array_equal(den, o[..., V]) and np.array_equal(z, ht[..., V])
+
+
 ALL_PINS = [pin_chunk_local_cumsum, pin_hand_example, pin_brute_force, pin_zero_gate, pin_full_forget,
             pin_split_sequence, pin_varlen_equals_per_sequence, pin_chunk_form,
             pin_gamma_is_broadcast_g, pin_retnet_closed_form, pin_invariants,
             pin_prefill_then_decode, pin_step_brute_force, pin_gqa_is_repeated_mha,
             pin_step_variants, pin_bwd_finite_differences, pin_bwd_gate_identity,
-            pin_state_v_first]
+            pin_state_v_first, pin_normalizer]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
