@@ -26,7 +26,8 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_bwd", "recurrent_step", "chunk_local_cumsum", "library_path", "lib",
+__all__ = ["chunk_fwd", "chunk_bwd", "chunk_normalizer", "recurrent_step_normalizer",
+           "recurrent_step", "chunk_local_cumsum", "library_path", "lib",
            "SglaError", "ABI_VERSION"]
 
 ABI_VERSION = 3
@@ -74,6 +75,12 @@ def _load():
     lib.sgla_chunk_bwd_workspace_size.argtypes = [pargs, vp]
     lib.sgla_chunk_bwd.restype = ctypes.c_int
     lib.sgla_chunk_bwd.argtypes = [pargs] + [vp] * 15 + [vp, sz, vp]
+    lib.sgla_chunk_normalizer_workspace_size.restype = sz
+    lib.sgla_chunk_normalizer_workspace_size.argtypes = [pargs, vp]
+    lib.sgla_chunk_normalizer.restype = ctypes.c_int
+    lib.sgla_chunk_normalizer.argtypes = [pargs] + [vp] * 9 + [sz, vp]
+    lib.sgla_recurrent_step_normalizer.restype = ctypes.c_int
+    lib.sgla_recurrent_step_normalizer.argtypes = [i32, i32, i32, i32, f32, i32] + [vp] * 7
     lib.sgla_chunk_local_cumsum.restype = ctypes.c_int
     lib.sgla_chunk_local_cumsum.argtypes = [pargs, vp, vp, vp, vp, sz, vp]
     lib.sgla_recurrent_step.restype = ctypes.c_int
@@ -272,6 +279,75 @@ def chunk_bwd(q, k, v, do, g=None, g_gamma=None, scale=None, initial_state=None,
     if st != _OK:
         _raise(st, "sgla_chunk_bwd")
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, dg_gamma=dgg, dh0=dh0)
+
+
+def chunk_normalizer(q, k, g=None, g_gamma=None, scale=None, initial_z=None,
+                     output_final_state=False, cu_seqlens=None, chunk_size=64):
+    """Running normalizer den_t = scale * q_t . z_t, z_t = exp(g_t) z_{t-1} +
+    k_t (the ones column of the relinear pages' augmented value).  q [B, T,
+    H, K], k [B, T, Hkv, K]; initial_z [N, H, K] float32 or None.  Returns
+    (den [B, T, H] float32, final_z [N, H, K] float32 or None)."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor [B, T, H, K]")
+    dev = q.device
+    B, T, H, K = q.shape
+    Hkv = _kv_heads(k, H, 2)
+    qkv = _dtype_code(q.dtype, "q")
+    _check_dev("q", q, dev)
+    _check_dev("k", k, dev, q.dtype, (B, T, Hkv, K))
+    if g is not None and g_gamma is not None:
+        raise ValueError("g and g_gamma are mutually exclusive; pass at most one")
+    _check_dev("g", g, dev, torch.float32, (B, T, H))
+    _check_dev("g_gamma", g_gamma, dev, torch.float32, (H,))
+    cu = _host_cu(cu_seqlens)
+    N = B if cu is None else cu.numel() - 1
+    if cu is not None and B != 1:
+        raise ValueError(f"packed input (cu_seqlens) requires B == 1, got B={B}")
+    _check_dev("initial_z", initial_z, dev, torch.float32, (N, H, K))
+    if scale is None:
+        scale = K ** -0.5
+    args = _chunk_args(B, T, H, K, 0, N, chunk_size, qkv, _F32, scale, output_final_state, Hkv)
+    cu_ptr = None if cu is None else ctypes.c_void_p(cu.data_ptr())
+    n = lib.sgla_chunk_normalizer_workspace_size(ctypes.byref(args), cu_ptr)
+    if n == 0 and lib.sgla_last_error():
+        raise ValueError(f"sgla_chunk_normalizer_workspace_size: "
+                         f"{lib.sgla_last_error().decode(errors='replace')}")
+    den = torch.empty((B, T, H), device=dev, dtype=torch.float32)
+    zt = torch.empty((N, H, K), device=dev, dtype=torch.float32) if output_final_state else None
+    ws = torch.empty(max(n, 1), device=dev, dtype=torch.uint8)
+    st = lib.sgla_chunk_normalizer(ctypes.byref(args), _ptr(q), _ptr(k), _ptr(g), _ptr(g_gamma),
+                                   _ptr(initial_z), cu_ptr, _ptr(den), _ptr(zt), _ptr(ws), n,
+                                   _stream(dev))
+    if st != _OK:
+        _raise(st, "sgla_chunk_normalizer")
+    return den, zt
+
+
+def recurrent_step_normalizer(q, k, g, z, scale=None, g_gamma=None):
+    """One decode step of the running normalizer; ``z`` [N, H, K] float32 is
+    updated in place.  q [N, H, K], k [N, Hkv, K]; g [N, H] or None, g_gamma
+    [H] or None.  Returns den [N, H] float32."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a 3-D tensor [N, H, K]")
+    dev = q.device
+    N, H, K = q.shape
+    Hkv = _kv_heads(k, H, 1)
+    qkv = _dtype_code(q.dtype, "q")
+    _check_dev("q", q, dev)
+    _check_dev("k", k, dev, q.dtype, (N, Hkv, K))
+    if g is not None and g_gamma is not None:
+        raise ValueError("g and g_gamma are mutually exclusive; pass at most one")
+    _check_dev("g", g, dev, torch.float32, (N, H))
+    _check_dev("g_gamma", g_gamma, dev, torch.float32, (H,))
+    _check_dev("z", z, dev, torch.float32, (N, H, K))
+    if scale is None:
+        scale = K ** -0.5
+    den = torch.empty((N, H), device=dev, dtype=torch.float32)
+    st = lib.sgla_recurrent_step_normalizer(N, H, Hkv, K, float(scale), qkv, _ptr(q), _ptr(k), _ptr(g),
+                                            _ptr(g_gamma), _ptr(z), _ptr(den), _stream(dev))
+    if st != _OK:
+        _raise(st, "sgla_recurrent_step_normalizer")
+    return den
 
 
 def chunk_local_cumsum(g, chunk_size=64, cu_seqlens=None):

@@ -385,6 +385,94 @@ sgla_status sgla_chunk_bwd(const sgla_chunk_args* args, const void* q, const voi
   return ok();
 }
 
+size_t sgla_chunk_normalizer_workspace_size(const sgla_chunk_args* args, const int64_t* cu_seqlens_host) {
+  Plan P;
+  if (plan_shape(args, cu_seqlens_host, false, &P) != SGLA_OK) return 0;
+  g_last_error.clear();
+  return P.total_bytes;
+}
+
+sgla_status sgla_chunk_normalizer(const sgla_chunk_args* args, const void* q, const void* k, const float* g,
+                                  const float* g_gamma, const float* initial_z, const int64_t* cu_seqlens_host,
+                                  float* den, float* final_z, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  Plan P;
+  sgla_status st = plan_shape(args, cu_seqlens_host, false, &P);
+  if (st != SGLA_OK) return st;
+  const sgla_chunk_args& a = *args;
+  if (a.qkv_dtype != SGLA_BF16 && a.qkv_dtype != SGLA_F32)
+    return fail(SGLA_ERR_DTYPE, "qkv_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", a.qkv_dtype);
+  if (!(a.K == 16 || a.K == 32 || a.K == 64 || a.K == 128 || a.K == 256))
+    return fail(SGLA_ERR_UNSUPPORTED, "the normalizer supports K in {16,32,64,128,256} (got %d)", a.K);
+  if (!std::isfinite(a.scale)) return fail(SGLA_ERR_INVALID_ARG, "scale must be finite");
+  if (g != nullptr && g_gamma != nullptr)
+    return fail(SGLA_ERR_INVALID_ARG, "g and g_gamma are mutually exclusive; pass at most one");
+  const bool any_tokens = P.total_tokens > 0;
+  if (any_tokens && (q == nullptr || k == nullptr || den == nullptr))
+    return fail(SGLA_ERR_INVALID_ARG, "q, k and den must be non-NULL");
+  if (a.output_final_state && final_z == nullptr)
+    return fail(SGLA_ERR_INVALID_ARG, "output_final_state is set but final_z is NULL");
+  if (any_tokens && !(aligned(q, 16) && aligned(k, 16)))
+    return fail(SGLA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  if (P.packed && (workspace == nullptr || workspace_bytes < P.total_bytes))
+    return fail(SGLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", P.total_bytes, workspace_bytes);
+  char* ws = static_cast<char*>(workspace);
+  st = upload_tables(P, ws, stream);
+  if (st != SGLA_OK) return st;
+  sgla::NormalizerParams p;
+  p.q = q;
+  p.k = k;
+  p.g = g;
+  p.g_gamma = g_gamma;
+  p.z0 = initial_z;
+  p.den = den;
+  p.zt = a.output_final_state ? final_z : nullptr;
+  p.scale = a.scale;
+  p.H = a.H;
+  p.Hkv = P.Hkv;
+  p.K = a.K;
+  p.qkv_bf16 = a.qkv_dtype == SGLA_BF16;
+  p.seqs = layout_of(args, P, ws);
+  hipError_t e = sgla::launch_chunk_normalizer(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "launching the normalizer kernel");
+  return ok();
+}
+
+sgla_status sgla_recurrent_step_normalizer(int32_t N, int32_t H, int32_t num_kv_heads, int32_t K, float scale,
+                                           int32_t qkv_dtype, const void* q, const void* k, const float* g,
+                                           const float* g_gamma, float* z, float* den, hipStream_t stream) {
+  if (N < 0 || H <= 0) return fail(SGLA_ERR_SHAPE, "N must be >= 0 and H > 0 (got N=%d H=%d)", N, H);
+  const int32_t Hkv = num_kv_heads == 0 ? H : num_kv_heads;
+  if (Hkv < 0 || H % Hkv != 0)
+    return fail(SGLA_ERR_SHAPE, "num_kv_heads must divide H (got num_kv_heads=%d, H=%d)", num_kv_heads, H);
+  if ((int64_t)N * H > INT32_MAX) return fail(SGLA_ERR_UNSUPPORTED, "N*H exceeds 2^31-1");
+  if (K < 1 || K > 4096) return fail(SGLA_ERR_UNSUPPORTED, "the normalizer step supports 1 <= K <= 4096 (got %d)", K);
+  if (qkv_dtype != SGLA_BF16 && qkv_dtype != SGLA_F32)
+    return fail(SGLA_ERR_DTYPE, "qkv_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", qkv_dtype);
+  if (!std::isfinite(scale)) return fail(SGLA_ERR_INVALID_ARG, "scale must be finite");
+  if (g != nullptr && g_gamma != nullptr)
+    return fail(SGLA_ERR_INVALID_ARG, "g and g_gamma are mutually exclusive; pass at most one");
+  if (N == 0) return ok();
+  if (q == nullptr || k == nullptr || z == nullptr || den == nullptr)
+    return fail(SGLA_ERR_INVALID_ARG, "q, k, z and den must be non-NULL");
+  sgla::StepNormalizerParams p;
+  p.q = q;
+  p.k = k;
+  p.g = g;
+  p.g_gamma = g_gamma;
+  p.z = z;
+  p.den = den;
+  p.scale = scale;
+  p.N = N;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.K = K;
+  p.qkv_bf16 = qkv_dtype == SGLA_BF16;
+  hipError_t e = sgla::launch_step_normalizer(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "launching the normalizer step kernel");
+  return ok();
+}
+
 sgla_status sgla_chunk_local_cumsum(const sgla_chunk_args* args, const float* g, const int64_t* cu_seqlens_host,
                                     float* gc, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Plan P;

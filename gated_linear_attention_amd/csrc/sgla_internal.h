@@ -136,6 +136,37 @@ struct ChunkBwdParams {
 
 hipError_t launch_chunk_bwd(const ChunkBwdParams& p, hipStream_t stream);
 
+// Running normalizer (the ones column of the augmented value): den [T_total,
+// H] = scale q . z, z [N, H, K] carried from z0 to zt.
+struct NormalizerParams {
+  const void* q;
+  const void* k;
+  const float* g;
+  const float* g_gamma;
+  const float* z0;           // [N, H, K] or nullptr
+  float* den;                // [T_total, H]
+  float* zt;                 // [N, H, K] or nullptr
+  float scale;
+  int32_t H, Hkv, K;
+  int32_t qkv_bf16;
+  SeqLayout seqs;
+};
+
+struct StepNormalizerParams {
+  const void* q;             // [N, H, K]
+  const void* k;             // [N, Hkv, K]
+  const float* g;            // [N, H] or nullptr
+  const float* g_gamma;      // [H] or nullptr
+  float* z;                  // [N, H, K], in place
+  float* den;                // [N, H]
+  float scale;
+  int32_t N, H, Hkv, K;
+  int32_t qkv_bf16;
+};
+
+hipError_t launch_chunk_normalizer(const NormalizerParams& p, hipStream_t stream);
+hipError_t launch_step_normalizer(const StepNormalizerParams& p, hipStream_t stream);
+
 struct StepParams {
   const void* q;
   const void* k;

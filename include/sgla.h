@@ -196,6 +196,49 @@ sgla_status sgla_chunk_bwd(const sgla_chunk_args *args,
                            hipStream_t stream);
 
 /*
+ * Running normalizer of normalized linear attention (page "relinear": the
+ * output divided by q . z, which the pages obtain by appending a column of
+ * ones to v -- its state column is z and its output the normalizer):
+ *     z_t = exp(g_t) z_{t-1} + k_t ,    den_t = scale * q_t . z_t
+ * per sequence and query head, computed on its own (no widening of V).
+ * Together with sgla_chunk_fwd it gives o_t / den_t.
+ *
+ * Arguments (device pointers unless stated):
+ *   args            B, T, H, K, num_seqs, chunk_size, qkv_dtype, scale,
+ *                   num_kv_heads and output_final_state are read; V, o_dtype
+ *                   and state_v_first are not.
+ *   q               [B, T, H, K];  k [B, T, Hkv, K] in qkv_dtype
+ *   g, g_gamma      as for sgla_chunk_fwd (at most one; neither = no decay)
+ *   initial_z       [N, H, K] float32, or NULL for zeros
+ *   cu_seqlens_host as for sgla_chunk_fwd
+ *   den             [B, T, H] float32 output
+ *   final_z         [N, H, K] float32, written when output_final_state is
+ *                   nonzero (may alias initial_z exactly)
+ *   workspace       >= sgla_chunk_normalizer_workspace_size(args, cu) bytes
+ *                   (the packed-sequence table; 0 for dense input)
+ * Supported: K in {16, 32, 64, 128, 256}, bf16 or float32 inputs.
+ */
+size_t sgla_chunk_normalizer_workspace_size(const sgla_chunk_args *args, const int64_t *cu_seqlens_host);
+sgla_status sgla_chunk_normalizer(const sgla_chunk_args *args, const void *q, const void *k,
+                                  const float *g, const float *g_gamma, const float *initial_z,
+                                  const int64_t *cu_seqlens_host, float *den, float *final_z,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One decode step of the running normalizer, in place (the decode side of
+ * sgla_chunk_normalizer, beside sgla_recurrent_step):
+ *     z <- exp(g) z + k ;   den = scale * q . z
+ *   q [N, H, K], k [N, Hkv, K] in qkv_dtype; g [N, H] or g_gamma [H] (at
+ *   most one); z [N, H, K] float32 in place; den [N, H] float32.
+ * Supported: 1 <= K <= 4096.
+ */
+sgla_status sgla_recurrent_step_normalizer(int32_t N, int32_t H, int32_t num_kv_heads, int32_t K,
+                                           float scale, int32_t qkv_dtype,
+                                           const void *q, const void *k,
+                                           const float *g, const float *g_gamma,
+                                           float *z, float *den, hipStream_t stream);
+
+/*
  * Step (1) alone: chunk-local inclusive cumulative sum of g times 1/ln 2,
  * restarting at every chunk_size-token chunk of every sequence (section 三,
  * the chunk_local_cumsum call with the RCP_LN2 scale).  g and gc are device

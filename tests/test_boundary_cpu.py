@@ -316,3 +316,50 @@ def test_chunk_bwd_workspace_size(G):
     tasks = 2 * 3 * 3
     rec = tasks * 64 * 96 * 4
     assert n == 2 * rec + ((tasks * 4 + 255) // 256) * 256
+
+
+NORM_CASES = [
+    ("K=512", dict(K=512), {}, UNSUPPORTED, "K in"),
+    ("K=48", dict(K=48), {}, UNSUPPORTED, "K in"),
+    ("both gates", {}, dict(gg=True), INVALID, "mutually exclusive"),
+    ("fp16", dict(qkv=3), {}, DTYPE, "qkv_dtype"),
+    ("kv heads not dividing", dict(H=2, Hkv=3), {}, SHAPE, "num_kv_heads"),
+    ("final without pointer", {}, dict(zt=None), INVALID, "final_z is NULL"),
+    ("workspace small", dict(N=2), dict(cu=[0, 64, 128], ws_bytes=8), WORKSPACE, "workspace"),
+]
+
+
+@pytest.mark.parametrize("desc,aover,cover,status,frag", NORM_CASES, ids=[c[0] for c in NORM_CASES])
+def test_chunk_normalizer_rejects_without_writing(G, desc, aover, cover, status, frag):
+    b = Buffers()
+    args = mkargs(G, **aover)
+    cu = cover.get("cu")
+    cu_arr = None if cu is None else np.asarray(cu, dtype=np.int64)
+    ptrs = dict(q=b.p("q"), k=b.p("k"), g=b.p("g"), gg=b.p("gg") if cover.get("gg") else None,
+                z0=b.p("h0"), den=b.p("dg"), zt=b.p("ht"), ws=b.p("ws"))
+    if "zt" in cover:
+        ptrs["zt"] = cover["zt"]
+    st = G.lib.sgla_chunk_normalizer(
+        ctypes.byref(args), ptrs["q"], ptrs["k"], ptrs["g"], ptrs["gg"], ptrs["z0"],
+        None if cu_arr is None else ctypes.c_void_p(cu_arr.ctypes.data), ptrs["den"], ptrs["zt"],
+        ptrs["ws"], cover.get("ws_bytes", 1 << 22), None)
+    msg = G.lib.sgla_last_error().decode()
+    assert st == status, (st, msg)
+    assert frag in msg, msg
+    assert b.unchanged()
+
+
+def test_step_normalizer_rejects_without_writing(G):
+    b = Buffers(B=1, T=4, H=2, K=64, V=64, N=4)
+    cases = [(dict(K=0), UNSUPPORTED), (dict(K=5000), UNSUPPORTED), (dict(qkv=3), DTYPE),
+             (dict(gg="gg"), INVALID), (dict(Hkv=3), SHAPE), (dict(z=None), INVALID)]
+    for over, status in cases:
+        kw = dict(N=4, H=2, Hkv=0, K=64, scale=0.125, qkv=BF16, q=b.p("q"), k=b.p("k"), g=b.p("g"),
+                  gg=None, z=b.p("h0"), den=b.p("dg"))
+        for key, val in over.items():
+            kw[key] = b.p("gg") if val == "gg" else val
+        st = G.lib.sgla_recurrent_step_normalizer(kw["N"], kw["H"], kw["Hkv"], kw["K"], kw["scale"],
+                                                  kw["qkv"], kw["q"], kw["k"], kw["g"], kw["gg"],
+                                                  kw["z"], kw["den"], None)
+        assert st == status, (over, st, G.lib.sgla_last_error())
+        assert b.unchanged()

@@ -1,0 +1,91 @@
+"""GPU parity of the running normalizer (sgla_chunk_normalizer and
+sgla_recurrent_step_normalizer) against the oracle: the output of a ones
+column appended to v (page "relinear": the normalizer q . z of normalized
+linear attention via the augmented value).  Inputs are used exactly and the
+recurrence runs in fp32, so both dtypes are held to the float32 bar (1e-4);
+the cross-check against the augmented forward uses the bf16 bar."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gla_workloads import ChunkWorkload, DecodeWorkload, make_chunk_inputs, make_decode_inputs
+from gpu_common import TOL_BF16, TOL_F32, device_inputs, err_ratio, to_dev
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+if torch.cuda.is_available():
+    import gated_linear_attention_amd as sgla
+else:  # pragma: no cover - collected on CPU-only hosts, never run
+    sgla = None
+
+
+def small(name, **kw):
+    base = dict(B=2, T=150, H=2, K=64, V=64, dtype="bf16", gate="g", seed=51)
+    base.update(kw)
+    return ChunkWorkload(name, **base)
+
+
+CASES = [
+    small("k64"),
+    small("k16_f32", K=16, dtype="f32", T=97),
+    small("k128_gamma_h0", K=128, gate="gamma", initial_state=True, normalize_k=True, T=300),
+    small("k256_no_gate", K=256, gate="none", T=129),
+    small("k32_varlen", B=1, T=0, K=32, fixed_lengths=(15, 0, 1, 64, 200), initial_state=True),
+    small("gqa_k64", H=6, Hkv=2, K=64, T=140, initial_state=True),
+    small("empty", T=0, initial_state=True),
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_chunk_normalizer(w):
+    inp = make_chunk_inputs(w)
+    d = device_inputs(inp)
+    rng = np.random.default_rng(w.seed + 7)
+    z0 = (rng.standard_normal((inp["N"], inp["H"], inp["K"])).astype(np.float32)
+          if inp["initial_state"] is not None else None)
+    den, zt = sgla.chunk_normalizer(d["q"], d["k"], g=d["g"], g_gamma=d["g_gamma"], scale=inp["scale"],
+                                    initial_z=to_dev(z0, torch.float32), output_final_state=True,
+                                    cu_seqlens=inp["cu_seqlens"])
+    torch.cuda.synchronize()
+    den_ref, z_ref = oracle.normalizer(inp["q"], inp["k"], g=inp["g"], g_gamma=inp["g_gamma"],
+                                       scale=inp["scale"], initial_z=z0, cu_seqlens=inp["cu_seqlens"])
+    assert err_ratio(den.cpu().numpy(), den_ref) <= TOL_F32
+    assert err_ratio(zt.cpu().numpy(), z_ref) <= TOL_F32
+
+
+def test_normalizer_is_the_ones_column_of_the_augmented_forward():
+    """chunk_fwd on v extended by a ones column (padded to the kernel's V
+    granularity with zero columns) gives the normalizer in that column."""
+    inp = make_chunk_inputs(small("aug", B=1, T=0, K=64, V=64, fixed_lengths=(200, 70)))
+    d = device_inputs(inp)
+    T = inp["T"]
+    extra = np.zeros((1, T, 2, 64), dtype=np.float32)
+    extra[..., 0] = 1.0
+    v_aug = to_dev(np.concatenate([inp["v"], extra], axis=-1), torch.bfloat16)
+    o, _ = sgla.chunk_fwd(d["q"], d["k"], v_aug, g=d["g"], scale=inp["scale"], cu_seqlens=inp["cu_seqlens"])
+    den, _ = sgla.chunk_normalizer(d["q"], d["k"], g=d["g"], scale=inp["scale"], cu_seqlens=inp["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert err_ratio(o[..., 64].cpu().numpy(), den.cpu().numpy()) <= TOL_BF16
+
+
+@pytest.mark.parametrize("gate,Hkv,K", [("g", 4, 128), ("gamma", 2, 64), ("none", 1, 100)])
+def test_step_normalizer(gate, Hkv, K):
+    w = DecodeWorkload("nrm", N=5, H=4, K=K, V=32, steps=3, Hkv=Hkv, gate=gate, seed=K)
+    inp = make_decode_inputs(w)
+    rng = np.random.default_rng(2)
+    z_np = rng.standard_normal((5, 4, K)).astype(np.float32)
+    z = to_dev(z_np, torch.float32)
+    z_ref = z_np.astype(np.float64)
+    gg = to_dev(inp["g_gamma"], torch.float32)
+    for s in range(inp["steps"]):
+        g = None if inp["g"] is None else inp["g"][s]
+        den = sgla.recurrent_step_normalizer(to_dev(inp["q"][s], torch.bfloat16), to_dev(inp["k"][s], torch.bfloat16),
+                                             to_dev(g, torch.float32), z, scale=inp["scale"], g_gamma=gg)
+        den_ref, z_ref = oracle.normalizer(inp["q"][s][:, None], inp["k"][s][:, None],
+                                           g=None if g is None else g[:, None], g_gamma=inp["g_gamma"],
+                                           scale=inp["scale"], initial_z=z_ref)
+        torch.cuda.synchronize()
+        assert err_ratio(den.cpu().numpy(), den_ref[:, 0]) <= TOL_F32
+    assert err_ratio(z.cpu().numpy(), z_ref) <= TOL_F32
