@@ -27,6 +27,7 @@ The JSON line also carries:
   backward      -- sgla_chunk_bwd on the packed K = V = 128 workload (dq, dk,
                    dv, dg, dh0), against the fp32 matrix-core peak its kernels
                    run on;
+  normalizer    -- sgla_chunk_normalizer on the same workload, HBM GB/s;
   cpu_baseline  -- the fp64 CPU oracle timed on the host cores on whole
                    batches of the same workload (a reported baseline only).
 
@@ -361,6 +362,49 @@ def bench_backward(workload: str, steps: int, warmup: int, warm_seconds: float):
             "hbm": {"achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
+def bench_normalizer(workload: str, steps: int, warmup: int, warm_seconds: float):
+    """sgla_chunk_normalizer on a chunked workload: q and k read once, g read
+    once, den written once (fp32), final z written -- an HBM stream."""
+    import numpy as np
+    import torch
+
+    import gated_linear_attention_amd as sgla
+    from gla_workloads import CHUNK_CONFIGS, make_chunk_inputs
+
+    w = CHUNK_CONFIGS[workload]
+    inp = make_chunk_inputs(w)
+    dev = torch.device("cuda:0")
+    qdt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+    t = lambda a, dt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+    q, k = t(inp["q"], qdt), t(inp["k"], qdt)
+    g, gg = t(inp["g"], torch.float32), t(inp["g_gamma"], torch.float32)
+    step = lambda _i: sgla.chunk_normalizer(q, k, g=g, g_gamma=gg, scale=inp["scale"],
+                                            output_final_state=True, cu_seqlens=inp["cu_seqlens"])
+    warm_device(step, warm_seconds)
+    for i in range(warmup):
+        step(i)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    ms = sum(per) / len(per)
+    B, T, H, K, N, Hkv = inp["B"], inp["T"], inp["H"], inp["K"], inp["N"], inp["Hkv"]
+    esz = 2 if inp["dtype"] == "bf16" else 4
+    nbytes = B * T * ((H + Hkv) * K * esz + H * 4 + (H * 4 if g is not None else 0)) + N * H * K * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": workload, "kernel": "chunk_normalizer_kernel", "ms_per_call_mean": round(ms, 5),
+            "ms_per_call_median": round(per[len(per) // 2], 5), "algorithmic_bytes_per_call": int(nbytes),
+            "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
 def cpu_baseline(inp, min_seconds: float = 10.0):
     """The fp64 CPU oracle on whole batches of the timed workload, repeated
     until at least ``min_seconds`` of wall time (a bounded sample)."""
@@ -493,6 +537,7 @@ def main():
         out["decode_state_v_first"] = bench_decode(64, a.warmup, a.warm_seconds, state_v_first=True)
     if not a.no_backward:
         out["backward"] = bench_backward(a.backward_workload, 20, a.warmup, a.warm_seconds)
+        out["normalizer"] = bench_normalizer(a.backward_workload, 20, a.warmup, a.warm_seconds)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)
