@@ -48,6 +48,9 @@ def _bind(lib):
     lib.sgla_oracle_bwd.restype = ctypes.c_int
     lib.sgla_oracle_bwd.argtypes = ([ctypes.c_int] * 5 + [dp] * 5 + [ctypes.c_double, dp, lp, ctypes.c_int]
                                     + [dp] * 8 + [ctypes.c_int])
+    lib.sgla_oracle_gla_fwd.restype = ctypes.c_int
+    lib.sgla_oracle_gla_fwd.argtypes = ([ctypes.c_int] * 6 + [dp] * 4 + [ctypes.c_double, dp, lp, ctypes.c_int]
+                                        + [dp] * 2 + [ctypes.c_int])
     lib.sgla_oracle_step.restype = ctypes.c_int
     lib.sgla_oracle_step.argtypes = [ctypes.c_int] * 5 + [dp] * 5 + [ctypes.c_double, dp, dp,
                                                                      ctypes.c_int]
@@ -175,6 +178,36 @@ def bwd(q, k, v, do, g=None, g_gamma=None, scale=None, initial_state=None, dht=N
     if rc != 0:
         raise ValueError(f"sgla_oracle_bwd rejected its arguments (code {rc})")
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, dg_gamma=dgg, dh0=_vk(dh0, state_v_first))
+
+
+def gla_fwd(q, k, v, gk, scale=None, initial_state=None, cu_seqlens=None, output_final_state=True,
+            nthreads=None, lib=None):
+    """Elementwise-gate GLA, token by token: S_t = diag(exp(gk_t)) S_{t-1} +
+    k_t v_t^T, o_t = scale S_t^T q_t.  q, gk: [B, T, H, K]; k: [B, T, Hkv, K];
+    v: [B, T, Hkv, V]; initial_state [N, H, K, V] or None; cu_seqlens as for
+    fwd.  Returns (o [B, T, H, V], final_state [N, H, K, V] or None)."""
+    q, k, v, gk = _f64(q), _f64(k), _f64(v), _f64(gk)
+    B, T, H, K = q.shape
+    Hkv = k.shape[2]
+    V = v.shape[-1]
+    if scale is None:
+        scale = K ** -0.5
+    h0 = _f64(initial_state)
+    cu = None
+    N = B
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N = cu.shape[0] - 1
+    o = np.zeros((B, T, H, V))
+    ht = np.zeros((N, H, K, V)) if output_final_state else None
+    lib = lib or load()
+    rc = lib.sgla_oracle_gla_fwd(B, T, H, Hkv, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(gk), float(scale),
+                                 _ptr(h0),
+                                 None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                 N, _ptr(o), _ptr(ht), int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"sgla_oracle_gla_fwd rejected its arguments (code {rc})")
+    return o, ht
 
 
 def normalizer(q, k, g=None, g_gamma=None, scale=None, initial_z=None, cu_seqlens=None,

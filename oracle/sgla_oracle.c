@@ -539,3 +539,129 @@ int sgla_oracle_bwd(int B, int T, int H, int K, int V,
     free(part);
     return rc;
 }
+
+/*
+ * Elementwise-gate GLA (the general GLA the Simple GLA page contrasts with:
+ * its gate decays every state element independently; the relinear pages pass
+ * fla's chunk_gla a gate vector over the key dimension, of which the
+ * head-wise scalar gate is the special case):
+ *
+ *     S_t = diag(exp(gk_t)) S_{t-1} + k_t v_t^T ,    o_t = scale * S_t^T q_t
+ *
+ * with gk_t a log gate per (token, head, key): row a of the state decays by
+ * exp(gk_t[a]).
+ *   q, gk : [B, T, H, K]   k : [B, T, Hkv, K]   v : [B, T, Hkv, V]
+ *   o : [B, T, H, V]   h0, ht : [N, H, K, V] or NULL; cu_seqlens as above.
+ */
+typedef struct {
+    int H, Hkv, K, V;
+    const double *q, *k, *v, *gk, *h0;
+    double scale;
+    double *o, *ht;
+    const unit_t *units;
+    int64_t n_units, next;
+    pthread_mutex_t mu;
+} gla_job_t;
+
+static void *gla_worker(void *arg)
+{
+    gla_job_t *J = (gla_job_t *)arg;
+    const int H = J->H, Hkv = J->Hkv, K = J->K, V = J->V;
+    double *S = (double *)malloc((size_t)K * V * sizeof(double));
+    if (!S) return (void *)1;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int64_t i = J->next++;
+        pthread_mutex_unlock(&J->mu);
+        if (i >= J->n_units) break;
+        const unit_t *u = &J->units[i];
+        const int h = u->head;
+#if SGLA_ORACLE_MUTANT == 13
+        const int hk = h % Hkv;
+#else
+        const int hk = h / (H / Hkv);
+#endif
+        const double *h0 = J->h0 ? J->h0 + ((size_t)u->seq * H + h) * K * V : NULL;
+        for (int64_t e = 0; e < (int64_t)K * V; ++e) S[e] = h0 ? h0[e] : 0.0;
+        for (int64_t s = 0; s < u->len; ++s) {
+            const int64_t t = u->bos + s;
+            const double *qt = J->q + ((size_t)t * H + h) * K;
+            const double *gt = J->gk + ((size_t)t * H + h) * K;
+            const double *kt = J->k + ((size_t)t * Hkv + hk) * K;
+            const double *vt = J->v + ((size_t)t * Hkv + hk) * V;
+            for (int a = 0; a < K; ++a) {
+                const double decay = exp(gt[a]);
+                for (int b = 0; b < V; ++b) {
+#if SGLA_ORACLE_MUTANT == 14
+                    /* planted: gate indexed by the value column */
+                    S[(int64_t)a * V + b] = exp(gt[b % K]) * S[(int64_t)a * V + b] + kt[a] * vt[b];
+#else
+                    S[(int64_t)a * V + b] = decay * S[(int64_t)a * V + b] + kt[a] * vt[b];
+#endif
+                }
+            }
+            double *ot = J->o + ((size_t)t * H + h) * V;
+            for (int b = 0; b < V; ++b) {
+                double acc = 0.0;
+                for (int a = 0; a < K; ++a) acc += S[(int64_t)a * V + b] * qt[a];
+                ot[b] = J->scale * acc;
+            }
+        }
+        if (J->ht) {
+            double *ht = J->ht + ((size_t)u->seq * H + h) * K * V;
+            for (int64_t e = 0; e < (int64_t)K * V; ++e) ht[e] = S[e];
+        }
+    }
+    free(S);
+    return NULL;
+}
+
+int sgla_oracle_gla_fwd(int B, int T, int H, int Hkv, int K, int V,
+                        const double *q, const double *k, const double *v, const double *gk,
+                        double scale, const double *h0, const int64_t *cu_seqlens, int num_seqs,
+                        double *o, double *ht, int nthreads)
+{
+    if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0 || !gk) return -1;
+    if (Hkv <= 0 || H % Hkv != 0) return -6;
+    if (cu_seqlens && B != 1) return -3;
+    int N = cu_seqlens ? num_seqs : B;
+    if (N < 0) return -1;
+    int64_t n_units = (int64_t)N * H;
+    unit_t *units = (unit_t *)malloc((size_t)(n_units > 0 ? n_units : 1) * sizeof(unit_t));
+    if (!units) return -4;
+    for (int n = 0; n < N; ++n) {
+        int64_t bos, len;
+        if (cu_seqlens) {
+            bos = cu_seqlens[n];
+            len = cu_seqlens[n + 1] - cu_seqlens[n];
+            if (len < 0 || bos < 0 || cu_seqlens[n + 1] > (int64_t)T) { free(units); return -5; }
+        } else {
+            bos = (int64_t)n * T;
+            len = T;
+        }
+        for (int hh = 0; hh < H; ++hh) {
+            unit_t *u = &units[(int64_t)n * H + hh];
+            u->bos = bos; u->len = len; u->seq = n; u->head = hh;
+        }
+    }
+    gla_job_t J;
+    J.H = H; J.Hkv = Hkv; J.K = K; J.V = V;
+    J.q = q; J.k = k; J.v = v; J.gk = gk; J.h0 = h0; J.scale = scale; J.o = o; J.ht = ht;
+    J.units = units; J.n_units = n_units; J.next = 0;
+    pthread_mutex_init(&J.mu, NULL);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    int started = 0, rc = 0;
+    for (int i = 1; i < nthreads; ++i)
+        if (pthread_create(&th[started], NULL, gla_worker, &J) == 0) ++started;
+    if (gla_worker(&J) != NULL) rc = -4;
+    for (int i = 0; i < started; ++i) {
+        void *r = NULL;
+        pthread_join(th[i], &r);
+        if (r != NULL) rc = -4;
+    }
+    pthread_mutex_destroy(&J.mu);
+    free(units);
+    return rc;
+}

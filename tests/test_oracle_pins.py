@@ -508,12 +508,55 @@ def pin_normalizer(lib, seed=16, H=3, K=4, V=5):
     return np.array_equal(den, o[..., V]) and np.array_equal(z, ht[..., V])
 
 
+def pin_gla_scalar_gate_is_simple_gla(lib, seed=17, H=4, Hkv=2, K=3, V=5):
+    """Elementwise-gate GLA with every key's gate equal to the head's scalar
+    gate is Simple GLA (the pages: the head-wise gate is the special case of
+    the key-vector gate), bit for bit, on packed sequences with grouped kv
+    heads and an initial state."""
+    rng = np.random.default_rng(seed)
+    cu = np.array([0, 9, 9, 50], dtype=np.int64)
+    T = 50
+    q, k, v = _rand(rng, 1, T, H, K), _rand(rng, 1, T, Hkv, K), _rand(rng, 1, T, Hkv, V)
+    g = logsigmoid(_rand(rng, 1, T, H))
+    S0 = _rand(rng, 3, H, K, V)
+    o1, h1 = oracle.fwd(q, k, v, g=g, scale=0.4, initial_state=S0, cu_seqlens=cu, lib=lib)
+    gk = np.repeat(g[..., None], K, axis=-1)
+    o2, h2 = oracle.gla_fwd(q, k, v, gk, scale=0.4, initial_state=S0, cu_seqlens=cu, lib=lib)
+    return np.array_equal(o1, o2) and np.array_equal(h1, h2)
+
+
+def pin_gla_brute_force(lib, seed=18, T=60, H=2, K=4, V=3):
+    """Elementwise-gate GLA against its explicit attention form (one sequence):
+    o_t = scale [ sum_{j<=t} sum_a q_t[a] k_j[a] exp(G_t[a] - G_j[a]) v_j
+                  + sum_a q_t[a] exp(G_t[a]) S0[a, :] ],  G = cumsum of gk
+    (different gates on different keys, so a gate applied to the wrong index
+    changes the result)."""
+    rng = np.random.default_rng(seed)
+    q, k, v = _rand(rng, 1, T, H, K), _rand(rng, 1, T, H, K), _rand(rng, 1, T, H, V)
+    gk = logsigmoid(_rand(rng, 1, T, H, K)) * np.linspace(0.2, 2.0, K)
+    S0 = _rand(rng, 1, H, K, V)
+    o, ht = oracle.gla_fwd(q, k, v, gk, scale=0.6, initial_state=S0, lib=lib)
+    for h in range(H):
+        G = np.cumsum(gk[0, :, h], axis=0)                        # [T, K]
+        for t in range(T):
+            w = np.exp(G[t][None, :] - G[: t + 1]) * q[0, t, h][None, :] * k[0, : t + 1, h]   # [t+1, K]
+            ref = w.sum(axis=1) @ v[0, : t + 1, h] + (q[0, t, h] * np.exp(G[t])) @ S0[0, h]
+            if _rel(o[0, t, h], 0.6 * ref) > 1e-11:
+                return False
+        Sref = np.exp(G[-1])[:, None] * S0[0, h] + sum(
+            np.exp(G[-1] - G[j])[:, None] * np.outer(k[0, j, h], v[0, j, h]) for j in range(T))
+        if _rel(ht[0, h], Sref) > 1e-11:
+            return False
+    return True
+
+
 ALL_PINS = [pin_chunk_local_cumsum, pin_hand_example, pin_brute_force, pin_zero_gate, pin_full_forget,
             pin_split_sequence, pin_varlen_equals_per_sequence, pin_chunk_form,
             pin_gamma_is_broadcast_g, pin_retnet_closed_form, pin_invariants,
             pin_prefill_then_decode, pin_step_brute_force, pin_gqa_is_repeated_mha,
             pin_step_variants, pin_bwd_finite_differences, pin_bwd_gate_identity,
-            pin_state_v_first, pin_normalizer]
+            pin_state_v_first, pin_normalizer, pin_gla_scalar_gate_is_simple_gla,
+            pin_gla_brute_force]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -561,6 +604,8 @@ MUTANTS = {
     10: "backward: state gradient not decayed between tokens",
     11: "backward: gate gradient pairs with the state after the token",
     12: "backward: k and v gradients miss the token's own output term",
+    13: "elementwise GLA: interleaved kv grouping",
+    14: "elementwise GLA: gate indexed by the value column instead of the key",
 }
 
 
