@@ -26,7 +26,7 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_bwd", "chunk_normalizer", "recurrent_step_normalizer",
+__all__ = ["chunk_fwd", "chunk_bwd", "gla_chunk_fwd", "chunk_normalizer", "recurrent_step_normalizer",
            "recurrent_step", "chunk_local_cumsum", "library_path", "lib",
            "SglaError", "ABI_VERSION"]
 
@@ -75,6 +75,8 @@ def _load():
     lib.sgla_chunk_bwd_workspace_size.argtypes = [pargs, vp]
     lib.sgla_chunk_bwd.restype = ctypes.c_int
     lib.sgla_chunk_bwd.argtypes = [pargs] + [vp] * 15 + [vp, sz, vp]
+    lib.sgla_gla_chunk_fwd.restype = ctypes.c_int
+    lib.sgla_gla_chunk_fwd.argtypes = [pargs] + [vp] * 9 + [sz, vp]
     lib.sgla_chunk_normalizer_workspace_size.restype = sz
     lib.sgla_chunk_normalizer_workspace_size.argtypes = [pargs, vp]
     lib.sgla_chunk_normalizer.restype = ctypes.c_int
@@ -279,6 +281,51 @@ def chunk_bwd(q, k, v, do, g=None, g_gamma=None, scale=None, initial_state=None,
     if st != _OK:
         _raise(st, "sgla_chunk_bwd")
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, dg_gamma=dgg, dh0=dh0)
+
+
+def gla_chunk_fwd(q, k, v, gk, scale=None, initial_state=None, output_final_state=False,
+                  cu_seqlens=None, chunk_size=64, o_dtype=torch.float32, state_v_first=False):
+    """Chunked forward of elementwise-gate GLA: S_t = diag(exp(gk_t)) S_{t-1} +
+    k_t v_t^T, o_t = scale S_t^T q_t.  q [B, T, H, K], k [B, T, Hkv, K], v [B,
+    T, Hkv, V] (bf16 or float32), gk [B, T, H, K] float32 log gates (one per
+    key).  Returns (o, final_state or None)."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor [B, T, H, K]")
+    dev = q.device
+    B, T, H, K = q.shape
+    if not isinstance(v, torch.Tensor) or v.dim() != 4:
+        raise ValueError("v must be a 4-D tensor [B, T, Hkv, V]")
+    V = v.shape[-1]
+    Hkv = _kv_heads(k, H, 2)
+    qkv = _dtype_code(q.dtype, "q")
+    _check_dev("q", q, dev)
+    _check_dev("k", k, dev, q.dtype, (B, T, Hkv, K))
+    _check_dev("v", v, dev, q.dtype, (B, T, Hkv, V))
+    _check_dev("gk", gk, dev, torch.float32, (B, T, H, K))
+    cu = _host_cu(cu_seqlens)
+    N = B if cu is None else cu.numel() - 1
+    if cu is not None and B != 1:
+        raise ValueError(f"packed input (cu_seqlens) requires B == 1, got B={B}")
+    sshape = _state_shape(N, H, K, V, state_v_first)
+    _check_dev("initial_state", initial_state, dev, torch.float32, sshape)
+    if scale is None:
+        scale = K ** -0.5
+    od = _dtype_code(o_dtype, "o_dtype")
+    args = _chunk_args(B, T, H, K, V, N, chunk_size, qkv, od, scale, output_final_state, Hkv,
+                       state_v_first)
+    cu_ptr = None if cu is None else ctypes.c_void_p(cu.data_ptr())
+    n = lib.sgla_chunk_normalizer_workspace_size(ctypes.byref(args), cu_ptr)
+    if n == 0 and lib.sgla_last_error():
+        raise ValueError(lib.sgla_last_error().decode(errors="replace"))
+    o = torch.empty((B, T, H, V), device=dev, dtype=o_dtype)
+    ht = torch.empty(sshape, device=dev, dtype=torch.float32) if output_final_state else None
+    ws = torch.empty(max(n, 1), device=dev, dtype=torch.uint8)
+    st = lib.sgla_gla_chunk_fwd(ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(gk),
+                                _ptr(initial_state), cu_ptr, _ptr(o), _ptr(ht), _ptr(ws), n,
+                                _stream(dev))
+    if st != _OK:
+        _raise(st, "sgla_gla_chunk_fwd")
+    return o, ht
 
 
 def chunk_normalizer(q, k, g=None, g_gamma=None, scale=None, initial_z=None,

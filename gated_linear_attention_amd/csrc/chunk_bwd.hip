@@ -34,11 +34,15 @@
 #include <hip/hip_runtime.h>
 
 #include "gate_scan.h"
+#include "row_stage.h"
 #include "sgla_internal.h"
 #include "unit_map.h"
 
 namespace sgla {
 namespace {
+
+using stage::load4;
+using stage::RowTile;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -52,53 +56,6 @@ constexpr float kRcpLn2f = 1.44269504088896341f;
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
-
-__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-
-// Four consecutive input elements as loaded (bf16 kept packed until they are
-// widened on their way into LDS, which halves the registers a prefetch holds).
-template <typename T> struct Raw4;
-template <> struct Raw4<float> { typedef f32x4 type; };
-template <> struct Raw4<__bf16> { typedef uint2 type; };
-__device__ __forceinline__ f32x4 raw_load(const float* p) { return load4(p); }
-__device__ __forceinline__ uint2 raw_load(const __bf16* p) { return *reinterpret_cast<const uint2*>(p); }
-__device__ __forceinline__ void raw_zero(f32x4& x) { x = f32x4{0.f, 0.f, 0.f, 0.f}; }
-__device__ __forceinline__ void raw_zero(uint2& x) { x = make_uint2(0u, 0u); }
-__device__ __forceinline__ f32x4 widen(f32x4 x) { return x; }
-__device__ __forceinline__ f32x4 widen(uint2 u) {
-  return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-               __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
-}
-
-// Staging of rows [0, 64) x cols [0, W) of a token-major input (row stride
-// RS elements) into LDS as fp32 (row stride LD floats) by NTH threads; rows
-// at or past `rows` read as zero.  Split into a register load and an LDS
-// store so that every load of a stage is in flight before the first store
-// (the stores go through a generic pointer the compiler cannot separate from
-// the loads), and so that a stage can be loaded ahead of its use.
-template <int W, int NTH, typename T>
-struct RowTile {
-  static constexpr int P = C * (W / 4);           // 4-element pieces
-  static constexpr int N = (P + NTH - 1) / NTH;   // per thread
-  typename Raw4<T>::type x[N];
-  __device__ __forceinline__ void load(const T* src, int64_t RS, int rows) {
-#pragma unroll
-    for (int u = 0; u < N; ++u) {
-      const int i = threadIdx.x + u * NTH;
-      const int c = i / (W / 4), c4 = i % (W / 4);
-      raw_zero(x[u]);
-      if ((P % NTH == 0 || i < P) && c < rows) x[u] = raw_load(src + c * RS + 4 * c4);
-    }
-  }
-  __device__ __forceinline__ void store(float* dst, int LD) const {
-#pragma unroll
-    for (int u = 0; u < N; ++u) {
-      const int i = threadIdx.x + u * NTH;
-      if (P % NTH == 0 || i < P)
-        *reinterpret_cast<f32x4*>(dst + (i / (W / 4)) * LD + 4 * (i % (W / 4))) = widen(x[u]);
-    }
-  }
-};
 
 // K rows x 32 columns of a [K][V] fp32 record, columns [c0, c0 + 32), by NTH
 // threads.

@@ -385,6 +385,65 @@ sgla_status sgla_chunk_bwd(const sgla_chunk_args* args, const void* q, const voi
   return ok();
 }
 
+sgla_status sgla_gla_chunk_fwd(const sgla_chunk_args* args, const void* q, const void* k, const void* v,
+                               const float* gk, const float* initial_state, const int64_t* cu_seqlens_host,
+                               void* o, float* final_state, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  Plan P;
+  sgla_status st = plan_shape(args, cu_seqlens_host, false, &P);
+  if (st != SGLA_OK) return st;
+  const sgla_chunk_args& a = *args;
+  if (a.qkv_dtype != SGLA_BF16 && a.qkv_dtype != SGLA_F32)
+    return fail(SGLA_ERR_DTYPE, "qkv_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", a.qkv_dtype);
+  if (a.o_dtype != SGLA_BF16 && a.o_dtype != SGLA_F32)
+    return fail(SGLA_ERR_DTYPE, "o_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", a.o_dtype);
+  if (!(a.K == 16 || a.K == 32 || a.K == 64 || a.K == 128))
+    return fail(SGLA_ERR_UNSUPPORTED, "elementwise-gate GLA supports K in {16,32,64,128} (got %d)", a.K);
+  if (a.V <= 0 || a.V % 32 != 0)
+    return fail(SGLA_ERR_UNSUPPORTED, "elementwise-gate GLA supports V a multiple of 32 (got %d)", a.V);
+  if (!std::isfinite(a.scale)) return fail(SGLA_ERR_INVALID_ARG, "scale must be finite");
+  const bool any_tokens = P.total_tokens > 0;
+  if (any_tokens && (q == nullptr || k == nullptr || v == nullptr || gk == nullptr || o == nullptr))
+    return fail(SGLA_ERR_INVALID_ARG, "q, k, v, gk and o must be non-NULL");
+  if (a.output_final_state && final_state == nullptr)
+    return fail(SGLA_ERR_INVALID_ARG, "output_final_state is set but final_state is NULL");
+  if (any_tokens && !(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(gk, 16) && aligned(o, 16)))
+    return fail(SGLA_ERR_INVALID_ARG, "q, k, v, gk and o must be 16-byte aligned");
+  if (P.packed && (workspace == nullptr || workspace_bytes < P.total_bytes))
+    return fail(SGLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", P.total_bytes, workspace_bytes);
+  if (final_state != nullptr && initial_state != nullptr && final_state != initial_state) {
+    const size_t sb = (size_t)P.N * a.H * a.K * a.V * sizeof(float);
+    const char* f0 = reinterpret_cast<const char*>(final_state);
+    const char* i0 = reinterpret_cast<const char*>(initial_state);
+    if (f0 < i0 + sb && i0 < f0 + sb)
+      return fail(SGLA_ERR_INVALID_ARG, "final_state partially overlaps initial_state (only exact aliasing is allowed)");
+  }
+  char* ws = static_cast<char*>(workspace);
+  st = upload_tables(P, ws, stream);
+  if (st != SGLA_OK) return st;
+  sgla::GlaFwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.gk = gk;
+  p.h0 = initial_state;
+  p.o = o;
+  p.ht = a.output_final_state ? final_state : nullptr;
+  p.scale = a.scale;
+  p.H = a.H;
+  p.Hkv = P.Hkv;
+  p.K = a.K;
+  p.V = a.V;
+  p.qkv_bf16 = a.qkv_dtype == SGLA_BF16;
+  p.o_bf16 = a.o_dtype == SGLA_BF16;
+  p.sl = state_layout(a);
+  p.seqs = layout_of(args, P, ws);
+  if (p.ht == nullptr && !any_tokens) return ok();
+  hipError_t e = sgla::launch_gla_chunk_fwd(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "launching the elementwise-gate GLA kernel");
+  return ok();
+}
+
 size_t sgla_chunk_normalizer_workspace_size(const sgla_chunk_args* args, const int64_t* cu_seqlens_host) {
   Plan P;
   if (plan_shape(args, cu_seqlens_host, false, &P) != SGLA_OK) return 0;

@@ -136,6 +136,26 @@ struct ChunkBwdParams {
 
 hipError_t launch_chunk_bwd(const ChunkBwdParams& p, hipStream_t stream);
 
+// Elementwise-gate GLA forward: gk [T_total, H, K] float32 natural-log gates,
+// one per key.  K in {16, 32, 64, 128}, V % 32 == 0.
+struct GlaFwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* gk;
+  const float* h0;
+  void* o;
+  float* ht;
+  float scale;
+  int32_t H, Hkv, K, V;
+  int32_t qkv_bf16;
+  int32_t o_bf16;
+  StateLayout sl;
+  SeqLayout seqs;
+};
+
+hipError_t launch_gla_chunk_fwd(const GlaFwdParams& p, hipStream_t stream);
+
 // Running normalizer (the ones column of the augmented value): den [T_total,
 // H] = scale q . z, z [N, H, K] carried from z0 to zt.
 struct NormalizerParams {

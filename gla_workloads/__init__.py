@@ -28,7 +28,7 @@ import numpy as np
 
 __all__ = ["ChunkWorkload", "DecodeWorkload", "CHUNK_CONFIGS", "DECODE_CONFIGS",
            "round_to_bf16", "logsigmoid", "make_chunk_inputs", "make_decode_inputs",
-           "make_backward_inputs",
+           "make_backward_inputs", "make_key_gates",
            "retnet_gamma"]
 
 
@@ -197,6 +197,15 @@ def make_backward_inputs(inp: dict, seed: int, final_state_grad: bool = True) ->
     if final_state_grad:
         dht = rng.standard_normal((N, H, K, V), dtype=np.float32) * np.float32(0.1)
     return dict(do=do, dht=dht)
+
+
+def make_key_gates(inp: dict, seed: int, normalizer: float = 1.0) -> np.ndarray:
+    """Per-key log gates gk [B, T, H, K] = logsigmoid(N(0, 1)) / normalizer,
+    float32, for elementwise-gate GLA on a batch from make_chunk_inputs (the
+    same recipe as the head-wise gate, one draw per key)."""
+    rng = np.random.default_rng(seed)
+    B, T, H, K = inp["B"], inp["T"], inp["H"], inp["K"]
+    return (logsigmoid(rng.standard_normal((B, T, H, K))) / normalizer).astype(np.float32)
 
 
 def make_decode_inputs(w: DecodeWorkload, steps: Optional[int] = None) -> dict:

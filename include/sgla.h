@@ -196,6 +196,29 @@ sgla_status sgla_chunk_bwd(const sgla_chunk_args *args,
                            hipStream_t stream);
 
 /*
+ * Chunked forward of elementwise-gate GLA, the general form Simple GLA is the
+ * head-wise special case of (section 一: the elementwise gate decays every
+ * state element on its own; the relinear pages pass a gate vector over the
+ * key dimension):
+ *     S_t = diag(exp(gk_t)) S_{t-1} + k_t v_t^T ,   o_t = scale * S_t^T q_t
+ * Arguments as for sgla_chunk_fwd, with gk in place of g / g_gamma:
+ *   gk              [B, T, H, K] float32 log gates, one per key (required);
+ *                   accurate for gk <= 0, the forget-gate range
+ *   q [B, T, H, K]; k [B, T, Hkv, K]; v [B, T, Hkv, V]; o [B, T, H, V];
+ *   initial_state / final_state [N, H, K, V] (or [N, H, V, K] with
+ *   state_v_first); cu_seqlens_host and workspace as for
+ *   sgla_chunk_normalizer (the packed-sequence table only:
+ *   sgla_chunk_normalizer_workspace_size gives the bytes).
+ * One launch, all products on the fp32 matrix cores.  Supported: K in {16,
+ * 32, 64, 128}, V a multiple of 32, bf16 or float32 inputs, chunk_size 64.
+ */
+sgla_status sgla_gla_chunk_fwd(const sgla_chunk_args *args,
+                               const void *q, const void *k, const void *v, const float *gk,
+                               const float *initial_state, const int64_t *cu_seqlens_host,
+                               void *o, float *final_state,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Running normalizer of normalized linear attention (page "relinear": the
  * output divided by q . z, which the pages obtain by appending a column of
  * ones to v -- its state column is z and its output the normalizer):

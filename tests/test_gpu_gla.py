@@ -1,0 +1,117 @@
+"""GPU parity of elementwise-gate GLA (sgla_gla_chunk_fwd) against the fp64
+oracle: per-key log gates gk [B, T, H, K], S_t = diag(exp(gk_t)) S_{t-1} +
+k_t v_t^T, o_t = scale S_t^T q_t (the general gate Simple GLA specialises,
+page "flash-linear-attention 中的 Simple GLA", section 一).  The bar per
+output tensor: max |gpu - oracle| / RMS(oracle) <= 2e-2 for bf16 inputs and
+1e-4 for float32 inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gla_workloads import CHUNK_CONFIGS, ChunkWorkload, make_chunk_inputs, make_key_gates
+from gpu_common import TOL_BF16, TOL_F32, device_inputs, err_ratio, to_dev
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+if torch.cuda.is_available():
+    import gated_linear_attention_amd as sgla
+else:  # pragma: no cover - collected on CPU-only hosts, never run
+    sgla = None
+
+
+def small(name, **kw):
+    base = dict(B=2, T=150, H=2, K=64, V=64, dtype="bf16", gate="none", seed=61)
+    base.update(kw)
+    return ChunkWorkload(name, **base)
+
+
+CASES = [
+    (small("k64_v64"), 1.0),
+    (small("k128_v96_h0", K=128, V=96, T=131, initial_state=True), 1.0),
+    (small("k16_v32", K=16, V=32, T=97), 1.0),
+    (small("k32_v64_strong", K=32, V=64, T=200), 0.1),
+    (small("k128_weak", K=128, V=32, T=70), 10.0),
+    (small("t1", T=1, initial_state=True), 1.0),
+    (small("t65", T=65), 1.0),
+    (small("empty", T=0, initial_state=True), 1.0),
+    (small("varlen", B=1, T=0, K=64, V=64, fixed_lengths=(15, 0, 1, 85, 200), initial_state=True), 1.0),
+    (small("gqa", H=4, Hkv=2, K=64, V=32, T=130, initial_state=True), 1.0),
+    (small("f32_k32", dtype="f32", K=32, V=64, T=150, initial_state=True), 1.0),
+    (small("f32_k128_strong", dtype="f32", K=128, V=32, T=100), 0.1),
+]
+
+
+def run(inp, gk, o_dtype=torch.float32, state_v_first=False):
+    d = device_inputs(inp)
+    h0 = d["initial_state"]
+    if state_v_first and h0 is not None:
+        h0 = h0.transpose(-1, -2).contiguous()
+    o, ht = sgla.gla_chunk_fwd(d["q"], d["k"], d["v"], to_dev(gk, torch.float32), scale=inp["scale"],
+                               initial_state=h0, output_final_state=True, cu_seqlens=inp["cu_seqlens"],
+                               o_dtype=o_dtype, state_v_first=state_v_first)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), ht.cpu().numpy()
+
+
+@pytest.mark.parametrize("w,norm", CASES, ids=lambda x: x.name if hasattr(x, "name") else str(x))
+def test_gla_small(w, norm):
+    inp = make_chunk_inputs(w)
+    gk = make_key_gates(inp, seed=w.seed + 3, normalizer=norm)
+    o, ht = run(inp, gk)
+    o_ref, h_ref = oracle.gla_fwd(inp["q"], inp["k"], inp["v"], gk, scale=inp["scale"],
+                                  initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"])
+    tol = TOL_BF16 if inp["dtype"] == "bf16" else TOL_F32
+    eo, eh = err_ratio(o, o_ref), err_ratio(ht, h_ref)
+    print(f"[gla {w.name}] o {eo:.2e} final {eh:.2e}", flush=True)
+    assert np.all(np.isfinite(o)) and eo <= tol and eh <= tol
+
+
+def test_gla_scalar_gate_matches_simple_gla():
+    """Every key given the head's gate: the GLA kernel agrees with the Simple
+    GLA kernel (different paths) within the bf16 bar."""
+    inp = make_chunk_inputs(small("scal", B=1, T=0, K=128, V=128, gate="g",
+                                  fixed_lengths=(300, 77), initial_state=True))
+    gk = np.repeat(inp["g"][..., None], inp["K"], axis=-1)
+    o1, h1 = run(inp, gk)
+    d = device_inputs(inp)
+    o2, h2 = sgla.chunk_fwd(d["q"], d["k"], d["v"], g=d["g"], scale=inp["scale"],
+                            initial_state=d["initial_state"], output_final_state=True,
+                            cu_seqlens=inp["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert err_ratio(o1, o2.cpu().numpy()) <= TOL_BF16
+    assert err_ratio(h1, h2.cpu().numpy()) <= TOL_BF16
+
+
+def test_gla_state_v_first_and_bf16_output():
+    inp = make_chunk_inputs(small("vf", K=64, V=96, T=140, initial_state=True))
+    gk = make_key_gates(inp, seed=5)
+    o1, h1 = run(inp, gk)
+    o2, h2 = run(inp, gk, state_v_first=True)
+    assert np.array_equal(o1, o2) and np.array_equal(np.swapaxes(h1, -1, -2), h2)
+    # a bf16 o is the fp32 one rounded once: within half a bf16 ulp per element
+    o3, _ = run(inp, gk, o_dtype=torch.bfloat16)
+    assert np.all(np.abs(o3 - o1) <= 2.0 ** -8 * np.abs(o1))
+
+
+def test_gla_named_workload_sampled():
+    """The packed K = V = 128 workload (8 sequences of 64..4096 tokens, 16
+    heads, h0) with per-key gates, in one launch; the oracle checks sampled
+    (sequence, head) units one by one."""
+    inp = make_chunk_inputs(CHUNK_CONFIGS["varlen_bf16_k128"])
+    gk = make_key_gates(inp, seed=77)
+    o, ht = run(inp, gk)
+    cu = inp["cu_seqlens"]
+    lens = np.diff(cu)
+    units = [(int(np.argmax(lens)), 0), (int(np.argmin(lens)), 15), (3, 7), (5, 2)]
+    worst_o = worst_h = 0.0
+    for n, h in units:
+        s, e = int(cu[n]), int(cu[n + 1])
+        sl = lambda x: x[:, s:e, h:h + 1]
+        o_ref, h_ref = oracle.gla_fwd(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(gk), scale=inp["scale"],
+                                      initial_state=inp["initial_state"][n:n + 1, h:h + 1], nthreads=1)
+        worst_o = max(worst_o, err_ratio(o[:, s:e, h:h + 1], o_ref))
+        worst_h = max(worst_h, err_ratio(ht[n:n + 1, h:h + 1], h_ref))
+    print(f"[gla varlen] o {worst_o:.2e} final {worst_h:.2e}", flush=True)
+    assert worst_o <= TOL_BF16 and worst_h <= TOL_BF16
