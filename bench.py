@@ -28,6 +28,8 @@ The JSON line also carries:
                    dv, dg, dh0), against the fp32 matrix-core peak its kernels
                    run on;
   normalizer    -- sgla_chunk_normalizer on the same workload, HBM GB/s;
+  gla           -- sgla_gla_chunk_fwd (per-key gates) on the same workload,
+                   against the fp32 matrix-core peak;
   cpu_baseline  -- the fp64 CPU oracle timed on the host cores on whole
                    batches of the same workload (a reported baseline only).
 
@@ -405,6 +407,57 @@ def bench_normalizer(workload: str, steps: int, warmup: int, warm_seconds: float
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
+def bench_gla(workload: str, steps: int, warmup: int, warm_seconds: float):
+    """sgla_gla_chunk_fwd (elementwise per-key gates) on a chunked workload
+    with gk = logsigmoid(N(0,1)) per key.  Algorithmic FLOPs as the head-wise
+    forward's (the per-key decays are elementwise work on top); the kernels
+    run on the fp32 matrix cores, so that is the peak it is priced against."""
+    import numpy as np
+    import torch
+
+    import gated_linear_attention_amd as sgla
+    from gla_workloads import CHUNK_CONFIGS, make_chunk_inputs, make_key_gates
+
+    w = CHUNK_CONFIGS[workload]
+    inp = make_chunk_inputs(w)
+    gk_np = make_key_gates(inp, seed=w.seed + 200)
+    dev = torch.device("cuda:0")
+    qdt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+    t = lambda a, dt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+    q, k, v, gk = t(inp["q"], qdt), t(inp["k"], qdt), t(inp["v"], qdt), t(gk_np, torch.float32)
+    h0 = t(inp["initial_state"], torch.float32)
+    step = lambda _i: sgla.gla_chunk_fwd(q, k, v, gk, scale=inp["scale"], initial_state=h0,
+                                         output_final_state=True, cu_seqlens=inp["cu_seqlens"])
+    warm_device(step, warm_seconds)
+    for i in range(warmup):
+        step(i)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    ms = sum(per) / len(per)
+    nbytes, flops = chunk_algorithmic(inp)
+    B, T, H, K = inp["B"], inp["T"], inp["H"], inp["K"]
+    if inp["g"] is not None:
+        nbytes -= B * T * H * 4
+    nbytes += B * T * H * K * 4            # the per-key gates
+    tf = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": workload, "gate": "per-key gk", "kernel": "gla_chunk_fwd_kernel",
+            "ms_per_call_mean": round(ms, 5), "ms_per_call_median": round(per[len(per) // 2], 5),
+            "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "algorithmic_flops_per_call": int(flops), "algorithmic_bytes_per_call": int(nbytes),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": F32_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / F32_MFMA_PEAK_TFLOPS, 4), "dtype": "f32"},
+            "hbm": {"achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
 def cpu_baseline(inp, min_seconds: float = 10.0):
     """The fp64 CPU oracle on whole batches of the timed workload, repeated
     until at least ``min_seconds`` of wall time (a bounded sample)."""
@@ -538,6 +591,7 @@ def main():
     if not a.no_backward:
         out["backward"] = bench_backward(a.backward_workload, 20, a.warmup, a.warm_seconds)
         out["normalizer"] = bench_normalizer(a.backward_workload, 20, a.warmup, a.warm_seconds)
+        out["gla"] = bench_gla(a.backward_workload, 20, a.warmup, a.warm_seconds)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)

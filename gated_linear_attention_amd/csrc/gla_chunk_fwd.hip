@@ -12,12 +12,17 @@
 //   A[c][j] = sum_a q_c[a] k_j[a] 2^(B[c][a] - B[j][a])  for j <= c, else 0
 //   h_n+1 = diag(2^B_last) h_n + (K (.) 2^(B_last - B))^T V
 // Unlike the head-wise gate, the decay between two tokens differs per key, so
-// A is no plain product of Q and K^T.  It is formed by 16 x 16 blocks:
-//   * blocks below the diagonal (c-block I > j-block J) on the matrix cores,
-//     both operands rescaled against the first token r of block I:
-//     (q_c 2^(B_c - B_r)) . (k_j 2^(B_r - B_j)), each factor <= 1 for
-//     non-positive gates, so nothing can overflow whatever the gates;
-//   * the four diagonal blocks elementwise, 2^(B_c - B_j) per key.
+// A is no plain product of Q and K^T.  It is formed by 16 x 16 blocks on the
+// matrix cores, each with both operands rescaled against a reference token r
+// of the block: (q_c 2^(B_c - B_r)) . (k_j 2^(B_r - B_j)) = q_c k_j 2^(B_c -
+// B_j) per key.
+//   * Below the diagonal (c-block I > j-block J) r is the first token of
+//     block I, so both factors are <= 1 for non-positive gates: nothing can
+//     overflow whatever the gates.
+//   * On the diagonal r is the block's middle token; the factors are then
+//     bounded by the decay over half a block, which is checked per block
+//     (every key's exponent span within 2^+-100); a block whose gates are
+//     stronger than that is formed elementwise, 2^(B_c - B_j) per term.
 // Everything runs in fp32 (the state, the accumulation, the fp32 matrix
 // cores v_mfma_f32_16x16x4_f32), so the only rounding is fp32's.
 //
@@ -46,7 +51,10 @@ constexpr int NT = 256;
 constexpr int LDV = VT + 4;
 constexpr int LDA = C + 4;
 constexpr int LDH = VT + 4;
-constexpr double kRcpLn2 = 1.4426950408889634074;
+constexpr double kRcpLn2d = 1.4426950408889634074;
+constexpr float kMaxSpan = 100.f;   // |log2 factor| allowed for a diagonal block's operands
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -71,6 +79,10 @@ gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   __shared__ float sV[C * LDV];
   __shared__ float sA[C * LDA];
   __shared__ float sH[K * LDH];
+  constexpr int NPART = NT / K;       // token parts of the per-key scan
+  constexpr int TL = C / NPART;       // tokens per part
+  static_assert(NPART * K == NT && TL * NPART == C, "scan split");
+  __shared__ float sTot[NT];
 
   const UnitMap um = map_unit(blockIdx.x, V / VT, Hkv, H / Hkv, seqs.num_seqs);
   if (!um.valid) return;
@@ -140,6 +152,25 @@ gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   };
   if (nchunks > 0) load_chunk(0);
 
+  // A chunk's outputs are stored at the start of the next iteration (or after
+  // the loop): the wait for the prefetched rows at the top of an iteration
+  // covers every memory operation issued before it, stores included, so
+  // stores issued right after that wait have a whole iteration to complete.
+  const int ct0 = w >> 1, ct1 = ct0 + 2, cv = w & 1;
+  float pend[8];
+  int64_t pend_t0 = 0;
+  int pend_cl = 0;
+  auto flush_out = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c0 = 16 * ct0 + 4 * g4 + i, c1 = 16 * ct1 + 4 * g4 + i;
+      if (c0 < pend_cl)
+        o[((pend_t0 + c0) * H + hd) * (int64_t)V + vt * VT + 16 * cv + r] = out_cast<TOut>(pend[i]);
+      if (c1 < pend_cl)
+        o[((pend_t0 + c1) * H + hd) * (int64_t)V + vt * VT + 16 * cv + r] = out_cast<TOut>(pend[4 + i]);
+    }
+  };
+
   for (int m = 0; m < nchunks; ++m) {
     const int64_t t0 = bos + (int64_t)m * C;
     const int cl = min(C, len - m * C);
@@ -147,110 +178,188 @@ gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     kt.store(sK, LDQ);
     gt.store(sB, LDQ);
     vtl.store(sV, LDV);
+    if (m > 0) flush_out();
     __syncthreads();
-    if (m + 1 < nchunks) load_chunk(m + 1);
 
-    // ---- B: chunk-local cumulative log2 gate of every key (padding adds 0) --
-    for (int a = tid; a < K; a += NT) {
+    // ---- B: chunk-local cumulative log2 gate of every key (padding adds 0).
+    //      Thread (key a, part p) sums tokens [p TL, +TL) in double; the parts'
+    //      totals are exchanged through LDS, then each part writes its running
+    //      sums with the earlier parts' total added ---------------------------
+    {
+      const int a = tid % K, p = tid / K;
+      float gv[TL];
+      double tot = 0.0;
+#pragma unroll
+      for (int u = 0; u < TL; ++u) {
+        gv[u] = sB[(p * TL + u) * LDQ + a];
+        tot += (double)gv[u];
+      }
+      sTot[p * K + a] = (float)tot;
+      __syncthreads();
       double b = 0.0;
-      for (int c = 0; c < C; ++c) {
-        b += (double)sB[c * LDQ + a];
-        sB[c * LDQ + a] = (float)(b * kRcpLn2);
+      for (int pp = 0; pp < p; ++pp) b += (double)sTot[pp * K + a];
+#pragma unroll
+      for (int u = 0; u < TL; ++u) {
+        b += (double)gv[u];
+        sB[(p * TL + u) * LDQ + a] = (float)(b * kRcpLn2d);
       }
     }
     __syncthreads();
 
-    // ---- A, blocks below the diagonal: wave w takes blocks w and w + 4 ------
-    //      (I, J) in order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+    // ---- A below the diagonal: blocks (I, J) in the order (1,0) (2,0) (2,1)
+    //      (3,0) (3,1) (3,2); waves 0 and 1 take two (interleaved), waves 2 and
+    //      3 one; the reference token is the first of block I ------------------
+    {
+      auto block_ij = [](int bi, int& I, int& J) {
+        I = bi == 0 ? 1 : (bi < 3 ? 2 : 3);
+        J = bi == 0 ? 0 : (bi < 3 ? bi - 1 : bi - 3);
+      };
+      auto store_block = [&](int I, int J, const f32x4& acc) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int bi = w + 4 * t;
-      if (bi >= 6) continue;
-      const int I = bi == 0 ? 1 : (bi < 3 ? 2 : 3);
-      const int J = bi == 0 ? 0 : (bi < 3 ? bi - 1 : bi - 3);
-      const int rr = 16 * I;           // reference token: first of block I
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 4; ++i) sA[(16 * I + 4 * g4 + i) * LDA + 16 * J + r] = acc[i] * scale;
+      };
+      int I0, J0, I1, J1;
+      block_ij(w, I0, J0);
+      block_ij(w < 2 ? w + 4 : w, I1, J1);
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+      if (w < 2) {
 #pragma unroll 4
-      for (int ks = 0; ks < K / 4; ++ks) {
-        const int a = 4 * ks + g4;
-        const float br = sB[rr * LDQ + a];
-        const int ci = (16 * I + r) * LDQ + a, ji = (16 * J + r) * LDQ + a;
-        acc = mfma4(sQ[ci] * exp2f(sB[ci] - br), sK[ji] * exp2f(br - sB[ji]), acc);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sA[(16 * I + 4 * g4 + i) * LDA + 16 * J + r] = acc[i] * scale;
-    }
-    // ---- A, diagonal blocks: wave w takes block w, one (c, j) pair per lane
-    //      and pass over the block's 256 entries (the upper ones are zero) ----
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      const int e = lane + 64 * pp;
-      const int cl16 = e >> 4, jl16 = e & 15;
-      const int c = 16 * w + cl16, j = 16 * w + jl16;
-      float x = 0.f;
-      if (jl16 <= cl16) {
-        const f32x4* qc = reinterpret_cast<const f32x4*>(sQ + c * LDQ);
-        const f32x4* bc = reinterpret_cast<const f32x4*>(sB + c * LDQ);
-        const f32x4* kj = reinterpret_cast<const f32x4*>(sK + j * LDQ);
-        const f32x4* bj = reinterpret_cast<const f32x4*>(sB + j * LDQ);
+        for (int ks = 0; ks < K / 4; ++ks) {
+          const int a = 4 * ks + g4;
+          const float br0 = sB[16 * I0 * LDQ + a], br1 = sB[16 * I1 * LDQ + a];
+          const int c0 = (16 * I0 + r) * LDQ + a, j0 = (16 * J0 + r) * LDQ + a;
+          const int c1 = (16 * I1 + r) * LDQ + a, j1 = (16 * J1 + r) * LDQ + a;
+          acc0 = mfma4(sQ[c0] * exp2_hw(sB[c0] - br0), sK[j0] * exp2_hw(br0 - sB[j0]), acc0);
+          acc1 = mfma4(sQ[c1] * exp2_hw(sB[c1] - br1), sK[j1] * exp2_hw(br1 - sB[j1]), acc1);
+        }
+        store_block(I1, J1, acc1);
+      } else {
 #pragma unroll 4
-        for (int a4 = 0; a4 < K / 4; ++a4) {
-          const f32x4 qv = qc[a4], bcv = bc[a4], kv = kj[a4], bjv = bj[a4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) x = fmaf(qv[u] * kv[u], exp2f(bcv[u] - bjv[u]), x);
+        for (int ks = 0; ks < K / 4; ++ks) {
+          const int a = 4 * ks + g4;
+          const float br0 = sB[16 * I0 * LDQ + a];
+          const int c0 = (16 * I0 + r) * LDQ + a, j0 = (16 * J0 + r) * LDQ + a;
+          acc0 = mfma4(sQ[c0] * exp2_hw(sB[c0] - br0), sK[j0] * exp2_hw(br0 - sB[j0]), acc0);
         }
       }
-      sA[c * LDA + j] = x * scale;
+      store_block(I0, J0, acc0);
+    }
+    // ---- A on the diagonal: wave w takes block w, reference its middle token;
+    //      a block whose exponent span is too wide is formed elementwise -------
+    {
+      const int I = w, rr = 16 * I + 8;
+      float span = 0.f;
+      for (int a = lane; a < K; a += 64) {
+        const float br = sB[rr * LDQ + a];
+        span = fmaxf(span, fmaxf(sB[(16 * I) * LDQ + a] - br, br - sB[(16 * I + 15) * LDQ + a]));
+      }
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) span = fmaxf(span, __shfl_xor(span, d, 64));
+      if (span <= kMaxSpan) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int ks = 0; ks < K / 4; ++ks) {
+          const int a = 4 * ks + g4;
+          const float br = sB[rr * LDQ + a];
+          const int ci = (16 * I + r) * LDQ + a;
+          acc = mfma4(sQ[ci] * exp2_hw(sB[ci] - br), sK[ci] * exp2_hw(br - sB[ci]), acc);
+        }
+        const int j = 16 * I + r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = 16 * I + 4 * g4 + i;
+          sA[c * LDA + j] = j <= c ? acc[i] * scale : 0.f;   // a select: an overflowed upper entry is dropped
+        }
+      } else {
+        // elementwise: one (c, j) entry of the block per lane and pass
+        for (int pp = 0; pp < 4; ++pp) {
+          const int e = lane + 64 * pp;
+          const int c = 16 * I + (e >> 4), j = 16 * I + (e & 15);
+          float x = 0.f;
+          if (j <= c) {
+            const f32x4* qc = reinterpret_cast<const f32x4*>(sQ + c * LDQ);
+            const f32x4* bc = reinterpret_cast<const f32x4*>(sB + c * LDQ);
+            const f32x4* kj = reinterpret_cast<const f32x4*>(sK + j * LDQ);
+            const f32x4* bj = reinterpret_cast<const f32x4*>(sB + j * LDQ);
+            for (int a4 = 0; a4 < K / 4; ++a4) {
+              const f32x4 qv = qc[a4], bcv = bc[a4], kv = kj[a4], bjv = bj[a4];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) x = fmaf(qv[u] * kv[u], exp2_hw(bcv[u] - bjv[u]), x);
+            }
+          }
+          sA[c * LDA + j] = x * scale;
+        }
+      }
     }
     __syncthreads();
+    // the next chunk's rows go into registers now: they are held through the
+    // rest of this chunk, not through the A phase
+    if (m + 1 < nchunks) load_chunk(m + 1);
 
     // ---- Q (.) 2^B and K (.) 2^(B_last - B), in place ------------------------
     for (int i = tid; i < C * K; i += NT) {
       const int c = i / K, a = i % K;
       const float b = sB[c * LDQ + a];
-      sQ[c * LDQ + a] *= exp2f(b);
-      sK[c * LDQ + a] *= exp2f(sB[(C - 1) * LDQ + a] - b);
+      sQ[c * LDQ + a] *= exp2_hw(b);
+      sK[c * LDQ + a] *= exp2_hw(sB[(C - 1) * LDQ + a] - b);
     }
     __syncthreads();
 
-    // ---- output tiles (ct, cv), two per wave ---------------------------------
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int ot = w + 4 * t;
-      const int ctile = ot >> 1, cv = ot & 1;
-      f32x4 inter = {0.f, 0.f, 0.f, 0.f}, intra = {0.f, 0.f, 0.f, 0.f};
+    // ---- output tiles (ct, cv) and (ct + 2, cv), ct = w / 2, cv = w % 2: the
+    //      two tiles share their B operands and run as interleaved chains ------
+    {
+      f32x4 in0 = {0.f, 0.f, 0.f, 0.f}, in1 = in0, ia0 = in0, ia1 = in0;
 #pragma unroll 8
-      for (int ks = 0; ks < K / 4; ++ks)
-        inter = mfma4(sQ[(16 * ctile + r) * LDQ + 4 * ks + g4], sH[(4 * ks + g4) * LDH + 16 * cv + r], inter);
-      for (int js = 0; js < 4 * (ctile + 1); ++js)
-        intra = mfma4(sA[(16 * ctile + r) * LDA + 4 * js + g4], sV[(4 * js + g4) * LDV + 16 * cv + r], intra);
+      for (int ks = 0; ks < K / 4; ++ks) {
+        const float b = sH[(4 * ks + g4) * LDH + 16 * cv + r];
+        in0 = mfma4(sQ[(16 * ct0 + r) * LDQ + 4 * ks + g4], b, in0);
+        in1 = mfma4(sQ[(16 * ct1 + r) * LDQ + 4 * ks + g4], b, in1);
+      }
+      for (int js = 0; js < 4 * (ct0 + 1); ++js) {
+        const float b = sV[(4 * js + g4) * LDV + 16 * cv + r];
+        ia0 = mfma4(sA[(16 * ct0 + r) * LDA + 4 * js + g4], b, ia0);
+        ia1 = mfma4(sA[(16 * ct1 + r) * LDA + 4 * js + g4], b, ia1);
+      }
+      for (int js = 4 * (ct0 + 1); js < 4 * (ct1 + 1); ++js)
+        ia1 = mfma4(sA[(16 * ct1 + r) * LDA + 4 * js + g4], sV[(4 * js + g4) * LDV + 16 * cv + r], ia1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c = 16 * ctile + 4 * g4 + i;
-        if (c < cl)
-          o[((t0 + c) * H + hd) * (int64_t)V + vt * VT + 16 * cv + r] = out_cast<TOut>(intra[i] + scale * inter[i]);
+        pend[i] = ia0[i] + scale * in0[i];
+        pend[4 + i] = ia1[i] + scale * in1[i];
       }
+      pend_t0 = t0;
+      pend_cl = cl;
     }
 
     // ---- state: h <- diag(2^B_last) h + (K (.) 2^(B_last - B))^T V ---------------
+    //      (the wave's tiles share the column tile ctl = w % 2, so they share
+    //      the V operand and run as interleaved chains)
+    {
+      const int ctl = w & 1;
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-      const int st = w + 4 * s;
-      if (NST % 4 != 0 && st >= NST) continue;
-      const int kt = st >> 1, ctl = st & 1;
-      f32x4 acc = hs[s];
+      for (int s = 0; s < SPW; ++s) {
+        const int st = w + 4 * s;
+        if (NST % 4 != 0 && st >= NST) continue;
+        const int kt = st >> 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] *= exp2f(sB[(C - 1) * LDQ + 16 * kt + 4 * g4 + i]);
-#pragma unroll 8
+        for (int i = 0; i < 4; ++i) hs[s][i] *= exp2_hw(sB[(C - 1) * LDQ + 16 * kt + 4 * g4 + i]);
+      }
+#pragma unroll 4
       for (int cs = 0; cs < C / 4; ++cs) {
         const int c = 4 * cs + g4;
-        acc = mfma4(sK[c * LDQ + 16 * kt + r], sV[c * LDV + 16 * ctl + r], acc);
+        const float b = sV[c * LDV + 16 * ctl + r];
+#pragma unroll
+        for (int s = 0; s < SPW; ++s) {
+          const int st = w + 4 * s;
+          if (NST % 4 != 0 && st >= NST) continue;
+          hs[s] = mfma4(sK[c * LDQ + 16 * (st >> 1) + r], b, hs[s]);
+        }
       }
-      hs[s] = acc;
     }
     __syncthreads();   // every read of sQ, sK, sB, sV, sA and the old sH is done
     publish_state();
   }
+  if (nchunks > 0) flush_out();
   if (ht != nullptr) {
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
