@@ -56,13 +56,22 @@ MALL_BYTES = 256 << 20
 METRIC = "chunked Simple-GLA fwd tokens/s + % bf16 MFMA peak; decode HBM GB/s"
 
 
-def kernel_source_hash() -> str:
+# The sources each measured path's kernels are built from: a committed traffic
+# record is used only while these files are unchanged.
+KERNEL_SOURCES = {
+    "chunk_fwd": ("chunk_prep_bf16.hip", "chunk_fwd_bf16_wide.hip", "chunk_fwd_bf16.hip",
+                  "chunk_fwd_f32.hip", "mfma_common.h", "gate_scan.h", "unit_map.h"),
+    "recurrent_step_kernel": ("recurrent_step.hip",),
+}
+
+
+def kernel_source_hash(name: str = "chunk_fwd") -> str:
     d = os.path.join(ROOT, "gated_linear_attention_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(d)):
-        with open(os.path.join(d, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
+    for f in sorted(KERNEL_SOURCES[name]):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -118,7 +127,7 @@ def load_traffic(workload: str, kernel: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 

@@ -114,7 +114,7 @@ def traffic(a):
            "copy_calibration": {"bytes": copy_bytes, "fetch_size_kib": statistics.median(cf),
                                 "write_size_kib": statistics.median(cw),
                                 "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)},
-           "kernel_source_hash": kernel_source_hash()}
+           "kernel_source_hash": kernel_source_hash(a.name)}
     with open(a.out_json, "w") as f:
         json.dump(rec, f, indent=1)
     lines = [f"# HBM traffic of {a.name} on {a.workload} (rocprofv3 counters)", "",
