@@ -375,7 +375,10 @@ def bench_backward(workload: str, steps: int, warmup: int, warm_seconds: float):
 
 def bench_normalizer(workload: str, steps: int, warmup: int, warm_seconds: float):
     """sgla_chunk_normalizer on a chunked workload: q and k read once, g read
-    once, den written once (fp32), final z written -- an HBM stream."""
+    once, den written once (fp32), final z written -- an HBM stream.  One
+    call is three launches (per-chunk key sums, the scan over chunks, the
+    per-chunk outputs) plus the packed-table upload; the roofline divides the
+    algorithmic bytes by the whole call's time."""
     import numpy as np
     import torch
 
@@ -409,7 +412,8 @@ def bench_normalizer(workload: str, steps: int, warmup: int, warm_seconds: float
     esz = 2 if inp["dtype"] == "bf16" else 4
     nbytes = B * T * ((H + Hkv) * K * esz + H * 4 + (H * 4 if g is not None else 0)) + N * H * K * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": workload, "kernel": "chunk_normalizer_kernel", "ms_per_call_mean": round(ms, 5),
+    return {"workload": workload, "kernel": "norm_chunk_sum_kernel+norm_scan_kernel+norm_chunk_out_kernel",
+            "launches_per_call": 3, "ms_per_call_mean": round(ms, 5),
             "ms_per_call_median": round(per[len(per) // 2], 5), "algorithmic_bytes_per_call": int(nbytes),
             "tokens_per_s": round(B * T / (ms * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

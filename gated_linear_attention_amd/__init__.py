@@ -30,7 +30,7 @@ __all__ = ["chunk_fwd", "chunk_bwd", "gla_chunk_fwd", "chunk_normalizer", "recur
            "recurrent_step", "chunk_local_cumsum", "library_path", "lib",
            "SglaError", "ABI_VERSION"]
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsgla.so")
 
@@ -79,6 +79,8 @@ def _load():
     lib.sgla_gla_chunk_fwd.argtypes = [pargs] + [vp] * 9 + [sz, vp]
     lib.sgla_chunk_normalizer_workspace_size.restype = sz
     lib.sgla_chunk_normalizer_workspace_size.argtypes = [pargs, vp]
+    lib.sgla_gla_chunk_fwd_workspace_size.restype = sz
+    lib.sgla_gla_chunk_fwd_workspace_size.argtypes = [pargs, vp]
     lib.sgla_chunk_normalizer.restype = ctypes.c_int
     lib.sgla_chunk_normalizer.argtypes = [pargs] + [vp] * 9 + [sz, vp]
     lib.sgla_recurrent_step_normalizer.restype = ctypes.c_int
@@ -314,7 +316,7 @@ def gla_chunk_fwd(q, k, v, gk, scale=None, initial_state=None, output_final_stat
     args = _chunk_args(B, T, H, K, V, N, chunk_size, qkv, od, scale, output_final_state, Hkv,
                        state_v_first)
     cu_ptr = None if cu is None else ctypes.c_void_p(cu.data_ptr())
-    n = lib.sgla_chunk_normalizer_workspace_size(ctypes.byref(args), cu_ptr)
+    n = lib.sgla_gla_chunk_fwd_workspace_size(ctypes.byref(args), cu_ptr)
     if n == 0 and lib.sgla_last_error():
         raise ValueError(lib.sgla_last_error().decode(errors="replace"))
     o = torch.empty((B, T, H, V), device=dev, dtype=o_dtype)

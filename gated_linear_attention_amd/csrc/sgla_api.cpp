@@ -184,14 +184,14 @@ sgla_status hip_fail(hipError_t e, const char* what) {
 // host source is staged by the runtime before the call returns).
 sgla_status upload_tables(const Plan& P, char* ws, hipStream_t stream) {
   if (!P.packed) return SGLA_OK;
-  hipError_t e = hipMemcpyAsync(ws + P.seq_off, P.seqs.data(), P.seqs.size() * sizeof(sgla::SeqEntry),
-                                hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return hip_fail(e, "copying the sequence table");
-  if (!P.chunks.empty()) {
-    e = hipMemcpyAsync(ws + P.chunk_off, P.chunks.data(), P.chunks.size() * sizeof(sgla::ChunkEntry),
-                       hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess) return hip_fail(e, "copying the chunk table");
-  }
+  // both tables in one copy: [seq table | pad | chunk table]
+  const size_t bytes = P.chunk_off + P.chunks.size() * sizeof(sgla::ChunkEntry);
+  std::vector<char> host(bytes, 0);
+  std::memcpy(host.data() + P.seq_off, P.seqs.data(), P.seqs.size() * sizeof(sgla::SeqEntry));
+  if (!P.chunks.empty())
+    std::memcpy(host.data() + P.chunk_off, P.chunks.data(), P.chunks.size() * sizeof(sgla::ChunkEntry));
+  hipError_t e = hipMemcpyAsync(ws, host.data(), bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "copying the sequence and chunk tables");
   return SGLA_OK;
 }
 
@@ -385,6 +385,13 @@ sgla_status sgla_chunk_bwd(const sgla_chunk_args* args, const void* q, const voi
   return ok();
 }
 
+size_t sgla_gla_chunk_fwd_workspace_size(const sgla_chunk_args* args, const int64_t* cu_seqlens_host) {
+  Plan P;
+  if (plan_shape(args, cu_seqlens_host, false, &P) != SGLA_OK) return 0;
+  g_last_error.clear();
+  return P.total_bytes;
+}
+
 sgla_status sgla_gla_chunk_fwd(const sgla_chunk_args* args, const void* q, const void* k, const void* v,
                                const float* gk, const float* initial_state, const int64_t* cu_seqlens_host,
                                void* o, float* final_state, void* workspace, size_t workspace_bytes,
@@ -444,11 +451,27 @@ sgla_status sgla_gla_chunk_fwd(const sgla_chunk_args* args, const void* q, const
   return ok();
 }
 
+// Normalizer workspace: the packed-sequence tables, then per (chunk, head) a
+// K-float z record and one log2 decay.
+struct NormPlan {
+  size_t zrec_off = 0, dlog_off = 0, total_bytes = 0;
+};
+
+NormPlan plan_norm(const sgla_chunk_args* a, const Plan& P) {
+  NormPlan N;
+  const size_t tasks = (size_t)P.num_chunks * a->H;
+  N.zrec_off = align_up(P.total_bytes, 256);
+  N.dlog_off = N.zrec_off + align_up(tasks * (size_t)a->K * sizeof(float), 256);
+  N.total_bytes = tasks == 0 ? P.total_bytes : N.dlog_off + align_up(tasks * sizeof(float), 256);
+  return N;
+}
+
 size_t sgla_chunk_normalizer_workspace_size(const sgla_chunk_args* args, const int64_t* cu_seqlens_host) {
   Plan P;
   if (plan_shape(args, cu_seqlens_host, false, &P) != SGLA_OK) return 0;
+  if (args->K <= 0) return 0;
   g_last_error.clear();
-  return P.total_bytes;
+  return plan_norm(args, P).total_bytes;
 }
 
 sgla_status sgla_chunk_normalizer(const sgla_chunk_args* args, const void* q, const void* k, const float* g,
@@ -473,8 +496,9 @@ sgla_status sgla_chunk_normalizer(const sgla_chunk_args* args, const void* q, co
     return fail(SGLA_ERR_INVALID_ARG, "output_final_state is set but final_z is NULL");
   if (any_tokens && !(aligned(q, 16) && aligned(k, 16)))
     return fail(SGLA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
-  if (P.packed && (workspace == nullptr || workspace_bytes < P.total_bytes))
-    return fail(SGLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", P.total_bytes, workspace_bytes);
+  const NormPlan NP = plan_norm(args, P);
+  if (NP.total_bytes > 0 && (workspace == nullptr || workspace_bytes < NP.total_bytes))
+    return fail(SGLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", NP.total_bytes, workspace_bytes);
   char* ws = static_cast<char*>(workspace);
   st = upload_tables(P, ws, stream);
   if (st != SGLA_OK) return st;
@@ -492,6 +516,8 @@ sgla_status sgla_chunk_normalizer(const sgla_chunk_args* args, const void* q, co
   p.K = a.K;
   p.qkv_bf16 = a.qkv_dtype == SGLA_BF16;
   p.seqs = layout_of(args, P, ws);
+  p.zrec = P.num_chunks > 0 ? reinterpret_cast<float*>(ws + NP.zrec_off) : nullptr;
+  p.dlog = P.num_chunks > 0 ? reinterpret_cast<float*>(ws + NP.dlog_off) : nullptr;
   hipError_t e = sgla::launch_chunk_normalizer(p, stream);
   if (e != hipSuccess) return hip_fail(e, "launching the normalizer kernel");
   return ok();

@@ -170,6 +170,8 @@ struct NormalizerParams {
   int32_t H, Hkv, K;
   int32_t qkv_bf16;
   SeqLayout seqs;
+  float* zrec;               // workspace [num_chunks, H, K]: chunk sums, then z entering each chunk
+  float* dlog;               // workspace [num_chunks, H]: each chunk's total log2 decay
 };
 
 struct StepNormalizerParams {

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SGLA_ABI_VERSION 3
+#define SGLA_ABI_VERSION 4
 
 typedef enum {
   SGLA_OK = 0,
@@ -206,12 +206,13 @@ sgla_status sgla_chunk_bwd(const sgla_chunk_args *args,
  *                   accurate for gk <= 0, the forget-gate range
  *   q [B, T, H, K]; k [B, T, Hkv, K]; v [B, T, Hkv, V]; o [B, T, H, V];
  *   initial_state / final_state [N, H, K, V] (or [N, H, V, K] with
- *   state_v_first); cu_seqlens_host and workspace as for
- *   sgla_chunk_normalizer (the packed-sequence table only:
- *   sgla_chunk_normalizer_workspace_size gives the bytes).
+ *   state_v_first); cu_seqlens_host as for sgla_chunk_fwd;
+ *   workspace >= sgla_gla_chunk_fwd_workspace_size(args, cu) bytes (the
+ *   packed-sequence table; 0 for dense input).
  * One launch, all products on the fp32 matrix cores.  Supported: K in {16,
  * 32, 64, 128}, V a multiple of 32, bf16 or float32 inputs, chunk_size 64.
  */
+size_t sgla_gla_chunk_fwd_workspace_size(const sgla_chunk_args *args, const int64_t *cu_seqlens_host);
 sgla_status sgla_gla_chunk_fwd(const sgla_chunk_args *args,
                                const void *q, const void *k, const void *v, const float *gk,
                                const float *initial_state, const int64_t *cu_seqlens_host,
@@ -238,7 +239,8 @@ sgla_status sgla_gla_chunk_fwd(const sgla_chunk_args *args,
  *   final_z         [N, H, K] float32, written when output_final_state is
  *                   nonzero (may alias initial_z exactly)
  *   workspace       >= sgla_chunk_normalizer_workspace_size(args, cu) bytes
- *                   (the packed-sequence table; 0 for dense input)
+ *                   (the packed-sequence table, then per (chunk, head) K + 1
+ *                   floats of chunk records; 0 when there are no tokens)
  * Supported: K in {16, 32, 64, 128, 256}, bf16 or float32 inputs.
  */
 size_t sgla_chunk_normalizer_workspace_size(const sgla_chunk_args *args, const int64_t *cu_seqlens_host);

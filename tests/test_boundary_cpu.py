@@ -59,7 +59,7 @@ def test_single_hip_runtime_in_process(G):
 
 
 def test_abi_version(G):
-    assert G.lib.sgla_abi_version() == G.ABI_VERSION == 3
+    assert G.lib.sgla_abi_version() == G.ABI_VERSION == 4
 
 
 class Buffers:
@@ -185,6 +185,26 @@ def test_workspace_size(G):
     bad = mkargs(G, K=96)
     assert G.lib.sgla_chunk_fwd_workspace_size(ctypes.byref(bad), None) == 0
     assert "K in" in G.lib.sgla_last_error().decode()
+
+
+def test_normalizer_and_gla_workspace_size(G):
+    """Normalizer: the tables, then per (chunk, head) K floats of z records and
+    one float of log2 decay, each piece 256-byte aligned.  Elementwise-gate
+    GLA: the tables only."""
+    al = lambda x: (x + 255) // 256 * 256
+    a = mkargs(G, B=2, T=100, H=3, K=64)
+    tasks = 2 * 2 * 3
+    assert G.lib.sgla_chunk_normalizer_workspace_size(ctypes.byref(a), None) == al(tasks * 64 * 4) + al(tasks * 4)
+    assert G.lib.sgla_gla_chunk_fwd_workspace_size(ctypes.byref(a), None) == 0
+    assert G.lib.sgla_chunk_normalizer_workspace_size(ctypes.byref(mkargs(G, B=2, T=0, H=3)), None) == 0
+    cu = np.array([0, 15, 100, 300], dtype=np.int64)
+    a = mkargs(G, B=1, T=300, H=3, N=3, K=128)
+    cup = ctypes.c_void_p(cu.ctypes.data)
+    tables = G.lib.sgla_gla_chunk_fwd_workspace_size(ctypes.byref(a), cup)
+    assert tables == G.lib.sgla_chunk_fwd_workspace_size(ctypes.byref(a), cup) > 0
+    tasks = (1 + 2 + 4) * 3
+    assert G.lib.sgla_chunk_normalizer_workspace_size(ctypes.byref(a), cup) == \
+        tables + al(tasks * 128 * 4) + al(tasks * 4)
 
 
 def test_workspace_size_wide_keys(G):
@@ -326,6 +346,7 @@ NORM_CASES = [
     ("kv heads not dividing", dict(H=2, Hkv=3), {}, SHAPE, "num_kv_heads"),
     ("final without pointer", {}, dict(zt=None), INVALID, "final_z is NULL"),
     ("workspace small", dict(N=2), dict(cu=[0, 64, 128], ws_bytes=8), WORKSPACE, "workspace"),
+    ("dense workspace small", {}, dict(ws_bytes=8), WORKSPACE, "workspace"),
 ]
 
 
