@@ -13,9 +13,9 @@
 // One 256-thread workgroup (4 waves) per (sequence, head, 32-wide V tile).
 // The K x 32 state lives in MFMA accumulators of the wave that owns its
 // 16 x 16 tiles, with a copy in LDS that all waves read as the q.h operand.
-// Per chunk: stage Q, K, V and the gates in LDS; the waves split the ten
-// causal 16 x 16 tiles of A, then the eight 16 x 16 output tiles and the
-// state tiles.
+// Per chunk: stage Q, K, V and the gates in LDS (from registers the previous
+// chunk loaded them into); the waves split the ten causal 16 x 16 tiles of A,
+// then the eight 16 x 16 output tiles and the state tiles.
 //
 // v_mfma_f32_16x16x4_f32 operands, per lane l with g = l / 16, r = l % 16:
 //   A operand A[m = r][k = g], B operand B[k = g][n = r],
@@ -81,7 +81,8 @@ chunk_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
     seq = rank;
   }
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  // wave index as a scalar, so per-wave tile choices are scalar branches
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g4 = lane >> 4;
   const int r = lane & 15;
@@ -117,36 +118,67 @@ chunk_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
   publish_state();
 
   const int nchunks = (len + C - 1) / C;
+  // ---- chunk staging registers: every thread's share of the Q, K and V
+  //      rows and (first wave) its token's log gate; rows past the chunk's
+  //      end read as zeros
+  constexpr int NQ4 = C * (K / 4) / NTHREADS;   // float4 pieces of Q (and K) per thread
+  constexpr int NV4 = C * (VT / 4) / NTHREADS;  // float4 pieces of the V tile per thread
+  static_assert(NQ4 * NTHREADS == C * (K / 4) && NV4 * NTHREADS == C * (VT / 4), "staging split");
+  f32x4 pq[NQ4], pk[NQ4], pv[NV4];
+  float pg = 0.f;
+  auto load_chunk = [&](int m) {
+    const int64_t t0 = bos + (int64_t)m * C;
+    const int cl = m < nchunks ? min(C, len - m * C) : 0;
+#pragma unroll
+    for (int u = 0; u < NQ4; ++u) {
+      const int i = tid + NTHREADS * u;
+      const int c = i / (K / 4), k4 = i % (K / 4);
+      pq[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      pk[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (c < cl) {
+        pq[u] = *reinterpret_cast<const f32x4*>(q + ((t0 + c) * H + hd) * (int64_t)K + 4 * k4);
+        pk[u] = *reinterpret_cast<const f32x4*>(k + ((t0 + c) * Hkv + hk) * (int64_t)K + 4 * k4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NV4; ++u) {
+      const int i = tid + NTHREADS * u;
+      const int c = i / (VT / 4), v4 = i % (VT / 4);
+      pv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (c < cl) pv[u] = *reinterpret_cast<const f32x4*>(v + ((t0 + c) * Hkv + hk) * (int64_t)V + vt * VT + 4 * v4);
+    }
+    pg = (g != nullptr && tid < cl) ? g[(t0 + tid) * H + hd] : 0.f;
+  };
+  load_chunk(0);
   for (int m = 0; m < nchunks; ++m) {
     const int64_t t0 = bos + (int64_t)m * C;
     const int cl = min(C, len - m * C);
-    // ---- stage the chunk (rows past its end read as zeros) ---------------
-    for (int i = tid; i < C * (K / 4); i += NTHREADS) {
+    // ---- stage the chunk -------------------------------------------------
+#pragma unroll
+    for (int u = 0; u < NQ4; ++u) {
+      const int i = tid + NTHREADS * u;
       const int c = i / (K / 4), k4 = i % (K / 4);
-      f32x4 xq = {0.f, 0.f, 0.f, 0.f}, xk = {0.f, 0.f, 0.f, 0.f};
-      if (c < cl) {
-        xq = *reinterpret_cast<const f32x4*>(q + ((t0 + c) * H + hd) * (int64_t)K + 4 * k4);
-        xk = *reinterpret_cast<const f32x4*>(k + ((t0 + c) * Hkv + hk) * (int64_t)K + 4 * k4);
-      }
-      *reinterpret_cast<f32x4*>(sQ + c * LDQ + 4 * k4) = xq;
-      *reinterpret_cast<f32x4*>(sK + c * LDQ + 4 * k4) = xk;
+      *reinterpret_cast<f32x4*>(sQ + c * LDQ + 4 * k4) = pq[u];
+      *reinterpret_cast<f32x4*>(sK + c * LDQ + 4 * k4) = pk[u];
     }
-    for (int i = tid; i < C * (VT / 4); i += NTHREADS) {
+#pragma unroll
+    for (int u = 0; u < NV4; ++u) {
+      const int i = tid + NTHREADS * u;
       const int c = i / (VT / 4), v4 = i % (VT / 4);
-      f32x4 xv = {0.f, 0.f, 0.f, 0.f};
-      if (c < cl) xv = *reinterpret_cast<const f32x4*>(v + ((t0 + c) * Hkv + hk) * (int64_t)V + vt * VT + 4 * v4);
-      *reinterpret_cast<f32x4*>(sV + c * LDV + 4 * v4) = xv;
+      *reinterpret_cast<f32x4*>(sV + c * LDV + 4 * v4) = pv[u];
     }
-    if (tid < C) {
+    if (w == 0) {
       // step (1): chunk-local cumulative log2 gate (padding rows add 0)
       float b;
-      if (g != nullptr) b = wave_cumsum_log2(tid < cl ? g[(t0 + tid) * H + hd] : 0.f);
+      if (g != nullptr) b = wave_cumsum_log2(pg);
       else b = (float)min(tid + 1, cl) * gam2;
       const float blast = __shfl(b, C - 1, 64);
       sG[tid] = b;
       sEb[tid] = exp2f(b) * scale;
       sDk[tid] = exp2f(blast - b);
     }
+    __syncthreads();
+    load_chunk(m + 1);   // in flight while this chunk computes
     __syncthreads();
 
     // ---- A tiles: (Q K^T) (.) M, scale folded in --------------------------
