@@ -462,7 +462,8 @@ def bench_gla(workload: str, steps: int, warmup: int, warm_seconds: float):
     nbytes += B * T * H * K * 4            # the per-key gates
     tf = flops / (ms * 1e-3) / 1e12
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": workload, "gate": "per-key gk", "kernel": "gla_chunk_fwd_kernel",
+    return {"workload": workload, "gate": "per-key gk", "kernel": "gla_prep_kernel+gla_chunk_fwd_kernel",
+            "launches_per_call": 2,
             "ms_per_call_mean": round(ms, 5), "ms_per_call_median": round(per[len(per) // 2], 5),
             "tokens_per_s": round(B * T / (ms * 1e-3), 1),
             "algorithmic_flops_per_call": int(flops), "algorithmic_bytes_per_call": int(nbytes),

@@ -26,10 +26,15 @@
 // Everything runs in fp32 (the state, the accumulation, the fp32 matrix
 // cores v_mfma_f32_16x16x4_f32), so the only rounding is fp32's.
 //
-// Work layout as the fp32 head-wise kernel: one workgroup of 4 waves per
-// (sequence, head, 32-wide V tile), the K x 32 state in MFMA accumulators
-// with an LDS copy read as the q.h operand; the next chunk's rows are loaded
-// into registers while the current chunk computes.
+// Two launches.  The preparation kernel, one 8-wave workgroup per (chunk,
+// head) and so parallel over every chunk, forms B and the 64 x 64 A of its
+// chunk (scale folded in, zeros above the diagonal) into the workspace.  The
+// chunk kernel then walks each sequence: one workgroup of 4 waves per
+// (sequence, head, 32-wide V tile), the K x 32 state in MFMA accumulators with
+// an LDS copy read as the q.h operand; it forms B again (a cheap per-key scan,
+// needed for the q and k scaling) and reads A with the chunk's rows, the next
+// chunk's rows and A being loaded into registers while the current chunk
+// computes.
 // v_mfma_f32_16x16x4_f32 operands, per lane l with g = l / 16, r = l % 16:
 //   A operand A[m = r][k = g], B operand B[k = g][n = r],
 //   result acc[i] = D[m = 4 g + i][n = r].
@@ -63,12 +68,175 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 template <typename TOut>
 __device__ __forceinline__ TOut out_cast(float x) { return (TOut)x; }
 
+// Chunk-local cumulative log2 gate of every key, in place over the log gates
+// staged in sB (row stride LD; padding rows hold 0, so they add nothing).
+// Thread (key a, part p) of NTH sums tokens [p TL, +TL) in double; the
+// parts' totals are exchanged through sTot (NTH floats), then each part
+// writes its running sums with the earlier parts' total added.  Ends with
+// the workgroup's barrier.
+template <int K, int NTH, int LD>
+__device__ __forceinline__ void key_cumsum_log2(float* sB, float* sTot) {
+  constexpr int NPART = NTH / K;      // token parts of the per-key scan
+  constexpr int TL = C / NPART;       // tokens per part
+  static_assert(NPART * K == NTH && TL * NPART == C, "scan split");
+  const int tid = threadIdx.x;
+  const int a = tid % K, p = tid / K;
+  float gv[TL];
+  double tot = 0.0;
+#pragma unroll
+  for (int u = 0; u < TL; ++u) {
+    gv[u] = sB[(p * TL + u) * LD + a];
+    tot += (double)gv[u];
+  }
+  sTot[p * K + a] = (float)tot;
+  __syncthreads();
+  double b = 0.0;
+  for (int pp = 0; pp < p; ++pp) b += (double)sTot[pp * K + a];
+#pragma unroll
+  for (int u = 0; u < TL; ++u) {
+    b += (double)gv[u];
+    sB[(p * TL + u) * LD + a] = (float)(b * kRcpLn2d);
+  }
+  __syncthreads();
+}
+
+constexpr int NTP = 512;   // preparation threads (8 waves)
+
+// Preparation: A of one (chunk, query head) into amat[chunk, hd], 64 x 64
+// row-major, scale folded in, zeros above the diagonal.
+template <int K, typename TIn>
+__global__ void __launch_bounds__(NTP)
+gla_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ gk,
+                float* __restrict__ amat, float scale, int32_t H, int32_t Hkv, SeqLayout seqs) {
+  constexpr int LDQ = K + 4;
+  __shared__ __attribute__((aligned(16))) float sQ[C * LDQ];
+  __shared__ __attribute__((aligned(16))) float sK[C * LDQ];
+  __shared__ __attribute__((aligned(16))) float sB[C * LDQ];   // gates, then B
+  __shared__ float sTot[NTP];
+
+  const UnitMap um = map_unit(blockIdx.x, 1, Hkv, H / Hkv, seqs.num_chunks);
+  if (!um.valid) return;
+  const int32_t chunk = um.rank;
+  const int hd = um.hd, hk = um.hk;
+  int64_t t0;
+  int cl;
+  if (seqs.chunk_table != nullptr) {
+    const ChunkEntry e = seqs.chunk_table[chunk];
+    t0 = e.t0;
+    cl = e.len;
+  } else {
+    const int32_t ncs = (seqs.T + C - 1) / C;
+    const int32_t row = chunk / ncs, m = chunk - row * ncs;
+    t0 = (int64_t)row * seqs.T + (int64_t)m * C;
+    cl = min(C, seqs.T - m * C);
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, g4 = lane >> 4, r = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+  {
+    RowTile<K, NTP, TIn> qt, kt;
+    RowTile<K, NTP, float> gt;
+    qt.load(q + (t0 * H + hd) * K, (int64_t)H * K, cl);
+    kt.load(k + (t0 * Hkv + hk) * K, (int64_t)Hkv * K, cl);
+    gt.load(gk + (t0 * H + hd) * K, (int64_t)H * K, cl);
+    qt.store(sQ, LDQ);
+    kt.store(sK, LDQ);
+    gt.store(sB, LDQ);
+  }
+  __syncthreads();
+  key_cumsum_log2<K, NTP, LDQ>(sB, sTot);
+
+  float* ab = amat + ((int64_t)chunk * H + hd) * (C * C);
+  if (w < 3) {
+    // ---- below the diagonal: blocks (I, J) in the order (1,0) (2,0) (2,1)
+    //      (3,0) (3,1) (3,2), two per wave as interleaved chains; the
+    //      reference token is the first of block I, so both factors are <= 1
+    auto block_ij = [](int bi, int& I, int& J) {
+      I = bi == 0 ? 1 : (bi < 3 ? 2 : 3);
+      J = bi == 0 ? 0 : (bi < 3 ? bi - 1 : bi - 3);
+    };
+    int I0, J0, I1, J1;
+    block_ij(2 * w, I0, J0);
+    block_ij(2 * w + 1, I1, J1);
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll 4
+    for (int ks = 0; ks < K / 4; ++ks) {
+      const int a = 4 * ks + g4;
+      const float br0 = sB[16 * I0 * LDQ + a], br1 = sB[16 * I1 * LDQ + a];
+      const int c0 = (16 * I0 + r) * LDQ + a, j0 = (16 * J0 + r) * LDQ + a;
+      const int c1 = (16 * I1 + r) * LDQ + a, j1 = (16 * J1 + r) * LDQ + a;
+      acc0 = mfma4(sQ[c0] * exp2_hw(sB[c0] - br0), sK[j0] * exp2_hw(br0 - sB[j0]), acc0);
+      acc1 = mfma4(sQ[c1] * exp2_hw(sB[c1] - br1), sK[j1] * exp2_hw(br1 - sB[j1]), acc1);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ab[(16 * I0 + 4 * g4 + i) * C + 16 * J0 + r] = acc0[i] * scale;
+      ab[(16 * I1 + 4 * g4 + i) * C + 16 * J1 + r] = acc1[i] * scale;
+    }
+  } else if (w < 7) {
+    // ---- on the diagonal: block I = w - 3, reference its middle token; a
+    //      block whose exponent span is too wide is formed elementwise -------
+    const int I = w - 3, rr = 16 * I + 8;
+    float span = 0.f;
+    for (int a = lane; a < K; a += 64) {
+      const float br = sB[rr * LDQ + a];
+      span = fmaxf(span, fmaxf(sB[(16 * I) * LDQ + a] - br, br - sB[(16 * I + 15) * LDQ + a]));
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) span = fmaxf(span, __shfl_xor(span, d, 64));
+    if (span <= kMaxSpan) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int ks = 0; ks < K / 4; ++ks) {
+        const int a = 4 * ks + g4;
+        const float br = sB[rr * LDQ + a];
+        const int ci = (16 * I + r) * LDQ + a;
+        acc = mfma4(sQ[ci] * exp2_hw(sB[ci] - br), sK[ci] * exp2_hw(br - sB[ci]), acc);
+      }
+      const int j = 16 * I + r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * I + 4 * g4 + i;
+        ab[c * C + j] = j <= c ? acc[i] * scale : 0.f;   // a select: an overflowed upper entry is dropped
+      }
+    } else {
+      // elementwise: one (c, j) entry of the block per lane and pass
+      for (int pp = 0; pp < 4; ++pp) {
+        const int e = lane + 64 * pp;
+        const int c = 16 * I + (e >> 4), j = 16 * I + (e & 15);
+        float x = 0.f;
+        if (j <= c) {
+          const f32x4* qc = reinterpret_cast<const f32x4*>(sQ + c * LDQ);
+          const f32x4* bc = reinterpret_cast<const f32x4*>(sB + c * LDQ);
+          const f32x4* kj = reinterpret_cast<const f32x4*>(sK + j * LDQ);
+          const f32x4* bj = reinterpret_cast<const f32x4*>(sB + j * LDQ);
+          for (int a4 = 0; a4 < K / 4; ++a4) {
+            const f32x4 qv = qc[a4], bcv = bc[a4], kv = kj[a4], bjv = bj[a4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x = fmaf(qv[u] * kv[u], exp2_hw(bcv[u] - bjv[u]), x);
+          }
+        }
+        ab[c * C + j] = x * scale;
+      }
+    }
+  } else {
+    // ---- the six blocks above the diagonal are zero ----------------------
+    for (int i = lane; i < 6 * 256; i += 64) {
+      const int tt = i >> 8, e = i & 255;
+      const int ctile = tt < 3 ? 0 : (tt < 5 ? 1 : 2);
+      const int jtile = tt < 3 ? tt + 1 : (tt < 5 ? tt - 1 : 3);
+      ab[(16 * ctile + (e >> 4)) * C + 16 * jtile + (e & 15)] = 0.f;
+    }
+  }
+}
+
 template <int K, typename TIn, typename TOut>
 __global__ void __launch_bounds__(NT)
 gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                      const TIn* __restrict__ v, const float* __restrict__ gk,
-                     const float* __restrict__ h0, TOut* __restrict__ o, float* __restrict__ ht,
-                     float scale, int32_t H, int32_t Hkv, int32_t V, StateLayout sl, SeqLayout seqs) {
+                     const float* __restrict__ h0, const float* __restrict__ amat, TOut* __restrict__ o,
+                     float* __restrict__ ht, float scale, int32_t H, int32_t Hkv, int32_t V, StateLayout sl,
+                     SeqLayout seqs) {
   constexpr int LDQ = K + 4;          // row stride of Q, K, B (floats; 16-byte rows)
   constexpr int NKT = K / 16;
   constexpr int NST = NKT * 2;        // 16 x 16 state tiles (x 2 column tiles)
@@ -76,42 +244,33 @@ gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   __shared__ __attribute__((aligned(16))) float sQ[C * LDQ];
   __shared__ __attribute__((aligned(16))) float sK[C * LDQ];
   __shared__ __attribute__((aligned(16))) float sB[C * LDQ];   // gates, then B
-  __shared__ float sV[C * LDV];
-  __shared__ float sA[C * LDA];
+  __shared__ __attribute__((aligned(16))) float sV[C * LDV];
+  __shared__ __attribute__((aligned(16))) float sA[C * LDA];
   __shared__ float sH[K * LDH];
-  constexpr int NPART = NT / K;       // token parts of the per-key scan
-  constexpr int TL = C / NPART;       // tokens per part
-  static_assert(NPART * K == NT && TL * NPART == C, "scan split");
   __shared__ float sTot[NT];
 
   const UnitMap um = map_unit(blockIdx.x, V / VT, Hkv, H / Hkv, seqs.num_seqs);
   if (!um.valid) return;
   const int hd = um.hd, hk = um.hk, vt = um.vt;
   int64_t bos;
-  int32_t len, seq;
+  int32_t len, seq, chunk0;
   if (seqs.seq_table != nullptr) {
     const SeqEntry e = seqs.seq_table[um.rank];
     bos = e.bos;
     len = e.len;
     seq = e.seq;
+    chunk0 = e.chunk0;
   } else {
     bos = (int64_t)um.rank * seqs.T;
     len = seqs.T;
     seq = um.rank;
+    chunk0 = um.rank * ((seqs.T + C - 1) / C);
   }
   const int tid = threadIdx.x;
   const int lane = tid & 63, g4 = lane >> 4, r = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int64_t su = ((int64_t)seq * H + hd) * K * V;
   auto sidx = [&](int row, int c) { return su + (int64_t)row * sl.rs + (int64_t)(vt * VT + c) * sl.cs; };
-
-  // blocks above the diagonal of A are never written: zero them once
-  for (int i = tid; i < 6 * 256; i += NT) {
-    const int tt = i >> 8, e = i & 255;
-    const int ctile = tt < 3 ? 0 : (tt < 5 ? 1 : 2);
-    const int jtile = tt < 3 ? tt + 1 : (tt < 5 ? tt - 1 : 3);
-    sA[(16 * ctile + (e >> 4)) * LDA + 16 * jtile + (e & 15)] = 0.f;
-  }
 
   f32x4 hs[SPW];
 #pragma unroll
@@ -137,10 +296,11 @@ gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   };
   publish_state();
 
-  // next chunk's rows, loaded one chunk ahead
+  // next chunk's rows and A, loaded one chunk ahead
   RowTile<K, NT, TIn> qt, kt;
   RowTile<K, NT, float> gt;
   RowTile<VT, NT, TIn> vtl;
+  RowTile<C, NT, float> at;
   const int nchunks = (len + C - 1) / C;
   auto load_chunk = [&](int m) {
     const int64_t t0 = bos + (int64_t)m * C;
@@ -149,6 +309,7 @@ gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     kt.load(k + (t0 * Hkv + hk) * K, (int64_t)Hkv * K, cl);
     gt.load(gk + (t0 * H + hd) * K, (int64_t)H * K, cl);
     vtl.load(v + (t0 * Hkv + hk) * V + vt * VT, (int64_t)Hkv * V, cl);
+    at.load(amat + ((int64_t)(chunk0 + m) * H + hd) * (C * C), C, C);
   };
   if (nchunks > 0) load_chunk(0);
 
@@ -178,122 +339,14 @@ gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     kt.store(sK, LDQ);
     gt.store(sB, LDQ);
     vtl.store(sV, LDV);
+    at.store(sA, LDA);
     if (m > 0) flush_out();
     __syncthreads();
 
-    // ---- B: chunk-local cumulative log2 gate of every key (padding adds 0).
-    //      Thread (key a, part p) sums tokens [p TL, +TL) in double; the parts'
-    //      totals are exchanged through LDS, then each part writes its running
-    //      sums with the earlier parts' total added ---------------------------
-    {
-      const int a = tid % K, p = tid / K;
-      float gv[TL];
-      double tot = 0.0;
-#pragma unroll
-      for (int u = 0; u < TL; ++u) {
-        gv[u] = sB[(p * TL + u) * LDQ + a];
-        tot += (double)gv[u];
-      }
-      sTot[p * K + a] = (float)tot;
-      __syncthreads();
-      double b = 0.0;
-      for (int pp = 0; pp < p; ++pp) b += (double)sTot[pp * K + a];
-#pragma unroll
-      for (int u = 0; u < TL; ++u) {
-        b += (double)gv[u];
-        sB[(p * TL + u) * LDQ + a] = (float)(b * kRcpLn2d);
-      }
-    }
-    __syncthreads();
-
-    // ---- A below the diagonal: blocks (I, J) in the order (1,0) (2,0) (2,1)
-    //      (3,0) (3,1) (3,2); waves 0 and 1 take two (interleaved), waves 2 and
-    //      3 one; the reference token is the first of block I ------------------
-    {
-      auto block_ij = [](int bi, int& I, int& J) {
-        I = bi == 0 ? 1 : (bi < 3 ? 2 : 3);
-        J = bi == 0 ? 0 : (bi < 3 ? bi - 1 : bi - 3);
-      };
-      auto store_block = [&](int I, int J, const f32x4& acc) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sA[(16 * I + 4 * g4 + i) * LDA + 16 * J + r] = acc[i] * scale;
-      };
-      int I0, J0, I1, J1;
-      block_ij(w, I0, J0);
-      block_ij(w < 2 ? w + 4 : w, I1, J1);
-      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-      if (w < 2) {
-#pragma unroll 4
-        for (int ks = 0; ks < K / 4; ++ks) {
-          const int a = 4 * ks + g4;
-          const float br0 = sB[16 * I0 * LDQ + a], br1 = sB[16 * I1 * LDQ + a];
-          const int c0 = (16 * I0 + r) * LDQ + a, j0 = (16 * J0 + r) * LDQ + a;
-          const int c1 = (16 * I1 + r) * LDQ + a, j1 = (16 * J1 + r) * LDQ + a;
-          acc0 = mfma4(sQ[c0] * exp2_hw(sB[c0] - br0), sK[j0] * exp2_hw(br0 - sB[j0]), acc0);
-          acc1 = mfma4(sQ[c1] * exp2_hw(sB[c1] - br1), sK[j1] * exp2_hw(br1 - sB[j1]), acc1);
-        }
-        store_block(I1, J1, acc1);
-      } else {
-#pragma unroll 4
-        for (int ks = 0; ks < K / 4; ++ks) {
-          const int a = 4 * ks + g4;
-          const float br0 = sB[16 * I0 * LDQ + a];
-          const int c0 = (16 * I0 + r) * LDQ + a, j0 = (16 * J0 + r) * LDQ + a;
-          acc0 = mfma4(sQ[c0] * exp2_hw(sB[c0] - br0), sK[j0] * exp2_hw(br0 - sB[j0]), acc0);
-        }
-      }
-      store_block(I0, J0, acc0);
-    }
-    // ---- A on the diagonal: wave w takes block w, reference its middle token;
-    //      a block whose exponent span is too wide is formed elementwise -------
-    {
-      const int I = w, rr = 16 * I + 8;
-      float span = 0.f;
-      for (int a = lane; a < K; a += 64) {
-        const float br = sB[rr * LDQ + a];
-        span = fmaxf(span, fmaxf(sB[(16 * I) * LDQ + a] - br, br - sB[(16 * I + 15) * LDQ + a]));
-      }
-#pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) span = fmaxf(span, __shfl_xor(span, d, 64));
-      if (span <= kMaxSpan) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int ks = 0; ks < K / 4; ++ks) {
-          const int a = 4 * ks + g4;
-          const float br = sB[rr * LDQ + a];
-          const int ci = (16 * I + r) * LDQ + a;
-          acc = mfma4(sQ[ci] * exp2_hw(sB[ci] - br), sK[ci] * exp2_hw(br - sB[ci]), acc);
-        }
-        const int j = 16 * I + r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = 16 * I + 4 * g4 + i;
-          sA[c * LDA + j] = j <= c ? acc[i] * scale : 0.f;   // a select: an overflowed upper entry is dropped
-        }
-      } else {
-        // elementwise: one (c, j) entry of the block per lane and pass
-        for (int pp = 0; pp < 4; ++pp) {
-          const int e = lane + 64 * pp;
-          const int c = 16 * I + (e >> 4), j = 16 * I + (e & 15);
-          float x = 0.f;
-          if (j <= c) {
-            const f32x4* qc = reinterpret_cast<const f32x4*>(sQ + c * LDQ);
-            const f32x4* bc = reinterpret_cast<const f32x4*>(sB + c * LDQ);
-            const f32x4* kj = reinterpret_cast<const f32x4*>(sK + j * LDQ);
-            const f32x4* bj = reinterpret_cast<const f32x4*>(sB + j * LDQ);
-            for (int a4 = 0; a4 < K / 4; ++a4) {
-              const f32x4 qv = qc[a4], bcv = bc[a4], kv = kj[a4], bjv = bj[a4];
-#pragma unroll
-              for (int u = 0; u < 4; ++u) x = fmaf(qv[u] * kv[u], exp2_hw(bcv[u] - bjv[u]), x);
-            }
-          }
-          sA[c * LDA + j] = x * scale;
-        }
-      }
-    }
-    __syncthreads();
+    // ---- B: chunk-local cumulative log2 gate of every key ------------------
+    key_cumsum_log2<K, NT, LDQ>(sB, sTot);
     // the next chunk's rows go into registers now: they are held through the
-    // rest of this chunk, not through the A phase
+    // rest of this chunk
     if (m + 1 < nchunks) load_chunk(m + 1);
 
     // ---- Q (.) 2^B and K (.) 2^(B_last - B), in place ------------------------
@@ -376,11 +429,17 @@ gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
 template <int K, typename TIn, typename TOut>
 hipError_t launch_k(const GlaFwdParams& p, hipStream_t stream) {
   if (p.seqs.num_seqs == 0) return hipSuccess;
+  if (p.seqs.num_chunks > 0) {
+    const dim3 pgrid((unsigned)unit_grid(p.seqs.num_chunks, p.Hkv, p.H / p.Hkv, 1));
+    hipLaunchKernelGGL((gla_prep_kernel<K, TIn>), pgrid, dim3(NTP), 0, stream,
+                       static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k), p.gk, p.amat, p.scale,
+                       p.H, p.Hkv, p.seqs);
+  }
   const dim3 grid((unsigned)unit_grid(p.seqs.num_seqs, p.Hkv, p.H / p.Hkv, p.V / VT));
   hipLaunchKernelGGL((gla_chunk_fwd_kernel<K, TIn, TOut>), grid, dim3(NT), 0, stream,
                      static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k),
-                     static_cast<const TIn*>(p.v), p.gk, p.h0, static_cast<TOut*>(p.o), p.ht, p.scale,
-                     p.H, p.Hkv, p.V, p.sl, p.seqs);
+                     static_cast<const TIn*>(p.v), p.gk, p.h0, p.amat, static_cast<TOut*>(p.o), p.ht,
+                     p.scale, p.H, p.Hkv, p.V, p.sl, p.seqs);
   return hipGetLastError();
 }
 

@@ -385,11 +385,20 @@ sgla_status sgla_chunk_bwd(const sgla_chunk_args* args, const void* q, const voi
   return ok();
 }
 
+// Elementwise-gate GLA workspace: the packed-sequence tables, then per
+// (chunk, query head) the 64 x 64 float32 decay-masked A of the chunk.
+size_t gla_workspace_bytes(const sgla_chunk_args* a, const Plan& P, size_t* amat_off) {
+  const size_t tasks = (size_t)P.num_chunks * a->H;
+  *amat_off = align_up(P.total_bytes, 256);
+  return tasks == 0 ? P.total_bytes : *amat_off + tasks * sgla::kChunk * sgla::kChunk * sizeof(float);
+}
+
 size_t sgla_gla_chunk_fwd_workspace_size(const sgla_chunk_args* args, const int64_t* cu_seqlens_host) {
   Plan P;
   if (plan_shape(args, cu_seqlens_host, false, &P) != SGLA_OK) return 0;
   g_last_error.clear();
-  return P.total_bytes;
+  size_t off = 0;
+  return gla_workspace_bytes(args, P, &off);
 }
 
 sgla_status sgla_gla_chunk_fwd(const sgla_chunk_args* args, const void* q, const void* k, const void* v,
@@ -416,8 +425,10 @@ sgla_status sgla_gla_chunk_fwd(const sgla_chunk_args* args, const void* q, const
     return fail(SGLA_ERR_INVALID_ARG, "output_final_state is set but final_state is NULL");
   if (any_tokens && !(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(gk, 16) && aligned(o, 16)))
     return fail(SGLA_ERR_INVALID_ARG, "q, k, v, gk and o must be 16-byte aligned");
-  if (P.packed && (workspace == nullptr || workspace_bytes < P.total_bytes))
-    return fail(SGLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", P.total_bytes, workspace_bytes);
+  size_t amat_off = 0;
+  const size_t need = gla_workspace_bytes(args, P, &amat_off);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(SGLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (final_state != nullptr && initial_state != nullptr && final_state != initial_state) {
     const size_t sb = (size_t)P.N * a.H * a.K * a.V * sizeof(float);
     const char* f0 = reinterpret_cast<const char*>(final_state);
@@ -445,6 +456,7 @@ sgla_status sgla_gla_chunk_fwd(const sgla_chunk_args* args, const void* q, const
   p.o_bf16 = a.o_dtype == SGLA_BF16;
   p.sl = state_layout(a);
   p.seqs = layout_of(args, P, ws);
+  p.amat = P.num_chunks > 0 ? reinterpret_cast<float*>(ws + amat_off) : nullptr;
   if (p.ht == nullptr && !any_tokens) return ok();
   hipError_t e = sgla::launch_gla_chunk_fwd(p, stream);
   if (e != hipSuccess) return hip_fail(e, "launching the elementwise-gate GLA kernel");

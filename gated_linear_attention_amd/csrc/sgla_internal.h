@@ -152,6 +152,7 @@ struct GlaFwdParams {
   int32_t o_bf16;
   StateLayout sl;
   SeqLayout seqs;
+  float* amat;               // workspace [num_chunks, H, 64, 64]: decay-masked, scaled A per chunk
 };
 
 hipError_t launch_gla_chunk_fwd(const GlaFwdParams& p, hipStream_t stream);

@@ -208,8 +208,10 @@ sgla_status sgla_chunk_bwd(const sgla_chunk_args *args,
  *   initial_state / final_state [N, H, K, V] (or [N, H, V, K] with
  *   state_v_first); cu_seqlens_host as for sgla_chunk_fwd;
  *   workspace >= sgla_gla_chunk_fwd_workspace_size(args, cu) bytes (the
- *   packed-sequence table; 0 for dense input).
- * One launch, all products on the fp32 matrix cores.  Supported: K in {16,
+ *   packed-sequence table, then a 64 x 64 float32 matrix per (chunk, head);
+ *   0 when there are no tokens).
+ * Two launches (per-chunk A in parallel over chunks, then the chunk chain),
+ * all products on the fp32 matrix cores.  Supported: K in {16,
  * 32, 64, 128}, V a multiple of 32, bf16 or float32 inputs, chunk_size 64.
  */
 size_t sgla_gla_chunk_fwd_workspace_size(const sgla_chunk_args *args, const int64_t *cu_seqlens_host);

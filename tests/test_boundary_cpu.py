@@ -190,19 +190,22 @@ def test_workspace_size(G):
 def test_normalizer_and_gla_workspace_size(G):
     """Normalizer: the tables, then per (chunk, head) K floats of z records and
     one float of log2 decay, each piece 256-byte aligned.  Elementwise-gate
-    GLA: the tables only."""
+    GLA: the tables, then a 64 x 64 float32 A per (chunk, head)."""
     al = lambda x: (x + 255) // 256 * 256
     a = mkargs(G, B=2, T=100, H=3, K=64)
     tasks = 2 * 2 * 3
     assert G.lib.sgla_chunk_normalizer_workspace_size(ctypes.byref(a), None) == al(tasks * 64 * 4) + al(tasks * 4)
-    assert G.lib.sgla_gla_chunk_fwd_workspace_size(ctypes.byref(a), None) == 0
-    assert G.lib.sgla_chunk_normalizer_workspace_size(ctypes.byref(mkargs(G, B=2, T=0, H=3)), None) == 0
+    assert G.lib.sgla_gla_chunk_fwd_workspace_size(ctypes.byref(a), None) == tasks * 64 * 64 * 4
+    a0 = mkargs(G, B=2, T=0, H=3)
+    assert G.lib.sgla_chunk_normalizer_workspace_size(ctypes.byref(a0), None) == 0
+    assert G.lib.sgla_gla_chunk_fwd_workspace_size(ctypes.byref(a0), None) == 0
     cu = np.array([0, 15, 100, 300], dtype=np.int64)
     a = mkargs(G, B=1, T=300, H=3, N=3, K=128)
     cup = ctypes.c_void_p(cu.ctypes.data)
-    tables = G.lib.sgla_gla_chunk_fwd_workspace_size(ctypes.byref(a), cup)
-    assert tables == G.lib.sgla_chunk_fwd_workspace_size(ctypes.byref(a), cup) > 0
+    tables = G.lib.sgla_chunk_fwd_workspace_size(ctypes.byref(a), cup)
+    assert tables > 0
     tasks = (1 + 2 + 4) * 3
+    assert G.lib.sgla_gla_chunk_fwd_workspace_size(ctypes.byref(a), cup) == tables + tasks * 64 * 64 * 4
     assert G.lib.sgla_chunk_normalizer_workspace_size(ctypes.byref(a), cup) == \
         tables + al(tasks * 128 * 4) + al(tasks * 4)
 
