@@ -102,15 +102,43 @@ __device__ __forceinline__ void key_cumsum_log2(float* sB, float* sTot) {
 
 constexpr int NTP = 512;   // preparation threads (8 waves)
 
-// Preparation: A of one (chunk, query head) into amat[chunk, hd], 64 x 64
-// row-major, scale folded in, zeros above the diagonal.
-template <int K, typename TIn>
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 pair of x: hi = bf16(x), lo = bf16(x - hi), both rounded to nearest
+// even.
+__device__ __forceinline__ void split1(float x, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)x;
+  lo = (__bf16)(x - (float)hi);
+}
+
+// split1 of a and b, packed two to a word (a in the low half)
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  __bf16 ha, la, hb, lb;
+  split1(a, ha, la);
+  split1(b, hb, lb);
+  hi = (uint32_t)__builtin_bit_cast(unsigned short, ha) | ((uint32_t)__builtin_bit_cast(unsigned short, hb) << 16);
+  lo = (uint32_t)__builtin_bit_cast(unsigned short, la) | ((uint32_t)__builtin_bit_cast(unsigned short, lb) << 16);
+}
+
+// Preparation of one (chunk, query head): A, 64 x 64 row-major, scale folded
+// in, zeros above the diagonal -- as float32 into amat (HL = false, for the
+// fp32 chain), or (HL = true, for the bf16 chain) as bf16 hi/lo planes into
+// a_hl together with q~ = scale q (.) 2^B and k~ = k (.) 2^(B_last - B) as
+// hi/lo planes into qk_hl and the per-key chunk decay 2^B_last into dl.
+template <int K, typename TIn, bool HL>
 __global__ void __launch_bounds__(NTP)
 gla_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ gk,
-                float* __restrict__ amat, float scale, int32_t H, int32_t Hkv, SeqLayout seqs) {
-  constexpr int LDQ = K + 4;
-  __shared__ __attribute__((aligned(16))) float sQ[C * LDQ];
-  __shared__ __attribute__((aligned(16))) float sK[C * LDQ];
+                float* __restrict__ amat, __bf16* __restrict__ qk_hl, __bf16* __restrict__ a_hl,
+                float* __restrict__ dl, float scale, int32_t H, int32_t Hkv, SeqLayout seqs) {
+  constexpr int LDQ = K + 4;                    // sB row stride (floats)
+  constexpr int EPL = 16 / (int)sizeof(TIn);    // elements per 16-byte piece
+  constexpr int LDX = K + EPL;                  // q / k row stride (elements; 16-byte rows)
+  constexpr int PR = K / EPL;                   // pieces per row
+  constexpr int NPC = (C * PR + NTP - 1) / NTP; // pieces per thread
+  // q and k stay in their input type in LDS (bf16: half the space, so two
+  // workgroups fit a CU); the gates are float
+  __shared__ __attribute__((aligned(16))) TIn sQ[C * LDX];
+  __shared__ __attribute__((aligned(16))) TIn sK[C * LDX];
   __shared__ __attribute__((aligned(16))) float sB[C * LDQ];   // gates, then B
   __shared__ float sTot[NTP];
 
@@ -134,19 +162,85 @@ gla_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
   const int lane = tid & 63, g4 = lane >> 4, r = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   {
-    RowTile<K, NTP, TIn> qt, kt;
+    // rows past the chunk's end are zero
+    uint4 qx[NPC], kx[NPC];
+    const TIn* qb = q + (t0 * H + hd) * K;
+    const TIn* kb = k + (t0 * Hkv + hk) * K;
+#pragma unroll
+    for (int u = 0; u < NPC; ++u) {
+      const int p = tid + NTP * u;
+      const int c = p / PR, e = (p % PR) * EPL;
+      qx[u] = make_uint4(0u, 0u, 0u, 0u);
+      kx[u] = make_uint4(0u, 0u, 0u, 0u);
+      if ((C * PR % NTP == 0 || p < C * PR) && c < cl) {
+        qx[u] = *reinterpret_cast<const uint4*>(qb + c * (int64_t)H * K + e);
+        kx[u] = *reinterpret_cast<const uint4*>(kb + c * (int64_t)Hkv * K + e);
+      }
+    }
     RowTile<K, NTP, float> gt;
-    qt.load(q + (t0 * H + hd) * K, (int64_t)H * K, cl);
-    kt.load(k + (t0 * Hkv + hk) * K, (int64_t)Hkv * K, cl);
     gt.load(gk + (t0 * H + hd) * K, (int64_t)H * K, cl);
-    qt.store(sQ, LDQ);
-    kt.store(sK, LDQ);
+#pragma unroll
+    for (int u = 0; u < NPC; ++u) {
+      const int p = tid + NTP * u;
+      if (C * PR % NTP == 0 || p < C * PR) {
+        *reinterpret_cast<uint4*>(sQ + (p / PR) * LDX + (p % PR) * EPL) = qx[u];
+        *reinterpret_cast<uint4*>(sK + (p / PR) * LDX + (p % PR) * EPL) = kx[u];
+      }
+    }
     gt.store(sB, LDQ);
   }
   __syncthreads();
   key_cumsum_log2<K, NTP, LDQ>(sB, sTot);
+  auto fq = [&](int c, int a) { return (float)sQ[c * LDX + a]; };
+  auto fk = [&](int c, int a) { return (float)sK[c * LDX + a]; };
 
-  float* ab = amat + ((int64_t)chunk * H + hd) * (C * C);
+  const int64_t rec = (int64_t)chunk * H + hd;
+  float* ab = HL ? nullptr : amat + rec * (C * C);
+  __bf16* ahl = HL ? a_hl + rec * (2 * C * C) : nullptr;
+  auto put_a = [&](int c, int j, float x) {
+    if constexpr (HL) {
+      __bf16 hi, lo;
+      split1(x, hi, lo);
+      ahl[c * C + j] = hi;
+      ahl[C * C + c * C + j] = lo;
+    } else {
+      ab[c * C + j] = x;
+    }
+  };
+  if constexpr (HL) {
+    // q~ and k~, eight keys of one row per thread and step, as 16-byte stores
+    // of each plane (rows past the chunk's end are zero in sQ and sK); the
+    // chunk's decay per key
+    __bf16* qo = qk_hl + rec * (4 * C * K);
+    __bf16* ko = qo + 2 * C * K;
+    for (int i = tid; i < C * K / 8; i += NTP) {
+      const int c = i / (K / 8), a0 = (i % (K / 8)) * 8;
+      u32x4 qh, ql, kh, kl;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float xq[2], xk[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int a = a0 + e + u;
+          const float b = sB[c * LDQ + a];
+          xq[u] = scale * fq(c, a) * exp2_hw(b);
+          xk[u] = fk(c, a) * exp2_hw(sB[(C - 1) * LDQ + a] - b);
+        }
+        uint32_t h2, l2;
+        split2(xq[0], xq[1], h2, l2);
+        qh[e / 2] = h2;
+        ql[e / 2] = l2;
+        split2(xk[0], xk[1], h2, l2);
+        kh[e / 2] = h2;
+        kl[e / 2] = l2;
+      }
+      *reinterpret_cast<u32x4*>(qo + 8 * i) = qh;
+      *reinterpret_cast<u32x4*>(qo + C * K + 8 * i) = ql;
+      *reinterpret_cast<u32x4*>(ko + 8 * i) = kh;
+      *reinterpret_cast<u32x4*>(ko + C * K + 8 * i) = kl;
+    }
+    for (int a = tid; a < K; a += NTP) dl[rec * K + a] = exp2_hw(sB[(C - 1) * LDQ + a]);
+  }
   if (w < 3) {
     // ---- below the diagonal: blocks (I, J) in the order (1,0) (2,0) (2,1)
     //      (3,0) (3,1) (3,2), two per wave as interleaved chains; the
@@ -163,15 +257,14 @@ gla_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
     for (int ks = 0; ks < K / 4; ++ks) {
       const int a = 4 * ks + g4;
       const float br0 = sB[16 * I0 * LDQ + a], br1 = sB[16 * I1 * LDQ + a];
-      const int c0 = (16 * I0 + r) * LDQ + a, j0 = (16 * J0 + r) * LDQ + a;
-      const int c1 = (16 * I1 + r) * LDQ + a, j1 = (16 * J1 + r) * LDQ + a;
-      acc0 = mfma4(sQ[c0] * exp2_hw(sB[c0] - br0), sK[j0] * exp2_hw(br0 - sB[j0]), acc0);
-      acc1 = mfma4(sQ[c1] * exp2_hw(sB[c1] - br1), sK[j1] * exp2_hw(br1 - sB[j1]), acc1);
+      const int c0 = 16 * I0 + r, j0 = 16 * J0 + r, c1 = 16 * I1 + r, j1 = 16 * J1 + r;
+      acc0 = mfma4(fq(c0, a) * exp2_hw(sB[c0 * LDQ + a] - br0), fk(j0, a) * exp2_hw(br0 - sB[j0 * LDQ + a]), acc0);
+      acc1 = mfma4(fq(c1, a) * exp2_hw(sB[c1 * LDQ + a] - br1), fk(j1, a) * exp2_hw(br1 - sB[j1 * LDQ + a]), acc1);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ab[(16 * I0 + 4 * g4 + i) * C + 16 * J0 + r] = acc0[i] * scale;
-      ab[(16 * I1 + 4 * g4 + i) * C + 16 * J1 + r] = acc1[i] * scale;
+      put_a(16 * I0 + 4 * g4 + i, 16 * J0 + r, acc0[i] * scale);
+      put_a(16 * I1 + 4 * g4 + i, 16 * J1 + r, acc1[i] * scale);
     }
   } else if (w < 7) {
     // ---- on the diagonal: block I = w - 3, reference its middle token; a
@@ -190,14 +283,14 @@ gla_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
       for (int ks = 0; ks < K / 4; ++ks) {
         const int a = 4 * ks + g4;
         const float br = sB[rr * LDQ + a];
-        const int ci = (16 * I + r) * LDQ + a;
-        acc = mfma4(sQ[ci] * exp2_hw(sB[ci] - br), sK[ci] * exp2_hw(br - sB[ci]), acc);
+        const int ci = 16 * I + r;
+        acc = mfma4(fq(ci, a) * exp2_hw(sB[ci * LDQ + a] - br), fk(ci, a) * exp2_hw(br - sB[ci * LDQ + a]), acc);
       }
       const int j = 16 * I + r;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = 16 * I + 4 * g4 + i;
-        ab[c * C + j] = j <= c ? acc[i] * scale : 0.f;   // a select: an overflowed upper entry is dropped
+        put_a(c, j, j <= c ? acc[i] * scale : 0.f);   // a select: an overflowed upper entry is dropped
       }
     } else {
       // elementwise: one (c, j) entry of the block per lane and pass
@@ -206,17 +299,10 @@ gla_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
         const int c = 16 * I + (e >> 4), j = 16 * I + (e & 15);
         float x = 0.f;
         if (j <= c) {
-          const f32x4* qc = reinterpret_cast<const f32x4*>(sQ + c * LDQ);
-          const f32x4* bc = reinterpret_cast<const f32x4*>(sB + c * LDQ);
-          const f32x4* kj = reinterpret_cast<const f32x4*>(sK + j * LDQ);
-          const f32x4* bj = reinterpret_cast<const f32x4*>(sB + j * LDQ);
-          for (int a4 = 0; a4 < K / 4; ++a4) {
-            const f32x4 qv = qc[a4], bcv = bc[a4], kv = kj[a4], bjv = bj[a4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) x = fmaf(qv[u] * kv[u], exp2_hw(bcv[u] - bjv[u]), x);
-          }
+          for (int a = 0; a < K; ++a)
+            x = fmaf(fq(c, a) * fk(j, a), exp2_hw(sB[c * LDQ + a] - sB[j * LDQ + a]), x);
         }
-        ab[c * C + j] = x * scale;
+        put_a(c, j, x * scale);
       }
     }
   } else {
@@ -225,7 +311,7 @@ gla_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
       const int tt = i >> 8, e = i & 255;
       const int ctile = tt < 3 ? 0 : (tt < 5 ? 1 : 2);
       const int jtile = tt < 3 ? tt + 1 : (tt < 5 ? tt - 1 : 3);
-      ab[(16 * ctile + (e >> 4)) * C + 16 * jtile + (e & 15)] = 0.f;
+      put_a(16 * ctile + (e >> 4), 16 * jtile + (e & 15), 0.f);
     }
   }
 }
@@ -429,11 +515,24 @@ gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
 template <int K, typename TIn, typename TOut>
 hipError_t launch_k(const GlaFwdParams& p, hipStream_t stream) {
   if (p.seqs.num_seqs == 0) return hipSuccess;
+  const bool hl = gla_bf16_chain(sizeof(TIn) == 2, K, p.V);
   if (p.seqs.num_chunks > 0) {
     const dim3 pgrid((unsigned)unit_grid(p.seqs.num_chunks, p.Hkv, p.H / p.Hkv, 1));
-    hipLaunchKernelGGL((gla_prep_kernel<K, TIn>), pgrid, dim3(NTP), 0, stream,
-                       static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k), p.gk, p.amat, p.scale,
-                       p.H, p.Hkv, p.seqs);
+    if (hl) {
+      hipLaunchKernelGGL((gla_prep_kernel<K, TIn, true>), pgrid, dim3(NTP), 0, stream,
+                         static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k), p.gk, nullptr,
+                         static_cast<__bf16*>(p.qk_hl), static_cast<__bf16*>(p.a_hl), p.dl, p.scale, p.H,
+                         p.Hkv, p.seqs);
+    } else {
+      hipLaunchKernelGGL((gla_prep_kernel<K, TIn, false>), pgrid, dim3(NTP), 0, stream,
+                         static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k), p.gk, p.amat, nullptr,
+                         nullptr, nullptr, p.scale, p.H, p.Hkv, p.seqs);
+    }
+  }
+  if (hl) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_gla_chain_bf16(p, stream);
   }
   const dim3 grid((unsigned)unit_grid(p.seqs.num_seqs, p.Hkv, p.H / p.Hkv, p.V / VT));
   hipLaunchKernelGGL((gla_chunk_fwd_kernel<K, TIn, TOut>), grid, dim3(NT), 0, stream,

@@ -386,19 +386,37 @@ sgla_status sgla_chunk_bwd(const sgla_chunk_args* args, const void* q, const voi
 }
 
 // Elementwise-gate GLA workspace: the packed-sequence tables, then per
-// (chunk, query head) the 64 x 64 float32 decay-masked A of the chunk.
-size_t gla_workspace_bytes(const sgla_chunk_args* a, const Plan& P, size_t* amat_off) {
+// (chunk, query head) the preparation kernel's records: the 64 x 64 float32
+// A (fp32 chain), or bf16 hi/lo planes of q~, k~ and A plus K floats of decay
+// (bf16 chain).
+struct GlaPlan {
+  size_t amat_off = 0, qk_off = 0, a_off = 0, dl_off = 0, total_bytes = 0;
+};
+
+GlaPlan plan_gla(const sgla_chunk_args* a, const Plan& P) {
+  GlaPlan G;
   const size_t tasks = (size_t)P.num_chunks * a->H;
-  *amat_off = align_up(P.total_bytes, 256);
-  return tasks == 0 ? P.total_bytes : *amat_off + tasks * sgla::kChunk * sgla::kChunk * sizeof(float);
+  const size_t C = sgla::kChunk;
+  if (tasks == 0) {
+    G.total_bytes = P.total_bytes;
+    return G;
+  }
+  G.amat_off = G.qk_off = align_up(P.total_bytes, 256);
+  if (sgla::gla_bf16_chain(a->qkv_dtype == SGLA_BF16, a->K, a->V)) {
+    G.a_off = G.qk_off + tasks * 4 * C * (size_t)a->K * 2;
+    G.dl_off = G.a_off + tasks * 2 * C * C * 2;
+    G.total_bytes = G.dl_off + tasks * (size_t)a->K * sizeof(float);
+  } else {
+    G.total_bytes = G.amat_off + tasks * C * C * sizeof(float);
+  }
+  return G;
 }
 
 size_t sgla_gla_chunk_fwd_workspace_size(const sgla_chunk_args* args, const int64_t* cu_seqlens_host) {
   Plan P;
   if (plan_shape(args, cu_seqlens_host, false, &P) != SGLA_OK) return 0;
   g_last_error.clear();
-  size_t off = 0;
-  return gla_workspace_bytes(args, P, &off);
+  return plan_gla(args, P).total_bytes;
 }
 
 sgla_status sgla_gla_chunk_fwd(const sgla_chunk_args* args, const void* q, const void* k, const void* v,
@@ -425,8 +443,8 @@ sgla_status sgla_gla_chunk_fwd(const sgla_chunk_args* args, const void* q, const
     return fail(SGLA_ERR_INVALID_ARG, "output_final_state is set but final_state is NULL");
   if (any_tokens && !(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(gk, 16) && aligned(o, 16)))
     return fail(SGLA_ERR_INVALID_ARG, "q, k, v, gk and o must be 16-byte aligned");
-  size_t amat_off = 0;
-  const size_t need = gla_workspace_bytes(args, P, &amat_off);
+  const GlaPlan GP = plan_gla(args, P);
+  const size_t need = GP.total_bytes;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(SGLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (final_state != nullptr && initial_state != nullptr && final_state != initial_state) {
@@ -456,7 +474,12 @@ sgla_status sgla_gla_chunk_fwd(const sgla_chunk_args* args, const void* q, const
   p.o_bf16 = a.o_dtype == SGLA_BF16;
   p.sl = state_layout(a);
   p.seqs = layout_of(args, P, ws);
-  p.amat = P.num_chunks > 0 ? reinterpret_cast<float*>(ws + amat_off) : nullptr;
+  const bool any_chunks = P.num_chunks > 0;
+  const bool bf16_chain = sgla::gla_bf16_chain(p.qkv_bf16 != 0, a.K, a.V);
+  p.amat = any_chunks && !bf16_chain ? reinterpret_cast<float*>(ws + GP.amat_off) : nullptr;
+  p.qk_hl = any_chunks && bf16_chain ? ws + GP.qk_off : nullptr;
+  p.a_hl = any_chunks && bf16_chain ? ws + GP.a_off : nullptr;
+  p.dl = any_chunks && bf16_chain ? reinterpret_cast<float*>(ws + GP.dl_off) : nullptr;
   if (p.ht == nullptr && !any_tokens) return ok();
   hipError_t e = sgla::launch_gla_chunk_fwd(p, stream);
   if (e != hipSuccess) return hip_fail(e, "launching the elementwise-gate GLA kernel");

@@ -152,10 +152,22 @@ struct GlaFwdParams {
   int32_t o_bf16;
   StateLayout sl;
   SeqLayout seqs;
-  float* amat;               // workspace [num_chunks, H, 64, 64]: decay-masked, scaled A per chunk
+  float* amat;               // fp32 chain: workspace [num_chunks, H, 64, 64] decay-masked, scaled A
+  // bf16 chain (gla_bf16_chain): per (chunk, query head) records written by
+  // the preparation kernel, each a bf16 hi plane followed by its lo plane
+  void* qk_hl;               // [num_chunks, H, 2 (q~, k~), 2, 64, K]
+  void* a_hl;                // [num_chunks, H, 2, 64, 64]
+  float* dl;                 // [num_chunks, H, K]: 2^(chunk's total log2 decay) per key
 };
 
+// The bf16 chain (bf16 matrix cores, hi/lo operands) serves bf16 inputs with
+// K in {64, 128} and V a multiple of 64; everything else takes the fp32 chain.
+inline bool gla_bf16_chain(bool qkv_bf16, int32_t K, int32_t V) {
+  return qkv_bf16 && (K == 64 || K == 128) && V % 64 == 0;
+}
+
 hipError_t launch_gla_chunk_fwd(const GlaFwdParams& p, hipStream_t stream);
+hipError_t launch_gla_chain_bf16(const GlaFwdParams& p, hipStream_t stream);
 
 // Running normalizer (the ones column of the augmented value): den [T_total,
 // H] = scale q . z, z [N, H, K] carried from z0 to zt.

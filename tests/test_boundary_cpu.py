@@ -190,12 +190,18 @@ def test_workspace_size(G):
 def test_normalizer_and_gla_workspace_size(G):
     """Normalizer: the tables, then per (chunk, head) K floats of z records and
     one float of log2 decay, each piece 256-byte aligned.  Elementwise-gate
-    GLA: the tables, then a 64 x 64 float32 A per (chunk, head)."""
+    GLA: the tables, then per (chunk, head) a 64 x 64 float32 A (fp32 chain:
+    float32 inputs, K < 64 or V not a multiple of 64) or bf16 hi/lo planes of
+    q~, k~ (64 x K each) and A plus K floats of decay (bf16 chain)."""
     al = lambda x: (x + 255) // 256 * 256
     a = mkargs(G, B=2, T=100, H=3, K=64)
     tasks = 2 * 2 * 3
     assert G.lib.sgla_chunk_normalizer_workspace_size(ctypes.byref(a), None) == al(tasks * 64 * 4) + al(tasks * 4)
-    assert G.lib.sgla_gla_chunk_fwd_workspace_size(ctypes.byref(a), None) == tasks * 64 * 64 * 4
+    bf16_chain = lambda K: 4 * 64 * K * 2 + 2 * 64 * 64 * 2 + K * 4
+    assert G.lib.sgla_gla_chunk_fwd_workspace_size(ctypes.byref(a), None) == tasks * bf16_chain(64)
+    for over in (dict(qkv=F32), dict(V=96), dict(K=32)):
+        af = mkargs(G, **dict(dict(B=2, T=100, H=3, K=64), **over))
+        assert G.lib.sgla_gla_chunk_fwd_workspace_size(ctypes.byref(af), None) == tasks * 64 * 64 * 4, over
     a0 = mkargs(G, B=2, T=0, H=3)
     assert G.lib.sgla_chunk_normalizer_workspace_size(ctypes.byref(a0), None) == 0
     assert G.lib.sgla_gla_chunk_fwd_workspace_size(ctypes.byref(a0), None) == 0
@@ -205,7 +211,7 @@ def test_normalizer_and_gla_workspace_size(G):
     tables = G.lib.sgla_chunk_fwd_workspace_size(ctypes.byref(a), cup)
     assert tables > 0
     tasks = (1 + 2 + 4) * 3
-    assert G.lib.sgla_gla_chunk_fwd_workspace_size(ctypes.byref(a), cup) == tables + tasks * 64 * 64 * 4
+    assert G.lib.sgla_gla_chunk_fwd_workspace_size(ctypes.byref(a), cup) == tables + tasks * bf16_chain(128)
     assert G.lib.sgla_chunk_normalizer_workspace_size(ctypes.byref(a), cup) == \
         tables + al(tasks * 128 * 4) + al(tasks * 4)
 

@@ -38,6 +38,12 @@ CASES = [
     (small("empty", T=0, initial_state=True), 1.0),
     (small("varlen", B=1, T=0, K=64, V=64, fixed_lengths=(15, 0, 1, 85, 200), initial_state=True), 1.0),
     (small("gqa", H=4, Hkv=2, K=64, V=32, T=130, initial_state=True), 1.0),
+    # bf16 inputs with K in {64, 128} and V a multiple of 64 take the bf16
+    # chain; the cases above with V = 32 or 96, or K < 64, the fp32 chain
+    (small("k128_v128_strong", K=128, V=128, T=150, initial_state=True), 0.1),
+    (small("k64_v128_weak", K=64, V=128, T=100, initial_state=True), 10.0),
+    (small("gqa_v64", H=4, Hkv=2, K=64, V=64, T=130, initial_state=True), 1.0),
+    (small("varlen_k128_v64", B=1, T=0, K=128, V=64, fixed_lengths=(64, 1, 0, 129), initial_state=True), 1.0),
     (small("f32_k32", dtype="f32", K=32, V=64, T=150, initial_state=True), 1.0),
     (small("f32_k128_strong", dtype="f32", K=128, V=32, T=100), 0.1),
 ]
