@@ -303,6 +303,13 @@ def bwd_algorithmic(inp) -> tuple[float, float]:
 
 
 def bench_backward(workload: str, steps: int, warmup: int, warm_seconds: float):
+    """sgla_chunk_bwd (dq, dk, dv, dg or dg_gamma, dh0) on a chunked workload.
+    bf16 inputs with K in {64, 128} run both passes on the bf16 matrix cores;
+    at their algorithmic intensity (about 78 flop/B at K = V = 128), far
+    below the bf16 ridge, the call is priced against HBM with its
+    algorithmic bytes (the per-chunk state records the state pass writes and
+    the gradient pass reads are design traffic on top, not counted).  Other
+    inputs run on the fp32 matrix cores and are priced against their peak."""
     import ctypes
 
     import numpy as np
@@ -361,16 +368,28 @@ def bench_backward(workload: str, steps: int, warmup: int, warm_seconds: float):
     nbytes, flops = bwd_algorithmic(inp)
     tf = flops / (ms * 1e-3) / 1e12
     gbs = nbytes / (ms * 1e-3) / 1e9
+    bf16_path = inp["dtype"] == "bf16" and K in (64, 128)
+    if bf16_path:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": F32_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / F32_MFMA_PEAK_TFLOPS, 4), "dtype": "f32"}
+    kern = ("chunk_bwd_state_bf16_kernel+chunk_bwd_grad_bf16_kernel" if bf16_path
+            else "chunk_bwd_state_kernel+chunk_bwd_grad_kernel")
+    n_chunks = sum(-(-int(L) // 64) for L in (np.diff(inp["cu_seqlens"]) if inp["cu_seqlens"] is not None
+                                                 else [T] * B))
     return {"workload": workload, "B": B, "T": T, "H": H, "K": K, "V": V, "num_seqs": N,
-            "kernel": "chunk_bwd_state_kernel+chunk_bwd_grad_kernel",
+            "kernel": kern,
             "launches_per_call": 2 + (1 if gg is not None else 0),
             "ms_per_call_mean": round(ms, 5), "ms_per_call_median": round(per[len(per) // 2], 5),
             "tokens_per_s": round(B * T / (ms * 1e-3), 1),
             "algorithmic_flops_per_call": int(flops), "algorithmic_bytes_per_call": int(nbytes),
-            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": F32_MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / F32_MFMA_PEAK_TFLOPS, 4),
-                         "dtype": "f32"},
-            "hbm": {"achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+            "state_record_bytes_per_call": int(2 * 2 * n_chunks * H * K * V * 4),
+            "roofline": roof,
+            "mfma": {"achieved_tflops": round(tf, 2),
+                     "peak_tflops": BF16_MFMA_PEAK_TFLOPS if bf16_path else F32_MFMA_PEAK_TFLOPS,
+                     "dtype": "bf16" if bf16_path else "f32"}}
 
 
 def bench_normalizer(workload: str, steps: int, warmup: int, warm_seconds: float):

@@ -26,8 +26,11 @@
 //               dg is the reverse cumulative sum of r over the chunk; with
 //               g_gamma its gradient is the sum of dg over every token.
 //
-// Every product runs on the fp32 matrix cores (v_mfma_f32_16x16x4_f32), so
-// inputs are used exactly and states, gradients and accumulation are fp32.
+// The kernels below run every product on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32), so inputs are used exactly and states, gradients
+// and accumulation are fp32; they serve float32 inputs and K in {16, 32}.
+// bf16 inputs with K in {64, 128} take the bf16-matrix-core passes of
+// chunk_bwd_bf16.hip instead.
 // Operand layout, per lane l with g = l / 16 and r = l % 16:
 //   A operand A[m = r][k = g], B operand B[k = g][n = r],
 //   result acc[i] = D[m = 4 g + i][n = r].
@@ -525,7 +528,10 @@ hipError_t launch_k(const ChunkBwdParams& p, hipStream_t stream) {
   const TIn* k = static_cast<const TIn*>(p.k);
   const TIn* v = static_cast<const TIn*>(p.v);
   const TIn* dout = static_cast<const TIn*>(p.dout);
-  if (p.seqs.num_seqs > 0) {
+  if (p.seqs.num_seqs > 0 && bwd_bf16_grad(sizeof(TIn) == 2, K)) {
+    const hipError_t e = launch_chunk_bwd_state_bf16(p, per_row, stream);
+    if (e != hipSuccess) return e;
+  } else if (p.seqs.num_seqs > 0) {
     const int units = (int)unit_grid(p.seqs.num_seqs, p.H, 1, p.V / VT);
     hipLaunchKernelGGL((chunk_bwd_state_kernel<K, TIn>), dim3((unsigned)(2 * units)), dim3(NT), 0, stream,
                        q, k, v, dout, p.g, p.g_gamma, p.h0, p.dht, p.dh0, p.scale, p.H, p.V, p.sl, p.seqs,
@@ -533,7 +539,10 @@ hipError_t launch_k(const ChunkBwdParams& p, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (p.seqs.num_chunks > 0) {
+  if (p.seqs.num_chunks > 0 && bwd_bf16_grad(sizeof(TIn) == 2, K)) {
+    const hipError_t e = launch_chunk_bwd_grad_bf16(p, per_row, stream);
+    if (e != hipSuccess) return e;
+  } else if (p.seqs.num_chunks > 0) {
     hipLaunchKernelGGL((chunk_bwd_grad_kernel<K, TIn>), dim3((unsigned)p.seqs.num_chunks, (unsigned)p.H),
                        dim3(NTG), 0, stream, q, k, v, dout, p.g, p.g_gamma, p.scale, p.H, p.V, p.seqs,
                        per_row, p.hbuf, p.dhbuf, p.dq, p.dk, p.dv, p.dg,

@@ -136,6 +136,13 @@ struct ChunkBwdParams {
 
 hipError_t launch_chunk_bwd(const ChunkBwdParams& p, hipStream_t stream);
 
+// The backward (state pass and per-chunk gradients) runs on the bf16 matrix
+// cores (hi/lo splits of the fp32 operands) for bf16 inputs with K in {64,
+// 128}; otherwise on the fp32 matrix cores.
+inline bool bwd_bf16_grad(bool qkv_bf16, int32_t K) { return qkv_bf16 && (K == 64 || K == 128); }
+hipError_t launch_chunk_bwd_state_bf16(const ChunkBwdParams& p, int32_t chunks_per_row, hipStream_t stream);
+hipError_t launch_chunk_bwd_grad_bf16(const ChunkBwdParams& p, int32_t chunks_per_row, hipStream_t stream);
+
 // Elementwise-gate GLA forward: gk [T_total, H, K] float32 natural-log gates,
 // one per key.  K in {16, 32, 64, 128}, V % 32 == 0.
 struct GlaFwdParams {

@@ -165,7 +165,9 @@ size_t sgla_chunk_bwd_workspace_size(const sgla_chunk_args *args, const int64_t 
  * the same arguments.  Three launches: a state pass (forward states and
  * reverse state gradients, one workgroup per (sequence, head, 32-column V
  * tile) each), a per-(chunk, head) gradient kernel, and with g_gamma a
- * per-head reduction.  Every product runs on the fp32 matrix cores.
+ * per-head reduction.  bf16 inputs with K in {64, 128} run both passes on
+ * the bf16 matrix cores (the fp32 states, state gradients and intra-chunk
+ * matrices split into bf16 hi + lo); other inputs on the fp32 matrix cores.
  *
  * Arguments (device pointers unless stated):
  *   args            as for sgla_chunk_fwd; o_dtype and output_final_state
