@@ -56,11 +56,12 @@ MALL_BYTES = 256 << 20
 METRIC = "chunked Simple-GLA fwd tokens/s + % bf16 MFMA peak; decode HBM GB/s"
 
 
-# The sources each measured path's kernels are built from: a committed traffic
-# record is used only while these files are unchanged.
+# The device sources each traffic record's kernels are built from (the dense
+# K = 512 forward: preparation + state/output kernels; the decode step): a
+# committed traffic record is used only while these files are unchanged.
 KERNEL_SOURCES = {
-    "chunk_fwd": ("chunk_prep_bf16.hip", "chunk_fwd_bf16_wide.hip", "chunk_fwd_bf16.hip",
-                  "chunk_fwd_f32.hip", "mfma_common.h", "gate_scan.h", "unit_map.h"),
+    "chunk_fwd": ("chunk_prep_bf16.hip", "chunk_fwd_bf16_wide.hip", "mfma_common.h", "gate_scan.h",
+                  "unit_map.h"),
     "recurrent_step_kernel": ("recurrent_step.hip",),
 }
 
