@@ -148,8 +148,9 @@ recurrent_step_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
 // of a unit's state is S[.][v], K contiguous floats.  Each thread owns four
 // adjacent keys (16-byte accesses) of every RG-th row, so each load of a wave
 // covers whole contiguous rows; o[v] = scale * sum_k S[k][v] q[k] becomes a
-// reduction along the row: over the row's lanes by shuffles, and through LDS
-// when a row spans two waves (K = 512).
+// reduction along the row: over the row's lanes by a halving butterfly that
+// reduces a thread's 16 rows together, and through LDS when a row spans two
+// waves (K = 512).
 template <int K, typename TIn, typename TOut>
 __global__ void __launch_bounds__(256)
 recurrent_step_vk_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
@@ -194,8 +195,10 @@ recurrent_step_vk_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
         vr[b] = to_f32(vu[row]);
       }
     }
+    float pq[BATCH];
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) {
+      pq[b] = 0.f;
       if (b0 + b < rpt) {                  // uniform over the workgroup
         const int row = rg + RG * (b0 + b);
         f32x4 x = sv[b];
@@ -204,10 +207,46 @@ recurrent_step_vk_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
         x.z = fmaf(gamma, x.z, vr[b] * kk.z);
         x.w = fmaf(gamma, x.w, vr[b] * kk.w);
         __builtin_nontemporal_store(x, &S[(int64_t)row * TPR + cq]);
-        float pq = fmaf(x.x, qq.x, fmaf(x.y, qq.y, fmaf(x.z, qq.z, x.w * qq.w)));
+        pq[b] = fmaf(x.x, qq.x, fmaf(x.y, qq.y, fmaf(x.z, qq.z, x.w * qq.w)));
+      }
+    }
+    // sum each row's BATCH partials over the row's LW lanes: a butterfly that
+    // halves the values a lane carries at every step (the lane keeps the upper
+    // half when its mask bit is set), so a lane ends with the sums of `cnt`
+    // consecutive rows starting at `bsel`; once one value is left the
+    // remaining steps just add
+    static_assert(BATCH == 16, "four halving stages");
+    int bsel = 0;
+    auto halve = [&](auto cnt_c, int m) {
+      constexpr int HALF = decltype(cnt_c)::value / 2;
+      const bool upper = (lane & m) != 0;
 #pragma unroll
-        for (int d = LW / 2; d >= 1; d >>= 1) pq += __shfl_xor(pq, d, 64);
-        if (lane % LW == 0) part[row * NSUB + cq / LW] = pq;
+      for (int i = 0; i < HALF; ++i) {
+        const float send = upper ? pq[i] : pq[i + HALF];
+        const float keep = upper ? pq[i + HALF] : pq[i];
+        pq[i] = keep + __shfl_xor(send, m, 64);
+      }
+      if (upper) bsel += HALF;
+    };
+    constexpr int M0 = LW / 2;
+    if constexpr (M0 >= 1) halve(std::integral_constant<int, 16>{}, M0);
+    if constexpr (M0 / 2 >= 1) halve(std::integral_constant<int, 8>{}, M0 / 2);
+    if constexpr (M0 / 4 >= 1) halve(std::integral_constant<int, 4>{}, M0 / 4);
+    if constexpr (M0 / 8 >= 1) halve(std::integral_constant<int, 2>{}, M0 / 8);
+    constexpr int cnt = M0 >= 8 ? 1 : (M0 >= 4 ? 2 : (M0 >= 2 ? 4 : 8));   // values left per lane
+    int addmask = 0;
+#pragma unroll
+    for (int m = M0 / 16; m >= 1; m >>= 1) {
+      pq[0] += __shfl_xor(pq[0], m, 64);
+      addmask |= m;
+    }
+    if ((lane & addmask) == 0) {
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        if (i < cnt && b0 + bsel + i < rpt) {
+          const int row = rg + RG * (b0 + bsel + i);
+          part[row * NSUB + cq / LW] = pq[i];
+        }
       }
     }
   }
