@@ -80,6 +80,10 @@ SMALL = [
           initial_state=True),
     small("varlen_k128_gamma", B=1, T=0, H=2, K=128, V=128, fixed_lengths=(70, 130, 5),
           gate="gamma", initial_state=True),
+    # bf16 with K in {64, 128} runs the bf16-matrix-core passes: V walked in
+    # three 32-column slices, and in one
+    small("k64_v96_h0", K=64, V=96, T=100, initial_state=True),
+    small("k128_v32_gamma", K=128, V=32, T=90, gate="gamma"),
     small("f32_k32_v64", dtype="f32", K=32, V=64, T=150, initial_state=True),
     small("f32_k128_varlen", dtype="f32", B=1, T=0, K=128, V=32, fixed_lengths=(15, 85, 200),
           initial_state=True),
