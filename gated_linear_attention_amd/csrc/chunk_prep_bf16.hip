@@ -30,10 +30,13 @@
 // With grouped kv heads the K^T blocks depend on the kv head alone: they are
 // stored once per (chunk, kv head), by the group's first query head.
 //
-// One workgroup of four waves per (chunk, query head).  All HBM reads (the K chunk
-// into registers then LDS, the wave's Q blocks into registers) are issued
-// up front.  Q K^T runs on v_mfma_f32_32x32x16_bf16: wave w covers query
-// rows [32 (w / 2), +32) over key half w % 2; the two halves are added in LDS.
+// One workgroup of four waves per (chunk, query head), walking the keys in
+// slices of 128: while a slice's K rows go to LDS and its Q and K^T blocks are
+// written out, the next slice's K rows and Q blocks are already loading, so
+// the reads and the writes of a workgroup overlap.  Q K^T runs on
+// v_mfma_f32_32x32x16_bf16: wave w covers query rows [32 (w / 2), +32) over
+// half of every slice's keys (blocks 4 sl + 2 (w % 2) + {0, 1}); the two halves
+// are added in LDS.
 #include <hip/hip_runtime.h>
 
 #include "gate_scan.h"
@@ -56,11 +59,13 @@ chunk_prep_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                        int32_t H, int32_t Hkv, SeqLayout seqs, int32_t chunks_per_row,
                        float* __restrict__ gates,
                        bf16* __restrict__ amat, bf16* __restrict__ ktf, bf16* __restrict__ qfr) {
-  constexpr int LDK = K + 8;      // key row stride: conflict-free 16-byte row reads
-  constexpr int KP = K / 8;       // 16-byte pieces per key row
-  constexpr int NKS = C * KP / NTP;
-  constexpr int NKB = K / 64;     // 32-key blocks per wave (half the keys)
-  static_assert(C * LDS_ACC * 4 <= C * LDK * 2, "A accumulator aliases the K chunk");
+  constexpr int KSL = 128;              // keys per slice
+  constexpr int NS = K / KSL;           // slices
+  constexpr int LDK = KSL + 8;          // slice row stride: conflict-free 16-byte row reads
+  constexpr int KP = KSL / 8;           // 16-byte pieces per slice row
+  constexpr int NKS = C * KP / NTP;     // K pieces per thread and slice
+  static_assert(NKS * NTP == C * KP, "slice split");
+  static_assert(C * LDS_ACC * 4 <= C * LDK * 2, "A accumulator aliases the K slice");
   __shared__ __attribute__((aligned(16))) bf16 sK[C * LDK];
   __shared__ float sb[C];
 
@@ -99,28 +104,36 @@ chunk_prep_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int g4 = lane >> 4;
   const int r = lane & 15;
   const int c2 = w >> 1;           // query rows [32 c2, +32)
-  const int kb0 = (w & 1) * NKB;   // key blocks [kb0, kb0 + NKB)
+  const int kh2 = w & 1;           // key half of every slice: blocks 4 sl + 2 kh2 + {0, 1}
   const int64_t task = (int64_t)gc * H + hd;
   const int RS = H * K;            // elements between consecutive tokens of q
   const int RSK = Hkv * K;         //                                     of k
 
-  // ---- all HBM reads up front ----------------------------------------------
+  // ---- slice loads: the K slice (all rows) and this wave's Q blocks ---------
   const auto rk = make_rsrc(k + (t0 * Hkv + hk) * (int64_t)K, (uint32_t)cl * RSK * 2);
   const auto rq = make_rsrc(q + (t0 * H + hd) * (int64_t)K, (uint32_t)cl * RS * 2);
   u32x4 kx[NKS];
+  bf16x8 qa[2][2], qb[2][2];   // Q blocks of two consecutive slices
+  auto load_k = [&](int sl) {
 #pragma unroll
-  for (int i = 0; i < NKS; ++i) {
-    const int p = tid + NTP * i;
-    kx[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)((p / KP) * RSK + (p % KP) * 8) * 2, 0, 0);
-  }
-  bf16x8 qx[NKB][2];
+    for (int i = 0; i < NKS; ++i) {
+      const int p = tid + NTP * i;
+      kx[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)((p / KP) * RSK + KSL * sl + (p % KP) * 8) * 2,
+                                                    0, 0);
+    }
+  };
+  auto load_q = [&](int sl, bf16x8 (&qx)[2][2]) {
 #pragma unroll
-  for (int i = 0; i < NKB; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-      qx[i][s] = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                      rq, (uint32_t)((32 * c2 + l32) * RS + 32 * (kb0 + i) + 16 * s + 8 * hf) * 2, 0, 0));
+      for (int s = 0; s < 2; ++s)
+        qx[i][s] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                        rq, (uint32_t)((32 * c2 + l32) * RS + 32 * (4 * sl + 2 * kh2 + i) + 16 * s + 8 * hf) * 2,
+                        0, 0));
+  };
+  load_k(0);
+  load_q(0, qa);
   float gx = 0.f;
   if (w == 0 && g != nullptr) {
     const auto rg = make_rsrc(g + t0 * H + hd, (uint32_t)cl * H * 4);
@@ -145,54 +158,61 @@ chunk_prep_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     if (lane == 0) gt[2 * C] = exp2_hw(blast);
   }
 
-  // ---- K chunk to LDS; Q blocks out ----------------------------------------
-#pragma unroll
-  for (int i = 0; i < NKS; ++i) {
-    const int p = tid + NTP * i;
-    *reinterpret_cast<u32x4*>(sK + (p / KP) * LDK + (p % KP) * 8) = kx[i];
-  }
-  {
-    bf16* qo = qfr + task * (int64_t)K * C;
-#pragma unroll
-    for (int i = 0; i < NKB; ++i)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        *reinterpret_cast<bf16x8*>(qo + ((((kb0 + i) * 2 + c2) * 2 + s) * 64 + lane) * 8) = qx[i][s];
-  }
-  __syncthreads();
-
-  // ---- K^T blocks (once per kv head) --------------------------------------------
-  if (write_kt) {
-    bf16* kt = ktf + ((int64_t)gc * Hkv + hk) * K * C;
-#pragma unroll
-    for (int f = w; f < (K / 32) * 4; f += 4) {
-      const int kb = f >> 2, ts = f & 3;
-      const int row0 = 16 * ts + 8 * (grp >> 1);
-      const int col0 = 32 * kb + 16 * (grp & 1);
-      const bf16x8 x = cat(tr_read_perm(sK, LDK, row0, col0), tr_read_perm(sK, LDK, row0 + 4, col0));
-      *reinterpret_cast<bf16x8*>(kt + (f * 64 + lane) * 8) = x;
-    }
-  }
-
-  // ---- partial Q K^T over this wave's key half: tiles (c2, j2), j2 <= c2 ---
+  // ---- per slice: K slice to LDS, Q and K^T blocks out, partial Q K^T ------
   f32x16 acc[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int a = 0; a < 16; ++a) acc[t][a] = 0.f;
+  bf16* qo = qfr + task * (int64_t)K * C;
+  bf16* kt = ktf + ((int64_t)gc * Hkv + hk) * K * C;
+  auto slice = [&](const int sl, const bf16x8 (&qx)[2][2], bf16x8 (&qn)[2][2]) {
 #pragma unroll
-  for (int i = 0; i < NKB; ++i)
+    for (int i = 0; i < NKS; ++i) {
+      const int p = tid + NTP * i;
+      *reinterpret_cast<u32x4*>(sK + (p / KP) * LDK + (p % KP) * 8) = kx[i];
+    }
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int col = 32 * (kb0 + i) + 16 * s + 8 * hf;
-      const bf16x8 k0f = *reinterpret_cast<const bf16x8*>(sK + l32 * LDK + col);
-      acc[0] = mfma32(qx[i][s], k0f, acc[0]);
-      if (c2 == 1) {
-        const bf16x8 k1f = *reinterpret_cast<const bf16x8*>(sK + (32 + l32) * LDK + col);
-        acc[1] = mfma32(qx[i][s], k1f, acc[1]);
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        *reinterpret_cast<bf16x8*>(qo + ((((4 * sl + 2 * kh2 + i) * 2 + c2) * 2 + s) * 64 + lane) * 8) = qx[i][s];
+    __syncthreads();   // slice sl staged
+    if (sl + 1 < NS) {
+      load_k(sl + 1);
+      load_q(sl + 1, qn);
+    }
+    // K^T blocks (kb, ts) of this slice's four key blocks, once per kv head
+    if (write_kt) {
+#pragma unroll
+      for (int f = w; f < 16; f += 4) {
+        const int kbl = f >> 2, ts = f & 3;
+        const int row0 = 16 * ts + 8 * (grp >> 1);
+        const int col0 = 32 * kbl + 16 * (grp & 1);
+        const bf16x8 x = cat(tr_read_perm(sK, LDK, row0, col0), tr_read_perm(sK, LDK, row0 + 4, col0));
+        *reinterpret_cast<bf16x8*>(kt + (((4 * sl + kbl) * 4 + ts) * 64 + lane) * 8) = x;
       }
     }
-  __syncthreads();   // every read of the K chunk is done: reuse it as the accumulator
+    // partial Q K^T over this wave's two key blocks: tiles (c2, j2), j2 <= c2
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int col = 32 * (2 * kh2 + i) + 16 * s + 8 * hf;
+        const bf16x8 k0f = *reinterpret_cast<const bf16x8*>(sK + l32 * LDK + col);
+        acc[0] = mfma32(qx[i][s], k0f, acc[0]);
+        if (c2 == 1) {
+          const bf16x8 k1f = *reinterpret_cast<const bf16x8*>(sK + (32 + l32) * LDK + col);
+          acc[1] = mfma32(qx[i][s], k1f, acc[1]);
+        }
+      }
+    __syncthreads();   // every read of the slice is done
+  };
+#pragma unroll
+  for (int sl = 0; sl < NS; sl += 2) {
+    slice(sl, qa, qb);
+    if (sl + 1 < NS) slice(sl + 1, qb, qa);
+  }
 
   // ---- add the two key halves in LDS (fixed order: deterministic) ---------
   // acc[t][4 jj + i] = D[c = 32 c2 + 8 jj + 4 hf + i][j = 32 t + l32]
