@@ -4,9 +4,11 @@
 // chunk_local_cumsum with the RCP_LN2 scale; the sum is per head and per chunk
 // because the gate is one scalar per head).
 //
-// One 64-lane wavefront per (chunk, head): lane c holds token c of the chunk,
-// and a wave-level inclusive scan (log2(64) = 6 shuffle rounds) forms the
-// prefix sums.  The scan accumulates in float64 and rounds once to float32.
+// One 64-lane wavefront per (64-token block, head): lane c holds token c of
+// the block, and a wave-level inclusive scan (log2(64) = 6 shuffle rounds)
+// forms the prefix sums, restarting every chunk_size lanes (chunk_size a power
+// of two <= 64; blocks start at sequence starts, so chunks do too).  The scan
+// accumulates in float64 and rounds once to float32.
 // The chunk kernels run the same scan in their chunk prologue; this kernel
 // serves the standalone sgla_chunk_local_cumsum entry point.
 #include <hip/hip_runtime.h>
@@ -19,7 +21,7 @@ namespace {
 
 __global__ void __launch_bounds__(256)
 gate_cumsum_kernel(const float* __restrict__ g, float* __restrict__ gc, int32_t H,
-                   SeqLayout seqs) {
+                   SeqLayout seqs, int32_t chunk_size) {
   const int lane = threadIdx.x & 63;
   const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
   if (head >= H) return;
@@ -37,17 +39,18 @@ gate_cumsum_kernel(const float* __restrict__ g, float* __restrict__ gc, int32_t 
     len = min(kChunk, seqs.T - m * kChunk);
   }
   const bool active = lane < len;
-  const float b = wave_cumsum_log2(active ? g[(t0 + lane) * H + head] : 0.f);
+  const float b = wave_segmented_cumsum_log2(active ? g[(t0 + lane) * H + head] : 0.f, chunk_size);
   if (active) gc[(t0 + lane) * H + head] = b;
 }
 
 }  // namespace
 
 hipError_t launch_gate_cumsum(const float* g, float* gc, int32_t H, const SeqLayout& seqs,
-                              hipStream_t stream) {
+                              int32_t chunk_size, hipStream_t stream) {
   if (seqs.num_chunks <= 0) return hipSuccess;
+  if (chunk_size < 1 || chunk_size > kChunk || (chunk_size & (chunk_size - 1)) != 0) return hipErrorInvalidValue;
   dim3 grid(seqs.num_chunks, (H + 3) / 4);
-  hipLaunchKernelGGL(gate_cumsum_kernel, grid, dim3(256), 0, stream, g, gc, H, seqs);
+  hipLaunchKernelGGL(gate_cumsum_kernel, grid, dim3(256), 0, stream, g, gc, H, seqs, chunk_size);
   return hipGetLastError();
 }
 

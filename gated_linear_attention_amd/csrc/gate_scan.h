@@ -24,4 +24,19 @@ __device__ __forceinline__ float wave_cumsum_log2(float x) {
   return (float)(s * kRcpLn2d);
 }
 
+// The same scan restarting every `seg` lanes (seg a power of two <= 64): lane
+// i receives the sum over lanes [i - i % seg, i], times 1/ln 2.  Must be
+// called by all 64 lanes of the wave.
+__device__ __forceinline__ float wave_segmented_cumsum_log2(float x, int seg) {
+  const int lane = threadIdx.x & 63;
+  const int pos = lane & (seg - 1);
+  double s = (double)x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double y = __shfl_up(s, d, 64);
+    if (d < seg && pos >= d) s += y;
+  }
+  return (float)(s * kRcpLn2d);
+}
+
 }  // namespace sgla

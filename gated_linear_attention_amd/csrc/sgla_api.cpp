@@ -52,6 +52,7 @@ struct Plan {
   bool packed = false;
   std::vector<sgla::SeqEntry> seqs;      // packed only, longest first
   std::vector<sgla::ChunkEntry> chunks;  // packed only
+  int32_t chunk_size = 0;                // requested chunk size (power of two <= 64)
   bool prep = false;                     // wide-key bf16 path: per-chunk preparation buffers
   size_t seq_off = 0, chunk_off = 0, gate_off = 0, amat_off = 0, kt_off = 0, q_off = 0, total_bytes = 0;
 };
@@ -66,8 +67,9 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
     return fail(SGLA_ERR_SHAPE, "num_kv_heads must divide H (got num_kv_heads=%d, H=%d)", a->num_kv_heads, a->H);
   const int32_t cs = a->chunk_size == 0 ? sgla::kChunk : a->chunk_size;
   if (!is_pow2(cs)) return fail(SGLA_ERR_SHAPE, "chunk_size must be a power of two (got %d)", cs);
-  if (cs != sgla::kChunk)
-    return fail(SGLA_ERR_UNSUPPORTED, "chunk_size %d is not implemented (only 64)", cs);
+  if (cs > sgla::kChunk)
+    return fail(SGLA_ERR_UNSUPPORTED, "chunk_size %d is not implemented (at most 64)", cs);
+  P->chunk_size = cs;
   if (need_kv_support) {
     if (a->K <= 0 || a->V <= 0) return fail(SGLA_ERR_SHAPE, "K and V must be > 0");
     if (a->qkv_dtype == SGLA_BF16) {
@@ -146,6 +148,15 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
   return SGLA_OK;
 }
 
+// The fused chunk kernels work on 64-token chunks; smaller chunk sizes are
+// accepted by the standalone gate cumsum only.
+sgla_status need_chunk64(const Plan& P) {
+  if (P.chunk_size != sgla::kChunk)
+    return fail(SGLA_ERR_UNSUPPORTED, "chunk_size %d is not implemented for this entry point (only 64)",
+                P.chunk_size);
+  return SGLA_OK;
+}
+
 // Backward request: the forward's shape rules, then the backward's own
 // support set; workspace = tables, per-chunk states and state gradients,
 // per-chunk gate sums.
@@ -156,6 +167,8 @@ struct BwdPlan {
 
 sgla_status plan_bwd(const sgla_chunk_args* a, const int64_t* cu, BwdPlan* B) {
   sgla_status st = plan_shape(a, cu, false, &B->P);
+  if (st != SGLA_OK) return st;
+  st = need_chunk64(B->P);
   if (st != SGLA_OK) return st;
   if (a->qkv_dtype != SGLA_BF16 && a->qkv_dtype != SGLA_F32)
     return fail(SGLA_ERR_DTYPE, "qkv_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", a->qkv_dtype);
@@ -233,6 +246,8 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Plan P;
   sgla_status st = plan_shape(args, cu_seqlens_host, true, &P);
+  if (st != SGLA_OK) return st;
+  st = need_chunk64(P);
   if (st != SGLA_OK) return st;
   const sgla_chunk_args& a = *args;
   if (g != nullptr && g_gamma != nullptr)
@@ -426,6 +441,8 @@ sgla_status sgla_gla_chunk_fwd(const sgla_chunk_args* args, const void* q, const
   Plan P;
   sgla_status st = plan_shape(args, cu_seqlens_host, false, &P);
   if (st != SGLA_OK) return st;
+  st = need_chunk64(P);
+  if (st != SGLA_OK) return st;
   const sgla_chunk_args& a = *args;
   if (a.qkv_dtype != SGLA_BF16 && a.qkv_dtype != SGLA_F32)
     return fail(SGLA_ERR_DTYPE, "qkv_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", a.qkv_dtype);
@@ -515,6 +532,8 @@ sgla_status sgla_chunk_normalizer(const sgla_chunk_args* args, const void* q, co
                                   hipStream_t stream) {
   Plan P;
   sgla_status st = plan_shape(args, cu_seqlens_host, false, &P);
+  if (st != SGLA_OK) return st;
+  st = need_chunk64(P);
   if (st != SGLA_OK) return st;
   const sgla_chunk_args& a = *args;
   if (a.qkv_dtype != SGLA_BF16 && a.qkv_dtype != SGLA_F32)
@@ -606,7 +625,7 @@ sgla_status sgla_chunk_local_cumsum(const sgla_chunk_args* args, const float* g,
   st = upload_tables(P, ws, stream);
   if (st != SGLA_OK) return st;
   const sgla::SeqLayout L = layout_of(args, P, ws);
-  hipError_t e = sgla::launch_gate_cumsum(g, gc, args->H, L, stream);
+  hipError_t e = sgla::launch_gate_cumsum(g, gc, args->H, L, P.chunk_size, stream);
   if (e != hipSuccess) return hip_fail(e, "launching the gate cumsum kernel");
   return ok();
 }

@@ -92,8 +92,10 @@ struct ChunkFwdParams {
   const void* qfr;
 };
 
+// chunk_size: a power of two <= kChunk (the scan restarts inside each
+// kChunk-token block of the layout)
 hipError_t launch_gate_cumsum(const float* g, float* gc, int32_t H, const SeqLayout& seqs,
-                              hipStream_t stream);
+                              int32_t chunk_size, hipStream_t stream);
 
 // bf16 q/k/v, MFMA path, whole key dimension per chunk step.  K in {64,128},
 // V % 64 == 0.

@@ -66,7 +66,8 @@ typedef enum { SGLA_BF16 = 1, SGLA_F32 = 2 } sgla_dtype;
 typedef struct {
   int32_t B, T, H, K, V;      /* packed input: B == 1 and T = total tokens */
   int32_t num_seqs;           /* packed: number of sequences N; dense: ignored (N = B) */
-  int32_t chunk_size;         /* tokens per chunk; 0 selects 64; must be 64 (see below) */
+  int32_t chunk_size;         /* tokens per chunk; 0 selects 64; 64 for the fused entry points,
+                                 any power of two up to 64 for sgla_chunk_local_cumsum */
   int32_t qkv_dtype;          /* sgla_dtype of q, k and v */
   int32_t o_dtype;            /* sgla_dtype of o */
   float scale;                /* finite; callers wanting the default pass 1/sqrt(K) */
@@ -275,7 +276,8 @@ sgla_status sgla_recurrent_step_normalizer(int32_t N, int32_t H, int32_t num_kv_
  * (device) must hold sgla_chunk_fwd_workspace_size(args, cu_seqlens_host)
  * bytes when cu_seqlens_host is not NULL (it carries the sequence table) and
  * may be NULL otherwise.  Only B, T, H, num_seqs and chunk_size of `args` are
- * read.  Exposed for testing the step in isolation.
+ * read; chunk_size may be any power of two up to 64 (section 五 tests
+ * chunk sizes 16, 32 and 64).  Exposed for testing the step in isolation.
  */
 sgla_status sgla_chunk_local_cumsum(const sgla_chunk_args *args, const float *g,
                                     const int64_t *cu_seqlens_host, float *gc,

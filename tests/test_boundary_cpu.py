@@ -124,6 +124,7 @@ CASES = [
     ("cu not ending at T", dict(N=2), dict(cu=[0, 64, 127]), SHAPE, "equal T"),
     ("chunk not power of 2", dict(chunk=48), {}, SHAPE, "power of two"),
     ("chunk 32 unsupported", dict(chunk=32), {}, UNSUPPORTED, "chunk_size"),
+    ("chunk 128 unsupported", dict(chunk=128), {}, UNSUPPORTED, "at most 64"),
     ("bf16 K=96", dict(K=96), {}, UNSUPPORTED, "K in"),
     ("bf16 V=96", dict(V=96), {}, UNSUPPORTED, "V a multiple"),
     ("bf16 K=512 V=48", dict(K=512, V=48), {}, UNSUPPORTED, "V a multiple"),
@@ -393,3 +394,19 @@ def test_step_normalizer_rejects_without_writing(G):
                                                   kw["z"], kw["den"], None)
         assert st == status, (over, st, G.lib.sgla_last_error())
         assert b.unchanged()
+
+
+def test_gate_cumsum_chunk_sizes(G):
+    """The standalone gate cumsum takes any power-of-two chunk size up to 64;
+    larger sizes are unsupported, others a shape error; the fused entry points
+    take 64 only (the case list above)."""
+    b = Buffers()
+    for chunk, status, frag in ((128, UNSUPPORTED, "at most 64"), (48, SHAPE, "power of two")):
+        a = mkargs(G, chunk=chunk)
+        st = G.lib.sgla_chunk_local_cumsum(ctypes.byref(a), b.p("g"), None, b.p("dg"), None, 0, None)
+        assert st == status and frag in G.lib.sgla_last_error().decode()
+    assert b.unchanged()
+    cu = np.array([0, 15, 100, 300], dtype=np.int64)
+    for chunk in (1, 16, 32, 64):
+        a = mkargs(G, B=1, T=300, H=3, N=3, chunk=chunk)
+        assert G.lib.sgla_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.c_void_p(cu.ctypes.data)) > 0

@@ -66,16 +66,17 @@ def small(name, **kw):
 # step (1): chunk-local cumulative gate
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("chunk", [16, 32, 64])
 @pytest.mark.parametrize("cu", [None, [0, 15, 100, 300, 1200, 2000], [0, 0, 1, 65, 65, 200]])
-def test_gate_cumsum(cu):
+def test_gate_cumsum(cu, chunk):
     rng = np.random.default_rng(3)
     if cu is None:
         g = (-np.abs(rng.standard_normal((3, 333, 5)))).astype(np.float32)
     else:
         g = (-np.abs(rng.standard_normal((1, cu[-1], 5)))).astype(np.float32)
-    gc = sgla.chunk_local_cumsum(to_dev(g, torch.float32), chunk_size=64, cu_seqlens=cu)
+    gc = sgla.chunk_local_cumsum(to_dev(g, torch.float32), chunk_size=chunk, cu_seqlens=cu)
     torch.cuda.synchronize()
-    ref = oracle.chunk_local_cumsum(g, chunk_size=64, cu_seqlens=cu)
+    ref = oracle.chunk_local_cumsum(g, chunk_size=chunk, cu_seqlens=cu)
     got = gc.cpu().numpy().astype(np.float64)
     # one float32 rounding of a float64 sum
     assert np.all(np.abs(got - ref) <= 1e-6 * np.maximum(1.0, np.abs(ref)))
