@@ -90,8 +90,9 @@ def test_gla_scalar_gate_matches_simple_gla():
     assert err_ratio(h1, h2.cpu().numpy()) <= TOL_BF16
 
 
-def test_gla_state_v_first_and_bf16_output():
-    inp = make_chunk_inputs(small("vf", K=64, V=96, T=140, initial_state=True))
+@pytest.mark.parametrize("V", [96, 128], ids=["fp32_chain", "bf16_chain"])
+def test_gla_state_v_first_and_bf16_output(V):
+    inp = make_chunk_inputs(small("vf", K=64, V=V, T=140, initial_state=True))
     gk = make_key_gates(inp, seed=5)
     o1, h1 = run(inp, gk)
     o2, h2 = run(inp, gk, state_v_first=True)
