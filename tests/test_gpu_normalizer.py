@@ -35,6 +35,10 @@ CASES = [
     small("k32_varlen", B=1, T=0, K=32, fixed_lengths=(15, 0, 1, 64, 200), initial_state=True),
     small("gqa_k64", H=6, Hkv=2, K=64, T=140, initial_state=True),
     small("empty", T=0, initial_state=True),
+    # more than 32 chunks in a sequence: the chunk scan takes several batches
+    small("long_k64", B=1, T=2600, K=64, initial_state=True),
+    small("long_varlen_k128_gamma", B=1, T=0, K=128, gate="gamma", fixed_lengths=(2100, 5, 0, 700),
+          initial_state=True),
 ]
 
 
