@@ -51,6 +51,9 @@ def _bind(lib):
     lib.sgla_oracle_gla_fwd.restype = ctypes.c_int
     lib.sgla_oracle_gla_fwd.argtypes = ([ctypes.c_int] * 6 + [dp] * 4 + [ctypes.c_double, dp, lp, ctypes.c_int]
                                         + [dp] * 2 + [ctypes.c_int])
+    lib.sgla_oracle_parallel.restype = ctypes.c_int
+    lib.sgla_oracle_parallel.argtypes = [ctypes.c_int] * 6 + [dp] * 5 + [ctypes.c_double, dp, dp,
+                                                                         ctypes.c_int]
     lib.sgla_oracle_step.restype = ctypes.c_int
     lib.sgla_oracle_step.argtypes = [ctypes.c_int] * 5 + [dp] * 5 + [ctypes.c_double, dp, dp,
                                                                      ctypes.c_int]
@@ -226,6 +229,32 @@ def normalizer(q, k, g=None, g_gamma=None, scale=None, initial_z=None, cu_seqlen
     o, ht = fwd(q, k, ones, g=g, g_gamma=g_gamma, scale=scale, initial_state=h0,
                 cu_seqlens=cu_seqlens, nthreads=nthreads, lib=lib)
     return o[..., 0], ht[..., 0]
+
+
+def parallel(q, k, v, g=None, g_gamma=None, scale=None, output_attn=True, nthreads=None, lib=None):
+    """Parallel form (page "flash-linear-attention 中的 Simple GLA", section 二:
+    the parallel entry builds the decayed attention matrix explicitly).  Per
+    batch row and query head, with G_t the running sum of the log gates,
+    A[i, j] = scale (q_i . k_j) exp(G_i - G_j) for j <= i and 0 above the
+    diagonal; o = A v.  Dense input from a zero state.
+
+    q: [B, T, H, K]; k: [B, T, Hkv, K]; v: [B, T, Hkv, V]; g: [B, T, H] or
+    None; g_gamma: [H] or None.  Returns (o [B, T, H, V], A [B, H, T, T] or
+    None), float64."""
+    q, k, v, g, g_gamma = _f64(q), _f64(k), _f64(v), _f64(g), _f64(g_gamma)
+    B, T, H, K = q.shape
+    Hkv = k.shape[2]
+    V = v.shape[-1]
+    if scale is None:
+        scale = K ** -0.5
+    o = np.zeros((B, T, H, V))
+    attn = np.zeros((B, H, T, T)) if output_attn else None
+    lib = lib or load()
+    rc = lib.sgla_oracle_parallel(B, T, H, Hkv, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(g_gamma),
+                                  float(scale), _ptr(o), _ptr(attn), int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"sgla_oracle_parallel rejected its arguments (code {rc})")
+    return o, attn
 
 
 def step(q, k, v, g, state, scale=None, g_gamma=None, nthreads=None, lib=None,

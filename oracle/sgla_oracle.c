@@ -665,3 +665,113 @@ int sgla_oracle_gla_fwd(int B, int T, int H, int Hkv, int K, int V,
     free(units);
     return rc;
 }
+
+/*
+ * Parallel form (page "flash-linear-attention 中的 Simple GLA", section 二:
+ * the parallel entry builds the decayed attention matrix A explicitly;
+ * section 五: its test compares that A with a directly built decay matrix).
+ * Per batch row b and query head h, with G_t = g_0 + ... + g_t (g_t = g_gamma[h]
+ * for the data-independent decay, 0 when neither gate is given):
+ *
+ *     A[i][j] = scale * (q_i . k_j) * exp(G_i - G_j)   for j <= i,  else 0
+ *     o_i     = sum_j A[i][j] v_j
+ *
+ * which is the recurrence above unrolled from a zero state: exp(G_i - G_j)
+ * is the product of the gates of tokens j+1 .. i.
+ *   q [B, T, H, K], k [B, T, Hkv, K], v [B, T, Hkv, V], g [B, T, H] or NULL,
+ *   g_gamma [H] or NULL; o [B, T, H, V]; attn [B, H, T, T] or NULL.
+ * Dense input only (no initial state, no final state).
+ */
+typedef struct {
+    int T, H, Hkv, K, V;
+    const double *q, *k, *v, *g, *g_gamma;
+    double scale;
+    double *o, *attn;
+    int64_t n_units, next;
+    pthread_mutex_t mu;
+} par_job_t;
+
+static void *par_worker(void *arg)
+{
+    par_job_t *J = (par_job_t *)arg;
+    const int T = J->T, H = J->H, Hkv = J->Hkv, K = J->K, V = J->V;
+    double *G = (double *)malloc((size_t)(T > 0 ? T : 1) * sizeof(double));
+    if (!G) return (void *)1;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int64_t u = J->next++;
+        pthread_mutex_unlock(&J->mu);
+        if (u >= J->n_units) break;
+        const int64_t b = u / H;
+        const int h = (int)(u % H);
+        const int hk = h / (H / Hkv);
+        double run = 0.0;
+        for (int t = 0; t < T; ++t) {
+            const double gt = J->g ? J->g[((size_t)b * T + t) * H + h]
+                                   : (J->g_gamma ? J->g_gamma[h] : 0.0);
+            run += gt;
+            G[t] = run;
+        }
+        double *A = J->attn ? J->attn + (size_t)u * T * T : NULL;
+        for (int i = 0; i < T; ++i) {
+            const double *qi = J->q + (((size_t)b * T + i) * H + h) * K;
+            double *oi = J->o + (((size_t)b * T + i) * H + h) * V;
+            for (int c = 0; c < V; ++c) oi[c] = 0.0;
+            for (int j = 0; j < T; ++j) {
+#if SGLA_ORACLE_MUTANT == 15
+                /* planted: strictly causal mask, the token's own term dropped */
+                const int keep = j < i;
+#else
+                const int keep = j <= i;
+#endif
+                double a = 0.0;
+                if (keep) {
+                    const double *kj = J->k + (((size_t)b * T + j) * Hkv + hk) * K;
+                    double dot = 0.0;
+                    for (int e = 0; e < K; ++e) dot += qi[e] * kj[e];
+#if SGLA_ORACLE_MUTANT == 16
+                    /* planted: the key token's own gate counted in the decay */
+                    const double gj = G[j] - (j > 0 ? G[j - 1] : 0.0);
+                    a = J->scale * dot * exp(G[i] - G[j] + gj);
+#else
+                    a = J->scale * dot * exp(G[i] - G[j]);
+#endif
+                    const double *vj = J->v + (((size_t)b * T + j) * Hkv + hk) * V;
+                    for (int c = 0; c < V; ++c) oi[c] += a * vj[c];
+                }
+                if (A) A[(size_t)i * T + j] = a;
+            }
+        }
+    }
+    free(G);
+    return NULL;
+}
+
+int sgla_oracle_parallel(int B, int T, int H, int Hkv, int K, int V,
+                         const double *q, const double *k, const double *v,
+                         const double *g, const double *g_gamma, double scale,
+                         double *o, double *attn, int nthreads)
+{
+    if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return -1;
+    if (Hkv <= 0 || H % Hkv != 0) return -6;
+    if (g && g_gamma) return -2;
+    par_job_t J;
+    J.T = T; J.H = H; J.Hkv = Hkv; J.K = K; J.V = V;
+    J.q = q; J.k = k; J.v = v; J.g = g; J.g_gamma = g_gamma; J.scale = scale;
+    J.o = o; J.attn = attn; J.n_units = (int64_t)B * H; J.next = 0;
+    pthread_mutex_init(&J.mu, NULL);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    int started = 0, rc = 0;
+    for (int i = 1; i < nthreads; ++i)
+        if (pthread_create(&th[started], NULL, par_worker, &J) == 0) ++started;
+    if (par_worker(&J) != NULL) rc = -4;
+    for (int i = 0; i < started; ++i) {
+        void *r = NULL;
+        pthread_join(th[i], &r);
+        if (r != NULL) rc = -4;
+    }
+    pthread_mutex_destroy(&J.mu);
+    return rc;
+}

@@ -550,13 +550,51 @@ def pin_gla_brute_force(lib, seed=18, T=60, H=2, K=4, V=3):
     return True
 
 
+def pin_parallel_equals_recurrence(lib, seed=19, B=2, T=45, H=4, Hkv=2, K=5, V=3):
+    """The parallel form (explicit decayed attention matrix) equals the
+    token-by-token recurrence from a zero state, with per-token gates and with
+    a per-head g_gamma, on grouped kv heads; its o is A v."""
+    rng = np.random.default_rng(seed)
+    q, k, v = _rand(rng, B, T, H, K), _rand(rng, B, T, Hkv, K), _rand(rng, B, T, Hkv, V)
+    g = logsigmoid(_rand(rng, B, T, H)) * 0.7
+    gg = np.log1p(-np.exp2(-np.arange(1, H + 1, dtype=np.float64)))
+    for kw in ({"g": g}, {"g_gamma": gg}, {}):
+        o_r, _ = oracle.fwd(q, k, v, scale=0.45, output_final_state=False, lib=lib, **kw)
+        o_p, A = oracle.parallel(q, k, v, scale=0.45, lib=lib, **kw)
+        if _rel(o_p, o_r) > TIGHT:
+            return False
+        vq = np.repeat(v, H // Hkv, axis=2)                     # kv head of each query head
+        if _rel(np.einsum("bhij,bjhv->bihv", A, vq), o_p) > TIGHT:
+            return False
+    return True
+
+
+def pin_parallel_special_gates(lib, seed=20, T=37, H=2, K=4, V=3):
+    """Closed forms of the attention matrix: g = 0 gives scale * tril(Q K^T)
+    (causal linear attention); g -> -inf leaves only the diagonal
+    scale * q_i . k_i.  Entries above the diagonal are exactly zero."""
+    rng = np.random.default_rng(seed)
+    q, k, v = _rand(rng, 1, T, H, K), _rand(rng, 1, T, H, K), _rand(rng, 1, T, H, V)
+    _, A0 = oracle.parallel(q, k, v, g=np.zeros((1, T, H)), scale=0.8, lib=lib)
+    _, Af = oracle.parallel(q, k, v, g=np.full((1, T, H), -1e4), scale=0.8, lib=lib)
+    for h in range(H):
+        qk = q[0, :, h] @ k[0, :, h].T
+        if _rel(A0[0, h], 0.8 * np.tril(qk)) > TIGHT:
+            return False
+        if _rel(Af[0, h], 0.8 * np.diag(np.diag(qk))) > TIGHT:
+            return False
+        if np.any(np.triu(A0[0, h], 1) != 0):
+            return False
+    return True
+
+
 ALL_PINS = [pin_chunk_local_cumsum, pin_hand_example, pin_brute_force, pin_zero_gate, pin_full_forget,
             pin_split_sequence, pin_varlen_equals_per_sequence, pin_chunk_form,
             pin_gamma_is_broadcast_g, pin_retnet_closed_form, pin_invariants,
             pin_prefill_then_decode, pin_step_brute_force, pin_gqa_is_repeated_mha,
             pin_step_variants, pin_bwd_finite_differences, pin_bwd_gate_identity,
             pin_state_v_first, pin_normalizer, pin_gla_scalar_gate_is_simple_gla,
-            pin_gla_brute_force]
+            pin_gla_brute_force, pin_parallel_equals_recurrence, pin_parallel_special_gates]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -606,6 +644,8 @@ MUTANTS = {
     12: "backward: k and v gradients miss the token's own output term",
     13: "elementwise GLA: interleaved kv grouping",
     14: "elementwise GLA: gate indexed by the value column instead of the key",
+    15: "parallel form: strictly causal mask (the token's own term dropped)",
+    16: "parallel form: the key token's own gate counted in the decay",
 }
 
 
