@@ -27,10 +27,11 @@ import os
 import torch
 
 __all__ = ["chunk_fwd", "chunk_bwd", "gla_chunk_fwd", "chunk_normalizer", "recurrent_step_normalizer",
+           "parallel_fwd",
            "recurrent_step", "chunk_local_cumsum", "library_path", "lib",
            "SglaError", "ABI_VERSION"]
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsgla.so")
 
@@ -90,6 +91,8 @@ def _load():
     lib.sgla_recurrent_step.restype = ctypes.c_int
     lib.sgla_recurrent_step.argtypes = [i32, i32, i32, i32, i32, f32, i32, i32, i32, vp, vp, vp,
                                         vp, vp, vp, vp, vp]
+    lib.sgla_parallel_fwd.restype = ctypes.c_int
+    lib.sgla_parallel_fwd.argtypes = [pargs] + [vp] * 8
     if lib.sgla_abi_version() != ABI_VERSION:
         raise ImportError(f"libsgla ABI {lib.sgla_abi_version()} != binding ABI {ABI_VERSION}")
     return lib
@@ -370,6 +373,43 @@ def chunk_normalizer(q, k, g=None, g_gamma=None, scale=None, initial_z=None,
     if st != _OK:
         _raise(st, "sgla_chunk_normalizer")
     return den, zt
+
+
+def parallel_fwd(q, k, v, g=None, g_gamma=None, scale=None, output_attn=True, out_dtype=None):
+    """Parallel form (page "flash-linear-attention 中的 Simple GLA", section 二:
+    the parallel entry writes out the decayed attention matrix).  Per batch
+    row and query head, A[i, j] = scale (q_i . k_j) exp(G_i - G_j) for j <= i
+    (G the running sum of the log gates) and 0 above the diagonal; o = A v.
+    Dense bf16 q [B, T, H, K], k [B, T, Hkv, K], v [B, T, Hkv, V]; g [B, T, H]
+    or g_gamma [H] (at most one).  Returns (o [B, T, H, V] in out_dtype
+    (default: q's dtype), A [B, H, T, T] float32 or None)."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor [B, T, H, K]")
+    dev = q.device
+    B, T, H, K = q.shape
+    Hkv = _kv_heads(k, H, 2)
+    if not isinstance(v, torch.Tensor) or v.dim() != 4:
+        raise ValueError("v must be a 4-D tensor [B, T, Hkv, V]")
+    V = v.shape[-1]
+    qkv = _dtype_code(q.dtype, "q")
+    _check_dev("q", q, dev)
+    _check_dev("k", k, dev, q.dtype, (B, T, Hkv, K))
+    _check_dev("v", v, dev, q.dtype, (B, T, Hkv, V))
+    if g is not None and g_gamma is not None:
+        raise ValueError("g and g_gamma are mutually exclusive; pass at most one")
+    _check_dev("g", g, dev, torch.float32, (B, T, H))
+    _check_dev("g_gamma", g_gamma, dev, torch.float32, (H,))
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if scale is None:
+        scale = K ** -0.5
+    args = _chunk_args(B, T, H, K, V, B, 64, qkv, _dtype_code(out_dtype, "out_dtype"), scale, False, Hkv)
+    o = torch.empty((B, T, H, V), device=dev, dtype=out_dtype)
+    attn = torch.empty((B, H, T, T), device=dev, dtype=torch.float32) if output_attn else None
+    st = lib.sgla_parallel_fwd(ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(g_gamma),
+                               _ptr(o), _ptr(attn), _stream(dev))
+    if st != _OK:
+        _raise(st, "sgla_parallel_fwd")
+    return o, attn
 
 
 def recurrent_step_normalizer(q, k, g, z, scale=None, g_gamma=None):

@@ -689,4 +689,62 @@ sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t num_kv_heads, int3
   return ok();
 }
 
+sgla_status sgla_parallel_fwd(const sgla_chunk_args* args, const void* q, const void* k, const void* v,
+                              const float* g, const float* g_gamma, void* o, float* attn, hipStream_t stream) {
+  if (args == nullptr) return fail(SGLA_ERR_INVALID_ARG, "args is NULL");
+  const sgla_chunk_args& a = *args;
+  if (a.B < 0 || a.T < 0) return fail(SGLA_ERR_SHAPE, "B and T must be >= 0 (got B=%d T=%d)", a.B, a.T);
+  if (a.H <= 0) return fail(SGLA_ERR_SHAPE, "H must be > 0 (got %d)", a.H);
+  const int32_t Hkv = a.num_kv_heads == 0 ? a.H : a.num_kv_heads;
+  if (Hkv < 0 || a.H % Hkv != 0)
+    return fail(SGLA_ERR_SHAPE, "num_kv_heads must divide H (got num_kv_heads=%d, H=%d)", a.num_kv_heads, a.H);
+  if (a.K <= 0 || a.V <= 0) return fail(SGLA_ERR_SHAPE, "K and V must be > 0");
+  if (a.qkv_dtype == SGLA_F32)
+    return fail(SGLA_ERR_UNSUPPORTED, "the parallel form is implemented for bf16 q, k and v only");
+  if (a.qkv_dtype != SGLA_BF16)
+    return fail(SGLA_ERR_DTYPE, "qkv_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", a.qkv_dtype);
+  if (a.o_dtype != SGLA_BF16 && a.o_dtype != SGLA_F32)
+    return fail(SGLA_ERR_DTYPE, "o_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", a.o_dtype);
+  if (!sgla::parallel_supported(a.K, a.V))
+    return fail(SGLA_ERR_UNSUPPORTED,
+                "the parallel form supports K in {64,128,256} and V a multiple of 16 in [16, 256] (got K=%d V=%d)",
+                a.K, a.V);
+  if (!std::isfinite(a.scale)) return fail(SGLA_ERR_INVALID_ARG, "scale must be finite");
+  if (g != nullptr && g_gamma != nullptr)
+    return fail(SGLA_ERR_INVALID_ARG, "g and g_gamma are mutually exclusive; pass at most one");
+  if ((int64_t)a.B * a.T > INT32_MAX)
+    return fail(SGLA_ERR_UNSUPPORTED, "B*T = %lld tokens exceeds 2^31-1", (long long)a.B * a.T);
+  // one batch row of k or v (plus a tile of slack) is addressed with 32-bit byte offsets
+  if (((int64_t)a.T + sgla::kChunk) * Hkv * std::max(a.K, a.V) * 2 > INT32_MAX)
+    return fail(SGLA_ERR_UNSUPPORTED, "T x num_kv_heads x max(K, V) too large for the parallel form (T=%d)", a.T);
+  if (a.B == 0 || a.T == 0) return ok();
+  const int32_t nT = (a.T + sgla::kChunk - 1) / sgla::kChunk;
+  if (sgla::unit_grid(a.B, Hkv, a.H / Hkv, nT) > INT32_MAX)
+    return fail(SGLA_ERR_UNSUPPORTED, "B x H x %d row tiles exceeds 2^31-1 workgroups", nT);
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+    return fail(SGLA_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
+  if (!(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(o, 16)))
+    return fail(SGLA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (attn != nullptr && !aligned(attn, 16)) return fail(SGLA_ERR_INVALID_ARG, "attn must be 16-byte aligned");
+  sgla::ParallelParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = g;
+  p.g_gamma = g_gamma;
+  p.o = o;
+  p.attn = attn;
+  p.scale = a.scale;
+  p.B = a.B;
+  p.T = a.T;
+  p.H = a.H;
+  p.Hkv = Hkv;
+  p.K = a.K;
+  p.V = a.V;
+  p.o_f32 = a.o_dtype == SGLA_F32;
+  hipError_t e = sgla::launch_parallel_fwd(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "launching the parallel-form kernel");
+  return ok();
+}
+
 }  // extern "C"

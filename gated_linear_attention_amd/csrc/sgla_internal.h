@@ -211,6 +211,27 @@ struct StepNormalizerParams {
 hipError_t launch_chunk_normalizer(const NormalizerParams& p, hipStream_t stream);
 hipError_t launch_step_normalizer(const StepNormalizerParams& p, hipStream_t stream);
 
+// Parallel form: the decayed attention matrix of dense input written out
+// (bf16 q, k, v), and o = A v.
+struct ParallelParams {
+  const void* q;             // [B, T, H, K] bf16
+  const void* k;             // [B, T, Hkv, K] bf16
+  const void* v;             // [B, T, Hkv, V] bf16
+  const float* g;            // [B, T, H] or nullptr
+  const float* g_gamma;      // [H] or nullptr
+  void* o;                   // [B, T, H, V], float32 when o_f32 else bf16
+  float* attn;               // [B, H, T, T] or nullptr
+  float scale;
+  int32_t B, T, H, Hkv, K, V;
+  int32_t o_f32;
+};
+
+inline bool parallel_supported(int32_t K, int32_t V) {
+  return (K == 64 || K == 128 || K == 256) && V >= 16 && V <= 256 && V % 16 == 0;
+}
+
+hipError_t launch_parallel_fwd(const ParallelParams& p, hipStream_t stream);
+
 struct StepParams {
   const void* q;
   const void* k;

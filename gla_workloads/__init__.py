@@ -123,6 +123,11 @@ CHUNK_CONFIGS = {
 CHUNK_CONFIGS["gqa_bf16_k64_h9kv3"] = ChunkWorkload(
     "gqa_bf16_k64_h9kv3", B=32, T=2048, H=9, K=64, V=64, dtype="bf16", gate="g", Hkv=3,
     output_final_state=True, seed=1005)
+# Parallel form (explicit T x T attention matrix per head): dense rows of the
+# packed workload's head shape, 4096 tokens each.
+CHUNK_CONFIGS["parallel_bf16_k128"] = ChunkWorkload(
+    "parallel_bf16_k128", B=2, T=4096, H=16, K=128, V=128, dtype="bf16", gate="g",
+    output_final_state=False, seed=1006)
 DECODE_CONFIGS = {
     "decode_n256_h32_k128": DecodeWorkload("decode_n256_h32_k128", N=256, H=32, K=128, V=128,
                                            steps=64, dtype="bf16", seed=1004),

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SGLA_ABI_VERSION 4
+#define SGLA_ABI_VERSION 5
 
 typedef enum {
   SGLA_OK = 0,
@@ -308,6 +308,37 @@ sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t num_kv_heads, int3
                                 const void *q, const void *k, const void *v,
                                 const float *g, const float *g_gamma, float *state, void *o,
                                 hipStream_t stream);
+
+/*
+ * Parallel form (section 二: the parallel entry writes out the decayed
+ * attention matrix; section 五: its test checks that matrix).  Per batch row
+ * b and query head h, with G_t = g_0 + ... + g_t the running log gate of the
+ * row (g_t = g_gamma[h] for the per-head decay, 0 when neither is given):
+ *     A[i][j] = scale * (q_i . k_j) * exp(G_i - G_j)   for j <= i, else 0
+ *     o_i     = sum_j A[i][j] v_j
+ * i.e. sgla_chunk_fwd's output from a zero initial state, computed as dense
+ * causal attention with a decay mask instead of through chunk states.
+ *
+ * Arguments (device pointers):
+ *   args     B, T, H, K, V, num_kv_heads, qkv_dtype, o_dtype and scale are
+ *            read; num_seqs, chunk_size, output_final_state and
+ *            state_v_first are not (dense input only, no initial or final
+ *            state).
+ *   q        [B, T, H, K] bf16;  k [B, T, Hkv, K] bf16;  v [B, T, Hkv, V] bf16
+ *   g        [B, T, H] float32 log gates, or NULL
+ *   g_gamma  [H] float32 per-head log decay, or NULL (at most one of the two)
+ *   o        [B, T, H, V] in o_dtype
+ *   attn     [B, H, T, T] float32 written in full (zeros above the diagonal),
+ *            or NULL to compute o only.  B * H * T * T * 4 bytes: the caller
+ *            sizes T accordingly.
+ * All buffers 16-byte aligned; no output may alias an input.  No workspace,
+ * one kernel launch.  Supported: bf16 q, k, v (float32 inputs return
+ * SGLA_ERR_UNSUPPORTED), K in {64, 128, 256}, V a multiple of 16 in [16, 256].
+ */
+sgla_status sgla_parallel_fwd(const sgla_chunk_args *args,
+                              const void *q, const void *k, const void *v,
+                              const float *g, const float *g_gamma,
+                              void *o, float *attn, hipStream_t stream);
 
 #ifdef __cplusplus
 }

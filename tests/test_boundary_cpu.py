@@ -38,7 +38,7 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("sgla_chunk_fwd", "sgla_recurrent_step", "sgla_chunk_fwd_workspace_size",
               "sgla_chunk_bwd", "sgla_chunk_bwd_workspace_size",
-              "sgla_chunk_local_cumsum", "sgla_last_error", "sgla_abi_version"):
+              "sgla_chunk_local_cumsum", "sgla_last_error", "sgla_abi_version", "sgla_parallel_fwd"):
         assert n in names
 
 
@@ -59,7 +59,7 @@ def test_single_hip_runtime_in_process(G):
 
 
 def test_abi_version(G):
-    assert G.lib.sgla_abi_version() == G.ABI_VERSION == 4
+    assert G.lib.sgla_abi_version() == G.ABI_VERSION == 5
 
 
 class Buffers:
@@ -410,3 +410,44 @@ def test_gate_cumsum_chunk_sizes(G):
     for chunk in (1, 16, 32, 64):
         a = mkargs(G, B=1, T=300, H=3, N=3, chunk=chunk)
         assert G.lib.sgla_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.c_void_p(cu.ctypes.data)) > 0
+
+
+PAR_CASES = [
+    ("null args", None, {}, INVALID, "args"),
+    ("K=96", dict(K=96), {}, UNSUPPORTED, "K in"),
+    ("K=512", dict(K=512), {}, UNSUPPORTED, "K in"),
+    ("V=24", dict(V=24), {}, UNSUPPORTED, "V a multiple"),
+    ("V=272", dict(V=272), {}, UNSUPPORTED, "V a multiple"),
+    ("float32 inputs", dict(qkv=F32), {}, UNSUPPORTED, "bf16"),
+    ("fp16", dict(qkv=3), {}, DTYPE, "qkv_dtype"),
+    ("o dtype", dict(od=3), {}, DTYPE, "o_dtype"),
+    ("both gates", {}, dict(gg=True), INVALID, "mutually exclusive"),
+    ("kv heads not dividing", dict(H=2, Hkv=3), {}, SHAPE, "num_kv_heads"),
+    ("negative T", dict(T=-1), {}, SHAPE, "B and T"),
+    ("o NULL", {}, dict(o=None), INVALID, "non-NULL"),
+    ("attn misaligned", {}, dict(attn_off=4), INVALID, "aligned"),
+]
+
+
+@pytest.mark.parametrize("desc,aover,cover,status,frag", PAR_CASES, ids=[c[0] for c in PAR_CASES])
+def test_parallel_fwd_rejects_without_writing(G, desc, aover, cover, status, frag):
+    b = Buffers()
+    args = None if aover is None else ctypes.byref(mkargs(G, **aover))
+    o = cover.get("o", b.p("o"))
+    attn = ctypes.c_void_p(b.p("ht").value + cover.get("attn_off", 0))
+    st = G.lib.sgla_parallel_fwd(args, b.p("q"), b.p("k"), b.p("v"), b.p("g"),
+                                 b.p("gg") if cover.get("gg") else None, o, attn, None)
+    msg = G.lib.sgla_last_error().decode()
+    assert st == status, (st, msg)
+    assert frag in msg, msg
+    assert b.unchanged()
+
+
+def test_parallel_fwd_empty_is_ok(G):
+    """No tokens (or no batch rows) is a valid call that launches nothing."""
+    b = Buffers()
+    for over in (dict(T=0), dict(B=0)):
+        st = G.lib.sgla_parallel_fwd(ctypes.byref(mkargs(G, **over)), None, None, None, None, None,
+                                     None, None, None)
+        assert st == OK, G.lib.sgla_last_error()
+    assert b.unchanged()

@@ -1,0 +1,127 @@
+"""GPU parity of the parallel form (sgla_parallel_fwd) against the fp64
+oracle: the decayed attention matrix A[i, j] = scale (q_i . k_j) exp(G_i -
+G_j) for j <= i (0 above the diagonal) and o = A v (page "flash-linear-
+attention 中的 Simple GLA", section 二: the parallel entry writes out A;
+section 五: its test checks A).  The bar per output tensor: max |gpu -
+oracle| / RMS(oracle) <= 2e-2 (bf16 inputs); entries above the diagonal must
+be exactly zero."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gla_workloads import CHUNK_CONFIGS, ChunkWorkload, make_chunk_inputs
+from gpu_common import TOL_BF16, device_inputs, err_ratio
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+if torch.cuda.is_available():
+    import gated_linear_attention_amd as sgla
+else:  # pragma: no cover - collected on CPU-only hosts, never run
+    sgla = None
+
+
+def small(name, **kw):
+    base = dict(B=2, T=150, H=2, K=64, V=64, dtype="bf16", gate="g", seed=71, output_final_state=False)
+    base.update(kw)
+    return ChunkWorkload(name, **base)
+
+
+CASES = [
+    small("k64_v64"),
+    small("k128_v128_gamma", B=1, T=200, H=4, K=128, V=128, gate="gamma"),
+    small("k256_v256", B=1, T=130, K=256, V=256),
+    small("k128_v48_ragged", B=1, T=67, K=128, V=48),          # T % 4 != 0: element stores
+    small("gqa", H=4, Hkv=2, K=64, V=32, T=129),
+    small("no_gate_t64", B=1, T=64, K=128, V=64, gate="none"),
+    small("t1", B=3, T=1, K=64, V=16),
+    small("strong_gate", B=1, T=300, K=64, V=128, gate_normalizer=0.1),
+    small("weak_gate", B=1, T=300, K=128, V=64, gate_normalizer=10.0),
+    small("k64_v256_t190", B=1, T=190, H=3, K=64, V=256),
+    small("k256_v80", B=1, T=100, H=2, K=256, V=80),
+]
+
+
+def run(inp, out_dtype=torch.float32, output_attn=True):
+    d = device_inputs(inp)
+    o, A = sgla.parallel_fwd(d["q"], d["k"], d["v"], g=d["g"], g_gamma=d["g_gamma"], scale=inp["scale"],
+                             output_attn=output_attn, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), None if A is None else A.cpu().numpy()
+
+
+def check(o, A, o_ref, A_ref, label):
+    eo, ea = err_ratio(o, o_ref), err_ratio(A, A_ref)
+    T = A.shape[-1]
+    upper = np.triu(np.ones((T, T), dtype=bool), 1)
+    print(f"[parallel {label}] o {eo:.2e} A {ea:.2e}", flush=True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(A))
+    assert eo <= TOL_BF16 and ea <= TOL_BF16
+    assert not np.any(A[..., upper]), "entries above the diagonal must be zero"
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_parallel_small(w):
+    inp = make_chunk_inputs(w)
+    o, A = run(inp)
+    o_ref, A_ref = oracle.parallel(inp["q"], inp["k"], inp["v"], g=inp["g"], g_gamma=inp["g_gamma"],
+                                   scale=inp["scale"])
+    check(o, A, o_ref, A_ref, w.name)
+
+
+def test_parallel_bf16_output_and_no_matrix():
+    """Without A the kernel computes the same o bit for bit (the matrix is
+    optional); a bf16 o is the float32 one rounded once (within half a bf16
+    ulp per element)."""
+    inp = make_chunk_inputs(small("bf16_out", B=1, T=170, H=2, K=128, V=128))
+    o_ref, _ = oracle.parallel(inp["q"], inp["k"], inp["v"], g=inp["g"], scale=inp["scale"],
+                               output_attn=False)
+    o32, A = run(inp)
+    o_noa, none = run(inp, output_attn=False)
+    o16, _ = run(inp, out_dtype=torch.bfloat16)
+    assert none is None and A is not None
+    e32 = err_ratio(o32, o_ref)
+    print(f"[parallel bf16_out] o {e32:.2e}", flush=True)
+    assert e32 <= TOL_BF16
+    assert np.array_equal(o_noa, o32)
+    assert np.all(np.abs(o16 - o32) <= 2.0 ** -8 * np.abs(o32))
+
+
+def test_parallel_matches_chunked_forward():
+    """From a zero state the parallel form and the chunked forward compute the
+    same o (two different kernels), within the bf16 bar of each other."""
+    inp = make_chunk_inputs(small("vs_chunk", B=2, T=257, H=4, Hkv=2, K=128, V=128))
+    d = device_inputs(inp)
+    o_c, _ = sgla.chunk_fwd(d["q"], d["k"], d["v"], g=d["g"], scale=inp["scale"], output_final_state=False,
+                            o_dtype=torch.float32)
+    o_p, _ = sgla.parallel_fwd(d["q"], d["k"], d["v"], g=d["g"], scale=inp["scale"], output_attn=False,
+                               out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    e = err_ratio(o_p.cpu().numpy(), o_c.cpu().numpy())
+    print(f"[parallel vs chunk] {e:.2e}", flush=True)
+    assert e <= TOL_BF16
+
+
+def test_parallel_empty():
+    inp = make_chunk_inputs(small("empty", B=2, T=0))
+    o, A = run(inp)
+    assert o.shape == (2, 0, 2, 64) and A.shape == (2, 2, 0, 0)
+
+
+def test_parallel_full_size_sampled_heads():
+    """The benchmark workload (B=2, T=4096, H=16, K=V=128, per-token gates) in
+    the benchmark's launch: whole rows of A and o for two sampled (row, head)
+    units against the oracle run on exactly those units."""
+    w = CHUNK_CONFIGS["parallel_bf16_k128"]
+    inp = make_chunk_inputs(w)
+    d = device_inputs(inp)
+    o, A = sgla.parallel_fwd(d["q"], d["k"], d["v"], g=d["g"], scale=inp["scale"], output_attn=True,
+                             out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (1, w.H - 1)):
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        o_ref, A_ref = oracle.parallel(inp["q"][sl], inp["k"][sl], inp["v"][sl], g=inp["g"][sl],
+                                       scale=inp["scale"])
+        check(o[b, :, h].cpu().numpy(), A[b, h].cpu().numpy(), o_ref[0, :, 0], A_ref[0, 0],
+              f"full b={b} h={h}")
