@@ -23,6 +23,8 @@
 // so the work per workgroup is even whatever its position.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "gate_scan.h"
 #include "mfma_common.h"
 #include "sgla_internal.h"
@@ -33,8 +35,14 @@ namespace {
 
 using namespace mf;
 
-constexpr int C = 64;     // query rows per workgroup, keys per key tile
-constexpr int NTH = 256;  // 4 waves, 16 query rows each
+constexpr int C = 64;     // keys per key tile
+constexpr int NTH = 256;  // 4 waves
+
+// 16-row query blocks per wave: 2 (128 query rows per workgroup) where the
+// registers allow, so every key and value fragment read from LDS feeds two
+// products; 1 (64 rows) for the widest heads.
+template <int K, int VMAX>
+constexpr int row_blocks() { return (K <= 128 && VMAX <= 128) ? 2 : 1; }
 
 __device__ __forceinline__ float log_gate(const ParallelParams& p, int b, int h, int t) {
   if (t >= p.T) return 0.f;
@@ -42,8 +50,26 @@ __device__ __forceinline__ float log_gate(const ParallelParams& p, int b, int h,
   return p.g_gamma != nullptr ? p.g_gamma[h] : 0.f;
 }
 
+// Inclusive scan of one 64-token gate tile over the wave (lane i: the sum of
+// tokens 0..i times 1/ln 2, rounded to float32), and the tile's total in
+// float64 natural-log units (every lane).
+__device__ __forceinline__ float tile_scan(float x, double& total) {
+  const int lane = threadIdx.x & 63;
+  double s = (double)x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double y = __shfl_up(s, d, 64);
+    if (lane >= d) s += y;
+  }
+  total = __shfl(s, 63, 64);
+  return (float)(s * kRcpLn2d);
+}
+
 template <int K, int VMAX, typename TOut>
-__global__ __launch_bounds__(NTH) void parallel_fwd_kernel(ParallelParams p) {
+__global__ __launch_bounds__(NTH, (K == 256 && VMAX == 256) ? 1 : 2) void parallel_fwd_kernel(ParallelParams p) {
+  constexpr int QB = row_blocks<K, VMAX>();
+  constexpr int QR = 64 * QB;    // query rows per workgroup
+  constexpr int WR = 16 * QB;    // query rows per wave
   constexpr int LDK = K + 8;     // row pitch of the key tile (bf16), padded against bank conflicts
   constexpr int LDV = VMAX + 8;  // row pitch of the value tile
   constexpr int NKP = K / 32;    // 16-byte pieces of the key tile per thread
@@ -52,31 +78,53 @@ __global__ __launch_bounds__(NTH) void parallel_fwd_kernel(ParallelParams p) {
   __shared__ __attribute__((aligned(16))) bf16 sK[C * LDK];
   __shared__ __attribute__((aligned(16))) bf16 sV[C * LDV];
   __shared__ __attribute__((aligned(16))) float sL[C];   // key gates inside the tile (log2)
+  __shared__ double sTot;                                 // the tile's gate total (natural log)
 
   const int T = p.T, H = p.H, Hkv = p.Hkv, V = p.V;
   const int nT = (T + C - 1) / C;
-  const UnitMap u = map_unit((int32_t)blockIdx.x, nT, Hkv, H / Hkv, p.B);
+  const int nQ = (T + QR - 1) / QR;
+  const UnitMap u = map_unit((int32_t)blockIdx.x, nQ, Hkv, H / Hkv, p.B);
   if (!u.valid) return;
-  const int it = nT - 1 - u.vt;  // longest row tiles first
+  const int iq = nQ - 1 - u.vt;  // longest query tiles first
   const int b = u.rank, h = u.hd, hk = u.hk;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, r = lane & 15;
-  const int i0 = it * C;
-  const int qi = i0 + 16 * w + r;  // query row this lane accumulates
+  const int i0 = iq * QR;
+  const int wr0 = WR * w;        // first row of this wave inside the query tile
   const int nvt = V / 16;
 
+  // queries of this lane's rows (i0 + wr0 + 16 qb + r), the B operand of S^T = K Q^T
   const bf16* qg = static_cast<const bf16*>(p.q);
-
-  // queries of this lane's row, as the B operand of S^T = K Q^T
-  bf16x8 qf[NKP];
+  // scale enters as log2|scale| in the exponent and its sign on q (a bf16
+  // sign flip is exact)
+  const float lscale = log2f(fabsf(p.scale));
+  const uint32_t qsign = p.scale < 0.f ? 0x80008000u : 0u;
+  bf16x8 qf[QB][NKP];
 #pragma unroll
-  for (int kk = 0; kk < NKP; ++kk) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (qi < T) x = *reinterpret_cast<const u32x4*>(qg + (((int64_t)b * T + qi) * H + h) * K + 32 * kk + 8 * g4);
-    qf[kk] = __builtin_bit_cast(bf16x8, x);
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = i0 + wr0 + 16 * qb + r;
+#pragma unroll
+    for (int kk = 0; kk < NKP; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (qi < T) x = *reinterpret_cast<const u32x4*>(qg + (((int64_t)b * T + qi) * H + h) * K + 32 * kk + 8 * g4);
+      qf[qb][kk] = __builtin_bit_cast(bf16x8, x ^ qsign);
+    }
   }
-  // running log2 gate of the query rows inside their tile
-  const float Lrow = wave_cumsum_log2(log_gate(p, b, h, i0 + lane));
-  const float Lq = __shfl(Lrow, 16 * w + r, 64);
+  // running log2 gate R of the query rows from the start of the query tile:
+  // one 64-row scan per half, the second continuing from the first
+  float Rh[QB];
+#pragma unroll
+  for (int hh = 0; hh < QB; ++hh) Rh[hh] = wave_cumsum_log2(log_gate(p, b, h, i0 + 64 * hh + lane));
+  float R63 = 0.f;  // R at the last row of the first half
+  if constexpr (QB == 2) {
+    R63 = __shfl(Rh[0], 63, 64);
+    Rh[1] += R63;
+  }
+  float Lq[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int rr = wr0 + 16 * qb + r;  // row inside the query tile; its half is uniform per wave
+    Lq[qb] = __shfl(Rh[(wr0 + 16 * qb) / 64], rr & 63, 64);
+  }
 
   // Key and value tiles come through buffer descriptors that start at the
   // tile: rows past T read as zeros, and so do the value columns past V (their
@@ -108,72 +156,84 @@ __global__ __launch_bounds__(NTH) void parallel_fwd_kernel(ParallelParams p) {
       vr[m] = __builtin_amdgcn_raw_buffer_load_b128(rv, vok ? vof + m * vstep : 0xfffffff0u, 0, 0);
     if (w == 0) gr = log_gate(p, b, h, j0 + lane);
   };
-  auto stage = [&]() {
-#pragma unroll
-    for (int m = 0; m < NKP; ++m) *reinterpret_cast<u32x4*>(sK + kls + m * KRS * LDK) = kr[m];
-#pragma unroll
-    for (int m = 0; m < NVP; ++m) *reinterpret_cast<u32x4*>(sV + vls + m * VRS * LDV) = vr[m];
-    if (w == 0) sL[lane] = wave_cumsum_log2(gr);
-  };
 
-  // The 64 A rows of this workgroup through one descriptor: rows past T are
+  // The A rows of this workgroup through one descriptor: rows past T are
   // dropped by its bound (and every store when no A is wanted: bound 0);
   // columns past T are kept out by the key-tile test.  16-byte stores need
   // rows 16-byte aligned (T % 4 == 0); otherwise every tile takes the
   // element-wise stores (tlim = 0).
   const int tlim = (T & 3) == 0 ? T : 0;
-  const int rows = min(C, T - i0);
+  const int rows = min(QR, T - i0);
   const __amdgpu_buffer_rsrc_t ra =
       make_rsrc(p.attn + (((int64_t)b * H + h) * T + i0) * (int64_t)T,
                 p.attn != nullptr ? (uint32_t)rows * (uint32_t)T * 4u : 0u);
-  const uint32_t arow = (uint32_t)(16 * w + r) * (uint32_t)T * 4u;  // this lane's row in the descriptor
 
-  f32x4 O[NVT];
+  f32x4 O[QB][NVT];
 #pragma unroll
-  for (int vt = 0; vt < NVT; ++vt) O[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float D = 0.f;  // log2 decay over the whole key tiles between this key tile and the query tile
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt) O[qb][vt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load(it);
-#pragma nounroll
-  for (int jt = it; jt >= 0; --jt) {
-    __syncthreads();  // the previous tile's LDS reads are done
-    stage();
-    __syncthreads();
-    if (jt > 0) load(jt - 1);
+  // The exponent of A[i][j] is R_i + D - L_j (log2 units): L_j the key's
+  // running gate inside its tile and D the gate sum from the key tile's start
+  // to the query tile's start (negative for the key tile in the second half of
+  // the query tile).  Key tiles are walked from the query tile leftwards, so
+  // D grows by each tile's total (accumulated in float64); workgroups of one
+  // head start at different key tiles, which spreads their A stores over
+  // the memory channels.
+  const int jd = QB * iq;                      // first key tile inside the query tile
+  const int jlast = min(jd + QB - 1, nT - 1);  // last key tile any row of the tile reaches
+  double Dacc = 0.0;
+  double Tnext = 0.0;  // gate total and running gates of the next key tile to stage (wave 0)
+  float Lnext = 0.f;
+
+  // One key tile: S^T on the matrix cores, the decay and (in the tiles that
+  // hold a diagonal) the causal mask, the A stores, then O^T += V^T A^T.
+  auto tile = [&](int jt, auto masked) {
     const int j0 = jt * C;
-    if (jt < it) D += sL[C - 1];
-
-    f32x4 s[4];
+    if (jt < jd) Dacc += sTot;
+    const float D = jt > jd ? -R63 : (float)(Dacc * kRcpLn2d);
+    f32x4 s[QB][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int kk = 0; kk < NKP; ++kk) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sK + (16 * kb + r) * LDK + 32 * kk + 8 * g4);
-        s[kb] = mfma(ka, qf[kk], s[kb]);
-      }
-    }
-    // s[kb][e] = (k_j . q_i) for key j = j0 + 16 kb + 4 g4 + e and query qi
-    const float base = Lq + D;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const f32x4 Lk = *reinterpret_cast<const f32x4*>(sL + 16 * kb + 4 * g4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s[kb][e] = p.scale * s[kb][e] * exp2_hw(base - Lk[e]);
-    }
-    // causal mask: inside the diagonal tile keys past the lane's query row are
-    // dropped; further left every key is kept
-    const int lim = jt == it ? 16 * w + r - 4 * g4 : C;
+      for (int kb = 0; kb < 4; ++kb) s[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (16 * kb + e > lim) s[kb][e] = 0.f;
-    {
+      for (int kk = 0; kk < NKP; ++kk) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sK + (16 * kb + r) * LDK + 32 * kk + 8 * g4);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma(ka, qf[qb][kk], s[qb][kb]);
+      }
+    // s[qb][kb][e] = (k_j . q_i) for key j = j0 + 16 kb + 4 g4 + e and
+    // query i = i0 + wr0 + 16 qb + r (q already carries the sign of scale)
+    f32x4 Lk[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) Lk[kb] = *reinterpret_cast<const f32x4*>(sL + 16 * kb + 4 * g4);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float base = Lq[qb] + D + lscale;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[qb][kb][e] = s[qb][kb][e] * exp2_hw(base - Lk[kb][e]);
+      if constexpr (decltype(masked)::value) {
+        // keys past the lane's query row are dropped (a wave whose rows all
+        // precede the tile computes it fully masked)
+        const int off = i0 + wr0 + 16 * qb - j0;
+        const int lim = off < C - 1 ? off + r - 4 * g4 : C;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (16 * kb + e > lim) s[qb][kb][e] = 0.f;
+      }
+      const uint32_t arow = (uint32_t)(wr0 + 16 * qb + r) * (uint32_t)T * 4u;
       if (j0 + C <= tlim) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[kb]), ra,
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s[qb][kb]), ra,
                                                  arow + (uint32_t)(j0 + 16 * kb + 4 * g4) * 4u, 0, 0);
       } else {
 #pragma unroll
@@ -181,8 +241,8 @@ __global__ __launch_bounds__(NTH) void parallel_fwd_kernel(ParallelParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int j = j0 + 16 * kb + 4 * g4 + e;
-            const float x = s[kb][e];  // element copied out first: a bit_cast of a vector element
-                                       // subscript would reinterpret the vector's first element
+            const float x = s[qb][kb][e];  // element copied out first: a bit_cast of a vector
+                                           // element subscript reinterprets the first element
             if (j < T)
               __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), ra,
                                                     arow + (uint32_t)j * 4u, 0, 0);
@@ -190,48 +250,92 @@ __global__ __launch_bounds__(NTH) void parallel_fwd_kernel(ParallelParams p) {
       }
     }
     // O^T += V^T A^T: the lane's A values for keys 32 hf + {4 g4 .. 4 g4 + 3,
-    // 16 + 4 g4 .. 16 + 4 g4 + 3} are the B operand in that key order, and the
-    // two transposed reads of V take the same keys.
+    // 16 + 4 g4 .. 16 + 4 g4 + 3} are the B operand in that key order, and
+    // the two transposed reads of V take the same keys.
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const float x[8] = {s[2 * hf][0], s[2 * hf][1], s[2 * hf][2], s[2 * hf][3],
-                          s[2 * hf + 1][0], s[2 * hf + 1][1], s[2 * hf + 1][2], s[2 * hf + 1][3]};
-      bf16x8 ah, al;
-      split8(x, ah, al);
+      bf16x8 ah[QB], al[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float x[8] = {s[qb][2 * hf][0], s[qb][2 * hf][1], s[qb][2 * hf][2], s[qb][2 * hf][3],
+                            s[qb][2 * hf + 1][0], s[qb][2 * hf + 1][1], s[qb][2 * hf + 1][2],
+                            s[qb][2 * hf + 1][3]};
+        split8(x, ah[qb], al[qb]);
+      }
 #pragma unroll
       for (int vt = 0; vt < NVT; ++vt) {  // value columns past V are zeros in the tile
         const bf16x8 vt8 = cat(tr_read(sV, LDV, 32 * hf + 4 * g4, 16 * vt),
                                tr_read(sV, LDV, 32 * hf + 16 + 4 * g4, 16 * vt));
-        O[vt] = mfma(vt8, ah, O[vt]);
-        O[vt] = mfma(vt8, al, O[vt]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          O[qb][vt] = mfma(vt8, ah[qb], O[qb][vt]);
+          O[qb][vt] = mfma(vt8, al[qb], O[qb][vt]);
+        }
       }
     }
+  };
+  // Stage key tile jt (loaded into registers one step earlier) and prefetch
+  // the next one.
+  auto next = [&](int jt) {
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int m = 0; m < NKP; ++m) *reinterpret_cast<u32x4*>(sK + kls + m * KRS * LDK) = kr[m];
+#pragma unroll
+    for (int m = 0; m < NVP; ++m) *reinterpret_cast<u32x4*>(sV + vls + m * VRS * LDV) = vr[m];
+    if (w == 0) {
+      sL[lane] = Lnext;
+      if (lane == 0) sTot = Tnext;
+    }
+    __syncthreads();
+    if (jt > 0) load(jt - 1);
+  };
+  auto after = [&](int jt) {
+    if (w == 0 && jt > 0) Lnext = tile_scan(gr, Tnext);  // gates of the tile loaded above
+  };
+
+  load(jlast);
+  Lnext = w == 0 ? tile_scan(gr, Tnext) : 0.f;
+#pragma nounroll
+  for (int jt = jlast; jt >= jd; --jt) {  // key tiles inside the query tile: causal mask
+    next(jt);
+    tile(jt, std::true_type{});
+    after(jt);
+  }
+#pragma nounroll
+  for (int jt = jd - 1; jt >= 0; --jt) {  // key tiles wholly before it
+    next(jt);
+    tile(jt, std::false_type{});
+    after(jt);
   }
 
-  // o: lane holds o[qi][16 vt + 4 g4 + e]
-  if (qi < T) {
-    TOut* orow = static_cast<TOut*>(p.o) + (((int64_t)b * T + qi) * H + h) * V;
+  // o: lane holds o[i][16 vt + 4 g4 + e] for its rows i
 #pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) {
-      if (vt < nvt) {
-        if constexpr (sizeof(TOut) == 4) {
-          *reinterpret_cast<f32x4*>(orow + 16 * vt + 4 * g4) = O[vt];
-        } else {
-          bf16x4 y;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = i0 + wr0 + 16 * qb + r;
+    if (qi < T) {
+      TOut* orow = static_cast<TOut*>(p.o) + (((int64_t)b * T + qi) * H + h) * V;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = (bf16)O[vt][e];
-          *reinterpret_cast<bf16x4*>(orow + 16 * vt + 4 * g4) = y;
+      for (int vt = 0; vt < NVT; ++vt) {
+        if (vt < nvt) {
+          if constexpr (sizeof(TOut) == 4) {
+            *reinterpret_cast<f32x4*>(orow + 16 * vt + 4 * g4) = O[qb][vt];
+          } else {
+            bf16x4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = (bf16)O[qb][vt][e];
+            *reinterpret_cast<bf16x4*>(orow + 16 * vt + 4 * g4) = y;
+          }
         }
       }
     }
   }
 
-  // zeros right of the diagonal tile, one row per wave at a time
+  // zeros right of the tile that holds this wave's diagonal, one row at a time
   {
-    const int cz = p.attn != nullptr ? min(T, i0 + C) : T;
+    const int cz = p.attn != nullptr ? min(T, ((i0 + wr0) / C + 1) * C) : T;
     const bool vec = tlim != 0;
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-    for (int rr = w; rr < rows && cz < T; rr += 4) {
+    for (int rr = wr0; rr < wr0 + WR && rr < rows && cz < T; ++rr) {
       const uint32_t ro = (uint32_t)rr * (uint32_t)T * 4u;
       if (vec) {
         for (int c = cz + 4 * lane; c < T; c += 256)
@@ -245,7 +349,9 @@ __global__ __launch_bounds__(NTH) void parallel_fwd_kernel(ParallelParams p) {
 }
 
 template <int K, int VMAX>
-hipError_t launch_kv(const ParallelParams& p, dim3 grid, hipStream_t stream) {
+hipError_t launch_kv(const ParallelParams& p, hipStream_t stream) {
+  constexpr int QR = 64 * row_blocks<K, VMAX>();
+  const dim3 grid((uint32_t)unit_grid(p.B, p.Hkv, p.H / p.Hkv, (p.T + QR - 1) / QR));
   if (p.o_f32)
     hipLaunchKernelGGL((parallel_fwd_kernel<K, VMAX, float>), grid, dim3(NTH), 0, stream, p);
   else
@@ -254,9 +360,9 @@ hipError_t launch_kv(const ParallelParams& p, dim3 grid, hipStream_t stream) {
 }
 
 template <int K>
-hipError_t launch_k(const ParallelParams& p, dim3 grid, hipStream_t stream) {
-  if (p.V <= 64) return launch_kv<K, 64>(p, grid, stream);
-  return p.V <= 128 ? launch_kv<K, 128>(p, grid, stream) : launch_kv<K, 256>(p, grid, stream);
+hipError_t launch_k(const ParallelParams& p, hipStream_t stream) {
+  if (p.V <= 64) return launch_kv<K, 64>(p, stream);
+  return p.V <= 128 ? launch_kv<K, 128>(p, stream) : launch_kv<K, 256>(p, stream);
 }
 
 }  // namespace
@@ -264,12 +370,10 @@ hipError_t launch_k(const ParallelParams& p, dim3 grid, hipStream_t stream) {
 hipError_t launch_parallel_fwd(const ParallelParams& p, hipStream_t stream) {
   if (p.B == 0 || p.T == 0) return hipSuccess;
   if (!parallel_supported(p.K, p.V) || p.Hkv <= 0 || p.H % p.Hkv != 0) return hipErrorInvalidValue;
-  const int32_t nT = (p.T + C - 1) / C;
-  const dim3 grid((uint32_t)unit_grid(p.B, p.Hkv, p.H / p.Hkv, nT));
   switch (p.K) {
-    case 64: return launch_k<64>(p, grid, stream);
-    case 128: return launch_k<128>(p, grid, stream);
-    default: return launch_k<256>(p, grid, stream);
+    case 64: return launch_k<64>(p, stream);
+    case 128: return launch_k<128>(p, stream);
+    default: return launch_k<256>(p, stream);
   }
 }
 

@@ -40,6 +40,8 @@ CASES = [
     small("weak_gate", B=1, T=300, K=128, V=64, gate_normalizer=10.0),
     small("k64_v256_t190", B=1, T=190, H=3, K=64, V=256),
     small("k256_v80", B=1, T=100, H=2, K=256, V=80),
+    small("negative_scale", B=1, T=140, K=128, V=64, scale=-0.3),   # sign carried by q, |scale| by the exponent
+    small("zero_scale", B=1, T=70, K=64, V=64, scale=0.0),
 ]
 
 
@@ -52,6 +54,9 @@ def run(inp, out_dtype=torch.float32, output_attn=True):
 
 
 def check(o, A, o_ref, A_ref, label):
+    if not np.any(A_ref):  # scale 0: everything is exactly zero
+        assert not np.any(A) and not np.any(o), label
+        return
     eo, ea = err_ratio(o, o_ref), err_ratio(A, A_ref)
     T = A.shape[-1]
     upper = np.triu(np.ones((T, T), dtype=bool), 1)
