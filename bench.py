@@ -63,6 +63,7 @@ KERNEL_SOURCES = {
     "chunk_fwd": ("chunk_prep_bf16.hip", "chunk_fwd_bf16_wide.hip", "mfma_common.h", "gate_scan.h",
                   "unit_map.h"),
     "recurrent_step_kernel": ("recurrent_step.hip",),
+    "parallel_fwd_kernel": ("parallel_fwd.hip", "mfma_common.h", "gate_scan.h", "unit_map.h"),
 }
 
 
@@ -505,6 +506,71 @@ def bench_gla(workload: str, steps: int, warmup: int, warm_seconds: float):
                      "dtype": "bf16" if bf16_chain else "f32"}}
 
 
+def bench_parallel(workload: str, steps: int, warmup: int, warm_seconds: float):
+    """sgla_parallel_fwd on a dense workload: the decayed attention matrix A
+    [B, H, T, T] float32 (zeros above the diagonal) and o = A v.  Writing A
+    dominates the algorithmic bytes (B H T^2 4 against a few tens of MB of
+    q, k, v, g and o), so the call is priced against HBM; a plain fill of a
+    buffer of A's size is timed beside it as the practical write ceiling."""
+    import numpy as np
+    import torch
+
+    import gated_linear_attention_amd as sgla
+    from gla_workloads import CHUNK_CONFIGS, make_chunk_inputs
+
+    w = CHUNK_CONFIGS[workload]
+    inp = make_chunk_inputs(w)
+    dev = torch.device("cuda:0")
+    t = lambda a, dt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+    q, k, v = t(inp["q"], torch.bfloat16), t(inp["k"], torch.bfloat16), t(inp["v"], torch.bfloat16)
+    g, gg = t(inp["g"], torch.float32), t(inp["g_gamma"], torch.float32)
+    step = lambda _i: sgla.parallel_fwd(q, k, v, g=g, g_gamma=gg, scale=inp["scale"], output_attn=True,
+                                        out_dtype=torch.float32)
+    warm_device(step, warm_seconds)
+    for i in range(warmup):
+        step(i)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            ev[i][0].record(stream)
+            fn(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)
+
+    per = timed(step, steps)
+    ms = sum(per) / len(per)
+    B, T, H, K, V, Hkv = inp["B"], inp["T"], inp["H"], inp["K"], inp["V"], inp["Hkv"]
+    abytes = B * H * T * T * 4
+    nbytes = (B * T * (H * K + Hkv * (K + V)) * 2 + (B * T * H * 4 if g is not None else 0)
+              + B * T * H * V * 4 + abytes)
+    flops = B * H * (T * (T + 1) // 2) * (2 * K + 2 * V)   # causal q.k and A v, as in the definition
+    fill_buf = torch.empty(B * H * T * T, device=dev, dtype=torch.float32)
+    fill_buf.fill_(0.0)  # first touch of the allocation outside the timing
+    fper = timed(lambda _i: fill_buf.fill_(0.0), max(3, steps // 2))
+    fill_gbs = abytes / (fper[len(fper) // 2] * 1e-3) / 1e9
+    del fill_buf
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": workload, "kernel": "parallel_fwd_kernel", "launches_per_call": 1,
+            "config": {"B": B, "T": T, "H": H, "num_kv_heads": Hkv, "K": K, "V": V,
+                       "gate": "g" if g is not None else ("g_gamma" if gg is not None else "none"),
+                       "attn": "float32 [B, H, T, T]", "o_dtype": "f32"},
+            "ms_per_call_mean": round(ms, 5), "ms_per_call_median": round(per[len(per) // 2], 5),
+            "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "algorithmic_bytes_per_call": int(nbytes), "algorithmic_flops_per_call": int(flops),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": load_traffic(workload, "parallel_fwd_kernel")},
+            "write_ceiling": {"kernel": "torch fill_ of an A-sized float32 buffer",
+                              "achieved_gbs": round(fill_gbs, 1),
+                              "frac_of_ceiling": round((abytes / (ms * 1e-3) / 1e9) / fill_gbs, 4)},
+            "mfma": {"achieved_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "peak_tflops": BF16_MFMA_PEAK_TFLOPS, "dtype": "bf16"}}
+
+
 def cpu_baseline(inp, min_seconds: float = 10.0):
     """The fp64 CPU oracle on whole batches of the timed workload, repeated
     until at least ``min_seconds`` of wall time (a bounded sample)."""
@@ -570,6 +636,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device-to-device copy of known size (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
+    ap.add_argument("--parallel-only", action="store_true",
+                    help="only time the parallel form (sgla_parallel_fwd) and print its record")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {a.gpus} is not supported (every "
@@ -583,6 +651,10 @@ def main():
 
     if a.calibrate_copy:
         calibrate_copy()
+        return
+    if a.parallel_only:
+        print(json.dumps({"parallel": bench_parallel("parallel_bf16_k128", a.steps, a.warmup,
+                                                     a.warm_seconds)}), flush=True)
         return
     r = bench_chunk(a.workload, a.steps, a.warmup, a.warm_seconds, a.expand_kv)
     inp = r["inp"]
@@ -639,6 +711,7 @@ def main():
         out["backward"] = bench_backward(a.backward_workload, 20, a.warmup, a.warm_seconds)
         out["normalizer"] = bench_normalizer(a.backward_workload, 20, a.warmup, a.warm_seconds)
         out["gla"] = bench_gla(a.backward_workload, 20, a.warmup, a.warm_seconds)
+        out["parallel"] = bench_parallel("parallel_bf16_k128", 10, a.warmup, a.warm_seconds)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)
