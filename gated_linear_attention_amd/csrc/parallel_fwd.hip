@@ -7,20 +7,23 @@
 //     A[i][j] = scale * (q_i . k_j) * 2^(b_i - b_j)   for j <= i, else 0
 //     o_i     = sum_j A[i][j] v_j
 //
-// One workgroup owns 64 query rows of one (batch row, query head) and walks
-// the key tiles from its diagonal tile back to the first one.  Every tile is
-// a dense contraction on the bf16 matrix cores: S^T = K_j Q_i^T with the
-// queries held in registers, then O^T += V_j^T A^T with A split into bf16
-// hi + lo halves (A itself is an fp32 product with a decay, not a bf16
-// value).  The exponent never needs the absolute running gate: it is the
-// query's gate inside its tile, minus the key's gate inside its tile, plus the
-// sum of the whole-tile gates in between, accumulated as the walk moves left,
-// so far-apart tokens do not cancel two large running sums.
+// One workgroup owns 128 query rows (64 when K or V is 256) of one (batch
+// row, query head) and walks the 64-key tiles from the tiles that hold its
+// diagonal back to the first one.  Every tile is a dense contraction on the
+// bf16 matrix cores: S^T = K_j Q_i^T with the queries held in registers, then
+// O^T += V_j^T A^T with A split into bf16 hi + lo halves (A itself is an fp32
+// product with a decay, not a bf16 value).  The exponent never needs the
+// absolute running gate: it is the query's gate inside its query tile, minus
+// the key's gate inside its key tile, plus the sum of the whole-tile gates in
+// between, accumulated in float64 as the walk moves left, so far-apart tokens
+// do not cancel two large running sums.
 //
 // Written A is T x T float32 per head, written once and never read again:
-// the kernel is bound by those stores, and every workgroup writes the same 64
-// full rows (computed tiles on and left of the diagonal, zeros right of it),
-// so the work per workgroup is even whatever its position.
+// the kernel is bound by those stores.  Every workgroup writes the same
+// number of full rows (computed tiles on and left of the diagonal, zeros
+// right of it), so the store work per workgroup is even whatever its
+// position; the 256-byte row segments of the computed tiles are what keeps
+// it below a plain fill's write rate.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
