@@ -717,6 +717,10 @@ sgla_status sgla_parallel_fwd(const sgla_chunk_args* args, const void* q, const 
   // one batch row of k or v (plus a tile of slack) is addressed with 32-bit byte offsets
   if (((int64_t)a.T + sgla::kChunk) * Hkv * std::max(a.K, a.V) * 2 > INT32_MAX)
     return fail(SGLA_ERR_UNSUPPORTED, "T x num_kv_heads x max(K, V) too large for the parallel form (T=%d)", a.T);
+  // the rows of A one workgroup writes are addressed with 32-bit byte offsets
+  // (128 rows of T floats); T beyond that would need petabytes of A anyway
+  if (attn != nullptr && a.T > (1 << 22))
+    return fail(SGLA_ERR_UNSUPPORTED, "writing A supports T <= 4194304 (got T=%d)", a.T);
   if (a.B == 0 || a.T == 0) return ok();
   const int32_t nT = (a.T + sgla::kChunk - 1) / sgla::kChunk;
   if (sgla::unit_grid(a.B, Hkv, a.H / Hkv, nT) > INT32_MAX)

@@ -330,7 +330,7 @@ sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t num_kv_heads, int3
  *   o        [B, T, H, V] in o_dtype
  *   attn     [B, H, T, T] float32 written in full (zeros above the diagonal),
  *            or NULL to compute o only.  B * H * T * T * 4 bytes: the caller
- *            sizes T accordingly.
+ *            sizes T accordingly (T <= 4194304 when A is written).
  * All buffers 16-byte aligned; no output may alias an input.  No workspace,
  * one kernel launch.  Supported: bf16 q, k, v (float32 inputs return
  * SGLA_ERR_UNSUPPORTED), K in {64, 128, 256}, V a multiple of 16 in [16, 256].

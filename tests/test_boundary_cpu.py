@@ -426,6 +426,7 @@ PAR_CASES = [
     ("negative T", dict(T=-1), {}, SHAPE, "B and T"),
     ("o NULL", {}, dict(o=None), INVALID, "non-NULL"),
     ("attn misaligned", {}, dict(attn_off=4), INVALID, "aligned"),
+    ("A rows past 32-bit offsets", dict(T=(1 << 22) + 64), {}, UNSUPPORTED, "T <= 4194304"),
 ]
 
 
