@@ -40,6 +40,8 @@ CASES = [
     small("weak_gate", B=1, T=300, K=128, V=64, gate_normalizer=10.0),
     small("k64_v256_t190", B=1, T=190, H=3, K=64, V=256),
     small("k256_v80", B=1, T=100, H=2, K=256, V=80),
+    small("gqa_gamma_b3", B=3, T=300, H=6, Hkv=3, K=128, V=128, gate="gamma"),
+    small("k64_v128_t257", B=1, T=257, H=2, K=64, V=128),        # ragged tail in the second half of a query tile
     small("negative_scale", B=1, T=140, K=128, V=64, scale=-0.3),   # sign carried by q, |scale| by the exponent
     small("zero_scale", B=1, T=70, K=64, V=64, scale=0.0),
 ]
