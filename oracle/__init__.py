@@ -147,17 +147,33 @@ def bwd(q, k, v, do, g=None, g_gamma=None, scale=None, initial_state=None, dht=N
         cu_seqlens=None, nthreads=None, lib=None, state_v_first=False):
     """Token-by-token backward: gradients of sum <do, o> + sum <dht, final_state>.
 
-    q, k: [B, T, H, K]; v, do: [B, T, H, V]; g: [B, T, H] or None; g_gamma:
-    [H] or None; initial_state, dht: [N, H, K, V] or None; cu_seqlens as for
-    fwd.  Returns a dict of float64 arrays dq, dk [B, T, H, K], dv [B, T, H,
-    V], dg [B, T, H] (None without g), dg_gamma [H] (None without g_gamma),
-    dh0 [N, H, K, V].  state_v_first: initial_state, dht and dh0 are [N, H, V, K]."""
+    q: [B, T, H, K]; k: [B, T, Hkv, K]; v: [B, T, Hkv, V]; do: [B, T, H, V];
+    g: [B, T, H] or None; g_gamma: [H] or None; initial_state, dht: [N, H, K,
+    V] or None; cu_seqlens as for fwd.  Returns a dict of float64 arrays dq
+    [B, T, H, K], dk [B, T, Hkv, K], dv [B, T, Hkv, V], dg [B, T, H] (None
+    without g), dg_gamma [H] (None without g_gamma), dh0 [N, H, K, V].
+    state_v_first: initial_state, dht and dh0 are [N, H, V, K].
+
+    Grouped kv heads (Hkv < H): query head h reads kv head h // (H // Hkv),
+    i.e. the forward sees k and v repeated n_rep = H // Hkv times along the
+    head axis; by the chain rule through that repeat, dk and dv of a kv head
+    are the sums of the per-query-head gradients of its n_rep copies."""
     initial_state, dht = _vk(initial_state, state_v_first), _vk(dht, state_v_first)
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, T, H, K = q.shape
     V = v.shape[-1]
-    if k.shape[2] != H:
-        raise ValueError("the oracle backward takes multi-head k and v (H heads)")
+    Hkv = k.shape[2]
+    if H % Hkv != 0:
+        raise ValueError("the kv head count must divide the query head count")
+    if Hkv != H:
+        rep = H // Hkv
+        gr = bwd(q, np.repeat(k, rep, axis=2), np.repeat(v, rep, axis=2), do, g=g, g_gamma=g_gamma,
+                 scale=scale, initial_state=initial_state, dht=dht, cu_seqlens=cu_seqlens,
+                 nthreads=nthreads, lib=lib)
+        gr["dk"] = gr["dk"].reshape(B, T, Hkv, rep, K).sum(axis=3)
+        gr["dv"] = gr["dv"].reshape(B, T, Hkv, rep, V).sum(axis=3)
+        gr["dh0"] = _vk(gr["dh0"], state_v_first)
+        return gr
     if scale is None:
         scale = K ** -0.5
     g, g_gamma, h0, dht = _f64(g), _f64(g_gamma), _f64(initial_state), _f64(dht)

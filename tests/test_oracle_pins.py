@@ -425,6 +425,43 @@ def pin_bwd_finite_differences(lib, seed=13, H=2, K=3, V=2):
     return True
 
 
+def pin_bwd_gqa_finite_differences(lib, seed=21, H=4, Hkv=2, K=3, V=2):
+    """Backward with grouped kv heads (query head h reads kv head h // (H //
+    Hkv)): dq, dk [T, Hkv, K], dv [T, Hkv, V], dg and dh0 equal the central
+    finite differences of the grouped forward, which evaluates the kv rows of
+    each group directly (no repeat), on packed sequences."""
+    rng = np.random.default_rng(seed)
+    cu = np.array([0, 4, 9], dtype=np.int64)
+    T, N = 9, 2
+    q, k, v = _rand(rng, 1, T, H, K), _rand(rng, 1, T, Hkv, K), _rand(rng, 1, T, Hkv, V)
+    do = _rand(rng, 1, T, H, V)
+    dht = _rand(rng, N, H, K, V)
+    S0 = _rand(rng, N, H, K, V)
+    g = logsigmoid(_rand(rng, 1, T, H))
+    scale, eps = 0.6, 1e-6
+    gr = oracle.bwd(q, k, v, do, g=g, scale=scale, initial_state=S0, dht=dht, cu_seqlens=cu,
+                    nthreads=1, lib=lib)
+    if gr["dk"].shape != k.shape or gr["dv"].shape != v.shape:
+        return False
+    args = dict(q=q, k=k, v=v, g=g, S0=S0)
+    want = dict(q="dq", k="dk", v="dv", g="dg", S0="dh0")
+    for name, gname in want.items():
+        x = args[name]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            a = dict(args)
+            xp = x.copy(); xp[idx] += eps
+            xm = x.copy(); xm[idx] -= eps
+            a[name] = xp
+            lp = _loss(lib, a["q"], a["k"], a["v"], a["g"], None, scale, a["S0"], cu, do, dht)
+            a[name] = xm
+            lm = _loss(lib, a["q"], a["k"], a["v"], a["g"], None, scale, a["S0"], cu, do, dht)
+            fd[idx] = (lp - lm) / (2 * eps)
+        if _rel(gr[gname], fd) > 1e-6:
+            return False
+    return True
+
+
 def pin_bwd_gate_identity(lib, seed=14, B=2, T=150, H=2, K=5, V=4):
     """The gate gradient from the mathematics of the scalar gate: every term of
     o_t and of the final state depends on the log gates only through
@@ -594,7 +631,8 @@ ALL_PINS = [pin_chunk_local_cumsum, pin_hand_example, pin_brute_force, pin_zero_
             pin_prefill_then_decode, pin_step_brute_force, pin_gqa_is_repeated_mha,
             pin_step_variants, pin_bwd_finite_differences, pin_bwd_gate_identity,
             pin_state_v_first, pin_normalizer, pin_gla_scalar_gate_is_simple_gla,
-            pin_gla_brute_force, pin_parallel_equals_recurrence, pin_parallel_special_gates]
+            pin_gla_brute_force, pin_parallel_equals_recurrence, pin_parallel_special_gates,
+            pin_bwd_gqa_finite_differences]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
