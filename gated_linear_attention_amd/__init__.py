@@ -238,21 +238,24 @@ def chunk_bwd(q, k, v, do, g=None, g_gamma=None, scale=None, initial_state=None,
     """Backward of chunk_fwd on the GPU: gradients of sum <do, o> + sum <dht,
     final_state> (dht None: no loss on the final state).
 
-    q, k [B, T, H, K], v, do [B, T, H, V] (all bf16 or all float32), g, g_gamma,
-    initial_state and cu_seqlens as for chunk_fwd.  Returns a dict of float32
-    tensors: dq, dk [B, T, H, K], dv [B, T, H, V], dg [B, T, H] (None without g),
-    dg_gamma [H] (None without g_gamma), dh0 [N, H, K, V]."""
+    q [B, T, H, K], k [B, T, Hkv, K], v [B, T, Hkv, V], do [B, T, H, V] (all
+    bf16 or all float32; Hkv divides H), g, g_gamma, initial_state and
+    cu_seqlens as for chunk_fwd.  Returns a dict of float32 tensors: dq [B, T,
+    H, K], dk [B, T, Hkv, K], dv [B, T, Hkv, V] (a kv head's gradient sums
+    the query heads that read it), dg [B, T, H] (None without g), dg_gamma [H]
+    (None without g_gamma), dh0 [N, H, K, V]."""
     if not isinstance(q, torch.Tensor) or q.dim() != 4:
         raise ValueError("q must be a 4-D tensor [B, T, H, K]")
     dev = q.device
     B, T, H, K = q.shape
     if not isinstance(v, torch.Tensor) or v.dim() != 4:
-        raise ValueError("v must be a 4-D tensor [B, T, H, V]")
+        raise ValueError("v must be a 4-D tensor [B, T, Hkv, V]")
     V = v.shape[-1]
+    Hkv = _kv_heads(k, H, 2)
     qkv = _dtype_code(q.dtype, "q")
     _check_dev("q", q, dev)
-    _check_dev("k", k, dev, q.dtype, (B, T, H, K))
-    _check_dev("v", v, dev, q.dtype, (B, T, H, V))
+    _check_dev("k", k, dev, q.dtype, (B, T, Hkv, K))
+    _check_dev("v", v, dev, q.dtype, (B, T, Hkv, V))
     _check_dev("do", do, dev, q.dtype, (B, T, H, V))
     if g is not None and g_gamma is not None:
         raise ValueError("g and g_gamma are mutually exclusive; pass at most one")
@@ -267,15 +270,15 @@ def chunk_bwd(q, k, v, do, g=None, g_gamma=None, scale=None, initial_state=None,
     _check_dev("dht", dht, dev, torch.float32, sshape)
     if scale is None:
         scale = K ** -0.5
-    args = _chunk_args(B, T, H, K, V, N, chunk_size, qkv, _F32, scale, 0, H, state_v_first)
+    args = _chunk_args(B, T, H, K, V, N, chunk_size, qkv, _F32, scale, 0, Hkv, state_v_first)
     cu_ptr = None if cu is None else ctypes.c_void_p(cu.data_ptr())
     n = lib.sgla_chunk_bwd_workspace_size(ctypes.byref(args), cu_ptr)
     if n == 0 and lib.sgla_last_error():
         raise ValueError(f"sgla_chunk_bwd_workspace_size: {lib.sgla_last_error().decode(errors='replace')}")
     f32 = dict(device=dev, dtype=torch.float32)
     dq = torch.empty((B, T, H, K), **f32)
-    dk = torch.empty((B, T, H, K), **f32)
-    dv = torch.empty((B, T, H, V), **f32)
+    dk = torch.empty((B, T, Hkv, K), **f32)
+    dv = torch.empty((B, T, Hkv, V), **f32)
     dg = torch.empty((B, T, H), **f32) if g is not None else None
     dgg = torch.empty((H,), **f32) if g_gamma is not None else None
     dh0 = torch.empty(sshape, **f32)

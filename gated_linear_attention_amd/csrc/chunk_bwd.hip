@@ -131,8 +131,8 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                        const TIn* __restrict__ v, const TIn* __restrict__ dout,
                        const float* __restrict__ g, const float* __restrict__ g_gamma,
                        const float* __restrict__ h0, const float* __restrict__ dht,
-                       float* __restrict__ dh0, float scale, int32_t H, int32_t V, StateLayout sl,
-                       SeqLayout seqs,
+                       float* __restrict__ dh0, float scale, int32_t H, int32_t Hkv, int32_t V,
+                       StateLayout sl, SeqLayout seqs,
                        int32_t chunks_per_row, float* __restrict__ hbuf, float* __restrict__ dhbuf) {
   constexpr int LDX = K + 4;
   constexpr int NST = (K / 16) * 2;
@@ -149,6 +149,7 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   const UnitMap um = map_unit(bid, V / VT, H, 1, seqs.num_seqs);
   if (!um.valid) return;
   const int hd = um.hd, vt = um.vt;
+  const int hk = hd / (H / Hkv);   // kv head whose k and v rows this query head reads
   const SeqInfo si = seq_info(seqs, um.rank, chunks_per_row);
   const int nchunks = (si.len + C - 1) / C;
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
@@ -181,8 +182,9 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     const int m = rev ? nchunks - 1 - it : it;
     const int64_t t0 = si.bos + (int64_t)m * C;
     const int cl = min(C, si.len - m * C);
-    xt.load((rev ? q : k) + (t0 * H + hd) * K, (int64_t)H * K, cl);
-    yt.load((rev ? dout : v) + (t0 * H + hd) * V + ucol, (int64_t)H * V, cl);
+    xt.load(rev ? q + (t0 * H + hd) * K : k + (t0 * Hkv + hk) * K, (int64_t)(rev ? H : Hkv) * K, cl);
+    yt.load(rev ? dout + (t0 * H + hd) * V + ucol : v + (t0 * Hkv + hk) * V + ucol,
+            (int64_t)(rev ? H : Hkv) * V, cl);
     if (w == 0 && g != nullptr) gx = lane < cl ? g[(t0 + lane) * H + hd] : 0.f;
   };
   if (nchunks > 0) load_chunk(0);
@@ -262,7 +264,7 @@ __global__ void __launch_bounds__(NTG)
 chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                       const TIn* __restrict__ v, const TIn* __restrict__ dout,
                       const float* __restrict__ g, const float* __restrict__ g_gamma, float scale,
-                      int32_t H, int32_t V, SeqLayout seqs, int32_t chunks_per_row,
+                      int32_t H, int32_t Hkv, int32_t V, SeqLayout seqs, int32_t chunks_per_row,
                       const float* __restrict__ hbuf, const float* __restrict__ dhbuf,
                       float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
                       float* __restrict__ dg, float* __restrict__ gpart) {
@@ -299,7 +301,9 @@ chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   const int rw = w & 3, kh = w >> 2;
   const bool has_k = NKT >= 2 || kh == 0;       // K = 16: one column tile, taken by kh = 0
   const int kt0 = kh * NKH;
-  const int64_t RSK = (int64_t)H * K, RSV = (int64_t)H * V;
+  const int hk = hd / (H / Hkv);   // kv head whose k and v rows this query head reads
+  const int64_t RSK = (int64_t)H * K, RSV = (int64_t)H * V;        // q and dout rows
+  const int64_t RKK = (int64_t)Hkv * K, RKV = (int64_t)Hkv * V;    // k and v rows
   const int64_t KV = (int64_t)K * V;
   const float* hu = hbuf + ((int64_t)gc * H + hd) * KV;
   const float* dhu = dhbuf + ((int64_t)gc * H + hd) * KV;
@@ -307,7 +311,7 @@ chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   {
     RowTile<K, NTG, TIn> qt, kt;
     qt.load(q + (t0 * H + hd) * K, RSK, cl);
-    kt.load(k + (t0 * H + hd) * K, RSK, cl);
+    kt.load(k + (t0 * Hkv + hk) * K, RKK, cl);
     qt.store(sQ, LDQ);
     kt.store(sK, LDQ);
   }
@@ -322,7 +326,7 @@ chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   RowTile<VT, NTG, TIn> vtile, otile;
   RecTile<K, NTG> htile, dhtile;
   auto load_slice = [&](int vs) {
-    vtile.load(v + (t0 * H + hd) * V + vs * VT, RSV, cl);
+    vtile.load(v + (t0 * Hkv + hk) * V + vs * VT, RKV, cl);
     otile.load(dout + (t0 * H + hd) * V + vs * VT, RSV, cl);
     htile.load(hu, V, (int64_t)vs * VT);
     dhtile.load(dhu, V, (int64_t)vs * VT);
@@ -521,6 +525,24 @@ chunk_bwd_gamma_kernel(const float* __restrict__ gpart, int32_t num_chunks, int3
   if (threadIdx.x == 0) dg_gamma[hd] = (float)part[0];
 }
 
+// Gradients of k and v with grouped kv heads: a kv head's row is read by its
+// n_rep query heads, so its gradient is the sum of theirs (computed per query
+// head by the kernels above).  One thread per 4 consecutive elements of a
+// (token, kv head) row; the n_rep terms are added in query-head order.
+__global__ void __launch_bounds__(256)
+kv_group_sum_kernel(const float* __restrict__ src, float* __restrict__ dst, int64_t rows, int32_t n_rep,
+                    int32_t D) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // float4 index into dst
+  const int32_t d4 = D / 4;
+  if (i >= rows * d4) return;
+  const int64_t row = i / d4;                                   // token * Hkv + kv head
+  const int32_t c = (int32_t)(i - row * d4);
+  const f32x4* s = reinterpret_cast<const f32x4*>(src) + row * n_rep * d4 + c;
+  f32x4 acc = s[0];
+  for (int32_t j = 1; j < n_rep; ++j) acc += s[(int64_t)j * d4];
+  reinterpret_cast<f32x4*>(dst)[i] = acc;
+}
+
 template <int K, typename TIn>
 hipError_t launch_k(const ChunkBwdParams& p, hipStream_t stream) {
   const int per_row = p.seqs.T > 0 ? (p.seqs.T + C - 1) / C : 1;
@@ -534,8 +556,8 @@ hipError_t launch_k(const ChunkBwdParams& p, hipStream_t stream) {
   } else if (p.seqs.num_seqs > 0) {
     const int units = (int)unit_grid(p.seqs.num_seqs, p.H, 1, p.V / VT);
     hipLaunchKernelGGL((chunk_bwd_state_kernel<K, TIn>), dim3((unsigned)(2 * units)), dim3(NT), 0, stream,
-                       q, k, v, dout, p.g, p.g_gamma, p.h0, p.dht, p.dh0, p.scale, p.H, p.V, p.sl, p.seqs,
-                       per_row, p.hbuf, p.dhbuf);
+                       q, k, v, dout, p.g, p.g_gamma, p.h0, p.dht, p.dh0, p.scale, p.H, p.Hkv, p.V, p.sl,
+                       p.seqs, per_row, p.hbuf, p.dhbuf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -544,7 +566,7 @@ hipError_t launch_k(const ChunkBwdParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   } else if (p.seqs.num_chunks > 0) {
     hipLaunchKernelGGL((chunk_bwd_grad_kernel<K, TIn>), dim3((unsigned)p.seqs.num_chunks, (unsigned)p.H),
-                       dim3(NTG), 0, stream, q, k, v, dout, p.g, p.g_gamma, p.scale, p.H, p.V, p.seqs,
+                       dim3(NTG), 0, stream, q, k, v, dout, p.g, p.g_gamma, p.scale, p.H, p.Hkv, p.V, p.seqs,
                        per_row, p.hbuf, p.dhbuf, p.dq, p.dk, p.dv, p.dg,
                        p.dg_gamma != nullptr ? p.gpart : nullptr);
     hipError_t e = hipGetLastError();
@@ -570,6 +592,16 @@ hipError_t launch_in(const ChunkBwdParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_kv_group_sum(const float* src, float* dst, int64_t tokens, int32_t H, int32_t Hkv,
+                               int32_t D, hipStream_t stream) {
+  const int64_t n4 = tokens * Hkv * (D / 4);
+  if (n4 == 0) return hipSuccess;
+  if (D % 4 != 0 || Hkv <= 0 || H % Hkv != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kv_group_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, src, dst,
+                     tokens * Hkv, H / Hkv, D);
+  return hipGetLastError();
+}
 
 hipError_t launch_chunk_bwd(const ChunkBwdParams& p, hipStream_t stream) {
   return p.qkv_bf16 ? launch_in<__bf16>(p, stream) : launch_in<float>(p, stream);

@@ -83,7 +83,7 @@ __global__ void __launch_bounds__(NTG)
 chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                            const bf16* __restrict__ v, const bf16* __restrict__ dout,
                            const float* __restrict__ g, const float* __restrict__ g_gamma, float scale,
-                           int32_t H, int32_t V, SeqLayout seqs, int32_t chunks_per_row,
+                           int32_t H, int32_t Hkv, int32_t V, SeqLayout seqs, int32_t chunks_per_row,
                            const float* __restrict__ hbuf, const float* __restrict__ dhbuf,
                            float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
                            float* __restrict__ dg, float* __restrict__ gpart) {
@@ -128,7 +128,8 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int rw = w & 3, kh = w >> 2;
   const int kt0 = kh * NKH;
-  const int64_t RSK = (int64_t)H * K, RSV = (int64_t)H * V;
+  const int hk = hd / (H / Hkv);   // kv head whose k and v rows this query head reads
+  const int64_t RSV = (int64_t)H * V, RKV = (int64_t)Hkv * V;   // dout and v row strides
   const int64_t KV = (int64_t)K * V;
   const float* hu = hbuf + ((int64_t)gc * H + hd) * KV;
   const float* dhu = dhbuf + ((int64_t)gc * H + hd) * KV;
@@ -147,7 +148,7 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
       kx[u] = make_uint4(0u, 0u, 0u, 0u);
       if (c < cl) {
         qx[u] = *reinterpret_cast<const uint4*>(q + ((t0 + c) * H + hd) * K + e);
-        kx[u] = *reinterpret_cast<const uint4*>(k + ((t0 + c) * H + hd) * K + e);
+        kx[u] = *reinterpret_cast<const uint4*>(k + ((t0 + c) * Hkv + hk) * K + e);
       }
     }
 #pragma unroll
@@ -185,9 +186,9 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
       vx[u] = make_uint2(0u, 0u);
       ox[u] = make_uint2(0u, 0u);
       if (row < cl) {
-        const int64_t off = (t0 + row) * RSV + (int64_t)hd * V + vs * VS + 4 * c4;
-        vx[u] = *reinterpret_cast<const uint2*>(v + off);
-        ox[u] = *reinterpret_cast<const uint2*>(dout + off);
+        const int64_t col = vs * VS + 4 * c4;
+        vx[u] = *reinterpret_cast<const uint2*>(v + (t0 + row) * RKV + (int64_t)hk * V + col);
+        ox[u] = *reinterpret_cast<const uint2*>(dout + (t0 + row) * RSV + (int64_t)hd * V + col);
       }
     }
 #pragma unroll
@@ -432,8 +433,8 @@ chunk_bwd_state_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__
                             const bf16* __restrict__ v, const bf16* __restrict__ dout,
                             const float* __restrict__ g, const float* __restrict__ g_gamma,
                             const float* __restrict__ h0, const float* __restrict__ dht,
-                            float* __restrict__ dh0, float scale, int32_t H, int32_t V, StateLayout sl,
-                            SeqLayout seqs, int32_t chunks_per_row, float* __restrict__ hbuf,
+                            float* __restrict__ dh0, float scale, int32_t H, int32_t Hkv, int32_t V,
+                            StateLayout sl, SeqLayout seqs, int32_t chunks_per_row, float* __restrict__ hbuf,
                             float* __restrict__ dhbuf) {
   constexpr int LDX = K + 16;          // K / Q row stride (elements)
   constexpr int RT = K / 64;           // 16-row state tiles per wave (K/4 rows)
@@ -454,6 +455,7 @@ chunk_bwd_state_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__
   const UnitMap um = map_unit(bid, V / VS, H, 1, seqs.num_seqs);
   if (!um.valid) return;
   const int hd = um.hd, vt = um.vt;
+  const int hk = hd / (H / Hkv);   // kv head whose k and v rows this query head reads
   int64_t bos;
   int32_t len, seq, chunk0;
   if (seqs.seq_table != nullptr) {
@@ -494,8 +496,10 @@ chunk_bwd_state_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__
   // chunk m's rows and gate, loaded into registers one iteration ahead
   uint4 xx[NX], yx;
   float gx = 0.f;
-  const bf16* xsrc = rev ? q : k;
-  const bf16* ysrc = rev ? dout : v;
+  // reverse: q and dout rows of the query head; forward: k and v rows of its kv head
+  const bf16* xsrc = rev ? q + hd * K : k + hk * K;
+  const bf16* ysrc = rev ? dout + hd * V : v + hk * V;
+  const int64_t xrs = (int64_t)(rev ? H : Hkv) * K, yrs = (int64_t)(rev ? H : Hkv) * V;
   auto load_chunk = [&](int it) {
     const int m = rev ? nchunks - 1 - it : it;
     const int64_t t0 = bos + (int64_t)m * C;
@@ -505,12 +509,12 @@ chunk_bwd_state_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__
       const int p = tid + NTS * u;
       const int c = p / PRX;
       xx[u] = make_uint4(0u, 0u, 0u, 0u);
-      if (c < cl) xx[u] = *reinterpret_cast<const uint4*>(xsrc + ((t0 + c) * H + hd) * K + 8 * (p % PRX));
+      if (c < cl) xx[u] = *reinterpret_cast<const uint4*>(xsrc + (t0 + c) * xrs + 8 * (p % PRX));
     }
     {
       const int c = tid / (VS / 8);
       yx = make_uint4(0u, 0u, 0u, 0u);
-      if (c < cl) yx = *reinterpret_cast<const uint4*>(ysrc + ((t0 + c) * H + hd) * V + ucol + 8 * (tid % (VS / 8)));
+      if (c < cl) yx = *reinterpret_cast<const uint4*>(ysrc + (t0 + c) * yrs + ucol + 8 * (tid % (VS / 8)));
     }
     if (w == 0 && g != nullptr) gx = lane < cl ? g[(t0 + lane) * H + hd] : 0.f;
   };
@@ -605,7 +609,7 @@ hipError_t launch_grad_k(const ChunkBwdParams& p, int32_t chunks_per_row, hipStr
   hipLaunchKernelGGL((chunk_bwd_grad_bf16_kernel<K>), dim3((unsigned)p.seqs.num_chunks, (unsigned)p.H),
                      dim3(NTG), 0, stream, static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
                      static_cast<const bf16*>(p.v), static_cast<const bf16*>(p.dout), p.g, p.g_gamma,
-                     p.scale, p.H, p.V, p.seqs, chunks_per_row, p.hbuf, p.dhbuf, p.dq, p.dk, p.dv, p.dg,
+                     p.scale, p.H, p.Hkv, p.V, p.seqs, chunks_per_row, p.hbuf, p.dhbuf, p.dq, p.dk, p.dv, p.dg,
                      p.dg_gamma != nullptr ? p.gpart : nullptr);
   return hipGetLastError();
 }
@@ -616,7 +620,7 @@ hipError_t launch_state_k(const ChunkBwdParams& p, int32_t chunks_per_row, hipSt
   hipLaunchKernelGGL((chunk_bwd_state_bf16_kernel<K>), dim3((unsigned)(2 * units)), dim3(NTS), 0, stream,
                      static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
                      static_cast<const bf16*>(p.v), static_cast<const bf16*>(p.dout), p.g, p.g_gamma, p.h0,
-                     p.dht, p.dh0, p.scale, p.H, p.V, p.sl, p.seqs, chunks_per_row, p.hbuf, p.dhbuf);
+                     p.dht, p.dh0, p.scale, p.H, p.Hkv, p.V, p.sl, p.seqs, chunks_per_row, p.hbuf, p.dhbuf);
   return hipGetLastError();
 }
 

@@ -162,7 +162,7 @@ sgla_status need_chunk64(const Plan& P) {
 // per-chunk gate sums.
 struct BwdPlan {
   Plan P;
-  size_t h_off = 0, dh_off = 0, gpart_off = 0, total_bytes = 0;
+  size_t h_off = 0, dh_off = 0, gpart_off = 0, dkq_off = 0, dvq_off = 0, total_bytes = 0;
 };
 
 sgla_status plan_bwd(const sgla_chunk_args* a, const int64_t* cu, BwdPlan* B) {
@@ -176,16 +176,20 @@ sgla_status plan_bwd(const sgla_chunk_args* a, const int64_t* cu, BwdPlan* B) {
     return fail(SGLA_ERR_UNSUPPORTED, "the backward supports K in {16,32,64,128} (got %d)", a->K);
   if (a->V <= 0 || a->V % 32 != 0)
     return fail(SGLA_ERR_UNSUPPORTED, "the backward supports V a multiple of 32 (got %d)", a->V);
-  if (B->P.Hkv != a->H)
-    return fail(SGLA_ERR_UNSUPPORTED, "the backward supports multi-head k and v only (num_kv_heads=%d, H=%d)",
-                a->num_kv_heads, a->H);
   if (!std::isfinite(a->scale)) return fail(SGLA_ERR_INVALID_ARG, "scale must be finite");
   const size_t tasks = (size_t)B->P.num_chunks * a->H;
   const size_t rec = tasks * (size_t)a->K * a->V * sizeof(float);
   B->h_off = align_up(B->P.total_bytes, 256);
   B->dh_off = B->h_off + align_up(rec, 256);
   B->gpart_off = B->dh_off + align_up(rec, 256);
-  B->total_bytes = B->gpart_off + align_up(tasks * sizeof(float), 256);
+  B->dkq_off = B->gpart_off + align_up(tasks * sizeof(float), 256);
+  B->total_bytes = B->dkq_off;
+  if (B->P.Hkv != a->H) {
+    // grouped kv heads: k and v gradients per query head, summed over each group
+    const size_t th = (size_t)B->P.total_tokens * a->H;
+    B->dvq_off = B->dkq_off + align_up(th * (size_t)a->K * sizeof(float), 256);
+    B->total_bytes = B->dvq_off + align_up(th * (size_t)a->V * sizeof(float), 256);
+  }
   return SGLA_OK;
 }
 
@@ -379,14 +383,16 @@ sgla_status sgla_chunk_bwd(const sgla_chunk_args* args, const void* q, const voi
   p.g_gamma = g_gamma;
   p.h0 = initial_state;
   p.dht = dht;
+  const bool grouped = P.Hkv != a.H;
   p.dq = dq;
-  p.dk = dk;
-  p.dv = dv;
+  p.dk = grouped ? reinterpret_cast<float*>(ws + B.dkq_off) : dk;
+  p.dv = grouped ? reinterpret_cast<float*>(ws + B.dvq_off) : dv;
   p.dg = g != nullptr ? dg : nullptr;
   p.dg_gamma = g_gamma != nullptr ? dg_gamma : nullptr;
   p.dh0 = dh0;
   p.scale = a.scale;
   p.H = a.H;
+  p.Hkv = P.Hkv;
   p.K = a.K;
   p.V = a.V;
   p.qkv_bf16 = a.qkv_dtype == SGLA_BF16;
@@ -397,6 +403,11 @@ sgla_status sgla_chunk_bwd(const sgla_chunk_args* args, const void* q, const voi
   p.gpart = reinterpret_cast<float*>(ws + B.gpart_off);
   hipError_t e = sgla::launch_chunk_bwd(p, stream);
   if (e != hipSuccess) return hip_fail(e, "launching the backward kernels");
+  if (grouped) {
+    e = sgla::launch_kv_group_sum(p.dk, dk, P.total_tokens, a.H, P.Hkv, a.K, stream);
+    if (e == hipSuccess) e = sgla::launch_kv_group_sum(p.dv, dv, P.total_tokens, a.H, P.Hkv, a.V, stream);
+    if (e != hipSuccess) return hip_fail(e, "launching the kv-group gradient sum");
+  }
   return ok();
 }
 

@@ -121,13 +121,14 @@ struct ChunkBwdParams {
   const float* h0;           // [N, H, K, V] or nullptr
   const float* dht;          // [N, H, K, V] or nullptr
   float* dq;                 // [T_total, H, K]
-  float* dk;
-  float* dv;                 // [T_total, H, V]
+  float* dk;                 // [T_total, H, K]: per query head (summed over kv groups afterwards)
+  float* dv;                 // [T_total, H, V]: per query head
   float* dg;                 // [T_total, H] or nullptr
   float* dg_gamma;           // [H] or nullptr
   float* dh0;                // [N, H, K, V] or nullptr
   float scale;
   int32_t H, K, V;
+  int32_t Hkv;               // kv heads of k and v (divides H); query head h reads kv head h / (H / Hkv)
   int32_t qkv_bf16;
   StateLayout sl;            // layout of h0, dht and dh0
   SeqLayout seqs;
@@ -137,6 +138,10 @@ struct ChunkBwdParams {
 };
 
 hipError_t launch_chunk_bwd(const ChunkBwdParams& p, hipStream_t stream);
+// dk [T_total, Hkv, K] (and dv likewise) = the sum of the n_rep = H / Hkv
+// query-head gradients of each kv head, in query-head order
+hipError_t launch_kv_group_sum(const float* src, float* dst, int64_t tokens, int32_t H, int32_t Hkv,
+                               int32_t D, hipStream_t stream);
 
 // The backward (state pass and per-chunk gradients) runs on the bf16 matrix
 // cores (hi/lo splits of the fp32 operands) for bf16 inputs with K in {64,

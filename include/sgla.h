@@ -150,9 +150,10 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args *args,
 /*
  * Bytes of device workspace sgla_chunk_bwd needs: the packed-sequence tables,
  * the fp32 state entering every 64-token chunk and the fp32 gradient of the
- * state leaving it (2 * 4 K V bytes per chunk and head), and 4 bytes per
- * chunk and head for the g_gamma reduction.  Returns 0 on invalid arguments
- * (reason in sgla_last_error()).
+ * state leaving it (2 * 4 K V bytes per chunk and head), 4 bytes per
+ * chunk and head for the g_gamma reduction, and with grouped kv heads (Hkv <
+ * H) the per-query-head k and v gradients (4 (K + V) bytes per token and
+ * query head).  Returns 0 on invalid arguments (reason in sgla_last_error()).
  */
 size_t sgla_chunk_bwd_workspace_size(const sgla_chunk_args *args, const int64_t *cu_seqlens_host);
 
@@ -166,26 +167,30 @@ size_t sgla_chunk_bwd_workspace_size(const sgla_chunk_args *args, const int64_t 
  * the same arguments.  Three launches: a state pass (forward states and
  * reverse state gradients, one workgroup per (sequence, head, 32-column V
  * tile) each), a per-(chunk, head) gradient kernel, and with g_gamma a
- * per-head reduction.  bf16 inputs with K in {64, 128} run both passes on
+ * per-head reduction; with grouped kv heads one more launch per gradient
+ * sums the query heads of each kv group.  bf16 inputs with K in {64, 128} run both passes on
  * the bf16 matrix cores (the fp32 states, state gradients and intra-chunk
  * matrices split into bf16 hi + lo); other inputs on the fp32 matrix cores.
  *
  * Arguments (device pointers unless stated):
  *   args            as for sgla_chunk_fwd; o_dtype and output_final_state
- *                   are not read; num_kv_heads must be 0 or H.
+ *                   are not read.
  *   q, k, v, g, g_gamma, initial_state, cu_seqlens_host
  *                   the forward's inputs (same layouts and rules).
  *   dout            [B, T, H, V] in qkv_dtype: gradient of o.
  *   dht             [N, H, K, V] float32 gradient of final_state, or NULL
  *                   (no loss on the final state).
- *   dq, dk          [B, T, H, K] float32;  dv [B, T, H, V] float32.
+ *   dq              [B, T, H, K] float32.
+ *   dk, dv          [B, T, Hkv, K] and [B, T, Hkv, V] float32: with grouped
+ *                   kv heads the gradient of a kv head's row is the sum over
+ *                   the H / Hkv query heads that read it.
  *   dg              [B, T, H] float32; required when g is given, else unused.
  *   dg_gamma        [H] float32; required when g_gamma is given, else unused.
  *   dh0             [N, H, K, V] float32 gradient of initial_state, or NULL.
  *   workspace       >= sgla_chunk_bwd_workspace_size(args, cu_seqlens_host).
  * Outputs must not overlap inputs or each other.
  * Supported: K in {16, 32, 64, 128}, V a multiple of 32, bf16 or float32
- * inputs, chunk_size 64, multi-head k and v.
+ * inputs, chunk_size 64, any Hkv dividing H.
  */
 sgla_status sgla_chunk_bwd(const sgla_chunk_args *args,
                            const void *q, const void *k, const void *v,

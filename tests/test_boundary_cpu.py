@@ -316,7 +316,6 @@ def bwd_call(G, args, b, cu=None, g=True, gg=False, dg=True, dgg=False, ws_bytes
 BWD_CASES = [
     ("K=256", dict(K=256), {}, UNSUPPORTED, "K in"),
     ("V=48", dict(V=48), {}, UNSUPPORTED, "V a multiple"),
-    ("grouped kv heads", dict(H=2, Hkv=1), {}, UNSUPPORTED, "multi-head"),
     ("fp16", dict(qkv=3), {}, DTYPE, "qkv_dtype"),
     ("both gates", {}, dict(gg=True), INVALID, "mutually exclusive"),
     ("g without dg", {}, dict(dg=False), INVALID, "dg is NULL"),
@@ -337,6 +336,18 @@ def test_chunk_bwd_rejects_without_writing(G, desc, aover, cover, status, frag):
     assert st == status, (st, msg)
     assert frag in msg, msg
     assert b.unchanged()
+
+
+def test_chunk_bwd_workspace_size_grouped(G):
+    """Grouped kv heads add the per-query-head k and v gradients (4 (K + V)
+    bytes per token and query head) after the records."""
+    a1 = mkargs(G, B=2, T=130, H=4, K=64, V=96)
+    a2 = mkargs(G, B=2, T=130, H=4, K=64, V=96, Hkv=2)
+    n1 = G.lib.sgla_chunk_bwd_workspace_size(ctypes.byref(a1), None)
+    n2 = G.lib.sgla_chunk_bwd_workspace_size(ctypes.byref(a2), None)
+    th = 2 * 130 * 4
+    up = lambda x: (x + 255) // 256 * 256
+    assert n2 == n1 + up(th * 64 * 4) + up(th * 96 * 4)
 
 
 def test_chunk_bwd_workspace_size(G):

@@ -87,6 +87,13 @@ SMALL = [
     small("f32_k32_v64", dtype="f32", K=32, V=64, T=150, initial_state=True),
     small("f32_k128_varlen", dtype="f32", B=1, T=0, K=128, V=32, fixed_lengths=(15, 85, 200),
           initial_state=True),
+    # grouped kv heads: dk, dv per kv head, summed over the query heads that read it
+    small("gqa_k64_v64", H=4, Hkv=2, K=64, V=64, T=130, initial_state=True),
+    small("gqa_k128_gamma_varlen", B=1, T=0, H=6, Hkv=2, K=128, V=128, fixed_lengths=(70, 0, 150),
+          gate="gamma", initial_state=True),
+    small("gqa_mqa_k64_v96", H=3, Hkv=1, K=64, V=96, T=100),
+    small("gqa_f32_k32", dtype="f32", H=4, Hkv=2, K=32, V=64, T=97, initial_state=True),
+    small("gqa_bf16_k16", H=4, Hkv=1, K=16, V=32, T=70),
 ]
 
 
@@ -141,8 +148,22 @@ def test_bwd_named_workload_sampled():
     assert all(v <= TOL_BF16 for v in worst.values()), worst
 
 
-def test_bwd_rejects_grouped_heads():
-    q = torch.zeros(1, 64, 4, 64, dtype=torch.bfloat16, device=DEV)
-    kv = torch.zeros(1, 64, 2, 64, dtype=torch.bfloat16, device=DEV)
-    with pytest.raises(ValueError):
-        sgla.chunk_bwd(q, kv, kv, torch.zeros(1, 64, 4, 64, dtype=torch.bfloat16, device=DEV))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_grouped_equals_repeated_heads(dtype):
+    """With grouped kv heads every query head's gradients are those of the
+    same run on k and v repeated per query head, and dk, dv of a kv head are
+    the sums over its query heads in head order: bit for bit."""
+    K = 64 if dtype == "bf16" else 32
+    inp = make_chunk_inputs(small("grp", B=1, T=0, H=4, Hkv=2, K=K, V=64, fixed_lengths=(100, 37),
+                                  dtype=dtype, initial_state=True))
+    bi = make_backward_inputs(inp, seed=5)
+    got = run_bwd(inp, bi)
+    rep = dict(inp)
+    rep["k"] = np.repeat(inp["k"], 2, axis=2)
+    rep["v"] = np.repeat(inp["v"], 2, axis=2)
+    full = run_bwd(rep, bi)
+    for name in ("dq", "dg", "dh0"):
+        assert np.array_equal(got[name], full[name]), name
+    for name, D in (("dk", K), ("dv", 64)):
+        pairs = full[name].reshape(1, -1, 2, 2, D)
+        assert np.array_equal(got[name], pairs[:, :, :, 0] + pairs[:, :, :, 1]), name
