@@ -26,6 +26,10 @@
 //               dg is the reverse cumulative sum of r over the chunk; with
 //               g_gamma its gradient is the sum of dg over every token.
 //
+// Grouped kv heads: query head h reads the k and v rows of kv head
+// h / (H / Hkv); dk and dv come out per query head and kv_group_sum_kernel
+// adds each group's query heads (the chain rule through the head repeat).
+//
 // The kernels below run every product on the fp32 matrix cores
 // (v_mfma_f32_16x16x4_f32), so inputs are used exactly and states, gradients
 // and accumulation are fp32; they serve float32 inputs and K in {16, 32}.

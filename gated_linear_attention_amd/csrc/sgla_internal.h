@@ -109,8 +109,9 @@ hipError_t launch_chunk_fwd_bf16_wide(const ChunkFwdParams& p, hipStream_t strea
 // float32 q/k/v, VALU path.  K in {16,32,64,128}, V % 32 == 0.
 hipError_t launch_chunk_fwd_f32(const ChunkFwdParams& p, hipStream_t stream);
 
-// Backward (fp32 matrix-core path): q, k, v, dout all bf16 or all float32;
-// every gradient float32.  K in {16, 32, 64, 128}, V % 32 == 0, multi-head.
+// Backward: q, k, v, dout all bf16 or all float32; every gradient float32.
+// K in {16, 32, 64, 128}, V % 32 == 0, any Hkv dividing H (k and v read by
+// kv head, dk and dv written per query head for the group sum).
 struct ChunkBwdParams {
   const void* q;
   const void* k;
