@@ -63,7 +63,7 @@ chunk_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
   __shared__ float sV[C * LDV];
   __shared__ float sA[C * LDA];
   __shared__ float sH[K * LDH];
-  __shared__ float sG[C], sEb[C], sDk[C];
+  __shared__ float sG[C], sGl[C], sEb[C], sDk[C];   // sG + sGl: the running log2 gate
 
   const UnitMap um = map_unit(blockIdx.x, V / VT, Hkv, H / Hkv, seqs.num_seqs);
   if (!um.valid) return;
@@ -169,13 +169,14 @@ chunk_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
     if (w == 0) {
       // step (1): chunk-local cumulative log2 gate (padding rows add 0)
-      float b;
-      if (g != nullptr) b = wave_cumsum_log2(pg);
+      float b, bl = 0.f;
+      if (g != nullptr) b = wave_cumsum_log2_split(pg, bl);
       else b = (float)min(tid + 1, cl) * gam2;
-      const float blast = __shfl(b, C - 1, 64);
+      const float blast = __shfl(b, C - 1, 64), bllast = __shfl(bl, C - 1, 64);
       sG[tid] = b;
+      sGl[tid] = bl;
       sEb[tid] = exp2f(b) * scale;
-      sDk[tid] = exp2f(blast - b);
+      sDk[tid] = exp2f((blast - b) + (bllast - bl));
     }
     __syncthreads();
     load_chunk(m + 1);   // in flight while this chunk computes
@@ -192,11 +193,11 @@ chunk_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
       for (int ks = 0; ks < K / 4; ++ks)
         acc = mfma4(sQ[(16 * ctile + r) * LDQ + 4 * ks + g4], sK[(16 * jtile + r) * LDQ + 4 * ks + g4], acc);
       const int j = 16 * jtile + r;
-      const float bj = sG[j];
+      const float bj = sG[j], blj = sGl[j];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = 16 * ctile + 4 * g4 + i;
-        sA[c * LDA + j] = j <= c ? acc[i] * exp2f(sG[c] - bj) * scale : 0.f;
+        sA[c * LDA + j] = j <= c ? acc[i] * exp2f((sG[c] - bj) + (sGl[c] - blj)) * scale : 0.f;
       }
     }
     // zero the upper-triangle tiles (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)

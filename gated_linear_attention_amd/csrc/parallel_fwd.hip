@@ -112,22 +112,18 @@ __global__ __launch_bounds__(NTH, (K == 256 && VMAX == 256) ? 1 : 2) void parall
       qf[qb][kk] = __builtin_bit_cast(bf16x8, x ^ qsign);
     }
   }
-  // running log2 gate R of the query rows from the start of the query tile:
-  // one 64-row scan per half, the second continuing from the first
+  // running log2 gate R of the query rows from the start of their 64-row
+  // half of the query tile (one scan per half, each from zero, so a very
+  // negative gate in the first half does not leave the second half's R as a
+  // small difference of two large floats)
   float Rh[QB];
 #pragma unroll
   for (int hh = 0; hh < QB; ++hh) Rh[hh] = wave_cumsum_log2(log_gate(p, b, h, i0 + 64 * hh + lane));
-  float R63 = 0.f;  // R at the last row of the first half
-  if constexpr (QB == 2) {
-    R63 = __shfl(Rh[0], 63, 64);
-    Rh[1] += R63;
-  }
+  const float R63 = QB == 2 ? __shfl(Rh[0], 63, 64) : 0.f;   // the first half's total
+  const bool upper = QB == 2 && wr0 >= 64;   // this wave's rows are in the second half
   float Lq[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int rr = wr0 + 16 * qb + r;  // row inside the query tile; its half is uniform per wave
-    Lq[qb] = __shfl(Rh[(wr0 + 16 * qb) / 64], rr & 63, 64);
-  }
+  for (int qb = 0; qb < QB; ++qb) Lq[qb] = __shfl(Rh[upper ? 1 : 0], (wr0 + 16 * qb + r) & 63, 64);
 
   // Key and value tiles come through buffer descriptors that start at the
   // tile: rows past T read as zeros, and so do the value columns past V (their
@@ -179,14 +175,14 @@ __global__ __launch_bounds__(NTH, (K == 256 && VMAX == 256) ? 1 : 2) void parall
 
   // The exponent of A[i][j] is R_i + D - L_j (log2 units): L_j the key's
   // running gate inside its tile and D the gate sum from the key tile's start
-  // to the query tile's start (negative for the key tile in the second half of
-  // the query tile).  Key tiles are walked from the query tile leftwards, so
-  // D grows by each tile's total (accumulated in float64); workgroups of one
-  // head start at different key tiles, which spreads their A stores over
-  // the memory channels.
+  // to the start of the row's half of the query tile.  Key tiles are walked
+  // from the query tile leftwards, so D grows by each tile's total
+  // (accumulated in float64); workgroups of one head start at different key
+  // tiles, which spreads their A stores over the memory channels.
   const int jd = QB * iq;                      // first key tile inside the query tile
   const int jlast = min(jd + QB - 1, nT - 1);  // last key tile any row of the tile reaches
-  double Dacc = 0.0;
+  double Dacc = 0.0;   // gate total of the key tiles walked so far before the query tile
+  double Tjd = 0.0;    // gate total of key tile jd (the query tile's first half)
   double Tnext = 0.0;  // gate total and running gates of the next key tile to stage (wave 0)
   float Lnext = 0.f;
 
@@ -195,7 +191,10 @@ __global__ __launch_bounds__(NTH, (K == 256 && VMAX == 256) ? 1 : 2) void parall
   auto tile = [&](int jt, auto masked) {
     const int j0 = jt * C;
     if (jt < jd) Dacc += sTot;
-    const float D = jt > jd ? -R63 : (float)(Dacc * kRcpLn2d);
+    if (jt == jd) Tjd = sTot;
+    float D;
+    if (!upper) D = jt > jd ? -R63 : (float)(Dacc * kRcpLn2d);   // tile jd + 1 is masked for these rows
+    else D = jt > jd ? 0.f : (float)((Dacc + Tjd) * kRcpLn2d);
     f32x4 s[QB][4];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)

@@ -491,3 +491,61 @@ def test_decode_state_v_first(K, V, dtype):
         torch.cuda.synchronize()
         assert err_ratio(o.cpu().numpy(), o_ref) <= TOL_F32
     assert err_ratio(state.cpu().numpy(), S_ref) <= TOL_F32
+
+
+# ---------------------------------------------------------------------------
+# degenerate gates: full forget everywhere, and resets inside sequences
+# ---------------------------------------------------------------------------
+
+def _reset_gates(inp, kind):
+    g = np.array(inp["g"], dtype=np.float32, copy=True)
+    if kind == "forget":
+        g[:] = -1e4                      # every token forgets all history
+    else:
+        g[:, ::37, :] = -1e4             # a reset every 37 tokens, normal gates between
+    return g
+
+
+@pytest.mark.parametrize("kind", ["forget", "resets"])
+@pytest.mark.parametrize("cfg", [dict(K=64, V=64), dict(K=128, V=128), dict(K=512, V=64, H=1),
+                                 dict(dtype="f32", K=32, V=64)],
+                         ids=["k64", "k128", "k512", "f32_k32"])
+def test_chunk_degenerate_gates(cfg, kind):
+    """Gates of -1e4 (a full reset) at every token or every 37th: the forward
+    stays finite and matches the oracle (which gives o_t = scale (q_t . k_t)
+    v_t for a reset at every token)."""
+    inp = make_chunk_inputs(small(f"deg_{kind}", T=150, initial_state=True, **cfg))
+    inp["g"] = _reset_gates(inp, kind)
+    o, ht = run_chunk(inp)
+    check_full(inp, o, ht)
+
+
+@pytest.mark.parametrize("kind", ["forget", "resets"])
+def test_parallel_and_decode_degenerate_gates(kind):
+    """The parallel form and the decode step under the same reset gates."""
+    inp = make_chunk_inputs(small(f"degp_{kind}", T=150, K=128, V=64, initial_state=False))
+    inp["g"] = _reset_gates(inp, kind)
+    d = device_inputs(inp)
+    o, A = sgla.parallel_fwd(d["q"], d["k"], d["v"], g=d["g"], scale=inp["scale"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, A_ref = oracle.parallel(inp["q"], inp["k"], inp["v"], g=inp["g"], scale=inp["scale"])
+    assert np.all(np.isfinite(o.cpu().numpy())) and np.all(np.isfinite(A.cpu().numpy()))
+    assert err_ratio(o.cpu().numpy(), o_ref) <= TOL_BF16
+    assert err_ratio(A.cpu().numpy(), A_ref) <= TOL_BF16
+    # decode: the first 8 tokens of every row as 8 steps from a random state
+    N, H, K, V = inp["B"], inp["H"], inp["K"], inp["V"]   # one decode step per batch row
+    rng = np.random.default_rng(3)
+    S0 = (rng.standard_normal((N, H, K, V)) * 0.1).astype(np.float32)
+    S = to_dev(S0, torch.float32)
+    Sref = S0.astype(np.float64)
+    for t in range(8):
+        qt, kt, vt = inp["q"][:, t], inp["k"][:, t], inp["v"][:, t]
+        gt = inp["g"][:, t]
+        ot = sgla.recurrent_step(to_dev(qt, torch.bfloat16), to_dev(kt, torch.bfloat16),
+                                 to_dev(vt, torch.bfloat16), to_dev(gt, torch.float32), S,
+                                 scale=inp["scale"])
+        o_ref_t, Sref = oracle.step(qt, kt, vt, gt, Sref, scale=inp["scale"])
+        torch.cuda.synchronize()
+        assert np.all(np.isfinite(ot.cpu().numpy()))
+        assert err_ratio(ot.cpu().numpy(), o_ref_t) <= TOL_BF16
+    assert err_ratio(S.cpu().numpy(), Sref) <= TOL_BF16
