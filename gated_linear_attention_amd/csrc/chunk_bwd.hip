@@ -113,10 +113,14 @@ __device__ __forceinline__ SeqInfo seq_info(const SeqLayout& seqs, int rank, int
 
 // Chunk-local cumulative log2 gate of the chunk starting at token t0 with cl
 // tokens, for lane = token offset; padding tokens add nothing.  Wave-wide.
+// lo receives the rounding remainder of a per-token gate's running sum (0
+// for the per-head decay), so differences of two running gates stay exact
+// to fp32 after a very negative gate.
 __device__ __forceinline__ float chunk_gate(const float* g, const float* g_gamma, int H, int hd,
-                                            int64_t t0, int cl) {
+                                            int64_t t0, int cl, float& lo) {
   const int lane = threadIdx.x & 63;
-  if (g != nullptr) return wave_cumsum_log2(lane < cl ? g[(t0 + lane) * H + hd] : 0.f);
+  lo = 0.f;
+  if (g != nullptr) return wave_cumsum_log2_split(lane < cl ? g[(t0 + lane) * H + hd] : 0.f, lo);
   if (g_gamma != nullptr) return (float)min(lane + 1, cl) * (g_gamma[hd] * kRcpLn2f);
   return 0.f;
 }
@@ -210,12 +214,12 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     xt.store(sX, LDX);
     yt.store(sY, LDT);
     if (w == 0) {
-      float b;
-      if (g != nullptr) b = wave_cumsum_log2(gx);
+      float b, bl = 0.f;
+      if (g != nullptr) b = wave_cumsum_log2_split(gx, bl);
       else if (g_gamma != nullptr) b = (float)min(lane + 1, cl) * (g_gamma[hd] * kRcpLn2f);
       else b = 0.f;
-      const float blast = __shfl(b, C - 1, 64);
-      sW[lane] = rev ? exp2f(b) * scale : exp2f(blast - b);
+      const float blast = __shfl(b, C - 1, 64), bllast = __shfl(bl, C - 1, 64);
+      sW[lane] = rev ? exp2f(b) * scale : exp2f((blast - b) + (bllast - bl));
       if (lane == 0) sDall = exp2f(blast);
     }
     __syncthreads();
@@ -282,7 +286,7 @@ chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   __shared__ float sdO[C * LDT];
   __shared__ float sH[K * LDT];
   __shared__ float sdH[K * LDT];
-  __shared__ float sb[C], ssc[C], sdv[C];
+  __shared__ float sb[C], sbl[C], ssc[C], sdv[C];   // sb + sbl: the running log2 gate
   __shared__ float sR[2][C], sKs[2][C];
   __shared__ float sFrob[8];
 
@@ -320,11 +324,13 @@ chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     kt.store(sK, LDQ);
   }
   if (w == 0) {
-    const float b = chunk_gate(g, g_gamma, H, hd, t0, cl);
-    const float blast = __shfl(b, C - 1, 64);
+    float bl;
+    const float b = chunk_gate(g, g_gamma, H, hd, t0, cl, bl);
+    const float blast = __shfl(b, C - 1, 64), bllast = __shfl(bl, C - 1, 64);
     sb[lane] = b;
+    sbl[lane] = bl;
     ssc[lane] = exp2f(b) * scale;
-    sdv[lane] = exp2f(blast - b);
+    sdv[lane] = exp2f((blast - b) + (bllast - bl));
   }
   // slice tiles, loaded one slice ahead of their use
   RowTile<VT, NTG, TIn> vtile, otile;
@@ -354,7 +360,7 @@ chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = 16 * rw + 4 * g4 + i;
-        sA[c * LDA + j] = j <= c ? acc[t][i] * exp2f(sb[c] - sb[j]) * scale : 0.f;
+        sA[c * LDA + j] = j <= c ? acc[t][i] * exp2f((sb[c] - sb[j]) + (sbl[c] - sbl[j])) * scale : 0.f;
       }
     }
   }
@@ -420,7 +426,7 @@ chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = 16 * rw + 4 * g4 + i;
-      sA[c * LDA + j] = j <= c ? dAacc[t][i] * exp2f(sb[c] - sb[j]) * scale : 0.f;
+      sA[c * LDA + j] = j <= c ? dAacc[t][i] * exp2f((sb[c] - sb[j]) + (sbl[c] - sbl[j])) * scale : 0.f;
     }
   }
   // Frobenius product <dH, h> of the whole chunk record

@@ -167,3 +167,19 @@ def test_bwd_grouped_equals_repeated_heads(dtype):
     for name, D in (("dk", K), ("dv", 64)):
         pairs = full[name].reshape(1, -1, 2, 2, D)
         assert np.array_equal(got[name], pairs[:, :, :, 0] + pairs[:, :, :, 1]), name
+
+
+@pytest.mark.parametrize("kind", ["forget", "resets"])
+@pytest.mark.parametrize("dtype,K", [("bf16", 64), ("bf16", 128), ("f32", 32)], ids=["k64", "k128", "f32_k32"])
+def test_bwd_degenerate_gates(dtype, K, kind):
+    """Gates of -1e4 (a full reset) at every token or every 37th token: every
+    gradient stays finite and within the bar."""
+    inp = make_chunk_inputs(small(f"bdeg_{kind}", dtype=dtype, K=K, V=64, T=150, initial_state=True))
+    g = np.array(inp["g"], dtype=np.float32, copy=True)
+    if kind == "forget":
+        g[:] = -1e4
+    else:
+        g[:, ::37, :] = -1e4
+    inp["g"] = g
+    bi = make_backward_inputs(inp, seed=9)
+    compare(run_bwd(inp, bi), oracle_bwd(inp, bi), TOL_BF16 if dtype == "bf16" else TOL_F32, f"deg {kind}")
