@@ -132,11 +132,14 @@ norm_chunk_sum_kernel(const TIn* __restrict__ k, const float* __restrict__ g,
   if (tid < C) {
     const float lg = token_gate(g, g_gamma, cr.t0, tid, cr.len, H, hd);
     // chunk-local cumulative log2 gate (closed form for a per-head decay)
-    const float b = g != nullptr         ? wave_cumsum_log2(lg)
+    // (per-token gates: carried as hi + lo, so 2^(b_last - b) stays exact to
+    // fp32 after a very negative gate inside the chunk)
+    float bl = 0.f;
+    const float b = g != nullptr         ? wave_cumsum_log2_split(lg, bl)
                     : g_gamma != nullptr ? (float)min(tid + 1, cr.len) * (g_gamma[hd] * (float)kRcpLn2d)
                                          : 0.f;
-    const float blast = __shfl(b, C - 1, 64);
-    sW[tid] = exp2f(blast - b);
+    const float blast = __shfl(b, C - 1, 64), bllast = __shfl(bl, C - 1, 64);
+    sW[tid] = exp2f((blast - b) + (bllast - bl));
     if (tid == C - 1) dlog[(int64_t)chunk * H + hd] = blast;
   }
   __syncthreads();

