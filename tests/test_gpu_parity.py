@@ -549,3 +549,36 @@ def test_parallel_and_decode_degenerate_gates(kind):
         assert np.all(np.isfinite(ot.cpu().numpy()))
         assert err_ratio(ot.cpu().numpy(), o_ref_t) <= TOL_BF16
     assert err_ratio(S.cpu().numpy(), Sref) <= TOL_BF16
+
+
+# ---------------------------------------------------------------------------
+# odd shapes: many heads, many short rows, many tiny packed sequences
+# ---------------------------------------------------------------------------
+
+ODD_SHAPES = [
+    small("h64_k64", B=1, T=70, H=64, K=64, V=64),
+    small("b48_t3", B=48, T=3, H=2, K=128, V=64, initial_state=True),
+    small("n200_tiny_varlen", B=1, T=0, H=2, K=64, V=64, initial_state=True,
+          fixed_lengths=tuple(int(x) for x in np.random.default_rng(0).integers(0, 6, size=200))),
+    small("f32_b40_t2", dtype="f32", B=40, T=2, H=3, K=32, V=32, initial_state=True),
+    small("k512_b6_t5", B=6, T=5, H=1, K=512, V=64, initial_state=True),
+]
+
+
+@pytest.mark.parametrize("w", ODD_SHAPES, ids=lambda w: w.name)
+def test_chunk_odd_shapes(w):
+    inp = make_chunk_inputs(w)
+    o, ht = run_chunk(inp)
+    check_full(inp, o, ht)
+
+
+@pytest.mark.parametrize("B,T,H,K,V", [(1, 70, 64, 64, 64), (48, 3, 2, 128, 64), (5, 1, 3, 64, 16)],
+                         ids=["h64", "b48_t3", "b5_t1"])
+def test_parallel_odd_shapes(B, T, H, K, V):
+    inp = make_chunk_inputs(small("par_odd", B=B, T=T, H=H, K=K, V=V))
+    d = device_inputs(inp)
+    o, A = sgla.parallel_fwd(d["q"], d["k"], d["v"], g=d["g"], scale=inp["scale"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, A_ref = oracle.parallel(inp["q"], inp["k"], inp["v"], g=inp["g"], scale=inp["scale"])
+    assert err_ratio(o.cpu().numpy(), o_ref) <= TOL_BF16
+    assert err_ratio(A.cpu().numpy(), A_ref) <= TOL_BF16
