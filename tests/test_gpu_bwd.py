@@ -183,3 +183,16 @@ def test_bwd_degenerate_gates(dtype, K, kind):
     inp["g"] = g
     bi = make_backward_inputs(inp, seed=9)
     compare(run_bwd(inp, bi), oracle_bwd(inp, bi), TOL_BF16 if dtype == "bf16" else TOL_F32, f"deg {kind}")
+
+
+@pytest.mark.parametrize("w", [
+    small("b_h32_k64", B=1, T=70, H=32, K=64, V=64),
+    small("b_b24_t3", B=24, T=3, H=2, K=128, V=64, initial_state=True),
+    small("b_n120_tiny_varlen", B=1, T=0, H=2, K=64, V=32, initial_state=True,
+          fixed_lengths=tuple(int(x) for x in np.random.default_rng(1).integers(0, 6, size=120))),
+    small("b_f32_b20_t2", dtype="f32", B=20, T=2, H=2, K=32, V=32, initial_state=True),
+], ids=lambda w: w.name)
+def test_bwd_odd_shapes(w):
+    inp = make_chunk_inputs(w)
+    bi = make_backward_inputs(inp, seed=12)
+    compare(run_bwd(inp, bi), oracle_bwd(inp, bi), TOL_BF16 if inp["dtype"] == "bf16" else TOL_F32, w.name)

@@ -114,3 +114,13 @@ def test_chunk_normalizer_degenerate_gates(dtype, K, kind):
     e1, e2 = err_ratio(den.cpu().numpy(), den_ref), err_ratio(zt.cpu().numpy(), z_ref)
     print(f"[norm deg {kind} {dtype}] den {e1:.2e} z {e2:.2e}", flush=True)
     assert e1 <= TOL_F32 and e2 <= TOL_F32
+
+
+@pytest.mark.parametrize("w", [
+    small("n_h48_k64", B=1, T=70, H=48, K=64),
+    small("n_b40_t3", B=40, T=3, H=2, K=128, initial_state=True),
+    small("n_n150_tiny_varlen", B=1, T=0, H=2, K=64, initial_state=True,
+          fixed_lengths=tuple(int(x) for x in np.random.default_rng(2).integers(0, 6, size=150))),
+], ids=lambda w: w.name)
+def test_chunk_normalizer_odd_shapes(w):
+    test_chunk_normalizer(w)
