@@ -148,3 +148,14 @@ def test_gla_degenerate_gates(dtype, K, V, kind, request):
     eo, eh = err_ratio(o, o_ref), err_ratio(ht, h_ref)
     print(f"[gla deg {kind} {dtype} K={K}] o {eo:.2e} final {eh:.2e}", flush=True)
     assert np.all(np.isfinite(o)) and eo <= tol and eh <= tol
+
+
+@pytest.mark.parametrize("w", [
+    small("g_h32_k64", B=1, T=70, H=32, K=64, V=64),
+    small("g_b24_t3", B=24, T=3, H=2, K=128, V=128, initial_state=True),
+    small("g_n120_tiny_varlen", B=1, T=0, H=2, K=64, V=64, initial_state=True,
+          fixed_lengths=tuple(int(x) for x in np.random.default_rng(3).integers(0, 6, size=120))),
+    small("g_f32_b20_t2", dtype="f32", B=20, T=2, H=2, K=32, V=32, initial_state=True),
+], ids=lambda w: w.name)
+def test_gla_odd_shapes(w):
+    test_gla_small(w, 1.0)

@@ -582,3 +582,27 @@ def test_parallel_odd_shapes(B, T, H, K, V):
     o_ref, A_ref = oracle.parallel(inp["q"], inp["k"], inp["v"], g=inp["g"], scale=inp["scale"])
     assert err_ratio(o.cpu().numpy(), o_ref) <= TOL_BF16
     assert err_ratio(A.cpu().numpy(), A_ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("N,H,Hkv,K,V,vf", [(1, 1, 1, 1, 32, 0), (3000, 1, 1, 16, 32, 0), (7, 5, 5, 96, 64, 0),
+                                            (2, 3, 1, 512, 512, 1), (9, 2, 2, 32, 1024, 1)],
+                         ids=["k1", "n3000", "k96", "vf_k512_mqa", "vf_v1024"])
+def test_decode_odd_shapes(N, H, Hkv, K, V, vf):
+    """Decode at the edges of its support: K = 1, thousands of tiny units, a
+    non-power-of-two K, and the [V, K] state at its largest K and V."""
+    rng = np.random.default_rng(N + K)
+    q = rng.standard_normal((N, H, K)).astype(np.float32)
+    k = rng.standard_normal((N, Hkv, K)).astype(np.float32)
+    v = rng.standard_normal((N, Hkv, V)).astype(np.float32)
+    g = np.log(rng.uniform(0.5, 1.0, (N, H))).astype(np.float32)
+    S0 = (rng.standard_normal((N, H, K, V)) * 0.1).astype(np.float32)
+    S = to_dev(np.swapaxes(S0, -1, -2).copy() if vf else S0, torch.float32)
+    o = sgla.recurrent_step(to_dev(q, torch.float32), to_dev(k, torch.float32), to_dev(v, torch.float32),
+                            to_dev(g, torch.float32), S, scale=0.3, state_v_first=bool(vf))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.step(q, k, v, g, S0, scale=0.3)
+    S_got = S.cpu().numpy()
+    if vf:
+        S_got = np.swapaxes(S_got, -1, -2)
+    assert err_ratio(o.cpu().numpy(), o_ref) <= TOL_F32
+    assert err_ratio(S_got, S_ref) <= TOL_F32
