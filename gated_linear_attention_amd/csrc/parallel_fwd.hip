@@ -164,7 +164,7 @@ __global__ __launch_bounds__(NTH, (K == 256 && VMAX == 256) ? 1 : 2) void parall
   const int tlim = (T & 3) == 0 ? T : 0;
   const int rows = min(QR, T - i0);
   const __amdgpu_buffer_rsrc_t ra =
-      make_rsrc(p.attn + (((int64_t)b * H + h) * T + i0) * (int64_t)T,
+      make_rsrc(p.attn != nullptr ? p.attn + (((int64_t)b * H + h) * T + i0) * (int64_t)T : nullptr,
                 p.attn != nullptr ? (uint32_t)rows * (uint32_t)T * 4u : 0u);
 
   f32x4 O[QB][NVT];
