@@ -71,11 +71,14 @@ __device__ __forceinline__ TOut out_cast(float x) { return (TOut)x; }
 // Chunk-local cumulative log2 gate of every key, in place over the log gates
 // staged in sB (row stride LD; padding rows hold 0, so they add nothing).
 // Thread (key a, part p) of NTH sums tokens [p TL, +TL) in double; the
-// parts' totals are exchanged through sTot (NTH floats), then each part
-// writes its running sums with the earlier parts' total added.  Ends with
-// the workgroup's barrier.
-template <int K, int NTH, int LD>
-__device__ __forceinline__ void key_cumsum_log2(float* sB, float* sTot) {
+// parts' totals are exchanged through sTot (NTH doubles), then each part
+// writes its running sums with the earlier parts' total added.  With LO the
+// rounding remainder of each running sum goes to sBl (hi + lo carries the
+// running gate to ~2^-48 relative, so the difference of two running gates
+// stays exact to float32 after a very negative gate has pushed both far from
+// zero).  Ends with the workgroup's barrier.
+template <int K, int NTH, int LD, bool LO>
+__device__ __forceinline__ void key_cumsum_log2(float* sB, float* sBl, double* sTot) {
   constexpr int NPART = NTH / K;      // token parts of the per-key scan
   constexpr int TL = C / NPART;       // tokens per part
   static_assert(NPART * K == NTH && TL * NPART == C, "scan split");
@@ -88,15 +91,59 @@ __device__ __forceinline__ void key_cumsum_log2(float* sB, float* sTot) {
     gv[u] = sB[(p * TL + u) * LD + a];
     tot += (double)gv[u];
   }
-  sTot[p * K + a] = (float)tot;
+  sTot[p * K + a] = tot;
   __syncthreads();
   double b = 0.0;
-  for (int pp = 0; pp < p; ++pp) b += (double)sTot[pp * K + a];
+  for (int pp = 0; pp < p; ++pp) b += sTot[pp * K + a];
 #pragma unroll
   for (int u = 0; u < TL; ++u) {
     b += (double)gv[u];
-    sB[(p * TL + u) * LD + a] = (float)(b * kRcpLn2d);
+    const double t = b * kRcpLn2d;
+    const float hi = (float)t;
+    sB[(p * TL + u) * LD + a] = hi;
+    if constexpr (LO) sBl[(p * TL + u) * LD + a] = (float)(t - (double)hi);
   }
+  __syncthreads();
+}
+
+// The chunk chain's per-key scan fused with its operand scaling, over the
+// log gates staged in sG: q_c (.) 2^B_c and k_c (.) 2^(B_last - B_c) in place
+// in sQ and sK, and 2^B_last per key into sDl.  The suffix B_last - B_c is
+// formed in double before its one rounding, so the decay of k stays exact to
+// float32 whatever the gates.  Thread (key a, part p) as in key_cumsum_log2.
+// Ends with the workgroup's barrier.
+template <int K, int NTH, int LD>
+__device__ __forceinline__ void key_scan_scale(const float* sG, float* sQ, float* sK, float* sDl,
+                                               double* sTot) {
+  constexpr int NPART = NTH / K;
+  constexpr int TL = C / NPART;
+  static_assert(NPART * K == NTH && TL * NPART == C, "scan split");
+  const int tid = threadIdx.x;
+  const int a = tid % K, p = tid / K;
+  float gv[TL];
+  double part = 0.0;
+#pragma unroll
+  for (int u = 0; u < TL; ++u) {
+    gv[u] = sG[(p * TL + u) * LD + a];
+    part += (double)gv[u];
+  }
+  sTot[p * K + a] = part;
+  __syncthreads();
+  double b = 0.0, total = 0.0;
+#pragma unroll
+  for (int pp = 0; pp < NPART; ++pp) {
+    const double x = sTot[pp * K + a];
+    if (pp < p) b += x;
+    total += x;
+  }
+#pragma unroll
+  for (int u = 0; u < TL; ++u) {
+    b += (double)gv[u];
+    const int c = p * TL + u;
+    sQ[c * LD + a] *= exp2_hw((float)(b * kRcpLn2d));
+    sK[c * LD + a] *= exp2_hw((float)((total - b) * kRcpLn2d));
+  }
+  if (p == NPART - 1) sDl[a] = exp2_hw((float)(total * kRcpLn2d));
   __syncthreads();
 }
 
@@ -139,8 +186,13 @@ gla_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
   // workgroups fit a CU); the gates are float
   __shared__ __attribute__((aligned(16))) TIn sQ[C * LDX];
   __shared__ __attribute__((aligned(16))) TIn sK[C * LDX];
+  // float32 inputs carry B as hi + lo (sB + sBl) so decays stay float32-exact
+  // after a very negative gate; bf16 inputs keep one float (their error bar
+  // is met with it, and the smaller footprint keeps two workgroups per CU)
+  constexpr bool LO = sizeof(TIn) == 4;
   __shared__ __attribute__((aligned(16))) float sB[C * LDQ];   // gates, then B
-  __shared__ float sTot[NTP];
+  __shared__ __attribute__((aligned(16))) float sBl[LO ? C * LDQ : 1];
+  __shared__ double sTot[NTP];
 
   const UnitMap um = map_unit(blockIdx.x, 1, Hkv, H / Hkv, seqs.num_chunks);
   if (!um.valid) return;
@@ -190,9 +242,15 @@ gla_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
     gt.store(sB, LDQ);
   }
   __syncthreads();
-  key_cumsum_log2<K, NTP, LDQ>(sB, sTot);
+  key_cumsum_log2<K, NTP, LDQ, LO>(sB, sBl, sTot);
   auto fq = [&](int c, int a) { return (float)sQ[c * LDX + a]; };
   auto fk = [&](int c, int a) { return (float)sK[c * LDX + a]; };
+  // log2 decay B[c][a] - B[j][a] (hi + lo when carried)
+  auto dB = [&](int c, int j, int a) {
+    const float d = sB[c * LDQ + a] - sB[j * LDQ + a];
+    if constexpr (LO) return d + (sBl[c * LDQ + a] - sBl[j * LDQ + a]);
+    return d;
+  };
 
   const int64_t rec = (int64_t)chunk * H + hd;
   float* ab = HL ? nullptr : amat + rec * (C * C);
@@ -256,10 +314,10 @@ gla_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
 #pragma unroll 4
     for (int ks = 0; ks < K / 4; ++ks) {
       const int a = 4 * ks + g4;
-      const float br0 = sB[16 * I0 * LDQ + a], br1 = sB[16 * I1 * LDQ + a];
+      const int r0 = 16 * I0, r1 = 16 * I1;
       const int c0 = 16 * I0 + r, j0 = 16 * J0 + r, c1 = 16 * I1 + r, j1 = 16 * J1 + r;
-      acc0 = mfma4(fq(c0, a) * exp2_hw(sB[c0 * LDQ + a] - br0), fk(j0, a) * exp2_hw(br0 - sB[j0 * LDQ + a]), acc0);
-      acc1 = mfma4(fq(c1, a) * exp2_hw(sB[c1 * LDQ + a] - br1), fk(j1, a) * exp2_hw(br1 - sB[j1 * LDQ + a]), acc1);
+      acc0 = mfma4(fq(c0, a) * exp2_hw(dB(c0, r0, a)), fk(j0, a) * exp2_hw(dB(r0, j0, a)), acc0);
+      acc1 = mfma4(fq(c1, a) * exp2_hw(dB(c1, r1, a)), fk(j1, a) * exp2_hw(dB(r1, j1, a)), acc1);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -282,9 +340,8 @@ gla_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
 #pragma unroll 4
       for (int ks = 0; ks < K / 4; ++ks) {
         const int a = 4 * ks + g4;
-        const float br = sB[rr * LDQ + a];
         const int ci = 16 * I + r;
-        acc = mfma4(fq(ci, a) * exp2_hw(sB[ci * LDQ + a] - br), fk(ci, a) * exp2_hw(br - sB[ci * LDQ + a]), acc);
+        acc = mfma4(fq(ci, a) * exp2_hw(dB(ci, rr, a)), fk(ci, a) * exp2_hw(dB(rr, ci, a)), acc);
       }
       const int j = 16 * I + r;
 #pragma unroll
@@ -299,8 +356,7 @@ gla_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
         const int c = 16 * I + (e >> 4), j = 16 * I + (e & 15);
         float x = 0.f;
         if (j <= c) {
-          for (int a = 0; a < K; ++a)
-            x = fmaf(fq(c, a) * fk(j, a), exp2_hw(sB[c * LDQ + a] - sB[j * LDQ + a]), x);
+          for (int a = 0; a < K; ++a) x = fmaf(fq(c, a) * fk(j, a), exp2_hw(dB(c, j, a)), x);
         }
         put_a(c, j, x * scale);
       }
@@ -329,11 +385,12 @@ gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   constexpr int SPW = (NST + 3) / 4;  // per wave
   __shared__ __attribute__((aligned(16))) float sQ[C * LDQ];
   __shared__ __attribute__((aligned(16))) float sK[C * LDQ];
-  __shared__ __attribute__((aligned(16))) float sB[C * LDQ];   // gates, then B
+  __shared__ __attribute__((aligned(16))) float sB[C * LDQ];   // log gates
   __shared__ __attribute__((aligned(16))) float sV[C * LDV];
   __shared__ __attribute__((aligned(16))) float sA[C * LDA];
   __shared__ float sH[K * LDH];
-  __shared__ float sTot[NT];
+  __shared__ float sDl[K];                                      // 2^B_last per key
+  __shared__ double sTot[NT];
 
   const UnitMap um = map_unit(blockIdx.x, V / VT, Hkv, H / Hkv, seqs.num_seqs);
   if (!um.valid) return;
@@ -429,20 +486,12 @@ gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     if (m > 0) flush_out();
     __syncthreads();
 
-    // ---- B: chunk-local cumulative log2 gate of every key ------------------
-    key_cumsum_log2<K, NT, LDQ>(sB, sTot);
+    // ---- B, the chunk-local cumulative log2 gate of every key, applied in
+    //      place: Q (.) 2^B and K (.) 2^(B_last - B) ------------------------
+    key_scan_scale<K, NT, LDQ>(sB, sQ, sK, sDl, sTot);
     // the next chunk's rows go into registers now: they are held through the
     // rest of this chunk
     if (m + 1 < nchunks) load_chunk(m + 1);
-
-    // ---- Q (.) 2^B and K (.) 2^(B_last - B), in place ------------------------
-    for (int i = tid; i < C * K; i += NT) {
-      const int c = i / K, a = i % K;
-      const float b = sB[c * LDQ + a];
-      sQ[c * LDQ + a] *= exp2_hw(b);
-      sK[c * LDQ + a] *= exp2_hw(sB[(C - 1) * LDQ + a] - b);
-    }
-    __syncthreads();
 
     // ---- output tiles (ct, cv) and (ct + 2, cv), ct = w / 2, cv = w % 2: the
     //      two tiles share their B operands and run as interleaved chains ------
@@ -481,7 +530,7 @@ gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
         if (NST % 4 != 0 && st >= NST) continue;
         const int kt = st >> 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hs[s][i] *= exp2_hw(sB[(C - 1) * LDQ + 16 * kt + 4 * g4 + i]);
+        for (int i = 0; i < 4; ++i) hs[s][i] *= sDl[16 * kt + 4 * g4 + i];
       }
 #pragma unroll 4
       for (int cs = 0; cs < C / 4; ++cs) {
@@ -495,7 +544,7 @@ gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
         }
       }
     }
-    __syncthreads();   // every read of sQ, sK, sB, sV, sA and the old sH is done
+    __syncthreads();   // every read of sQ, sK, sV, sA, sDl and the old sH is done
     publish_state();
   }
   if (nchunks > 0) flush_out();

@@ -9,10 +9,6 @@
 
 #include <cstdint>
 
-#ifndef SGLA_TR_READ
-#define SGLA_TR_READ 1
-#endif
-
 namespace sgla {
 namespace mf {
 
@@ -52,15 +48,8 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
 // same for the 16 lanes of a group; addresses must be 8-byte aligned.
 __device__ __forceinline__ bf16x4 tr_read(const bf16* base, int ld, int row0, int col0) {
   const int lane = threadIdx.x & 15;
-#if SGLA_TR_READ
   const bf16* p = base + (row0 + (lane >> 2)) * ld + col0 + 4 * (lane & 3);
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
-#else
-  bf16x4 out;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) out[e] = base[(row0 + e) * ld + col0 + lane];
-  return out;
-#endif
 }
 
 // Transposed LDS read with the key order used by the wide-key state layout:

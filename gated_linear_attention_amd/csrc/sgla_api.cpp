@@ -51,7 +51,6 @@ struct Plan {
   int32_t num_chunks = 0;
   bool packed = false;
   std::vector<sgla::SeqEntry> seqs;      // packed only, longest first
-  std::vector<sgla::ChunkEntry> chunks;  // packed only
   int32_t chunk_size = 0;                // requested chunk size (power of two <= 64)
   bool prep = false;                     // wide-key bf16 path: per-chunk preparation buffers
   size_t seq_off = 0, chunk_off = 0, gate_off = 0, amat_off = 0, kt_off = 0, q_off = 0, total_bytes = 0;
@@ -66,7 +65,7 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
   if (P->Hkv < 0 || a->H % P->Hkv != 0)
     return fail(SGLA_ERR_SHAPE, "num_kv_heads must divide H (got num_kv_heads=%d, H=%d)", a->num_kv_heads, a->H);
   const int32_t cs = a->chunk_size == 0 ? sgla::kChunk : a->chunk_size;
-  if (!is_pow2(cs)) return fail(SGLA_ERR_SHAPE, "chunk_size must be a power of two (got %d)", cs);
+  if (!is_pow2(cs)) return fail(SGLA_ERR_UNSUPPORTED, "chunk_size must be a power of two (got %d)", cs);
   if (cs > sgla::kChunk)
     return fail(SGLA_ERR_UNSUPPORTED, "chunk_size %d is not implemented (at most 64)", cs);
   P->chunk_size = cs;
@@ -119,10 +118,9 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
     // longest sequences first: they bound the critical path
     std::stable_sort(P->seqs.begin(), P->seqs.end(),
                      [](const sgla::SeqEntry& x, const sgla::SeqEntry& y) { return x.len > y.len; });
-    for (int32_t n = 0; n < P->N; ++n)
-      for (int64_t t = cu[n]; t < cu[n + 1]; t += sgla::kChunk)
-        P->chunks.push_back({(int32_t)t, (int32_t)std::min<int64_t>(sgla::kChunk, cu[n + 1] - t)});
-    P->num_chunks = (int32_t)P->chunks.size();
+    int64_t nch = 0;
+    for (int32_t n = 0; n < P->N; ++n) nch += (cu[n + 1] - cu[n] + sgla::kChunk - 1) / sgla::kChunk;
+    P->num_chunks = (int32_t)nch;
   } else {
     P->N = a->B;
     P->num_chunks = a->T > 0 ? a->B * ((a->T + sgla::kChunk - 1) / sgla::kChunk) : 0;
@@ -130,10 +128,10 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
   // workgroup counts of the launches must fit a 32-bit grid
   if ((int64_t)P->num_chunks * a->H > INT32_MAX)
     return fail(SGLA_ERR_UNSUPPORTED, "%d chunks x %d heads exceeds 2^31-1 work units", P->num_chunks, a->H);
-  P->prep = need_kv_support && a->qkv_dtype == SGLA_BF16 && a->K >= 256;
+  P->prep = need_kv_support && a->qkv_dtype == SGLA_BF16 && a->K >= 256 && cs == sgla::kChunk;
   P->seq_off = 0;
   P->chunk_off = P->seq_off + align_up(P->seqs.size() * sizeof(sgla::SeqEntry), 256);
-  P->gate_off = P->chunk_off + align_up(P->chunks.size() * sizeof(sgla::ChunkEntry), 256);
+  P->gate_off = P->chunk_off + align_up((P->packed ? (size_t)P->num_chunks : 0) * sizeof(sgla::ChunkEntry), 256);
   P->amat_off = P->gate_off;
   if (P->prep) {
     const size_t tasks = (size_t)P->num_chunks * a->H;        // (chunk, query head)
@@ -197,18 +195,24 @@ sgla_status hip_fail(hipError_t e, const char* what) {
   return fail(SGLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Copy the packed-sequence tables into the workspace (stream-ordered; the
-// host source is staged by the runtime before the call returns).
+// Write the packed-sequence tables into the workspace, stream-ordered: the
+// sequence entries travel by value in the arguments of table_put launches
+// (kTablePut per launch), which also expand each sequence into its chunk
+// rows.  No host buffer outlives the call, nothing is copied from pageable
+// memory and the host never waits.
 sgla_status upload_tables(const Plan& P, char* ws, hipStream_t stream) {
   if (!P.packed) return SGLA_OK;
-  // both tables in one copy: [seq table | pad | chunk table]
-  const size_t bytes = P.chunk_off + P.chunks.size() * sizeof(sgla::ChunkEntry);
-  std::vector<char> host(bytes, 0);
-  std::memcpy(host.data() + P.seq_off, P.seqs.data(), P.seqs.size() * sizeof(sgla::SeqEntry));
-  if (!P.chunks.empty())
-    std::memcpy(host.data() + P.chunk_off, P.chunks.data(), P.chunks.size() * sizeof(sgla::ChunkEntry));
-  hipError_t e = hipMemcpyAsync(ws, host.data(), bytes, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return hip_fail(e, "copying the sequence and chunk tables");
+  auto* seq_table = reinterpret_cast<sgla::SeqEntry*>(ws + P.seq_off);
+  auto* chunk_table = P.num_chunks == 0 ? nullptr : reinterpret_cast<sgla::ChunkEntry*>(ws + P.chunk_off);
+  sgla::TablePut put;
+  for (size_t first = 0; first < P.seqs.size(); first += sgla::kTablePut) {
+    const size_t n = std::min<size_t>(sgla::kTablePut, P.seqs.size() - first);
+    put.first = (int32_t)first;
+    put.count = (int32_t)n;
+    std::memcpy(put.e, P.seqs.data() + first, n * sizeof(sgla::SeqEntry));
+    const hipError_t e = sgla::launch_table_put(put, seq_table, chunk_table, stream);
+    if (e != hipSuccess) return hip_fail(e, "writing the sequence and chunk tables");
+  }
   return SGLA_OK;
 }
 
@@ -251,8 +255,8 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
   Plan P;
   sgla_status st = plan_shape(args, cu_seqlens_host, true, &P);
   if (st != SGLA_OK) return st;
-  st = need_chunk64(P);
-  if (st != SGLA_OK) return st;
+  if (P.chunk_size != sgla::kChunk && P.chunk_size != 32 && P.chunk_size != 16)
+    return fail(SGLA_ERR_UNSUPPORTED, "chunk_size %d is not implemented (16, 32 or 64)", P.chunk_size);
   const sgla_chunk_args& a = *args;
   if (g != nullptr && g_gamma != nullptr)
     return fail(SGLA_ERR_INVALID_ARG, "g and g_gamma are mutually exclusive; pass at most one");
@@ -307,7 +311,9 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
   p.qfr = P.prep ? ws + P.q_off : nullptr;
   if (p.ht == nullptr && !any_tokens) return ok();
   hipError_t e;
-  if (P.prep) {
+  if (P.chunk_size != sgla::kChunk) {
+    e = sgla::launch_chunk_fwd_small(p, P.chunk_size, a.qkv_dtype == SGLA_BF16, stream);
+  } else if (P.prep) {
     sgla::ChunkPrepParams pp;
     pp.q = q;
     pp.k = k;

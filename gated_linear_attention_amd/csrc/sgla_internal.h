@@ -33,6 +33,19 @@ struct ChunkEntry {
   int32_t len;   // tokens in the chunk (1..kChunk)
 };
 
+// Up to kTablePut sequence-table entries carried by value in the arguments
+// of one table_put launch (2 KiB of payload); the launch writes them at rows
+// [first, first + count) of the sequence table and expands each into its
+// rows of the chunk table.
+constexpr int kTablePut = 126;
+struct TablePut {
+  int32_t first;
+  int32_t count;
+  SeqEntry e[kTablePut];
+};
+hipError_t launch_table_put(const TablePut& put, SeqEntry* seq_table, ChunkEntry* chunk_table,
+                            hipStream_t stream);
+
 // Layout of a caller's [N, H, K, V] or [N, H, V, K] state ([SG] 二,
 // state_v_first): element (k, v) of one (sequence, head) state sits at
 // k * rs + v * cs.
@@ -105,6 +118,10 @@ hipError_t launch_chunk_fwd_bf16(const ChunkFwdParams& p, hipStream_t stream);
 // preparation, then the state and output passes reading its results.
 hipError_t launch_chunk_prep_bf16(const ChunkPrepParams& p, hipStream_t stream);
 hipError_t launch_chunk_fwd_bf16_wide(const ChunkFwdParams& p, hipStream_t stream);
+
+// Chunk sizes 16 and 32 (any supported dtype and K; V % 16 == 0): one
+// generic kernel on the fp32 matrix cores.
+hipError_t launch_chunk_fwd_small(const ChunkFwdParams& p, int chunk, bool qkv_bf16, hipStream_t stream);
 
 // float32 q/k/v, VALU path.  K in {16,32,64,128}, V % 32 == 0.
 hipError_t launch_chunk_fwd_f32(const ChunkFwdParams& p, hipStream_t stream);

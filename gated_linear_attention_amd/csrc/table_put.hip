@@ -1,0 +1,44 @@
+// Packed-sequence tables written into the workspace by kernels whose payload
+// travels in the kernel arguments.  The host builds the sequence table
+// (longest sequence first); each launch carries up to kTablePut entries by
+// value, so no host buffer has to outlive the call and nothing is copied
+// from pageable memory.  The same launch expands every entry it carries into
+// that sequence's rows of the chunk table (FlashAttention-style packing, page
+// "flash-linear-attention 中的 Simple GLA", section 二: a sequence's chunks
+// start at its first packed token, the last one may be partial).
+#include <hip/hip_runtime.h>
+
+#include "sgla_internal.h"
+
+namespace sgla {
+namespace {
+
+// One workgroup per carried sequence: thread 0 stores the sequence entry,
+// all threads stride over the sequence's chunk rows.
+__global__ void __launch_bounds__(64)
+table_put_kernel(TablePut put, SeqEntry* __restrict__ seq_table, ChunkEntry* __restrict__ chunk_table) {
+  const int i = blockIdx.x;
+  if (i >= put.count) return;
+  const SeqEntry e = put.e[i];
+  if (threadIdx.x == 0) seq_table[put.first + i] = e;
+  if (chunk_table == nullptr) return;
+  const int32_t nch = (e.len + kChunk - 1) / kChunk;
+  for (int32_t c = threadIdx.x; c < nch; c += 64) {
+    ChunkEntry ce;
+    ce.t0 = e.bos + c * kChunk;
+    ce.len = min(kChunk, e.len - c * kChunk);
+    chunk_table[e.chunk0 + c] = ce;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_table_put(const TablePut& put, SeqEntry* seq_table, ChunkEntry* chunk_table,
+                            hipStream_t stream) {
+  if (put.count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(table_put_kernel, dim3((unsigned)put.count), dim3(64), 0, stream, put, seq_table,
+                     chunk_table);
+  return hipGetLastError();
+}
+
+}  // namespace sgla

@@ -66,8 +66,9 @@ typedef enum { SGLA_BF16 = 1, SGLA_F32 = 2 } sgla_dtype;
 typedef struct {
   int32_t B, T, H, K, V;      /* packed input: B == 1 and T = total tokens */
   int32_t num_seqs;           /* packed: number of sequences N; dense: ignored (N = B) */
-  int32_t chunk_size;         /* tokens per chunk; 0 selects 64; 64 for the fused entry points,
-                                 any power of two up to 64 for sgla_chunk_local_cumsum */
+  int32_t chunk_size;         /* tokens per chunk; 0 selects 64.  sgla_chunk_fwd: 16, 32 or 64;
+                                 sgla_chunk_local_cumsum: any power of two up to 64; the other
+                                 chunked entry points: 64 */
   int32_t qkv_dtype;          /* sgla_dtype of q, k and v */
   int32_t o_dtype;            /* sgla_dtype of o */
   float scale;                /* finite; callers wanting the default pass 1/sqrt(K) */
@@ -87,7 +88,7 @@ const char *sgla_last_error(void);
 /*
  * Bytes of device workspace sgla_chunk_fwd needs for these arguments: for
  * packed input the sequence and chunk tables; for bf16 inputs with K = 256 or
- * 512 also the per-(chunk, head) preparation records (gates, the masked
+ * 512 at chunk_size 64 also the per-(chunk, head) preparation records (gates, the masked
  * intra-chunk q k^T as bf16 hi/lo, and the chunk's q and k^T rearranged for
  * the state kernel: 128 K + 16 KiB + 768 bytes per 64-token chunk and query
  * head, plus 128 K bytes per 64-token chunk and kv head).
@@ -134,9 +135,17 @@ size_t sgla_chunk_fwd_workspace_size(const sgla_chunk_args *args, const int64_t 
  * Supported (any Hkv dividing H): K in {64, 128} with V a multiple of 64, or K in {256, 512}
  * with V a multiple of 32 (bf16 inputs);
  * K in {16, 32, 64, 128} and V a multiple of 32 (float32 inputs);
- * chunk_size 64.  Other powers of two are valid requests that return
- * SGLA_ERR_UNSUPPORTED; a chunk_size that is not a power of two is
- * SGLA_ERR_SHAPE (section 二 requires a power of two).
+ * chunk_size 16, 32 or 64 (section 二: a power of two; section 五 tests 16,
+ * 32 and 64).  64 runs the tuned kernels described above; 16 and 32 run one
+ * generic kernel per (sequence, head, 16-column V tile) on the fp32 matrix
+ * cores (float32 accuracy for either input dtype, a single launch, no
+ * preparation records).  Other powers of two, and values that are not a
+ * power of two, return SGLA_ERR_UNSUPPORTED.
+ *
+ * Packed input: the sequence and chunk tables are written into the
+ * workspace by small kernels enqueued on `stream` ahead of the chunk
+ * kernels; their contents travel in the kernel arguments, so
+ * cu_seqlens_host may be freed or reused as soon as the call returns.
  */
 sgla_status sgla_chunk_fwd(const sgla_chunk_args *args,
                            const void *q, const void *k, const void *v,

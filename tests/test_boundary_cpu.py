@@ -122,8 +122,8 @@ CASES = [
     ("cu not from 0", dict(N=2), dict(cu=[1, 64, 128]), SHAPE, "cu_seqlens[0]"),
     ("cu decreasing", dict(N=2), dict(cu=[0, 100, 90]), SHAPE, "non-decreasing"),
     ("cu not ending at T", dict(N=2), dict(cu=[0, 64, 127]), SHAPE, "equal T"),
-    ("chunk not power of 2", dict(chunk=48), {}, SHAPE, "power of two"),
-    ("chunk 32 unsupported", dict(chunk=32), {}, UNSUPPORTED, "chunk_size"),
+    ("chunk not power of 2", dict(chunk=48), {}, UNSUPPORTED, "power of two"),
+    ("chunk 8 unsupported", dict(chunk=8), {}, UNSUPPORTED, "16, 32 or 64"),
     ("chunk 128 unsupported", dict(chunk=128), {}, UNSUPPORTED, "at most 64"),
     ("bf16 K=96", dict(K=96), {}, UNSUPPORTED, "K in"),
     ("bf16 V=96", dict(V=96), {}, UNSUPPORTED, "V a multiple"),
@@ -409,10 +409,10 @@ def test_step_normalizer_rejects_without_writing(G):
 
 def test_gate_cumsum_chunk_sizes(G):
     """The standalone gate cumsum takes any power-of-two chunk size up to 64;
-    larger sizes are unsupported, others a shape error; the fused entry points
-    take 64 only (the case list above)."""
+    larger sizes and non-powers of two are unsupported; the chunked forward
+    takes 16, 32 and 64 (the case list above)."""
     b = Buffers()
-    for chunk, status, frag in ((128, UNSUPPORTED, "at most 64"), (48, SHAPE, "power of two")):
+    for chunk, status, frag in ((128, UNSUPPORTED, "at most 64"), (48, UNSUPPORTED, "power of two")):
         a = mkargs(G, chunk=chunk)
         st = G.lib.sgla_chunk_local_cumsum(ctypes.byref(a), b.p("g"), None, b.p("dg"), None, 0, None)
         assert st == status and frag in G.lib.sgla_last_error().decode()

@@ -102,39 +102,28 @@ def test_gla_state_v_first_and_bf16_output(V):
     assert np.all(np.abs(o3 - o1) <= 2.0 ** -8 * np.abs(o1))
 
 
-def test_gla_named_workload_sampled():
+def test_gla_named_workload_full():
     """The packed K = V = 128 workload (8 sequences of 64..4096 tokens, 16
-    heads, h0) with per-key gates, in one launch; the oracle checks sampled
-    (sequence, head) units one by one."""
+    heads, h0) with per-key gates, in one launch, compared with the oracle
+    over the whole o and final_state tensors."""
     inp = make_chunk_inputs(CHUNK_CONFIGS["varlen_bf16_k128"])
     gk = make_key_gates(inp, seed=77)
     o, ht = run(inp, gk)
-    cu = inp["cu_seqlens"]
-    lens = np.diff(cu)
-    units = [(int(np.argmax(lens)), 0), (int(np.argmin(lens)), 15), (3, 7), (5, 2)]
-    worst_o = worst_h = 0.0
-    for n, h in units:
-        s, e = int(cu[n]), int(cu[n + 1])
-        sl = lambda x: x[:, s:e, h:h + 1]
-        o_ref, h_ref = oracle.gla_fwd(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(gk), scale=inp["scale"],
-                                      initial_state=inp["initial_state"][n:n + 1, h:h + 1], nthreads=1)
-        worst_o = max(worst_o, err_ratio(o[:, s:e, h:h + 1], o_ref))
-        worst_h = max(worst_h, err_ratio(ht[n:n + 1, h:h + 1], h_ref))
-    print(f"[gla varlen] o {worst_o:.2e} final {worst_h:.2e}", flush=True)
-    assert worst_o <= TOL_BF16 and worst_h <= TOL_BF16
+    o_ref, h_ref = oracle.gla_fwd(inp["q"], inp["k"], inp["v"], gk, scale=inp["scale"],
+                                  initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"])
+    eo, eh = err_ratio(o, o_ref), err_ratio(ht, h_ref)
+    print(f"[gla varlen] whole-tensor o {eo:.2e} final {eh:.2e}", flush=True)
+    assert np.all(np.isfinite(o)) and eo <= TOL_BF16 and eh <= TOL_BF16
 
 
 @pytest.mark.parametrize("kind", ["forget", "resets"])
 @pytest.mark.parametrize("dtype,K,V", [("bf16", 128, 128), ("bf16", 64, 96), ("f32", 32, 64)],
                          ids=["bf16_chain", "fp32_chain", "f32"])
-def test_gla_degenerate_gates(dtype, K, V, kind, request):
-    if dtype == "f32" and kind == "resets":
-        # the per-key running gates are float32: after a -1e4 gate inside a
-        # chunk their differences keep ~1e-3 absolute accuracy, which meets
-        # the bf16 bar but not the float32 one (measured 3.8e-3)
-        request.node.add_marker(pytest.mark.xfail(strict=True, reason="per-key running gates in float32"))
+def test_gla_degenerate_gates(dtype, K, V, kind):
     """Per-key gates of -1e4 (a full reset) at every token, or for every key of
-    every 37th token."""
+    every 37th token.  Float32 inputs carry each key's running gate as hi + lo
+    (and form the decays of k from suffix sums in double), so their decays
+    stay exact to float32 and the 1e-4 bar holds after a reset."""
     inp = make_chunk_inputs(small(f"gdeg_{kind}", dtype=dtype, K=K, V=V, T=150, initial_state=True))
     gk = np.array(make_key_gates(inp, seed=8), dtype=np.float32, copy=True)
     if kind == "forget":

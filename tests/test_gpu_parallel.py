@@ -116,19 +116,36 @@ def test_parallel_empty():
     assert o.shape == (2, 0, 2, 64) and A.shape == (2, 2, 0, 0)
 
 
-def test_parallel_full_size_sampled_heads():
+def test_parallel_full_size_whole_tensor():
     """The benchmark workload (B=2, T=4096, H=16, K=V=128, per-token gates) in
-    the benchmark's launch: whole rows of A and o for two sampled (row, head)
-    units against the oracle run on exactly those units."""
+    the benchmark's launch, every element of A and o against the oracle.  The
+    oracle runs one batch row at a time (A in float64 is 2.1 GB per row);
+    max |err| and the RMS are accumulated over the whole tensors."""
     w = CHUNK_CONFIGS["parallel_bf16_k128"]
     inp = make_chunk_inputs(w)
     d = device_inputs(inp)
     o, A = sgla.parallel_fwd(d["q"], d["k"], d["v"], g=d["g"], scale=inp["scale"], output_attn=True,
                              out_dtype=torch.float32)
     torch.cuda.synchronize()
-    for b, h in ((0, 0), (1, w.H - 1)):
-        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+    acc = {"o": [0.0, 0.0, 0], "A": [0.0, 0.0, 0]}   # max |err|, sum ref^2, count
+
+    def add(name, x, ref):
+        x = np.asarray(x, dtype=np.float64)
+        acc[name][0] = max(acc[name][0], float(np.max(np.abs(x - ref))))
+        acc[name][1] += float(np.sum(ref * ref))
+        acc[name][2] += ref.size
+
+    for b in range(inp["B"]):
+        sl = slice(b, b + 1)
         o_ref, A_ref = oracle.parallel(inp["q"][sl], inp["k"][sl], inp["v"][sl], g=inp["g"][sl],
                                        scale=inp["scale"])
-        check(o[b, :, h].cpu().numpy(), A[b, h].cpu().numpy(), o_ref[0, :, 0], A_ref[0, 0],
-              f"full b={b} h={h}")
+        A_got = A[b].cpu().numpy()
+        T = inp["T"]
+        upper = np.triu(np.ones((T, T), dtype=bool), 1)
+        assert not np.any(A_got[:, upper]), f"row {b}: nonzero entries above the diagonal"
+        add("A", A_got, A_ref[0])
+        del A_got, A_ref
+        add("o", o[b].cpu().numpy(), o_ref[0])
+    errs = {k: v[0] / np.sqrt(v[1] / v[2]) for k, v in acc.items()}
+    print(f"[parallel full] whole-tensor o {errs['o']:.2e} A {errs['A']:.2e}", flush=True)
+    assert errs["o"] <= TOL_BF16 and errs["A"] <= TOL_BF16
