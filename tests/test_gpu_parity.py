@@ -698,7 +698,7 @@ def test_back_to_back_varlen_calls():
         inp = make_chunk_inputs(small(f"b2b{i}", B=1, T=0, H=2, K=128, V=64, fixed_lengths=lens,
                                       initial_state=True, seed=50 + i))
         d = device_inputs(inp)
-        cu = np.ascontiguousarray(inp["cu_seqlens"], dtype=np.int64)
+        cu = np.array(inp["cu_seqlens"], dtype=np.int64, copy=True)   # the call's own host array
         N, T = len(cu) - 1, int(cu[-1])
         args = sgla._chunk_args(1, T, 2, 128, 64, N, 64, 1, 2, inp["scale"], 1)
         cu_ptr = ctypes.c_void_p(cu.ctypes.data)
