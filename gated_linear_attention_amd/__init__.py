@@ -26,7 +26,7 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_bwd", "gla_chunk_fwd", "chunk_normalizer", "recurrent_step_normalizer",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_bwd", "gla_chunk_fwd", "chunk_normalizer", "recurrent_step_normalizer",
            "parallel_fwd",
            "recurrent_step", "chunk_local_cumsum", "library_path", "lib",
            "SglaError", "ABI_VERSION"]
@@ -72,6 +72,10 @@ def _load():
     lib.sgla_chunk_fwd_workspace_size.argtypes = [pargs, vp]
     lib.sgla_chunk_fwd.restype = ctypes.c_int
     lib.sgla_chunk_fwd.argtypes = [pargs, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sgla_chunk_fwd_noalloc_max_bytes.restype = sz
+    lib.sgla_chunk_fwd_noalloc_max_bytes.argtypes = []
+    lib.sgla_chunk_fwd_noalloc.restype = ctypes.c_int
+    lib.sgla_chunk_fwd_noalloc.argtypes = [pargs, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.sgla_chunk_bwd_workspace_size.restype = sz
     lib.sgla_chunk_bwd_workspace_size.argtypes = [pargs, vp]
     lib.sgla_chunk_bwd.restype = ctypes.c_int
@@ -186,6 +190,22 @@ def chunk_fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None,
 
     Returns ``(o, final_state)``; ``final_state`` is None unless
     ``output_final_state``.  ``out`` optionally supplies a preallocated o."""
+    return _chunk_fwd(q, k, v, g, g_gamma, scale, initial_state, output_final_state, cu_seqlens,
+                      chunk_size, o_dtype, out, state_v_first, None, False)
+
+
+def chunk_fwd_noalloc(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None,
+                      output_final_state=False, cu_seqlens=None, chunk_size=64,
+                      o_dtype=torch.float32, out=None, final_state=None, state_v_first=False):
+    """chunk_fwd through sgla_chunk_fwd_noalloc: the library's fixed scratch
+    array replaces the workspace.  With ``out`` (and ``final_state`` when
+    ``output_final_state``) supplied, the call allocates nothing."""
+    return _chunk_fwd(q, k, v, g, g_gamma, scale, initial_state, output_final_state, cu_seqlens,
+                      chunk_size, o_dtype, out, state_v_first, final_state, True)
+
+
+def _chunk_fwd(q, k, v, g, g_gamma, scale, initial_state, output_final_state, cu_seqlens,
+               chunk_size, o_dtype, out, state_v_first, final_state, noalloc):
     if not isinstance(q, torch.Tensor) or q.dim() != 4:
         raise ValueError("q must be a 4-D tensor [B, T, H, K]")
     dev = q.device
@@ -217,13 +237,26 @@ def chunk_fwd(q, k, v, g=None, g_gamma=None, scale=None, initial_state=None,
     args = _chunk_args(B, T, H, K, V, N, chunk_size, qkv, od, scale, output_final_state, Hkv,
                        state_v_first)
     cu_ptr = None if cu is None else ctypes.c_void_p(cu.data_ptr())
-    ws_bytes = _workspace_size(args, cu_ptr)
     if out is None:
         o = torch.empty((B, T, H, V), device=dev, dtype=o_dtype)
     else:
         _check_dev("out", out, dev, o_dtype, (B, T, H, V))
         o = out
-    ht = torch.empty(sshape, device=dev, dtype=torch.float32) if output_final_state else None
+    ht = None
+    if output_final_state:
+        if final_state is None:
+            ht = torch.empty(sshape, device=dev, dtype=torch.float32)
+        else:
+            _check_dev("final_state", final_state, dev, torch.float32, sshape)
+            ht = final_state
+    if noalloc:
+        st = lib.sgla_chunk_fwd_noalloc(ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                        _ptr(g_gamma), _ptr(initial_state), cu_ptr, _ptr(o), _ptr(ht),
+                                        _stream(dev))
+        if st != _OK:
+            _raise(st, "sgla_chunk_fwd_noalloc")
+        return o, ht
+    ws_bytes = _workspace_size(args, cu_ptr)
     ws = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
     st = lib.sgla_chunk_fwd(ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                             _ptr(g_gamma), _ptr(initial_state), cu_ptr, _ptr(o), _ptr(ht),

@@ -235,23 +235,25 @@ sgla::SeqLayout layout_of(const sgla_chunk_args* a, const Plan& P, char* ws) {
 
 }  // namespace
 
-extern "C" {
+namespace sgla {
 
-int sgla_abi_version(void) { return SGLA_ABI_VERSION; }
-
-const char* sgla_last_error(void) { return g_last_error.c_str(); }
-
-size_t sgla_chunk_fwd_workspace_size(const sgla_chunk_args* args, const int64_t* cu_seqlens_host) {
+size_t chunk_fwd_workspace(const sgla_chunk_args* args, const int64_t* cu_seqlens_host, sgla_status* status) {
   Plan P;
-  if (plan_shape(args, cu_seqlens_host, true, &P) != SGLA_OK) return 0;
-  g_last_error.clear();
+  *status = plan_shape(args, cu_seqlens_host, true, &P);
+  if (*status != SGLA_OK) return 0;
+  if (P.chunk_size != kChunk && P.chunk_size != 32 && P.chunk_size != 16) {
+    *status = fail(SGLA_ERR_UNSUPPORTED, "chunk_size %d is not implemented (16, 32 or 64)", P.chunk_size);
+    return 0;
+  }
   return P.total_bytes;
 }
 
-sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const void* k, const void* v,
-                           const float* g, const float* g_gamma, const float* initial_state,
-                           const int64_t* cu_seqlens_host, void* o, float* final_state,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+sgla_status report(sgla_status st, const char* msg) { return fail(st, "%s", msg); }
+
+sgla_status chunk_fwd_enqueue(const sgla_chunk_args* args, const void* q, const void* k, const void* v,
+                              const float* g, const float* g_gamma, const float* initial_state,
+                              const int64_t* cu_seqlens_host, void* o, float* final_state, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream, WorkspaceAcquire acquire) {
   Plan P;
   sgla_status st = plan_shape(args, cu_seqlens_host, true, &P);
   if (st != SGLA_OK) return st;
@@ -271,10 +273,6 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
       (final_state && !aligned(final_state, 16)))
     return fail(SGLA_ERR_INVALID_ARG, "g and state pointers must be aligned");
   const size_t need = P.total_bytes;
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(SGLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
-                workspace == nullptr ? " (NULL)" : "");
-  if (need > 0 && !aligned(workspace, 256)) return fail(SGLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (final_state != nullptr && initial_state != nullptr && final_state != initial_state) {
     const size_t sb = (size_t)P.N * a.H * a.K * a.V * sizeof(float);
     const char* f0 = reinterpret_cast<const char*>(final_state);
@@ -282,6 +280,15 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
     if (f0 < i0 + sb && i0 < f0 + sb)
       return fail(SGLA_ERR_INVALID_ARG, "final_state partially overlaps initial_state (only exact aliasing is allowed)");
   }
+  if (need > 0 && acquire != nullptr) {
+    // every argument is valid: now obtain the library-owned scratch memory
+    st = acquire(&workspace);
+    if (st != SGLA_OK) return st;
+  }
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(SGLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
+                workspace == nullptr ? " (NULL)" : "");
+  if (need > 0 && !aligned(workspace, 256)) return fail(SGLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
   char* ws = static_cast<char*>(workspace);
   st = upload_tables(P, ws, stream);
@@ -337,6 +344,32 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const voi
   }
   if (e != hipSuccess) return hip_fail(e, "launching the chunk kernel");
   return ok();
+}
+
+
+}  // namespace sgla
+
+extern "C" {
+
+int sgla_abi_version(void) { return SGLA_ABI_VERSION; }
+
+const char* sgla_last_error(void) { return g_last_error.c_str(); }
+
+size_t sgla_chunk_fwd_workspace_size(const sgla_chunk_args* args, const int64_t* cu_seqlens_host) {
+  // sized for any power-of-two chunk size: sgla_chunk_local_cumsum takes its
+  // workspace from here too
+  Plan P;
+  if (plan_shape(args, cu_seqlens_host, true, &P) != SGLA_OK) return 0;
+  g_last_error.clear();
+  return P.total_bytes;
+}
+
+sgla_status sgla_chunk_fwd(const sgla_chunk_args* args, const void* q, const void* k, const void* v,
+                           const float* g, const float* g_gamma, const float* initial_state,
+                           const int64_t* cu_seqlens_host, void* o, float* final_state,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return sgla::chunk_fwd_enqueue(args, q, k, v, g, g_gamma, initial_state, cu_seqlens_host, o, final_state,
+                                 workspace, workspace_bytes, stream, nullptr);
 }
 
 size_t sgla_chunk_bwd_workspace_size(const sgla_chunk_args* args, const int64_t* cu_seqlens_host) {

@@ -6,7 +6,24 @@
 #include <cstdint>
 #include <hip/hip_runtime_api.h>
 
+#include "sgla.h"
+
 namespace sgla {
+
+// sgla_chunk_fwd with the validation, table upload and launches it performs
+// (the C entry points call it with their own workspace).  With `acquire`
+// given, the workspace pointer is obtained from it once every argument has
+// passed validation (and only if the call needs workspace at all).
+// chunk_fwd_workspace validates the arguments and returns the workspace
+// bytes such a call needs (0 with *status != SGLA_OK on invalid arguments);
+// report() records a message for sgla_last_error().
+typedef sgla_status (*WorkspaceAcquire)(void** workspace);
+sgla_status chunk_fwd_enqueue(const sgla_chunk_args* args, const void* q, const void* k, const void* v,
+                              const float* g, const float* g_gamma, const float* initial_state,
+                              const int64_t* cu_seqlens_host, void* o, float* final_state, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream, WorkspaceAcquire acquire);
+size_t chunk_fwd_workspace(const sgla_chunk_args* args, const int64_t* cu_seqlens_host, sgla_status* status);
+sgla_status report(sgla_status st, const char* msg);
 
 constexpr int kChunk = 64;        // tokens per chunk
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin

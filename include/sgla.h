@@ -157,6 +157,34 @@ sgla_status sgla_chunk_fwd(const sgla_chunk_args *args,
                            hipStream_t stream);
 
 /*
+ * sgla_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, semantics,
+ * kernels and results as sgla_chunk_fwd; the scratch memory (the packed
+ * sequence tables, and for bf16 K = 256 / 512 at chunk_size 64 the
+ * preparation records) comes from a fixed device array inside the library,
+ * sgla_chunk_fwd_noalloc_max_bytes() bytes (16 MiB) per GPU, held until the
+ * process ends.  The call allocates nothing, frees nothing and does not
+ * synchronize.
+ *   - A request whose sgla_chunk_fwd_workspace_size exceeds that size
+ *     returns SGLA_ERR_WORKSPACE before anything is enqueued.
+ *   - The array is found for the current device; `stream` must belong to
+ *     the current device.
+ *   - Every call on one GPU shares that GPU's array and it keeps the last
+ *     call's contents: calls that overlap on one GPU (different streams, or
+ *     threads without ordering) race and must be serialized by the caller.
+ *     Calls enqueued on one stream are ordered and safe.
+ */
+size_t sgla_chunk_fwd_noalloc_max_bytes(void);
+sgla_status sgla_chunk_fwd_noalloc(const sgla_chunk_args *args,
+                                   const void *q, const void *k, const void *v,
+                                   const float *g, const float *g_gamma,
+                                   const float *initial_state,
+                                   const int64_t *cu_seqlens_host,
+                                   void *o, float *final_state,
+                                   hipStream_t stream);
+
+/*
  * Bytes of device workspace sgla_chunk_bwd needs: the packed-sequence tables,
  * the fp32 state entering every 64-token chunk and the fp32 gradient of the
  * state leaving it (2 * 4 K V bytes per chunk and head), 4 bytes per

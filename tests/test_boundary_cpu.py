@@ -463,3 +463,31 @@ def test_parallel_fwd_empty_is_ok(G):
                                      None, None, None)
         assert st == OK, G.lib.sgla_last_error()
     assert b.unchanged()
+
+
+def test_chunk_fwd_noalloc_rejects_without_device(G):
+    """sgla_chunk_fwd_noalloc validates everything on the host before it looks
+    up its scratch array (no device call is made): a request needing more
+    scratch than the fixed array holds and every invalid argument return
+    their status with nothing written."""
+    b = Buffers()
+    cap = G.lib.sgla_chunk_fwd_noalloc_max_bytes()
+    assert cap == 16 << 20
+    # bf16 K = 512, 5120 tokens x 2 heads: ~24 MB of preparation records
+    a = mkargs(G, B=1, T=64 * 80, H=2, K=512, V=64)
+    assert G.lib.sgla_chunk_fwd_workspace_size(ctypes.byref(a), None) > cap
+    st = G.lib.sgla_chunk_fwd_noalloc(ctypes.byref(a), b.p("q"), b.p("k"), b.p("v"), b.p("g"), None,
+                                      None, None, b.p("o"), b.p("ht"), None)
+    assert st == WORKSPACE and "scratch" in G.lib.sgla_last_error().decode()
+    cu = np.array([0, 64, 128], dtype=np.int64)
+    cases = [(mkargs(G, N=2), dict(gg=b.p("gg")), INVALID, "mutually exclusive"),
+             (mkargs(G, N=2, chunk=8), {}, UNSUPPORTED, "chunk_size"),
+             (mkargs(G, N=2), dict(q=None), INVALID, "non-NULL")]
+    for args, over, status, frag in cases:
+        kw = dict(q=b.p("q"), gg=None)
+        kw.update(over)
+        st = G.lib.sgla_chunk_fwd_noalloc(ctypes.byref(args), kw["q"], b.p("k"), b.p("v"), b.p("g"), kw["gg"],
+                                          b.p("h0"), ctypes.c_void_p(cu.ctypes.data), b.p("o"), b.p("ht"), None)
+        msg = G.lib.sgla_last_error().decode()
+        assert st == status and frag in msg, (st, msg)
+    assert b.unchanged()
