@@ -2,15 +2,15 @@
 """Benchmark of the Simple GLA hot path on one MI355X.
 
 A step is one pass of the whole chunked forward (chunk-local gate cumsum,
-inter-chunk state pass and output pass: one sgla_chunk_fwd call, which for
-K >= 256 is a per-chunk preparation kernel followed by the state/output
-kernel) over one batch of the dense bf16 prefill workload: B=4, T=2048, H=4,
-K=V=512, q/k/v ~ N(0,1) in bf16, g = logsigmoid(N(0,1)), scale 1/sqrt(K),
-chunk 64, fp32 o, final state written.  ``value`` is tokens/s over the K timed
-steps with all inputs already resident in HBM (input/output copies are
-rotated so the 256 MB last-level cache cannot hold a step's working set).
-Before the counted warmup steps the device runs untimed steps for
---warm-seconds (default 1 s) so the timed steps see steady-state clocks.
+inter-chunk state pass and output pass: one sgla_chunk_fwd call) over one
+batch of the long hybrid-layer prefill workload: B=8, T=8192, H=16,
+K=V=128, bf16 q/k/v ~ N(0,1) with k L2-normalised per head, the per-head
+RetNet decay g_gamma[h] = log(1 - 2^(-5-5h/16)), scale 1/sqrt(K), chunk 64,
+fp32 o, final state written.  ``value`` is tokens/s over the K timed steps
+with all inputs already resident in HBM (input/output copies are rotated so
+the 256 MB last-level cache cannot hold a step's working set).  Before the
+counted warmup steps the device runs untimed steps for --warm-seconds
+(default 1 s) so the timed steps see steady-state clocks.
 
 The JSON line also carries:
   roofline      -- the chunked forward against its bound (HBM for this
@@ -22,16 +22,24 @@ The JSON line also carries:
                    matches the current kernel sources, else null;
   mfma          -- the same call's algorithmic FLOPs against the bf16 dense
                    MFMA peak;
+  configs       -- the same record for every named chunked workload (tiny
+                   fp32, dense bf16 K=V=512, packed varlen K=V=128 and the
+                   headline), each with tokens/s, TFLOP/s, the HBM and MFMA
+                   fractions, the attainable-roofline fraction, traffic and
+                   (from the cpu_baseline leg) its parity against the oracle;
   decode        -- the in-place decode step on 256 sequences x 32 heads x
                    128 x 128 fp32 state, 64 consecutive steps, HBM GB/s;
   backward      -- sgla_chunk_bwd on the packed K = V = 128 workload (dq, dk,
-                   dv, dg, dh0), against the fp32 matrix-core peak its kernels
-                   run on;
+                   dv, dg, dh0);
   normalizer    -- sgla_chunk_normalizer on the same workload, HBM GB/s;
-  gla           -- sgla_gla_chunk_fwd (per-key gates) on the same workload,
-                   against the fp32 matrix-core peak;
+  gla           -- sgla_gla_chunk_fwd (per-key gates) on the same workload;
+  parallel      -- sgla_parallel_fwd with the decayed attention matrix;
   cpu_baseline  -- the fp64 CPU oracle timed on the host cores on whole
-                   batches of the same workload (a reported baseline only).
+                   batches of the headline workload (a reported baseline
+                   only), with the host CPU model; the same leg runs the
+                   oracle once per timed workload and reports the GPU
+                   outputs' error against it (max |err| / RMS and RMS err /
+                   RMS over the whole o and final state) in each record.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -62,6 +70,8 @@ METRIC = "chunked Simple-GLA fwd tokens/s + % bf16 MFMA peak; decode HBM GB/s"
 KERNEL_SOURCES = {
     "chunk_fwd": ("chunk_prep_bf16.hip", "chunk_fwd_bf16_wide.hip", "mfma_common.h", "gate_scan.h",
                   "unit_map.h"),
+    "chunk_fwd_bf16_kernel": ("chunk_fwd_bf16.hip", "mfma_common.h", "gate_scan.h", "unit_map.h"),
+    "chunk_fwd_f32_kernel": ("chunk_fwd_f32.hip", "gate_scan.h", "unit_map.h"),
     "recurrent_step_kernel": ("recurrent_step.hip",),
     "parallel_fwd_kernel": ("parallel_fwd.hip", "mfma_common.h", "gate_scan.h", "unit_map.h"),
 }
@@ -227,9 +237,63 @@ def bench_chunk(workload: str, steps: int, warmup: int, warm_seconds: float,
     total_ms = t_start.elapsed_time(t_end)
     per = sorted(a.elapsed_time(b) for a, b in ev)
     kern_ms = sum(per) / len(per)
+    last = copies[(steps - 1) % ncopies]
+    o_host = last["o"].cpu().numpy()
+    ht_host = None if last["ht"] is None else last["ht"].cpu().numpy()
+    del copies
     return dict(inp=inp, total_ms=total_ms, wall_s=wall, kernel_ms_mean=kern_ms,
                 kernel_ms_median=per[len(per) // 2], alg_bytes=alg_bytes, alg_flops=alg_flops,
-                ncopies=ncopies)
+                ncopies=ncopies, o=o_host, ht=ht_host)
+
+
+def traffic_key(inp) -> str:
+    """Name of the traffic record (and of its kernel-source set) for a call."""
+    if inp["dtype"] != "bf16":
+        return "chunk_fwd_f32_kernel"
+    return "chunk_fwd" if inp["K"] >= 256 else "chunk_fwd_bf16_kernel"
+
+
+def chunk_record(workload: str, r: dict, steps: int) -> dict:
+    """The per-workload record: throughput, roofline fractions, traffic."""
+    inp = r["inp"]
+    tokens = inp["B"] * inp["T"]
+    kern_s = r["kernel_ms_mean"] * 1e-3
+    t_mem = r["alg_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = r["alg_flops"] / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+    gbs = r["alg_bytes"] / kern_s / 1e9
+    tflops = r["alg_flops"] / kern_s / 1e12
+    if t_mem >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
+    roof["traffic"] = load_traffic(workload, traffic_key(inp))
+    kernels = chunk_kernels(inp)
+    roof.update({"kernel": "+".join(kernels), "launches_per_call": len(kernels),
+                 "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
+                 "kernel_ms_median": round(r["kernel_ms_median"], 5),
+                 "algorithmic_bytes_per_launch": int(r["alg_bytes"]),
+                 "algorithmic_flops_per_launch": int(r["alg_flops"]),
+                 "attainable_frac": round(max(t_mem, t_mfma) / kern_s, 4)})
+    ms_step = r["total_ms"] / steps
+    return {
+        "workload": workload,
+        "config": {"B": inp["B"], "T": inp["T"], "H": inp["H"], "num_kv_heads": inp["Hkv"], "K": inp["K"],
+                   "V": inp["V"], "num_seqs": inp["N"], "tokens": tokens, "chunk_size": inp["chunk_size"],
+                   "qkv_dtype": inp["dtype"], "o_dtype": "f32",
+                   "gate": "g" if inp["g"] is not None else ("g_gamma" if inp["g_gamma"] is not None else "none"),
+                   "initial_state": inp["initial_state"] is not None,
+                   "output_final_state": bool(inp["output_final_state"]),
+                   "rotated_input_copies": r["ncopies"], "seed": _seed_of(workload)},
+        "steps": steps, "ms_per_step": round(ms_step, 5),
+        "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
+        "tflops": round(tflops, 2),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+        "attainable_frac": round(max(t_mem, t_mfma) / kern_s, 4),
+        "roofline": roof,
+    }
 
 
 def bench_decode(steps_timed: int, warmup: int, warm_seconds: float, state_v_first: bool = False):
@@ -273,6 +337,30 @@ def bench_decode(steps_timed: int, warmup: int, warm_seconds: float, state_v_fir
             "peak_GBs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
             "tokens_per_s": round(N / (mean_ms * 1e-3), 1),
             "traffic": None if state_v_first else load_traffic(w.name, "recurrent_step_kernel")}
+
+
+def decode_fresh_run(steps: int = 4):
+    """A fresh run of the first ``steps`` decode steps of the named decode
+    workload from its initial state: the outputs of every step and the state
+    after the last, for the parity check of the cpu_baseline leg."""
+    import numpy as np
+    import torch
+
+    import gated_linear_attention_amd as sgla
+    from gla_workloads import DECODE_CONFIGS, make_decode_inputs
+
+    inp = make_decode_inputs(DECODE_CONFIGS["decode_n256_h32_k128"], steps=steps)
+    dev = torch.device("cuda:0")
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+    state = t(inp["state"], torch.float32)
+    outs = []
+    for s in range(steps):
+        o = sgla.recurrent_step(t(inp["q"][s], torch.bfloat16), t(inp["k"][s], torch.bfloat16),
+                                t(inp["v"][s], torch.bfloat16), t(inp["g"][s], torch.float32), state,
+                                scale=inp["scale"])
+        outs.append(o.cpu().numpy())
+    torch.cuda.synchronize()
+    return {"inp": inp, "o": outs, "state": state.cpu().numpy()}
 
 
 def bwd_algorithmic(inp) -> tuple[float, float]:
@@ -571,29 +659,86 @@ def bench_parallel(workload: str, steps: int, warmup: int, warm_seconds: float):
                      "peak_tflops": BF16_MFMA_PEAK_TFLOPS, "dtype": "bf16"}}
 
 
-def cpu_baseline(inp, min_seconds: float = 10.0):
-    """The fp64 CPU oracle on whole batches of the timed workload, repeated
-    until at least ``min_seconds`` of wall time (a bounded sample)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _errs(x, ref) -> dict:
+    import numpy as np
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    d = np.abs(x - ref)
+    if rms == 0.0:
+        return {"max_err_over_rms": float(d.max()) if d.size else 0.0, "rms_err_over_rms": 0.0}
+    return {"max_err_over_rms": float(f"{float(d.max()) / rms:.3e}"),
+            "rms_err_over_rms": float(f"{float(np.sqrt(np.mean(d * d))) / rms:.3e}")}
+
+
+def cpu_baseline(inp, chunk_results: dict, decode_check, min_seconds: float = 10.0):
+    """The fp64 CPU oracle on whole batches of the headline workload,
+    repeated until at least ``min_seconds`` of wall time (a bounded sample),
+    then run once on every other timed workload; its outputs give each
+    record's parity (whole o and final state, against the GPU outputs of the
+    timed calls; decode: every step of a fresh 4-step run and the state
+    after it)."""
     import oracle
     threads = oracle.default_threads()
     units = inp["N"] * inp["H"]
     reps = 0
     t0 = time.perf_counter()
+    ref = None
     while True:
-        oracle.fwd(inp["q"], inp["k"], inp["v"], g=inp["g"], g_gamma=inp["g_gamma"],
-                   scale=inp["scale"], initial_state=inp["initial_state"],
-                   cu_seqlens=inp["cu_seqlens"], output_final_state=inp["output_final_state"],
-                   nthreads=threads)
+        ref = oracle.fwd(inp["q"], inp["k"], inp["v"], g=inp["g"], g_gamma=inp["g_gamma"],
+                         scale=inp["scale"], initial_state=inp["initial_state"],
+                         cu_seqlens=inp["cu_seqlens"], output_final_state=inp["output_final_state"],
+                         nthreads=threads)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
     tokens = inp["B"] * inp["T"] * reps
+    parity = {}
+    for name, r in chunk_results.items():
+        ri = r["inp"]
+        if ri is inp:
+            o_ref, ht_ref = ref
+        else:
+            o_ref, ht_ref = oracle.fwd(ri["q"], ri["k"], ri["v"], g=ri["g"], g_gamma=ri["g_gamma"],
+                                       scale=ri["scale"], initial_state=ri["initial_state"],
+                                       cu_seqlens=ri["cu_seqlens"], nthreads=threads)
+        p = {"o": _errs(r["o"], o_ref), "scope": "whole tensors"}
+        if r["ht"] is not None:
+            p["final_state"] = _errs(r["ht"], ht_ref)
+        p["tolerance"] = 2e-2 if ri["dtype"] == "bf16" else 1e-4
+        p["pass"] = all(v["max_err_over_rms"] <= p["tolerance"] for k, v in p.items()
+                        if k in ("o", "final_state"))
+        parity[name] = p
+    if decode_check is not None:
+        d = decode_check
+        S = d["inp"]["state"].astype("float64")
+        worst = 0.0
+        for s, o_gpu in enumerate(d["o"]):
+            o_ref, S = oracle.step(d["inp"]["q"][s], d["inp"]["k"][s], d["inp"]["v"][s], d["inp"]["g"][s], S,
+                                   scale=d["inp"]["scale"], nthreads=threads)
+            worst = max(worst, _errs(o_gpu, o_ref)["max_err_over_rms"])
+        es = _errs(d["state"], S)
+        parity["decode"] = {"o_worst_step": {"max_err_over_rms": worst}, "state": es,
+                            "scope": f"whole tensors, {len(d['o'])} steps from the initial state",
+                            "tolerance": 2e-2, "pass": worst <= 2e-2 and es["max_err_over_rms"] <= 2e-2}
     return {"value": round(tokens / dt, 2), "unit": "tokens/s", "cores": min(threads, units),
-            "kind": "oracle", "seconds": round(dt, 3),
+            "kind": "oracle", "seconds": round(dt, 3), "cpu_model": cpu_model(),
+            "host_threads_available": threads,
             "sample": f"{reps} repetitions of one full batch of the timed workload "
                       f"(B={inp['B']}, T={inp['T']}, H={inp['H']}, K={inp['K']}, V={inp['V']}: "
-                      f"{units} sequence-head units, one per thread), fp64 token-by-token"}
+                      f"{units} sequence-head units, one per thread), fp64 token-by-token"}, parity
 
 
 COPY_BYTES = 512 << 20
@@ -616,13 +761,20 @@ def calibrate_copy(reps: int = 3):
                       "bytes_written_per_launch": COPY_BYTES, "launches": reps}), flush=True)
 
 
+CHUNK_LEGS = ("long_gamma_k128", "varlen_bf16_k128", "dense_bf16_k512", "tiny_f32")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dense_bf16_k512",
-                    help="chunked workload to time (default: the dense bf16 K=V=512 prefill)")
+    ap.add_argument("--workload", default="long_gamma_k128",
+                    help="chunked workload of the headline (default: the long hybrid-layer prefill, "
+                         "B=8 T=8192 H=16 K=V=128 with g_gamma)")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="time the headline workload only (no other configs, no decode, backward, "
+                         "normalizer, GLA or parallel legs)")
     ap.add_argument("--warm-seconds", type=float, default=1.0,
                     help="untimed device warm-up before the counted warmup steps")
     ap.add_argument("--expand-kv", action="store_true",
@@ -632,7 +784,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--backward-workload", default="varlen_bf16_k128",
                     help="workload of the backward timing (K <= 128)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (CPU timing and the parity of every record)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device-to-device copy of known size (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -656,64 +809,56 @@ def main():
         print(json.dumps({"parallel": bench_parallel("parallel_bf16_k128", a.steps, a.warmup,
                                                      a.warm_seconds)}), flush=True)
         return
-    r = bench_chunk(a.workload, a.steps, a.warmup, a.warm_seconds, a.expand_kv)
-    inp = r["inp"]
-    tokens = inp["B"] * inp["T"]
-    ms_step = r["total_ms"] / a.steps
-    kern_s = r["kernel_ms_mean"] * 1e-3
-    t_mem = r["alg_bytes"] / (HBM_PEAK_GBS * 1e9)
-    t_mfma = r["alg_flops"] / (BF16_MFMA_PEAK_TFLOPS * 1e12)
-    bound = "hbm" if t_mem >= t_mfma else "mfma"
-    gbs = r["alg_bytes"] / kern_s / 1e9
-    tflops = r["alg_flops"] / kern_s / 1e12
-    if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    else:
-        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
-    roof["traffic"] = load_traffic(a.workload, "chunk_fwd")
-    roof.update({"kernel": "+".join(chunk_kernels(inp)),
-                 "launches_per_call": len(chunk_kernels(inp)),
-                 "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
-                 "kernel_ms_median": round(r["kernel_ms_median"], 5),
-                 "algorithmic_bytes_per_launch": int(r["alg_bytes"]),
-                 "algorithmic_flops_per_launch": int(r["alg_flops"]),
-                 "attainable_frac": round(max(t_mem, t_mfma) / kern_s, 4)})
+    legs = [a.workload] + ([] if a.only_headline else [w for w in CHUNK_LEGS if w != a.workload])
+    results, records = {}, {}
+    for wl in legs:
+        steps = a.steps if wl == a.workload else 20
+        print(f"[bench] {wl}", file=sys.stderr, flush=True)
+        results[wl] = bench_chunk(wl, steps, a.warmup, a.warm_seconds, a.expand_kv and wl == a.workload)
+        records[wl] = chunk_record(wl, results[wl], steps)
+    head = records[a.workload]
+    inp = results[a.workload]["inp"]
     out = {
         "metric": METRIC,
-        "value": round(tokens / (ms_step * 1e-3), 1),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": inp["dtype"],
         "data": "synthetic",
-        "config": {"workload": a.workload, "B": inp["B"], "T": inp["T"], "H": inp["H"],
-                   "num_kv_heads": inp["Hkv"], "K": inp["K"], "V": inp["V"], "num_seqs": inp["N"],
-                   "chunk_size": inp["chunk_size"], "o_dtype": "f32",
-                   "gate": "g" if inp["g"] is not None else
-                           ("g_gamma" if inp["g_gamma"] is not None else "none"),
-                   "output_final_state": bool(inp["output_final_state"]),
-                   "rotated_input_copies": r["ncopies"], "seed": _seed_of(a.workload)},
-        "roofline": roof,
-        "mfma": {"achieved_tflops": round(tflops, 2), "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
-                 "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)},
+        "config": dict({"workload": a.workload}, **head["config"]),
+        "roofline": head["roofline"],
+        "mfma": {"achieved_tflops": head["tflops"], "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+                 "frac": head["mfma_frac"]},
+        "configs": records,
     }
-    if not a.no_decode:
+    decode_check = None
+    if not a.no_decode and not a.only_headline:
+        print("[bench] decode", file=sys.stderr, flush=True)
         out["decode"] = bench_decode(64, a.warmup, a.warm_seconds)
         out["decode_state_v_first"] = bench_decode(64, a.warmup, a.warm_seconds, state_v_first=True)
-    if not a.no_backward:
+        if not a.no_cpu_baseline:
+            decode_check = decode_fresh_run(4)
+    if not a.no_backward and not a.only_headline:
+        print("[bench] backward, normalizer, GLA, parallel form", file=sys.stderr, flush=True)
         out["backward"] = bench_backward(a.backward_workload, 20, a.warmup, a.warm_seconds)
         out["normalizer"] = bench_normalizer(a.backward_workload, 20, a.warmup, a.warm_seconds)
         out["gla"] = bench_gla(a.backward_workload, 20, a.warmup, a.warm_seconds)
         out["parallel"] = bench_parallel("parallel_bf16_k128", 10, a.warmup, a.warm_seconds)
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp)
+        print("[bench] cpu baseline and parity", file=sys.stderr, flush=True)
+        out["cpu_baseline"], parity = cpu_baseline(inp, results, decode_check)
+        for wl, p in parity.items():
+            if wl in records:
+                records[wl]["parity"] = p
+            elif wl == "decode" and "decode" in out:
+                out["decode"]["parity"] = p
+        out["parity_pass"] = all(p["pass"] for p in parity.values())
     print(json.dumps(out), flush=True)
 
 

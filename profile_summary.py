@@ -7,6 +7,11 @@ kept under profiles/ and the per-launch HBM traffic record bench.py reads.
       the last N dispatches of the kernel matching REGEX (bench.py's timed
       launches) -- the figure to compare with bench.py's HIP-event timing.
 
+  python profile_summary.py counters --dir D [--dir D2] --kernel REGEX --title T --out F
+                                    --command CMD [--command CMD ...] [--source-key KEY]
+      median per-dispatch value of every counter collected for the kernel,
+      plus the MFMA utilisation and stall fractions derived from them.
+
   python profile_summary.py traffic --fetch D1 --write D2 --calib-fetch D3 --calib-write D4
                                     --kernel REGEX --name KERNEL --workload W --out-json J
                                     --out-txt F --command CMD [--command CMD ...]
@@ -135,6 +140,61 @@ def traffic(a):
     print("\n".join(lines))
 
 
+def counters(a):
+    """Median per-dispatch value of every collected counter for the kernels
+    matching the pattern, with the MFMA utilisation and issued bf16 MFMA
+    flops derived from them (GRBM_GUI_ACTIVE is summed over the XCDs in the
+    CSV, so one XCD's active cycles are its value divided by the XCD count;
+    SQ_VALU_MFMA_BUSY_CYCLES is summed over every SIMD)."""
+    pat = re.compile(a.kernel)
+    by = {}
+    names = set()
+    for d in a.dir:
+        for r in _rows(d, "counter_collection.csv"):
+            if not pat.search(r["Kernel_Name"]):
+                continue
+            names.add(r["Kernel_Name"])
+            key = (r["_file"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
+            per = by.setdefault(r["Counter_Name"], {})
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not by:
+        sys.exit(f"no counter rows for {a.kernel}")
+    med = {c: statistics.median(v.values()) for c, v in by.items()}
+    n = {c: len(v) for c, v in by.items()}
+    lines = [f"# rocprofv3 counters: {a.title}", "", "Commands (from the repository root; one counter group per run):", ""]
+    lines += [f"    {c}" for c in a.command]
+    lines += ["", f"Kernel(s): {', '.join('`' + k[:100] + '`' for k in sorted(names))}", "",
+              "| counter | median per dispatch | dispatches |", "|---|---|---|"]
+    lines += [f"| {c} | {med[c]:.6g} | {n[c]} |" for c in sorted(med)]
+    derived = {}
+    if "GRBM_GUI_ACTIVE" in med:
+        xcd_cycles = med["GRBM_GUI_ACTIVE"] / a.xcds
+        derived["active cycles per XCD"] = f"{xcd_cycles:.0f} ({xcd_cycles / a.clock_ghz / 1e3:.1f} us at {a.clock_ghz} GHz)"
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+            u = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_cycles * a.simds)
+            derived["MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x SIMDs))"] = f"{100 * u:.1f} %"
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
+        derived["bf16 MFMA flops issued (MOPS x 512)"] = f"{med['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.4g}"
+    if "SQ_WAVE_CYCLES" in med:
+        wc = med["SQ_WAVE_CYCLES"]
+        for c in ("SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS",
+                  "SQ_ACTIVE_INST_VALU", "SQ_WAIT_ANY"):
+            if c in med:
+                derived[f"{c} / SQ_WAVE_CYCLES"] = f"{100 * med[c] / wc:.1f} %"
+    if "SQ_LDS_BANK_CONFLICT" in med and "SQ_LDS_IDX_ACTIVE" in med and med["SQ_LDS_IDX_ACTIVE"]:
+        derived["LDS bank conflict / LDS active"] = f"{100 * med['SQ_LDS_BANK_CONFLICT'] / med['SQ_LDS_IDX_ACTIVE']:.1f} %"
+    if derived:
+        lines += ["", "Derived:", ""] + [f"- {k}: {v}" for k, v in derived.items()]
+    sys.path.insert(0, ROOT)
+    if a.source_key:
+        from bench import kernel_source_hash
+        lines += ["", f"Kernel source hash ({a.source_key}): {kernel_source_hash(a.source_key)}"]
+    lines += [""]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -151,8 +211,18 @@ def main():
         c.add_argument("--" + k.replace("_", "-"), required=True)
     c.add_argument("--calib-kernel", default="Mul")
     c.add_argument("--command", action="append", required=True)
+    k = sub.add_parser("counters")
+    k.add_argument("--dir", action="append", required=True)
+    k.add_argument("--kernel", required=True)
+    k.add_argument("--title", required=True)
+    k.add_argument("--out", required=True)
+    k.add_argument("--command", action="append", required=True)
+    k.add_argument("--source-key", default=None, help="bench.KERNEL_SOURCES key whose hash to record")
+    k.add_argument("--xcds", type=int, default=8)
+    k.add_argument("--simds", type=int, default=1024)
+    k.add_argument("--clock-ghz", type=float, default=2.4)
     a = ap.parse_args()
-    trace(a) if a.mode == "trace" else traffic(a)
+    {"trace": trace, "traffic": traffic, "counters": counters}[a.mode](a)
 
 
 if __name__ == "__main__":
