@@ -150,7 +150,9 @@ CASES = [
 
 @pytest.mark.parametrize("desc,aover,cover,status,frag", CASES, ids=[c[0] for c in CASES])
 def test_chunk_fwd_rejects_without_writing(G, desc, aover, cover, status, frag):
-    b = Buffers()
+    # state buffers sized for the case's sequence count, so no check sees
+    # two unrelated host buffers as overlapping states
+    b = Buffers(N=max(1, (aover or {}).get("N", 1)))
     args = None if aover is None else mkargs(G, **aover)
     cover = dict(cover)
     kw = {}
