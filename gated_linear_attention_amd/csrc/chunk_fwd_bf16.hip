@@ -18,19 +18,22 @@
 // being numerically stable).
 //
 // Layout of the work (gfx950, wave64, v_mfma_f32_16x16x32_bf16):
-//   * one workgroup of 4 waves per (sequence, head, 64-wide V tile); the
-//     workgroups of one (sequence, kv head) share an XCD so repeated reads of
-//     its q, k and v rows (other V tiles, other query heads of a kv group)
-//     are served by that XCD's L2;
-//   * wave w owns state columns [16w, 16w + 16) of the tile for all K rows, in
-//     MFMA accumulator registers (fp32), carried across chunks without ever
+//   * one workgroup of 8 waves per (unit, head, 64-wide V tile), where a unit
+//     is a whole sequence or, for segmented chains, a bin of sequence pieces
+//     processed one after another (each piece from its own entering state:
+//     the sequence's initial state or the record the segment state pass
+//     wrote); the workgroups of one (unit, kv head) share an XCD so repeated
+//     reads of its q, k and v rows (other V tiles, other query heads of a kv
+//     group) are served by that XCD's L2;
+//   * the state lives in MFMA accumulator registers (fp32), split over the
+//     waves as described at Layout below, carried across chunks without ever
 //     leaving the chip -- only the final state is written;
 //   * each chunk's Q, K (64 x K) and V tile (64 x 64) are staged in LDS
 //     row-major; the operands that need the token index contiguous per lane
 //     (K^T and V as MFMA operands reduced over tokens) are fetched with the
 //     gfx950 transposing LDS read ds_read_b64_tr_b16;
-//   * the next chunk's rows are loaded into registers while the current chunk
-//     computes (one chunk of latency hiding).
+//   * staging is double-buffered with one barrier per chunk, the rows of
+//     chunk m + 2 loading into registers while chunk m computes.
 //
 // Precision: the state, the accumulation and the output are fp32.  The three
 // MFMA operands that are not exact bf16 inputs -- the decay-masked A, the
@@ -95,7 +98,9 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                       const bf16* __restrict__ v, const float* __restrict__ g,
                       const float* __restrict__ g_gamma, const float* __restrict__ h0,
                       TOut* __restrict__ o, float* __restrict__ ht, float scale, int32_t H,
-                      int32_t Hkv, int32_t V, StateLayout sl, SeqLayout seqs) {
+                      int32_t Hkv, int32_t V, StateLayout sl, SeqLayout seqs,
+                      const SegEntry* __restrict__ segs, const BinEntry* __restrict__ bins, int32_t num_bins,
+                      const float* __restrict__ sin) {
   using L = Layout<K>;
   constexpr int NT = L::NT;
   constexpr int SEG = K / 8;                 // 16-byte segments per q/k row
@@ -105,25 +110,11 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
 
-  // ---- which (sequence, head, V tile) this workgroup owns ----------------
-  const UnitMap um = map_unit(blockIdx.x, V / VT, Hkv, H / Hkv, seqs.num_seqs);
+  // ---- which (sequence or bin of segments, head, V tile) this workgroup owns
+  const UnitMap um = map_unit(blockIdx.x, V / VT, Hkv, H / Hkv, segs != nullptr ? num_bins : seqs.num_seqs);
   if (!um.valid) return;
   const int rank = um.rank, hd = um.hd, hk = um.hk, vt = um.vt;
-  int64_t bos;
-  int32_t len, seq;
-  if (seqs.seq_table != nullptr) {
-    // workgroup-uniform: keep in scalar registers so buffer descriptors built
-    // from them stay scalar
-    const SeqEntry e = seqs.seq_table[rank];
-    bos = __builtin_amdgcn_readfirstlane(e.bos);
-    len = __builtin_amdgcn_readfirstlane(e.len);
-    seq = __builtin_amdgcn_readfirstlane(e.seq);
-  } else {
-    bos = (int64_t)rank * seqs.T;
-    len = seqs.T;
-    seq = rank;
-  }
-  const int nchunks = (len + C - 1) / C;
+
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -142,11 +133,6 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int RSK = Hkv * K;                  // token stride of k
   const int RSV = Hkv * V;                  // token stride of v
   const int RSO = H * V;                    // token stride of o
-  const bf16* qb = q + (bos * H + hd) * (int64_t)K;
-  const bf16* kb = k + (bos * Hkv + hk) * (int64_t)K;
-  const bf16* vb = v + (bos * Hkv + hk) * (int64_t)V + vt * VT;
-  const float* gb = g != nullptr ? g + bos * H + hd : nullptr;
-  TOut* ob = o + (bos * H + hd) * (int64_t)V + vt * VT;     // workgroup-uniform base
   const uint32_t ocol = (16 * vc + 4 * g4) * (uint32_t)sizeof(TOut);   // lane's 4 columns
   const float gam2 = g_gamma != nullptr
                          ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
@@ -171,319 +157,369 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int i = tid; i < L::SZ_A / 16; i += NT)
       reinterpret_cast<uint4*>(sA(p))[i] = make_uint4(0, 0, 0, 0);
 
-  // ---- state in registers: h[kt][i] = S[krow0 + 16kt + 4g + i][vcol] ------
-  f32x4 h[L::KT];
-  {
-    const float* h0u = h0 != nullptr ? h0 + ((int64_t)seq * H + hd) * K * V : nullptr;
-#pragma unroll
-    for (int kt = 0; kt < L::KT; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        h[kt][i] = h0u != nullptr ? h0u[(int64_t)(krow0 + 16 * kt + 4 * g4 + i) * sl.rs + (int64_t)vcol * sl.cs] : 0.f;
+  // One unit (a sequence, or each segment of this workgroup's bin in turn).
+  // A unit's first barrier orders every LDS access of the previous unit
+  // before its own writes of the A and exchange buffers.
+  int32_t seg0 = 0, nunits = 1;
+  if (segs != nullptr) {
+    const BinEntry be = bins[rank];
+    seg0 = __builtin_amdgcn_readfirstlane(be.first);
+    nunits = __builtin_amdgcn_readfirstlane(be.count);
   }
+  for (int32_t u = 0; u < nunits; ++u) {
+    int64_t bos;
+    int32_t len, seq;
+    int32_t init = -1;      // segment entering-state record (-1: the sequence's initial state)
+    bool last = true;       // writes the final state
+    // workgroup-uniform: kept in scalar registers so buffer descriptors built
+    // from them stay scalar
+    if (segs != nullptr) {
+      const SegEntry e = segs[seg0 + u];
+      bos = __builtin_amdgcn_readfirstlane(e.bos);
+      len = __builtin_amdgcn_readfirstlane(e.len);
+      seq = __builtin_amdgcn_readfirstlane(e.seq);
+      init = __builtin_amdgcn_readfirstlane(e.init);
+      last = __builtin_amdgcn_readfirstlane(e.last) != 0;
+    } else if (seqs.seq_table != nullptr) {
+      const SeqEntry e = seqs.seq_table[rank];
+      bos = __builtin_amdgcn_readfirstlane(e.bos);
+      len = __builtin_amdgcn_readfirstlane(e.len);
+      seq = __builtin_amdgcn_readfirstlane(e.seq);
+    } else {
+      bos = (int64_t)rank * seqs.T;
+      len = seqs.T;
+      seq = rank;
+    }
+    const int nchunks = (len + C - 1) / C;
+    const bf16* qb = q + (bos * H + hd) * (int64_t)K;
+    const bf16* kb = k + (bos * Hkv + hk) * (int64_t)K;
+    const bf16* vb = v + (bos * Hkv + hk) * (int64_t)V + vt * VT;
+    const float* gb = g != nullptr ? g + bos * H + hd : nullptr;
+    TOut* ob = o + (bos * H + hd) * (int64_t)V + vt * VT;     // workgroup-uniform base
 
-  // ---- chunk staging registers -------------------------------------------
-  struct Stage {
-    u32x4 q[NQ], k[NQ], v[NV];
-    float g;
-    int len;
-  };
-  // Loads chunk m (zeros past the sequence's end) into st; every thread issues
-  // the same instructions whatever m is.
-  auto load_chunk = [&](int m, Stage& st) {
-    const int cl = max(0, min(C, len - m * C));
-    st.len = cl;
-    const int64_t tok = (int64_t)m * C;
-    const auto rq = make_rsrc(qb + tok * RSQ, (uint32_t)cl * RSQ * 2);
-    const auto rk = make_rsrc(kb + tok * RSK, (uint32_t)cl * RSK * 2);
-    const auto rv = make_rsrc(vb + tok * RSV, (uint32_t)cl * RSV * 2);
+    // ---- state in registers: h[kt][i] = S[krow0 + 16kt + 4g + i][vcol] ------
+    f32x4 h[L::KT];
+    {
+      // a later segment starts from its entering-state record ([K][V] rows);
+      // the first from the sequence's initial state (layout sl) or zeros
+      const float* h0u = init >= 0 ? sin + ((int64_t)init * H + hd) * K * V
+                                   : (h0 != nullptr ? h0 + ((int64_t)seq * H + hd) * K * V : nullptr);
+      const int64_t rs = init >= 0 ? V : sl.rs, cs = init >= 0 ? 1 : sl.cs;
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int s = tid + i * NT;
-      st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((s / SEG) * RSQ + (s % SEG) * 8) * 2, 0, 0);
-      st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((s / SEG) * RSK + (s % SEG) * 8) * 2, 0, 0);
-    }
+      for (int kt = 0; kt < L::KT; ++kt)
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int s = tid + i * NT;
-      const uint32_t off = ((s / (VT / 8)) * RSV + (s % (VT / 8)) * 8) * 2;
-      st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+        for (int i = 0; i < 4; ++i)
+          h[kt][i] = h0u != nullptr ? h0u[(int64_t)(krow0 + 16 * kt + 4 * g4 + i) * rs + (int64_t)vcol * cs] : 0.f;
     }
-    // per-token log gate; rows past the chunk's end read 0, so their
-    // cumulative value equals the last real token's (a finite decay for their
-    // zero k and v rows)
-    st.g = 0.f;
-    if (gb != nullptr) {
-      const auto rg = make_rsrc(gb + tok * H, (uint32_t)cl * H * 4);
-      st.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)(lane * H * 4), 0, 0));
-    }
-  };
-  auto store_chunk = [&](int p, const Stage& st) {
-    bf16* q_s = sQ(p);
-    bf16* k_s = sK(p);
-    bf16* v_s = sV(p);
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int s = tid + i * NT;
-      *reinterpret_cast<u32x4*>(q_s + (s / SEG) * L::LDQ + (s % SEG) * 8) = st.q[i];
-      *reinterpret_cast<u32x4*>(k_s + (s / SEG) * L::LDK + (s % SEG) * 8) = st.k[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int s = tid + i * NT;
-      *reinterpret_cast<u32x4*>(v_s + (s / (VT / 8)) * LDV + (s % (VT / 8)) * 8) = st.v[i];
-    }
-    if (w == L::NW - 1) {
-      // step (1) on the last wave (it owns one A tile, the first waves two):
-      // chunk-local cumulative log2 gate b, plus the per-token factors
-      // scale * 2^b (inter-chunk term) and 2^(b_last - b) (state update)
-      float* g_s = sG(p);
-      const float b = gb != nullptr ? wave_cumsum_log2(st.g)
-                                    : (float)min(lane + 1, st.len) * gam2;
-      const float blast = __shfl(b, C - 1, 64);
-      g_s[lane] = b;
-      g_s[C + lane] = exp2_hw(b) * scale;
-      g_s[2 * C + lane] = exp2_hw(blast - b);
-    }
-  };
 
-  // ---- per-chunk phases ----------------------------------------------------
-  // A = (Q K^T) (.) M, split into bf16 hi + lo, into sA(p)
-  auto phase_A = [&](int p) {
-    const bf16* q_s = sQ(p);
-    const bf16* k_s = sK(p);
-    const float* g_s = sG(p);
-    bf16* a_hi = sA(p);
-    bf16* a_lo = a_hi + C * LDA;
-    for (int ti = w; ti < 10; ti += L::NW) {
-      const int ct = tile_c(ti), jt = tile_j(ti);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < L::KSF; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(k_s + (16 * jt + r) * L::LDK + 32 * s + 8 * g4);
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(q_s + (16 * ct + r) * L::LDQ + 32 * s + 8 * g4);
-        acc = mfma(a, b, acc);  // acc[i] = q_c . k_j, c = 16ct + r, j = 16jt + 4g + i
-      }
-      const int c = 16 * ct + r;
-      const float bc = g_s[c];
-      const f32x4 bj = *reinterpret_cast<const f32x4*>(g_s + 16 * jt + 4 * g4);
-      float x[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 16 * jt + 4 * g4 + i;
-        x[i] = (j <= c) ? acc[i] * exp2_hw(bc - bj[i]) * scale : 0.f;
-      }
-      uint32_t h0, l0, h1, l1;
-      split2(x[0], x[1], h0, l0);
-      split2(x[2], x[3], h1, l1);
-      const u32x2 hi = {h0, h1}, lo = {l0, l1};
-      *reinterpret_cast<u32x2*>(a_hi + c * LDA + 16 * jt + 4 * g4) = hi;
-      *reinterpret_cast<u32x2*>(a_lo + c * LDA + 16 * jt + 4 * g4) = lo;
-    }
-  };
-  // O^T partial = scale diag(2^b) (h^T Q^T) over this wave's K/2 state rows,
-  // for c tiles in the order (own0, own1, partner's two)
-  auto phase_inter = [&](int p, f32x4 (&oacc)[4]) {
-    const bf16* q_s = sQ(p);
-    const float* g_s = sG(p);
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < L::KS; ++s) {
-      // A operand from the state: rows krow0 + 32s + 4g + {0..3} and
-      // krow0 + 32s + 16 + 4g + {0..3}; q is read with the same k order
-      float x[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = h[2 * s][i];
-        x[4 + i] = h[2 * s + 1][i];
-      }
-      bf16x8 hh, hl;
-      split8(x, hh, hl);
-      bf16x8 b[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16* qrow = q_s + (16 * ctile[t] + r) * L::LDQ + krow0 + 32 * s + 4 * g4;
-        b[t] = cat(*reinterpret_cast<const bf16x4*>(qrow), *reinterpret_cast<const bf16x4*>(qrow + 16));
-      }
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) oacc[ct] = mfma(hh, b[ct], oacc[ct]);
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) oacc[ct] = mfma(hl, b[ct], oacc[ct]);
-    }
-    // scale * diag(2^b): O^T column c = 16 ctile + r
-#pragma unroll
-    for (int t = 0; t < 4; ++t) oacc[t] *= g_s[C + 16 * ctile[t] + r];
-  };
-  // V fragments vf[s][e] = V[32s + 8g + e][16vc + r]
-  auto load_vf = [&](int p, bf16x8 (&vf)[2]) {
-    const bf16* v_s = sV(p);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      vf[s] = cat(tr_read(v_s, LDV, 32 * s + 8 * g4, 16 * vc),
-                  tr_read(v_s, LDV, 32 * s + 8 * g4 + 4, 16 * vc));
-  };
-  // h <- 2^b_last h + K^T (diag(2^(b_last - b)) V) for this wave's rows
-  auto phase_update = [&](int p, const bf16x8 (&vf)[2]) {
-    const bf16* k_s = sK(p);
-    const float* g_s = sG(p);
-    const float dall = exp2_hw(g_s[C - 1]);   // 2^b_last
-#pragma unroll
-    for (int kt = 0; kt < L::KT; ++kt) h[kt] *= dall;
-    bf16x8 vth[2], vtl[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(g_s + 2 * C + 32 * s + 8 * g4);
-      const f32x4 d1 = *reinterpret_cast<const f32x4*>(g_s + 2 * C + 32 * s + 8 * g4 + 4);
-      const u32x4 raw = __builtin_bit_cast(u32x4, vf[s]);
-      float x[8];
-      x[0] = bf_lo(raw[0]) * d0[0];
-      x[1] = bf_hi(raw[0]) * d0[1];
-      x[2] = bf_lo(raw[1]) * d0[2];
-      x[3] = bf_hi(raw[1]) * d0[3];
-      x[4] = bf_lo(raw[2]) * d1[0];
-      x[5] = bf_hi(raw[2]) * d1[1];
-      x[6] = bf_lo(raw[3]) * d1[2];
-      x[7] = bf_hi(raw[3]) * d1[3];
-      split8(x, vth[s], vtl[s]);
-    }
-    constexpr int KG = L::KT < 4 ? L::KT : 4;   // state tiles per MFMA group
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int k0 = 0; k0 < L::KT; k0 += KG) {
-        // A operands: K^T[krow0 + 16kt + r][32s + 8g + e]
-        bf16x8 a[KG];
-#pragma unroll
-        for (int u = 0; u < KG; ++u)
-          a[u] = cat(tr_read(k_s, L::LDK, 32 * s + 8 * g4, krow0 + 16 * (k0 + u)),
-                     tr_read(k_s, L::LDK, 32 * s + 8 * g4 + 4, krow0 + 16 * (k0 + u)));
-#pragma unroll
-        for (int u = 0; u < KG; ++u) h[k0 + u] = mfma(a[u], vth[s], h[k0 + u]);
-#pragma unroll
-        for (int u = 0; u < KG; ++u) h[k0 + u] = mfma(a[u], vtl[s], h[k0 + u]);
-      }
-    }
-  };
-  // own c tiles: kh = 0 -> c tiles 0 (j < 32) and 3 (j < 64);
-  //              kh = 1 -> c tiles 1 (j < 32) and 2 (j < 64)
-  // O^T (own tiles) += V^T A^T with A from sA(p)
-  auto phase_intra = [&](int p, const bf16x8 (&vf)[2], f32x4& mine0, f32x4& mine1) {
-    const bf16* ah0 = sA(p) + (16 * own0 + r) * LDA + 8 * g4;
-    const bf16* ah1 = sA(p) + (16 * own1 + r) * LDA + 8 * g4;
-    const bf16x8 p0h = *reinterpret_cast<const bf16x8*>(ah0);
-    const bf16x8 p0l = *reinterpret_cast<const bf16x8*>(ah0 + C * LDA);
-    const bf16x8 p1h = *reinterpret_cast<const bf16x8*>(ah1);
-    const bf16x8 p1l = *reinterpret_cast<const bf16x8*>(ah1 + C * LDA);
-    const bf16x8 p2h = *reinterpret_cast<const bf16x8*>(ah1 + 32);
-    const bf16x8 p2l = *reinterpret_cast<const bf16x8*>(ah1 + 32 + C * LDA);
-    mine0 = mfma(vf[0], p0h, mine0);
-    mine1 = mfma(vf[0], p1h, mine1);
-    mine0 = mfma(vf[0], p0l, mine0);
-    mine1 = mfma(vf[0], p1l, mine1);
-    mine1 = mfma(vf[1], p2h, mine1);
-    mine1 = mfma(vf[1], p2l, mine1);
-  };
-  // the partner's two c tiles of this wave's q.h partial go through LDS
-  auto exchange_write = [&](int px, const f32x4 (&oacc)[4]) {
-    f32x4* x = sX(px);
-    x[(w * 2 + 0) * 64 + lane] = oacc[2];
-    x[(w * 2 + 1) * 64 + lane] = oacc[3];
-  };
-  // own tiles + partner's partial, scaled, stored (rows past the chunk's end
-  // fall outside the descriptor and are dropped; cl = 0 stores nothing)
-  auto finalize = [&](int px, int m, int cl, f32x4 mine0, f32x4 mine1) {
-    const f32x4* x = sX(px);
-    const f32x4 x0 = x[((w ^ 4) * 2 + 0) * 64 + lane];
-    const f32x4 x1 = x[((w ^ 4) * 2 + 1) * 64 + lane];
-    const auto ro = make_rsrc(ob + (int64_t)m * C * RSO, (uint32_t)cl * RSO * sizeof(TOut));
-    const uint32_t c0 = 16 * own0 + r, c1 = 16 * own1 + r;
-    store4<TOut>(ro, c0 * RSO * (uint32_t)sizeof(TOut) + ocol, mine0 + x0);
-    store4<TOut>(ro, c1 * RSO * (uint32_t)sizeof(TOut) + ocol, mine1 + x1);
-  };
-
-  Stage st0, st1;
-  load_chunk(0, st0);
-  if (L::PF2) load_chunk(1, st1);
-
-  if constexpr (L::DB) {
-    // Pipelined: one barrier per chunk.  Iteration m stages chunk m, then
-    // finishes chunk m-1 (A V and the output store, from buffers of parity
-    // p^1 and registers carried over) and forms chunk m's A, q.h partials
-    // and state update.
-    bf16x8 vf_prev[2] = {};
-    f32x4 mine0 = {0.f, 0.f, 0.f, 0.f}, mine1 = {0.f, 0.f, 0.f, 0.f};
-    int prev_m = 0, prev_cl = 0;   // prev_cl = 0: nothing to store yet
-    auto step = [&](const int m, const int p, Stage& st) {
-      const int cl = st.len;
-      store_chunk(p, st);
-      __syncthreads();   // chunk m staged; chunk m-1's A and exchange tiles visible
-      phase_intra(p ^ 1, vf_prev, mine0, mine1);
-      finalize(p ^ 1, prev_m, prev_cl, mine0, mine1);
-      load_chunk(m + 2, st);
-      phase_A(p);
-      f32x4 oacc[4];
-      phase_inter(p, oacc);
-      exchange_write(p, oacc);
-      mine0 = oacc[0];
-      mine1 = oacc[1];
-      load_vf(p, vf_prev);
-      phase_update(p, vf_prev);
-      prev_m = m;
-      prev_cl = cl;
+    // ---- chunk staging registers -------------------------------------------
+    struct Stage {
+      u32x4 q[NQ], k[NQ], v[NV];
+      float g;
+      int len;
     };
-    int m = 0;
-    for (; m + 1 < nchunks; m += 2) {
-      step(m, 0, st0);
-      step(m + 1, 1, st1);
-    }
-    if (m < nchunks) step(m, 0, st0);
-    __syncthreads();
-    const int pl = (nchunks - 1) & 1;
-    phase_intra(pl, vf_prev, mine0, mine1);
-    finalize(pl, prev_m, prev_cl, mine0, mine1);
-  } else {
-    for (int m = 0; m < nchunks; ++m) {
-      const int cl = st0.len;
-      store_chunk(0, st0);
-      __syncthreads();   // chunk m staged
-      load_chunk(m + 1, st0);
-      phase_A(0);
-      f32x4 oacc[4];
-      phase_inter(0, oacc);
-      bf16x8 vf[2];
-      load_vf(0, vf);
-      phase_update(0, vf);
-      __syncthreads();   // A complete
-      f32x4 mine0 = oacc[0];
-      f32x4 mine1 = oacc[1];
-      phase_intra(0, vf, mine0, mine1);
-      __syncthreads();   // Q area is about to hold exchange tiles
-      exchange_write(0, oacc);
-      __syncthreads();
-      finalize(0, m, cl, mine0, mine1);
-      __syncthreads();   // exchange tiles read before the next chunk is staged
-    }
-  }
+    // Loads chunk m (zeros past the sequence's end) into st; every thread issues
+    // the same instructions whatever m is.
+    auto load_chunk = [&](int m, Stage& st) {
+      const int cl = max(0, min(C, len - m * C));
+      st.len = cl;
+      const int64_t tok = (int64_t)m * C;
+      const auto rq = make_rsrc(qb + tok * RSQ, (uint32_t)cl * RSQ * 2);
+      const auto rk = make_rsrc(kb + tok * RSK, (uint32_t)cl * RSK * 2);
+      const auto rv = make_rsrc(vb + tok * RSV, (uint32_t)cl * RSV * 2);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const int s = tid + i * NT;
+        st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((s / SEG) * RSQ + (s % SEG) * 8) * 2, 0, 0);
+        st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((s / SEG) * RSK + (s % SEG) * 8) * 2, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int s = tid + i * NT;
+        const uint32_t off = ((s / (VT / 8)) * RSV + (s % (VT / 8)) * 8) * 2;
+        st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+      }
+      // per-token log gate; rows past the chunk's end read 0, so their
+      // cumulative value equals the last real token's (a finite decay for their
+      // zero k and v rows)
+      // issued whether or not there is a per-token gate (an empty descriptor
+      // reads zeros), so every chunk's loads are the same count of memory
+      // instructions and waiting for them never waits for a later store
+      const auto rg = make_rsrc(gb != nullptr ? (const void*)(gb + tok * H) : (const void*)qb,
+                                gb != nullptr ? (uint32_t)cl * H * 4 : 0u);
+      st.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)(lane * H * 4), 0, 0));
+    };
+    auto store_chunk = [&](int p, const Stage& st) {
+      bf16* q_s = sQ(p);
+      bf16* k_s = sK(p);
+      bf16* v_s = sV(p);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const int s = tid + i * NT;
+        *reinterpret_cast<u32x4*>(q_s + (s / SEG) * L::LDQ + (s % SEG) * 8) = st.q[i];
+        *reinterpret_cast<u32x4*>(k_s + (s / SEG) * L::LDK + (s % SEG) * 8) = st.k[i];
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int s = tid + i * NT;
+        *reinterpret_cast<u32x4*>(v_s + (s / (VT / 8)) * LDV + (s % (VT / 8)) * 8) = st.v[i];
+      }
+      if (w == L::NW - 1) {
+        // step (1) on the last wave (it owns one A tile, the first waves two):
+        // chunk-local cumulative log2 gate b, plus the per-token factors
+        // scale * 2^b (inter-chunk term) and 2^(b_last - b) (state update)
+        float* g_s = sG(p);
+        const float b = gb != nullptr ? wave_cumsum_log2(st.g)
+                                      : (float)min(lane + 1, st.len) * gam2;
+        const float blast = __shfl(b, C - 1, 64);
+        g_s[lane] = b;
+        g_s[C + lane] = exp2_hw(b) * scale;
+        g_s[2 * C + lane] = exp2_hw(blast - b);
+      }
+    };
 
-  if (ht != nullptr) {
-    float* htu = ht + ((int64_t)seq * H + hd) * K * V;
+    // ---- per-chunk phases ----------------------------------------------------
+    // A = (Q K^T) (.) M, split into bf16 hi + lo, into sA(p)
+    auto phase_A = [&](int p) {
+      const bf16* q_s = sQ(p);
+      const bf16* k_s = sK(p);
+      const float* g_s = sG(p);
+      bf16* a_hi = sA(p);
+      bf16* a_lo = a_hi + C * LDA;
+      for (int ti = w; ti < 10; ti += L::NW) {
+        const int ct = tile_c(ti), jt = tile_j(ti);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kt = 0; kt < L::KT; ++kt)
+        for (int s = 0; s < L::KSF; ++s) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(k_s + (16 * jt + r) * L::LDK + 32 * s + 8 * g4);
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(q_s + (16 * ct + r) * L::LDQ + 32 * s + 8 * g4);
+          acc = mfma(a, b, acc);  // acc[i] = q_c . k_j, c = 16ct + r, j = 16jt + 4g + i
+        }
+        const int c = 16 * ct + r;
+        const float bc = g_s[c];
+        const f32x4 bj = *reinterpret_cast<const f32x4*>(g_s + 16 * jt + 4 * g4);
+        float x[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        htu[(int64_t)(krow0 + 16 * kt + 4 * g4 + i) * sl.rs + (int64_t)vcol * sl.cs] = h[kt][i];
-  }
+        for (int i = 0; i < 4; ++i) {
+          const int j = 16 * jt + 4 * g4 + i;
+          x[i] = (j <= c) ? acc[i] * exp2_hw(bc - bj[i]) * scale : 0.f;
+        }
+        uint32_t h0, l0, h1, l1;
+        split2(x[0], x[1], h0, l0);
+        split2(x[2], x[3], h1, l1);
+        const u32x2 hi = {h0, h1}, lo = {l0, l1};
+        *reinterpret_cast<u32x2*>(a_hi + c * LDA + 16 * jt + 4 * g4) = hi;
+        *reinterpret_cast<u32x2*>(a_lo + c * LDA + 16 * jt + 4 * g4) = lo;
+      }
+    };
+    // O^T partial = scale diag(2^b) (h^T Q^T) over this wave's K/2 state rows,
+    // for c tiles in the order (own0, own1, partner's two)
+    auto phase_inter = [&](int p, f32x4 (&oacc)[4]) {
+      const bf16* q_s = sQ(p);
+      const float* g_s = sG(p);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < L::KS; ++s) {
+        // A operand from the state: rows krow0 + 32s + 4g + {0..3} and
+        // krow0 + 32s + 16 + 4g + {0..3}; q is read with the same k order
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = h[2 * s][i];
+          x[4 + i] = h[2 * s + 1][i];
+        }
+        bf16x8 hh, hl;
+        split8(x, hh, hl);
+        bf16x8 b[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16* qrow = q_s + (16 * ctile[t] + r) * L::LDQ + krow0 + 32 * s + 4 * g4;
+          b[t] = cat(*reinterpret_cast<const bf16x4*>(qrow), *reinterpret_cast<const bf16x4*>(qrow + 16));
+        }
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) oacc[ct] = mfma(hh, b[ct], oacc[ct]);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) oacc[ct] = mfma(hl, b[ct], oacc[ct]);
+      }
+      // scale * diag(2^b): O^T column c = 16 ctile + r
+#pragma unroll
+      for (int t = 0; t < 4; ++t) oacc[t] *= g_s[C + 16 * ctile[t] + r];
+    };
+    // V fragments vf[s][e] = V[32s + 8g + e][16vc + r]
+    auto load_vf = [&](int p, bf16x8 (&vf)[2]) {
+      const bf16* v_s = sV(p);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        vf[s] = cat(tr_read(v_s, LDV, 32 * s + 8 * g4, 16 * vc),
+                    tr_read(v_s, LDV, 32 * s + 8 * g4 + 4, 16 * vc));
+    };
+    // h <- 2^b_last h + K^T (diag(2^(b_last - b)) V) for this wave's rows
+    auto phase_update = [&](int p, const bf16x8 (&vf)[2]) {
+      const bf16* k_s = sK(p);
+      const float* g_s = sG(p);
+      const float dall = exp2_hw(g_s[C - 1]);   // 2^b_last
+#pragma unroll
+      for (int kt = 0; kt < L::KT; ++kt) h[kt] *= dall;
+      bf16x8 vth[2], vtl[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(g_s + 2 * C + 32 * s + 8 * g4);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(g_s + 2 * C + 32 * s + 8 * g4 + 4);
+        const u32x4 raw = __builtin_bit_cast(u32x4, vf[s]);
+        float x[8];
+        x[0] = bf_lo(raw[0]) * d0[0];
+        x[1] = bf_hi(raw[0]) * d0[1];
+        x[2] = bf_lo(raw[1]) * d0[2];
+        x[3] = bf_hi(raw[1]) * d0[3];
+        x[4] = bf_lo(raw[2]) * d1[0];
+        x[5] = bf_hi(raw[2]) * d1[1];
+        x[6] = bf_lo(raw[3]) * d1[2];
+        x[7] = bf_hi(raw[3]) * d1[3];
+        split8(x, vth[s], vtl[s]);
+      }
+      constexpr int KG = L::KT < 4 ? L::KT : 4;   // state tiles per MFMA group
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int k0 = 0; k0 < L::KT; k0 += KG) {
+          // A operands: K^T[krow0 + 16kt + r][32s + 8g + e]
+          bf16x8 a[KG];
+#pragma unroll
+          for (int u = 0; u < KG; ++u)
+            a[u] = cat(tr_read(k_s, L::LDK, 32 * s + 8 * g4, krow0 + 16 * (k0 + u)),
+                       tr_read(k_s, L::LDK, 32 * s + 8 * g4 + 4, krow0 + 16 * (k0 + u)));
+#pragma unroll
+          for (int u = 0; u < KG; ++u) h[k0 + u] = mfma(a[u], vth[s], h[k0 + u]);
+#pragma unroll
+          for (int u = 0; u < KG; ++u) h[k0 + u] = mfma(a[u], vtl[s], h[k0 + u]);
+        }
+      }
+    };
+    // own c tiles: kh = 0 -> c tiles 0 (j < 32) and 3 (j < 64);
+    //              kh = 1 -> c tiles 1 (j < 32) and 2 (j < 64)
+    // O^T (own tiles) += V^T A^T with A from sA(p)
+    auto phase_intra = [&](int p, const bf16x8 (&vf)[2], f32x4& mine0, f32x4& mine1) {
+      const bf16* ah0 = sA(p) + (16 * own0 + r) * LDA + 8 * g4;
+      const bf16* ah1 = sA(p) + (16 * own1 + r) * LDA + 8 * g4;
+      const bf16x8 p0h = *reinterpret_cast<const bf16x8*>(ah0);
+      const bf16x8 p0l = *reinterpret_cast<const bf16x8*>(ah0 + C * LDA);
+      const bf16x8 p1h = *reinterpret_cast<const bf16x8*>(ah1);
+      const bf16x8 p1l = *reinterpret_cast<const bf16x8*>(ah1 + C * LDA);
+      const bf16x8 p2h = *reinterpret_cast<const bf16x8*>(ah1 + 32);
+      const bf16x8 p2l = *reinterpret_cast<const bf16x8*>(ah1 + 32 + C * LDA);
+      mine0 = mfma(vf[0], p0h, mine0);
+      mine1 = mfma(vf[0], p1h, mine1);
+      mine0 = mfma(vf[0], p0l, mine0);
+      mine1 = mfma(vf[0], p1l, mine1);
+      mine1 = mfma(vf[1], p2h, mine1);
+      mine1 = mfma(vf[1], p2l, mine1);
+    };
+    // the partner's two c tiles of this wave's q.h partial go through LDS
+    auto exchange_write = [&](int px, const f32x4 (&oacc)[4]) {
+      f32x4* x = sX(px);
+      x[(w * 2 + 0) * 64 + lane] = oacc[2];
+      x[(w * 2 + 1) * 64 + lane] = oacc[3];
+    };
+    // own tiles + partner's partial, scaled, stored (rows past the chunk's end
+    // fall outside the descriptor and are dropped; cl = 0 stores nothing)
+    auto finalize = [&](int px, int m, int cl, f32x4 mine0, f32x4 mine1) {
+      const f32x4* x = sX(px);
+      const f32x4 x0 = x[((w ^ 4) * 2 + 0) * 64 + lane];
+      const f32x4 x1 = x[((w ^ 4) * 2 + 1) * 64 + lane];
+      const auto ro = make_rsrc(ob + (int64_t)m * C * RSO, (uint32_t)cl * RSO * sizeof(TOut));
+      const uint32_t c0 = 16 * own0 + r, c1 = 16 * own1 + r;
+      store4<TOut>(ro, c0 * RSO * (uint32_t)sizeof(TOut) + ocol, mine0 + x0);
+      store4<TOut>(ro, c1 * RSO * (uint32_t)sizeof(TOut) + ocol, mine1 + x1);
+    };
+
+    Stage st0, st1;
+    load_chunk(0, st0);
+    if (L::PF2) load_chunk(1, st1);
+
+    if constexpr (L::DB) {
+      // Pipelined: one barrier per chunk.  Iteration m stages chunk m, then
+      // finishes chunk m-1 (A V and the output store, from buffers of parity
+      // p^1 and registers carried over) and forms chunk m's A, q.h partials
+      // and state update.
+      bf16x8 vf_prev[2] = {};
+      f32x4 mine0 = {0.f, 0.f, 0.f, 0.f}, mine1 = {0.f, 0.f, 0.f, 0.f};
+      int prev_m = 0, prev_cl = 0;   // prev_cl = 0: nothing to store yet
+      auto step = [&](const int m, const int p, Stage& st) {
+        const int cl = st.len;
+        store_chunk(p, st);
+        __syncthreads();   // chunk m staged; chunk m-1's A and exchange tiles visible
+        // the loads of chunk m + 2 go out before chunk m - 1's output stores:
+        // a later wait for those loads then never has to wait for the stores
+        load_chunk(m + 2, st);
+        phase_intra(p ^ 1, vf_prev, mine0, mine1);
+        finalize(p ^ 1, prev_m, prev_cl, mine0, mine1);
+        phase_A(p);
+        f32x4 oacc[4];
+        load_vf(p, vf_prev);
+        phase_inter(p, oacc);
+        phase_update(p, vf_prev);
+        exchange_write(p, oacc);
+        mine0 = oacc[0];
+        mine1 = oacc[1];
+        prev_m = m;
+        prev_cl = cl;
+      };
+      int m = 0;
+      for (; m + 1 < nchunks; m += 2) {
+        step(m, 0, st0);
+        step(m + 1, 1, st1);
+      }
+      if (m < nchunks) step(m, 0, st0);
+      __syncthreads();
+      const int pl = (nchunks - 1) & 1;
+      phase_intra(pl, vf_prev, mine0, mine1);
+      finalize(pl, prev_m, prev_cl, mine0, mine1);
+    } else {
+      for (int m = 0; m < nchunks; ++m) {
+        const int cl = st0.len;
+        store_chunk(0, st0);
+        __syncthreads();   // chunk m staged
+        load_chunk(m + 1, st0);
+        phase_A(0);
+        f32x4 oacc[4];
+        phase_inter(0, oacc);
+        bf16x8 vf[2];
+        load_vf(0, vf);
+        phase_update(0, vf);
+        __syncthreads();   // A complete
+        f32x4 mine0 = oacc[0];
+        f32x4 mine1 = oacc[1];
+        phase_intra(0, vf, mine0, mine1);
+        __syncthreads();   // Q area is about to hold exchange tiles
+        exchange_write(0, oacc);
+        __syncthreads();
+        finalize(0, m, cl, mine0, mine1);
+        __syncthreads();   // exchange tiles read before the next chunk is staged
+      }
+    }
+
+    if (ht != nullptr && last) {
+      float* htu = ht + ((int64_t)seq * H + hd) * K * V;
+#pragma unroll
+      for (int kt = 0; kt < L::KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          htu[(int64_t)(krow0 + 16 * kt + 4 * g4 + i) * sl.rs + (int64_t)vcol * sl.cs] = h[kt][i];
+    }
+  }  // unit
 }
 
 template <int K, typename TOut>
 hipError_t launch_k(const ChunkFwdParams& p, hipStream_t stream) {
-  if (p.seqs.num_seqs == 0) return hipSuccess;
-  const dim3 grid((unsigned)unit_grid(p.seqs.num_seqs, p.Hkv, p.H / p.Hkv, p.V / VT));
+  const int32_t units = p.segs != nullptr ? p.num_bins : p.seqs.num_seqs;
+  if (units == 0) return hipSuccess;
+  const dim3 grid((unsigned)unit_grid(units, p.Hkv, p.H / p.Hkv, p.V / VT));
   hipLaunchKernelGGL((chunk_fwd_bf16_kernel<K, TOut>), grid, dim3(Layout<K>::NT), 0, stream,
                      static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
                      static_cast<const bf16*>(p.v), p.g, p.g_gamma, p.h0,
-                     static_cast<TOut*>(p.o), p.ht, p.scale, p.H, p.Hkv, p.V, p.sl, p.seqs);
+                     static_cast<TOut*>(p.o), p.ht, p.scale, p.H, p.Hkv, p.V, p.sl, p.seqs, p.segs,
+                     p.bins, p.num_bins, p.sin);
   return hipGetLastError();
 }
 
@@ -497,6 +533,8 @@ hipError_t launch_out(const ChunkFwdParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+int chunk_fwd_bf16_vtile(int32_t) { return VT; }
 
 hipError_t launch_chunk_fwd_bf16(const ChunkFwdParams& p, hipStream_t stream) {
   return p.o_bf16 ? launch_out<__bf16>(p, stream) : launch_out<float>(p, stream);

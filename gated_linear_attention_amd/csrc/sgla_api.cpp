@@ -54,7 +54,190 @@ struct Plan {
   int32_t chunk_size = 0;                // requested chunk size (power of two <= 64)
   bool prep = false;                     // wide-key bf16 path: per-chunk preparation buffers
   size_t seq_off = 0, chunk_off = 0, gate_off = 0, amat_off = 0, kt_off = 0, q_off = 0, total_bytes = 0;
+  // segmented chains (bf16 K <= 128 forward)
+  bool seg = false;
+  std::vector<sgla::SegEntry> segs;      // bin by bin
+  std::vector<sgla::BinEntry> bins;      // most loaded first
+  std::vector<sgla::BlockEntry> blocks;  // per scanned sequence, in token order
+  std::vector<sgla::ScanEntry> scans;
+  int32_t num_rec = 0;                   // entering-state records (segments after a sequence's first)
+  size_t segt_off = 0, bint_off = 0, blkt_off = 0, scnt_off = 0, urec_off = 0, ulog_off = 0, sin_off = 0;
 };
+
+// Segmented chains.  The chunk kernel gives each workgroup slot a bin of
+// units to run one after another; with one workgroup per (sequence, head, V
+// tile) the longest sequence's chain bounds the launch.  A sequence longer
+// than a chosen length T is cut at chunk boundaries into a leading remainder
+// and pieces of exactly T chunks, and all pieces are packed into the bins
+// (longest first onto the least loaded bin), which brings the bound towards
+// (all chunks) / (bins) when the lengths are uneven or there are fewer
+// sequences than bins.  Every chunk before a sequence's last piece costs one
+// more pass over its k and v in the state-only pre-pass, charged here at
+// kPrepassWeight of a chunk step spread over the whole GPU.
+constexpr int64_t kSegSlots = 256;      // one chunk workgroup per CU of the 256
+constexpr int64_t kMinSegChunks = 16;   // shortest T considered
+constexpr double kPrepassWeight = 0.6;
+
+struct BinPack {
+  int64_t makespan = 0;               // chunks of the most loaded bin
+  std::vector<int32_t> bin_of;        // per piece
+};
+
+// Longest-processing-time packing of piece lengths (chunks) into `bins`.
+BinPack pack_bins(const std::vector<int64_t>& lens, int64_t bins) {
+  BinPack bp;
+  bp.bin_of.assign(lens.size(), 0);
+  std::vector<int32_t> order(lens.size());
+  for (size_t i = 0; i < lens.size(); ++i) order[i] = (int32_t)i;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return lens[x] > lens[y]; });
+  // min-heap of (load, bin)
+  std::vector<std::pair<int64_t, int32_t>> heap;
+  for (int64_t b = 0; b < bins; ++b) heap.push_back({0, (int32_t)b});
+  auto cmp = [](const std::pair<int64_t, int32_t>& x, const std::pair<int64_t, int32_t>& y) {
+    return x.first != y.first ? x.first > y.first : x.second > y.second;
+  };
+  std::make_heap(heap.begin(), heap.end(), cmp);
+  for (int32_t i : order) {
+    std::pop_heap(heap.begin(), heap.end(), cmp);
+    heap.back().first += std::max<int64_t>(lens[i], 1);
+    bp.bin_of[i] = heap.back().second;
+    bp.makespan = std::max(bp.makespan, heap.back().first);
+    std::push_heap(heap.begin(), heap.end(), cmp);
+  }
+  return bp;
+}
+
+// Pieces of a sequence of c chunks at length T: the remainder first (if
+// any), then pieces of T.  Returns their lengths in order.
+std::vector<int64_t> pieces_of(int64_t c, int64_t T) {
+  std::vector<int64_t> out;
+  if (c <= T) {
+    out.push_back(c);
+    return out;
+  }
+  const int64_t k = (c + T - 1) / T;
+  const int64_t first = c - (k - 1) * T;
+  out.push_back(first);
+  for (int64_t j = 1; j < k; ++j) out.push_back(T);
+  return out;
+}
+
+void plan_segments(const sgla_chunk_args* a, const int64_t* cu, Plan* P) {
+  const int64_t C = sgla::kChunk;
+  const int32_t N = P->N;
+  const int64_t units = (int64_t)a->H * (a->V / sgla::chunk_fwd_bf16_vtile(a->V));   // workgroups per piece
+  const int64_t bins = std::max<int64_t>(1, kSegSlots / units);
+  auto bos_of = [&](int32_t n) { return cu != nullptr ? cu[n] : (int64_t)n * a->T; };
+  auto len_of = [&](int32_t n) { return cu != nullptr ? cu[n + 1] - cu[n] : (int64_t)a->T; };
+  std::vector<int64_t> chunks(N);
+  int64_t maxc = 0, total = 0;
+  for (int32_t n = 0; n < N; ++n) {
+    chunks[n] = (len_of(n) + C - 1) / C;
+    maxc = std::max(maxc, chunks[n]);
+    total += chunks[n];
+  }
+  if (maxc <= kMinSegChunks || N > 64 * bins) return;
+  auto cost_at = [&](int64_t T, double* cost) {
+    std::vector<int64_t> lens;
+    int64_t pre = 0;
+    for (int32_t n = 0; n < N; ++n) {
+      const std::vector<int64_t> pc = pieces_of(chunks[n], T);
+      lens.insert(lens.end(), pc.begin(), pc.end());
+      pre += chunks[n] - pc.back();
+    }
+    *cost = (double)pack_bins(lens, bins).makespan + kPrepassWeight * (double)pre * (double)units / (double)kSegSlots;
+  };
+  double base;
+  cost_at(maxc, &base);   // no piece cut
+  double best = base;
+  int64_t bestT = 0;
+  const int64_t t_lo = std::max(kMinSegChunks, (total + bins - 1) / bins);
+  // candidate lengths: the lower bound and the lengths that split the longest
+  // sequence into k equal parts
+  std::vector<int64_t> cand;
+  for (int64_t t = t_lo; t < t_lo + 8 && t < maxc; ++t) cand.push_back(t);
+  for (int64_t k = 2; k <= 64; ++k) {
+    const int64_t t = (maxc + k - 1) / k;
+    if (t >= t_lo && t < maxc) cand.push_back(t);
+  }
+  for (int64_t t : cand) {
+    double cost;
+    cost_at(t, &cost);
+    if (cost < best * 0.97) {
+      best = cost;
+      bestT = t;
+    }
+  }
+  if (bestT == 0) return;
+  P->seg = true;
+  std::vector<sgla::SegEntry> segs;
+  std::vector<int64_t> seg_chunks;
+  for (int32_t n = 0; n < N; ++n) {
+    const int64_t bos = bos_of(n), len = len_of(n);
+    const std::vector<int64_t> pc = pieces_of(chunks[n], bestT);
+    const int64_t S = (int64_t)pc.size();
+    int64_t start = 0;   // first chunk of the piece
+    for (int64_t s = 0; s < S; ++s) {
+      sgla::SegEntry e{};
+      e.bos = (int32_t)(bos + start * C);
+      e.len = (int32_t)std::min(len - start * C, pc[s] * C);
+      e.seq = n;
+      e.init = s == 0 ? -1 : P->num_rec + (int32_t)s - 1;
+      e.last = s == S - 1 ? 1 : 0;
+      segs.push_back(e);
+      seg_chunks.push_back(pc[s]);
+      start += pc[s];
+    }
+    if (S > 1) P->num_rec += (int32_t)S - 1;
+  }
+  // pre-pass blocks over every piece but a sequence's last: sized so the
+  // pre-pass has about two workgroups per CU, 4 to 16 chunks each
+  int64_t pre = 0;
+  for (int32_t n = 0; n < N; ++n) pre += chunks[n] - pieces_of(chunks[n], bestT).back();
+  const int64_t units_pre = (int64_t)a->H * (a->V / 64);
+  const int64_t block_chunks =
+      std::min<int64_t>(16, std::max<int64_t>(4, (pre * units_pre + 2 * kSegSlots - 1) / (2 * kSegSlots)));
+  int32_t rec = 0;
+  for (int32_t n = 0, i = 0; n < N; ++n) {
+    const std::vector<int64_t> pc = pieces_of(chunks[n], bestT);
+    const int32_t first_block = (int32_t)P->blocks.size();
+    for (size_t s = 0; s + 1 < pc.size(); ++s) {
+      const sgla::SegEntry& e = segs[i + s];
+      const int64_t nb = (pc[s] + block_chunks - 1) / block_chunks;
+      int64_t b0 = 0;
+      for (int64_t b = 0; b < nb; ++b) {
+        const int64_t bc = pc[s] / nb + (b < pc[s] % nb ? 1 : 0);
+        sgla::BlockEntry be{};
+        be.t0 = (int32_t)(e.bos + b0 * C);
+        be.len = (int32_t)(bc * C);
+        be.out_rec = b + 1 == nb ? rec + (int32_t)s : -1;
+        P->blocks.push_back(be);
+        b0 += bc;
+      }
+    }
+    if (pc.size() > 1) {
+      P->scans.push_back({n, first_block, (int32_t)P->blocks.size() - first_block, 0});
+      rec += (int32_t)pc.size() - 1;
+    }
+    i += (int32_t)pc.size();
+  }
+  // pack, then lay the pieces out bin by bin, most loaded bin first
+  const BinPack bp = pack_bins(seg_chunks, bins);
+  std::vector<int64_t> load(bins, 0);
+  std::vector<std::vector<int32_t>> members(bins);
+  for (size_t i = 0; i < segs.size(); ++i) {
+    load[bp.bin_of[i]] += seg_chunks[i];
+    members[bp.bin_of[i]].push_back((int32_t)i);
+  }
+  std::vector<int32_t> border(bins);
+  for (int64_t b = 0; b < bins; ++b) border[b] = (int32_t)b;
+  std::stable_sort(border.begin(), border.end(), [&](int32_t x, int32_t y) { return load[x] > load[y]; });
+  for (int32_t b : border) {
+    if (members[b].empty()) continue;
+    P->bins.push_back({(int32_t)P->segs.size(), (int32_t)members[b].size()});
+    for (int32_t i : members[b]) P->segs.push_back(segs[i]);
+  }
+}
 
 sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv_support,
                        Plan* P) {
@@ -143,6 +326,20 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
   } else {
     P->total_bytes = P->gate_off;
   }
+  if (need_kv_support && a->qkv_dtype == SGLA_BF16 && a->K <= 128 && cs == sgla::kChunk && a->V % 64 == 0) {
+    plan_segments(a, cu, P);
+    if (P->seg) {
+      const size_t KV = (size_t)a->K * a->V;
+      P->segt_off = align_up(P->total_bytes, 256);
+      P->bint_off = P->segt_off + align_up(P->segs.size() * sizeof(sgla::SegEntry), 256);
+      P->blkt_off = P->bint_off + align_up(P->bins.size() * sizeof(sgla::BinEntry), 256);
+      P->scnt_off = P->blkt_off + align_up(P->blocks.size() * sizeof(sgla::BlockEntry), 256);
+      P->urec_off = P->scnt_off + align_up(P->scans.size() * sizeof(sgla::ScanEntry), 256);
+      P->ulog_off = P->urec_off + align_up(P->blocks.size() * a->H * KV * sizeof(float), 256);
+      P->sin_off = P->ulog_off + align_up(P->blocks.size() * a->H * sizeof(float), 256);
+      P->total_bytes = P->sin_off + align_up((size_t)P->num_rec * a->H * KV * sizeof(float), 256);
+    }
+  }
   return SGLA_OK;
 }
 
@@ -212,6 +409,25 @@ sgla_status upload_tables(const Plan& P, char* ws, hipStream_t stream) {
     std::memcpy(put.e, P.seqs.data() + first, n * sizeof(sgla::SeqEntry));
     const hipError_t e = sgla::launch_table_put(put, seq_table, chunk_table, stream);
     if (e != hipSuccess) return hip_fail(e, "writing the sequence and chunk tables");
+  }
+  return SGLA_OK;
+}
+
+// Copy a host table into the workspace through table_words launches (the
+// payload travels in the launch arguments).
+template <typename T>
+sgla_status upload_words(const std::vector<T>& v, char* dst, hipStream_t stream) {
+  static_assert(sizeof(T) % 4 == 0, "word-sized entries");
+  const size_t words = v.size() * sizeof(T) / 4;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(v.data());
+  sgla::TableWords put;
+  for (size_t first = 0; first < words; first += sgla::kTableWords) {
+    const size_t n = std::min<size_t>(sgla::kTableWords, words - first);
+    put.first = (int32_t)first;
+    put.count = (int32_t)n;
+    std::memcpy(put.w, src + first, n * 4);
+    const hipError_t e = sgla::launch_table_words(put, reinterpret_cast<uint32_t*>(dst), stream);
+    if (e != hipSuccess) return hip_fail(e, "writing the segment tables");
   }
   return SGLA_OK;
 }
@@ -291,8 +507,10 @@ sgla_status chunk_fwd_enqueue(const sgla_chunk_args* args, const void* q, const 
   if (need > 0 && !aligned(workspace, 256)) return fail(SGLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
   char* ws = static_cast<char*>(workspace);
-  st = upload_tables(P, ws, stream);
-  if (st != SGLA_OK) return st;
+  if (!P.seg) {
+    st = upload_tables(P, ws, stream);
+    if (st != SGLA_OK) return st;
+  }
   const sgla::SeqLayout L = layout_of(args, P, ws);
 
   sgla::ChunkFwdParams p;
@@ -318,6 +536,48 @@ sgla_status chunk_fwd_enqueue(const sgla_chunk_args* args, const void* q, const 
   p.qfr = P.prep ? ws + P.q_off : nullptr;
   if (p.ht == nullptr && !any_tokens) return ok();
   hipError_t e;
+  if (P.seg) {
+    // segmented chains: tables, the later segments' entering states, then
+    // one chunk workgroup per (segment, head, V tile)
+    {
+      // the four tables are adjacent in the workspace: one region, uploaded
+      // with as few launches as its size allows
+      std::vector<uint32_t> region((P.urec_off - P.segt_off) / 4, 0u);
+      auto put = [&](const void* src, size_t bytes, size_t off) {
+        if (bytes > 0) std::memcpy(reinterpret_cast<char*>(region.data()) + (off - P.segt_off), src, bytes);
+      };
+      put(P.segs.data(), P.segs.size() * sizeof(sgla::SegEntry), P.segt_off);
+      put(P.bins.data(), P.bins.size() * sizeof(sgla::BinEntry), P.bint_off);
+      put(P.blocks.data(), P.blocks.size() * sizeof(sgla::BlockEntry), P.blkt_off);
+      put(P.scans.data(), P.scans.size() * sizeof(sgla::ScanEntry), P.scnt_off);
+      st = upload_words(region, ws + P.segt_off, stream);
+      if (st != SGLA_OK) return st;
+    }
+    sgla::SegmentParams sp;
+    sp.k = k;
+    sp.v = v;
+    sp.g = g;
+    sp.g_gamma = g_gamma;
+    sp.h0 = initial_state;
+    sp.H = a.H;
+    sp.Hkv = P.Hkv;
+    sp.K = a.K;
+    sp.V = a.V;
+    sp.sl = state_layout(a);
+    sp.blocks = reinterpret_cast<const sgla::BlockEntry*>(ws + P.blkt_off);
+    sp.num_blocks = (int32_t)P.blocks.size();
+    sp.scans = reinterpret_cast<const sgla::ScanEntry*>(ws + P.scnt_off);
+    sp.num_scans = (int32_t)P.scans.size();
+    sp.urec = reinterpret_cast<float*>(ws + P.urec_off);
+    sp.ulog = reinterpret_cast<float*>(ws + P.ulog_off);
+    sp.sin = reinterpret_cast<float*>(ws + P.sin_off);
+    e = sgla::launch_segment_states(sp, stream);
+    if (e != hipSuccess) return hip_fail(e, "launching the segment state passes");
+    p.segs = reinterpret_cast<const sgla::SegEntry*>(ws + P.segt_off);
+    p.bins = reinterpret_cast<const sgla::BinEntry*>(ws + P.bint_off);
+    p.num_bins = (int32_t)P.bins.size();
+    p.sin = sp.sin;
+  }
   if (P.chunk_size != sgla::kChunk) {
     e = sgla::launch_chunk_fwd_small(p, P.chunk_size, a.qkv_dtype == SGLA_BF16, stream);
   } else if (P.prep) {

@@ -82,6 +82,70 @@ struct SeqLayout {
   int32_t num_chunks;        // total chunks over all sequences
 };
 
+// Segments of long sequences (bf16 K <= 128 forward).  A sequence whose
+// chain of 64-token chunks is long compared with the work the launch has for
+// the rest of the GPU is cut at chunk boundaries into segments processed in
+// parallel, each from its own initial state: segment 0 from the sequence's
+// initial state, segment s > 0 from the state after segment s - 1.  Those
+// entering states come from a state-only pass over the earlier segments
+// (per block of chunks: the state each block adds from a zero start, and the
+// block's total log2 decay) followed by a scan over the blocks.
+struct SegEntry {
+  int32_t bos;     // first packed token of the segment
+  int32_t len;     // tokens
+  int32_t seq;     // sequence index (initial_state / final_state row)
+  int32_t init;    // -1: start from the sequence's initial state; else entering-state record
+  int32_t last;    // 1: the sequence's last segment (writes final_state)
+  int32_t pad[3];
+};
+// The segments one chunk workgroup processes in turn: rows [first, first +
+// count) of the segment table.
+struct BinEntry {
+  int32_t first;
+  int32_t count;
+};
+struct BlockEntry {
+  int32_t t0;       // first packed token of the block
+  int32_t len;      // tokens (a whole number of chunks, except a sequence's last)
+  int32_t out_rec;  // after this block the scan writes entering-state record out_rec (-1: none)
+  int32_t pad;
+};
+struct ScanEntry {
+  int32_t seq;          // sequence index
+  int32_t first_block;  // its blocks are [first_block, first_block + num_blocks)
+  int32_t num_blocks;
+  int32_t pad;
+};
+
+// Raw words carried by value in one table_words launch and written at
+// dst[first, first + count).
+constexpr int kTableWords = 500;
+struct TableWords {
+  int32_t first;
+  int32_t count;
+  uint32_t w[kTableWords];
+};
+hipError_t launch_table_words(const TableWords& put, uint32_t* dst, hipStream_t stream);
+
+struct SegmentParams {
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* g_gamma;
+  const float* h0;            // [N, H, K, V] (layout sl) or nullptr
+  int32_t H, Hkv, K, V;
+  StateLayout sl;
+  const BlockEntry* blocks;
+  int32_t num_blocks;
+  const ScanEntry* scans;
+  int32_t num_scans;
+  float* urec;                // [num_blocks, H, K, V]: state added by each block from a zero start
+  float* ulog;                // [num_blocks, H]: each block's total log2 decay
+  float* sin;                 // [records, H, K, V]: entering state of each later segment
+};
+// state-only pass over the blocks, then the scan writing the entering states
+hipError_t launch_segment_states(const SegmentParams& p, hipStream_t stream);
+
 // Per-(chunk, head) outputs of the preparation kernel (wide-key bf16 path):
 // kGateStride floats of gates [sc[64], dv[64], dall, pad] and a [2][64][64]
 // bf16 hi/lo pair of the decay-masked, scaled q k^T, plus the chunk's Q and
@@ -120,6 +184,12 @@ struct ChunkFwdParams {
   const void* amat;
   const void* ktf;
   const void* qfr;
+  // segmented chains (bf16 K <= 128): one workgroup per bin of segments
+  // instead of per sequence; nullptr = one workgroup per sequence
+  const SegEntry* segs = nullptr;
+  const BinEntry* bins = nullptr;
+  int32_t num_bins = 0;
+  const float* sin = nullptr;  // [records, H, K, V] entering states of later segments
 };
 
 // chunk_size: a power of two <= kChunk (the scan restarts inside each
@@ -128,8 +198,10 @@ hipError_t launch_gate_cumsum(const float* g, float* gc, int32_t H, const SeqLay
                               int32_t chunk_size, hipStream_t stream);
 
 // bf16 q/k/v, MFMA path, whole key dimension per chunk step.  K in {64,128},
-// V % 64 == 0.
+// V % 64 == 0; one workgroup per (sequence or segment, head, V tile of
+// chunk_fwd_bf16_vtile(V) columns).
 hipError_t launch_chunk_fwd_bf16(const ChunkFwdParams& p, hipStream_t stream);
+int chunk_fwd_bf16_vtile(int32_t V);
 
 // Wide-key bf16 path (K in {256,512}, V % 32 == 0): per-(chunk, head)
 // preparation, then the state and output passes reading its results.

@@ -1,5 +1,6 @@
-// Packed-sequence tables written into the workspace by kernels whose payload
-// travels in the kernel arguments.  The host builds the sequence table
+// Tables written into the workspace by kernels whose payload travels in the
+// kernel arguments (the packed-sequence tables; the segment, block and scan
+// tables of segmented chains).  The host builds the sequence table
 // (longest sequence first); each launch carries up to kTablePut entries by
 // value, so no host buffer has to outlive the call and nothing is copied
 // from pageable memory.  The same launch expands every entry it carries into
@@ -31,7 +32,18 @@ table_put_kernel(TablePut put, SeqEntry* __restrict__ seq_table, ChunkEntry* __r
   }
 }
 
+// Raw words: thread i of the launch writes word i of the payload.
+__global__ void __launch_bounds__(256) table_words_kernel(TableWords put, uint32_t* __restrict__ dst) {
+  for (int i = threadIdx.x; i < put.count; i += 256) dst[put.first + i] = put.w[i];
+}
+
 }  // namespace
+
+hipError_t launch_table_words(const TableWords& put, uint32_t* dst, hipStream_t stream) {
+  if (put.count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(table_words_kernel, dim3(1), dim3(256), 0, stream, put, dst);
+  return hipGetLastError();
+}
 
 hipError_t launch_table_put(const TablePut& put, SeqEntry* seq_table, ChunkEntry* chunk_table,
                             hipStream_t stream) {

@@ -716,3 +716,51 @@ def test_back_to_back_varlen_calls():
     torch.cuda.synchronize()
     for inp, o, ht, _, _ in runs:
         check_full(inp, o.cpu().numpy(), ht.cpu().numpy())
+
+
+# ---------------------------------------------------------------------------
+# segmented chains: long sequences with little other work are cut into
+# segments that run in parallel from entering states computed by a
+# state-only pass and a scan (bf16, K <= 128)
+# ---------------------------------------------------------------------------
+
+SEGMENT_CASES = [
+    small("seg_dense_g", B=1, T=3000, H=2, K=128, V=64),
+    small("seg_dense_h0_gamma", B=2, T=2500, H=1, K=128, V=128, gate="gamma", normalize_k=True,
+          initial_state=True),
+    small("seg_k64_no_gate", B=1, T=2100, H=1, K=64, V=64, gate="none", initial_state=True),
+    small("seg_packed", B=1, T=0, H=2, K=128, V=64, fixed_lengths=(15, 2100, 1, 1500, 0, 64),
+          initial_state=True),
+    small("seg_gqa", B=1, T=2200, H=4, Hkv=2, K=128, V=64, initial_state=True),
+    small("seg_strong_gate", B=1, T=2048, H=1, K=64, V=128, gate_normalizer=0.1, scale=0.1),
+]
+
+
+@pytest.mark.parametrize("w", SEGMENT_CASES, ids=lambda w: w.name)
+def test_segmented_chains(w):
+    inp = make_chunk_inputs(w)
+    o, ht = run_chunk(inp, output_final_state=True)
+    check_full(inp, o, ht)
+    o2, ht2 = run_chunk(inp, output_final_state=True)
+    assert np.array_equal(o, o2) and np.array_equal(ht, ht2)   # deterministic
+
+
+@pytest.mark.parametrize("kind", ["forget", "resets"])
+def test_segmented_degenerate_gates(kind):
+    inp = make_chunk_inputs(small(f"segdeg_{kind}", B=1, T=2500, H=1, K=128, V=64, initial_state=True))
+    inp["g"] = _reset_gates(inp, kind)
+    o, ht = run_chunk(inp, output_final_state=True)
+    check_full(inp, o, ht)
+
+
+def test_segmented_state_v_first():
+    inp = make_chunk_inputs(small("seg_vf", B=1, T=2300, H=2, K=128, V=64, initial_state=True, seed=8))
+    d = device_inputs(inp)
+    kw = dict(g=d["g"], scale=inp["scale"], output_final_state=True)
+    o1, h1 = sgla.chunk_fwd(d["q"], d["k"], d["v"], initial_state=d["initial_state"], **kw)
+    o2, h2 = sgla.chunk_fwd(d["q"], d["k"], d["v"],
+                            initial_state=d["initial_state"].transpose(-1, -2).contiguous(),
+                            state_v_first=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1.transpose(-1, -2), h2)
+    check_full(inp, o1.cpu().numpy(), h1.cpu().numpy())
