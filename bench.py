@@ -31,6 +31,7 @@ The JSON line also carries:
                    128 x 128 fp32 state, 64 consecutive steps, HBM GB/s;
   backward      -- sgla_chunk_bwd on the packed K = V = 128 workload (dq, dk,
                    dv, dg, dh0);
+  backward_wide -- sgla_chunk_bwd on the dense K = V = 512 workload;
   normalizer    -- sgla_chunk_normalizer on the same workload, HBM GB/s;
   gla           -- sgla_gla_chunk_fwd (per-key gates) on the same workload;
   parallel      -- sgla_parallel_fwd with the decayed attention matrix;
@@ -394,7 +395,9 @@ def bwd_algorithmic(inp) -> tuple[float, float]:
 
 def bench_backward(workload: str, steps: int, warmup: int, warm_seconds: float):
     """sgla_chunk_bwd (dq, dk, dv, dg or dg_gamma, dh0) on a chunked workload.
-    bf16 inputs with K in {64, 128} run both passes on the bf16 matrix cores;
+    bf16 inputs with K in {64, 128, 256, 512} run both passes on the bf16
+    matrix cores (K > 128: key-tiled state pass and dq/dk kernel, then the
+    dv kernel over all keys and the gate kernel);
     at their algorithmic intensity (about 78 flop/B at K = V = 128), far
     below the bf16 ridge, the call is priced against HBM with its
     algorithmic bytes (the per-chunk state records the state pass writes and
@@ -458,7 +461,8 @@ def bench_backward(workload: str, steps: int, warmup: int, warm_seconds: float):
     nbytes, flops = bwd_algorithmic(inp)
     tf = flops / (ms * 1e-3) / 1e12
     gbs = nbytes / (ms * 1e-3) / 1e9
-    bf16_path = inp["dtype"] == "bf16" and K in (64, 128)
+    bf16_path = inp["dtype"] == "bf16" and K in (64, 128, 256, 512)
+    wide = bf16_path and K > 128
     if bf16_path:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4)}
@@ -467,15 +471,20 @@ def bench_backward(workload: str, steps: int, warmup: int, warm_seconds: float):
                 "unit": "TFLOP/s", "frac": round(tf / F32_MFMA_PEAK_TFLOPS, 4), "dtype": "f32"}
     kern = ("chunk_bwd_state_bf16_kernel+chunk_bwd_grad_bf16_kernel" if bf16_path
             else "chunk_bwd_state_kernel+chunk_bwd_grad_kernel")
+    if wide:
+        kern += "+chunk_bwd_dv_wide_kernel" + ("+chunk_bwd_gate_wide_kernel" if g is not None or gg is not None
+                                               else "")
     n_chunks = sum(-(-int(L) // 64) for L in (np.diff(inp["cu_seqlens"]) if inp["cu_seqlens"] is not None
                                                  else [T] * B))
     return {"workload": workload, "B": B, "T": T, "H": H, "K": K, "V": V, "num_seqs": N,
             "kernel": kern,
-            "launches_per_call": 2 + (1 if gg is not None else 0),
+            "launches_per_call": len(kern.split("+")) + (1 if gg is not None else 0),
             "ms_per_call_mean": round(ms, 5), "ms_per_call_median": round(per[len(per) // 2], 5),
             "tokens_per_s": round(B * T / (ms * 1e-3), 1),
             "algorithmic_flops_per_call": int(flops), "algorithmic_bytes_per_call": int(nbytes),
-            "state_record_bytes_per_call": int(2 * 2 * n_chunks * H * K * V * 4),
+            # written once each, read by the gradient kernel, dH once more by
+            # the wide dv kernel
+            "state_record_bytes_per_call": int((5 if wide else 4) * n_chunks * H * K * V * 4),
             "roofline": roof,
             "mfma": {"achieved_tflops": round(tf, 2),
                      "peak_tflops": BF16_MFMA_PEAK_TFLOPS if bf16_path else F32_MFMA_PEAK_TFLOPS,
@@ -784,6 +793,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--backward-workload", default="varlen_bf16_k128",
                     help="workload of the backward timing (K <= 128)")
+    ap.add_argument("--backward-wide-workload", default="dense_bf16_k512",
+                    help="workload of the wide-key backward timing (K = 256 or 512)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (CPU timing and the parity of every record)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -847,6 +858,7 @@ def main():
     if not a.no_backward and not a.only_headline:
         print("[bench] backward, normalizer, GLA, parallel form", file=sys.stderr, flush=True)
         out["backward"] = bench_backward(a.backward_workload, 20, a.warmup, a.warm_seconds)
+        out["backward_wide"] = bench_backward(a.backward_wide_workload, 10, a.warmup, a.warm_seconds)
         out["normalizer"] = bench_normalizer(a.backward_workload, 20, a.warmup, a.warm_seconds)
         out["gla"] = bench_gla(a.backward_workload, 20, a.warmup, a.warm_seconds)
         out["parallel"] = bench_parallel("parallel_bf16_k128", 10, a.warmup, a.warm_seconds)

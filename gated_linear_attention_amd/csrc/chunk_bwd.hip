@@ -32,9 +32,9 @@
 //
 // The kernels below run every product on the fp32 matrix cores
 // (v_mfma_f32_16x16x4_f32), so inputs are used exactly and states, gradients
-// and accumulation are fp32; they serve float32 inputs and K in {16, 32}.
-// bf16 inputs with K in {64, 128} take the bf16-matrix-core passes of
-// chunk_bwd_bf16.hip instead.
+// and accumulation are fp32; they serve float32 inputs and bf16 inputs with
+// K in {16, 32}.  bf16 inputs with K in {64, 128, 256, 512} take the
+// bf16-matrix-core passes of chunk_bwd_bf16.hip instead.
 // Operand layout, per lane l with g = l / 16 and r = l % 16:
 //   A operand A[m = r][k = g], B operand B[k = g][n = r],
 //   result acc[i] = D[m = 4 g + i][n = r].
@@ -554,49 +554,44 @@ kv_group_sum_kernel(const float* __restrict__ src, float* __restrict__ dst, int6
 }
 
 template <int K, typename TIn>
-hipError_t launch_k(const ChunkBwdParams& p, hipStream_t stream) {
-  const int per_row = p.seqs.T > 0 ? (p.seqs.T + C - 1) / C : 1;
+hipError_t launch_k(const ChunkBwdParams& p, int32_t per_row, hipStream_t stream) {
   const TIn* q = static_cast<const TIn*>(p.q);
   const TIn* k = static_cast<const TIn*>(p.k);
   const TIn* v = static_cast<const TIn*>(p.v);
   const TIn* dout = static_cast<const TIn*>(p.dout);
-  if (p.seqs.num_seqs > 0 && bwd_bf16_grad(sizeof(TIn) == 2, K)) {
-    const hipError_t e = launch_chunk_bwd_state_bf16(p, per_row, stream);
-    if (e != hipSuccess) return e;
-  } else if (p.seqs.num_seqs > 0) {
+  if (p.seqs.num_seqs > 0) {
     const int units = (int)unit_grid(p.seqs.num_seqs, p.H, 1, p.V / VT);
     hipLaunchKernelGGL((chunk_bwd_state_kernel<K, TIn>), dim3((unsigned)(2 * units)), dim3(NT), 0, stream,
                        q, k, v, dout, p.g, p.g_gamma, p.h0, p.dht, p.dh0, p.scale, p.H, p.Hkv, p.V, p.sl,
                        p.seqs, per_row, p.hbuf, p.dhbuf);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (p.seqs.num_chunks > 0 && bwd_bf16_grad(sizeof(TIn) == 2, K)) {
-    const hipError_t e = launch_chunk_bwd_grad_bf16(p, per_row, stream);
-    if (e != hipSuccess) return e;
-  } else if (p.seqs.num_chunks > 0) {
+  if (p.seqs.num_chunks > 0) {
     hipLaunchKernelGGL((chunk_bwd_grad_kernel<K, TIn>), dim3((unsigned)p.seqs.num_chunks, (unsigned)p.H),
                        dim3(NTG), 0, stream, q, k, v, dout, p.g, p.g_gamma, p.scale, p.H, p.Hkv, p.V, p.seqs,
                        per_row, p.hbuf, p.dhbuf, p.dq, p.dk, p.dv, p.dg,
                        p.dg_gamma != nullptr ? p.gpart : nullptr);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (p.dg_gamma != nullptr) {
-    hipLaunchKernelGGL(chunk_bwd_gamma_kernel, dim3((unsigned)p.H), dim3(NT), 0, stream, p.gpart,
-                       p.seqs.num_chunks, p.H, p.dg_gamma);
     return hipGetLastError();
   }
   return hipSuccess;
 }
 
-template <typename TIn>
-hipError_t launch_in(const ChunkBwdParams& p, hipStream_t stream) {
+// The fp32-matrix-core passes: float32 inputs (K <= 128) and bf16 inputs
+// with K in {16, 32}.
+hipError_t launch_fp32_passes(const ChunkBwdParams& p, int32_t per_row, hipStream_t stream) {
+  if (p.qkv_bf16) {
+    switch (p.K) {
+      case 16: return launch_k<16, __bf16>(p, per_row, stream);
+      case 32: return launch_k<32, __bf16>(p, per_row, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (p.K) {
-    case 16: return launch_k<16, TIn>(p, stream);
-    case 32: return launch_k<32, TIn>(p, stream);
-    case 64: return launch_k<64, TIn>(p, stream);
-    case 128: return launch_k<128, TIn>(p, stream);
+    case 16: return launch_k<16, float>(p, per_row, stream);
+    case 32: return launch_k<32, float>(p, per_row, stream);
+    case 64: return launch_k<64, float>(p, per_row, stream);
+    case 128: return launch_k<128, float>(p, per_row, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -614,7 +609,20 @@ hipError_t launch_kv_group_sum(const float* src, float* dst, int64_t tokens, int
 }
 
 hipError_t launch_chunk_bwd(const ChunkBwdParams& p, hipStream_t stream) {
-  return p.qkv_bf16 ? launch_in<__bf16>(p, stream) : launch_in<float>(p, stream);
+  const int32_t per_row = p.seqs.T > 0 ? (p.seqs.T + C - 1) / C : 1;
+  hipError_t e;
+  if (bwd_bf16_grad(p.qkv_bf16 != 0, p.K)) {
+    e = launch_chunk_bwd_state_bf16(p, per_row, stream);
+    if (e == hipSuccess) e = launch_chunk_bwd_grad_bf16(p, per_row, stream);
+  } else {
+    e = launch_fp32_passes(p, per_row, stream);
+  }
+  if (e == hipSuccess && p.dg_gamma != nullptr) {
+    hipLaunchKernelGGL(chunk_bwd_gamma_kernel, dim3((unsigned)p.H), dim3(NT), 0, stream, p.gpart,
+                       p.seqs.num_chunks, p.H, p.dg_gamma);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace sgla

@@ -1,6 +1,6 @@
 // The chunked Simple GLA backward on the bf16 matrix cores, for bf16 q, k, v
-// and dO with K in {64, 128}: the state pass (further below) and the
-// per-(chunk, head) gradients (page
+// and dO with K in {64, 128, 256, 512}: the state pass (further below) and
+// the per-(chunk, head) gradients (page
 // "flash-linear-attention 中的 Simple GLA", section 三: the backward's
 // q/k/gate and v gradient passes over the fp32 state trajectory; section 五:
 // dq, dk, dv, dg).  The algebra is the fp32 gradient kernel's
@@ -21,10 +21,19 @@
 //
 // 8 waves (two per SIMD).  Wave w works on row tile rw = w % 4 (tokens
 // [16 rw, +16)) and half kh = w / 4: A and dA column tiles {2 kh, 2 kh + 1},
-// dQ and dK key tiles [kh K/32, +K/32), dV columns [16 kh, +16) of each
+// dQ and dK key tiles [kh KT/32, +KT/32), dV columns [16 kh, +16) of each
 // 32-column V slice.  V is walked in 32-column slices, each loaded one slice
 // ahead; operands reduced over tokens come from LDS through the transposing
 // read ds_read_b64_tr_b16.
+//
+// Keys beyond 128 (K = 256, 512): every dQ and dK column depends on the keys
+// only through A and through its own key column, so one workgroup per
+// (chunk, head, 128-key tile) runs the same kernel on its key tile (dA is a
+// reduction over V and each tile forms it itself) and leaves its share of
+// the gate terms in a partial record; dV, which sums over all keys, comes
+// from chunk_bwd_bf16_wide.hip, as does the gate gradient from the partials.
+// The state pass splits the keys the same way: the rows of the state and of
+// its gradient evolve independently.
 #include <hip/hip_runtime.h>
 
 #include "gate_scan.h"
@@ -78,21 +87,26 @@ __device__ __forceinline__ void put_split(bf16* plane, int i, int lo_off, float 
   plane[i + lo_off] = (bf16)(x - (float)hi);
 }
 
-template <int K>
+// KT keys per workgroup.  WIDE = false: KT = K, the whole chunk's
+// gradients.  WIDE = true: K > KT; workgroup (chunk, head, key tile kz) of
+// map_unit writes dq and dk of keys [kz KT, +KT) and its gate partial record
+// wpart[(chunk H + head) (K / KT) + kz] = {r_c (64), dv_c k_c . (V dH^T)_c (64),
+// <dH, h> over its key rows}; A and dV are left to the wide dV kernel.
+template <int KT, bool WIDE>
 __global__ void __launch_bounds__(NTG)
 chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                            const bf16* __restrict__ v, const bf16* __restrict__ dout,
                            const float* __restrict__ g, const float* __restrict__ g_gamma, float scale,
-                           int32_t H, int32_t Hkv, int32_t V, SeqLayout seqs, int32_t chunks_per_row,
+                           int32_t H, int32_t Hkv, int32_t K, int32_t V, SeqLayout seqs, int32_t chunks_per_row,
                            const float* __restrict__ hbuf, const float* __restrict__ dhbuf,
                            float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
-                           float* __restrict__ dg, float* __restrict__ gpart) {
-  using L = GradLayout<K>;
+                           float* __restrict__ dg, float* __restrict__ gpart, float* __restrict__ wpart) {
+  using L = GradLayout<KT>;
   constexpr int LDQ = L::LDQ;
-  constexpr int NKT = K / 16;          // 16-key tiles of dQ / dK
+  constexpr int NKT = KT / 16;         // 16-key tiles of dQ / dK
   constexpr int NKH = NKT / 2;         // per wave
-  constexpr int KSTEP = K / 32;        // 32-deep steps over the keys
-  static_assert(NKH >= 2 && KSTEP >= 2, "K");
+  constexpr int KSTEP = KT / 32;       // 32-deep steps over the keys
+  static_assert(NKH >= 2 && KSTEP >= 2, "KT");
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   bf16* const sQ = reinterpret_cast<bf16*>(smem + L::OFF_Q);
   bf16* const sK = reinterpret_cast<bf16*>(smem + L::OFF_K);
@@ -108,10 +122,22 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
   float* const sKs = sb + 5 * C;       // [2][C]
   float* const sFrob = sb + 7 * C;     // [8]
   constexpr int ALO = C * LDA;         // offset of the lo planes
-  constexpr int HLO = K * LDS_;
+  constexpr int HLO = KT * LDS_;
 
-  const int gc = blockIdx.x;
-  const int hd = blockIdx.y;
+  int gc, hd, kz = 0;
+  if constexpr (WIDE) {
+    // the key tiles of one (chunk, head) run on one XCD, whose L2 then
+    // serves their repeated reads of V and dO
+    const UnitMap um = map_unit((int32_t)blockIdx.x, K / KT, H, 1, seqs.num_chunks);
+    if (!um.valid) return;
+    gc = um.rank;
+    hd = um.hk;
+    kz = um.vt;
+  } else {
+    gc = blockIdx.x;
+    hd = blockIdx.y;
+  }
+  const int kb = kz * KT;              // first key of the tile
   int64_t t0;
   int cl;
   if (seqs.chunk_table != nullptr) {
@@ -131,12 +157,12 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
   const int hk = hd / (H / Hkv);   // kv head whose k and v rows this query head reads
   const int64_t RSV = (int64_t)H * V, RKV = (int64_t)Hkv * V;   // dout and v row strides
   const int64_t KV = (int64_t)K * V;
-  const float* hu = hbuf + ((int64_t)gc * H + hd) * KV;
-  const float* dhu = dhbuf + ((int64_t)gc * H + hd) * KV;
+  const float* hu = hbuf + ((int64_t)gc * H + hd) * KV + (int64_t)kb * V;
+  const float* dhu = dhbuf + ((int64_t)gc * H + hd) * KV + (int64_t)kb * V;
 
-  // ---- Q and K rows (zero past the chunk's end) and the gates --------------
+  // ---- Q and K rows of the key tile (zero past the chunk's end) and the gates
   {
-    constexpr int PR = K / 8;                 // 16-byte pieces per row
+    constexpr int PR = KT / 8;                // 16-byte pieces per row
     constexpr int NPC = C * PR / NTG;
     static_assert(NPC * NTG == C * PR, "staging split");
     uint4 qx[NPC], kx[NPC];
@@ -147,8 +173,8 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
       qx[u] = make_uint4(0u, 0u, 0u, 0u);
       kx[u] = make_uint4(0u, 0u, 0u, 0u);
       if (c < cl) {
-        qx[u] = *reinterpret_cast<const uint4*>(q + ((t0 + c) * H + hd) * K + e);
-        kx[u] = *reinterpret_cast<const uint4*>(k + ((t0 + c) * Hkv + hk) * K + e);
+        qx[u] = *reinterpret_cast<const uint4*>(q + ((t0 + c) * H + hd) * K + kb + e);
+        kx[u] = *reinterpret_cast<const uint4*>(k + ((t0 + c) * Hkv + hk) * K + kb + e);
       }
     }
 #pragma unroll
@@ -173,7 +199,7 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
   //      4-float pieces, loaded one slice ahead --------------------------------
   constexpr int PVS = C * (VS / 4);
   constexpr int NVS = PVS / NTG;
-  constexpr int PHS = K * (VS / 4);
+  constexpr int PHS = KT * (VS / 4);
   constexpr int NHS = PHS / NTG;
   static_assert(NVS * NTG == PVS && NHS * NTG == PHS, "slice split");
   uint2 vx[NVS], ox[NVS];
@@ -228,7 +254,7 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
 
   // ---- A = scale (Q K^T) (.) M: row tile rw against column tiles 2 kh,
   //      2 kh + 1 (tiles above the diagonal come out as zeros) -----------------
-  {
+  if constexpr (!WIDE) {
     f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int s = 0; s < KSTEP; ++s) {
@@ -285,7 +311,7 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
       }
     }
     // dV rows [16 rw, +16), columns [16 kh, +16) of the slice
-    {
+    if constexpr (!WIDE) {
       f32x4 in = {0.f, 0.f, 0.f, 0.f}, st = in;
       for (int cs = cs0; cs < 2; ++cs) {
         const int c0 = 32 * cs + 8 * g4;
@@ -365,8 +391,8 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
       rk[i] += kv * xk;
       ks4[i] += kv * dKs[t][i];
       if (c < cl) {
-        dq[((t0 + c) * H + hd) * (int64_t)K + col] = xq;
-        dk[((t0 + c) * H + hd) * (int64_t)K + col] = xk;
+        dq[((t0 + c) * H + hd) * (int64_t)K + kb + col] = xq;
+        dk[((t0 + c) * H + hd) * (int64_t)K + kb + col] = xk;
       }
     }
   }
@@ -387,6 +413,21 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
   }
   __syncthreads();
 
+  if constexpr (WIDE) {
+    // the tile's gate terms, reduced over key tiles by the wide gate kernel
+    if (w == 0) {
+      float* rec = wpart + (((int64_t)gc * H + hd) * (K / KT) + kz) * kWidePart;
+      rec[lane] = sR[lane] + sR[C + lane];
+      rec[C + lane] = sKs[lane] + sKs[C + lane];
+      if (lane == 0) {
+        float frob_all = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) frob_all += sFrob[i];
+        rec[2 * C] = frob_all;
+      }
+    }
+    return;
+  }
   // ---- gate gradient: reverse cumulative sum over the chunk ---------------
   if (w == 0) {
     float frob_all = 0.f;
@@ -421,24 +462,25 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
 // recurrence dH <- dall dH + Q^T diag(sc) dO from dht and stores the gradient
 // of the state leaving every chunk, then dh0.  K (Q) is an exact bf16
 // operand; the weighted V (dO) is split into bf16 hi + lo planes once per
-// chunk in LDS.  4 waves; wave w owns state rows [w K/4, +K/4) of the tile's
-// 32 columns as 16 x 16 fp32 accumulators.
+// chunk in LDS.  A workgroup covers KT state rows (key tile kz: rows
+// [kz KT, +KT), KT = K up to 256) and 32 columns; 4 waves, wave w owns rows
+// [w KT/4, +KT/4) of the tile as 16 x 16 fp32 accumulators.
 // ---------------------------------------------------------------------------
 constexpr int NTS = 256;        // state-pass threads (4 waves)
 constexpr int LDY = VS + 8;     // V / dO tile row stride (elements)
 
-template <int K>
+template <int KT>
 __global__ void __launch_bounds__(NTS)
 chunk_bwd_state_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                             const bf16* __restrict__ v, const bf16* __restrict__ dout,
                             const float* __restrict__ g, const float* __restrict__ g_gamma,
                             const float* __restrict__ h0, const float* __restrict__ dht,
-                            float* __restrict__ dh0, float scale, int32_t H, int32_t Hkv, int32_t V,
-                            StateLayout sl, SeqLayout seqs, int32_t chunks_per_row, float* __restrict__ hbuf,
-                            float* __restrict__ dhbuf) {
-  constexpr int LDX = K + 16;          // K / Q row stride (elements)
-  constexpr int RT = K / 64;           // 16-row state tiles per wave (K/4 rows)
-  constexpr int PRX = K / 8;           // 16-byte pieces per K / Q row
+                            float* __restrict__ dh0, float scale, int32_t H, int32_t Hkv, int32_t K,
+                            int32_t V, StateLayout sl, SeqLayout seqs, int32_t chunks_per_row,
+                            float* __restrict__ hbuf, float* __restrict__ dhbuf) {
+  constexpr int LDX = KT + 16;         // K / Q row stride (elements)
+  constexpr int RT = KT / 64;          // 16-row state tiles per wave (KT/4 rows)
+  constexpr int PRX = KT / 8;          // 16-byte pieces per K / Q row
   constexpr int NX = C * PRX / NTS;    // per thread
   constexpr int PY = C * (VS / 8);     // 16-byte pieces of the V / dO tile (256)
   static_assert(NX * NTS == C * PRX && PY == NTS && RT >= 1, "staging split");
@@ -452,9 +494,10 @@ chunk_bwd_state_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__
   // the longest units start both at once
   const bool rev = (blockIdx.x & 1) != 0;
   const int bid = (int)(blockIdx.x >> 1);
-  const UnitMap um = map_unit(bid, V / VS, H, 1, seqs.num_seqs);
+  const int nvt = V / VS;
+  const UnitMap um = map_unit(bid, nvt * (K / KT), H, 1, seqs.num_seqs);
   if (!um.valid) return;
-  const int hd = um.hd, vt = um.vt;
+  const int hd = um.hd, kz = um.vt / nvt, vt = um.vt - kz * nvt;
   const int hk = hd / (H / Hkv);   // kv head whose k and v rows this query head reads
   int64_t bos;
   int32_t len, seq, chunk0;
@@ -473,7 +516,7 @@ chunk_bwd_state_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__
   const int nchunks = (len + C - 1) / C;
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
-  const int krow0 = w * (K / 4);
+  const int krow0 = kz * KT + w * (KT / 4);
   const int64_t KV = (int64_t)K * V;
   const int64_t ucol = (int64_t)vt * VS;
 
@@ -497,7 +540,7 @@ chunk_bwd_state_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__
   uint4 xx[NX], yx;
   float gx = 0.f;
   // reverse: q and dout rows of the query head; forward: k and v rows of its kv head
-  const bf16* xsrc = rev ? q + hd * K : k + hk * K;
+  const bf16* xsrc = (rev ? q + hd * K : k + hk * K) + kz * KT;
   const bf16* ysrc = rev ? dout + hd * V : v + hk * V;
   const int64_t xrs = (int64_t)(rev ? H : Hkv) * K, yrs = (int64_t)(rev ? H : Hkv) * V;
   auto load_chunk = [&](int it) {
@@ -581,8 +624,9 @@ chunk_bwd_state_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__
       }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        // A operand: X^T[krow0 + 16 rt + r][c0 + e]
-        const bf16x8 a = cat(tr_read(sX, LDX, c0, krow0 + 16 * rt), tr_read(sX, LDX, c0 + 4, krow0 + 16 * rt));
+        // A operand: X^T[key krow0 + 16 rt + r][token c0 + e]
+        const int xc = w * (KT / 4) + 16 * rt;   // the tile's key column in sX
+        const bf16x8 a = cat(tr_read(sX, LDX, c0, xc), tr_read(sX, LDX, c0 + 4, xc));
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           hs[rt][ct] = mfma(a, bh[ct], hs[rt][ct]);
@@ -604,23 +648,26 @@ chunk_bwd_state_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__
   }
 }
 
-template <int K>
+template <int KT, bool WIDE>
 hipError_t launch_grad_k(const ChunkBwdParams& p, int32_t chunks_per_row, hipStream_t stream) {
-  hipLaunchKernelGGL((chunk_bwd_grad_bf16_kernel<K>), dim3((unsigned)p.seqs.num_chunks, (unsigned)p.H),
-                     dim3(NTG), 0, stream, static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
+  const dim3 grid = WIDE ? dim3((unsigned)unit_grid(p.seqs.num_chunks, p.H, 1, p.K / KT))
+                         : dim3((unsigned)p.seqs.num_chunks, (unsigned)p.H);
+  hipLaunchKernelGGL((chunk_bwd_grad_bf16_kernel<KT, WIDE>), grid, dim3(NTG), 0, stream,
+                     static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
                      static_cast<const bf16*>(p.v), static_cast<const bf16*>(p.dout), p.g, p.g_gamma,
-                     p.scale, p.H, p.Hkv, p.V, p.seqs, chunks_per_row, p.hbuf, p.dhbuf, p.dq, p.dk, p.dv, p.dg,
-                     p.dg_gamma != nullptr ? p.gpart : nullptr);
+                     p.scale, p.H, p.Hkv, p.K, p.V, p.seqs, chunks_per_row, p.hbuf, p.dhbuf, p.dq, p.dk, p.dv,
+                     p.dg, p.dg_gamma != nullptr ? p.gpart : nullptr, p.wpart);
   return hipGetLastError();
 }
 
-template <int K>
+template <int KT>
 hipError_t launch_state_k(const ChunkBwdParams& p, int32_t chunks_per_row, hipStream_t stream) {
-  const int units = (int)unit_grid(p.seqs.num_seqs, p.H, 1, p.V / VS);
-  hipLaunchKernelGGL((chunk_bwd_state_bf16_kernel<K>), dim3((unsigned)(2 * units)), dim3(NTS), 0, stream,
+  const int units = (int)unit_grid(p.seqs.num_seqs, p.H, 1, (p.V / VS) * (p.K / KT));
+  hipLaunchKernelGGL((chunk_bwd_state_bf16_kernel<KT>), dim3((unsigned)(2 * units)), dim3(NTS), 0, stream,
                      static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k),
                      static_cast<const bf16*>(p.v), static_cast<const bf16*>(p.dout), p.g, p.g_gamma, p.h0,
-                     p.dht, p.dh0, p.scale, p.H, p.Hkv, p.V, p.sl, p.seqs, chunks_per_row, p.hbuf, p.dhbuf);
+                     p.dht, p.dh0, p.scale, p.H, p.Hkv, p.K, p.V, p.sl, p.seqs, chunks_per_row, p.hbuf,
+                     p.dhbuf);
   return hipGetLastError();
 }
 
@@ -629,13 +676,27 @@ hipError_t launch_state_k(const ChunkBwdParams& p, int32_t chunks_per_row, hipSt
 hipError_t launch_chunk_bwd_state_bf16(const ChunkBwdParams& p, int32_t chunks_per_row, hipStream_t stream) {
   if (!bwd_bf16_grad(p.qkv_bf16 != 0, p.K) || p.V % VS != 0) return hipErrorInvalidValue;
   if (p.seqs.num_seqs == 0) return hipSuccess;
-  return p.K == 64 ? launch_state_k<64>(p, chunks_per_row, stream) : launch_state_k<128>(p, chunks_per_row, stream);
+  switch (p.K) {
+    case 64: return launch_state_k<64>(p, chunks_per_row, stream);
+    case 128: return launch_state_k<128>(p, chunks_per_row, stream);
+    default: return launch_state_k<256>(p, chunks_per_row, stream);   // K = 256, 512
+  }
 }
 
 hipError_t launch_chunk_bwd_grad_bf16(const ChunkBwdParams& p, int32_t chunks_per_row, hipStream_t stream) {
   if (!bwd_bf16_grad(p.qkv_bf16 != 0, p.K) || p.V % VS != 0) return hipErrorInvalidValue;
   if (p.seqs.num_chunks == 0) return hipSuccess;
-  return p.K == 64 ? launch_grad_k<64>(p, chunks_per_row, stream) : launch_grad_k<128>(p, chunks_per_row, stream);
+  switch (p.K) {
+    case 64: return launch_grad_k<64, false>(p, chunks_per_row, stream);
+    case 128: return launch_grad_k<128, false>(p, chunks_per_row, stream);
+    default: {   // K = 256, 512: key tiles of 128, then dV and the gate gradient
+      if (p.wpart == nullptr || p.V % kWideDvCols != 0) return hipErrorInvalidValue;
+      hipError_t e = launch_grad_k<128, true>(p, chunks_per_row, stream);
+      if (e == hipSuccess) e = launch_chunk_bwd_dv_wide(p, chunks_per_row, stream);
+      if (e == hipSuccess) e = launch_chunk_bwd_gate_wide(p, chunks_per_row, stream);
+      return e;
+    }
+  }
 }
 
 }  // namespace sgla

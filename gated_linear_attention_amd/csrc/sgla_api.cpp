@@ -354,10 +354,10 @@ sgla_status need_chunk64(const Plan& P) {
 
 // Backward request: the forward's shape rules, then the backward's own
 // support set; workspace = tables, per-chunk states and state gradients,
-// per-chunk gate sums.
+// per-chunk gate sums, for K > 128 the key-tile gate records.
 struct BwdPlan {
   Plan P;
-  size_t h_off = 0, dh_off = 0, gpart_off = 0, dkq_off = 0, dvq_off = 0, total_bytes = 0;
+  size_t h_off = 0, dh_off = 0, gpart_off = 0, wpart_off = 0, dkq_off = 0, dvq_off = 0, total_bytes = 0;
 };
 
 sgla_status plan_bwd(const sgla_chunk_args* a, const int64_t* cu, BwdPlan* B) {
@@ -367,17 +367,25 @@ sgla_status plan_bwd(const sgla_chunk_args* a, const int64_t* cu, BwdPlan* B) {
   if (st != SGLA_OK) return st;
   if (a->qkv_dtype != SGLA_BF16 && a->qkv_dtype != SGLA_F32)
     return fail(SGLA_ERR_DTYPE, "qkv_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", a->qkv_dtype);
-  if (!(a->K == 16 || a->K == 32 || a->K == 64 || a->K == 128))
-    return fail(SGLA_ERR_UNSUPPORTED, "the backward supports K in {16,32,64,128} (got %d)", a->K);
+  const bool wide = a->K == 256 || a->K == 512;
+  if (!(a->K == 16 || a->K == 32 || a->K == 64 || a->K == 128 || wide))
+    return fail(SGLA_ERR_UNSUPPORTED, "the backward supports K in {16,32,64,128,256,512} (got %d)", a->K);
+  if (wide && a->qkv_dtype != SGLA_BF16)
+    return fail(SGLA_ERR_UNSUPPORTED, "the backward supports K = %d for bf16 inputs only", a->K);
   if (a->V <= 0 || a->V % 32 != 0)
     return fail(SGLA_ERR_UNSUPPORTED, "the backward supports V a multiple of 32 (got %d)", a->V);
+  if (wide && a->V % sgla::kWideDvCols != 0)
+    return fail(SGLA_ERR_UNSUPPORTED, "the backward with K = %d supports V a multiple of %d (got %d)", a->K,
+                sgla::kWideDvCols, a->V);
   if (!std::isfinite(a->scale)) return fail(SGLA_ERR_INVALID_ARG, "scale must be finite");
   const size_t tasks = (size_t)B->P.num_chunks * a->H;
   const size_t rec = tasks * (size_t)a->K * a->V * sizeof(float);
   B->h_off = align_up(B->P.total_bytes, 256);
   B->dh_off = B->h_off + align_up(rec, 256);
   B->gpart_off = B->dh_off + align_up(rec, 256);
-  B->dkq_off = B->gpart_off + align_up(tasks * sizeof(float), 256);
+  B->wpart_off = B->gpart_off + align_up(tasks * sizeof(float), 256);
+  B->dkq_off = B->wpart_off;
+  if (wide) B->dkq_off += align_up(tasks * (size_t)(a->K / 128) * sgla::kWidePart * sizeof(float), 256);
   B->total_bytes = B->dkq_off;
   if (B->P.Hkv != a->H) {
     // grouped kv heads: k and v gradients per query head, summed over each group
@@ -700,6 +708,7 @@ sgla_status sgla_chunk_bwd(const sgla_chunk_args* args, const void* q, const voi
   p.hbuf = reinterpret_cast<float*>(ws + B.h_off);
   p.dhbuf = reinterpret_cast<float*>(ws + B.dh_off);
   p.gpart = reinterpret_cast<float*>(ws + B.gpart_off);
+  p.wpart = a.K > 128 ? reinterpret_cast<float*>(ws + B.wpart_off) : nullptr;
   hipError_t e = sgla::launch_chunk_bwd(p, stream);
   if (e != hipSuccess) return hip_fail(e, "launching the backward kernels");
   if (grouped) {

@@ -216,8 +216,9 @@ hipError_t launch_chunk_fwd_small(const ChunkFwdParams& p, int chunk, bool qkv_b
 hipError_t launch_chunk_fwd_f32(const ChunkFwdParams& p, hipStream_t stream);
 
 // Backward: q, k, v, dout all bf16 or all float32; every gradient float32.
-// K in {16, 32, 64, 128}, V % 32 == 0, any Hkv dividing H (k and v read by
-// kv head, dk and dv written per query head for the group sum).
+// K in {16, 32, 64, 128} (float32 or bf16) or {256, 512} (bf16, V % 64 ==
+// 0), V % 32 == 0, any Hkv dividing H (k and v read by kv head, dk and dv
+// written per query head for the group sum).
 struct ChunkBwdParams {
   const void* q;
   const void* k;
@@ -242,7 +243,14 @@ struct ChunkBwdParams {
   float* hbuf;               // workspace [num_chunks, H, K, V]: state entering each chunk
   float* dhbuf;              // workspace [num_chunks, H, K, V]: gradient of the state leaving it
   float* gpart;              // workspace [num_chunks, H]: per-chunk sums of dg (g_gamma)
+  float* wpart;              // workspace [num_chunks, H, K / 128, kWidePart] for K > 128: per
+                             // key tile gate terms (r_c, dv_c k_c . (V dH^T)_c, <dH, h>)
 };
+
+// Floats per key-tile gate record of the wide-key backward (64 + 64 + 1,
+// padded), and the V columns per workgroup of its dV kernel.
+constexpr int kWidePart = 132;
+constexpr int kWideDvCols = 64;
 
 hipError_t launch_chunk_bwd(const ChunkBwdParams& p, hipStream_t stream);
 // dk [T_total, Hkv, K] (and dv likewise) = the sum of the n_rep = H / Hkv
@@ -252,10 +260,15 @@ hipError_t launch_kv_group_sum(const float* src, float* dst, int64_t tokens, int
 
 // The backward (state pass and per-chunk gradients) runs on the bf16 matrix
 // cores (hi/lo splits of the fp32 operands) for bf16 inputs with K in {64,
-// 128}; otherwise on the fp32 matrix cores.
-inline bool bwd_bf16_grad(bool qkv_bf16, int32_t K) { return qkv_bf16 && (K == 64 || K == 128); }
+// 128, 256, 512}; otherwise on the fp32 matrix cores.
+inline bool bwd_bf16_grad(bool qkv_bf16, int32_t K) {
+  return qkv_bf16 && (K == 64 || K == 128 || K == 256 || K == 512);
+}
 hipError_t launch_chunk_bwd_state_bf16(const ChunkBwdParams& p, int32_t chunks_per_row, hipStream_t stream);
 hipError_t launch_chunk_bwd_grad_bf16(const ChunkBwdParams& p, int32_t chunks_per_row, hipStream_t stream);
+// K > 128: dV over all keys, and the gate gradient from the key-tile records
+hipError_t launch_chunk_bwd_dv_wide(const ChunkBwdParams& p, int32_t chunks_per_row, hipStream_t stream);
+hipError_t launch_chunk_bwd_gate_wide(const ChunkBwdParams& p, int32_t chunks_per_row, hipStream_t stream);
 
 // Elementwise-gate GLA forward: gk [T_total, H, K] float32 natural-log gates,
 // one per key.  K in {16, 32, 64, 128}, V % 32 == 0.

@@ -227,7 +227,9 @@ size_t sgla_chunk_bwd_workspace_size(const sgla_chunk_args *args, const int64_t 
  *   workspace       >= sgla_chunk_bwd_workspace_size(args, cu_seqlens_host).
  * Outputs must not overlap inputs or each other.
  * Supported: K in {16, 32, 64, 128}, V a multiple of 32, bf16 or float32
- * inputs, chunk_size 64, any Hkv dividing H.
+ * inputs; K in {256, 512} with bf16 inputs and V a multiple of 64;
+ * chunk_size 64, any Hkv dividing H.  Other K, or K > 128 with float32
+ * inputs, return SGLA_ERR_UNSUPPORTED.
  */
 sgla_status sgla_chunk_bwd(const sgla_chunk_args *args,
                            const void *q, const void *k, const void *v,

@@ -316,8 +316,10 @@ def bwd_call(G, args, b, cu=None, g=True, gg=False, dg=True, dgg=False, ws_bytes
 
 
 BWD_CASES = [
-    ("K=256", dict(K=256), {}, UNSUPPORTED, "K in"),
+    ("K=384", dict(K=384), {}, UNSUPPORTED, "K in"),
     ("V=48", dict(V=48), {}, UNSUPPORTED, "V a multiple"),
+    ("f32 K=256", dict(qkv=F32, K=256), {}, UNSUPPORTED, "bf16 inputs only"),
+    ("K=512 V=96", dict(K=512, V=96), {}, UNSUPPORTED, "multiple of 64"),
     ("fp16", dict(qkv=3), {}, DTYPE, "qkv_dtype"),
     ("both gates", {}, dict(gg=True), INVALID, "mutually exclusive"),
     ("g without dg", {}, dict(dg=False), INVALID, "dg is NULL"),
@@ -338,6 +340,19 @@ def test_chunk_bwd_rejects_without_writing(G, desc, aover, cover, status, frag):
     assert st == status, (st, msg)
     assert frag in msg, msg
     assert b.unchanged()
+
+
+def test_chunk_bwd_workspace_size_wide(G):
+    """K > 128 adds one gate record of 132 floats per (chunk, head, 128-key
+    tile) after the per-chunk gate sums."""
+    def align(n):
+        return (n + 255) // 256 * 256
+    for K in (256, 512):
+        a = mkargs(G, B=2, T=130, H=4, K=K, V=64)
+        tasks = 2 * 3 * 4
+        rec = tasks * K * 64 * 4
+        want = 2 * align(rec) + align(tasks * 4) + align(tasks * (K // 128) * 132 * 4)
+        assert G.lib.sgla_chunk_bwd_workspace_size(ctypes.byref(a), None) == want, K
 
 
 def test_chunk_bwd_workspace_size_grouped(G):

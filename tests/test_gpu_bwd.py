@@ -93,6 +93,14 @@ SMALL = [
     small("gqa_mqa_k64_v96", H=3, Hkv=1, K=64, V=96, T=100),
     small("gqa_f32_k32", dtype="f32", H=4, Hkv=2, K=32, V=64, T=97, initial_state=True),
     small("gqa_bf16_k16", H=4, Hkv=1, K=16, V=32, T=70),
+    # K in {256, 512}: key tiles of 128 for dq and dk, dv over 64-key slices,
+    # the gate gradient from the key-tile records
+    small("k256_v64_h0", K=256, V=64, T=150, initial_state=True),
+    small("k512_v128_gamma_h0", K=512, V=128, T=131, gate="gamma", initial_state=True),
+    small("k256_no_gate", K=256, V=64, T=70, gate="none"),
+    small("k512_varlen", B=1, T=0, H=2, K=512, V=64, fixed_lengths=(15, 85, 0, 1, 200),
+          initial_state=True),
+    small("gqa_k256_v128", H=4, Hkv=2, K=256, V=128, T=100, initial_state=True),
 ]
 
 
@@ -127,6 +135,19 @@ def test_bwd_named_workload_full():
     compare(got, oracle_bwd(inp, bi), TOL_BF16, "varlen_bf16_k128 whole-tensor")
 
 
+def test_bwd_dense_k512_full():
+    """The dense wide-key workload (B=4, T=2048, H=4, K = V = 512, bf16, g)
+    with a final-state gradient, every gradient compared with the oracle
+    backward over the whole tensor.  The oracle keeps every state of a
+    (sequence, head) in fp64 (2 MiB per token at K = V = 512), so it runs on
+    8 threads here to bound host memory."""
+    w = CHUNK_CONFIGS["dense_bf16_k512"]
+    inp = make_chunk_inputs(w)
+    bi = make_backward_inputs(inp, seed=w.seed + 100)
+    got = run_bwd(inp, bi)
+    compare(got, oracle_bwd(inp, bi, nthreads=8), TOL_BF16, "dense_bf16_k512 whole-tensor")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_bwd_grouped_equals_repeated_heads(dtype):
     """With grouped kv heads every query head's gradients are those of the
@@ -149,7 +170,8 @@ def test_bwd_grouped_equals_repeated_heads(dtype):
 
 
 @pytest.mark.parametrize("kind", ["forget", "resets"])
-@pytest.mark.parametrize("dtype,K", [("bf16", 64), ("bf16", 128), ("f32", 32)], ids=["k64", "k128", "f32_k32"])
+@pytest.mark.parametrize("dtype,K", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("f32", 32)],
+                         ids=["k64", "k128", "k256", "f32_k32"])
 def test_bwd_degenerate_gates(dtype, K, kind):
     """Gates of -1e4 (a full reset) at every token or every 37th token: every
     gradient stays finite and within the bar."""
