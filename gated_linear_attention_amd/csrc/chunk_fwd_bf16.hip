@@ -71,9 +71,7 @@ struct Layout {
   static constexpr int KT = KH / 16;          // 16-row state tiles per wave
   static constexpr int KS = KH / 32;          // 32-deep steps over a wave's rows
   static constexpr int KSF = K / 32;          // 32-deep steps over all K
-  static constexpr bool DB = K <= 128;        // double-buffered chunk staging
-  static constexpr bool PF2 = DB;             // loads run two chunks ahead
-  static constexpr int NBUF = DB ? 2 : 1;
+  static constexpr int NBUF = 2;              // double-buffered chunk staging
   static constexpr int LDQ = K + 8;           // row strides in elements; padding
   static constexpr int LDK = K + 16;          // keeps the 16-byte and transposing
   static constexpr int SZ_Q = C * LDQ * 2;    // reads free of bank conflicts
@@ -83,12 +81,8 @@ struct Layout {
   static constexpr int SZ_A = 2 * C * LDA * 2;   // hi and lo
   static constexpr int SZ_STAGE = SZ_Q + SZ_K + SZ_V + SZ_G + SZ_A;
   static constexpr int SZ_X = NW * 2 * 64 * 16;  // two 16x16 fp32 tiles per wave
-  // double-buffered (pipelined) mode: one exchange area per chunk parity;
-  // single-buffered mode: the exchange tiles reuse the Q staging area, which
-  // is no longer read once a chunk's A, q.h and state-update products exist
-  static constexpr int OFF_X = DB ? NBUF * SZ_STAGE : 0;
-  static constexpr int BYTES = NBUF * SZ_STAGE + (DB ? 2 * SZ_X : 0);
-  static_assert(DB || SZ_X <= SZ_Q, "exchange tiles must fit in the Q area");
+  static constexpr int OFF_X = NBUF * SZ_STAGE;   // one exchange area per chunk parity
+  static constexpr int BYTES = NBUF * SZ_STAGE + 2 * SZ_X;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -433,71 +427,46 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       store4<TOut>(ro, c1 * RSO * (uint32_t)sizeof(TOut) + ocol, mine1 + x1);
     };
 
+    // Pipelined, one barrier per chunk, loads running two chunks ahead.
+    // Iteration m stages chunk m, then finishes chunk m-1 (A V and the output
+    // store, from buffers of parity p^1 and registers carried over) and forms
+    // chunk m's A, q.h partials and state update.
     Stage st0, st1;
     load_chunk(0, st0);
-    if (L::PF2) load_chunk(1, st1);
-
-    if constexpr (L::DB) {
-      // Pipelined: one barrier per chunk.  Iteration m stages chunk m, then
-      // finishes chunk m-1 (A V and the output store, from buffers of parity
-      // p^1 and registers carried over) and forms chunk m's A, q.h partials
-      // and state update.
-      bf16x8 vf_prev[2] = {};
-      f32x4 mine0 = {0.f, 0.f, 0.f, 0.f}, mine1 = {0.f, 0.f, 0.f, 0.f};
-      int prev_m = 0, prev_cl = 0;   // prev_cl = 0: nothing to store yet
-      auto step = [&](const int m, const int p, Stage& st) {
-        const int cl = st.len;
-        store_chunk(p, st);
-        __syncthreads();   // chunk m staged; chunk m-1's A and exchange tiles visible
-        // the loads of chunk m + 2 go out before chunk m - 1's output stores:
-        // a later wait for those loads then never has to wait for the stores
-        load_chunk(m + 2, st);
-        phase_intra(p ^ 1, vf_prev, mine0, mine1);
-        finalize(p ^ 1, prev_m, prev_cl, mine0, mine1);
-        phase_A(p);
-        f32x4 oacc[4];
-        load_vf(p, vf_prev);
-        phase_inter(p, oacc);
-        phase_update(p, vf_prev);
-        exchange_write(p, oacc);
-        mine0 = oacc[0];
-        mine1 = oacc[1];
-        prev_m = m;
-        prev_cl = cl;
-      };
-      int m = 0;
-      for (; m + 1 < nchunks; m += 2) {
-        step(m, 0, st0);
-        step(m + 1, 1, st1);
-      }
-      if (m < nchunks) step(m, 0, st0);
-      __syncthreads();
-      const int pl = (nchunks - 1) & 1;
-      phase_intra(pl, vf_prev, mine0, mine1);
-      finalize(pl, prev_m, prev_cl, mine0, mine1);
-    } else {
-      for (int m = 0; m < nchunks; ++m) {
-        const int cl = st0.len;
-        store_chunk(0, st0);
-        __syncthreads();   // chunk m staged
-        load_chunk(m + 1, st0);
-        phase_A(0);
-        f32x4 oacc[4];
-        phase_inter(0, oacc);
-        bf16x8 vf[2];
-        load_vf(0, vf);
-        phase_update(0, vf);
-        __syncthreads();   // A complete
-        f32x4 mine0 = oacc[0];
-        f32x4 mine1 = oacc[1];
-        phase_intra(0, vf, mine0, mine1);
-        __syncthreads();   // Q area is about to hold exchange tiles
-        exchange_write(0, oacc);
-        __syncthreads();
-        finalize(0, m, cl, mine0, mine1);
-        __syncthreads();   // exchange tiles read before the next chunk is staged
-      }
+    load_chunk(1, st1);
+    bf16x8 vf_prev[2] = {};
+    f32x4 mine0 = {0.f, 0.f, 0.f, 0.f}, mine1 = {0.f, 0.f, 0.f, 0.f};
+    int prev_m = 0, prev_cl = 0;   // prev_cl = 0: nothing to store yet
+    auto step = [&](const int m, const int p, Stage& st) {
+      const int cl = st.len;
+      store_chunk(p, st);
+      __syncthreads();   // chunk m staged; chunk m-1's A and exchange tiles visible
+      // the loads of chunk m + 2 go out before chunk m - 1's output stores:
+      // a later wait for those loads then never has to wait for the stores
+      load_chunk(m + 2, st);
+      phase_intra(p ^ 1, vf_prev, mine0, mine1);
+      finalize(p ^ 1, prev_m, prev_cl, mine0, mine1);
+      phase_A(p);
+      f32x4 oacc[4];
+      load_vf(p, vf_prev);
+      phase_inter(p, oacc);
+      phase_update(p, vf_prev);
+      exchange_write(p, oacc);
+      mine0 = oacc[0];
+      mine1 = oacc[1];
+      prev_m = m;
+      prev_cl = cl;
+    };
+    int m = 0;
+    for (; m + 1 < nchunks; m += 2) {
+      step(m, 0, st0);
+      step(m + 1, 1, st1);
     }
+    if (m < nchunks) step(m, 0, st0);
+    __syncthreads();
+    const int pl = (nchunks - 1) & 1;
+    phase_intra(pl, vf_prev, mine0, mine1);
+    finalize(pl, prev_m, prev_cl, mine0, mine1);
 
     if (ht != nullptr && last) {
       float* htu = ht + ((int64_t)seq * H + hd) * K * V;

@@ -46,6 +46,7 @@ def check_full(inp, o_gpu, ht_gpu):
                                cu_seqlens=inp["cu_seqlens"])
     tol = _tol(inp["dtype"])
     eo = err_ratio(o_gpu, o_ref)
+    print(f"[parity {inp['dtype']} K={inp['K']} V={inp['V']}] o err/RMS={eo:.3e}", flush=True)
     assert np.all(np.isfinite(o_gpu))
     assert eo <= tol, f"o: max err / RMS = {eo:.3e} > {tol}"
     if ht_gpu is not None:
