@@ -71,7 +71,10 @@ METRIC = "chunked Simple-GLA fwd tokens/s + % bf16 MFMA peak; decode HBM GB/s"
 KERNEL_SOURCES = {
     "chunk_fwd": ("chunk_prep_bf16.hip", "chunk_fwd_bf16_wide.hip", "mfma_common.h", "gate_scan.h",
                   "unit_map.h"),
-    "chunk_fwd_bf16_kernel": ("chunk_fwd_bf16.hip", "mfma_common.h", "gate_scan.h", "unit_map.h"),
+    # with packed or segmented inputs the call also runs the table and
+    # segment-state kernels, whose traffic the record includes
+    "chunk_fwd_bf16_kernel": ("chunk_fwd_bf16.hip", "segment_state.hip", "table_put.hip", "mfma_common.h",
+                              "gate_scan.h", "unit_map.h"),
     "chunk_fwd_f32_kernel": ("chunk_fwd_f32.hip", "gate_scan.h", "unit_map.h"),
     "recurrent_step_kernel": ("recurrent_step.hip",),
     "parallel_fwd_kernel": ("parallel_fwd.hip", "mfma_common.h", "gate_scan.h", "unit_map.h"),

@@ -60,16 +60,21 @@ def trace(a):
              "| kernel | dispatches | mean us | median us | min us | max us |", "|---|---|---|---|---|---|"]
     pat = re.compile(a.kernel)
     timed = []
+    others = 0
     for name, v in sorted(by.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        if not pat.search(name):
+            others += 1
+            continue
         durs = [d / 1e3 for _, d in v]
         short = name if len(name) < 110 else name[:107] + "..."
         lines.append(f"| `{short}` | {len(durs)} | {statistics.mean(durs):.2f} | "
                      f"{statistics.median(durs):.2f} | {min(durs):.2f} | {max(durs):.2f} |")
-        if pat.search(name):
-            last = [d / 1e3 for _, d in sorted(v)[-a.steps:]]
-            timed.append((short, len(last), statistics.mean(last), statistics.median(last)))
+        last = [d / 1e3 for _, d in sorted(v)[-a.steps:]]
+        timed.append((short, len(last), statistics.mean(last), statistics.median(last)))
     if not timed:
         sys.exit(f"no kernel matches {a.kernel}")
+    lines += ["", f"({others} other kernels of the traced process -- input set-up, copies, "
+              "other bench legs -- are not listed.)"]
     lines += ["", f"Timed launches: the last {timed[0][1]} dispatches of each kernel matching "
               f"`{a.kernel}` (the ones bench.py times after its warm-up):", ""]
     lines += [f"- `{n}`: mean {mn:.2f} us, median {md:.2f} us" for n, _, mn, md in timed]
@@ -147,7 +152,7 @@ def counters(a):
     CSV, so one XCD's active cycles are its value divided by the XCD count;
     SQ_VALU_MFMA_BUSY_CYCLES is summed over every SIMD)."""
     pat = re.compile(a.kernel)
-    by = {}
+    by = {}   # counter -> kernel -> dispatch -> value
     names = set()
     for d in a.dir:
         for r in _rows(d, "counter_collection.csv"):
@@ -155,16 +160,18 @@ def counters(a):
                 continue
             names.add(r["Kernel_Name"])
             key = (r["_file"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
-            per = by.setdefault(r["Counter_Name"], {})
+            per = by.setdefault(r["Counter_Name"], {}).setdefault(r["Kernel_Name"], {})
             per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
     if not by:
         sys.exit(f"no counter rows for {a.kernel}")
-    med = {c: statistics.median(v.values()) for c, v in by.items()}
-    n = {c: len(v) for c, v in by.items()}
+    # per call: the median over a kernel's dispatches, summed over the
+    # matching kernels (one call launches each of them once)
+    med = {c: sum(statistics.median(v.values()) for v in ks.values()) for c, ks in by.items()}
+    n = {c: max(len(v) for v in ks.values()) for c, ks in by.items()}
     lines = [f"# rocprofv3 counters: {a.title}", "", "Commands (from the repository root; one counter group per run):", ""]
     lines += [f"    {c}" for c in a.command]
     lines += ["", f"Kernel(s): {', '.join('`' + k[:100] + '`' for k in sorted(names))}", "",
-              "| counter | median per dispatch | dispatches |", "|---|---|---|"]
+              "| counter | per call (median per kernel, summed) | dispatches per kernel |", "|---|---|---|"]
     lines += [f"| {c} | {med[c]:.6g} | {n[c]} |" for c in sorted(med)]
     derived = {}
     if "GRBM_GUI_ACTIVE" in med:
