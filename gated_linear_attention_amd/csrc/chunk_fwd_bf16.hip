@@ -32,8 +32,12 @@
 //     row-major; the operands that need the token index contiguous per lane
 //     (K^T and V as MFMA operands reduced over tokens) are fetched with the
 //     gfx950 transposing LDS read ds_read_b64_tr_b16;
-//   * staging is double-buffered with one barrier per chunk, the rows of
-//     chunk m + 2 loading into registers while chunk m computes.
+//   * staging is double-buffered in LDS with one barrier per chunk, the rows
+//     of chunk m + 1 loading into registers while chunk m computes;
+//   * the phases of a chunk step are independent of one another, and the two
+//     waves that share a SIMD (kh = 0 and kh = 1) take them in different
+//     orders (A first or last), so that one of them forms A while the other
+//     runs its q.h and state-update products.
 //
 // Precision: the state, the accumulation and the output are fp32.  The three
 // MFMA operands that are not exact bf16 inputs -- the decay-masked A, the
@@ -282,13 +286,18 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       bf16* a_lo = a_hi + C * LDA;
       for (int ti = w; ti < 10; ti += L::NW) {
         const int ct = tile_c(ti), jt = tile_j(ti);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // every operand read first (one wait instead of one per step), then
+        // two independent accumulation chains
+        bf16x8 a[L::KSF], b[L::KSF];
 #pragma unroll
         for (int s = 0; s < L::KSF; ++s) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(k_s + (16 * jt + r) * L::LDK + 32 * s + 8 * g4);
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(q_s + (16 * ct + r) * L::LDQ + 32 * s + 8 * g4);
-          acc = mfma(a, b, acc);  // acc[i] = q_c . k_j, c = 16ct + r, j = 16jt + 4g + i
+          a[s] = *reinterpret_cast<const bf16x8*>(k_s + (16 * jt + r) * L::LDK + 32 * s + 8 * g4);
+          b[s] = *reinterpret_cast<const bf16x8*>(q_s + (16 * ct + r) * L::LDQ + 32 * s + 8 * g4);
         }
+        f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int s = 0; s < L::KSF; ++s) acc2[s & 1] = mfma(a[s], b[s], acc2[s & 1]);
+        const f32x4 acc = acc2[0] + acc2[1];   // acc[i] = q_c . k_j, c = 16ct + r, j = 16jt + 4g + i
         const int c = 16 * ct + r;
         const float bc = g_s[c];
         const f32x4 bj = *reinterpret_cast<const f32x4*>(g_s + 16 * jt + 4 * g4);
@@ -427,31 +436,31 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       store4<TOut>(ro, c1 * RSO * (uint32_t)sizeof(TOut) + ocol, mine1 + x1);
     };
 
-    // Pipelined, one barrier per chunk, loads running two chunks ahead.
+    // Pipelined, one barrier per chunk, loads running one chunk ahead.
     // Iteration m stages chunk m, then finishes chunk m-1 (A V and the output
     // store, from buffers of parity p^1 and registers carried over) and forms
     // chunk m's A, q.h partials and state update.
-    Stage st0, st1;
-    load_chunk(0, st0);
-    load_chunk(1, st1);
+    Stage st;
+    load_chunk(0, st);
     bf16x8 vf_prev[2] = {};
     f32x4 mine0 = {0.f, 0.f, 0.f, 0.f}, mine1 = {0.f, 0.f, 0.f, 0.f};
     int prev_m = 0, prev_cl = 0;   // prev_cl = 0: nothing to store yet
-    auto step = [&](const int m, const int p, Stage& st) {
+    auto step = [&](const int m, const int p) {
       const int cl = st.len;
       store_chunk(p, st);
       __syncthreads();   // chunk m staged; chunk m-1's A and exchange tiles visible
-      // the loads of chunk m + 2 go out before chunk m - 1's output stores:
+      // the loads of chunk m + 1 go out before chunk m - 1's output stores:
       // a later wait for those loads then never has to wait for the stores
-      load_chunk(m + 2, st);
+      load_chunk(m + 1, st);
       phase_intra(p ^ 1, vf_prev, mine0, mine1);
       finalize(p ^ 1, prev_m, prev_cl, mine0, mine1);
-      phase_A(p);
+      if (kh == 0) phase_A(p);   // A first on one wave of each SIMD, last on the other
       f32x4 oacc[4];
       load_vf(p, vf_prev);
       phase_inter(p, oacc);
       phase_update(p, vf_prev);
       exchange_write(p, oacc);
+      if (kh != 0) phase_A(p);
       mine0 = oacc[0];
       mine1 = oacc[1];
       prev_m = m;
@@ -459,10 +468,10 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     };
     int m = 0;
     for (; m + 1 < nchunks; m += 2) {
-      step(m, 0, st0);
-      step(m + 1, 1, st1);
+      step(m, 0);
+      step(m + 1, 1);
     }
-    if (m < nchunks) step(m, 0, st0);
+    if (m < nchunks) step(m, 0);
     __syncthreads();
     const int pl = (nchunks - 1) & 1;
     phase_intra(pl, vf_prev, mine0, mine1);

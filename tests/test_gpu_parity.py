@@ -65,7 +65,7 @@ def small(name, **kw):
 # step (1): chunk-local cumulative gate
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("chunk", [1, 4, 8, 16, 32, 64])
 @pytest.mark.parametrize("cu", [None, [0, 15, 100, 300, 1200, 2000], [0, 0, 1, 65, 65, 200]])
 def test_gate_cumsum(cu, chunk):
     rng = np.random.default_rng(3)
