@@ -262,6 +262,12 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const int s = tid + i * NT;
         *reinterpret_cast<u32x4*>(v_s + (s / (VT / 8)) * LDV + (s % (VT / 8)) * 8) = st.v[i];
       }
+      // Every wave takes delivery of the gate word here, although only the last
+      // wave uses it: a load whose register is still pending when the register
+      // is reused makes the compiler wait on the vector-memory counter there,
+      // and that counter retires loads and stores in issue order -- at the
+      // next chunk's start that wait would include this chunk's output stores.
+      asm volatile("" ::"v"(st.g));
       if (w == L::NW - 1) {
         // step (1) on the last wave (it owns one A tile, the first waves two):
         // chunk-local cumulative log2 gate b, plus the per-token factors
