@@ -177,11 +177,16 @@ def counters(a):
     if "GRBM_GUI_ACTIVE" in med:
         xcd_cycles = med["GRBM_GUI_ACTIVE"] / a.xcds
         derived["active cycles per XCD"] = f"{xcd_cycles:.0f} ({xcd_cycles / a.clock_ghz / 1e3:.1f} us at {a.clock_ghz} GHz)"
+        if "TA_BUSY_avr" in med:
+            derived["texture-address unit busy (TA_BUSY_avr / active cycles)"] = \
+                f"{100 * med['TA_BUSY_avr'] / xcd_cycles:.1f} %"
         if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
             u = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_cycles * a.simds)
             derived["MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x SIMDs))"] = f"{100 * u:.1f} %"
     if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
         derived["bf16 MFMA flops issued (MOPS x 512)"] = f"{med['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.4g}"
+    if "SQ_INSTS_VALU_MFMA_MOPS_F32" in med:
+        derived["fp32 MFMA flops issued (MOPS x 512)"] = f"{med['SQ_INSTS_VALU_MFMA_MOPS_F32'] * 512:.4g}"
     if "SQ_WAVE_CYCLES" in med:
         wc = med["SQ_WAVE_CYCLES"]
         for c in ("SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS",
