@@ -24,6 +24,11 @@
 //   segment_scan_kernel -- per (sequence, head, 1024 state elements), walks
 //     the sequence's blocks in order and writes S into the entering-state
 //     record a block ends on.
+// When the segment, bin, block and scan tables fit one kernel-argument
+// payload, the pre-pass carries them: its workgroup 0 writes them to the
+// workspace (for the scan and the chunk kernel, which run after it) and every
+// workgroup reads its block entry from the arguments, so no separate table
+// launch is needed.
 #include <hip/hip_runtime.h>
 
 #include "gate_scan.h"
@@ -51,11 +56,25 @@ struct PreLayout {
   static constexpr int BYTES = 2 * SZ_STAGE;
 };
 
-template <int K>
+// The tables travel in the arguments (INLINE) or sit in the workspace.
+template <bool INLINE>
+struct PreTables;
+template <>
+struct PreTables<false> {
+  const BlockEntry* blocks;
+};
+template <>
+struct PreTables<true> {
+  TableWords words;   // the table region, from its first word
+  uint32_t* dst;      // where the region goes in the workspace
+  int32_t blk_word;   // first word of the block table within the region
+};
+
+template <int K, bool INLINE>
 __global__ void __launch_bounds__(NT)
 segment_prepass_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ g,
                        const float* __restrict__ g_gamma, int32_t H, int32_t Hkv, int32_t V,
-                       const BlockEntry* __restrict__ blocks, int32_t num_blocks, float* __restrict__ urec,
+                       PreTables<INLINE> tables, int32_t num_blocks, float* __restrict__ urec,
                        float* __restrict__ ulog) {
   using L = PreLayout<K>;
   constexpr int SEG = K / 8;                 // 16-byte pieces per k row
@@ -65,10 +84,22 @@ segment_prepass_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v, c
   static_assert(NK * NT == C * SEG && NV * NT == C * (VT / 8), "load split");
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
 
+  if constexpr (INLINE) {
+    if (blockIdx.x == 0)
+      for (int i = threadIdx.x; i < tables.words.count; i += NT) tables.dst[i] = tables.words.w[i];
+  }
   const UnitMap um = map_unit(blockIdx.x, V / VT, Hkv, H / Hkv, num_blocks);
   if (!um.valid) return;
   const int rank = um.rank, hd = um.hd, hk = um.hk, vt = um.vt;
-  const BlockEntry be = blocks[rank];
+  BlockEntry be;
+  if constexpr (INLINE) {
+    const uint32_t* bw = tables.words.w + tables.blk_word + 4 * rank;
+    be.t0 = (int32_t)bw[0];
+    be.len = (int32_t)bw[1];
+    be.out_rec = (int32_t)bw[2];
+  } else {
+    be = tables.blocks[rank];
+  }
   const int64_t t0 = __builtin_amdgcn_readfirstlane(be.t0);
   const int32_t len = __builtin_amdgcn_readfirstlane(be.len);
   const int nchunks = (len + C - 1) / C;
@@ -251,9 +282,21 @@ segment_scan_kernel(const float* __restrict__ h0, int32_t H, int32_t K, int32_t 
 template <int K>
 hipError_t launch_pre(const SegmentParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)unit_grid(p.num_blocks, p.Hkv, p.H / p.Hkv, p.V / VT));
-  hipLaunchKernelGGL((segment_prepass_kernel<K>), grid, dim3(NT), 0, stream, static_cast<const bf16*>(p.k),
-                     static_cast<const bf16*>(p.v), p.g, p.g_gamma, p.H, p.Hkv, p.V, p.blocks, p.num_blocks,
-                     p.urec, p.ulog);
+  const bf16* kp = static_cast<const bf16*>(p.k);
+  const bf16* vp = static_cast<const bf16*>(p.v);
+  if (p.inline_tables != nullptr) {
+    PreTables<true> t;
+    t.words = *p.inline_tables;
+    t.dst = p.table_dst;
+    t.blk_word = p.blk_word;
+    hipLaunchKernelGGL((segment_prepass_kernel<K, true>), grid, dim3(NT), 0, stream, kp, vp, p.g, p.g_gamma, p.H,
+                       p.Hkv, p.V, t, p.num_blocks, p.urec, p.ulog);
+  } else {
+    PreTables<false> t;
+    t.blocks = p.blocks;
+    hipLaunchKernelGGL((segment_prepass_kernel<K, false>), grid, dim3(NT), 0, stream, kp, vp, p.g, p.g_gamma,
+                       p.H, p.Hkv, p.V, t, p.num_blocks, p.urec, p.ulog);
+  }
   return hipGetLastError();
 }
 

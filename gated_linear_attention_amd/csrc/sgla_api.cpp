@@ -547,6 +547,8 @@ sgla_status chunk_fwd_enqueue(const sgla_chunk_args* args, const void* q, const 
   if (P.seg) {
     // segmented chains: tables, the later segments' entering states, then
     // one chunk workgroup per (segment, head, V tile)
+    sgla::TableWords inline_words;
+    bool tables_inline = false;
     {
       // the four tables are adjacent in the workspace: one region, uploaded
       // with as few launches as its size allows
@@ -558,8 +560,16 @@ sgla_status chunk_fwd_enqueue(const sgla_chunk_args* args, const void* q, const 
       put(P.bins.data(), P.bins.size() * sizeof(sgla::BinEntry), P.bint_off);
       put(P.blocks.data(), P.blocks.size() * sizeof(sgla::BlockEntry), P.blkt_off);
       put(P.scans.data(), P.scans.size() * sizeof(sgla::ScanEntry), P.scnt_off);
-      st = upload_words(region, ws + P.segt_off, stream);
-      if (st != SGLA_OK) return st;
+      if (region.size() <= (size_t)sgla::kTableWords && !P.blocks.empty()) {
+        // small: the pre-pass carries the region in its arguments
+        inline_words.first = 0;
+        inline_words.count = (int32_t)region.size();
+        std::memcpy(inline_words.w, region.data(), region.size() * sizeof(uint32_t));
+        tables_inline = true;
+      } else {
+        st = upload_words(region, ws + P.segt_off, stream);
+        if (st != SGLA_OK) return st;
+      }
     }
     sgla::SegmentParams sp;
     sp.k = k;
@@ -579,6 +589,11 @@ sgla_status chunk_fwd_enqueue(const sgla_chunk_args* args, const void* q, const 
     sp.urec = reinterpret_cast<float*>(ws + P.urec_off);
     sp.ulog = reinterpret_cast<float*>(ws + P.ulog_off);
     sp.sin = reinterpret_cast<float*>(ws + P.sin_off);
+    if (tables_inline) {
+      sp.inline_tables = &inline_words;
+      sp.table_dst = reinterpret_cast<uint32_t*>(ws + P.segt_off);
+      sp.blk_word = (int32_t)((P.blkt_off - P.segt_off) / 4);
+    }
     e = sgla::launch_segment_states(sp, stream);
     if (e != hipSuccess) return hip_fail(e, "launching the segment state passes");
     p.segs = reinterpret_cast<const sgla::SegEntry*>(ws + P.segt_off);

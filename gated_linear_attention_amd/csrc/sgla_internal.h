@@ -142,6 +142,12 @@ struct SegmentParams {
   float* urec;                // [num_blocks, H, K, V]: state added by each block from a zero start
   float* ulog;                // [num_blocks, H]: each block's total log2 decay
   float* sin;                 // [records, H, K, V]: entering state of each later segment
+  // the table region carried in the pre-pass arguments (written to table_dst
+  // by its workgroup 0; blocks then read from word blk_word of the payload),
+  // or nullptr when the tables are already in the workspace
+  const TableWords* inline_tables = nullptr;
+  uint32_t* table_dst = nullptr;
+  int32_t blk_word = 0;
 };
 // state-only pass over the blocks, then the scan writing the entering states
 hipError_t launch_segment_states(const SegmentParams& p, hipStream_t stream);
