@@ -251,6 +251,12 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
   };
   load_slice(0);
   __syncthreads();   // Q, K and the gates staged
+  // the per-token factors this lane needs, read once: rows c = 16 rw + 4 g + i
+  // and columns j = 16 (2 kh + t) + r of the A / dA tiles
+  const f32x4 b_c = *reinterpret_cast<const f32x4*>(sb + 16 * rw + 4 * g4);
+  const f32x4 sc_c = *reinterpret_cast<const f32x4*>(ssc + 16 * rw + 4 * g4);
+  const f32x4 dv_c = *reinterpret_cast<const f32x4*>(sdv + 16 * rw + 4 * g4);
+  const float b_j[2] = {sb[16 * (2 * kh) + r], sb[16 * (2 * kh + 1) + r]};
 
   // ---- A = scale (Q K^T) (.) M: row tile rw against column tiles 2 kh,
   //      2 kh + 1 (tiles above the diagonal come out as zeros) -----------------
@@ -270,7 +276,7 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = 16 * rw + 4 * g4 + i;
-        put_split(sA, c * LDA + j, ALO, j <= c ? acc[t][i] * exp2f(sb[c] - sb[j]) * scale : 0.f);
+        put_split(sA, c * LDA + j, ALO, j <= c ? acc[t][i] * exp2f(b_c[i] - b_j[t]) * scale : 0.f);
       }
     }
   }
@@ -333,7 +339,7 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 16 * rw + 4 * g4 + i;
-        if (j < cl) dv[((t0 + j) * H + hd) * (int64_t)V + vs * VS + 16 * kh + r] = in[i] + sdv[j] * st[i];
+        if (j < cl) dv[((t0 + j) * H + hd) * (int64_t)V + vs * VS + 16 * kh + r] = in[i] + dv_c[i] * st[i];
       }
     }
   }
@@ -346,7 +352,7 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = 16 * rw + 4 * g4 + i;
-      put_split(sA, c * LDA + j, ALO, j <= c ? dAacc[t][i] * exp2f(sb[c] - sb[j]) * scale : 0.f);
+      put_split(sA, c * LDA + j, ALO, j <= c ? dAacc[t][i] * exp2f(b_c[i] - b_j[t]) * scale : 0.f);
     }
   }
   // Frobenius product <dH, h> of the whole chunk record
@@ -380,16 +386,21 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
       ak = mfma(ah, bq, ak);
       ak = mfma(al, bq, ak);
     }
+    const int col = 16 * kt + r;
+    float qv[4], kv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qv[i] = (float)sQ[(16 * rw + 4 * g4 + i) * LDQ + col];
+      kv[i] = (float)sK[(16 * rw + 4 * g4 + i) * LDQ + col];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = 16 * rw + 4 * g4 + i;
-      const int col = 16 * kt + r;
-      const float xq = ssc[c] * dQi[t][i] + aq[i];
-      const float xk = ak[i] + sdv[c] * dKs[t][i];
-      const float qv = (float)sQ[c * LDQ + col], kv = (float)sK[c * LDQ + col];
-      rq[i] += qv * xq;
-      rk[i] += kv * xk;
-      ks4[i] += kv * dKs[t][i];
+      const float xq = sc_c[i] * dQi[t][i] + aq[i];
+      const float xk = ak[i] + dv_c[i] * dKs[t][i];
+      rq[i] += qv[i] * xq;
+      rk[i] += kv[i] * xk;
+      ks4[i] += kv[i] * dKs[t][i];
       if (c < cl) {
         dq[((t0 + c) * H + hd) * (int64_t)K + kb + col] = xq;
         dk[((t0 + c) * H + hd) * (int64_t)K + kb + col] = xk;
@@ -408,7 +419,7 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
     if (r == 0) {
       const int c = 16 * rw + 4 * g4 + i;
       sR[kh * C + c] = rq[i] - rk[i];
-      sKs[kh * C + c] = sdv[c] * ks4[i];
+      sKs[kh * C + c] = dv_c[i] * ks4[i];
     }
   }
   __syncthreads();
