@@ -268,10 +268,11 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       // and that counter retires loads and stores in issue order -- at the
       // next chunk's start that wait would include this chunk's output stores.
       asm volatile("" ::"v"(st.g));
-      if (w == L::NW - 1) {
-        // step (1) on the last wave (it owns one A tile, the first waves two):
-        // chunk-local cumulative log2 gate b, plus the per-token factors
-        // scale * 2^b (inter-chunk term) and 2^(b_last - b) (state update)
+      if (w == 3) {
+        // step (1) on wave 3: it owns one A tile (waves 0 and 1 own two) and
+        // forms it first, so it reaches the barrier early; chunk-local
+        // cumulative log2 gate b, plus the per-token factors scale * 2^b
+        // (inter-chunk term) and 2^(b_last - b) (state update)
         float* g_s = sG(p);
         const float b = gb != nullptr ? wave_cumsum_log2(st.g)
                                       : (float)min(lane + 1, st.len) * gam2;
@@ -443,9 +444,9 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     };
 
     // Pipelined, one barrier per chunk, loads running one chunk ahead.
-    // Iteration m stages chunk m, then finishes chunk m-1 (A V and the output
-    // store, from buffers of parity p^1 and registers carried over) and forms
-    // chunk m's A, q.h partials and state update.
+    // Iteration m stages chunk m, forms chunk m-1's A V (from buffers of
+    // parity p^1 and registers carried over), chunk m's A, q.h partials and
+    // state update, and then stores chunk m-1's output.
     Stage st;
     load_chunk(0, st);
     bf16x8 vf_prev[2] = {};
@@ -459,12 +460,18 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       // a later wait for those loads then never has to wait for the stores
       load_chunk(m + 1, st);
       phase_intra(p ^ 1, vf_prev, mine0, mine1);
-      finalize(p ^ 1, prev_m, prev_cl, mine0, mine1);
+      // V fragments read before A: A's LDS writes would otherwise keep the
+      // compiler from issuing these reads ahead of it
+      load_vf(p, vf_prev);
       if (kh == 0) phase_A(p);   // A first on one wave of each SIMD, last on the other
       f32x4 oacc[4];
-      load_vf(p, vf_prev);
       phase_inter(p, oacc);
       phase_update(p, vf_prev);
+      // chunk m-1's output leaves after this chunk's products have been
+      // issued: read at the start of the step, the partner's exchange tiles
+      // made every wave wait on the LDS counter before its first product, and
+      // the step took ~10 % longer
+      finalize(p ^ 1, prev_m, prev_cl, mine0, mine1);
       exchange_write(p, oacc);
       if (kh != 0) phase_A(p);
       mine0 = oacc[0];
