@@ -284,49 +284,66 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     };
 
     // ---- per-chunk phases ----------------------------------------------------
-    // A = (Q K^T) (.) M, split into bf16 hi + lo, into sA(p)
-    auto phase_A = [&](int p) {
+    // A = (Q K^T) (.) M, split into bf16 hi + lo, into sA(p), for this wave's
+    // tiles (w, and w + 8 on waves 0 and 1).  The products and the epilogue
+    // that needs their results are separate calls so that other products can
+    // be issued between them; nmax bounds the tile count where the caller
+    // knows it, so unused accumulators take no registers.
+    auto phase_A_mma = [&](int p, f32x4 (&acc)[2][2], const int nmax) {
       const bf16* q_s = sQ(p);
       const bf16* k_s = sK(p);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int ti = w + L::NW * u;
+        if (u < nmax && ti < 10) {
+          const int ct = tile_c(ti), jt = tile_j(ti);
+          // every operand read first (one wait instead of one per step), then
+          // two independent accumulation chains
+          bf16x8 a[L::KSF], b[L::KSF];
+#pragma unroll
+          for (int s = 0; s < L::KSF; ++s) {
+            a[s] = *reinterpret_cast<const bf16x8*>(k_s + (16 * jt + r) * L::LDK + 32 * s + 8 * g4);
+            b[s] = *reinterpret_cast<const bf16x8*>(q_s + (16 * ct + r) * L::LDQ + 32 * s + 8 * g4);
+          }
+          acc[u][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+          acc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < L::KSF; ++s) acc[u][s & 1] = mfma(a[s], b[s], acc[u][s & 1]);
+        }
+      }
+    };
+    auto phase_A_epi = [&](int p, const f32x4 (&accs)[2][2], const int nmax) {
       const float* g_s = sG(p);
       bf16* a_hi = sA(p);
       bf16* a_lo = a_hi + C * LDA;
-      for (int ti = w; ti < 10; ti += L::NW) {
-        const int ct = tile_c(ti), jt = tile_j(ti);
-        // every operand read first (one wait instead of one per step), then
-        // two independent accumulation chains
-        bf16x8 a[L::KSF], b[L::KSF];
 #pragma unroll
-        for (int s = 0; s < L::KSF; ++s) {
-          a[s] = *reinterpret_cast<const bf16x8*>(k_s + (16 * jt + r) * L::LDK + 32 * s + 8 * g4);
-          b[s] = *reinterpret_cast<const bf16x8*>(q_s + (16 * ct + r) * L::LDQ + 32 * s + 8 * g4);
+      for (int u = 0; u < 2; ++u) {
+        const int ti = w + L::NW * u;
+        if (u < nmax && ti < 10) {
+          const int ct = tile_c(ti), jt = tile_j(ti);
+          const f32x4 acc = accs[u][0] + accs[u][1];   // acc[i] = q_c . k_j, c = 16ct + r, j = 16jt + 4g + i
+          const int c = 16 * ct + r;
+          const float bc = g_s[c];
+          const f32x4 bj = *reinterpret_cast<const f32x4*>(g_s + 16 * jt + 4 * g4);
+          float x[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = 16 * jt + 4 * g4 + i;
+            x[i] = (j <= c) ? acc[i] * exp2_hw(bc - bj[i]) * scale : 0.f;
+          }
+          uint32_t h0, l0, h1, l1;
+          split2(x[0], x[1], h0, l0);
+          split2(x[2], x[3], h1, l1);
+          const u32x2 hi = {h0, h1}, lo = {l0, l1};
+          *reinterpret_cast<u32x2*>(a_hi + c * LDA + 16 * jt + 4 * g4) = hi;
+          *reinterpret_cast<u32x2*>(a_lo + c * LDA + 16 * jt + 4 * g4) = lo;
         }
-        f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int s = 0; s < L::KSF; ++s) acc2[s & 1] = mfma(a[s], b[s], acc2[s & 1]);
-        const f32x4 acc = acc2[0] + acc2[1];   // acc[i] = q_c . k_j, c = 16ct + r, j = 16jt + 4g + i
-        const int c = 16 * ct + r;
-        const float bc = g_s[c];
-        const f32x4 bj = *reinterpret_cast<const f32x4*>(g_s + 16 * jt + 4 * g4);
-        float x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = 16 * jt + 4 * g4 + i;
-          x[i] = (j <= c) ? acc[i] * exp2_hw(bc - bj[i]) * scale : 0.f;
-        }
-        uint32_t h0, l0, h1, l1;
-        split2(x[0], x[1], h0, l0);
-        split2(x[2], x[3], h1, l1);
-        const u32x2 hi = {h0, h1}, lo = {l0, l1};
-        *reinterpret_cast<u32x2*>(a_hi + c * LDA + 16 * jt + 4 * g4) = hi;
-        *reinterpret_cast<u32x2*>(a_lo + c * LDA + 16 * jt + 4 * g4) = lo;
       }
     };
     // O^T partial = scale diag(2^b) (h^T Q^T) over this wave's K/2 state rows,
     // for c tiles in the order (own0, own1, partner's two)
     auto phase_inter = [&](int p, f32x4 (&oacc)[4]) {
       const bf16* q_s = sQ(p);
-      const float* g_s = sG(p);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -352,7 +369,11 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) oacc[ct] = mfma(hl, b[ct], oacc[ct]);
       }
-      // scale * diag(2^b): O^T column c = 16 ctile + r
+    };
+    // scale * diag(2^b): O^T column c = 16 ctile + r (a separate call, so
+    // that the wait for the q.h products falls after the update is issued)
+    auto inter_scale = [&](int p, f32x4 (&oacc)[4]) {
+      const float* g_s = sG(p);
 #pragma unroll
       for (int t = 0; t < 4; ++t) oacc[t] *= g_s[C + 16 * ctile[t] + r];
     };
@@ -459,21 +480,28 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       // the loads of chunk m + 1 go out before chunk m - 1's output stores:
       // a later wait for those loads then never has to wait for the stores
       load_chunk(m + 1, st);
-      phase_intra(p ^ 1, vf_prev, mine0, mine1);
-      // V fragments read before A: A's LDS writes would otherwise keep the
-      // compiler from issuing these reads ahead of it
-      load_vf(p, vf_prev);
-      if (kh == 0) phase_A(p);   // A first on one wave of each SIMD, last on the other
+      // Every wait for a product's result is placed after other products
+      // have been issued (measured on the long and packed workloads; each
+      // earlier placement cost 1-10 % of the step):
+      //  - A on the first wave of each SIMD: products, then q.h, then the
+      //    epilogue; on the second wave A comes last, after the exchange;
+      //  - chunk m-1's A V after q.h, the q.h scaling after the update;
+      //  - chunk m-1's output (the partner's exchange tiles, the stores) last.
+      f32x4 accA[2][2];
+      if (kh == 0) phase_A_mma(p, accA, 2);
       f32x4 oacc[4];
       phase_inter(p, oacc);
+      if (kh == 0) phase_A_epi(p, accA, 2);
+      phase_intra(p ^ 1, vf_prev, mine0, mine1);
+      load_vf(p, vf_prev);
       phase_update(p, vf_prev);
-      // chunk m-1's output leaves after this chunk's products have been
-      // issued: read at the start of the step, the partner's exchange tiles
-      // made every wave wait on the LDS counter before its first product, and
-      // the step took ~10 % longer
+      inter_scale(p, oacc);
       finalize(p ^ 1, prev_m, prev_cl, mine0, mine1);
       exchange_write(p, oacc);
-      if (kh != 0) phase_A(p);
+      if (kh != 0) {
+        phase_A_mma(p, accA, 1);
+        phase_A_epi(p, accA, 1);
+      }
       mine0 = oacc[0];
       mine1 = oacc[1];
       prev_m = m;

@@ -222,10 +222,9 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
 
   // ---- output tile (ct, vh) of chunk m: rows 16 ct + 4 g4 + i, column
   //      16 vh + r ---------------------------------------------------------------
-  auto finish = [&](int m) {
+  auto finish = [&](int m) -> f32x4 {
     const float* sg = sG(m % 3);
     const bf16* sv = sV(m % 3);
-    const int cl = min(C, len - m * C);
     f32x4 acc = *reinterpret_cast<const f32x4*>(sPb + (16 * vh + r) * LDP + 16 * ct + 4 * g4);
 #pragma unroll
     for (int w2 = 1; w2 < NW; ++w2)
@@ -241,6 +240,12 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
       acc = mfma(af[1][0], vf, acc);
       acc = mfma(af[1][1], vf, acc);
     }
+    return acc;
+  };
+  // stored one chunk later, after that chunk's q.h products are issued, so
+  // the wait for this tile's A V products does not hold the wave
+  auto store_out = [&](int m, const f32x4& acc) {
+    const int cl = min(C, len - m * C);
     const auto ro = make_rsrc(ob + (int64_t)m * C * RSO, (uint32_t)cl * RSO * (uint32_t)sizeof(TOut));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -274,6 +279,7 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
   decay_v(0);
   __syncthreads();
 
+  f32x4 oprev = {0.f, 0.f, 0.f, 0.f};
   for (int m = 0; m < nchunks; ++m) {
     const float* sg = sG(m % 3);
     const bf16* stv = sT(m & 1);
@@ -299,6 +305,7 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
           pacc[c2] = mfma32(qf[c2][rt][s], hl, pacc[c2]);
         }
       }
+    if (m > 0) store_out(m - 1, oprev);
     load_q(m + 1);
 
     // ---- 2. state update: h <- dall h + K^T (decayed V hi + lo) ------------
@@ -331,8 +338,8 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
     }
     __syncthreads();
 
-    // ---- 4. output of chunk m; next decayed V; V and gates two ahead -------
-    finish(m);
+    // ---- 4. output tile of chunk m; next decayed V; V and gates two ahead --
+    oprev = finish(m);
     load_a(m + 1);
     if (m + 1 < nchunks) decay_v(m + 1);
     store_vg(vg, (m + 2) % 3);
@@ -340,6 +347,7 @@ chunk_fwd_bf16_wide_kernel(const bf16* __restrict__ qfr, const bf16* __restrict_
     __syncthreads();
   }
 
+  if (nchunks > 0) store_out(nchunks - 1, oprev);
   if (ht != nullptr) {
     float* htu = ht + ((int64_t)seq * H + hd) * K * V + (int64_t)(vt * VT + l32) * sl.cs;
 #pragma unroll
