@@ -373,9 +373,14 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // scale * diag(2^b): O^T column c = 16 ctile + r (a separate call, so
     // that the wait for the q.h products falls after the update is issued)
     auto inter_scale = [&](int p, f32x4 (&oacc)[4]) {
-      const float* g_s = sG(p);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) oacc[t] *= g_s[C + 16 * ctile[t] + r];
+      // the four factors from one base (immediate offsets, one wait); ctile
+      // is {0, 3, 1, 2} for kh = 0 and {1, 2, 0, 3} for kh = 1
+      const float* gs = sG(p) + C + r;
+      const float s0 = gs[0], s1 = gs[16], s2 = gs[32], s3 = gs[48];
+      oacc[0] *= kh == 0 ? s0 : s1;
+      oacc[1] *= kh == 0 ? s3 : s2;
+      oacc[2] *= kh == 0 ? s1 : s0;
+      oacc[3] *= kh == 0 ? s2 : s3;
     };
     // V fragments vf[s][e] = V[32s + 8g + e][16vc + r]
     auto load_vf = [&](int p, bf16x8 (&vf)[2]) {
@@ -452,12 +457,15 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       x[(w * 2 + 0) * 64 + lane] = oacc[2];
       x[(w * 2 + 1) * 64 + lane] = oacc[3];
     };
-    // own tiles + partner's partial, scaled, stored (rows past the chunk's end
-    // fall outside the descriptor and are dropped; cl = 0 stores nothing)
-    auto finalize = [&](int px, int m, int cl, f32x4 mine0, f32x4 mine1) {
+    // the partner's two tiles of this wave's own output rows
+    auto exchange_read = [&](int px, f32x4& x0, f32x4& x1) {
       const f32x4* x = sX(px);
-      const f32x4 x0 = x[((w ^ 4) * 2 + 0) * 64 + lane];
-      const f32x4 x1 = x[((w ^ 4) * 2 + 1) * 64 + lane];
+      x0 = x[((w ^ 4) * 2 + 0) * 64 + lane];
+      x1 = x[((w ^ 4) * 2 + 1) * 64 + lane];
+    };
+    // own tiles + partner's partial (x0, x1), stored (rows past the chunk's end
+    // fall outside the descriptor and are dropped; cl = 0 stores nothing)
+    auto finalize = [&](int m, int cl, f32x4 mine0, f32x4 mine1, const f32x4& x0, const f32x4& x1) {
       const auto ro = make_rsrc(ob + (int64_t)m * C * RSO, (uint32_t)cl * RSO * sizeof(TOut));
       const uint32_t c0 = 16 * own0 + r, c1 = 16 * own1 + r;
       store4<TOut>(ro, c0 * RSO * (uint32_t)sizeof(TOut) + ocol, mine0 + x0);
@@ -486,7 +494,8 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       //  - A on the first wave of each SIMD: products, then q.h, then the
       //    epilogue; on the second wave A comes last, after the exchange;
       //  - chunk m-1's A V after q.h, the q.h scaling after the update;
-      //  - chunk m-1's output (the partner's exchange tiles, the stores) last.
+      //  - chunk m-1's output stores last, the partner's exchange tiles
+      //    for them read before the update.
       f32x4 accA[2][2];
       if (kh == 0) phase_A_mma(p, accA, 2);
       f32x4 oacc[4];
@@ -494,9 +503,11 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       if (kh == 0) phase_A_epi(p, accA, 2);
       phase_intra(p ^ 1, vf_prev, mine0, mine1);
       load_vf(p, vf_prev);
+      f32x4 x0, x1;
+      exchange_read(p ^ 1, x0, x1);
       phase_update(p, vf_prev);
       inter_scale(p, oacc);
-      finalize(p ^ 1, prev_m, prev_cl, mine0, mine1);
+      finalize(prev_m, prev_cl, mine0, mine1, x0, x1);
       exchange_write(p, oacc);
       if (kh != 0) {
         phase_A_mma(p, accA, 1);
@@ -516,7 +527,11 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     __syncthreads();
     const int pl = (nchunks - 1) & 1;
     phase_intra(pl, vf_prev, mine0, mine1);
-    finalize(pl, prev_m, prev_cl, mine0, mine1);
+    {
+      f32x4 x0, x1;
+      exchange_read(pl, x0, x1);
+      finalize(prev_m, prev_cl, mine0, mine1, x0, x1);
+    }
 
     if (ht != nullptr && last) {
       float* htu = ht + ((int64_t)seq * H + hd) * K * V;
