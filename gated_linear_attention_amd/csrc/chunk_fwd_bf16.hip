@@ -485,9 +485,6 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const int cl = st.len;
       store_chunk(p, st);
       __syncthreads();   // chunk m staged; chunk m-1's A and exchange tiles visible
-      // the loads of chunk m + 1 go out before chunk m - 1's output stores:
-      // a later wait for those loads then never has to wait for the stores
-      load_chunk(m + 1, st);
       // Every wait for a product's result is placed after other products
       // have been issued (measured on the long and packed workloads; each
       // earlier placement cost 1-10 % of the step):
@@ -496,8 +493,13 @@ chunk_fwd_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       //  - chunk m-1's A V after q.h, the q.h scaling after the update;
       //  - chunk m-1's output stores last, the partner's exchange tiles
       //    for them read before the update.
+      // The loads of chunk m + 1 go out after the first wave's A products
+      // (before them they held up the step's first products: 4-6 % of the
+      // step) and before chunk m - 1's output stores, so waiting for them
+      // never waits for the stores.
       f32x4 accA[2][2];
       if (kh == 0) phase_A_mma(p, accA, 2);
+      load_chunk(m + 1, st);
       f32x4 oacc[4];
       phase_inter(p, oacc);
       if (kh == 0) phase_A_epi(p, accA, 2);
