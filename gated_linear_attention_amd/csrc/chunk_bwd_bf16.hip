@@ -601,7 +601,6 @@ chunk_bwd_state_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__
       if (lane == 0) sDall = exp2f(blast);
     }
     __syncthreads();   // rows, tile and weights staged
-    if (it + 1 < nchunks) load_chunk(it + 1);
     // weighted tile, split: thread tid takes 8 columns of one token
     {
       const int c = tid / (VS / 8), c8 = 8 * (tid % (VS / 8));
@@ -619,6 +618,9 @@ chunk_bwd_state_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__
       *reinterpret_cast<bf16x8*>(sYd + C * LDY + c * LDY + c8) = lo;
     }
     __syncthreads();   // weighted tile split
+    // the next chunk's rows load from here (issued before the split they
+    // delayed it, and with it every wave's first product: ~2 % of the pass)
+    if (it + 1 < nchunks) load_chunk(it + 1);
     const float dall = sDall;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
