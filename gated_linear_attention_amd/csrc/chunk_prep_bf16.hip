@@ -31,9 +31,10 @@
 // stored once per (chunk, kv head), by the group's first query head.
 //
 // One workgroup of four waves per (chunk, query head), walking the keys in
-// slices of 128: while a slice's K rows go to LDS and its Q and K^T blocks are
-// written out, the next slice's K rows and Q blocks are already loading, so
-// the reads and the writes of a workgroup overlap.  Q K^T runs on
+// slices of 128.  Every slice's K rows and Q blocks are loaded into registers
+// up front (a slice staged while only the next one was loading waited a full
+// memory latency per slice: -4 % on the K = 512 call), then each slice's K
+// rows go to LDS and its Q and K^T blocks are written out.  Q K^T runs on
 // v_mfma_f32_32x32x16_bf16: wave w covers query rows [32 (w / 2), +32) over
 // half of every slice's keys (blocks 4 sl + 2 (w % 2) + {0, 1}); the two halves
 // are added in LDS.
@@ -112,32 +113,31 @@ chunk_prep_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // ---- slice loads: the K slice (all rows) and this wave's Q blocks ---------
   const auto rk = make_rsrc(k + (t0 * Hkv + hk) * (int64_t)K, (uint32_t)cl * RSK * 2);
   const auto rq = make_rsrc(q + (t0 * H + hd) * (int64_t)K, (uint32_t)cl * RS * 2);
-  u32x4 kx[NKS];
-  bf16x8 qa[2][2], qb[2][2];   // Q blocks of two consecutive slices
-  auto load_k = [&](int sl) {
-#pragma unroll
-    for (int i = 0; i < NKS; ++i) {
-      const int p = tid + NTP * i;
-      kx[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)((p / KP) * RSK + KSL * sl + (p % KP) * 8) * 2,
-                                                    0, 0);
-    }
-  };
-  auto load_q = [&](int sl, bf16x8 (&qx)[2][2]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        qx[i][s] = __builtin_bit_cast(
-            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                        rq, (uint32_t)((32 * c2 + l32) * RS + 32 * (4 * sl + 2 * kh2 + i) + 16 * s + 8 * hf) * 2,
-                        0, 0));
-  };
-  load_k(0);
-  load_q(0, qa);
+  // the gate word first: the gate scan waits for it alone, not for the rows
   float gx = 0.f;
   if (w == 0 && g != nullptr) {
     const auto rg = make_rsrc(g + t0 * H + hd, (uint32_t)cl * H * 4);
     gx = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)(lane * H * 4), 0, 0));
+  }
+  // every slice's K rows and Q blocks, loaded up front
+  u32x4 kx[NS][NKS];
+  bf16x8 qx[NS][2][2];
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) {
+#pragma unroll
+    for (int i = 0; i < NKS; ++i) {
+      const int p = tid + NTP * i;
+      kx[sl][i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rk, (uint32_t)((p / KP) * RSK + KSL * sl + (p % KP) * 8) * 2, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        qx[sl][i][s] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                        rq, (uint32_t)((32 * c2 + l32) * RS + 32 * (4 * sl + 2 * kh2 + i) + 16 * s + 8 * hf) * 2,
+                        0, 0));
   }
 
   // ---- gates ----------------------------------------------------------------
@@ -166,22 +166,18 @@ chunk_prep_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int a = 0; a < 16; ++a) acc[t][a] = 0.f;
   bf16* qo = qfr + task * (int64_t)K * C;
   bf16* kt = ktf + ((int64_t)gc * Hkv + hk) * K * C;
-  auto slice = [&](const int sl, const bf16x8 (&qx)[2][2], bf16x8 (&qn)[2][2]) {
+  auto slice = [&](const int sl) {
 #pragma unroll
     for (int i = 0; i < NKS; ++i) {
       const int p = tid + NTP * i;
-      *reinterpret_cast<u32x4*>(sK + (p / KP) * LDK + (p % KP) * 8) = kx[i];
+      *reinterpret_cast<u32x4*>(sK + (p / KP) * LDK + (p % KP) * 8) = kx[sl][i];
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        *reinterpret_cast<bf16x8*>(qo + ((((4 * sl + 2 * kh2 + i) * 2 + c2) * 2 + s) * 64 + lane) * 8) = qx[i][s];
+        *reinterpret_cast<bf16x8*>(qo + ((((4 * sl + 2 * kh2 + i) * 2 + c2) * 2 + s) * 64 + lane) * 8) = qx[sl][i][s];
     __syncthreads();   // slice sl staged
-    if (sl + 1 < NS) {
-      load_k(sl + 1);
-      load_q(sl + 1, qn);
-    }
     // K^T blocks (kb, ts) of this slice's four key blocks, once per kv head
     if (write_kt) {
 #pragma unroll
@@ -200,19 +196,16 @@ chunk_prep_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int s = 0; s < 2; ++s) {
         const int col = 32 * (2 * kh2 + i) + 16 * s + 8 * hf;
         const bf16x8 k0f = *reinterpret_cast<const bf16x8*>(sK + l32 * LDK + col);
-        acc[0] = mfma32(qx[i][s], k0f, acc[0]);
+        acc[0] = mfma32(qx[sl][i][s], k0f, acc[0]);
         if (c2 == 1) {
           const bf16x8 k1f = *reinterpret_cast<const bf16x8*>(sK + (32 + l32) * LDK + col);
-          acc[1] = mfma32(qx[i][s], k1f, acc[1]);
+          acc[1] = mfma32(qx[sl][i][s], k1f, acc[1]);
         }
       }
     __syncthreads();   // every read of the slice is done
   };
 #pragma unroll
-  for (int sl = 0; sl < NS; sl += 2) {
-    slice(sl, qa, qb);
-    if (sl + 1 < NS) slice(sl + 1, qb, qa);
-  }
+  for (int sl = 0; sl < NS; ++sl) slice(sl);
 
   // ---- add the two key halves in LDS (fixed order: deterministic) ---------
   // acc[t][4 jj + i] = D[c = 32 c2 + 8 jj + 4 hf + i][j = 32 t + l32]
