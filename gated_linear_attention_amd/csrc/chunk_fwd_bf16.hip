@@ -34,10 +34,12 @@
 //     gfx950 transposing LDS read ds_read_b64_tr_b16;
 //   * staging is double-buffered in LDS with one barrier per chunk, the rows
 //     of chunk m + 1 loading into registers while chunk m computes;
-//   * the phases of a chunk step are independent of one another, and the two
+//   * the phases of a chunk step are independent of one another: the two
 //     waves that share a SIMD (kh = 0 and kh = 1) take them in different
 //     orders (A first or last), so that one of them forms A while the other
-//     runs its q.h and state-update products.
+//     runs its q.h and state-update products, and every wave issues other
+//     products before it waits for a product's result (the step is a latency
+//     chain; where a wave stalls decides its length).
 //
 // Precision: the state, the accumulation and the output are fp32.  The three
 // MFMA operands that are not exact bf16 inputs -- the decay-masked A, the
