@@ -164,6 +164,7 @@ recurrent_step_vk_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   constexpr int BATCH = 16;                   // rows in flight per thread
   static_assert(RG >= 2 && RG * TPR == 256, "K must be a power of two in [32, 512]");
   __shared__ float part[1024 * NSUB];
+  __shared__ float vsh[1024];         // the unit's v row (V <= 1024)
 
   const int64_t unit = blockIdx.x;    // n * H + h
   const uint32_t n = blockIdx.x / (uint32_t)H;
@@ -184,17 +185,24 @@ recurrent_step_vk_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   const TIn* vu = v + ukv * V;
   f32x4* S = reinterpret_cast<f32x4*>(state + unit * (int64_t)K * V);
   const int rpt = V / RG;             // rows per row group (V % 32 == 0)
+  auto load_batch = [&](int b0, f32x4 (&sv)[BATCH]) {
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b)
+      if (b0 + b < rpt) sv[b] = __builtin_nontemporal_load(&S[(int64_t)(rg + RG * (b0 + b)) * TPR + cq]);
+  };
+  // v goes through LDS once per workgroup (one load per element instead of
+  // one per element and row group), staged while the first batch of state
+  // rows is in flight
+  f32x4 sv[BATCH];
+  load_batch(0, sv);
+  for (int c = tid; c < V; c += 256) vsh[c] = to_f32(vu[c]);
+  __syncthreads();
   for (int b0 = 0; b0 < rpt; b0 += BATCH) {
-    f32x4 sv[BATCH];
+    if (b0 > 0) load_batch(b0, sv);
     float vr[BATCH];
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      if (b0 + b < rpt) {
-        const int row = rg + RG * (b0 + b);
-        sv[b] = __builtin_nontemporal_load(&S[(int64_t)row * TPR + cq]);
-        vr[b] = to_f32(vu[row]);
-      }
-    }
+    for (int b = 0; b < BATCH; ++b)
+      if (b0 + b < rpt) vr[b] = vsh[rg + RG * (b0 + b)];
     float pq[BATCH];
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) {
