@@ -416,7 +416,8 @@ def parallel_fwd(q, k, v, g=None, g_gamma=None, scale=None, output_attn=True, ou
     the parallel entry writes out the decayed attention matrix).  Per batch
     row and query head, A[i, j] = scale (q_i . k_j) exp(G_i - G_j) for j <= i
     (G the running sum of the log gates) and 0 above the diagonal; o = A v.
-    Dense bf16 q [B, T, H, K], k [B, T, Hkv, K], v [B, T, Hkv, V]; g [B, T, H]
+    Dense q [B, T, H, K], k [B, T, Hkv, K], v [B, T, Hkv, V], all bf16 or all
+    float32 (float32 inputs run on the fp32 matrix cores); g [B, T, H]
     or g_gamma [H] (at most one).  Returns (o [B, T, H, V] in out_dtype
     (default: q's dtype), A [B, H, T, T] float32 or None)."""
     if not isinstance(q, torch.Tensor) or q.dim() != 4:

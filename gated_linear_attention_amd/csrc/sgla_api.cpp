@@ -1033,15 +1033,20 @@ sgla_status sgla_parallel_fwd(const sgla_chunk_args* args, const void* q, const 
   if (Hkv < 0 || a.H % Hkv != 0)
     return fail(SGLA_ERR_SHAPE, "num_kv_heads must divide H (got num_kv_heads=%d, H=%d)", a.num_kv_heads, a.H);
   if (a.K <= 0 || a.V <= 0) return fail(SGLA_ERR_SHAPE, "K and V must be > 0");
-  if (a.qkv_dtype == SGLA_F32)
-    return fail(SGLA_ERR_UNSUPPORTED, "the parallel form is implemented for bf16 q, k and v only");
-  if (a.qkv_dtype != SGLA_BF16)
+  if (a.qkv_dtype != SGLA_BF16 && a.qkv_dtype != SGLA_F32)
     return fail(SGLA_ERR_DTYPE, "qkv_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", a.qkv_dtype);
   if (a.o_dtype != SGLA_BF16 && a.o_dtype != SGLA_F32)
     return fail(SGLA_ERR_DTYPE, "o_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", a.o_dtype);
-  if (!sgla::parallel_supported(a.K, a.V))
+  const bool f32 = a.qkv_dtype == SGLA_F32;
+  if (!f32 && !sgla::parallel_supported(a.K, a.V))
     return fail(SGLA_ERR_UNSUPPORTED,
-                "the parallel form supports K in {64,128,256} and V a multiple of 16 in [16, 256] (got K=%d V=%d)",
+                "the parallel form supports K in {64,128,256} and V a multiple of 16 in [16, 256] for bf16 "
+                "inputs (got K=%d V=%d)",
+                a.K, a.V);
+  if (f32 && !sgla::parallel_f32_supported(a.K, a.V))
+    return fail(SGLA_ERR_UNSUPPORTED,
+                "the parallel form supports K and V multiples of 16 in [16, 256] for float32 inputs "
+                "(got K=%d V=%d)",
                 a.K, a.V);
   if (!std::isfinite(a.scale)) return fail(SGLA_ERR_INVALID_ARG, "scale must be finite");
   if (g != nullptr && g_gamma != nullptr)
@@ -1049,7 +1054,7 @@ sgla_status sgla_parallel_fwd(const sgla_chunk_args* args, const void* q, const 
   if ((int64_t)a.B * a.T > INT32_MAX)
     return fail(SGLA_ERR_UNSUPPORTED, "B*T = %lld tokens exceeds 2^31-1", (long long)a.B * a.T);
   // one batch row of k or v (plus a tile of slack) is addressed with 32-bit byte offsets
-  if (((int64_t)a.T + sgla::kChunk) * Hkv * std::max(a.K, a.V) * 2 > INT32_MAX)
+  if (!f32 && ((int64_t)a.T + sgla::kChunk) * Hkv * std::max(a.K, a.V) * 2 > INT32_MAX)
     return fail(SGLA_ERR_UNSUPPORTED, "T x num_kv_heads x max(K, V) too large for the parallel form (T=%d)", a.T);
   // the rows of A one workgroup writes are addressed with 32-bit byte offsets
   // (128 rows of T floats); T beyond that would need petabytes of A anyway
@@ -1080,7 +1085,7 @@ sgla_status sgla_parallel_fwd(const sgla_chunk_args* args, const void* q, const 
   p.K = a.K;
   p.V = a.V;
   p.o_f32 = a.o_dtype == SGLA_F32;
-  hipError_t e = sgla::launch_parallel_fwd(p, stream);
+  hipError_t e = f32 ? sgla::launch_parallel_fwd_f32(p, stream) : sgla::launch_parallel_fwd(p, stream);
   if (e != hipSuccess) return hip_fail(e, "launching the parallel-form kernel");
   return ok();
 }

@@ -342,12 +342,12 @@ struct StepNormalizerParams {
 hipError_t launch_chunk_normalizer(const NormalizerParams& p, hipStream_t stream);
 hipError_t launch_step_normalizer(const StepNormalizerParams& p, hipStream_t stream);
 
-// Parallel form: the decayed attention matrix of dense input written out
-// (bf16 q, k, v), and o = A v.
+// Parallel form: the decayed attention matrix of dense input written out,
+// and o = A v.
 struct ParallelParams {
-  const void* q;             // [B, T, H, K] bf16
-  const void* k;             // [B, T, Hkv, K] bf16
-  const void* v;             // [B, T, Hkv, V] bf16
+  const void* q;             // [B, T, H, K] bf16 (launch_parallel_fwd) or float32 (launch_parallel_fwd_f32)
+  const void* k;             // [B, T, Hkv, K], same dtype
+  const void* v;             // [B, T, Hkv, V], same dtype
   const float* g;            // [B, T, H] or nullptr
   const float* g_gamma;      // [H] or nullptr
   void* o;                   // [B, T, H, V], float32 when o_f32 else bf16
@@ -362,6 +362,13 @@ inline bool parallel_supported(int32_t K, int32_t V) {
 }
 
 hipError_t launch_parallel_fwd(const ParallelParams& p, hipStream_t stream);
+
+// float32 q, k, v: K and V multiples of 16 in [16, 256].
+inline bool parallel_f32_supported(int32_t K, int32_t V) {
+  return K >= 16 && K <= 256 && K % 16 == 0 && V >= 16 && V <= 256 && V % 16 == 0;
+}
+
+hipError_t launch_parallel_fwd_f32(const ParallelParams& p, hipStream_t stream);
 
 struct StepParams {
   const void* q;

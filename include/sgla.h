@@ -368,7 +368,8 @@ sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t num_kv_heads, int3
  *            read; num_seqs, chunk_size, output_final_state and
  *            state_v_first are not (dense input only, no initial or final
  *            state).
- *   q        [B, T, H, K] bf16;  k [B, T, Hkv, K] bf16;  v [B, T, Hkv, V] bf16
+ *   q        [B, T, H, K];  k [B, T, Hkv, K];  v [B, T, Hkv, V]: all bf16 or
+ *            all float32 (qkv_dtype)
  *   g        [B, T, H] float32 log gates, or NULL
  *   g_gamma  [H] float32 per-head log decay, or NULL (at most one of the two)
  *   o        [B, T, H, V] in o_dtype
@@ -376,8 +377,11 @@ sgla_status sgla_recurrent_step(int32_t N, int32_t H, int32_t num_kv_heads, int3
  *            or NULL to compute o only.  B * H * T * T * 4 bytes: the caller
  *            sizes T accordingly (T <= 4194304 when A is written).
  * All buffers 16-byte aligned; no output may alias an input.  No workspace,
- * one kernel launch.  Supported: bf16 q, k, v (float32 inputs return
- * SGLA_ERR_UNSUPPORTED), K in {64, 128, 256}, V a multiple of 16 in [16, 256].
+ * one kernel launch.  Supported: bf16 q, k, v with K in {64, 128, 256} and V
+ * a multiple of 16 in [16, 256] (bf16 matrix cores, A split into hi + lo);
+ * float32 q, k, v with K and V multiples of 16 in [16, 256] (fp32 matrix
+ * cores, decay exponents formed in float64).  Other shapes return
+ * SGLA_ERR_UNSUPPORTED.
  */
 sgla_status sgla_parallel_fwd(const sgla_chunk_args *args,
                               const void *q, const void *k, const void *v,

@@ -446,7 +446,10 @@ PAR_CASES = [
     ("K=512", dict(K=512), {}, UNSUPPORTED, "K in"),
     ("V=24", dict(V=24), {}, UNSUPPORTED, "V a multiple"),
     ("V=272", dict(V=272), {}, UNSUPPORTED, "V a multiple"),
-    ("float32 inputs", dict(qkv=F32), {}, UNSUPPORTED, "bf16"),
+    ("float32 K=40", dict(qkv=F32, K=40), {}, UNSUPPORTED, "float32 inputs"),
+    ("float32 K=272", dict(qkv=F32, K=272), {}, UNSUPPORTED, "float32 inputs"),
+    ("float32 V=8", dict(qkv=F32, V=8), {}, UNSUPPORTED, "float32 inputs"),
+    ("bf16 K=96", dict(K=96), {}, UNSUPPORTED, "bf16 inputs"),
     ("fp16", dict(qkv=3), {}, DTYPE, "qkv_dtype"),
     ("o dtype", dict(od=3), {}, DTYPE, "o_dtype"),
     ("both gates", {}, dict(gg=True), INVALID, "mutually exclusive"),
