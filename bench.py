@@ -35,6 +35,8 @@ The JSON line also carries:
   normalizer    -- sgla_chunk_normalizer on the same workload, HBM GB/s;
   gla           -- sgla_gla_chunk_fwd (per-key gates) on the same workload;
   parallel      -- sgla_parallel_fwd with the decayed attention matrix;
+  parallel_f32  -- the same for float32 inputs (B=1, T=4096, H=16,
+                   K=V=128), priced against the fp32 matrix-core peak;
   cpu_baseline  -- the fp64 CPU oracle timed on the host cores on whole
                    batches of the headline workload (a reported baseline
                    only), with the host CPU model; the same leg runs the
@@ -78,6 +80,7 @@ KERNEL_SOURCES = {
     "chunk_fwd_f32_kernel": ("chunk_fwd_f32.hip", "gate_scan.h", "unit_map.h"),
     "recurrent_step_kernel": ("recurrent_step.hip",),
     "parallel_fwd_kernel": ("parallel_fwd.hip", "mfma_common.h", "gate_scan.h", "unit_map.h"),
+    "parallel_fwd_f32_kernel": ("parallel_fwd_f32.hip", "mfma_common.h", "gate_scan.h", "unit_map.h"),
 }
 
 
@@ -608,10 +611,13 @@ def bench_gla(workload: str, steps: int, warmup: int, warm_seconds: float):
 
 def bench_parallel(workload: str, steps: int, warmup: int, warm_seconds: float):
     """sgla_parallel_fwd on a dense workload: the decayed attention matrix A
-    [B, H, T, T] float32 (zeros above the diagonal) and o = A v.  Writing A
-    dominates the algorithmic bytes (B H T^2 4 against a few tens of MB of
-    q, k, v, g and o), so the call is priced against HBM; a plain fill of a
-    buffer of A's size is timed beside it as the practical write ceiling."""
+    [B, H, T, T] float32 (zeros above the diagonal) and o = A v.  With bf16
+    inputs writing A dominates (B H T^2 4 bytes against a few tens of MB of
+    q, k, v, g and o), so the call is priced against HBM, with a plain fill
+    of a buffer of A's size timed beside it as the practical write ceiling.
+    With float32 inputs the products run on the fp32 matrix cores, whose
+    157.3 TFLOP/s put the call's floor above the HBM one: it is priced
+    against that peak (the HBM figure is reported beside it)."""
     import numpy as np
     import torch
 
@@ -622,7 +628,9 @@ def bench_parallel(workload: str, steps: int, warmup: int, warm_seconds: float):
     inp = make_chunk_inputs(w)
     dev = torch.device("cuda:0")
     t = lambda a, dt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
-    q, k, v = t(inp["q"], torch.bfloat16), t(inp["k"], torch.bfloat16), t(inp["v"], torch.bfloat16)
+    f32 = inp["dtype"] == "f32"
+    dt = torch.float32 if f32 else torch.bfloat16
+    q, k, v = t(inp["q"], dt), t(inp["k"], dt), t(inp["v"], dt)
     g, gg = t(inp["g"], torch.float32), t(inp["g_gamma"], torch.float32)
     step = lambda _i: sgla.parallel_fwd(q, k, v, g=g, g_gamma=gg, scale=inp["scale"], output_attn=True,
                                         out_dtype=torch.float32)
@@ -645,7 +653,7 @@ def bench_parallel(workload: str, steps: int, warmup: int, warm_seconds: float):
     ms = sum(per) / len(per)
     B, T, H, K, V, Hkv = inp["B"], inp["T"], inp["H"], inp["K"], inp["V"], inp["Hkv"]
     abytes = B * H * T * T * 4
-    nbytes = (B * T * (H * K + Hkv * (K + V)) * 2 + (B * T * H * 4 if g is not None else 0)
+    nbytes = (B * T * (H * K + Hkv * (K + V)) * (4 if f32 else 2) + (B * T * H * 4 if g is not None else 0)
               + B * T * H * V * 4 + abytes)
     flops = B * H * (T * (T + 1) // 2) * (2 * K + 2 * V)   # causal q.k and A v, as in the definition
     fill_buf = torch.empty(B * H * T * T, device=dev, dtype=torch.float32)
@@ -654,6 +662,21 @@ def bench_parallel(workload: str, steps: int, warmup: int, warm_seconds: float):
     fill_gbs = abytes / (fper[len(fper) // 2] * 1e-3) / 1e9
     del fill_buf
     gbs = nbytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    if f32:
+        return {"workload": workload, "kernel": "parallel_fwd_f32_kernel", "launches_per_call": 1,
+                "config": {"B": B, "T": T, "H": H, "num_kv_heads": Hkv, "K": K, "V": V, "qkv_dtype": "f32",
+                           "gate": "g" if g is not None else ("g_gamma" if gg is not None else "none"),
+                           "attn": "float32 [B, H, T, T]", "o_dtype": "f32"},
+                "ms_per_call_mean": round(ms, 5), "ms_per_call_median": round(per[len(per) // 2], 5),
+                "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+                "algorithmic_bytes_per_call": int(nbytes), "algorithmic_flops_per_call": int(flops),
+                "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": F32_MFMA_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tflops / F32_MFMA_PEAK_TFLOPS, 4),
+                             "dtype": "f32", "traffic": load_traffic(workload, "parallel_fwd_f32_kernel")},
+                "hbm": {"achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                "write_ceiling": {"kernel": "torch fill_ of an A-sized float32 buffer",
+                                  "achieved_gbs": round(fill_gbs, 1)}}
     return {"workload": workload, "kernel": "parallel_fwd_kernel", "launches_per_call": 1,
             "config": {"B": B, "T": T, "H": H, "num_kv_heads": Hkv, "K": K, "V": V,
                        "gate": "g" if g is not None else ("g_gamma" if gg is not None else "none"),
@@ -821,7 +844,9 @@ def main():
         return
     if a.parallel_only:
         print(json.dumps({"parallel": bench_parallel("parallel_bf16_k128", a.steps, a.warmup,
-                                                     a.warm_seconds)}), flush=True)
+                                                     a.warm_seconds),
+                          "parallel_f32": bench_parallel("parallel_f32_k128", a.steps, a.warmup,
+                                                         a.warm_seconds)}), flush=True)
         return
     legs = [a.workload] + ([] if a.only_headline else [w for w in CHUNK_LEGS if w != a.workload])
     results, records = {}, {}
@@ -865,6 +890,7 @@ def main():
         out["normalizer"] = bench_normalizer(a.backward_workload, 20, a.warmup, a.warm_seconds)
         out["gla"] = bench_gla(a.backward_workload, 20, a.warmup, a.warm_seconds)
         out["parallel"] = bench_parallel("parallel_bf16_k128", 10, a.warmup, a.warm_seconds)
+        out["parallel_f32"] = bench_parallel("parallel_f32_k128", 5, a.warmup, a.warm_seconds)
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline and parity", file=sys.stderr, flush=True)
         out["cpu_baseline"], parity = cpu_baseline(inp, results, decode_check)

@@ -7,17 +7,24 @@
 //     A[i][j] = scale * (q_i . k_j) * exp(G_i - G_j)   for j <= i, else 0
 //     o_i     = sum_j A[i][j] v_j
 //
-// The products run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32: fp32
-// operands, fp32 accumulation), so no operand is rounded below float32 and
-// the 1e-4 bar of float32 inputs holds.  One workgroup (4 waves, 16 query
+// No operand is rounded below float32.  One workgroup (4 waves, 16 query
 // rows each) owns 64 query rows of one (batch row, query head) and walks the
 // 64-key tiles from the one holding its diagonal back to the first:
-//   S^T = K_j Q_i^T      queries in registers, the key tile from LDS; the
-//                        result layout puts four consecutive keys of one
-//                        query row in each lane (one 16-byte store of A);
-//   O^T += V_j^T A^T     the lane's A values are already the B operand of
+//   S^T = K_j Q_i^T      on the fp64 matrix cores (v_mfma_f64_16x16x4_f64:
+//                        the float32 inputs' products are exact in float64
+//                        and so is nearly all of their sum), queries in
+//                        registers, the key tile from LDS; A = scale S decay
+//                        is formed in float64 and rounded once.  A is mostly
+//                        zeros and decayed entries, so its RMS is a few
+//                        hundredths of its largest entries: a float32 dot
+//                        product's ~10 ulp on those entries would already
+//                        exceed 1e-4 of the RMS;
+//   O^T += V_j^T A^T     on the fp32 matrix cores (v_mfma_f32_16x16x4_f32);
+//                        the lane's A values are already the B operand of
 //                        this product (the key order of the k-steps follows
-//                        the result layout), so A never leaves registers.
+//                        the result layout of S^T, which puts four
+//                        consecutive keys of one query row in each lane: one
+//                        16-byte store of A), so A never leaves registers.
 // The decay exponent is formed in float64 before its one rounding to float32:
 // the query's running gate inside the query tile, plus the gate totals of the
 // key tiles walked so far, minus the key's running gate inside its tile.  A
@@ -50,6 +57,13 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f64_16x16x4_f64: the same operand layout, float64 values, but the
+// result rows interleaved: result D[m = g + 4i][n = r] (measured)
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f64x4 mfma4d(double a, double b, f64x4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ double gate_at(const ParallelParams& p, int b, int h, int t) {
   if (t >= p.T) return 0.0;
   if (p.g != nullptr) return (double)p.g[((int64_t)b * p.T + t) * p.H + h];
@@ -79,7 +93,7 @@ __global__ __launch_bounds__(NTH) void parallel_fwd_f32_kernel(ParallelParams p)
   const int i0 = iq * C;
   const int qrow = 16 * w + r;   // this lane's query row inside the tile
   const int qi = i0 + qrow;
-  const int nkb = K / 16, nvt = V / 16;
+  const int nkb = K / 16, nvt = V / 16;   // blocks past these are zero padding
 
   // qf[m][e] = q[qi][16 m + 4 g4 + e]: the B operand of S^T for k-step (m, e)
   const float* qg = static_cast<const float*>(p.q);
@@ -142,28 +156,33 @@ __global__ __launch_bounds__(NTH) void parallel_fwd_f32_kernel(ParallelParams p)
     if (jt < iq) D += sTot;
     const double base = Rq + D * kRcpLn2d;  // exponent of A = base - sL[key] (log2)
 
-    // S^T = K_j Q_i^T: s[kb][e] = k_j . q_i for key j = j0 + 16 kb + 4 g4 + e
-    f32x4 s[4];
+    // S^T = K_j Q_i^T: sd[kb][e] = k_j . q_i for key j = j0 + 16 kb + 4 g4 + e.
+    // Product row m holds key 4 (m % 4) + m / 4 of the 16-key block, so that
+    // the interleaved result rows g4 + 4 e are the keys 4 g4 + e.
+    const int krow = 4 * (r & 3) + (r >> 2);
+    f64x4 sd[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < 4; ++kb) sd[kb] = f64x4{0.0, 0.0, 0.0, 0.0};
+    // (padding columns of q and of the key tile are zeros: every product is
+    // issued, a runtime bound here would make the compiler copy accumulators)
 #pragma unroll
     for (int m = 0; m < NKB; ++m) {
-      if (m < nkb) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const f32x4 ka = *reinterpret_cast<const f32x4*>(sK + (16 * kb + r) * LDK + 16 * m + 4 * g4);
+      for (int kb = 0; kb < 4; ++kb) {
+        const f32x4 ka = *reinterpret_cast<const f32x4*>(sK + (16 * kb + krow) * LDK + 16 * m + 4 * g4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s[kb] = mfma4(ka[e], qf[m][e], s[kb]);
-        }
+        for (int e = 0; e < 4; ++e) sd[kb] = mfma4d((double)ka[e], (double)qf[m][e], sd[kb]);
       }
     }
-    // decay, scale and (in the diagonal tile) the causal mask
+    // decay, scale and (in the diagonal tile) the causal mask; A rounded once
+    f32x4 s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int jj = 16 * kb + 4 * g4 + e;
-        const float x = (s[kb][e] * scale) * exp2_hw((float)(base - sL[jj]));
+        const float dec = exp2_hw((float)(base - sL[jj]));
+        const float x = (float)(sd[kb][e] * (double)scale * (double)dec);
         s[kb][e] = (jt == iq && jj > qrow) ? 0.f : x;
       }
     }
@@ -191,8 +210,7 @@ __global__ __launch_bounds__(NTH) void parallel_fwd_f32_kernel(ParallelParams p)
       for (int e = 0; e < 4; ++e) {
         const float* vrow = sV + (16 * kb + 4 * g4 + e) * LDV + r;
 #pragma unroll
-        for (int vt = 0; vt < NVT; ++vt)
-          if (vt < nvt) O[vt] = mfma4(vrow[16 * vt], s[kb][e], O[vt]);
+        for (int vt = 0; vt < NVT; ++vt) O[vt] = mfma4(vrow[16 * vt], s[kb][e], O[vt]);   // zeros past V
       }
   }
 

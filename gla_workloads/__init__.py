@@ -128,6 +128,10 @@ CHUNK_CONFIGS["gqa_bf16_k64_h9kv3"] = ChunkWorkload(
 CHUNK_CONFIGS["parallel_bf16_k128"] = ChunkWorkload(
     "parallel_bf16_k128", B=2, T=4096, H=16, K=128, V=128, dtype="bf16", gate="g",
     output_final_state=False, seed=1006)
+# The parallel form for float32 inputs (fp32 matrix cores): one such row.
+CHUNK_CONFIGS["parallel_f32_k128"] = ChunkWorkload(
+    "parallel_f32_k128", B=1, T=4096, H=16, K=128, V=128, dtype="f32", gate="g",
+    output_final_state=False, seed=1007)
 DECODE_CONFIGS = {
     "decode_n256_h32_k128": DecodeWorkload("decode_n256_h32_k128", N=256, H=32, K=128, V=128,
                                            steps=64, dtype="bf16", seed=1004),

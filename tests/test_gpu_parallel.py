@@ -117,12 +117,14 @@ def test_parallel_empty():
     assert o.shape == (2, 0, 2, 64) and A.shape == (2, 2, 0, 0)
 
 
-def test_parallel_full_size_whole_tensor():
-    """The benchmark workload (B=2, T=4096, H=16, K=V=128, per-token gates) in
-    the benchmark's launch, every element of A and o against the oracle.  The
-    oracle runs one batch row at a time (A in float64 is 2.1 GB per row);
-    max |err| and the RMS are accumulated over the whole tensors."""
-    w = CHUNK_CONFIGS["parallel_bf16_k128"]
+@pytest.mark.parametrize("workload,tol", [("parallel_bf16_k128", TOL_BF16), ("parallel_f32_k128", TOL_F32)])
+def test_parallel_full_size_whole_tensor(workload, tol):
+    """The benchmark workloads (bf16: B=2, T=4096, H=16, K=V=128; float32: one
+    such row; per-token gates) in the benchmark's launch, every element of A
+    and o against the oracle.  The oracle runs one batch row at a time (A in
+    float64 is 2.1 GB per row); max |err| and the RMS are accumulated over
+    the whole tensors."""
+    w = CHUNK_CONFIGS[workload]
     inp = make_chunk_inputs(w)
     d = device_inputs(inp)
     o, A = sgla.parallel_fwd(d["q"], d["k"], d["v"], g=d["g"], scale=inp["scale"], output_attn=True,
@@ -148,8 +150,8 @@ def test_parallel_full_size_whole_tensor():
         del A_got, A_ref
         add("o", o[b].cpu().numpy(), o_ref[0])
     errs = {k: v[0] / np.sqrt(v[1] / v[2]) for k, v in acc.items()}
-    print(f"[parallel full] whole-tensor o {errs['o']:.2e} A {errs['A']:.2e}", flush=True)
-    assert errs["o"] <= TOL_BF16 and errs["A"] <= TOL_BF16
+    print(f"[parallel full {workload}] whole-tensor o {errs['o']:.2e} A {errs['A']:.2e}", flush=True)
+    assert errs["o"] <= tol and errs["A"] <= tol
 
 
 # float32 inputs: the fp32 matrix-core kernel, held to the float32 bar
@@ -166,6 +168,7 @@ F32_CASES = [
     small("f32_strong_gate", dtype="f32", B=1, T=300, K=64, V=128, gate_normalizer=0.1),
     small("f32_weak_gate", dtype="f32", B=1, T=300, K=128, V=64, gate_normalizer=10.0),
     small("f32_k256_v64_t300", dtype="f32", B=2, T=300, H=3, Hkv=1, K=256, V=64, gate="gamma"),
+    small("f32_k256_v128", dtype="f32", B=1, T=150, H=2, K=256, V=128),
     small("f32_negative_scale", dtype="f32", B=1, T=140, K=128, V=64, scale=-0.3),
     small("f32_zero_scale", dtype="f32", B=1, T=70, K=64, V=64, scale=0.0),
 ]
