@@ -159,7 +159,7 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   const int hd = um.hd, vt = um.vt;
   const int hk = hd / (H / Hkv);   // kv head whose k and v rows this query head reads
   const SeqInfo si = seq_info(seqs, um.rank, chunks_per_row);
-  const int nchunks = (si.len + C - 1) / C;
+  const int nchunks = (si.len + seqs.chunk - 1) / seqs.chunk;
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int64_t KV = (int64_t)K * V;
@@ -188,8 +188,8 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   float gx = 0.f;
   auto load_chunk = [&](int it) {
     const int m = rev ? nchunks - 1 - it : it;
-    const int64_t t0 = si.bos + (int64_t)m * C;
-    const int cl = min(C, si.len - m * C);
+    const int64_t t0 = si.bos + (int64_t)m * seqs.chunk;
+    const int cl = min(seqs.chunk, si.len - m * seqs.chunk);
     xt.load(rev ? q + (t0 * H + hd) * K : k + (t0 * Hkv + hk) * K, (int64_t)(rev ? H : Hkv) * K, cl);
     yt.load(rev ? dout + (t0 * H + hd) * V + ucol : v + (t0 * Hkv + hk) * V + ucol,
             (int64_t)(rev ? H : Hkv) * V, cl);
@@ -198,7 +198,7 @@ chunk_bwd_state_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   if (nchunks > 0) load_chunk(0);
   for (int it = 0; it < nchunks; ++it) {
     const int m = rev ? nchunks - 1 - it : it;
-    const int cl = min(C, si.len - m * C);
+    const int cl = min(seqs.chunk, si.len - m * seqs.chunk);
     // record: forward -> the state entering chunk m; reverse -> the gradient
     // of the state leaving chunk m
     float* rec = (rev ? dhbuf : hbuf) + ((int64_t)(si.chunk0 + m) * H + hd) * KV + ucol;
@@ -301,8 +301,8 @@ chunk_bwd_grad_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   } else {
     const int row = gc / chunks_per_row;
     const int m = gc - row * chunks_per_row;
-    t0 = (int64_t)row * seqs.T + (int64_t)m * C;
-    cl = min(C, seqs.T - m * C);
+    t0 = (int64_t)row * seqs.T + (int64_t)m * seqs.chunk;
+    cl = min(seqs.chunk, seqs.T - m * seqs.chunk);
   }
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
@@ -609,7 +609,7 @@ hipError_t launch_kv_group_sum(const float* src, float* dst, int64_t tokens, int
 }
 
 hipError_t launch_chunk_bwd(const ChunkBwdParams& p, hipStream_t stream) {
-  const int32_t per_row = p.seqs.T > 0 ? (p.seqs.T + C - 1) / C : 1;
+  const int32_t per_row = p.seqs.T > 0 ? (p.seqs.T + p.seqs.chunk - 1) / p.seqs.chunk : 1;
   hipError_t e;
   if (bwd_bf16_grad(p.qkv_bf16 != 0, p.K)) {
     e = launch_chunk_bwd_state_bf16(p, per_row, stream);

@@ -147,8 +147,8 @@ chunk_bwd_grad_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ 
   } else {
     const int row = gc / chunks_per_row;
     const int m = gc - row * chunks_per_row;
-    t0 = (int64_t)row * seqs.T + (int64_t)m * C;
-    cl = min(C, seqs.T - m * C);
+    t0 = (int64_t)row * seqs.T + (int64_t)m * seqs.chunk;
+    cl = min(seqs.chunk, seqs.T - m * seqs.chunk);
   }
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
@@ -524,7 +524,7 @@ chunk_bwd_state_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__
     seq = um.rank;
     chunk0 = um.rank * chunks_per_row;
   }
-  const int nchunks = (len + C - 1) / C;
+  const int nchunks = (len + seqs.chunk - 1) / seqs.chunk;
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, r = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int krow0 = kz * KT + w * (KT / 4);
@@ -556,8 +556,8 @@ chunk_bwd_state_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__
   const int64_t xrs = (int64_t)(rev ? H : Hkv) * K, yrs = (int64_t)(rev ? H : Hkv) * V;
   auto load_chunk = [&](int it) {
     const int m = rev ? nchunks - 1 - it : it;
-    const int64_t t0 = bos + (int64_t)m * C;
-    const int cl = min(C, len - m * C);
+    const int64_t t0 = bos + (int64_t)m * seqs.chunk;
+    const int cl = min(seqs.chunk, len - m * seqs.chunk);
 #pragma unroll
     for (int u = 0; u < NX; ++u) {
       const int p = tid + NTS * u;
@@ -575,7 +575,7 @@ chunk_bwd_state_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__
   if (nchunks > 0) load_chunk(0);
   for (int it = 0; it < nchunks; ++it) {
     const int m = rev ? nchunks - 1 - it : it;
-    const int cl = min(C, len - m * C);
+    const int cl = min(seqs.chunk, len - m * seqs.chunk);
     // record: forward -> the state entering chunk m; reverse -> the gradient
     // of the state leaving chunk m
     float* rec = (rev ? dhbuf : hbuf) + ((int64_t)(chunk0 + m) * H + hd) * KV + ucol;

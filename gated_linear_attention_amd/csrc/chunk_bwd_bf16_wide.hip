@@ -68,8 +68,8 @@ __device__ __forceinline__ void chunk_of(const SeqLayout& seqs, int gc, int chun
   } else {
     const int row = gc / chunks_per_row;
     const int m = gc - row * chunks_per_row;
-    t0 = (int64_t)row * seqs.T + (int64_t)m * C;
-    cl = min(C, seqs.T - m * C);
+    t0 = (int64_t)row * seqs.T + (int64_t)m * seqs.chunk;
+    cl = min(seqs.chunk, seqs.T - m * seqs.chunk);
   }
 }
 

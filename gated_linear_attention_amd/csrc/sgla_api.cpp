@@ -52,6 +52,8 @@ struct Plan {
   bool packed = false;
   std::vector<sgla::SeqEntry> seqs;      // packed only, longest first
   int32_t chunk_size = 0;                // requested chunk size (power of two <= 64)
+  int32_t grid_chunk = sgla::kChunk;     // tokens per chunk of the chunk tables: 64, or for the
+                                         // backward the requested chunk size
   bool prep = false;                     // wide-key bf16 path: per-chunk preparation buffers
   size_t seq_off = 0, chunk_off = 0, gate_off = 0, amat_off = 0, kt_off = 0, q_off = 0, total_bytes = 0;
   // segmented chains (bf16 K <= 128 forward)
@@ -239,8 +241,11 @@ void plan_segments(const sgla_chunk_args* a, const int64_t* cu, Plan* P) {
   }
 }
 
+// chunk_grid: lay the chunk tables out at the requested chunk size (the
+// backward, whose 64-row tiles take chunks of 16 or 32 tokens as short
+// chunks); every other entry point keeps its 64-token grid.
 sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv_support,
-                       Plan* P) {
+                       Plan* P, bool chunk_grid = false) {
   if (a == nullptr) return fail(SGLA_ERR_INVALID_ARG, "args is NULL");
   if (a->B < 0 || a->T < 0) return fail(SGLA_ERR_SHAPE, "B and T must be >= 0 (got B=%d T=%d)", a->B, a->T);
   if (a->H <= 0) return fail(SGLA_ERR_SHAPE, "H must be > 0 (got %d)", a->H);
@@ -252,6 +257,8 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
   if (cs > sgla::kChunk)
     return fail(SGLA_ERR_UNSUPPORTED, "chunk_size %d is not implemented (at most 64)", cs);
   P->chunk_size = cs;
+  P->grid_chunk = chunk_grid ? cs : sgla::kChunk;
+  const int64_t gcs = P->grid_chunk;
   if (need_kv_support) {
     if (a->K <= 0 || a->V <= 0) return fail(SGLA_ERR_SHAPE, "K and V must be > 0");
     if (a->qkv_dtype == SGLA_BF16) {
@@ -297,16 +304,19 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
       e.chunk0 = 0;
     }
     for (int32_t n = 1; n < P->N; ++n)
-      P->seqs[n].chunk0 = P->seqs[n - 1].chunk0 + (P->seqs[n - 1].len + sgla::kChunk - 1) / sgla::kChunk;
+      P->seqs[n].chunk0 = P->seqs[n - 1].chunk0 + (int32_t)((P->seqs[n - 1].len + gcs - 1) / gcs);
     // longest sequences first: they bound the critical path
     std::stable_sort(P->seqs.begin(), P->seqs.end(),
                      [](const sgla::SeqEntry& x, const sgla::SeqEntry& y) { return x.len > y.len; });
     int64_t nch = 0;
-    for (int32_t n = 0; n < P->N; ++n) nch += (cu[n + 1] - cu[n] + sgla::kChunk - 1) / sgla::kChunk;
+    for (int32_t n = 0; n < P->N; ++n) nch += (cu[n + 1] - cu[n] + gcs - 1) / gcs;
+    if (nch > INT32_MAX) return fail(SGLA_ERR_UNSUPPORTED, "%lld chunks exceed 2^31-1", (long long)nch);
     P->num_chunks = (int32_t)nch;
   } else {
     P->N = a->B;
-    P->num_chunks = a->T > 0 ? a->B * ((a->T + sgla::kChunk - 1) / sgla::kChunk) : 0;
+    const int64_t nch = a->T > 0 ? (int64_t)a->B * ((a->T + gcs - 1) / gcs) : 0;
+    if (nch > INT32_MAX) return fail(SGLA_ERR_UNSUPPORTED, "%lld chunks exceed 2^31-1", (long long)nch);
+    P->num_chunks = (int32_t)nch;
   }
   // workgroup counts of the launches must fit a 32-bit grid
   if ((int64_t)P->num_chunks * a->H > INT32_MAX)
@@ -361,10 +371,11 @@ struct BwdPlan {
 };
 
 sgla_status plan_bwd(const sgla_chunk_args* a, const int64_t* cu, BwdPlan* B) {
-  sgla_status st = plan_shape(a, cu, false, &B->P);
+  sgla_status st = plan_shape(a, cu, false, &B->P, true);
   if (st != SGLA_OK) return st;
-  st = need_chunk64(B->P);
-  if (st != SGLA_OK) return st;
+  if (B->P.chunk_size != sgla::kChunk && B->P.chunk_size != 32 && B->P.chunk_size != 16)
+    return fail(SGLA_ERR_UNSUPPORTED, "chunk_size %d is not implemented for the backward (16, 32 or 64)",
+                B->P.chunk_size);
   if (a->qkv_dtype != SGLA_BF16 && a->qkv_dtype != SGLA_F32)
     return fail(SGLA_ERR_DTYPE, "qkv_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", a->qkv_dtype);
   const bool wide = a->K == 256 || a->K == 512;
@@ -410,6 +421,8 @@ sgla_status upload_tables(const Plan& P, char* ws, hipStream_t stream) {
   auto* seq_table = reinterpret_cast<sgla::SeqEntry*>(ws + P.seq_off);
   auto* chunk_table = P.num_chunks == 0 ? nullptr : reinterpret_cast<sgla::ChunkEntry*>(ws + P.chunk_off);
   sgla::TablePut put;
+  put.chunk = P.grid_chunk;
+  put.pad = 0;
   for (size_t first = 0; first < P.seqs.size(); first += sgla::kTablePut) {
     const size_t n = std::min<size_t>(sgla::kTablePut, P.seqs.size() - first);
     put.first = (int32_t)first;
@@ -454,6 +467,7 @@ sgla::SeqLayout layout_of(const sgla_chunk_args* a, const Plan& P, char* ws) {
   L.seq_table = P.packed ? reinterpret_cast<const sgla::SeqEntry*>(ws + P.seq_off) : nullptr;
   L.chunk_table = P.packed ? reinterpret_cast<const sgla::ChunkEntry*>(ws + P.chunk_off) : nullptr;
   L.num_chunks = P.num_chunks;
+  L.chunk = P.grid_chunk;
   return L;
 }
 

@@ -47,7 +47,7 @@ struct SeqEntry {
 // Per-chunk entry used by the gate kernel for packed input.
 struct ChunkEntry {
   int32_t t0;    // first packed token of the chunk
-  int32_t len;   // tokens in the chunk (1..kChunk)
+  int32_t len;   // tokens in the chunk (1..chunk of the grid, at most kChunk)
 };
 
 // Up to kTablePut sequence-table entries carried by value in the arguments
@@ -58,6 +58,8 @@ constexpr int kTablePut = 126;
 struct TablePut {
   int32_t first;
   int32_t count;
+  int32_t chunk;   // tokens per chunk row (kChunk, or the backward's chunk_size)
+  int32_t pad;
   SeqEntry e[kTablePut];
 };
 hipError_t launch_table_put(const TablePut& put, SeqEntry* seq_table, ChunkEntry* chunk_table,
@@ -80,6 +82,8 @@ struct SeqLayout {
   const SeqEntry* seq_table; // packed only (device)
   const ChunkEntry* chunk_table; // packed only (device)
   int32_t num_chunks;        // total chunks over all sequences
+  int32_t chunk;             // tokens per chunk of this grid: kChunk, or for the backward the
+                             // requested chunk_size (16 or 32; such chunks run in 64-row tiles)
 };
 
 // Segments of long sequences (bf16 K <= 128 forward).  A sequence whose

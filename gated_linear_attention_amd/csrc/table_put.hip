@@ -23,11 +23,12 @@ table_put_kernel(TablePut put, SeqEntry* __restrict__ seq_table, ChunkEntry* __r
   const SeqEntry e = put.e[i];
   if (threadIdx.x == 0) seq_table[put.first + i] = e;
   if (chunk_table == nullptr) return;
-  const int32_t nch = (e.len + kChunk - 1) / kChunk;
+  const int32_t cs = put.chunk;
+  const int32_t nch = (e.len + cs - 1) / cs;
   for (int32_t c = threadIdx.x; c < nch; c += 64) {
     ChunkEntry ce;
-    ce.t0 = e.bos + c * kChunk;
-    ce.len = min(kChunk, e.len - c * kChunk);
+    ce.t0 = e.bos + c * cs;
+    ce.len = min(cs, e.len - c * cs);
     chunk_table[e.chunk0 + c] = ce;
   }
 }

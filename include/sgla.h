@@ -66,9 +66,9 @@ typedef enum { SGLA_BF16 = 1, SGLA_F32 = 2 } sgla_dtype;
 typedef struct {
   int32_t B, T, H, K, V;      /* packed input: B == 1 and T = total tokens */
   int32_t num_seqs;           /* packed: number of sequences N; dense: ignored (N = B) */
-  int32_t chunk_size;         /* tokens per chunk; 0 selects 64.  sgla_chunk_fwd: 16, 32 or 64;
-                                 sgla_chunk_local_cumsum: any power of two up to 64; the other
-                                 chunked entry points: 64 */
+  int32_t chunk_size;         /* tokens per chunk; 0 selects 64.  sgla_chunk_fwd and
+                                 sgla_chunk_bwd: 16, 32 or 64; sgla_chunk_local_cumsum: any
+                                 power of two up to 64; the other chunked entry points: 64 */
   int32_t qkv_dtype;          /* sgla_dtype of q, k and v */
   int32_t o_dtype;            /* sgla_dtype of o */
   float scale;                /* finite; callers wanting the default pass 1/sqrt(K) */
@@ -186,8 +186,8 @@ sgla_status sgla_chunk_fwd_noalloc(const sgla_chunk_args *args,
 
 /*
  * Bytes of device workspace sgla_chunk_bwd needs: the packed-sequence tables,
- * the fp32 state entering every 64-token chunk and the fp32 gradient of the
- * state leaving it (2 * 4 K V bytes per chunk and head), 4 bytes per
+ * the fp32 state entering every chunk (of chunk_size tokens) and the fp32
+ * gradient of the state leaving it (2 * 4 K V bytes per chunk and head), 4 bytes per
  * chunk and head for the g_gamma reduction, and with grouped kv heads (Hkv <
  * H) the per-query-head k and v gradients (4 (K + V) bytes per token and
  * query head).  Returns 0 on invalid arguments (reason in sgla_last_error()).
@@ -228,7 +228,10 @@ size_t sgla_chunk_bwd_workspace_size(const sgla_chunk_args *args, const int64_t 
  * Outputs must not overlap inputs or each other.
  * Supported: K in {16, 32, 64, 128}, V a multiple of 32, bf16 or float32
  * inputs; K in {256, 512} with bf16 inputs and V a multiple of 64;
- * chunk_size 64, any Hkv dividing H.  Other K, or K > 128 with float32
+ * chunk_size 16, 32 or 64 (section 二; section 五 runs the gradients at all
+ * three): the state records, the gate restarts and the per-chunk gradients
+ * follow chunks of that size, each computed in a 64-row tile whose rows past
+ * the chunk are zeros; any Hkv dividing H.  Other K, or K > 128 with float32
  * inputs, return SGLA_ERR_UNSUPPORTED.
  */
 sgla_status sgla_chunk_bwd(const sgla_chunk_args *args,

@@ -325,7 +325,8 @@ BWD_CASES = [
     ("g without dg", {}, dict(dg=False), INVALID, "dg is NULL"),
     ("g_gamma without dg_gamma", {}, dict(g=False, gg=True), INVALID, "dg_gamma is NULL"),
     ("NULL dout", {}, dict(do=None), INVALID, "non-NULL"),
-    ("chunk 32", dict(chunk=32), {}, UNSUPPORTED, "chunk_size"),
+    ("chunk 128", dict(chunk=128), {}, UNSUPPORTED, "chunk_size"),
+    ("chunk 48", dict(chunk=48), {}, UNSUPPORTED, "power of two"),
     ("cu not ending at T", dict(N=2), dict(cu=[0, 64, 100]), SHAPE, "equal T"),
     ("workspace small", dict(N=2), dict(cu=[0, 64, 128], ws_bytes=64), WORKSPACE, "workspace"),
     ("nan scale", dict(scale=float("nan")), {}, INVALID, "scale"),
@@ -374,6 +375,23 @@ def test_chunk_bwd_workspace_size(G):
     tasks = 2 * 3 * 3
     rec = tasks * 64 * 96 * 4
     assert n == 2 * rec + ((tasks * 4 + 255) // 256) * 256
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_chunk_bwd_workspace_size_small_chunks(G, chunk):
+    """At chunk_size 16 or 32 the backward's records follow the requested
+    chunk grid: one pair per chunk of that size (dense and packed)."""
+    up = lambda x: (x + 255) // 256 * 256
+    a = mkargs(G, B=2, T=130, H=3, K=64, V=96, chunk=chunk)
+    tasks = 2 * ((130 + chunk - 1) // chunk) * 3
+    assert G.lib.sgla_chunk_bwd_workspace_size(ctypes.byref(a), None) == \
+        2 * up(tasks * 64 * 96 * 4) + up(tasks * 4)
+    cu = np.array([0, 15, 100, 300], dtype=np.int64)
+    a = mkargs(G, B=1, T=300, H=3, N=3, K=64, V=96, chunk=chunk)
+    nch = sum((int(cu[i + 1] - cu[i]) + chunk - 1) // chunk for i in range(3))
+    tables = up(3 * 16) + up(nch * 8)
+    assert G.lib.sgla_chunk_bwd_workspace_size(ctypes.byref(a), ctypes.c_void_p(cu.ctypes.data)) == \
+        tables + 2 * up(nch * 3 * 64 * 96 * 4) + up(nch * 3 * 4)
 
 
 NORM_CASES = [

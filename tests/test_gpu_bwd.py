@@ -197,3 +197,52 @@ def test_bwd_odd_shapes(w):
     inp = make_chunk_inputs(w)
     bi = make_backward_inputs(inp, seed=12)
     compare(run_bwd(inp, bi), oracle_bwd(inp, bi), TOL_BF16 if inp["dtype"] == "bf16" else TOL_F32, w.name)
+
+
+# chunk sizes 16 and 32 (section 二: chunk_size is a power of two; section 五
+# runs the chunk kernels, gradients included, at 16, 32 and 64 with
+# cu_seqlens [0, 15, 100, 300, 1200, 2000])
+PAGES_LENGTHS = (15, 85, 200, 900, 800)
+CHUNK_CASES = [
+    small("cs_k64_varlen_pages", B=1, T=0, K=64, V=64, fixed_lengths=PAGES_LENGTHS, initial_state=True),
+    small("cs_k128_gamma", K=128, V=128, T=150, gate="gamma", initial_state=True),
+    small("cs_k16_v32", K=16, V=32, T=97),
+    small("cs_k256_h0", K=256, V=64, T=150, initial_state=True),
+    small("cs_k512_varlen", B=1, T=0, H=1, K=512, V=64, fixed_lengths=(15, 85, 0, 1, 200),
+          initial_state=True),
+    small("cs_f32_k32_varlen_pages", dtype="f32", B=1, T=0, K=32, V=64, fixed_lengths=PAGES_LENGTHS,
+          initial_state=True),
+    small("cs_gqa_k64", H=4, Hkv=2, K=64, V=64, T=130, initial_state=True),
+]
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("w", CHUNK_CASES, ids=lambda w: w.name)
+def test_bwd_chunk_sizes(w, chunk):
+    """The backward on the chunk grid of the requested size (the state
+    records, the gate restarts and the per-chunk gradients all follow
+    chunks of 16 or 32 tokens) against the oracle backward."""
+    inp = make_chunk_inputs(w)
+    inp["chunk_size"] = chunk
+    bi = make_backward_inputs(inp, seed=w.seed + 1)
+    got = run_bwd(inp, bi)
+    ref = oracle_bwd(inp, bi)
+    compare(got, ref, TOL_BF16 if inp["dtype"] == "bf16" else TOL_F32, f"{w.name} chunk {chunk}")
+
+
+@pytest.mark.parametrize("dtype,K", [("bf16", 128), ("f32", 64)])
+def test_bwd_chunk_sizes_agree(dtype, K):
+    """The three chunk sizes give the same gradients (three different chunk
+    grids, one function): within the bar of each other."""
+    inp = make_chunk_inputs(small("cs_agree", dtype=dtype, B=1, T=0, K=K, V=64, fixed_lengths=(70, 300, 33),
+                                  initial_state=True))
+    bi = make_backward_inputs(inp, seed=9)
+    outs = {}
+    for chunk in (16, 32, 64):
+        inp["chunk_size"] = chunk
+        outs[chunk] = run_bwd(inp, bi)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    for chunk in (16, 32):
+        for name in GRADS:
+            if outs[64][name] is not None:
+                assert err_ratio(outs[chunk][name], outs[64][name]) <= tol, (chunk, name)
