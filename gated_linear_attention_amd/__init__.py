@@ -13,7 +13,8 @@ Operator (page "flash-linear-attention 中的 Simple GLA", section 一):
 API conventions follow section 二 of that page: q [B, T, H, K], k [B, T, Hkv,
 K], v [B, T, Hkv, V], g [B, T, H] log gates or g_gamma [H] per-head log decay
 (not both), scale defaulting to 1/sqrt(K), states [N, H, K, V], cu_seqlens
-[N + 1] with B == 1 for packed input, chunk_size a power of two (64).  The kv
+[N + 1] with B == 1 for packed input, chunk_size 16, 32 or 64 (default 64;
+the decode and parallel entries take none).  The kv
 head count Hkv is read from k's shape and must divide H: query head h reads kv
 head h // (H // Hkv) (grouped-query attention, page "relinear", its GQA
 target); Hkv == H is plain multi-head attention.  ``state_v_first=True``

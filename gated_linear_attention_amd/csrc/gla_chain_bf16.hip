@@ -108,9 +108,9 @@ gla_chain_bf16_kernel(const bf16* __restrict__ v, const bf16* __restrict__ qk_hl
     bos = (int64_t)um.rank * seqs.T;
     len = seqs.T;
     seq = um.rank;
-    chunk0 = um.rank * ((seqs.T + C - 1) / C);
+    chunk0 = um.rank * ((seqs.T + seqs.chunk - 1) / seqs.chunk);
   }
-  const int nchunks = (len + C - 1) / C;
+  const int nchunks = (len + seqs.chunk - 1) / seqs.chunk;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -162,12 +162,12 @@ gla_chain_bf16_kernel(const bf16* __restrict__ v, const bf16* __restrict__ qk_hl
     }
 #pragma unroll
     for (int u = 0; u < NA; ++u) st.a[u] = *reinterpret_cast<const u32x4*>(arec + 8 * (tid + NT * u));
-    const int cl = min(C, len - m * C);
+    const int cl = min(seqs.chunk, len - m * seqs.chunk);
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int p = tid + NT * u;
       const int row = p / (VT / 8), seg = p % (VT / 8);
-      st.v[u] = row < cl ? *reinterpret_cast<const u32x4*>(vb + ((int64_t)m * C + row) * RSV + 8 * seg) : zero4;
+      st.v[u] = row < cl ? *reinterpret_cast<const u32x4*>(vb + ((int64_t)m * seqs.chunk + row) * RSV + 8 * seg) : zero4;
     }
     st.d = tid < K / 4 ? *reinterpret_cast<const u32x4*>(dl + rec * K + 4 * tid) : zero4;
   };
@@ -197,7 +197,7 @@ gla_chain_bf16_kernel(const bf16* __restrict__ v, const bf16* __restrict__ qk_hl
   Stage st;
   if (nchunks > 0) load_chunk(0, st);
   for (int m = 0; m < nchunks; ++m) {
-    const int cl = min(C, len - m * C);
+    const int cl = min(seqs.chunk, len - m * seqs.chunk);
     store_chunk(st);
     __syncthreads();   // chunk m staged; the previous chunk's exchange tiles read
     if (m + 1 < nchunks) load_chunk(m + 1, st);
@@ -292,7 +292,7 @@ gla_chain_bf16_kernel(const bf16* __restrict__ v, const bf16* __restrict__ qk_hl
     {
       const f32x4 x0 = sX[((w ^ 4) * 2 + 0) * 64 + lane];
       const f32x4 x1 = sX[((w ^ 4) * 2 + 1) * 64 + lane];
-      const auto ro = make_rsrc(ob + (int64_t)m * C * RSO, (uint32_t)cl * RSO * (uint32_t)sizeof(TOut));
+      const auto ro = make_rsrc(ob + (int64_t)m * seqs.chunk * RSO, (uint32_t)cl * RSO * (uint32_t)sizeof(TOut));
       const uint32_t c0 = 16 * own0 + r, c1 = 16 * own1 + r;
       store4<TOut>(ro, c0 * RSO * (uint32_t)sizeof(TOut) + ocol, mine0 + x0);
       store4<TOut>(ro, c1 * RSO * (uint32_t)sizeof(TOut) + ocol, mine1 + x1);

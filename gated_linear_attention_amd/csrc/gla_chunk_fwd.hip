@@ -205,10 +205,10 @@ gla_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const floa
     t0 = e.t0;
     cl = e.len;
   } else {
-    const int32_t ncs = (seqs.T + C - 1) / C;
+    const int32_t ncs = (seqs.T + seqs.chunk - 1) / seqs.chunk;
     const int32_t row = chunk / ncs, m = chunk - row * ncs;
-    t0 = (int64_t)row * seqs.T + (int64_t)m * C;
-    cl = min(C, seqs.T - m * C);
+    t0 = (int64_t)row * seqs.T + (int64_t)m * seqs.chunk;
+    cl = min(seqs.chunk, seqs.T - m * seqs.chunk);
   }
   const int tid = threadIdx.x;
   const int lane = tid & 63, g4 = lane >> 4, r = lane & 15;
@@ -407,7 +407,7 @@ gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     bos = (int64_t)um.rank * seqs.T;
     len = seqs.T;
     seq = um.rank;
-    chunk0 = um.rank * ((seqs.T + C - 1) / C);
+    chunk0 = um.rank * ((seqs.T + seqs.chunk - 1) / seqs.chunk);
   }
   const int tid = threadIdx.x;
   const int lane = tid & 63, g4 = lane >> 4, r = lane & 15;
@@ -444,10 +444,10 @@ gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   RowTile<K, NT, float> gt;
   RowTile<VT, NT, TIn> vtl;
   RowTile<C, NT, float> at;
-  const int nchunks = (len + C - 1) / C;
+  const int nchunks = (len + seqs.chunk - 1) / seqs.chunk;
   auto load_chunk = [&](int m) {
-    const int64_t t0 = bos + (int64_t)m * C;
-    const int cl = min(C, len - m * C);
+    const int64_t t0 = bos + (int64_t)m * seqs.chunk;
+    const int cl = min(seqs.chunk, len - m * seqs.chunk);
     qt.load(q + (t0 * H + hd) * K, (int64_t)H * K, cl);
     kt.load(k + (t0 * Hkv + hk) * K, (int64_t)Hkv * K, cl);
     gt.load(gk + (t0 * H + hd) * K, (int64_t)H * K, cl);
@@ -476,8 +476,8 @@ gla_chunk_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
   };
 
   for (int m = 0; m < nchunks; ++m) {
-    const int64_t t0 = bos + (int64_t)m * C;
-    const int cl = min(C, len - m * C);
+    const int64_t t0 = bos + (int64_t)m * seqs.chunk;
+    const int cl = min(seqs.chunk, len - m * seqs.chunk);
     qt.store(sQ, LDQ);
     kt.store(sK, LDQ);
     gt.store(sB, LDQ);

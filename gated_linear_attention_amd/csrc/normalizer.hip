@@ -59,10 +59,10 @@ __device__ __forceinline__ ChunkRange chunk_range(const SeqLayout& seqs, int32_t
     r.t0 = e.t0;
     r.len = e.len;
   } else {
-    const int32_t ncs = (seqs.T + C - 1) / C;
+    const int32_t ncs = (seqs.T + seqs.chunk - 1) / seqs.chunk;
     const int32_t row = chunk / ncs, m = chunk - row * ncs;
-    r.t0 = (int64_t)row * seqs.T + (int64_t)m * C;
-    r.len = min(C, seqs.T - m * C);
+    r.t0 = (int64_t)row * seqs.T + (int64_t)m * seqs.chunk;
+    r.len = min(seqs.chunk, seqs.T - m * seqs.chunk);
   }
   return r;
 }
@@ -187,9 +187,9 @@ norm_scan_kernel(float* __restrict__ zrec, const float* __restrict__ dlog,
   } else {
     len = seqs.T;
     seq = rank;
-    cbase = rank * ((seqs.T + C - 1) / C);
+    cbase = rank * ((seqs.T + seqs.chunk - 1) / seqs.chunk);
   }
-  const int nch = (len + C - 1) / C;
+  const int nch = (len + seqs.chunk - 1) / seqs.chunk;
   const int key = threadIdx.x;
   const int lane = key & 63;
   const bool mine = key < K;

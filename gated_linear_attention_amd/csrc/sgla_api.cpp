@@ -353,12 +353,11 @@ sgla_status plan_shape(const sgla_chunk_args* a, const int64_t* cu, bool need_kv
   return SGLA_OK;
 }
 
-// The fused chunk kernels work on 64-token chunks; smaller chunk sizes are
-// accepted by the standalone gate cumsum only.
-sgla_status need_chunk64(const Plan& P) {
-  if (P.chunk_size != sgla::kChunk)
-    return fail(SGLA_ERR_UNSUPPORTED, "chunk_size %d is not implemented for this entry point (only 64)",
-                P.chunk_size);
+// The entry points whose kernels run any chunk grid in 64-row tiles (the
+// backward, the elementwise-gate GLA, the normalizer): 16, 32 or 64.
+sgla_status need_chunk_16_32_64(const Plan& P) {
+  if (P.chunk_size != sgla::kChunk && P.chunk_size != 32 && P.chunk_size != 16)
+    return fail(SGLA_ERR_UNSUPPORTED, "chunk_size %d is not implemented (16, 32 or 64)", P.chunk_size);
   return SGLA_OK;
 }
 
@@ -373,9 +372,8 @@ struct BwdPlan {
 sgla_status plan_bwd(const sgla_chunk_args* a, const int64_t* cu, BwdPlan* B) {
   sgla_status st = plan_shape(a, cu, false, &B->P, true);
   if (st != SGLA_OK) return st;
-  if (B->P.chunk_size != sgla::kChunk && B->P.chunk_size != 32 && B->P.chunk_size != 16)
-    return fail(SGLA_ERR_UNSUPPORTED, "chunk_size %d is not implemented for the backward (16, 32 or 64)",
-                B->P.chunk_size);
+  st = need_chunk_16_32_64(B->P);
+  if (st != SGLA_OK) return st;
   if (a->qkv_dtype != SGLA_BF16 && a->qkv_dtype != SGLA_F32)
     return fail(SGLA_ERR_DTYPE, "qkv_dtype must be SGLA_BF16 or SGLA_F32 (got %d)", a->qkv_dtype);
   const bool wide = a->K == 256 || a->K == 512;
@@ -777,7 +775,7 @@ GlaPlan plan_gla(const sgla_chunk_args* a, const Plan& P) {
 
 size_t sgla_gla_chunk_fwd_workspace_size(const sgla_chunk_args* args, const int64_t* cu_seqlens_host) {
   Plan P;
-  if (plan_shape(args, cu_seqlens_host, false, &P) != SGLA_OK) return 0;
+  if (plan_shape(args, cu_seqlens_host, false, &P, true) != SGLA_OK) return 0;
   g_last_error.clear();
   return plan_gla(args, P).total_bytes;
 }
@@ -787,9 +785,9 @@ sgla_status sgla_gla_chunk_fwd(const sgla_chunk_args* args, const void* q, const
                                void* o, float* final_state, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
   Plan P;
-  sgla_status st = plan_shape(args, cu_seqlens_host, false, &P);
+  sgla_status st = plan_shape(args, cu_seqlens_host, false, &P, true);
   if (st != SGLA_OK) return st;
-  st = need_chunk64(P);
+  st = need_chunk_16_32_64(P);
   if (st != SGLA_OK) return st;
   const sgla_chunk_args& a = *args;
   if (a.qkv_dtype != SGLA_BF16 && a.qkv_dtype != SGLA_F32)
@@ -868,7 +866,7 @@ NormPlan plan_norm(const sgla_chunk_args* a, const Plan& P) {
 
 size_t sgla_chunk_normalizer_workspace_size(const sgla_chunk_args* args, const int64_t* cu_seqlens_host) {
   Plan P;
-  if (plan_shape(args, cu_seqlens_host, false, &P) != SGLA_OK) return 0;
+  if (plan_shape(args, cu_seqlens_host, false, &P, true) != SGLA_OK) return 0;
   if (args->K <= 0) return 0;
   g_last_error.clear();
   return plan_norm(args, P).total_bytes;
@@ -879,9 +877,9 @@ sgla_status sgla_chunk_normalizer(const sgla_chunk_args* args, const void* q, co
                                   float* den, float* final_z, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream) {
   Plan P;
-  sgla_status st = plan_shape(args, cu_seqlens_host, false, &P);
+  sgla_status st = plan_shape(args, cu_seqlens_host, false, &P, true);
   if (st != SGLA_OK) return st;
-  st = need_chunk64(P);
+  st = need_chunk_16_32_64(P);
   if (st != SGLA_OK) return st;
   const sgla_chunk_args& a = *args;
   if (a.qkv_dtype != SGLA_BF16 && a.qkv_dtype != SGLA_F32)

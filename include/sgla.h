@@ -66,9 +66,10 @@ typedef enum { SGLA_BF16 = 1, SGLA_F32 = 2 } sgla_dtype;
 typedef struct {
   int32_t B, T, H, K, V;      /* packed input: B == 1 and T = total tokens */
   int32_t num_seqs;           /* packed: number of sequences N; dense: ignored (N = B) */
-  int32_t chunk_size;         /* tokens per chunk; 0 selects 64.  sgla_chunk_fwd and
-                                 sgla_chunk_bwd: 16, 32 or 64; sgla_chunk_local_cumsum: any
-                                 power of two up to 64; the other chunked entry points: 64 */
+  int32_t chunk_size;         /* tokens per chunk; 0 selects 64.  sgla_chunk_fwd,
+                                 sgla_chunk_bwd, sgla_gla_chunk_fwd, sgla_chunk_normalizer:
+                                 16, 32 or 64; sgla_chunk_local_cumsum: any power of two up to
+                                 64 */
   int32_t qkv_dtype;          /* sgla_dtype of q, k and v */
   int32_t o_dtype;            /* sgla_dtype of o */
   float scale;                /* finite; callers wanting the default pass 1/sqrt(K) */
@@ -258,11 +259,13 @@ sgla_status sgla_chunk_bwd(const sgla_chunk_args *args,
  *   initial_state / final_state [N, H, K, V] (or [N, H, V, K] with
  *   state_v_first); cu_seqlens_host as for sgla_chunk_fwd;
  *   workspace >= sgla_gla_chunk_fwd_workspace_size(args, cu) bytes (the
- *   packed-sequence table, then a 64 x 64 float32 matrix per (chunk, head);
+ *   packed-sequence table, then a 64 x 64 float32 matrix per (chunk, head),
+ *   chunks of chunk_size tokens;
  *   0 when there are no tokens).
  * Two launches (per-chunk A in parallel over chunks, then the chunk chain),
  * all products on the fp32 matrix cores.  Supported: K in {16,
- * 32, 64, 128}, V a multiple of 32, bf16 or float32 inputs, chunk_size 64.
+ * 32, 64, 128}, V a multiple of 32, bf16 or float32 inputs, chunk_size 16,
+ * 32 or 64 (smaller chunks run as short chunks of the 64-row tiles).
  */
 size_t sgla_gla_chunk_fwd_workspace_size(const sgla_chunk_args *args, const int64_t *cu_seqlens_host);
 sgla_status sgla_gla_chunk_fwd(const sgla_chunk_args *args,
@@ -293,7 +296,8 @@ sgla_status sgla_gla_chunk_fwd(const sgla_chunk_args *args,
  *   workspace       >= sgla_chunk_normalizer_workspace_size(args, cu) bytes
  *                   (the packed-sequence table, then per (chunk, head) K + 1
  *                   floats of chunk records; 0 when there are no tokens)
- * Supported: K in {16, 32, 64, 128, 256}, bf16 or float32 inputs.
+ * Supported: K in {16, 32, 64, 128, 256}, bf16 or float32 inputs,
+ * chunk_size 16, 32 or 64 (the chunk records follow chunks of that size).
  */
 size_t sgla_chunk_normalizer_workspace_size(const sgla_chunk_args *args, const int64_t *cu_seqlens_host);
 sgla_status sgla_chunk_normalizer(const sgla_chunk_args *args, const void *q, const void *k,

@@ -56,7 +56,7 @@ def run(inp, gk, o_dtype=torch.float32, state_v_first=False):
         h0 = h0.transpose(-1, -2).contiguous()
     o, ht = sgla.gla_chunk_fwd(d["q"], d["k"], d["v"], to_dev(gk, torch.float32), scale=inp["scale"],
                                initial_state=h0, output_final_state=True, cu_seqlens=inp["cu_seqlens"],
-                               o_dtype=o_dtype, state_v_first=state_v_first)
+                               chunk_size=inp["chunk_size"], o_dtype=o_dtype, state_v_first=state_v_first)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), ht.cpu().numpy()
 
@@ -148,3 +148,30 @@ def test_gla_degenerate_gates(dtype, K, V, kind):
 ], ids=lambda w: w.name)
 def test_gla_odd_shapes(w):
     test_gla_small(w, 1.0)
+
+
+# chunk sizes 16 and 32 (section 二: a power of two; section 五 runs 16, 32
+# and 64 with cu_seqlens [0, 15, 100, 300, 1200, 2000]): both chains
+GLA_CHUNK_CASES = [
+    (small("cs_varlen_pages_bf16_chain", B=1, T=0, K=64, V=64, fixed_lengths=(15, 85, 200, 900, 800),
+           initial_state=True), 1.0),
+    (small("cs_k128_v128_strong", K=128, V=128, T=150, initial_state=True), 0.1),
+    (small("cs_fp32_chain_k32_v96", K=32, V=96, T=130, initial_state=True), 1.0),
+    (small("cs_f32_k64", dtype="f32", K=64, V=64, T=150, initial_state=True), 1.0),
+    (small("cs_gqa", H=4, Hkv=2, K=64, V=64, T=130, initial_state=True), 1.0),
+]
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("w,norm", GLA_CHUNK_CASES, ids=lambda x: x.name if hasattr(x, "name") else str(x))
+def test_gla_chunk_sizes(w, norm, chunk):
+    inp = make_chunk_inputs(w)
+    inp["chunk_size"] = chunk
+    gk = make_key_gates(inp, seed=w.seed + 3, normalizer=norm)
+    o, ht = run(inp, gk)
+    o_ref, h_ref = oracle.gla_fwd(inp["q"], inp["k"], inp["v"], gk, scale=inp["scale"],
+                                  initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"])
+    tol = TOL_BF16 if inp["dtype"] == "bf16" else TOL_F32
+    eo, eh = err_ratio(o, o_ref), err_ratio(ht, h_ref)
+    print(f"[gla {w.name} chunk {chunk}] o {eo:.2e} final {eh:.2e}", flush=True)
+    assert np.all(np.isfinite(o)) and eo <= tol and eh <= tol

@@ -42,8 +42,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
-def test_chunk_normalizer(w):
+def check_chunk_normalizer(w, chunk=64):
     inp = make_chunk_inputs(w)
     d = device_inputs(inp)
     rng = np.random.default_rng(w.seed + 7)
@@ -51,12 +50,35 @@ def test_chunk_normalizer(w):
           if inp["initial_state"] is not None else None)
     den, zt = sgla.chunk_normalizer(d["q"], d["k"], g=d["g"], g_gamma=d["g_gamma"], scale=inp["scale"],
                                     initial_z=to_dev(z0, torch.float32), output_final_state=True,
-                                    cu_seqlens=inp["cu_seqlens"])
+                                    cu_seqlens=inp["cu_seqlens"], chunk_size=chunk)
     torch.cuda.synchronize()
     den_ref, z_ref = oracle.normalizer(inp["q"], inp["k"], g=inp["g"], g_gamma=inp["g_gamma"],
                                        scale=inp["scale"], initial_z=z0, cu_seqlens=inp["cu_seqlens"])
     assert err_ratio(den.cpu().numpy(), den_ref) <= TOL_F32
     assert err_ratio(zt.cpu().numpy(), z_ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_chunk_normalizer(w):
+    check_chunk_normalizer(w)
+
+
+# chunk sizes 16 and 32 (section 二: a power of two; section 五 runs 16, 32
+# and 64 with cu_seqlens [0, 15, 100, 300, 1200, 2000])
+CHUNK_CASES = [
+    small("cs_varlen_pages", B=1, T=0, K=64, fixed_lengths=(15, 85, 200, 900, 800), initial_state=True),
+    small("cs_k128_gamma_h0", K=128, gate="gamma", initial_state=True, normalize_k=True, T=300),
+    small("cs_k16_f32", K=16, dtype="f32", T=97),
+    small("cs_gqa_k64", H=6, Hkv=2, K=64, T=140, initial_state=True),
+    # more than 32 chunks of 16 tokens: the chunk scan takes several batches
+    small("cs_long_varlen_k128", B=1, T=0, K=128, fixed_lengths=(1100, 5, 0, 700), initial_state=True),
+]
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("w", CHUNK_CASES, ids=lambda w: w.name)
+def test_chunk_normalizer_chunk_sizes(w, chunk):
+    check_chunk_normalizer(w, chunk)
 
 
 def test_normalizer_is_the_ones_column_of_the_augmented_forward():
