@@ -394,7 +394,24 @@ def test_chunk_bwd_workspace_size_small_chunks(G, chunk):
         tables + 2 * up(nch * 3 * 64 * 96 * 4) + up(nch * 3 * 4)
 
 
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_normalizer_and_gla_workspace_size_small_chunks(G, chunk):
+    """At chunk_size 16 or 32 the normalizer's and the elementwise-gate GLA's
+    per-chunk records follow the requested chunk grid (one record per chunk
+    of that size, each still a 64-row tile's worth)."""
+    al = lambda x: (x + 255) // 256 * 256
+    a = mkargs(G, B=2, T=100, H=3, K=64, chunk=chunk)
+    tasks = 2 * ((100 + chunk - 1) // chunk) * 3
+    assert G.lib.sgla_chunk_normalizer_workspace_size(ctypes.byref(a), None) == al(tasks * 64 * 4) + al(tasks * 4)
+    bf16_chain = lambda K: 4 * 64 * K * 2 + 2 * 64 * 64 * 2 + K * 4
+    assert G.lib.sgla_gla_chunk_fwd_workspace_size(ctypes.byref(a), None) == tasks * bf16_chain(64)
+    af = mkargs(G, B=2, T=100, H=3, K=64, qkv=F32, chunk=chunk)
+    assert G.lib.sgla_gla_chunk_fwd_workspace_size(ctypes.byref(af), None) == tasks * 64 * 64 * 4
+
+
 NORM_CASES = [
+    ("chunk 128", dict(chunk=128), {}, UNSUPPORTED, "chunk_size"),
+    ("chunk 24", dict(chunk=24), {}, UNSUPPORTED, "power of two"),
     ("K=512", dict(K=512), {}, UNSUPPORTED, "K in"),
     ("K=48", dict(K=48), {}, UNSUPPORTED, "K in"),
     ("both gates", {}, dict(gg=True), INVALID, "mutually exclusive"),
