@@ -63,6 +63,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 F32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA, TFLOP/s
+F64_MFMA_PEAK_TFLOPS = 78.6     # MI355X dense fp64 MFMA, TFLOP/s
 MALL_BYTES = 256 << 20
 METRIC = "chunked Simple-GLA fwd tokens/s + % bf16 MFMA peak; decode HBM GB/s"
 
@@ -663,6 +664,8 @@ def bench_parallel(workload: str, steps: int, warmup: int, warm_seconds: float):
     del fill_buf
     gbs = nbytes / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
+    qk_flops = B * H * (T * (T + 1) // 2) * 2 * K
+    floor_ms = (qk_flops / (F64_MFMA_PEAK_TFLOPS * 1e12) + (flops - qk_flops) / (F32_MFMA_PEAK_TFLOPS * 1e12)) * 1e3
     if f32:
         return {"workload": workload, "kernel": "parallel_fwd_f32_kernel", "launches_per_call": 1,
                 "config": {"B": B, "T": T, "H": H, "num_kv_heads": Hkv, "K": K, "V": V, "qkv_dtype": "f32",
@@ -673,7 +676,11 @@ def bench_parallel(workload: str, steps: int, warmup: int, warm_seconds: float):
                 "algorithmic_bytes_per_call": int(nbytes), "algorithmic_flops_per_call": int(flops),
                 "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": F32_MFMA_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tflops / F32_MFMA_PEAK_TFLOPS, 4),
-                             "dtype": "f32", "traffic": load_traffic(workload, "parallel_fwd_f32_kernel")},
+                             "dtype": "f32", "traffic": load_traffic(workload, "parallel_fwd_f32_kernel"),
+                             # the q.k half of the flops runs on the fp64 matrix cores (exact
+                             # products of float32 inputs), the A v half on the fp32 ones
+                             "design_floor_ms": round(floor_ms, 4),
+                             "attainable_frac": round(floor_ms / ms, 4)},
                 "hbm": {"achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)},
                 "write_ceiling": {"kernel": "torch fill_ of an A-sized float32 buffer",
                                   "achieved_gbs": round(fill_gbs, 1)}}
