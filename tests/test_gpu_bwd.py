@@ -246,3 +246,48 @@ def test_bwd_chunk_sizes_agree(dtype, K):
         for name in GRADS:
             if outs[64][name] is not None:
                 assert err_ratio(outs[chunk][name], outs[64][name]) <= tol, (chunk, name)
+
+
+# chunk sizes 16 and 32 at the edges: single tokens, exact multiples of the
+# chunk, one token past one, empty packed sequences, the [V, K] state layout
+CHUNK_EDGE_CASES = [
+    small("cse_t1", T=1, initial_state=True),
+    small("cse_t16", T=16, initial_state=True),
+    small("cse_t17_gamma", T=17, gate="gamma"),
+    small("cse_t33_k512", B=1, T=33, H=1, K=512, V=64, initial_state=True),
+    small("cse_tiny_varlen", B=1, T=0, K=128, V=64, fixed_lengths=(0, 1, 16, 17, 0, 32, 33, 2),
+          initial_state=True),
+    small("cse_f32_t48", dtype="f32", K=16, V=32, T=48, initial_state=True),
+]
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("w", CHUNK_EDGE_CASES, ids=lambda w: w.name)
+def test_bwd_chunk_sizes_edges(w, chunk):
+    inp = make_chunk_inputs(w)
+    inp["chunk_size"] = chunk
+    bi = make_backward_inputs(inp, seed=w.seed + 2)
+    got = run_bwd(inp, bi)
+    ref = oracle_bwd(inp, bi)
+    compare(got, ref, TOL_BF16 if inp["dtype"] == "bf16" else TOL_F32, f"{w.name} chunk {chunk}")
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_bwd_chunk_sizes_state_v_first(chunk):
+    """The [V, K] state layout at the small chunk sizes: the same gradients
+    bit for bit, dh0 transposed."""
+    inp = make_chunk_inputs(small("cs_vf", B=1, T=0, H=2, K=64, V=96, fixed_lengths=(100, 30),
+                                  initial_state=True, seed=3))
+    d = device_inputs(inp)
+    rng = np.random.default_rng(4)
+    do = to_dev(rng.standard_normal((1, inp["T"], 2, 96)).astype(np.float32), torch.bfloat16)
+    dht = to_dev(rng.standard_normal((2, 2, 64, 96)).astype(np.float32), torch.float32)
+    kw = dict(g=d["g"], scale=inp["scale"], cu_seqlens=inp["cu_seqlens"], chunk_size=chunk)
+    a = sgla.chunk_bwd(d["q"], d["k"], d["v"], do, initial_state=d["initial_state"], dht=dht, **kw)
+    b = sgla.chunk_bwd(d["q"], d["k"], d["v"], do,
+                       initial_state=d["initial_state"].transpose(-1, -2).contiguous(),
+                       dht=dht.transpose(-1, -2).contiguous(), state_v_first=True, **kw)
+    torch.cuda.synchronize()
+    for name in ("dq", "dk", "dv", "dg"):
+        assert torch.equal(a[name], b[name]), name
+    assert torch.equal(a["dh0"].transpose(-1, -2), b["dh0"])

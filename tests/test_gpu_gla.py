@@ -175,3 +175,35 @@ def test_gla_chunk_sizes(w, norm, chunk):
     eo, eh = err_ratio(o, o_ref), err_ratio(ht, h_ref)
     print(f"[gla {w.name} chunk {chunk}] o {eo:.2e} final {eh:.2e}", flush=True)
     assert np.all(np.isfinite(o)) and eo <= tol and eh <= tol
+
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("w,norm", [
+    (small("cse_t1", T=1, initial_state=True), 1.0),
+    (small("cse_t17_k128", K=128, V=128, T=17, initial_state=True), 1.0),
+    (small("cse_tiny_varlen", B=1, T=0, K=64, V=64, fixed_lengths=(0, 1, 16, 17, 0, 33), initial_state=True), 1.0),
+    (small("cse_f32_t48", dtype="f32", K=32, V=32, T=48, initial_state=True), 1.0),
+], ids=lambda x: x.name if hasattr(x, "name") else str(x))
+def test_gla_chunk_sizes_edges(w, norm, chunk):
+    inp = make_chunk_inputs(w)
+    inp["chunk_size"] = chunk
+    gk = make_key_gates(inp, seed=w.seed + 5, normalizer=norm)
+    o, ht = run(inp, gk)
+    o_ref, h_ref = oracle.gla_fwd(inp["q"], inp["k"], inp["v"], gk, scale=inp["scale"],
+                                  initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"])
+    tol = TOL_BF16 if inp["dtype"] == "bf16" else TOL_F32
+    assert np.all(np.isfinite(o)) and err_ratio(o, o_ref) <= tol and err_ratio(ht, h_ref) <= tol
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_gla_chunk_sizes_state_v_first(chunk):
+    """The [V, K] state layout at the small chunk sizes: the same o bit for
+    bit and the final state transposed."""
+    inp = make_chunk_inputs(small("cs_gla_vf", B=1, T=0, K=64, V=64, fixed_lengths=(70, 33), initial_state=True))
+    inp["chunk_size"] = chunk
+    gk = make_key_gates(inp, seed=11)
+    o_a, h_a = run(inp, gk)
+    o_b, h_b = run(inp, gk, state_v_first=True)
+    assert np.array_equal(o_a, o_b)
+    assert np.array_equal(h_a, np.swapaxes(h_b, -1, -2))

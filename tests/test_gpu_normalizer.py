@@ -72,6 +72,9 @@ CHUNK_CASES = [
     small("cs_gqa_k64", H=6, Hkv=2, K=64, T=140, initial_state=True),
     # more than 32 chunks of 16 tokens: the chunk scan takes several batches
     small("cs_long_varlen_k128", B=1, T=0, K=128, fixed_lengths=(1100, 5, 0, 700), initial_state=True),
+    small("cs_t1", T=1, initial_state=True),
+    small("cs_tiny_varlen", B=1, T=0, K=64, fixed_lengths=(0, 1, 16, 17, 0, 33), initial_state=True),
+    small("cs_empty", T=0, initial_state=True),
 ]
 
 
