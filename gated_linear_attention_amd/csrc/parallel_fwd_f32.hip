@@ -125,34 +125,60 @@ __global__ __launch_bounds__(NTH) void parallel_fwd_f32_kernel(ParallelParams p)
 #pragma unroll
   for (int vt = 0; vt < NVT; ++vt) O[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Key and value tiles (zeros past T, past K and past V).  Where the
+  // registers allow (K + V <= 256 after padding), the next tile is loaded
+  // into registers while the current one computes; otherwise each tile is
+  // loaded when it is staged.
+  constexpr bool PREF = KM + VM <= 256;
+  constexpr int NKL = KF4 * C / NTH, NVL = VF4 * C / NTH;
+  f32x4 kr[NKL], vr[NVL];
+  double gr = 0.0;
+  auto load_tile = [&](int jt) {
+    const int j0 = jt * C;
+#pragma unroll
+    for (int n = 0; n < NKL; ++n) {
+      const int f = tid + NTH * n, row = f / KF4, c4 = f % KF4;
+      kr[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (j0 + row < T && 4 * c4 < K)
+        kr[n] = *reinterpret_cast<const f32x4*>(kg + (((int64_t)b * T + j0 + row) * Hkv + hk) * K + 4 * c4);
+    }
+#pragma unroll
+    for (int n = 0; n < NVL; ++n) {
+      const int f = tid + NTH * n, row = f / VF4, c4 = f % VF4;
+      vr[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (j0 + row < T && 4 * c4 < V)
+        vr[n] = *reinterpret_cast<const f32x4*>(vg + (((int64_t)b * T + j0 + row) * Hkv + hk) * V + 4 * c4);
+    }
+    if (w == 0) gr = gate_at(p, b, h, j0 + lane);
+  };
+  auto stage_tile = [&]() {
+#pragma unroll
+    for (int n = 0; n < NKL; ++n) {
+      const int f = tid + NTH * n;
+      *reinterpret_cast<f32x4*>(sK + (f / KF4) * LDK + 4 * (f % KF4)) = kr[n];
+    }
+#pragma unroll
+    for (int n = 0; n < NVL; ++n) {
+      const int f = tid + NTH * n;
+      *reinterpret_cast<f32x4*>(sV + (f / VF4) * LDV + 4 * (f % VF4)) = vr[n];
+    }
+    if (w == 0) {
+      const double s = wave_scan_f64(gr, 64);
+      sL[lane] = s * kRcpLn2d;
+      if (lane == 63) sTot = s;
+    }
+  };
+
   double D = 0.0;  // gate sum from the key tile's start to the query tile's start (natural log)
+  if (PREF) load_tile(iq);
 #pragma nounroll
   for (int jt = iq; jt >= 0; --jt) {
     const int j0 = jt * C;
     __syncthreads();  // the previous tile's LDS reads are done
-    // stage the key and value tiles (zeros past T, past K and past V)
-#pragma unroll
-    for (int n = 0; n < KF4 * C / NTH; ++n) {
-      const int f = tid + NTH * n, row = f / KF4, c4 = f % KF4;
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (j0 + row < T && 4 * c4 < K)
-        x = *reinterpret_cast<const f32x4*>(kg + (((int64_t)b * T + j0 + row) * Hkv + hk) * K + 4 * c4);
-      *reinterpret_cast<f32x4*>(sK + row * LDK + 4 * c4) = x;
-    }
-#pragma unroll
-    for (int n = 0; n < VF4 * C / NTH; ++n) {
-      const int f = tid + NTH * n, row = f / VF4, c4 = f % VF4;
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (j0 + row < T && 4 * c4 < V)
-        x = *reinterpret_cast<const f32x4*>(vg + (((int64_t)b * T + j0 + row) * Hkv + hk) * V + 4 * c4);
-      *reinterpret_cast<f32x4*>(sV + row * LDV + 4 * c4) = x;
-    }
-    if (w == 0) {
-      const double s = wave_scan_f64(gate_at(p, b, h, j0 + lane), 64);
-      sL[lane] = s * kRcpLn2d;
-      if (lane == 63) sTot = s;
-    }
+    if (!PREF) load_tile(jt);
+    stage_tile();
     __syncthreads();
+    if (PREF && jt > 0) load_tile(jt - 1);   // in flight while this tile computes
     if (jt < iq) D += sTot;
     const double base = Rq + D * kRcpLn2d;  // exponent of A = base - sL[key] (log2)
 
