@@ -13,8 +13,7 @@ import torch
 import oracle
 from gla_workloads import (CHUNK_CONFIGS, DECODE_CONFIGS, ChunkWorkload, DecodeWorkload,
                            make_chunk_inputs, make_decode_inputs)
-from gpu_common import (DEV, TOL_BF16, TOL_F32, device_inputs, err_ratio, gpu_unit_slices,
-                        oracle_units, to_dev)
+from gpu_common import DEV, TOL_BF16, TOL_F32, device_inputs, err_ratio, to_dev
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -150,16 +149,8 @@ def test_chunk_bf16_output(K):
 
 
 # ---------------------------------------------------------------------------
-# the named workloads at full size (sampled units)
+# the named workloads at full size (whole tensors)
 # ---------------------------------------------------------------------------
-
-def _sample_units(N, H, n_units, seed, must=()):
-    rng = np.random.default_rng(seed)
-    units = set(must)
-    while len(units) < min(n_units, N * H):
-        units.add((int(rng.integers(N)), int(rng.integers(H))))
-    return sorted(units)
-
 
 def test_tiny_f32_full():
     inp = make_chunk_inputs(CHUNK_CONFIGS["tiny_f32"])
