@@ -80,6 +80,7 @@ KERNEL_SOURCES = {
                               "gate_scan.h", "unit_map.h"),
     "chunk_fwd_f32_kernel": ("chunk_fwd_f32.hip", "gate_scan.h", "unit_map.h"),
     "recurrent_step_kernel": ("recurrent_step.hip",),
+    "recurrent_step_vk_kernel": ("recurrent_step.hip",),
     "parallel_fwd_kernel": ("parallel_fwd.hip", "mfma_common.h", "gate_scan.h", "unit_map.h"),
     "parallel_fwd_f32_kernel": ("parallel_fwd_f32.hip", "mfma_common.h", "gate_scan.h", "unit_map.h"),
 }
@@ -344,7 +345,7 @@ def bench_decode(steps_timed: int, warmup: int, warm_seconds: float, state_v_fir
             "bytes_per_step": nbytes, "achieved_GBs": round(gbs, 1),
             "peak_GBs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
             "tokens_per_s": round(N / (mean_ms * 1e-3), 1),
-            "traffic": None if state_v_first else load_traffic(w.name, "recurrent_step_kernel")}
+            "traffic": load_traffic(w.name, "recurrent_step_vk_kernel" if state_v_first else "recurrent_step_kernel")}
 
 
 def decode_fresh_run(steps: int = 4):
